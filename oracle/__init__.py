@@ -1,0 +1,164 @@
+"""CPU oracle for the fp32 sum reduction -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The reduction library never does, and
+the oracle shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64 accumulation, built with
+gcc ``-O2 -fopenmp -ffp-contract=off``).  This module only builds that file
+and marshals numpy arrays into it.
+
+What it computes (the plain definition of a sum, see ``oracle.c``):
+
+* ``sum_1d(x)``            -> (S, A) with S = sum x[i], A = sum |x[i]|
+  ("High-Performance Reduction Kernels" README: 1D float32 sum reduction).
+* ``sum_dim(x, o, R, i)``  -> (S[o, i], A[o, i]) summed over the middle axis of a
+  contiguous [outer, R, inner] array (POPCORNBENCH level-1 problem 47 trace,
+  "sum over a dimension", reduce_dim = 1).
+* ``sum_dim_at(...)``      -> the same for a list of chosen outputs.
+* ``within_tolerance``     -> the acceptance rule |got - S| <= 1e-5*A + 1e-6,
+  NaN-aware.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+          "-shared", "-Wall", "-Wextra"]
+
+_default = None
+
+
+def build(force: bool = True, source: str = SOURCE, library: str = LIBRARY) -> str:
+    """Compile ``source`` (default ``oracle.c``) with gcc into ``library``."""
+    global _default
+    if not force and os.path.exists(library):
+        return library
+    tmp = library + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, "-lm"], check=True)
+    os.replace(tmp, library)
+    if library == LIBRARY:
+        _default = None
+    return library
+
+
+def _as_f32(x) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.float32:
+        raise TypeError("oracle takes float32 input, got %s" % x.dtype)
+    return x
+
+
+class Oracle:
+    """The oracle's entry points, bound to one compiled copy of ``oracle.c``."""
+
+    def __init__(self, library: str = LIBRARY):
+        lib = ctypes.CDLL(library)
+        i64, dp, vp = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p
+        lib.oracle_sum_1d.argtypes = [vp, i64, dp, dp]
+        lib.oracle_sum_1d.restype = None
+        lib.oracle_sum_dim.argtypes = [vp, i64, i64, i64, vp, vp, ctypes.c_int]
+        lib.oracle_sum_dim.restype = None
+        lib.oracle_sum_dim_at.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp]
+        lib.oracle_sum_dim_at.restype = None
+        lib.oracle_default_threads.argtypes = []
+        lib.oracle_default_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = library
+
+    def default_threads(self) -> int:
+        return int(self.lib.oracle_default_threads())
+
+    def sum_1d(self, x) -> Tuple[float, float]:
+        """(S, A): fp64 sum and fp64 sum of magnitudes of a float32 vector."""
+        x = _as_f32(x).reshape(-1)
+        s = ctypes.c_double()
+        a = ctypes.c_double()
+        self.lib.oracle_sum_1d(x.ctypes.data, x.size, ctypes.byref(s), ctypes.byref(a))
+        return s.value, a.value
+
+    def sum_dim(self, x, outer: int, R: int, inner: int, threads: int = 0):
+        """(S, A), each float64 [outer, inner]: sums over the middle axis."""
+        x = _as_f32(x).reshape(-1)
+        if x.size != outer * R * inner:
+            raise ValueError("size %d != %d*%d*%d" % (x.size, outer, R, inner))
+        s = np.empty((outer, inner), dtype=np.float64)
+        a = np.empty((outer, inner), dtype=np.float64)
+        self.lib.oracle_sum_dim(x.ctypes.data, outer, R, inner, s.ctypes.data,
+                                a.ctypes.data, int(threads))
+        return s, a
+
+    def sum_dim_at(self, x, outer: int, R: int, inner: int, o_idx, i_idx):
+        """(S, A) for the outputs (o_idx[k], i_idx[k]), each from the definition."""
+        x = _as_f32(x).reshape(-1)
+        if x.size != outer * R * inner:
+            raise ValueError("size %d != %d*%d*%d" % (x.size, outer, R, inner))
+        o_idx = np.ascontiguousarray(o_idx, dtype=np.int64)
+        i_idx = np.ascontiguousarray(i_idx, dtype=np.int64)
+        if o_idx.shape != i_idx.shape:
+            raise ValueError("index arrays differ in shape")
+        if o_idx.size and (o_idx.min() < 0 or o_idx.max() >= outer
+                           or i_idx.min() < 0 or i_idx.max() >= inner):
+            raise IndexError("sample index out of range")
+        s = np.empty(o_idx.size, dtype=np.float64)
+        a = np.empty(o_idx.size, dtype=np.float64)
+        self.lib.oracle_sum_dim_at(x.ctypes.data, outer, R, inner, o_idx.ctypes.data,
+                                   i_idx.ctypes.data, o_idx.size, s.ctypes.data,
+                                   a.ctypes.data)
+        return s, a
+
+
+def default() -> Oracle:
+    """The oracle built from ``oracle.c`` (compiled on first use if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def default_threads() -> int:
+    return default().default_threads()
+
+
+def sum_1d(x):
+    return default().sum_1d(x)
+
+
+def sum_dim(x, outer: int, R: int, inner: int, threads: int = 0):
+    return default().sum_dim(x, outer, R, inner, threads)
+
+
+def sum_dim_at(x, outer: int, R: int, inner: int, o_idx, i_idx):
+    return default().sum_dim_at(x, outer, R, inner, o_idx, i_idx)
+
+
+def tolerance(abs_sum):
+    """Per-output acceptance bound 1e-5 * A + 1e-6."""
+    return 1e-5 * np.asarray(abs_sum, dtype=np.float64) + 1e-6
+
+
+def within_tolerance(got, S, A) -> np.ndarray:
+    """Elementwise pass/fail of |got - S| <= 1e-5*A + 1e-6.
+
+    NaN-aware: an output passes when both sides are NaN; an infinite oracle
+    value must be matched exactly (same sign) by ``got``.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    both_nan = np.isnan(got) & np.isnan(S)
+    inf = np.isinf(S)
+    with np.errstate(invalid="ignore"):
+        close = np.abs(got - S) <= tolerance(A)
+    inf_ok = inf & (got == S)
+    return both_nan | inf_ok | (close & ~inf & ~np.isnan(S))

@@ -1,0 +1,120 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for the fp32 sum
+ * reduction.  TEST INFRASTRUCTURE ONLY: it is loaded by the test suite, by the
+ * smoke check and by the benchmark's CPU-baseline leg, never by the library.
+ * It shares no code, header or constant with the GPU path.
+ *
+ * What is computed is the plain definition of a sum; the pages never fix a
+ * summation order, so none is imitated here:
+ *
+ *   full reduce  S = sum_{i<n} x[i]
+ *       ("High-Performance Reduction Kernels" README: a 1D float32 sum of
+ *        n elements; "Seven-step reduction: 30x from one kernel": sum is the
+ *        first reduction it names)
+ *
+ *   axis reduce  out[o][i] = sum_{r<R} x[o][r][i]   over a contiguous
+ *                [outer, R, inner] array
+ *       (POPCORNBENCH Kimi-K2.6 level-1 problem 47 trace, "sum over a
+ *        dimension": shape [batch, dim1, dim2] reduced over dim 1, output
+ *        element (o, i) at o*inner + i, each one the sum of the R values that
+ *        sit inner elements apart)
+ *
+ * Every fp32 input is widened exactly to fp64 and accumulated in fp64, one
+ * element after the other in increasing index order (r increasing for the
+ * axis reduce).  Alongside each sum the oracle returns A = sum |x| over the
+ * same elements, which is what the acceptance bound |gpu - S| <= 1e-5*A + 1e-6
+ * is measured against.  IEEE semantics throughout: no fast-math, no
+ * contraction (built with -O2 -ffp-contract=off), NaN and Inf propagate, the
+ * empty sum is +0.0.
+ *
+ * The worst-case error of a sequential fp64 sum of n terms is below
+ * (n-1) * 2^-53 * A, i.e. 1.2e-7 * A at n = 1e9: two orders of magnitude under
+ * the acceptance bound.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of OpenMP threads a parallel region uses by default. */
+int oracle_default_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Full reduce of n floats: one sequential fp64 loop. */
+void oracle_sum_1d(const float* x, int64_t n, double* sum, double* abs_sum)
+{
+    double s = 0.0;
+    double a = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double v = (double)x[i];
+        s += v;
+        a += fabs(v);
+    }
+    *sum = s;
+    *abs_sum = a;
+}
+
+/*
+ * Axis reduce of a contiguous [outer, R, inner] float array into
+ * out[outer * inner] (and abs_out, same layout).  For one output (o, i) the
+ * terms are added in increasing r.  The loop over i sits inside the loop over
+ * r only so that rows are read front to back; it does not change the order in
+ * which any single output receives its terms.  Different o are independent
+ * and are shared out over `nthreads` OpenMP threads (<= 0: OpenMP default).
+ */
+void oracle_sum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
+                    double* out, double* abs_out, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = oracle_default_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t o = 0; o < outer; ++o) {
+        double* s = out + o * inner;
+        double* a = abs_out + o * inner;
+        for (int64_t i = 0; i < inner; ++i) {
+            s[i] = 0.0;
+            a[i] = 0.0;
+        }
+        for (int64_t r = 0; r < R; ++r) {
+            const float* row = x + (o * R + r) * inner;
+            for (int64_t i = 0; i < inner; ++i) {
+                double v = (double)row[i];
+                s[i] += v;
+                a[i] += fabs(v);
+            }
+        }
+    }
+}
+
+/*
+ * The same definition evaluated for m chosen outputs (o_idx[k], i_idx[k]),
+ * one at a time, straight from the formula.  Used to check sampled outputs of
+ * full-size inputs without reducing the whole array.
+ */
+void oracle_sum_dim_at(const float* x, int64_t outer, int64_t R, int64_t inner,
+                       const int64_t* o_idx, const int64_t* i_idx, int64_t m,
+                       double* out, double* abs_out)
+{
+    (void)outer;
+    for (int64_t k = 0; k < m; ++k) {
+        const int64_t o = o_idx[k];
+        const int64_t i = i_idx[k];
+        double s = 0.0;
+        double a = 0.0;
+        for (int64_t r = 0; r < R; ++r) {
+            double v = (double)x[(o * R + r) * inner + i];
+            s += v;
+            a += fabs(v);
+        }
+        out[k] = s;
+        abs_out[k] = a;
+    }
+}

@@ -1,0 +1,237 @@
+"""Pins for the CPU oracle: checks that tie it to something other than itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when that oracle is wrong.  ``test_oracle_pins.py`` runs them against the real
+oracle; ``test_oracle_mutants.py`` runs them against copies of ``oracle.c``
+with planted mistakes and requires every mistake to be caught.
+
+What the pins rest on (none of them re-types the oracle's own loop):
+
+* closed forms -- the harmonic number H_n for the README's synthetic input
+  x[i] = 1/(i+1); a constant c summed n times is n*c; index-encoded data
+  x[o, r, i] = o*B^2 + r*B + i sums over r to R*(o*B^2 + i) + B*R(R-1)/2;
+* exactness -- integer-valued data is summed exactly by any order, so the
+  oracle must equal the exact integer sum bit for bit;
+* a correctly rounded library sum -- ``math.fsum`` (Shewchuk), with the
+  sequential fp64 error bound (n-1) * 2^-53 * sum|x|;
+* a library axis routine -- numpy's ``sum(axis=1)`` on integer data (exact);
+* IEEE special cases -- NaN, +-Inf, signed zero, empty sums.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import workloads
+
+EULER_GAMMA = 0.5772156649015329
+U53 = 2.0 ** -53
+U24 = 2.0 ** -24
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def harmonic_closed_form(n: int) -> float:
+    """H_n = ln n + gamma + 1/(2n) - 1/(12 n^2) (next term: +1/(120 n^4))."""
+    return math.log(n) + EULER_GAMMA + 1.0 / (2 * n) - 1.0 / (12.0 * n * n)
+
+
+# --------------------------------------------------------------------------- 1D
+def pin_harmonic(orc):
+    """README synthetic input at n = 1e6 against the closed form of H_n.
+
+    Each fp32 term carries a relative rounding error <= 2^-24, so the exact sum
+    of the fp32 terms is within 2^-24 * H_n of H_n; the fp64 accumulation adds
+    at most (n-1) * 2^-53 * H_n.  A single dropped term (>= 1e-6) breaks it.
+    """
+    n = 1_000_000
+    x = workloads.harmonic(n)
+    S, A = orc.sum_1d(x)
+    H = harmonic_closed_form(n)
+    assert abs(S - H) <= U24 * H + n * U53 * H, (S, H)
+    assert S == A  # all terms positive
+    # and tighter: against the correctly rounded sum of the same fp32 terms
+    F = math.fsum(x.astype(np.float64).tolist())
+    assert abs(S - F) <= (n - 1) * U53 * A, (S, F)
+
+
+def pin_constants_1d(orc):
+    """A constant c summed n times is exactly n*c (all partials exact in fp64)."""
+    for c in (1.0, 0.5, -0.25, 3.0):
+        for n in (0, 1, 2, 3, 4, 5, 7, 64, 1000, 12345):
+            S, A = orc.sum_1d(np.full(n, c, dtype=np.float32))
+            assert S == n * c and A == n * abs(c), (c, n, S, A)
+
+
+def pin_integers_1d(orc):
+    """Integer-valued data: the oracle equals the exact integer sum."""
+    for seed, n in ((11, 1), (12, 17), (13, 4096), (14, 1_000_003)):
+        x = workloads.small_ints(n, seed)
+        exact = int(np.sum(x.astype(np.int64)))
+        exact_abs = int(np.sum(np.abs(x.astype(np.int64))))
+        S, A = orc.sum_1d(x)
+        assert S == exact and A == exact_abs, (n, S, exact, A, exact_abs)
+
+
+def pin_fsum_1d(orc):
+    """Random data against math.fsum within the sequential fp64 error bound."""
+    for seed, n, dist in ((21, 100_000, "normal"), (22, 1_000_000, "uniform"),
+                          (23, 999_999, "normal")):
+        lo, hi = (-1.0, 1.0) if dist == "uniform" else (0.0, 1.0)
+        x = workloads.random(n, seed, dist, lo, hi)
+        S, A = orc.sum_1d(x)
+        F = math.fsum(x.astype(np.float64).tolist())
+        Fa = math.fsum(np.abs(x.astype(np.float64)).tolist())
+        assert abs(S - F) <= (n - 1) * U53 * A, (n, S, F)
+        assert abs(A - Fa) <= (n - 1) * U53 * Fa, (n, A, Fa)
+
+
+def pin_special_values_1d(orc):
+    """IEEE propagation and signed zero; the empty sum is +0.0."""
+    S, A = orc.sum_1d(np.zeros(0, dtype=np.float32))
+    assert S == 0.0 and not math.copysign(1.0, S) < 0 and A == 0.0
+    S, _ = orc.sum_1d(np.full(9, -0.0, dtype=np.float32))
+    assert S == 0.0 and math.copysign(1.0, S) > 0, S
+    S, _ = orc.sum_1d(np.array([-0.0], dtype=np.float32))
+    assert math.copysign(1.0, S) > 0, S
+    x = np.ones(100, dtype=np.float32)
+    x[37] = np.nan
+    S, _ = orc.sum_1d(x)
+    assert math.isnan(S)
+    x = np.ones(100, dtype=np.float32)
+    x[5] = np.inf
+    S, A = orc.sum_1d(x)
+    assert S == math.inf and A == math.inf
+    x[90] = -np.inf
+    S, _ = orc.sum_1d(x)
+    assert math.isnan(S)
+    x = np.array([np.finfo(np.float32).max] * 4, dtype=np.float32)
+    S, _ = orc.sum_1d(x)  # finite in fp64
+    assert S == 4.0 * float(np.finfo(np.float32).max)
+    x = np.array([1e-45, 1e-45, -1e-45], dtype=np.float32)  # denormals kept
+    S, _ = orc.sum_1d(x)
+    assert S == float(x[0]) + float(x[1]) + float(x[2]) and S != 0.0
+
+
+# ------------------------------------------------------------------------- axis
+AXIS_SHAPES = ((3, 5, 7), (2, 9, 1), (1, 4, 6), (4, 1, 3), (5, 3, 2), (1, 1, 1),
+               (6, 33, 65), (2, 128, 4095 % 64 + 3))
+
+
+def index_encoded(outer, R, inner, B=64):
+    """x[o, r, i] = o*B^2 + r*B + i (exact in fp32 while < 2^24)."""
+    o = np.arange(outer, dtype=np.int64)[:, None, None]
+    r = np.arange(R, dtype=np.int64)[None, :, None]
+    i = np.arange(inner, dtype=np.int64)[None, None, :]
+    v = o * B * B + r * B + i
+    assert v.size == 0 or v.max() < 2 ** 24
+    return v.astype(np.float32).reshape(-1)
+
+
+def pin_index_closed_form(orc):
+    """Index-encoded data: sum over r is R*(o*B^2 + i) + B*R*(R-1)/2.
+
+    A transposed operand, a wrong stride, a dropped or repeated row or a
+    shifted column all change at least one output.
+    """
+    B = 64
+    for outer, R, inner in AXIS_SHAPES:
+        x = index_encoded(outer, R, inner, B)
+        S, A = orc.sum_dim(x, outer, R, inner)
+        o = np.arange(outer, dtype=np.float64)[:, None]
+        i = np.arange(inner, dtype=np.float64)[None, :]
+        want = R * (o * B * B + i) + B * R * (R - 1) / 2.0
+        assert np.array_equal(S, want), (outer, R, inner)
+        assert np.array_equal(A, want), (outer, R, inner)  # all terms >= 0
+        # the per-output entry point on a sample of outputs
+        oo, ii = np.meshgrid(np.arange(outer), np.arange(inner), indexing="ij")
+        s1, a1 = orc.sum_dim_at(x, outer, R, inner, oo.reshape(-1), ii.reshape(-1))
+        assert np.array_equal(s1, want.reshape(-1)), (outer, R, inner)
+        assert np.array_equal(a1, want.reshape(-1)), (outer, R, inner)
+
+
+def pin_constants_axis(orc):
+    """A constant c summed over R rows is exactly R*c in every output."""
+    for c in (1.0, 0.5, -0.25, 3.0):
+        for outer, R, inner in AXIS_SHAPES + ((2, 0, 3), (0, 4, 4), (3, 2, 0)):
+            x = np.full(outer * R * inner, c, dtype=np.float32)
+            S, A = orc.sum_dim(x, outer, R, inner)
+            assert S.shape == (outer, inner)
+            assert np.all(S == R * c) and np.all(A == R * abs(c)), (c, outer, R, inner)
+
+
+def pin_bruteforce_axis(orc):
+    """Every shape in [0..4]^3 (and a few wider) with integer data against
+    numpy's axis-1 sum in int64, which is exact."""
+    shapes = [(a, b, c) for a in range(5) for b in range(5) for c in range(5)]
+    shapes += [(3, 17, 63), (2, 64, 64), (1, 65, 129), (7, 3, 4095)]
+    for k, (outer, R, inner) in enumerate(shapes):
+        x = workloads.small_ints(outer * R * inner, 1000 + k)
+        want = x.astype(np.int64).reshape(outer, R, inner).sum(axis=1)
+        want_abs = np.abs(x.astype(np.int64)).reshape(outer, R, inner).sum(axis=1)
+        S, A = orc.sum_dim(x, outer, R, inner, threads=2)
+        assert np.array_equal(S, want.astype(np.float64)), (outer, R, inner)
+        assert np.array_equal(A, want_abs.astype(np.float64)), (outer, R, inner)
+
+
+def pin_fsum_axis(orc):
+    """Sampled outputs of random data against math.fsum of the strided column,
+    taken by numpy slicing (an indexing independent of the oracle's)."""
+    rng = np.random.default_rng(5)
+    for seed, (outer, R, inner) in ((31, (4, 1000, 37)), (32, (3, 4096, 5)),
+                                    (33, (64, 300, 1))):
+        x = workloads.random(outer * R * inner, seed, "normal")
+        S, A = orc.sum_dim(x, outer, R, inner)
+        x3 = x.reshape(outer, R, inner)
+        for _ in range(20):
+            o, i = int(rng.integers(outer)), int(rng.integers(inner))
+            col = x3[o, :, i].astype(np.float64)
+            F = math.fsum(col.tolist())
+            assert abs(S[o, i] - F) <= (R - 1) * U53 * A[o, i], (o, i)
+            assert abs(A[o, i] - math.fsum(np.abs(col).tolist())) <= R * U53 * A[o, i]
+
+
+def pin_special_values_axis(orc):
+    """NaN / Inf stay in their own output; signed zero gives +0.0."""
+    outer, R, inner = 2, 5, 3
+    x = np.ones(outer * R * inner, dtype=np.float32).reshape(outer, R, inner)
+    x[1, 3, 2] = np.nan
+    x[0, 0, 1] = np.inf
+    S, _ = orc.sum_dim(x, outer, R, inner)
+    assert math.isnan(S[1, 2]) and S[0, 1] == math.inf
+    assert np.isfinite(np.delete(S.reshape(-1), [1, 5])).all()
+    z = np.full(outer * R * inner, -0.0, dtype=np.float32)
+    S, _ = orc.sum_dim(z, outer, R, inner)
+    assert np.all(S == 0.0) and not np.any(np.signbit(S))
+
+
+def pin_page_shape_facts(orc):
+    """Shape arithmetic the problem-47 trace prints, checked against the
+    workload definition (the oracle is exercised on the page's own shape
+    family at a reduced R so the check stays small)."""
+    with open(os.path.join(GOLDEN, "problem47_shape_facts.json")) as f:
+        facts = json.load(f)
+    w = workloads.WORKLOADS["cols_128x4096x4095"]
+    assert list(w.shape) == facts["shape"]
+    outer, R, inner = w.outer, w.R, w.inner
+    assert R * inner == facts["slab_elements"]
+    assert (R * inner) % 16 == facts["slab_elements_mod_16"]
+    assert 4 * inner == facts["row_bytes"]
+    assert (4 * inner) % 16 == facts["row_bytes_mod_16"]
+    assert (4 * inner) % 128 == facts["row_bytes_over_128_line_offset"]
+    assert (4 * inner) // 128 == facts["row_bytes_line_index"]
+    assert w.out_numel == facts["outputs"]
+    # the oracle on that outer/inner with 4 rows: output count and layout
+    x = index_encoded(2, 4, inner, B=1)
+    S, _ = orc.sum_dim(x, 2, 4, inner)
+    assert S.size == 2 * inner
+
+
+ALL_PINS = [
+    pin_harmonic, pin_constants_1d, pin_integers_1d, pin_fsum_1d,
+    pin_special_values_1d, pin_index_closed_form, pin_constants_axis,
+    pin_bruteforce_axis, pin_fsum_axis, pin_special_values_axis,
+    pin_page_shape_facts,
+]

@@ -1,0 +1,80 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
+written into it (a dropped term, a wrong index, a transposed operand, a
+narrower accumulator, a wrong magnitude, a wrong starting value).  The copy is
+compiled into a temporary directory and the whole pin suite runs against it;
+the test requires at least one pin to fail for every mutant.  The real oracle
+is never modified.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+MUTANTS = {
+    # full reduce
+    "drops_last_element": (
+        "for (int64_t i = 0; i < n; ++i) {", "for (int64_t i = 0; i + 1 < n; ++i) {"),
+    "drops_first_element": (
+        "for (int64_t i = 0; i < n; ++i) {", "for (int64_t i = 1; i < n; ++i) {"),
+    "fp32_accumulator": (
+        "        double v = (double)x[i];\n        s += v;",
+        "        float v = x[i];\n        s = (float)((float)s + v);"),
+    "signed_magnitude_1d": (
+        "        s += v;\n        a += fabs(v);\n    }\n    *sum",
+        "        s += v;\n        a += v;\n    }\n    *sum"),
+    "negative_zero_start": (
+        "    double s = 0.0;\n    double a = 0.0;\n    for (int64_t i = 0; i < n;",
+        "    double s = -0.0;\n    double a = 0.0;\n    for (int64_t i = 0; i < n;"),
+    # axis reduce
+    "transposed_outer_and_R": (
+        "const float* row = x + (o * R + r) * inner;",
+        "const float* row = x + (r * outer + o) * inner;"),
+    "drops_last_row": (
+        "        for (int64_t r = 0; r < R; ++r) {\n            const float* row",
+        "        for (int64_t r = 0; r + 1 < R; ++r) {\n            const float* row"),
+    "shifted_column": (
+        "                double v = (double)row[i];",
+        "                double v = (double)row[(i + 1) % inner];"),
+    "row_stride_R_instead_of_inner": (
+        "const float* row = x + (o * R + r) * inner;",
+        "const float* row = x + o * R * inner + r * (inner > 1 ? inner - 1 : 1);"),
+    "signed_magnitude_axis": (
+        "                s[i] += v;\n                a[i] += fabs(v);",
+        "                s[i] += v;\n                a[i] += v;"),
+    # per-output entry point
+    "at_reversed_column": (
+        "double v = (double)x[(o * R + r) * inner + i];",
+        "double v = (double)x[(o * R + r) * inner + (inner - 1 - i)];"),
+    "at_drops_first_row": (
+        "        for (int64_t r = 0; r < R; ++r) {\n            double v",
+        "        for (int64_t r = 1; r < R; ++r) {\n            double v"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, "mutation site not unique: %s" % name
+    src = tmp_path / ("oracle_%s.c" % name)
+    src.write_text(source.replace(old, new))
+    lib = str(tmp_path / ("liboracle_%s.so" % name))
+    oracle.build(source=str(src), library=lib)
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, "mutant %s passed every pin" % name
