@@ -1,0 +1,228 @@
+"""Benchmark of the fp32 sum reduction on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME ...]
+
+One step is one pass of the whole reduction path over the two workloads the
+headline metric is quoted on:
+
+    rd_sum_1d  over normal_1e9          (1e9 floats, N(0,1), 4.0 GB)
+    rd_sum_dim over cols_128x4096x4095  ([128, 4096, 4095] reduced over dim 1,
+                                         U[0,1), 8.59 GB)
+
+Inputs are generated on the host (workloads.py), copied to HBM before the
+timed region, and stay resident.  W untimed steps, then K timed steps between
+two synchronisations.  `value` is the step's algorithmic bytes (every input
+read once, every output written once) over the step time, in GB/s.  Each call
+is also bracketed by HIP events on the stream the library launches on, which
+gives the per-call times of the `per_workload` block and the average launch
+time of the dominant kernel for `roofline`.
+
+`cpu_baseline` times the oracle (oracle/, fp64, the test reference) on the
+host over the same workloads: the full reduce single-threaded (it is one
+sequential loop), the axis reduce over all host threads.  The GPU results of
+the last step are checked against those oracle results (`parity`).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HBM GB/s & % of peak: fp32 sum n=1e9; [128,4096,4095] dim-1 reduce"
+PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+STEP_WORKLOADS = ["normal_1e9", "cols_128x4096x4095"]
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCE = os.path.join(ROOT, "sum_reduction_amd", "csrc", "rd_kernels.hip")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the workload's main kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source
+    (else None)."""
+    path = os.path.join(PROFILES, "traffic_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    digest = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    value = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not digest or not value or digest.group(1) != kernel_source_digest():
+        return None
+    return float(value.group(1))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", action="append", default=None,
+                    help="bench these workloads instead of the default step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: there is no multi-GPU path here "
+              "(a multi-GPU reduce would split the input and gather one partial "
+              "per GPU; it is not built)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sum_reduction_amd as rd
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    rd.load()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda", 0)
+    props = torch.cuda.get_device_properties(dev)
+    cu = props.multi_processor_count
+    names = args.workload or STEP_WORKLOADS
+    ws = [workloads.WORKLOADS[n] for n in names]
+
+    host, xs = {}, {}
+    for w in ws:
+        log("generating %s (%d floats)" % (w.name, w.numel))
+        host[w.name] = workloads.generate(w)
+        xs[w.name] = torch.from_numpy(host[w.name]).to(dev)
+    outs = {w.name: torch.empty(w.out_numel, dtype=torch.float32, device=dev) for w in ws}
+    plans = {w.name: (rd.rd_plan_1d(cu, w.numel) if w.full_reduce
+                      else rd.rd_plan_dim(cu, w.outer, w.R, w.inner)).as_dict()
+             for w in ws}
+    torch.cuda.synchronize()
+
+    def one_step(events=None):
+        for k, w in enumerate(ws):
+            if events is not None:
+                events[k][0].record()
+            if w.full_reduce:
+                rd.rd_sum_1d(xs[w.name], out=outs[w.name])
+            else:
+                rd.rd_sum_dim(xs[w.name], w.outer, w.R, w.inner, out=outs[w.name])
+            if events is not None:
+                events[k][1].record()
+
+    log("warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in ws] for _ in range(K)]
+    log("timing %d steps" % K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        one_step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    step_bytes = sum(w.algorithmic_bytes for w in ws)
+    value = step_bytes * K / elapsed / 1e9
+    per = {}
+    for k, w in enumerate(ws):
+        ms = sorted(ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(K))
+        med, mean = ms[len(ms) // 2], sum(ms) / len(ms)
+        per[w.name] = {
+            "ms_median": round(med, 5), "ms_mean": round(mean, 5),
+            "ms_min": round(ms[0], 5), "ms_max": round(ms[-1], 5),
+            "GBps_median": round(w.algorithmic_bytes / med / 1e6, 1),
+            "frac_of_peak": round(w.algorithmic_bytes / med / 1e6 / PEAK_GBS, 4),
+            "algorithmic_bytes": w.algorithmic_bytes,
+            "plan": plans[w.name],
+        }
+
+    # dominant kernel: the workload whose call takes longest; its call is one
+    # kernel launch when its plan has a single pass
+    dom = max(per, key=lambda n: per[n]["ms_mean"])
+    dw = workloads.WORKLOADS[dom]
+    achieved = dw.algorithmic_bytes / (per[dom]["ms_mean"] * 1e-3) / 1e9
+    traffic = measured_traffic(dom)
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
+        "kernel": "cols_kernel" if plans[dom]["path"] == "cols" else "rows_kernel",
+        "workload": dom, "launches_per_call": plans[dom]["passes"],
+        "kernel_source_sha256_16": kernel_source_digest(),
+    }
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": " + ".join(names),
+                   "shapes": {w.name: list(w.shape) for w in ws},
+                   "step_bytes": step_bytes,
+                   "frac_of_peak": round(value / PEAK_GBS, 4)},
+        "roofline": roofline,
+        "per_workload": per,
+        "device": {"name": props.name, "cu": cu, "gcn_arch": getattr(props, "gcnArchName", "")},
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = oracle.default_threads()
+        log("cpu baseline: oracle on %d host threads" % threads)
+        results, secs, nbytes, parity = {}, 0.0, 0, True
+        for w in ws:
+            t = time.perf_counter()
+            if w.full_reduce:
+                S, A = oracle.sum_1d(host[w.name])
+                S, A = np.array([S]), np.array([A])
+            else:
+                S, A = oracle.sum_dim(host[w.name], w.outer, w.R, w.inner, threads)
+            secs += time.perf_counter() - t
+            nbytes += w.algorithmic_bytes
+            got = outs[w.name].cpu().numpy()
+            ok = bool(oracle.within_tolerance(got.reshape(-1), S.reshape(-1),
+                                              A.reshape(-1)).all())
+            parity &= ok
+            results[w.name] = ok
+        result["cpu_baseline"] = {
+            "value": round(nbytes / secs / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "the whole step once: full reduce single-threaded, axis reduce "
+                      "over %d threads; %.1f s; %s" % (threads, secs, cpu_model()),
+        }
+        result["parity"] = {"ok": parity, "per_workload": results,
+                            "rule": "|gpu - S| <= 1e-5*sum|x| + 1e-6 per output"}
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,240 @@
+"""sum_reduction_amd -- fp32 sum reduction on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``librd.so``, the HIP library whose C ABI is
+``include/rd.h``.  Every step of a reduction runs in that library's kernels;
+this module only checks tensors, passes their device pointers and torch's
+current HIP stream, and turns status codes into exceptions.  There is no
+fallback: if ``librd.so`` is missing or fails to load, every call raises.
+
+    import torch, sum_reduction_amd as rd
+    x = torch.randn(128, 4096, 4095, device="cuda")
+    y = rd.rd_sum_dim(x, 128, 4096, 4095)      # [128, 4095], like x.sum(1)
+    s = rd.rd_sum_1d(x)                        # 1-element tensor, x.sum()
+
+Functions with the C names take the reduction's own sizes; ``sum`` is a
+torch-style convenience (``dim=None`` or one dimension) over them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "RdError", "RdPlan", "RdTune", "library_path", "load", "rd_sum_1d", "rd_sum_dim",
+    "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
+    "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "sum", "tuning",
+    "PATH_NAMES",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "librd.so")
+
+RD_OK = 0
+PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
+              5: "cols_narrow"}
+
+
+class RdError(RuntimeError):
+    """A non-RD_OK status from librd.so."""
+
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        super().__init__("%s: %s (hipError %d)" % (where, rd_status_string(status),
+                                                    hip_error))
+
+
+class RdPlan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("block_threads", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("col_waves", ctypes.c_int32),
+                ("row_waves", ctypes.c_int32), ("unroll", ctypes.c_int32),
+                ("nxcd", ctypes.c_int32), ("passes", ctypes.c_int32),
+                ("split", ctypes.c_int64), ("rows_per_split", ctypes.c_int64),
+                ("blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["path"] = PATH_NAMES.get(self.path, self.path)
+        return d
+
+
+class RdTune(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int32), ("col_waves", ctypes.c_int32),
+                ("row_waves", ctypes.c_int32), ("unroll", ctypes.c_int32),
+                ("split", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def load():
+    """Load librd.so (built by ``python -m sum_reduction_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError("librd.so is not built (%s); run `python -m "
+                           "sum_reduction_amd.build`" % LIBRARY)
+    lib = ctypes.CDLL(LIBRARY)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.rd_sum_1d.argtypes = [vp, i64, vp, vp]
+    lib.rd_sum_1d.restype = ctypes.c_int
+    lib.rd_sum_dim.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.rd_sum_dim.restype = ctypes.c_int
+    lib.rd_status_string.argtypes = [ctypes.c_int]
+    lib.rd_status_string.restype = ctypes.c_char_p
+    lib.rd_last_hip_error.argtypes = []
+    lib.rd_last_hip_error.restype = ctypes.c_int
+    lib.rd_version.argtypes = []
+    lib.rd_version.restype = ctypes.c_int
+    lib.rd_plan_dim.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(RdPlan)]
+    lib.rd_plan_dim.restype = ctypes.c_int
+    lib.rd_plan_1d.argtypes = [ctypes.c_int, i64, ctypes.POINTER(RdPlan)]
+    lib.rd_plan_1d.restype = ctypes.c_int
+    lib.rd_tune_set.argtypes = [ctypes.POINTER(RdTune)]
+    lib.rd_tune_set.restype = ctypes.c_int
+    lib.rd_tune_supported.argtypes = [i32, i32, i32, i32]
+    lib.rd_tune_supported.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != RD_OK:
+        raise RdError(status, where, load().rd_last_hip_error())
+
+
+def rd_status_string(status: int) -> str:
+    return load().rd_status_string(int(status)).decode()
+
+
+def rd_last_hip_error() -> int:
+    return load().rd_last_hip_error()
+
+
+def rd_version() -> int:
+    return load().rd_version()
+
+
+def rd_plan_dim(cu_count: int, outer: int, R: int, inner: int) -> RdPlan:
+    plan = RdPlan()
+    _check(load().rd_plan_dim(cu_count, outer, R, inner, ctypes.byref(plan)),
+           "rd_plan_dim")
+    return plan
+
+
+def rd_plan_1d(cu_count: int, n: int) -> RdPlan:
+    plan = RdPlan()
+    _check(load().rd_plan_1d(cu_count, n, ctypes.byref(plan)), "rd_plan_1d")
+    return plan
+
+
+def rd_tune_set(tune: Optional[RdTune]):
+    _check(load().rd_tune_set(ctypes.byref(tune) if tune is not None else None),
+           "rd_tune_set")
+
+
+def rd_tune_supported(path: str, group_or_col_waves: int, row_waves: int,
+                      unroll: int) -> bool:
+    code = {"rows": 2, "cols": 4}[path]
+    return bool(load().rd_tune_supported(code, group_or_col_waves, row_waves, unroll))
+
+
+class tuning:
+    """Context manager that sets a process-wide tuning override, then clears it."""
+
+    def __init__(self, **fields):
+        self.tune = RdTune(**fields)
+
+    def __enter__(self):
+        rd_tune_set(self.tune)
+        return self.tune
+
+    def __exit__(self, *exc):
+        rd_tune_set(None)
+
+
+# --------------------------------------------------------------- tensor API
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return h or None
+
+
+def _check_input(x, numel: int):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor, got device %s" % x.device)
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32, got %s" % x.dtype)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if x.numel() != numel:
+        raise ValueError("x has %d elements, the shape needs %d" % (x.numel(), numel))
+
+
+def _out_tensor(out, numel: int, device, shape):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if (not isinstance(out, torch.Tensor) or out.dtype != torch.float32
+            or out.device != device or not out.is_contiguous() or out.numel() != numel):
+        raise ValueError("out must be a contiguous float32 tensor of %d elements on %s"
+                         % (numel, device))
+    return out
+
+
+def rd_sum_1d(x, out=None, stream=None):
+    """Sum of all elements of the float32 GPU tensor ``x`` into ``out`` (a
+    1-element tensor, allocated when None).  Asynchronous on ``stream``
+    (default: torch's current stream)."""
+    _check_input(x, x.numel() if hasattr(x, "numel") else -1)
+    out = _out_tensor(out, 1, x.device, (1,))
+    ptr = x.data_ptr() if x.numel() else None
+    _check(load().rd_sum_1d(ptr, x.numel(), out.data_ptr(), _stream_handle(stream)),
+           "rd_sum_1d")
+    return out
+
+
+def rd_sum_dim(x, outer: int, R: int, inner: int, out=None, stream=None):
+    """out[o, i] = sum_r x[o, r, i] for x viewed as [outer, R, inner]; ``out``
+    is [outer, inner] (allocated when None)."""
+    _check_input(x, outer * R * inner)
+    out = _out_tensor(out, outer * inner, x.device, (outer, inner))
+    xp = x.data_ptr() if x.numel() else None
+    op = out.data_ptr() if out.numel() else None
+    _check(load().rd_sum_dim(xp, outer, R, inner, op, _stream_handle(stream)),
+           "rd_sum_dim")
+    return out
+
+
+def sum(x, dim: Optional[int] = None, out=None, stream=None):
+    """torch.sum(x) or torch.sum(x, dim) for a contiguous float32 GPU tensor,
+    through rd_sum_1d / rd_sum_dim.  Returns a 0-d tensor for dim=None."""
+    if dim is None:
+        return rd_sum_1d(x, None if out is None else out.view(1), stream).view(())
+    shape = tuple(x.shape)
+    d = dim % len(shape)
+    outer = 1
+    for s in shape[:d]:
+        outer *= s
+    inner = 1
+    for s in shape[d + 1:]:
+        inner *= s
+    res = rd_sum_dim(x, outer, shape[d], inner,
+                     None if out is None else out.view(outer, inner), stream)
+    return res.view(shape[:d] + shape[d + 1:])

@@ -1,0 +1,240 @@
+// rd_api.cpp -- the C ABI of include/rd.h: argument validation, per-device
+// state, the stream-ordered workspace and the launch sequence of a plan.
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include <hip/hip_runtime_api.h>
+
+#include "rd_internal.h"
+
+namespace {
+
+thread_local int t_last_hip = 0;
+
+// Per-device state, created once on first use of the device: its CU count
+// (which fixes the plan, hence the summation order) and a memory pool of the
+// library's own for workspaces, which keeps its memory between calls.
+constexpr int kMaxDevices = 64;
+struct Device {
+    std::once_flag once;
+    int cu = 0;
+    hipMemPool_t pool = nullptr;
+    hipError_t err = hipSuccess;
+};
+Device g_devices[kMaxDevices];
+
+std::mutex g_tune_mu;
+rd_tune g_tune;
+bool g_tune_on = false;
+
+rd_status hip_fail(hipError_t e, rd_status st) {
+    t_last_hip = static_cast<int>(e);
+    return st;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// [a, a + na) and [b, b + nb) in floats
+bool overlap(const float* a, int64_t na, const float* b, int64_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    const uintptr_t a1 = a0 + uintptr_t(na) * 4u, b1 = b0 + uintptr_t(nb) * 4u;
+    return a0 < b1 && b0 < a1;
+}
+
+rd_status current_device(Device** out) {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count < 1) {
+        t_last_hip = static_cast<int>(e);
+        return RD_ERR_NO_DEVICE;
+    }
+    int dev = -1;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, RD_ERR_NO_DEVICE);
+    if (dev < 0 || dev >= kMaxDevices) return RD_ERR_NO_DEVICE;
+    Device& d = g_devices[dev];
+    std::call_once(d.once, [&d, dev] {
+        int cu = 0;
+        hipError_t err =
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess || cu < 1) {
+            d.err = err != hipSuccess ? err : hipErrorInvalidDevice;
+            return;
+        }
+        hipMemPoolProps props;
+        memset(&props, 0, sizeof(props));
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        err = hipMemPoolCreate(&d.pool, &props);
+        if (err != hipSuccess) {
+            d.err = err;
+            return;
+        }
+        uint64_t keep = UINT64_MAX;  // hold freed workspace for the next call
+        err = hipMemPoolSetAttribute(d.pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (err != hipSuccess) {
+            d.err = err;
+            return;
+        }
+        d.cu = cu;
+    });
+    if (d.err != hipSuccess) return hip_fail(d.err, RD_ERR_HIP);
+    *out = &d;
+    return RD_OK;
+}
+
+rd_status make_plan(int cu, int64_t outer, int64_t R, int64_t inner, rd_plan* plan) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return rd::plan_dim(cu, outer, R, inner, g_tune_on ? &g_tune : nullptr, plan);
+}
+
+// Failure injection for tests of the error paths, read from the environment:
+// RD_TEST_FAIL_ALLOC makes the workspace allocation fail, RD_TEST_FAIL_LAUNCH
+// makes the first launch fail; neither enqueues any work.
+bool inject(const char* name) {
+    const char* v = getenv(name);
+    return v && v[0] && v[0] != '0';
+}
+
+rd_status execute(const rd_plan& p, Device& dev, const float* x, int64_t outer, int64_t R,
+                  int64_t inner, float* out, hipStream_t s) {
+    if (p.path == RD_PATH_NONE) return RD_OK;
+    if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
+    float* ws = nullptr;
+    if (p.workspace_bytes > 0) {
+        if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
+        hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
+                                              size_t(p.workspace_bytes), dev.pool, s);
+        if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
+    }
+    hipError_t e = hipSuccess;
+    switch (p.path) {
+        case RD_PATH_ZERO:
+            e = rd::launch_fill_zero(out, outer * inner, s);
+            break;
+        case RD_PATH_ROWS_SHORT:
+            e = rd::launch_rows_short(x, outer, R, out, s);
+            break;
+        case RD_PATH_ROWS:
+            if (p.split == 1) {
+                e = rd::launch_rows(p, x, outer, R, out, s);
+            } else {
+                e = rd::launch_rows(p, x, outer, R, ws, s);
+                if (e == hipSuccess) e = rd::launch_rows_combine(ws, outer, p.split, out, s);
+            }
+            break;
+        case RD_PATH_COLS:
+        case RD_PATH_COLS_NARROW: {
+            float* dst = p.split == 1 ? out : ws;
+            e = p.path == RD_PATH_COLS ? rd::launch_cols(p, x, outer, R, inner, dst, s)
+                                       : rd::launch_cols_narrow(p, x, outer, R, inner, dst, s);
+            if (e == hipSuccess && p.split > 1)
+                e = rd::launch_slab_combine(ws, p.split, outer * inner, out, s);
+            break;
+        }
+        default:
+            e = hipErrorInvalidValue;
+    }
+    if (ws) {
+        hipError_t f = hipFreeAsync(ws, s);
+        if (e == hipSuccess && f != hipSuccess) return hip_fail(f, RD_ERR_HIP);
+    }
+    if (e != hipSuccess) return hip_fail(e, RD_ERR_LAUNCH);
+    return RD_OK;
+}
+
+rd_status sum_dim_checked(const float* x, int64_t outer, int64_t R, int64_t inner,
+                          float* out, hipStream_t stream) {
+    Device* dev = nullptr;
+    rd_status st = current_device(&dev);
+    if (st != RD_OK) return st;
+    rd_plan plan;
+    st = make_plan(dev->cu, outer, R, inner, &plan);
+    if (st != RD_OK) return st;
+    return execute(plan, *dev, x, outer, R, inner, out, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+rd_status rd_sum_1d(const float* x, int64_t n, float* out, hipStream_t stream) {
+    if (n < 0 || n > INT64_MAX / 4 || !out || !aligned4(out)) return RD_ERR_INVALID_ARG;
+    if (n > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
+    if (overlap(x, n, out, 1)) return RD_ERR_INVALID_ARG;
+    return sum_dim_checked(x, 1, n, 1, out, stream);
+}
+
+rd_status rd_sum_dim(const float* x, int64_t outer, int64_t R, int64_t inner, float* out,
+                     hipStream_t stream) {
+    if (outer < 0 || R < 0 || inner < 0) return RD_ERR_INVALID_ARG;
+    const int64_t lim = INT64_MAX / 4;
+    if (outer && inner && inner > lim / outer) return RD_ERR_INVALID_ARG;
+    const int64_t nout = outer * inner;
+    if (nout && R && R > lim / nout) return RD_ERR_INVALID_ARG;
+    const int64_t nin = nout * R;
+    if (nout == 0) return RD_OK;  // nothing to write, no HIP call
+    if (!out || !aligned4(out)) return RD_ERR_INVALID_ARG;
+    if (nin > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
+    if (overlap(x, nin, out, nout)) return RD_ERR_INVALID_ARG;
+    return sum_dim_checked(x, outer, R, inner, out, stream);
+}
+
+const char* rd_status_string(rd_status status) {
+    switch (status) {
+        case RD_OK: return "RD_OK";
+        case RD_ERR_INVALID_ARG: return "RD_ERR_INVALID_ARG";
+        case RD_ERR_NO_DEVICE: return "RD_ERR_NO_DEVICE";
+        case RD_ERR_ALLOC: return "RD_ERR_ALLOC";
+        case RD_ERR_LAUNCH: return "RD_ERR_LAUNCH";
+        case RD_ERR_HIP: return "RD_ERR_HIP";
+    }
+    return "RD_ERR_UNKNOWN";
+}
+
+int rd_last_hip_error(void) { return t_last_hip; }
+
+int rd_version(void) {
+    return RD_VERSION_MAJOR * 10000 + RD_VERSION_MINOR * 100 + RD_VERSION_PATCH;
+}
+
+rd_status rd_plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                      rd_plan* plan) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return rd::plan_dim(cu_count, outer, R, inner, g_tune_on ? &g_tune : nullptr, plan);
+}
+
+rd_status rd_plan_1d(int cu_count, int64_t n, rd_plan* plan) {
+    return rd_plan_dim(cu_count, 1, n, 1, plan);
+}
+
+rd_status rd_tune_set(const rd_tune* tune) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    if (!tune) {
+        g_tune_on = false;
+        memset(&g_tune, 0, sizeof(g_tune));
+        return RD_OK;
+    }
+    if (tune->group < 0 || tune->col_waves < 0 || tune->row_waves < 0 || tune->unroll < 0 ||
+        tune->split < 0)
+        return RD_ERR_INVALID_ARG;
+    g_tune = *tune;
+    g_tune_on = true;
+    return RD_OK;
+}
+
+int rd_tune_supported(int32_t path, int32_t group_or_col_waves, int32_t row_waves,
+                      int32_t unroll) {
+    if (path == RD_PATH_ROWS) return rd::rows_shape_supported(group_or_col_waves, unroll);
+    if (path == RD_PATH_COLS)
+        return rd::cols_shape_supported(group_or_col_waves, row_waves, unroll);
+    return 0;
+}
+
+}  // extern "C"

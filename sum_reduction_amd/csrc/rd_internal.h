@@ -1,0 +1,47 @@
+// rd_internal.h -- declarations shared by the C ABI, the planner and the
+// kernel launchers.  Not installed; the public boundary is include/rd.h.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "rd.h"
+
+namespace rd {
+
+// Lanes per wavefront on CDNA.
+constexpr int kWave = 64;
+// Threads of every ROWS / combine / fill workgroup.
+constexpr int kBlock = 256;
+// Rows shorter than this take the lane-per-row path.
+constexpr int64_t kShortRow = 64;
+// Upper bound on workgroups per launch; larger problems loop inside the
+// kernels (a grid's total thread count must stay below 2^32 on AMD, and
+// workgroups have up to 1024 threads).
+constexpr int64_t kMaxBlocks = int64_t(1) << 20;
+
+// Planner (rd_plan.cpp).  `tune` may be null.
+rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                   const rd_tune* tune, rd_plan* plan);
+
+// Kernel launchers (rd_kernels.hip).  Each enqueues on `s` and returns the
+// error hipLaunchKernel reports for the launch.
+hipError_t launch_fill_zero(float* out, int64_t n, hipStream_t s);
+hipError_t launch_rows(const rd_plan& p, const float* x, int64_t outer, int64_t R,
+                       float* dst, hipStream_t s);
+hipError_t launch_rows_short(const float* x, int64_t outer, int64_t R, float* out,
+                             hipStream_t s);
+hipError_t launch_rows_combine(const float* part, int64_t outer, int64_t P,
+                               float* out, hipStream_t s);
+hipError_t launch_cols(const rd_plan& p, const float* x, int64_t outer, int64_t R,
+                       int64_t inner, float* dst, hipStream_t s);
+hipError_t launch_cols_narrow(const rd_plan& p, const float* x, int64_t outer,
+                              int64_t R, int64_t inner, float* dst, hipStream_t s);
+hipError_t launch_slab_combine(const float* slab, int64_t S, int64_t n, float* out,
+                               hipStream_t s);
+
+// Which kernel shapes this build instantiates (rd_kernels.hip).
+bool rows_shape_supported(int group, int unroll);
+bool cols_shape_supported(int col_waves, int row_waves, int unroll);
+
+}  // namespace rd

@@ -1,0 +1,172 @@
+// rd_plan.cpp -- how a reduction is cut into kernels (host logic, no HIP call).
+//
+// The pages size their grids from the SM count ("High-Performance Reduction
+// Kernels" README, key design decisions: blocks = multiProcessorCount x
+// max_blocks_per_SM) and worry that a grid of a few hundred blocks is too
+// small for the chip (POPCORNBENCH problem-47 trace, grid sizing discussion).
+// Here the grid is sized from the CU count to keep about 32 waves per CU in
+// flight (8 per SIMD), and a reduction whose natural parallelism is too small
+// is split along R, with a second, fixed-order pass over the partials.
+#include <string.h>
+
+#include "rd_internal.h"
+
+namespace rd {
+namespace {
+
+constexpr int64_t kWavesPerCu = 32;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int32_t nxcd_for(int cu_count) {
+    // MI355X: 8 XCDs of 32 CUs.  Only used to spread the workgroup numbering,
+    // so a wrong guess costs locality, never correctness.
+    return (cu_count >= 8 && cu_count % 8 == 0) ? 8 : 1;
+}
+
+rd_status plan_rows(int cu, int64_t outer, int64_t R, const rd_tune* t, rd_plan* p) {
+    const bool forced = t && (t->group || t->unroll || t->split);
+    if (R < kShortRow && !forced) {
+        p->path = RD_PATH_ROWS_SHORT;
+        p->block_threads = kBlock;
+        p->group = 1;
+        p->split = 1;
+        p->passes = 1;
+        p->blocks = ceil_div(outer, kBlock);
+        if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
+        return RD_OK;
+    }
+    p->path = RD_PATH_ROWS;
+    p->block_threads = kBlock;
+    p->group = (t && t->group) ? t->group : (R >= 4096 ? 256 : 64);
+    p->unroll = (t && t->unroll) ? t->unroll : 8;
+    if (!rows_shape_supported(p->group, p->unroll)) return RD_ERR_INVALID_ARG;
+
+    const int64_t nvec = R / 4;
+    int64_t P = 1;
+    if (t && t->split) {
+        P = t->split;
+        if (P < 1) return RD_ERR_INVALID_ARG;
+    } else {
+        const int64_t target_lanes = int64_t(cu) * kWavesPerCu * kWave;
+        if (outer < target_lanes / p->group) {
+            P = ceil_div(target_lanes, outer * p->group);
+            // every lane gets at least one full unrolled step of loads
+            int64_t cap = nvec / (int64_t(p->group) * p->unroll);
+            if (cap < 1) cap = 1;
+            if (P > cap) P = cap;
+        }
+    }
+    if (P > INT64_MAX / 4 / outer) return RD_ERR_INVALID_ARG;
+    p->split = P;
+    const int64_t segs = outer * P;
+    const int64_t groups_per_block = kBlock / p->group;
+    p->blocks = ceil_div(segs, groups_per_block);
+    if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
+    p->passes = P > 1 ? 2 : 1;
+    p->workspace_bytes = P > 1 ? segs * int64_t(sizeof(float)) : 0;
+    return RD_OK;
+}
+
+// Rows per slab for S slabs, and S again so that no slab is empty.
+void split_rows(int64_t R, int64_t S, rd_plan* p) {
+    if (S < 1) S = 1;
+    if (S > R) S = R;
+    const int64_t rps = ceil_div(R, S);
+    p->rows_per_split = rps;
+    p->split = ceil_div(R, rps);
+}
+
+rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, const rd_tune* t,
+                    rd_plan* p) {
+    const int64_t target_waves = int64_t(cu) * kWavesPerCu;
+    if (inner < 4) {
+        // one lane per output; only the split along R adds parallelism
+        p->path = RD_PATH_COLS_NARROW;
+        p->block_threads = kBlock;
+        const int64_t lanes = outer * inner;
+        int64_t S = 1;
+        if (t && t->split) {
+            S = t->split;
+        } else if (lanes < target_waves * kWave) {
+            S = ceil_div(target_waves * kWave, lanes);
+            int64_t cap = R / 16;
+            if (cap < 1) cap = 1;
+            if (S > cap) S = cap;
+        }
+        if (S < 1) return RD_ERR_INVALID_ARG;
+        split_rows(R, S, p);
+        if (p->split > INT64_MAX / 4 / lanes) return RD_ERR_INVALID_ARG;
+        p->blocks = ceil_div(p->split * lanes, kBlock);
+        if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
+        p->passes = p->split > 1 ? 2 : 1;
+        p->workspace_bytes = p->split > 1 ? p->split * lanes * int64_t(sizeof(float)) : 0;
+        return RD_OK;
+    }
+    p->path = RD_PATH_COLS;
+    p->col_waves = (t && t->col_waves) ? t->col_waves : 1;
+    p->row_waves = (t && t->row_waves) ? t->row_waves : 4;
+    p->unroll = (t && t->unroll) ? t->unroll : 8;
+    if (!cols_shape_supported(p->col_waves, p->row_waves, p->unroll))
+        return RD_ERR_INVALID_ARG;
+    p->block_threads = kWave * p->col_waves * p->row_waves;
+
+    const int64_t lane_cols = ceil_div(inner, 4);
+    const int64_t tiles = ceil_div(lane_cols, int64_t(kWave) * p->col_waves);
+    const int64_t base = tiles * outer;  // workgroups without a split
+    const int64_t target_blocks = target_waves / (p->col_waves * p->row_waves);
+    int64_t S = 1;
+    if (t && t->split) {
+        S = t->split;
+    } else if (base < target_blocks) {
+        S = ceil_div(target_blocks, base);
+        // every wave keeps at least one full unrolled step of rows per slab
+        int64_t cap = R / (int64_t(p->row_waves) * p->unroll);
+        if (cap < 1) cap = 1;
+        if (S > cap) S = cap;
+    }
+    if (S < 1) return RD_ERR_INVALID_ARG;
+    split_rows(R, S, p);
+    if (p->split > INT64_MAX / 4 / (outer * inner)) return RD_ERR_INVALID_ARG;
+    p->blocks = base * p->split;
+    if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
+    p->passes = p->split > 1 ? 2 : 1;
+    p->workspace_bytes =
+        p->split > 1 ? p->split * outer * inner * int64_t(sizeof(float)) : 0;
+    return RD_OK;
+}
+
+}  // namespace
+
+rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                   const rd_tune* tune, rd_plan* plan) {
+    if (!plan || cu_count < 1 || outer < 0 || R < 0 || inner < 0)
+        return RD_ERR_INVALID_ARG;
+    memset(plan, 0, sizeof(*plan));
+    // outer * R * inner * 4 must be representable
+    const int64_t lim = INT64_MAX / 4;
+    if (outer && R && inner) {
+        if (R > lim / outer || inner > lim / (outer * R)) return RD_ERR_INVALID_ARG;
+    } else if (outer && inner && inner > lim / outer) {
+        return RD_ERR_INVALID_ARG;
+    }
+    plan->nxcd = nxcd_for(cu_count);
+    plan->split = 1;
+    plan->passes = 1;
+    if (outer == 0 || inner == 0) {
+        plan->path = RD_PATH_NONE;
+        plan->passes = 0;
+        return RD_OK;
+    }
+    if (R == 0) {
+        plan->path = RD_PATH_ZERO;
+        plan->block_threads = kBlock;
+        plan->blocks = (outer * inner + kBlock - 1) / kBlock;
+        if (plan->blocks > kMaxBlocks) plan->blocks = kMaxBlocks;
+        return RD_OK;
+    }
+    if (inner == 1) return plan_rows(cu_count, outer, R, tune, plan);
+    return plan_cols(cu_count, outer, R, inner, tune, plan);
+}
+
+}  // namespace rd

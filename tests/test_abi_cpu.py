@@ -1,0 +1,125 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/rd.h declares, and rejects bad arguments before any HIP call (so these
+run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sum_reduction_amd as rd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rd.h")
+
+OK, INVALID, NO_DEVICE = 0, 1, 2
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("rd_sum_1d", "rd_sum_dim", "rd_status_string", "rd_last_hip_error",
+                 "rd_version", "rd_plan_dim", "rd_plan_1d", "rd_tune_set",
+                 "rd_tune_supported"):
+        assert want in names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(rd.library_path())
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    assert rd.rd_version() == 100
+    names = [rd.rd_status_string(s) for s in range(6)]
+    assert names == ["RD_OK", "RD_ERR_INVALID_ARG", "RD_ERR_NO_DEVICE", "RD_ERR_ALLOC",
+                     "RD_ERR_LAUNCH", "RD_ERR_HIP"]
+    assert rd.rd_status_string(99) == "RD_ERR_UNKNOWN"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rd.load()
+
+
+@pytest.fixture(scope="module")
+def host_buf():
+    # host memory stands in for device pointers: validation never dereferences
+    buf = (ctypes.c_float * 64)()
+    return ctypes.addressof(buf), buf
+
+
+def test_1d_invalid_arguments(lib, host_buf):
+    base, _ = host_buf
+    out = base + 4 * 32
+    cases = [
+        (base, -1, out),            # negative n
+        (base, 2 ** 62, out),       # n * 4 overflows int64
+        (base, 4, None),            # null out
+        (None, 4, out),             # null x with n > 0
+        (base + 2, 4, out),         # x not 4-B aligned
+        (base, 4, out + 1),         # out not 4-B aligned
+        (base, 4, base + 8),        # out inside x
+        (base, 4, base),            # out at x
+    ]
+    for x, n, o in cases:
+        assert lib.rd_sum_1d(x, n, o, None) == INVALID, (x, n, o)
+
+
+def test_dim_invalid_arguments(lib, host_buf):
+    base, _ = host_buf
+    out = base + 4 * 40
+    cases = [
+        (base, -1, 2, 2, out), (base, 2, -1, 2, out), (base, 2, 2, -1, out),
+        (base, 2 ** 40, 2 ** 40, 2, out),  # size overflow
+        (base, 2, 2, 2, None),             # null out, outputs exist
+        (None, 2, 2, 2, out),              # null x, inputs exist
+        (base + 1, 2, 2, 2, out),          # misaligned x
+        (base, 2, 2, 2, out + 2),          # misaligned out
+        (base, 2, 3, 4, base + 4 * 20),    # out overlaps x (x holds 24 floats)
+    ]
+    for x, o_, R, i, out_ in cases:
+        assert lib.rd_sum_dim(x, o_, R, i, out_, None) == INVALID, (o_, R, i)
+
+
+def test_empty_output_needs_nothing(lib):
+    # outer * inner == 0: nothing to write, RD_OK without a device, null ok
+    assert lib.rd_sum_dim(None, 0, 5, 3, None, None) == OK
+    assert lib.rd_sum_dim(None, 4, 5, 0, None, None) == OK
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="a GPU is visible")
+def test_no_device_is_reported(lib, host_buf):
+    base, _ = host_buf
+    assert lib.rd_sum_1d(base, 8, base + 4 * 32, None) == NO_DEVICE
+    assert lib.rd_sum_dim(base, 2, 2, 2, base + 4 * 32, None) == NO_DEVICE
+    assert lib.rd_sum_1d(None, 0, base + 4 * 32, None) == NO_DEVICE
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        rd.rd_sum_1d(torch.ones(4))
+    with pytest.raises(ValueError):
+        rd.rd_sum_dim(torch.ones(4), 1, 4, 1)
+
+
+def test_wrapper_raises_with_status():
+    with pytest.raises(rd.RdError) as e:
+        rd.rd_plan_dim(0, 1, 1, 1)
+    assert e.value.status == INVALID

@@ -1,0 +1,239 @@
+"""GPU parity on small and ragged shapes, through the C ABI, against the oracle.
+
+Integer-valued inputs (ints in [-8, 8]) make every partial sum exact in fp32
+whatever the order, so the GPU result must equal the oracle's bit for bit: a
+dropped, repeated or misplaced element changes a sum by at least 1.  Shapes
+span several tiles and ragged tails; every case also runs with the input
+starting 0..3 floats past an aligned address, and every output slot is
+followed by guard words that must survive.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sum_reduction_amd as rd
+import workloads
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _clear_tuning():
+    rd.rd_tune_set(None)
+    yield
+    rd.rd_tune_set(None)
+
+
+def _sweep_1d(ns, offsets, seed, tag):
+    data = workloads.small_ints(max(ns) + max(offsets) + 1, seed)
+    dev = H.upload(data)
+    cases = [(n, off) for n in ns for off in offsets]
+    slots = H.OutSlots([1] * len(cases))
+    H.say("%s: %d calls of rd_sum_1d, n in [%d, %d]" % (tag, len(cases), min(ns), max(ns)))
+    for k, (n, off) in enumerate(cases):
+        st = H.call_1d(dev[off:off + n], slots.ptr(k))
+        assert st == 0, (n, off, rd.rd_status_string(st))
+    outs = slots.fetch()
+    for k, (n, off) in enumerate(cases):
+        S, _ = oracle.sum_1d(data[off:off + n])
+        H.assert_bitwise_equal_oracle(outs[k], [S], "%s n=%d off=%d" % (tag, n, off))
+
+
+def _sweep_dim(shapes, offsets, seed, tag):
+    maxn = max(o * r * i for o, r, i in shapes)
+    data = workloads.small_ints(maxn + max(offsets) + 1, seed)
+    dev = H.upload(data)
+    cases = [(s, off) for s in shapes for off in offsets]
+    slots = H.OutSlots([o * i for (o, r, i), _ in cases])
+    H.say("%s: %d calls of rd_sum_dim" % (tag, len(cases)))
+    for k, ((o, r, i), off) in enumerate(cases):
+        st = H.call_dim(dev[off:off + o * r * i], o, r, i, slots.ptr(k))
+        assert st == 0, ((o, r, i), off, rd.rd_status_string(st))
+    outs = slots.fetch()
+    for k, ((o, r, i), off) in enumerate(cases):
+        S, _ = oracle.sum_dim(data[off:off + o * r * i], o, r, i, threads=1)
+        H.assert_bitwise_equal_oracle(outs[k], S, "%s shape=%s off=%d" % (tag, (o, r, i), off))
+
+
+def test_1d_every_n_up_to_4096():
+    _sweep_1d(list(range(0, 4097)), [0, 1, 2, 3], 101, "1d n<=4096")
+
+
+def test_1d_ragged_large():
+    ns = [4097, 8191, 65536 + 3, 262144 + 1, 1_000_003, 2_000_001]
+    _sweep_1d(ns, [0, 1, 2, 3], 102, "1d ragged")
+
+
+def test_dim_every_small_shape():
+    shapes = [(o, r, i) for o in range(7) for r in range(7) for i in range(7)]
+    _sweep_dim(shapes, [0, 1, 2, 3], 103, "dim [0..6]^3")
+
+
+def test_dim_wide_inner():
+    shapes = [(o, r, i) for i in (63, 64, 65, 127, 128, 129, 255, 256, 257, 1023, 1025, 4095)
+              for (o, r) in ((1, 1), (2, 5), (3, 17), (1, 64))]
+    _sweep_dim(shapes, [0, 1, 2, 3], 104, "dim wide inner")
+
+
+def test_dim_rows_paths():
+    """inner == 1: short rows (lane per row), wave per row, workgroup per row,
+    and rows split into pieces when there are few of them."""
+    shapes = [(1000, 3, 1), (257, 63, 1), (300, 64, 1), (65, 1000, 1), (33, 4095, 1),
+              (9, 4096, 1), (5, 12289, 1), (3, 100_003, 1), (1, 300_001, 1), (2, 65, 1)]
+    _sweep_dim(shapes, [0, 1, 2, 3], 105, "dim rows")
+
+
+def test_dim_problem47_family():
+    """The [128, 4096, 4095] dim-1 shape family at reduced outer and R:
+    misaligned rows (4095 floats = 16380 B, 12 B past a 16-B boundary) and a
+    3-column tail lane, then a split along R when the grid is too small."""
+    shapes = [(2, 4096, 4095), (1, 333, 4095), (3, 64, 4095), (2, 100, 4099)]
+    _sweep_dim(shapes, [0, 1, 3], 106, "dim problem-47 family")
+
+
+ROW_TUNES = [(g, u, p) for g in (64, 256) for u in (4, 8, 16) for p in (1, 2, 5)]
+
+
+@pytest.mark.parametrize("group,unroll,split", ROW_TUNES,
+                         ids=["g%d_u%d_p%d" % t for t in ROW_TUNES])
+def test_rows_kernel_shapes(group, unroll, split):
+    """Every instantiated rows-kernel shape, forced splits included."""
+    if not rd.rd_tune_supported("rows", group, 0, unroll):
+        pytest.skip("shape not built")
+    with rd.tuning(group=group, unroll=unroll, split=split):
+        _sweep_1d([0, 1, 3, 4, 5, 63, 64, 65, 1000, 4097, 65539, 300_007], [0, 1, 2, 3],
+                  200 + group + unroll + split, "rows g%d u%d p%d" % (group, unroll, split))
+        _sweep_dim([(3, 1001, 1), (2, 5, 1), (7, 4099, 1)], [0, 3],
+                   300 + group + unroll + split, "rows dim g%d u%d p%d" % (group, unroll, split))
+
+
+COL_TUNES = [(cw, rw, u, s) for (cw, rw) in ((1, 1), (1, 2), (1, 4), (1, 8), (1, 16), (2, 1),
+                                             (2, 2), (2, 4), (2, 8), (4, 1), (4, 2), (4, 4))
+             for u in (4, 8, 16) for s in (1, 3)]
+
+
+@pytest.mark.parametrize("cw,rw,unroll,split", COL_TUNES,
+                         ids=["cw%d_rw%d_u%d_s%d" % t for t in COL_TUNES])
+def test_cols_kernel_shapes(cw, rw, unroll, split):
+    """Every instantiated column-kernel shape, with and without a split of R."""
+    if not rd.rd_tune_supported("cols", cw, rw, unroll):
+        pytest.skip("shape not built")
+    shapes = [(1, 1, 4), (2, 5, 4), (3, 17, 5), (2, 33, 63), (1, 64, 64), (2, 7, 65),
+              (1, 100, 255), (2, 9, 256), (1, 13, 257), (1, 3, 1023), (2, 37, 4095),
+              (1, 19, 4 * 1024 + 3)]
+    with rd.tuning(col_waves=cw, row_waves=rw, unroll=unroll, split=split):
+        _sweep_dim(shapes, [0, 1, 2, 3], 400 + cw * 100 + rw * 10 + unroll + split,
+                   "cols cw%d rw%d u%d s%d" % (cw, rw, unroll, split))
+
+
+def test_cols_narrow_splits():
+    """inner in {2, 3}: one lane per output, with forced splits of R."""
+    shapes = [(5, 37, 2), (3, 1000, 3), (1, 4097, 2), (64, 9, 3)]
+    for split in (1, 2, 7):
+        with rd.tuning(split=split):
+            _sweep_dim(shapes, [0, 1], 500 + split, "cols narrow s%d" % split)
+
+
+def test_degenerate_shapes():
+    """n == 0 writes +0.0; R == 0 writes zeros; outer*inner == 0 writes nothing."""
+    t = H.torch()
+    out = t.full((3,), float("nan"), device="cuda")
+    x = H.upload(np.zeros(0, np.float32))
+    assert H.call_1d(x, out.data_ptr()) == 0
+    assert H.call_dim(x, 1, 0, 2, out.data_ptr() + 4) == 0
+    t.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert got[0] == 0.0 and not np.signbit(got[0])
+    assert got[1] == 0.0 and got[2] == 0.0 and not np.signbit(got[1:3]).any()
+    slots = H.OutSlots([0, 0])
+    assert H.call_dim(x, 0, 5, 3, slots.ptr(0)) == 0
+    assert H.call_dim(x, 4, 5, 0, slots.ptr(1)) == 0
+    slots.fetch()  # guards intact
+
+
+def test_special_values():
+    """NaN and Inf propagate to exactly the outputs that contain them; an
+    all -0.0 input sums to +0.0."""
+    t = H.torch()
+    x = np.ones(1_000_003, np.float32)
+    cases = []
+    a = x.copy(); a[777_777] = np.nan; cases.append(a)
+    a = x.copy(); a[5] = np.inf; cases.append(a)
+    a = x.copy(); a[5] = np.inf; a[999_999] = -np.inf; cases.append(a)
+    cases.append(np.full(100_000, -0.0, np.float32))
+    for k, a in enumerate(cases):
+        got = rd.rd_sum_1d(H.upload(a)).cpu().numpy()[0]
+        S, _ = oracle.sum_1d(a)
+        if np.isnan(S):
+            assert np.isnan(got), k
+        else:
+            assert got == S and np.signbit(got) == np.signbit(S), (k, got, S)
+    outer, R, inner = 3, 999, 70
+    a = np.ones(outer * R * inner, np.float32).reshape(outer, R, inner)
+    a[1, 500, 69] = np.nan
+    a[2, 0, 3] = -np.inf
+    got = rd.rd_sum_dim(H.upload(a), outer, R, inner).cpu().numpy()
+    assert np.isnan(got[1, 69]) and got[2, 3] == -np.inf
+    mask = np.ones_like(got, bool); mask[1, 69] = False; mask[2, 3] = False
+    assert (got[mask] == R).all()
+
+
+def test_constant_ones_exact():
+    """All-ones inputs sum to exactly n (n <= 2^24): every partial is an integer."""
+    t = H.torch()
+    for n in (1, 4095, 1_000_000, 1 << 24):
+        got = rd.rd_sum_1d(t.ones(n, device="cuda")).item()
+        assert got == float(n), (n, got)
+    got = rd.rd_sum_dim(t.ones(3 * 4096 * 4095, device="cuda"), 3, 4096, 4095)
+    assert bool((got == 4096.0).all())
+    got = rd.rd_sum_dim(t.ones(7 * 32768, device="cuda"), 7, 32768, 1)
+    assert bool((got == 32768.0).all())
+
+
+def test_address_independence_random():
+    """Random data placed 0..3 floats past an aligned address gives the same
+    bits: an element's place in the summation does not depend on the address."""
+    a = workloads.random(3_000_001, 77, "normal")
+    ref = None
+    for off in range(4):
+        got = rd.rd_sum_1d(H.upload(a, off)).cpu().numpy()
+        ref = got if ref is None else ref
+        assert got.view(np.uint32)[0] == ref.view(np.uint32)[0], off
+    outer, R, inner = 4, 1000, 4095
+    b = workloads.random(outer * R * inner, 78, "uniform")
+    ref = None
+    for off in range(4):
+        got = rd.rd_sum_dim(H.upload(b, off), outer, R, inner).cpu().numpy()
+        ref = got if ref is None else ref
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), off
+
+
+def test_failure_injection_leaves_out_untouched(monkeypatch):
+    """Forced allocation and launch failures return their status codes and
+    enqueue nothing."""
+    t = H.torch()
+    x = H.upload(np.ones(1_000_000, np.float32))
+    slots = H.OutSlots([1, 1])
+    monkeypatch.setenv("RD_TEST_FAIL_ALLOC", "1")
+    assert rd.rd_plan_1d(256, 1_000_000).workspace_bytes > 0
+    assert H.call_1d(x, slots.ptr(0)) == 3  # RD_ERR_ALLOC
+    monkeypatch.delenv("RD_TEST_FAIL_ALLOC")
+    monkeypatch.setenv("RD_TEST_FAIL_LAUNCH", "1")
+    assert H.call_1d(x, slots.ptr(1)) == 4  # RD_ERR_LAUNCH
+    monkeypatch.delenv("RD_TEST_FAIL_LAUNCH")
+    outs = slots.fetch()
+    assert all(o.view(np.uint32)[0] == H.GUARD_BITS for o in outs)
+    # and the library still works afterwards
+    assert rd.rd_sum_1d(x).item() == 1_000_000.0
+
+
+def test_torch_style_wrapper():
+    t = H.torch()
+    a = workloads.small_ints(6 * 7 * 8 * 9, 9).reshape(6, 7, 8, 9)
+    x = H.upload(a).view(6, 7, 8, 9)
+    for dim in range(4):
+        got = rd.sum(x, dim).cpu().numpy()
+        want = a.astype(np.int64).sum(axis=dim).astype(np.float32)
+        assert np.array_equal(got, want), dim
+    assert rd.sum(x).item() == float(a.astype(np.int64).sum())

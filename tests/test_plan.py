@@ -1,0 +1,135 @@
+"""The launch planner (host logic only; no GPU needed)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import sum_reduction_amd as rd
+import workloads
+
+CU = 256  # MI355X
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+MAX_BLOCKS = 1 << 20
+
+
+@pytest.fixture(autouse=True)
+def _clear_tuning():
+    rd.rd_tune_set(None)
+    yield
+    rd.rd_tune_set(None)
+
+
+def check_invariants(p, outer, R, inner):
+    d = p.as_dict()
+    assert 1 <= p.blocks <= MAX_BLOCKS or d["path"] == "none", d
+    if d["path"] in ("rows", "rows_short"):
+        assert inner == 1
+        if d["path"] == "rows":
+            assert p.group in (64, 256) and p.split >= 1
+            assert p.workspace_bytes == (4 * outer * p.split if p.split > 1 else 0)
+            groups = outer * p.split
+            assert p.blocks == min(-(-groups // (256 // p.group)), MAX_BLOCKS)
+        assert p.passes == (2 if p.split > 1 else 1)
+    if d["path"] in ("cols", "cols_narrow"):
+        # the slabs tile [0, R) with none empty
+        assert p.split * p.rows_per_split >= R
+        assert (p.split - 1) * p.rows_per_split < R
+        assert p.workspace_bytes == (4 * p.split * outer * inner if p.split > 1 else 0)
+        assert p.passes == (2 if p.split > 1 else 1)
+        if d["path"] == "cols":
+            assert inner >= 4
+            assert p.block_threads == 64 * p.col_waves * p.row_waves <= 1024
+    if d["path"] == "cols_narrow":
+        assert inner in (2, 3)
+
+
+def test_workload_plans():
+    plans = {}
+    for name, w in workloads.WORKLOADS.items():
+        p = (rd.rd_plan_1d(CU, w.numel) if w.full_reduce
+             else rd.rd_plan_dim(CU, w.outer, w.R, w.inner))
+        check_invariants(p, w.outer, w.R, w.inner)
+        plans[name] = p.as_dict()
+    # the 1D reduce of 1e9: a grid of 8 workgroups per CU, one partial each
+    assert plans["normal_1e9"]["path"] == "rows"
+    assert plans["normal_1e9"]["blocks"] == 8 * CU
+    assert plans["normal_1e9"]["passes"] == 2
+    # the [128, 4096, 4095] reduce fills the chip without a split along R
+    assert plans["cols_128x4096x4095"]["path"] == "cols"
+    assert plans["cols_128x4096x4095"]["split"] == 1
+    assert plans["cols_128x4096x4095"]["workspace_bytes"] == 0
+    # the row sum: one workgroup per row, written directly
+    assert plans["rows_32768x32768"]["path"] == "rows"
+    assert plans["rows_32768x32768"]["group"] == 256
+    assert plans["rows_32768x32768"]["split"] == 1
+    assert plans["rows_32768x32768"]["blocks"] == 32768
+
+
+def test_problem47_lane_columns():
+    """The trace's count: 4095 = 1023 * 4 + 3, so 1024 lane-columns per row,
+    the last holding 3 columns; 128 * 4095 = 524160 outputs."""
+    with open(os.path.join(GOLDEN, "problem47_shape_facts.json")) as f:
+        facts = json.load(f)
+    outer, R, inner = facts["shape"]
+    lane_cols = -(-inner // 4)
+    assert lane_cols == 1024 and inner - 4 * (lane_cols - 1) == 3
+    assert outer * inner == facts["outputs"]
+    p = rd.rd_plan_dim(CU, outer, R, inner)
+    tiles = -(-lane_cols // (64 * p.col_waves))
+    assert p.blocks == tiles * outer * p.split
+
+
+def test_degenerate_plans():
+    assert rd.rd_plan_dim(CU, 0, 5, 5).as_dict()["path"] == "none"
+    assert rd.rd_plan_dim(CU, 5, 5, 0).as_dict()["path"] == "none"
+    assert rd.rd_plan_dim(CU, 5, 0, 5).as_dict()["path"] == "zero"
+    assert rd.rd_plan_1d(CU, 0).as_dict()["path"] == "zero"
+    assert rd.rd_plan_1d(CU, 63).as_dict()["path"] == "rows_short"
+    assert rd.rd_plan_1d(CU, 64).as_dict()["path"] == "rows"
+    assert rd.rd_plan_dim(CU, 3, 9, 2).as_dict()["path"] == "cols_narrow"
+    assert rd.rd_plan_dim(CU, 3, 9, 4).as_dict()["path"] == "cols"
+
+
+def test_random_shapes_keep_invariants():
+    rng = np.random.default_rng(0)
+    for _ in range(3000):
+        outer, R, inner = (int(v) for v in np.exp(rng.uniform(0, 14, 3)).astype(np.int64))
+        if outer * R * inner > 2 ** 40:
+            continue
+        for cu in (1, 32, 80, 256, 304):
+            p = rd.rd_plan_dim(cu, outer, R, inner)
+            check_invariants(p, outer, R, inner)
+
+
+def test_small_problems_still_spread():
+    """A small outer*inner is split along R so that the grid fills the chip."""
+    p = rd.rd_plan_dim(CU, 1, 1 << 20, 64)
+    assert p.split > 1 and p.blocks >= CU
+    p = rd.rd_plan_dim(CU, 4, 1 << 24, 1)
+    assert p.split > 1 and p.blocks >= CU
+
+
+def test_plan_depends_only_on_cu_count_and_shape():
+    a = rd.rd_plan_dim(CU, 7, 100_000, 33).as_dict()
+    b = rd.rd_plan_dim(CU, 7, 100_000, 33).as_dict()
+    assert a == b
+
+
+def test_tuning_override():
+    with rd.tuning(group=64, unroll=4, split=3):
+        p = rd.rd_plan_1d(CU, 1000)
+        assert (p.group, p.unroll, p.split) == (64, 4, 3)
+    with rd.tuning(col_waves=2, row_waves=2, unroll=16, split=5):
+        p = rd.rd_plan_dim(CU, 3, 100, 1000)
+        assert (p.col_waves, p.row_waves, p.unroll, p.split) == (2, 2, 16, 5)
+    with rd.tuning(col_waves=3, row_waves=3):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 3, 100, 1000)
+    with rd.tuning(group=128):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_1d(CU, 10000)
+    assert rd.rd_tune_supported("rows", 256, 0, 8)
+    assert not rd.rd_tune_supported("rows", 256, 0, 6)
+    assert rd.rd_tune_supported("cols", 1, 4, 8)
+    assert not rd.rd_tune_supported("cols", 8, 4, 8)
