@@ -121,6 +121,12 @@ typedef enum rd_path {
     RD_PATH_COLS_NARROW = 5  /* inner in {2, 3}: one lane per output */
 } rd_path;
 
+/* Chunk order of the pieces of one row on the ROWS path. */
+typedef enum rd_order {
+    RD_ORDER_INTERLEAVED = 1, /* lane g of P*G takes chunks g, g + P*G, ... */
+    RD_ORDER_BLOCKED = 2      /* piece p owns one contiguous run of chunks */
+} rd_order;
+
 typedef struct rd_plan {
     int32_t path;            /* rd_path */
     int32_t block_threads;   /* threads per workgroup of the main pass */
@@ -130,6 +136,8 @@ typedef struct rd_plan {
     int32_t unroll;          /* 16-byte loads in flight per lane */
     int32_t nxcd;            /* XCDs the workgroup numbering is spread over */
     int32_t passes;          /* 1, or 2 when partials need a combine pass */
+    int32_t order;           /* ROWS: rd_order; 0 elsewhere */
+    int32_t nontemporal;     /* 1: main-pass loads carry the streaming hint */
     int64_t split;           /* ROWS: pieces per row; COLS*: slabs of R */
     int64_t rows_per_split;  /* COLS*: rows per slab */
     int64_t blocks;          /* workgroups of the main pass */
@@ -155,7 +163,9 @@ typedef struct rd_tune {
     int32_t group;           /* ROWS: 64 or 256 */
     int32_t col_waves;       /* COLS */
     int32_t row_waves;       /* COLS */
-    int32_t unroll;          /* ROWS, COLS */
+    int32_t unroll;          /* ROWS, COLS: 2, 4, 8 or 16 */
+    int32_t order;           /* ROWS: rd_order */
+    int32_t nontemporal;     /* ROWS, COLS: 1 = off, 2 = on */
     int64_t split;           /* ROWS: pieces per row; COLS*: slabs of R */
 } rd_tune;
 

@@ -33,6 +33,7 @@ LIBRARY = os.path.join(_HERE, "librd.so")
 RD_OK = 0
 PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
               5: "cols_narrow"}
+ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
 
 
 class RdError(RuntimeError):
@@ -50,18 +51,21 @@ class RdPlan(ctypes.Structure):
                 ("group", ctypes.c_int32), ("col_waves", ctypes.c_int32),
                 ("row_waves", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("nxcd", ctypes.c_int32), ("passes", ctypes.c_int32),
+                ("order", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
                 ("split", ctypes.c_int64), ("rows_per_split", ctypes.c_int64),
                 ("blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}
         d["path"] = PATH_NAMES.get(self.path, self.path)
+        d["order"] = ORDER_NAMES.get(self.order, self.order)
         return d
 
 
 class RdTune(ctypes.Structure):
     _fields_ = [("group", ctypes.c_int32), ("col_waves", ctypes.c_int32),
                 ("row_waves", ctypes.c_int32), ("unroll", ctypes.c_int32),
+                ("order", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
                 ("split", ctypes.c_int64)]
 
 

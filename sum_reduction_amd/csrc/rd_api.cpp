@@ -222,7 +222,7 @@ rd_status rd_tune_set(const rd_tune* tune) {
         return RD_OK;
     }
     if (tune->group < 0 || tune->col_waves < 0 || tune->row_waves < 0 || tune->unroll < 0 ||
-        tune->split < 0)
+        tune->order < 0 || tune->nontemporal < 0 || tune->split < 0)
         return RD_ERR_INVALID_ARG;
     g_tune = *tune;
     g_tune_on = true;

@@ -25,9 +25,9 @@
 // keeps the result independent of the input's address.
 //
 // Summation order (fixed for a given plan; every add is IEEE fp32):
-//  ROWS      lane g of a row (g = piece * G + lane) adds its k-th 16-byte
-//            chunk, chunk g + k*L (L = pieces * G), into float4 accumulator
-//            (k mod 2); the R % 4 tail elements go to acc[0].x of lanes 0..2;
+//  ROWS      a lane adds its k-th 16-byte chunk (interleaved or blocked
+//            order, see rows_kernel) into float4 accumulator (k mod 2); the
+//            R % 4 tail elements go to acc[0].x of the row's lanes 0..2;
 //            a = acc[0] + acc[1], lane total = (a.x + a.y) + (a.z + a.w); then
 //            the wave butterfly, then the wave sums in wave order; then (if
 //            the row has several pieces) the piece sums in piece order.
@@ -49,11 +49,19 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Four floats from a 4-byte-aligned address: one global_load_dwordx4.
+typedef float v4f_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// Four floats from a 4-byte-aligned address: one global_load_dwordx4, with
+// the nontemporal (streaming) hint when NT.
+template <bool NT>
 __device__ __forceinline__ v4f load4(const float* p) {
-    v4f v;
-    __builtin_memcpy(&v, p, sizeof(v));
-    return v;
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(reinterpret_cast<const v4f_a4*>(p));
+    } else {
+        v4f v;
+        __builtin_memcpy(&v, p, sizeof(v));
+        return v;
+    }
 }
 
 template <int kCtrl>
@@ -116,10 +124,16 @@ __device__ __forceinline__ int64_t xcd_block(uint32_t nxcd) {
 // P == 1, dst is the output (one value per row); otherwise dst holds the
 // outer x P piece sums for rows_combine_kernel.  The full 1D reduce is the
 // case outer == 1.
-template <int G, int U>
+// Chunk order of the pieces of a row (16-byte chunks, nvec = R / 4 of them):
+//   interleaved  lane g = p * G + lane takes chunks g, g + P*G, g + 2*P*G, ...
+//   blocked      piece p owns the contiguous chunks [p*C, (p+1)*C) with
+//                C = ceil(nvec / P) rounded up to a multiple of G, and its
+//                lane takes p*C + lane, p*C + lane + G, ... (each group streams
+//                one contiguous stretch of memory)
+template <int G, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ x,
                                                       int64_t R, int64_t nseg,
-                                                      int64_t P,
+                                                      int64_t P, int32_t blocked,
                                                       float* __restrict__ dst,
                                                       uint32_t nxcd) {
     static_assert(G == kWave || G == kBlock, "group is a wave or a workgroup");
@@ -128,27 +142,31 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
     const int gl = threadIdx.x % G;
     const int64_t nvec = R >> 2;
     const int64_t tail = R & 3;
-    const int64_t L = P * G;
-    const int64_t stride = int64_t(gridDim.x) * kGroups;
-    for (int64_t first = xcd_block(nxcd) * kGroups; first < nseg; first += stride) {
+    const int64_t span = ((nvec + P - 1) / P + G - 1) / G * G;  // blocked: chunks per piece
+    const int64_t L = blocked ? int64_t(G) : P * G;            // a lane's chunk stride
+    const int64_t gstride = int64_t(gridDim.x) * kGroups;
+    for (int64_t first = xcd_block(nxcd) * kGroups; first < nseg; first += gstride) {
         const int64_t seg = first + threadIdx.x / G;  // uniform per group
         float total = 0.f;
         if (seg < nseg) {
             const int64_t o = seg / P;
-            const int64_t g = (seg - o * P) * G + gl;
+            const int64_t piece = seg - o * P;
+            const int64_t g = piece * G + gl;
             const float* row = x + o * R;
+            int64_t j = blocked ? piece * span + gl : g;
+            int64_t end = nvec;
+            if (blocked && piece * span + span < nvec) end = piece * span + span;
             v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            int64_t j = g;
-            for (; j + (U - 1) * L < nvec; j += U * L) {
+            for (; j + (U - 1) * L < end; j += U * L) {
                 v4f v[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = load4(row + 4 * (j + u * L));
+                for (int u = 0; u < U; ++u) v[u] = load4<NT>(row + 4 * (j + u * L));
 #pragma unroll
                 for (int u = 0; u < U; ++u) acc[u & 1] += v[u];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (j + u * L < nvec) acc[u & 1] += load4(row + 4 * (j + u * L));
+                if (j + u * L < end) acc[u & 1] += load4<NT>(row + 4 * (j + u * L));
             if (g < tail) acc[0].x += row[4 * nvec + g];
             const v4f a = acc[0] + acc[1];
             total = (a.x + a.y) + (a.z + a.w);
@@ -174,7 +192,7 @@ __global__ __launch_bounds__(kBlock) void rows_short_kernel(const float* __restr
         const float* row = x + o * R;
         v4f acc = {0.f, 0.f, 0.f, 0.f};
         int64_t k = 0;
-        for (; k + 4 <= R; k += 4) acc += load4(row + k);
+        for (; k + 4 <= R; k += 4) acc += load4<false>(row + k);
         float t = (acc.x + acc.y) + (acc.z + acc.w);
         for (; k < R; ++k) t += row[k];
         out[o] = t;
@@ -207,7 +225,7 @@ __global__ __launch_bounds__(kBlock) void rows_combine_kernel(const float* __res
 // the slab, U rows in flight; the RW partial sums meet in LDS.  With S == 1,
 // dst is the output; otherwise dst is [S][outer][inner] for
 // slab_combine_kernel.  Needs inner >= 4.
-template <int CW, int RW, int U>
+template <int CW, int RW, int U, bool NT>
 __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
     const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t ntiles,
     int64_t S, int64_t rps, float* __restrict__ dst, uint32_t nxcd) {
@@ -236,14 +254,14 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
             for (; k + U <= m; k += U) {
                 v4f v[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = load4(p + u * step);
+                for (int u = 0; u < U; ++u) v[u] = load4<NT>(p + u * step);
 #pragma unroll
                 for (int u = 0; u < U; ++u) acc[u & 1] += v[u];
                 p += U * step;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (k + u < m) acc[u & 1] += load4(p + u * step);
+                if (k + u < m) acc[u & 1] += load4<NT>(p + u * step);
         }
         v4f a = acc[0] + acc[1];
         if constexpr (RW > 1) {
@@ -340,27 +358,48 @@ int64_t grid_for(int64_t items) {
 
 // Instantiated kernel shapes.
 constexpr int kRowGroups[] = {64, 256};
-constexpr int kUnrolls[] = {4, 8, 16};
+constexpr int kUnrolls[] = {2, 4, 8, 16};
 struct ColShape {
     int cw, rw;
 };
 constexpr ColShape kColShapes[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {1, 16}, {2, 1},
                                    {2, 2}, {2, 4}, {2, 8}, {4, 1}, {4, 2}, {4, 4}};
 
-template <int G, int U>
+template <int G, int U, bool NT>
 hipError_t rows_dispatch_u(const rd_plan& p, const float* x, int64_t outer, int64_t R,
                            float* dst, hipStream_t s) {
-    return launch(rows_kernel<G, U>, p.blocks, kBlock, s, x, R, outer * p.split, p.split,
-                  dst, uint32_t(p.nxcd));
+    return launch(rows_kernel<G, U, NT>, p.blocks, kBlock, s, x, R, outer * p.split,
+                  p.split, int32_t(p.order == RD_ORDER_BLOCKED), dst, uint32_t(p.nxcd));
 }
 
-template <int G>
+template <int G, bool NT>
 hipError_t rows_dispatch(const rd_plan& p, const float* x, int64_t outer, int64_t R,
                          float* dst, hipStream_t s) {
     switch (p.unroll) {
-        case 4: return rows_dispatch_u<G, 4>(p, x, outer, R, dst, s);
-        case 8: return rows_dispatch_u<G, 8>(p, x, outer, R, dst, s);
-        case 16: return rows_dispatch_u<G, 16>(p, x, outer, R, dst, s);
+        case 2: return rows_dispatch_u<G, 2, NT>(p, x, outer, R, dst, s);
+        case 4: return rows_dispatch_u<G, 4, NT>(p, x, outer, R, dst, s);
+        case 8: return rows_dispatch_u<G, 8, NT>(p, x, outer, R, dst, s);
+        case 16: return rows_dispatch_u<G, 16, NT>(p, x, outer, R, dst, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int CW, int RW, int U, bool NT>
+hipError_t cols_dispatch_u(const rd_plan& p, const float* x, int64_t outer, int64_t R,
+                           int64_t inner, float* dst, hipStream_t s) {
+    const int64_t ntiles = ((inner + 3) / 4 + CW * kWave - 1) / (CW * kWave);
+    return launch(cols_kernel<CW, RW, U, NT>, p.blocks, kWave * CW * RW, s, x, outer, R,
+                  inner, ntiles, p.split, p.rows_per_split, dst, uint32_t(p.nxcd));
+}
+
+template <int CW, int RW, bool NT>
+hipError_t cols_dispatch_nt(const rd_plan& p, const float* x, int64_t outer, int64_t R,
+                            int64_t inner, float* dst, hipStream_t s) {
+    switch (p.unroll) {
+        case 2: return cols_dispatch_u<CW, RW, 2, NT>(p, x, outer, R, inner, dst, s);
+        case 4: return cols_dispatch_u<CW, RW, 4, NT>(p, x, outer, R, inner, dst, s);
+        case 8: return cols_dispatch_u<CW, RW, 8, NT>(p, x, outer, R, inner, dst, s);
+        case 16: return cols_dispatch_u<CW, RW, 16, NT>(p, x, outer, R, inner, dst, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -368,20 +407,8 @@ hipError_t rows_dispatch(const rd_plan& p, const float* x, int64_t outer, int64_
 template <int CW, int RW>
 hipError_t cols_dispatch(const rd_plan& p, const float* x, int64_t outer, int64_t R,
                          int64_t inner, float* dst, hipStream_t s) {
-    const int64_t ntiles = ((inner + 3) / 4 + CW * kWave - 1) / (CW * kWave);
-    const int threads = kWave * CW * RW;
-    switch (p.unroll) {
-        case 4:
-            return launch(cols_kernel<CW, RW, 4>, p.blocks, threads, s, x, outer, R, inner,
-                          ntiles, p.split, p.rows_per_split, dst, uint32_t(p.nxcd));
-        case 8:
-            return launch(cols_kernel<CW, RW, 8>, p.blocks, threads, s, x, outer, R, inner,
-                          ntiles, p.split, p.rows_per_split, dst, uint32_t(p.nxcd));
-        case 16:
-            return launch(cols_kernel<CW, RW, 16>, p.blocks, threads, s, x, outer, R, inner,
-                          ntiles, p.split, p.rows_per_split, dst, uint32_t(p.nxcd));
-        default: return hipErrorInvalidValue;
-    }
+    if (p.nontemporal) return cols_dispatch_nt<CW, RW, true>(p, x, outer, R, inner, dst, s);
+    return cols_dispatch_nt<CW, RW, false>(p, x, outer, R, inner, dst, s);
 }
 
 }  // namespace
@@ -406,8 +433,12 @@ hipError_t launch_fill_zero(float* out, int64_t n, hipStream_t s) {
 
 hipError_t launch_rows(const rd_plan& p, const float* x, int64_t outer, int64_t R,
                        float* dst, hipStream_t s) {
-    if (p.group == kBlock) return rows_dispatch<kBlock>(p, x, outer, R, dst, s);
-    if (p.group == kWave) return rows_dispatch<kWave>(p, x, outer, R, dst, s);
+    if (p.group == kBlock)
+        return p.nontemporal ? rows_dispatch<kBlock, true>(p, x, outer, R, dst, s)
+                             : rows_dispatch<kBlock, false>(p, x, outer, R, dst, s);
+    if (p.group == kWave)
+        return p.nontemporal ? rows_dispatch<kWave, true>(p, x, outer, R, dst, s)
+                             : rows_dispatch<kWave, false>(p, x, outer, R, dst, s);
     return hipErrorInvalidValue;
 }
 

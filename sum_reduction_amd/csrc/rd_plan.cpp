@@ -4,9 +4,15 @@
 // Kernels" README, key design decisions: blocks = multiProcessorCount x
 // max_blocks_per_SM) and worry that a grid of a few hundred blocks is too
 // small for the chip (POPCORNBENCH problem-47 trace, grid sizing discussion).
-// Here the grid is sized from the CU count to keep about 32 waves per CU in
-// flight (8 per SIMD), and a reduction whose natural parallelism is too small
-// is split along R, with a second, fixed-order pass over the partials.
+//
+// Measured on MI355X (256 CUs, HBM3E), a read stream runs fastest with every
+// CU busy but few waves per CU: about 8 MB of 16-byte loads in flight over
+// the chip (32 KB per CU) saturates HBM, and more concurrent streams cost
+// DRAM locality.  So the planner aims for at least one workgroup per CU and
+// about 32 * CU 16-byte loads in flight per lane-wave, splits a reduction
+// along R only when its natural parallelism is below that, and turns on the
+// streaming hint, which keeps a once-read stream from allocating in the
+// caches (it was worth 10-15% on every path).
 #include <string.h>
 
 #include "rd_internal.h"
@@ -14,9 +20,24 @@
 namespace rd {
 namespace {
 
-constexpr int64_t kWavesPerCu = 32;
+// Waves x loads-in-flight per lane to aim for, per CU (8 waves x 4 loads).
+constexpr int64_t kLoadWavesPerCu = 32;
+// Defaults measured on MI355X for the two kernels.
+constexpr int kRowsUnrollBlock = 16;  // 256-lane groups
+constexpr int kRowsUnrollWave = 8;    // 64-lane groups
+constexpr int kColsUnroll = 4;
+constexpr int kColsMaxColWaves = 4;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The streaming-hint choice: the tuning override's (1 = off, 2 = on) or the
+// default.  False for an invalid request.
+bool nontemporal_choice(const rd_tune* t, bool dflt, int32_t* out) {
+    const int32_t v = t ? t->nontemporal : 0;
+    if (v < 0 || v > 2) return false;
+    *out = v == 0 ? int32_t(dflt) : int32_t(v == 2);
+    return true;
+}
 
 int32_t nxcd_for(int cu_count) {
     // MI355X: 8 XCDs of 32 CUs.  Only used to spread the workgroup numbering,
@@ -25,7 +46,7 @@ int32_t nxcd_for(int cu_count) {
 }
 
 rd_status plan_rows(int cu, int64_t outer, int64_t R, const rd_tune* t, rd_plan* p) {
-    const bool forced = t && (t->group || t->unroll || t->split);
+    const bool forced = t && (t->group || t->unroll || t->split || t->order);
     if (R < kShortRow && !forced) {
         p->path = RD_PATH_ROWS_SHORT;
         p->block_threads = kBlock;
@@ -38,29 +59,32 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, const rd_tune* t, rd_plan*
     }
     p->path = RD_PATH_ROWS;
     p->block_threads = kBlock;
-    p->group = (t && t->group) ? t->group : (R >= 4096 ? 256 : 64);
-    p->unroll = (t && t->unroll) ? t->unroll : 8;
+    p->group = (t && t->group) ? t->group : (R >= 4096 ? kBlock : kWave);
+    p->unroll = (t && t->unroll) ? t->unroll
+                                 : (p->group == kBlock ? kRowsUnrollBlock : kRowsUnrollWave);
     if (!rows_shape_supported(p->group, p->unroll)) return RD_ERR_INVALID_ARG;
+    p->order = (t && t->order) ? t->order : RD_ORDER_BLOCKED;
+    if (p->order != RD_ORDER_INTERLEAVED && p->order != RD_ORDER_BLOCKED)
+        return RD_ERR_INVALID_ARG;
+    if (!nontemporal_choice(t, true, &p->nontemporal)) return RD_ERR_INVALID_ARG;
 
     const int64_t nvec = R / 4;
+    const int64_t groups_per_block = kBlock / p->group;
     int64_t P = 1;
     if (t && t->split) {
         P = t->split;
         if (P < 1) return RD_ERR_INVALID_ARG;
-    } else {
-        const int64_t target_lanes = int64_t(cu) * kWavesPerCu * kWave;
-        if (outer < target_lanes / p->group) {
-            P = ceil_div(target_lanes, outer * p->group);
-            // every lane gets at least one full unrolled step of loads
-            int64_t cap = nvec / (int64_t(p->group) * p->unroll);
-            if (cap < 1) cap = 1;
-            if (P > cap) P = cap;
-        }
+    } else if (outer < int64_t(cu) * groups_per_block) {
+        // fewer rows than one workgroup per CU: cut each row into pieces
+        P = ceil_div(int64_t(cu) * groups_per_block, outer);
+        // every lane gets at least one full unrolled step of loads
+        int64_t cap = nvec / (int64_t(p->group) * p->unroll);
+        if (cap < 1) cap = 1;
+        if (P > cap) P = cap;
     }
     if (P > INT64_MAX / 4 / outer) return RD_ERR_INVALID_ARG;
     p->split = P;
     const int64_t segs = outer * P;
-    const int64_t groups_per_block = kBlock / p->group;
     p->blocks = ceil_div(segs, groups_per_block);
     if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
     p->passes = P > 1 ? 2 : 1;
@@ -79,17 +103,17 @@ void split_rows(int64_t R, int64_t S, rd_plan* p) {
 
 rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, const rd_tune* t,
                     rd_plan* p) {
-    const int64_t target_waves = int64_t(cu) * kWavesPerCu;
     if (inner < 4) {
         // one lane per output; only the split along R adds parallelism
         p->path = RD_PATH_COLS_NARROW;
         p->block_threads = kBlock;
         const int64_t lanes = outer * inner;
+        const int64_t target_lanes = int64_t(cu) * kLoadWavesPerCu * kWave;
         int64_t S = 1;
         if (t && t->split) {
             S = t->split;
-        } else if (lanes < target_waves * kWave) {
-            S = ceil_div(target_waves * kWave, lanes);
+        } else if (lanes < target_lanes) {
+            S = ceil_div(target_lanes, lanes);
             int64_t cap = R / 16;
             if (cap < 1) cap = 1;
             if (S > cap) S = cap;
@@ -104,26 +128,36 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, const rd_tu
         return RD_OK;
     }
     p->path = RD_PATH_COLS;
-    p->col_waves = (t && t->col_waves) ? t->col_waves : 1;
-    p->row_waves = (t && t->row_waves) ? t->row_waves : 4;
-    p->unroll = (t && t->unroll) ? t->unroll : 8;
+    const int64_t lane_cols = ceil_div(inner, 4);
+    // as many waves side by side as the row has columns for, up to 4
+    int32_t cw = kColsMaxColWaves;
+    while (cw > 1 && lane_cols <= int64_t(cw / 2) * kWave) cw /= 2;
+    p->col_waves = (t && t->col_waves) ? t->col_waves : cw;
+    p->row_waves = (t && t->row_waves) ? t->row_waves : 1;
+    p->unroll = (t && t->unroll) ? t->unroll : kColsUnroll;
     if (!cols_shape_supported(p->col_waves, p->row_waves, p->unroll))
         return RD_ERR_INVALID_ARG;
+    if (!nontemporal_choice(t, true, &p->nontemporal)) return RD_ERR_INVALID_ARG;
     p->block_threads = kWave * p->col_waves * p->row_waves;
 
-    const int64_t lane_cols = ceil_div(inner, 4);
     const int64_t tiles = ceil_div(lane_cols, int64_t(kWave) * p->col_waves);
     const int64_t base = tiles * outer;  // workgroups without a split
-    const int64_t target_blocks = target_waves / (p->col_waves * p->row_waves);
     int64_t S = 1;
     if (t && t->split) {
         S = t->split;
-    } else if (base < target_blocks) {
-        S = ceil_div(target_blocks, base);
-        // every wave keeps at least one full unrolled step of rows per slab
-        int64_t cap = R / (int64_t(p->row_waves) * p->unroll);
-        if (cap < 1) cap = 1;
-        if (S > cap) S = cap;
+    } else {
+        // loads in flight over the chip without a split, in lane-waves x U
+        const int64_t inflight = base * p->col_waves * p->row_waves * p->unroll;
+        const int64_t want = int64_t(cu) * kLoadWavesPerCu;
+        if (inflight < want || base < cu) {
+            S = ceil_div(want, inflight);
+            const int64_t fill = ceil_div(cu, base);
+            if (S < fill) S = fill;
+            // every wave keeps at least one full unrolled step of rows per slab
+            int64_t cap = R / (int64_t(p->row_waves) * p->unroll);
+            if (cap < 1) cap = 1;
+            if (S > cap) S = cap;
+        }
     }
     if (S < 1) return RD_ERR_INVALID_ARG;
     split_rows(R, S, p);

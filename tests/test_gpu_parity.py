@@ -92,39 +92,44 @@ def test_dim_problem47_family():
     _sweep_dim(shapes, [0, 1, 3], 106, "dim problem-47 family")
 
 
-ROW_TUNES = [(g, u, p) for g in (64, 256) for u in (4, 8, 16) for p in (1, 2, 5)]
+ROW_TUNES = [(g, u, p, order, nt) for g in (64, 256) for u in (2, 4, 8, 16)
+             for p in (1, 2, 5) for order in (1, 2) for nt in (1, 2)]
 
 
-@pytest.mark.parametrize("group,unroll,split", ROW_TUNES,
-                         ids=["g%d_u%d_p%d" % t for t in ROW_TUNES])
-def test_rows_kernel_shapes(group, unroll, split):
-    """Every instantiated rows-kernel shape, forced splits included."""
+@pytest.mark.parametrize("group,unroll,split,order,nt", ROW_TUNES,
+                         ids=["g%d_u%d_p%d_o%d_nt%d" % t for t in ROW_TUNES])
+def test_rows_kernel_shapes(group, unroll, split, order, nt):
+    """Every instantiated rows-kernel shape, both chunk orders, with and
+    without the streaming hint, forced splits included."""
     if not rd.rd_tune_supported("rows", group, 0, unroll):
         pytest.skip("shape not built")
-    with rd.tuning(group=group, unroll=unroll, split=split):
+    tag = "rows g%d u%d p%d o%d nt%d" % (group, unroll, split, order, nt)
+    seed = 200 + group + unroll + split + 7 * order + 11 * nt
+    with rd.tuning(group=group, unroll=unroll, split=split, order=order, nontemporal=nt):
         _sweep_1d([0, 1, 3, 4, 5, 63, 64, 65, 1000, 4097, 65539, 300_007], [0, 1, 2, 3],
-                  200 + group + unroll + split, "rows g%d u%d p%d" % (group, unroll, split))
-        _sweep_dim([(3, 1001, 1), (2, 5, 1), (7, 4099, 1)], [0, 3],
-                   300 + group + unroll + split, "rows dim g%d u%d p%d" % (group, unroll, split))
+                  seed, tag)
+        _sweep_dim([(3, 1001, 1), (2, 5, 1), (7, 4099, 1)], [0, 3], seed + 1, tag + " dim")
 
 
-COL_TUNES = [(cw, rw, u, s) for (cw, rw) in ((1, 1), (1, 2), (1, 4), (1, 8), (1, 16), (2, 1),
-                                             (2, 2), (2, 4), (2, 8), (4, 1), (4, 2), (4, 4))
-             for u in (4, 8, 16) for s in (1, 3)]
+COL_TUNES = [(cw, rw, u, s, nt) for (cw, rw) in ((1, 1), (1, 2), (1, 4), (1, 8), (1, 16),
+                                                 (2, 1), (2, 2), (2, 4), (2, 8), (4, 1),
+                                                 (4, 2), (4, 4))
+             for u in (2, 4, 8, 16) for s in (1, 3) for nt in (1, 2)]
 
 
-@pytest.mark.parametrize("cw,rw,unroll,split", COL_TUNES,
-                         ids=["cw%d_rw%d_u%d_s%d" % t for t in COL_TUNES])
-def test_cols_kernel_shapes(cw, rw, unroll, split):
-    """Every instantiated column-kernel shape, with and without a split of R."""
+@pytest.mark.parametrize("cw,rw,unroll,split,nt", COL_TUNES,
+                         ids=["cw%d_rw%d_u%d_s%d_nt%d" % t for t in COL_TUNES])
+def test_cols_kernel_shapes(cw, rw, unroll, split, nt):
+    """Every instantiated column-kernel shape, with and without a split of R
+    and the streaming hint."""
     if not rd.rd_tune_supported("cols", cw, rw, unroll):
         pytest.skip("shape not built")
     shapes = [(1, 1, 4), (2, 5, 4), (3, 17, 5), (2, 33, 63), (1, 64, 64), (2, 7, 65),
               (1, 100, 255), (2, 9, 256), (1, 13, 257), (1, 3, 1023), (2, 37, 4095),
               (1, 19, 4 * 1024 + 3)]
-    with rd.tuning(col_waves=cw, row_waves=rw, unroll=unroll, split=split):
-        _sweep_dim(shapes, [0, 1, 2, 3], 400 + cw * 100 + rw * 10 + unroll + split,
-                   "cols cw%d rw%d u%d s%d" % (cw, rw, unroll, split))
+    with rd.tuning(col_waves=cw, row_waves=rw, unroll=unroll, split=split, nontemporal=nt):
+        _sweep_dim(shapes, [0, 1, 2, 3], 400 + cw * 100 + rw * 10 + unroll + split + nt,
+                   "cols cw%d rw%d u%d s%d nt%d" % (cw, rw, unroll, split, nt))
 
 
 def test_cols_narrow_splits():

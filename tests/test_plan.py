@@ -51,12 +51,19 @@ def test_workload_plans():
              else rd.rd_plan_dim(CU, w.outer, w.R, w.inner))
         check_invariants(p, w.outer, w.R, w.inner)
         plans[name] = p.as_dict()
-    # the 1D reduce of 1e9: a grid of 8 workgroups per CU, one partial each
+    # the 1D reduce of 1e9: one workgroup per CU, each streaming one
+    # contiguous piece, one partial each
     assert plans["normal_1e9"]["path"] == "rows"
-    assert plans["normal_1e9"]["blocks"] == 8 * CU
+    assert plans["normal_1e9"]["blocks"] == CU
+    assert plans["normal_1e9"]["order"] == "blocked"
     assert plans["normal_1e9"]["passes"] == 2
-    # the [128, 4096, 4095] reduce fills the chip without a split along R
+    assert all(p["nontemporal"] == 1 for p in plans.values())
+    # the [128, 4096, 4095] reduce fills the chip without a split along R:
+    # 4 waves side by side cover 1024 lane-columns (4096 columns), 4 tiles
+    # per outer index, 512 workgroups
     assert plans["cols_128x4096x4095"]["path"] == "cols"
+    assert plans["cols_128x4096x4095"]["col_waves"] == 4
+    assert plans["cols_128x4096x4095"]["blocks"] == 512
     assert plans["cols_128x4096x4095"]["split"] == 1
     assert plans["cols_128x4096x4095"]["workspace_bytes"] == 0
     # the row sum: one workgroup per row, written directly
