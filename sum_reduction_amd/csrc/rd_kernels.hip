@@ -363,7 +363,8 @@ struct ColShape {
     int cw, rw;
 };
 constexpr ColShape kColShapes[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {1, 16}, {2, 1},
-                                   {2, 2}, {2, 4}, {2, 8}, {4, 1}, {4, 2}, {4, 4}};
+                                   {2, 2}, {2, 4}, {2, 8}, {4, 1}, {4, 2}, {4, 4},
+                                   {8, 1}, {8, 2}, {16, 1}};
 
 template <int G, int U, bool NT>
 hipError_t rows_dispatch_u(const rd_plan& p, const float* x, int64_t outer, int64_t R,
@@ -470,6 +471,9 @@ hipError_t launch_cols(const rd_plan& p, const float* x, int64_t outer, int64_t 
     RD_COLS_CASE(4, 1)
     RD_COLS_CASE(4, 2)
     RD_COLS_CASE(4, 4)
+    RD_COLS_CASE(8, 1)
+    RD_COLS_CASE(8, 2)
+    RD_COLS_CASE(16, 1)
 #undef RD_COLS_CASE
     return hipErrorInvalidValue;
 }

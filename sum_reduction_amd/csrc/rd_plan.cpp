@@ -26,7 +26,7 @@ constexpr int64_t kLoadWavesPerCu = 32;
 constexpr int kRowsUnrollBlock = 16;  // 256-lane groups
 constexpr int kRowsUnrollWave = 8;    // 64-lane groups
 constexpr int kColsUnroll = 4;
-constexpr int kColsMaxColWaves = 4;
+constexpr int kColsMaxColWaves = 8;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -129,9 +129,15 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, const rd_tu
     }
     p->path = RD_PATH_COLS;
     const int64_t lane_cols = ceil_div(inner, 4);
-    // as many waves side by side as the row has columns for, up to 4
-    int32_t cw = kColsMaxColWaves;
-    while (cw > 1 && lane_cols <= int64_t(cw / 2) * kWave) cw /= 2;
+    // Wide tiles: every tile edge inside a row is a cache line that two
+    // workgroups fetch.  Take the widest tile the row has columns for (up to
+    // 8 waves) that still gives every CU a workgroup; if no width does,
+    // keep the widest and let the split along R fill the chip.
+    int32_t widest = kColsMaxColWaves;
+    while (widest > 1 && lane_cols <= int64_t(widest / 2) * kWave) widest /= 2;
+    int32_t cw = widest;
+    while (cw > 1 && ceil_div(lane_cols, int64_t(cw) * kWave) * outer < cu) cw /= 2;
+    if (ceil_div(lane_cols, int64_t(cw) * kWave) * outer < cu) cw = widest;
     p->col_waves = (t && t->col_waves) ? t->col_waves : cw;
     p->row_waves = (t && t->row_waves) ? t->row_waves : 1;
     p->unroll = (t && t->unroll) ? t->unroll : kColsUnroll;

@@ -113,7 +113,7 @@ def test_rows_kernel_shapes(group, unroll, split, order, nt):
 
 COL_TUNES = [(cw, rw, u, s, nt) for (cw, rw) in ((1, 1), (1, 2), (1, 4), (1, 8), (1, 16),
                                                  (2, 1), (2, 2), (2, 4), (2, 8), (4, 1),
-                                                 (4, 2), (4, 4))
+                                                 (4, 2), (4, 4), (8, 1), (8, 2), (16, 1))
              for u in (2, 4, 8, 16) for s in (1, 3) for nt in (1, 2)]
 
 

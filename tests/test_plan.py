@@ -59,11 +59,12 @@ def test_workload_plans():
     assert plans["normal_1e9"]["passes"] == 2
     assert all(p["nontemporal"] == 1 for p in plans.values())
     # the [128, 4096, 4095] reduce fills the chip without a split along R:
-    # 4 waves side by side cover 1024 lane-columns (4096 columns), 4 tiles
-    # per outer index, 512 workgroups
+    # 8 waves side by side cover 512 lane-columns (2048 columns), 2 tiles
+    # per outer index, 256 workgroups -- one per CU
     assert plans["cols_128x4096x4095"]["path"] == "cols"
-    assert plans["cols_128x4096x4095"]["col_waves"] == 4
-    assert plans["cols_128x4096x4095"]["blocks"] == 512
+    assert plans["cols_128x4096x4095"]["col_waves"] == 8
+    assert plans["cols_128x4096x4095"]["unroll"] == 4
+    assert plans["cols_128x4096x4095"]["blocks"] == 256
     assert plans["cols_128x4096x4095"]["split"] == 1
     assert plans["cols_128x4096x4095"]["workspace_bytes"] == 0
     # the row sum: one workgroup per row, written directly
@@ -107,6 +108,16 @@ def test_random_shapes_keep_invariants():
         for cu in (1, 32, 80, 256, 304):
             p = rd.rd_plan_dim(cu, outer, R, inner)
             check_invariants(p, outer, R, inner)
+
+
+def test_column_tile_width():
+    """Widest tile that still gives every CU a workgroup."""
+    assert rd.rd_plan_dim(CU, 128, 4096, 4095).col_waves == 8
+    assert rd.rd_plan_dim(CU, 64, 4096, 4095).col_waves == 4
+    assert rd.rd_plan_dim(CU, 1000, 10, 100).col_waves == 1   # 25 lane-columns
+    assert rd.rd_plan_dim(CU, 1000, 10, 1000).col_waves == 4  # 250 lane-columns
+    p = rd.rd_plan_dim(CU, 1, 1 << 16, 4095)                  # never reaches CU tiles
+    assert p.col_waves == 8 and p.split > 1 and p.blocks >= CU
 
 
 def test_small_problems_still_spread():
