@@ -97,6 +97,10 @@ def main(argv=None):
     ap.add_argument("--workload", action="append", default=None,
                     help="bench these workloads instead of the default step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--report", action="store_true",
+                    help="instead of the step line: one JSON line per workload (all five "
+                         "unless --workload is given), warm and cold GPU times, the oracle's "
+                         "CPU time and the parity check")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="only run a device-to-device copy of this many bytes 3 times "
                          "(a known-size kernel for calibrating HBM byte counters)")
@@ -130,6 +134,8 @@ def main(argv=None):
         return 0
     props = torch.cuda.get_device_properties(dev)
     cu = props.multi_processor_count
+    if args.report:
+        return report(args, dev, cu)
     names = args.workload or STEP_WORKLOADS
     ws = [workloads.WORKLOADS[n] for n in names]
 
@@ -251,6 +257,105 @@ def main(argv=None):
                             "rule": "|gpu - S| <= 1e-5*sum|x| + 1e-6 per output"}
 
     print(json.dumps(result), flush=True)
+    return 0
+
+
+# Context figures printed by the pages for the same operation (another machine):
+# "High-Performance Reduction Kernels" README, results on an NVIDIA T4 (sm_75),
+# fastest implementation per n, averaged over 100 launches.
+PAGES_T4 = {
+    "harmonic_1e6": {"ms": 0.0137, "impl": "CUDA C", "hardware": "NVIDIA T4"},
+    "uniform_1e8": {"ms": 1.4716, "impl": "CUDA C", "hardware": "NVIDIA T4"},
+    "normal_1e9": {"ms": 14.4983, "impl": "PyTorch", "hardware": "NVIDIA T4"},
+}
+
+
+def report(args, dev, cu):
+    """One JSON line per workload: GPU time warm (back to back) and cold (a
+    1 GiB write between calls evicts the caches, outside the timed events),
+    GB/s and fraction of 8 TB/s, the oracle's CPU time, and parity."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import sum_reduction_amd as rd
+    import workloads
+
+    threads = oracle.default_threads()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for name in (args.workload or list(workloads.WORKLOADS)):
+        w = workloads.WORKLOADS[name]
+        log("report: %s" % name)
+        host = workloads.generate(w)
+        x = torch.from_numpy(host).to(dev)
+        out = torch.empty(w.out_numel, dtype=torch.float32, device=dev)
+
+        def call():
+            if w.full_reduce:
+                rd.rd_sum_1d(x, out=out)
+            else:
+                rd.rd_sum_dim(x, w.outer, w.R, w.inner, out=out)
+
+        small = w.in_bytes < (1 << 30)
+        reps = 200 if small else 30
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+
+        def timed(cold: bool):
+            ms = []
+            for _ in range(reps):
+                if cold:
+                    flush.fill_(1.0)
+                # keep the GPU busy while the host enqueues the call, so the
+                # events see GPU time and not Python's enqueue latency
+                torch.cuda._sleep(200_000)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                call()
+                b.record()
+                b.synchronize()
+                ms.append(a.elapsed_time(b))
+            ms.sort()
+            return {"ms_median": round(ms[len(ms) // 2], 5), "ms_min": round(ms[0], 5),
+                    "ms_p90": round(ms[int(0.9 * (len(ms) - 1))], 5),
+                    "GBps_median": round(w.algorithmic_bytes / ms[len(ms) // 2] / 1e6, 1),
+                    "frac_of_peak": round(w.algorithmic_bytes / ms[len(ms) // 2] / 1e6
+                                          / PEAK_GBS, 4)}
+
+        warm = timed(False)
+        cold = timed(True)
+        got = out.cpu().numpy().reshape(-1)
+        t0 = time.perf_counter()
+        if w.full_reduce:
+            S, A = oracle.sum_1d(host)
+            S, A = np.array([S]), np.array([A])
+        else:
+            S, A = oracle.sum_dim(host, w.outer, w.R, w.inner, threads)
+        cpu_s = time.perf_counter() - t0
+        err = np.abs(got.astype(np.float64) - S.reshape(-1))
+        tol = oracle.tolerance(A.reshape(-1))
+        plan = (rd.rd_plan_1d(cu, w.numel) if w.full_reduce
+                else rd.rd_plan_dim(cu, w.outer, w.R, w.inner)).as_dict()
+        line = {
+            "workload": name, "shape": list(w.shape), "algorithmic_bytes": w.algorithmic_bytes,
+            "warm": warm, "cold": cold, "reps": reps, "plan": plan,
+            "cpu_oracle": {"s": round(cpu_s, 4), "GBps": round(w.algorithmic_bytes / cpu_s / 1e9, 3),
+                           "threads": 1 if w.full_reduce else threads},
+            "gpu_over_cpu": round(cpu_s * 1e3 / warm["ms_median"], 1),
+            "parity": {"ok": bool(oracle.within_tolerance(got, S.reshape(-1),
+                                                          A.reshape(-1)).all()),
+                       "max_err_over_tol": round(float((err / tol).max()), 5)},
+            "pages": PAGES_T4.get(name),
+        }
+        if w.name == "harmonic_1e6":
+            line["harmonic_closed_form"] = float(
+                np.log(w.numel) + 0.5772156649015329 + 1 / (2 * w.numel)
+                - 1 / (12 * w.numel ** 2))
+            line["gpu_value"] = float(got[0])
+        print(json.dumps(line), flush=True)
+        del x, out, host
+        torch.cuda.empty_cache()
     return 0
 
 

@@ -29,7 +29,14 @@
  * Workspace.  Where a shape needs per-block partials, the library allocates
  *   them stream-ordered on `stream` from a pool of its own and frees them on
  *   the same stream, so concurrent calls on different streams never share
- *   memory.
+ *   memory.  The partials of a split reduce are summed by a second kernel
+ *   in fixed order.  With the RD_COMBINE_LAST_BLOCK option the last
+ *   workgroup of the first kernel sums them instead; the integer ticket
+ *   counter that elects it belongs to the stream (one per stream and device,
+ *   reset by the kernel itself), so calls on one stream, which never overlap,
+ *   never share it with calls on another, and a call made while its stream
+ *   is being captured into a graph falls back to the second kernel: same
+ *   bits either way.
  * Semantics.  IEEE fp32 adds, round to nearest even, no flush of denormals,
  *   NaN and Inf propagate.  Accumulators start at +0.0, so the empty sum is
  *   +0.0 and an all -0.0 input sums to +0.0.  R == 0 writes outer*inner zeros;
@@ -127,6 +134,17 @@ typedef enum rd_order {
     RD_ORDER_BLOCKED = 2      /* piece p owns one contiguous run of chunks */
 } rd_order;
 
+/* How the partial sums of a split reduction are combined. */
+typedef enum rd_combine {
+    RD_COMBINE_NONE = 0,       /* one pass, no partial sums */
+    RD_COMBINE_PASS = 1,       /* a second kernel sums them in fixed order */
+    RD_COMBINE_LAST_BLOCK = 2  /* the last workgroup of the first kernel sums
+                                  them in the same order (one launch; an
+                                  option: slower than RD_COMBINE_PASS on
+                                  MI355X); calls on a capturing stream use
+                                  RD_COMBINE_PASS, with identical results */
+} rd_combine;
+
 typedef struct rd_plan {
     int32_t path;            /* rd_path */
     int32_t block_threads;   /* threads per workgroup of the main pass */
@@ -135,7 +153,8 @@ typedef struct rd_plan {
     int32_t row_waves;       /* COLS: waves of one workgroup taking turns in R */
     int32_t unroll;          /* 16-byte loads in flight per lane */
     int32_t nxcd;            /* XCDs the workgroup numbering is spread over */
-    int32_t passes;          /* 1, or 2 when partials need a combine pass */
+    int32_t passes;          /* kernel launches of the planned combine */
+    int32_t combine;         /* rd_combine */
     int32_t order;           /* ROWS: rd_order; 0 elsewhere */
     int32_t nontemporal;     /* 1: main-pass loads carry the streaming hint */
     int64_t split;           /* ROWS: pieces per row; COLS*: slabs of R */
@@ -166,6 +185,7 @@ typedef struct rd_tune {
     int32_t unroll;          /* ROWS, COLS: 2, 4, 8 or 16 */
     int32_t order;           /* ROWS: rd_order */
     int32_t nontemporal;     /* ROWS, COLS: 1 = off, 2 = on */
+    int32_t combine;         /* ROWS: 1 = second pass, 2 = last workgroup */
     int64_t split;           /* ROWS: pieces per row; COLS*: slabs of R */
 } rd_tune;
 

@@ -33,6 +33,7 @@
  */
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 #include <math.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -69,28 +70,43 @@ void oracle_sum_1d(const float* x, int64_t n, double* sum, double* abs_sum)
  * r only so that rows are read front to back; it does not change the order in
  * which any single output receives its terms.  Different o are independent
  * and are shared out over `nthreads` OpenMP threads (<= 0: OpenMP default).
+ * Each thread accumulates one o at a time in buffers of its own and then
+ * copies them out, so that threads never write the same cache line while
+ * they add (with inner == 1, neighbouring o share lines of `out`).
  */
 void oracle_sum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
                     double* out, double* abs_out, int nthreads)
 {
     if (nthreads < 1)
         nthreads = oracle_default_threads();
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
-    for (int64_t o = 0; o < outer; ++o) {
-        double* s = out + o * inner;
-        double* a = abs_out + o * inner;
-        for (int64_t i = 0; i < inner; ++i) {
-            s[i] = 0.0;
-            a[i] = 0.0;
-        }
-        for (int64_t r = 0; r < R; ++r) {
-            const float* row = x + (o * R + r) * inner;
-            for (int64_t i = 0; i < inner; ++i) {
-                double v = (double)row[i];
-                s[i] += v;
-                a[i] += fabs(v);
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* s = (double*)malloc((size_t)(inner > 0 ? inner : 1) * sizeof(double));
+        double* a = (double*)malloc((size_t)(inner > 0 ? inner : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t o = 0; o < outer; ++o) {
+            if (!s || !a) {  /* no buffer: report NaN rather than a wrong sum */
+                for (int64_t i = 0; i < inner; ++i)
+                    out[o * inner + i] = abs_out[o * inner + i] = NAN;
+                continue;
             }
+            for (int64_t i = 0; i < inner; ++i) {
+                s[i] = 0.0;
+                a[i] = 0.0;
+            }
+            for (int64_t r = 0; r < R; ++r) {
+                const float* row = x + (o * R + r) * inner;
+                for (int64_t i = 0; i < inner; ++i) {
+                    double v = (double)row[i];
+                    s[i] += v;
+                    a[i] += fabs(v);
+                }
+            }
+            memcpy(out + o * inner, s, (size_t)inner * sizeof(double));
+            memcpy(abs_out + o * inner, a, (size_t)inner * sizeof(double));
         }
+        free(s);
+        free(a);
     }
 }
 

@@ -34,6 +34,7 @@ RD_OK = 0
 PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
               5: "cols_narrow"}
 ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
+COMBINE_NAMES = {0: "none", 1: "pass", 2: "last_block"}
 
 
 class RdError(RuntimeError):
@@ -51,6 +52,7 @@ class RdPlan(ctypes.Structure):
                 ("group", ctypes.c_int32), ("col_waves", ctypes.c_int32),
                 ("row_waves", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("nxcd", ctypes.c_int32), ("passes", ctypes.c_int32),
+                ("combine", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
                 ("split", ctypes.c_int64), ("rows_per_split", ctypes.c_int64),
                 ("blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
@@ -59,6 +61,7 @@ class RdPlan(ctypes.Structure):
         d = {name: getattr(self, name) for name, _ in self._fields_}
         d["path"] = PATH_NAMES.get(self.path, self.path)
         d["order"] = ORDER_NAMES.get(self.order, self.order)
+        d["combine"] = COMBINE_NAMES.get(self.combine, self.combine)
         return d
 
 
@@ -66,7 +69,7 @@ class RdTune(ctypes.Structure):
     _fields_ = [("group", ctypes.c_int32), ("col_waves", ctypes.c_int32),
                 ("row_waves", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
-                ("split", ctypes.c_int64)]
+                ("combine", ctypes.c_int32), ("split", ctypes.c_int64)]
 
 
 _lib = None

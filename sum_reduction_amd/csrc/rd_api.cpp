@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <unordered_map>
 
 #include <hip/hip_runtime_api.h>
 
@@ -18,13 +19,55 @@ thread_local int t_last_hip = 0;
 // (which fixes the plan, hence the summation order) and a memory pool of the
 // library's own for workspaces, which keeps its memory between calls.
 constexpr int kMaxDevices = 64;
+// Ticket counters for the fused (last-workgroup) combine: one per stream that
+// has made such a call on the device, zeroed once when the device is set up
+// and left at zero by every kernel that uses one.  Calls on one stream never
+// overlap, so a stream's counter is always 0 when its next kernel starts.
+constexpr int kTicketSlots = 4096;
 struct Device {
     std::once_flag once;
     int cu = 0;
     hipMemPool_t pool = nullptr;
     hipError_t err = hipSuccess;
+    uint32_t* tickets = nullptr;  // null: the fused combine is not used
+    std::mutex ticket_mu;
+    std::unordered_map<hipStream_t, int> ticket_of;
 };
 Device g_devices[kMaxDevices];
+
+// Zeroed ticket counters, or null if they cannot be had (then every split
+// reduce takes the two-kernel combine, with the same results).
+uint32_t* make_tickets() {
+    uint32_t* t = nullptr;
+    if (hipMalloc(reinterpret_cast<void**>(&t), kTicketSlots * sizeof(uint32_t)) != hipSuccess)
+        return nullptr;
+    hipStream_t s = nullptr;
+    bool ok = hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipMemsetAsync(t, 0, kTicketSlots * sizeof(uint32_t), s) == hipSuccess;
+    ok = ok && hipStreamSynchronize(s) == hipSuccess;
+    if (s) (void)hipStreamDestroy(s);
+    if (!ok) {
+        (void)hipFree(t);
+        return nullptr;
+    }
+    return t;
+}
+
+// The ticket counter of `stream`, or null for the two-kernel combine (stream
+// being captured, or every counter taken).
+uint32_t* stream_ticket(Device& d, hipStream_t stream) {
+    if (!d.tickets) return nullptr;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(d.ticket_mu);
+    auto it = d.ticket_of.find(stream);
+    if (it != d.ticket_of.end()) return d.tickets + it->second;
+    const int slot = static_cast<int>(d.ticket_of.size());
+    if (slot >= kTicketSlots) return nullptr;
+    d.ticket_of.emplace(stream, slot);
+    return d.tickets + slot;
+}
 
 std::mutex g_tune_mu;
 rd_tune g_tune;
@@ -82,6 +125,7 @@ rd_status current_device(Device** out) {
             d.err = err;
             return;
         }
+        d.tickets = make_tickets();
         d.cu = cu;
     });
     if (d.err != hipSuccess) return hip_fail(d.err, RD_ERR_HIP);
@@ -123,10 +167,13 @@ rd_status execute(const rd_plan& p, Device& dev, const float* x, int64_t outer, 
             break;
         case RD_PATH_ROWS:
             if (p.split == 1) {
-                e = rd::launch_rows(p, x, outer, R, out, s);
+                e = rd::launch_rows(p, x, outer, R, out, nullptr, nullptr, s);
             } else {
-                e = rd::launch_rows(p, x, outer, R, ws, s);
-                if (e == hipSuccess) e = rd::launch_rows_combine(ws, outer, p.split, out, s);
+                uint32_t* ticket =
+                    p.combine == RD_COMBINE_LAST_BLOCK ? stream_ticket(dev, s) : nullptr;
+                e = rd::launch_rows(p, x, outer, R, ws, ticket, out, s);
+                if (e == hipSuccess && !ticket)
+                    e = rd::launch_rows_combine(ws, outer, p.split, out, s);
             }
             break;
         case RD_PATH_COLS:
@@ -222,7 +269,7 @@ rd_status rd_tune_set(const rd_tune* tune) {
         return RD_OK;
     }
     if (tune->group < 0 || tune->col_waves < 0 || tune->row_waves < 0 || tune->unroll < 0 ||
-        tune->order < 0 || tune->nontemporal < 0 || tune->split < 0)
+        tune->order < 0 || tune->nontemporal < 0 || tune->combine < 0 || tune->split < 0)
         return RD_ERR_INVALID_ARG;
     g_tune = *tune;
     g_tune_on = true;

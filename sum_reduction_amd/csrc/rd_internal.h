@@ -27,8 +27,10 @@ rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
 // Kernel launchers (rd_kernels.hip).  Each enqueues on `s` and returns the
 // error hipLaunchKernel reports for the launch.
 hipError_t launch_fill_zero(float* out, int64_t n, hipStream_t s);
+// ticket == nullptr: dst receives the piece sums (or the row sums when
+// p.split == 1); otherwise the last workgroup also combines them into out.
 hipError_t launch_rows(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       float* dst, hipStream_t s);
+                       float* dst, uint32_t* ticket, float* out, hipStream_t s);
 hipError_t launch_rows_short(const float* x, int64_t outer, int64_t R, float* out,
                              hipStream_t s);
 hipError_t launch_rows_combine(const float* part, int64_t outer, int64_t P,

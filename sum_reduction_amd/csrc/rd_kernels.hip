@@ -30,7 +30,8 @@
 //            R % 4 tail elements go to acc[0].x of the row's lanes 0..2;
 //            a = acc[0] + acc[1], lane total = (a.x + a.y) + (a.z + a.w); then
 //            the wave butterfly, then the wave sums in wave order; then (if
-//            the row has several pieces) the piece sums in piece order.
+//            the row has several pieces) combine_row over the piece sums, in
+//            a second kernel or in the last workgroup of the first.
 //  COLS      wave (cw, rw) adds its k-th row, r0 + rw + k*RW, into float4
 //            accumulator (k mod 2); acc[0] + acc[1]; then the row phases in
 //            rw order; then (if split) the slabs in slab order.
@@ -118,6 +119,19 @@ __device__ __forceinline__ int64_t xcd_block(uint32_t nxcd) {
     return int64_t(x) * q + (x < r ? x : r) + i;
 }
 
+// out_o = the sum of the P piece sums of one row: lane t adds pieces t,
+// t + 256, ... in order, then the workgroup reduction.  Used by the second
+// pass and by the last workgroup of a fused first pass, so both give the same
+// bits.  Every thread of the workgroup must call it.
+__device__ __forceinline__ void combine_row(const float* __restrict__ part, int64_t P,
+                                            float* __restrict__ out_o, float* lds) {
+    float t = 0.f;
+    for (int64_t k = threadIdx.x; k < P; k += kBlock) t += part[k];
+    t = block_sum(t, lds);
+    if (threadIdx.x == 0) *out_o = t;
+    __syncthreads();
+}
+
 // ----------------------------------------------------------------- ROWS
 // Each group of G lanes (one wave, or the whole workgroup) reduces one row
 // piece: segment seg = (row o, piece p), o = seg / P, p = seg % P.  With
@@ -130,12 +144,21 @@ __device__ __forceinline__ int64_t xcd_block(uint32_t nxcd) {
 //                C = ceil(nvec / P) rounded up to a multiple of G, and its
 //                lane takes p*C + lane, p*C + lane + G, ... (each group streams
 //                one contiguous stretch of memory)
+// Fused combine (ticket != null, P > 1): after storing its piece sums, each
+// workgroup publishes them (device-scope release) and takes a ticket from an
+// integer counter; the workgroup that draws the last ticket acquires, sums
+// every row's pieces with combine_row into out[0 .. outer), and resets the
+// counter to 0 for the next call on the same stream.  The counter must be 0
+// at launch.  No float atomics: only the ticket is atomic, and the combine
+// order is the second pass's.
 template <int G, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ x,
                                                       int64_t R, int64_t nseg,
                                                       int64_t P, int32_t blocked,
                                                       float* __restrict__ dst,
-                                                      uint32_t nxcd) {
+                                                      uint32_t nxcd,
+                                                      uint32_t* __restrict__ ticket,
+                                                      float* __restrict__ out) {
     static_assert(G == kWave || G == kBlock, "group is a wave or a workgroup");
     constexpr int kGroups = kBlock / G;
     __shared__ float lds[kBlock / kWave];
@@ -180,6 +203,24 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
             if (gl == 0 && seg < nseg) dst[seg] = total;
         }
     }
+    if (ticket != nullptr) {
+        // One release per workgroup, one acquire in the last one: a full
+        // fence in every wave would write back and invalidate the L2 of
+        // each XCD thousands of times under the still-running stream.
+        __shared__ uint32_t last;
+        __syncthreads();  // the workgroup's piece sums are stored
+        if (threadIdx.x == 0)
+            last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELEASE,
+                                          __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+        __syncthreads();
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            const int64_t outer = nseg / P;
+            for (int64_t o = 0; o < outer; ++o) combine_row(dst + o * P, P, out + o, lds);
+            if (threadIdx.x == 0)
+                __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // Rows shorter than a wave's worth of chunks: one lane per row, 16-byte
@@ -199,20 +240,13 @@ __global__ __launch_bounds__(kBlock) void rows_short_kernel(const float* __restr
     }
 }
 
-// Second pass of ROWS: out[o] = sum of the P piece sums of row o, in piece
-// order per lane (p = lane, lane + 256, ...), then the workgroup reduction.
+// Second pass of ROWS: out[o] = combine_row over the P piece sums of row o.
 __global__ __launch_bounds__(kBlock) void rows_combine_kernel(const float* __restrict__ part,
                                                               int64_t outer, int64_t P,
                                                               float* __restrict__ out) {
     __shared__ float lds[kBlock / kWave];
-    for (int64_t o = blockIdx.x; o < outer; o += gridDim.x) {
-        const float* p = part + o * P;
-        float t = 0.f;
-        for (int64_t k = threadIdx.x; k < P; k += kBlock) t += p[k];
-        t = block_sum(t, lds);
-        if (threadIdx.x == 0) out[o] = t;
-        __syncthreads();
-    }
+    for (int64_t o = blockIdx.x; o < outer; o += gridDim.x)
+        combine_row(part + o * P, P, out + o, lds);
 }
 
 // ----------------------------------------------------------------- COLS
@@ -368,19 +402,20 @@ constexpr ColShape kColShapes[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {1, 16}, {2, 
 
 template <int G, int U, bool NT>
 hipError_t rows_dispatch_u(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                           float* dst, hipStream_t s) {
+                           float* dst, uint32_t* ticket, float* out, hipStream_t s) {
     return launch(rows_kernel<G, U, NT>, p.blocks, kBlock, s, x, R, outer * p.split,
-                  p.split, int32_t(p.order == RD_ORDER_BLOCKED), dst, uint32_t(p.nxcd));
+                  p.split, int32_t(p.order == RD_ORDER_BLOCKED), dst, uint32_t(p.nxcd),
+                  ticket, out);
 }
 
 template <int G, bool NT>
 hipError_t rows_dispatch(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                         float* dst, hipStream_t s) {
+                         float* dst, uint32_t* ticket, float* out, hipStream_t s) {
     switch (p.unroll) {
-        case 2: return rows_dispatch_u<G, 2, NT>(p, x, outer, R, dst, s);
-        case 4: return rows_dispatch_u<G, 4, NT>(p, x, outer, R, dst, s);
-        case 8: return rows_dispatch_u<G, 8, NT>(p, x, outer, R, dst, s);
-        case 16: return rows_dispatch_u<G, 16, NT>(p, x, outer, R, dst, s);
+        case 2: return rows_dispatch_u<G, 2, NT>(p, x, outer, R, dst, ticket, out, s);
+        case 4: return rows_dispatch_u<G, 4, NT>(p, x, outer, R, dst, ticket, out, s);
+        case 8: return rows_dispatch_u<G, 8, NT>(p, x, outer, R, dst, ticket, out, s);
+        case 16: return rows_dispatch_u<G, 16, NT>(p, x, outer, R, dst, ticket, out, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -433,13 +468,15 @@ hipError_t launch_fill_zero(float* out, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_rows(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       float* dst, hipStream_t s) {
+                       float* dst, uint32_t* ticket, float* out, hipStream_t s) {
     if (p.group == kBlock)
-        return p.nontemporal ? rows_dispatch<kBlock, true>(p, x, outer, R, dst, s)
-                             : rows_dispatch<kBlock, false>(p, x, outer, R, dst, s);
+        return p.nontemporal
+                   ? rows_dispatch<kBlock, true>(p, x, outer, R, dst, ticket, out, s)
+                   : rows_dispatch<kBlock, false>(p, x, outer, R, dst, ticket, out, s);
     if (p.group == kWave)
-        return p.nontemporal ? rows_dispatch<kWave, true>(p, x, outer, R, dst, s)
-                             : rows_dispatch<kWave, false>(p, x, outer, R, dst, s);
+        return p.nontemporal
+                   ? rows_dispatch<kWave, true>(p, x, outer, R, dst, ticket, out, s)
+                   : rows_dispatch<kWave, false>(p, x, outer, R, dst, ticket, out, s);
     return hipErrorInvalidValue;
 }
 

@@ -46,7 +46,7 @@ int32_t nxcd_for(int cu_count) {
 }
 
 rd_status plan_rows(int cu, int64_t outer, int64_t R, const rd_tune* t, rd_plan* p) {
-    const bool forced = t && (t->group || t->unroll || t->split || t->order);
+    const bool forced = t && (t->group || t->unroll || t->split || t->order || t->combine);
     if (R < kShortRow && !forced) {
         p->path = RD_PATH_ROWS_SHORT;
         p->block_threads = kBlock;
@@ -87,8 +87,20 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, const rd_tune* t, rd_plan*
     const int64_t segs = outer * P;
     p->blocks = ceil_div(segs, groups_per_block);
     if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
-    p->passes = P > 1 ? 2 : 1;
     p->workspace_bytes = P > 1 ? segs * int64_t(sizeof(float)) : 0;
+    p->combine = RD_COMBINE_NONE;
+    if (P > 1) {
+        // The second kernel is the default: measured on MI355X it is faster
+        // than the fused last-workgroup combine at every size (1e6: 12.8 vs
+        // 13.1 us, 1e7: 17.6 vs 22.3, 1e8: 71.8 vs 76.8, 1e9: 573 vs 581),
+        // whose cross-XCD publication (one L2 write-back per workgroup, an L2
+        // invalidate and a memory round trip in the last one) costs more than
+        // a queued launch.
+        const int32_t c = (t && t->combine) ? t->combine : RD_COMBINE_PASS;
+        if (c != RD_COMBINE_PASS && c != RD_COMBINE_LAST_BLOCK) return RD_ERR_INVALID_ARG;
+        p->combine = c;
+    }
+    p->passes = p->combine == RD_COMBINE_PASS ? 2 : 1;
     return RD_OK;
 }
 
@@ -124,6 +136,7 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, const rd_tu
         p->blocks = ceil_div(p->split * lanes, kBlock);
         if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
         p->passes = p->split > 1 ? 2 : 1;
+        p->combine = p->split > 1 ? RD_COMBINE_PASS : RD_COMBINE_NONE;
         p->workspace_bytes = p->split > 1 ? p->split * lanes * int64_t(sizeof(float)) : 0;
         return RD_OK;
     }
@@ -171,6 +184,7 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, const rd_tu
     p->blocks = base * p->split;
     if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
     p->passes = p->split > 1 ? 2 : 1;
+    p->combine = p->split > 1 ? RD_COMBINE_PASS : RD_COMBINE_NONE;
     p->workspace_bytes =
         p->split > 1 ? p->split * outer * inner * int64_t(sizeof(float)) : 0;
     return RD_OK;

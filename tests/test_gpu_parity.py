@@ -92,20 +92,22 @@ def test_dim_problem47_family():
     _sweep_dim(shapes, [0, 1, 3], 106, "dim problem-47 family")
 
 
-ROW_TUNES = [(g, u, p, order, nt) for g in (64, 256) for u in (2, 4, 8, 16)
-             for p in (1, 2, 5) for order in (1, 2) for nt in (1, 2)]
+ROW_TUNES = [(g, u, p, order, nt, c) for g in (64, 256) for u in (2, 4, 8, 16)
+             for p in (1, 2, 5) for order in (1, 2) for nt in (1, 2) for c in (1, 2)
+             if not (p == 1 and c == 2)]
 
 
-@pytest.mark.parametrize("group,unroll,split,order,nt", ROW_TUNES,
-                         ids=["g%d_u%d_p%d_o%d_nt%d" % t for t in ROW_TUNES])
-def test_rows_kernel_shapes(group, unroll, split, order, nt):
+@pytest.mark.parametrize("group,unroll,split,order,nt,combine", ROW_TUNES,
+                         ids=["g%d_u%d_p%d_o%d_nt%d_c%d" % t for t in ROW_TUNES])
+def test_rows_kernel_shapes(group, unroll, split, order, nt, combine):
     """Every instantiated rows-kernel shape, both chunk orders, with and
-    without the streaming hint, forced splits included."""
+    without the streaming hint, forced splits with both combines."""
     if not rd.rd_tune_supported("rows", group, 0, unroll):
         pytest.skip("shape not built")
-    tag = "rows g%d u%d p%d o%d nt%d" % (group, unroll, split, order, nt)
-    seed = 200 + group + unroll + split + 7 * order + 11 * nt
-    with rd.tuning(group=group, unroll=unroll, split=split, order=order, nontemporal=nt):
+    tag = "rows g%d u%d p%d o%d nt%d c%d" % (group, unroll, split, order, nt, combine)
+    seed = 200 + group + unroll + split + 7 * order + 11 * nt + 13 * combine
+    with rd.tuning(group=group, unroll=unroll, split=split, order=order, nontemporal=nt,
+                   combine=combine):
         _sweep_1d([0, 1, 3, 4, 5, 63, 64, 65, 1000, 4097, 65539, 300_007], [0, 1, 2, 3],
                   seed, tag)
         _sweep_dim([(3, 1001, 1), (2, 5, 1), (7, 4099, 1)], [0, 3], seed + 1, tag + " dim")
@@ -130,6 +132,58 @@ def test_cols_kernel_shapes(cw, rw, unroll, split, nt):
     with rd.tuning(col_waves=cw, row_waves=rw, unroll=unroll, split=split, nontemporal=nt):
         _sweep_dim(shapes, [0, 1, 2, 3], 400 + cw * 100 + rw * 10 + unroll + split + nt,
                    "cols cw%d rw%d u%d s%d nt%d" % (cw, rw, unroll, split, nt))
+
+
+def _run_1d_many(ns, data_dev, tag):
+    slots = H.OutSlots([1] * len(ns))
+    for k, n in enumerate(ns):
+        assert H.call_1d(data_dev[:n], slots.ptr(k)) == 0, (tag, n)
+    return [o.view(np.uint32)[0] for o in slots.fetch()]
+
+
+def test_fused_combine_matches_second_pass():
+    """The last-workgroup combine and the second kernel sum the piece sums in
+    the same order: identical bits on random data, for every row kernel
+    shape, and correct against the oracle."""
+    a = workloads.random(3_000_007, 61, "normal")
+    dev = H.upload(a)
+    ns = [70, 4097, 65539, 1_000_001, 3_000_007]
+    for group in (64, 256):
+        for order in (1, 2):
+            common = dict(group=group, order=order, unroll=8)
+            with rd.tuning(combine=1, **common):
+                two = _run_1d_many(ns, dev, "pass")
+            with rd.tuning(combine=2, **common):
+                one = _run_1d_many(ns, dev, "last block")
+                # and again: the stream's counter must have been reset
+                again = _run_1d_many(ns, dev, "last block again")
+            assert two == one == again, (group, order)
+    for n, bits in zip(ns, one):
+        S, A = oracle.sum_1d(a[:n])
+        got = np.array([bits], np.uint32).view(np.float32)
+        H.assert_within_tolerance(got, [S], [A], "fused n=%d" % n)
+
+
+def test_fused_combine_several_rows_and_streams():
+    """Split row sums (few long rows) combined by the last workgroup, on
+    several streams at once: each stream has its own ticket counter."""
+    t = H.torch()
+    outer, R = 5, 1_000_003
+    a = workloads.small_ints(outer * R, 62)
+    dev = H.upload(a)
+    S, _ = oracle.sum_dim(a, outer, R, 1)
+    want = S.reshape(-1).astype(np.float32)
+    streams = [t.cuda.Stream() for _ in range(4)]
+    outs = [t.empty(outer, device="cuda") for _ in range(4 * 8)]
+    t.cuda.synchronize()
+    with rd.tuning(combine=2):
+        assert rd.rd_plan_dim(256, outer, R, 1).as_dict()["combine"] == "last_block"
+        for k, o in enumerate(outs):
+            with t.cuda.stream(streams[k % 4]):
+                rd.rd_sum_dim(dev, outer, R, 1, out=o)
+    t.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o.cpu().numpy(), want)
 
 
 def test_cols_narrow_splits():

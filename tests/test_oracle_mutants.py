@@ -35,17 +35,17 @@ MUTANTS = {
         "const float* row = x + (o * R + r) * inner;",
         "const float* row = x + (r * outer + o) * inner;"),
     "drops_last_row": (
-        "        for (int64_t r = 0; r < R; ++r) {\n            const float* row",
-        "        for (int64_t r = 0; r + 1 < R; ++r) {\n            const float* row"),
+        "for (int64_t r = 0; r < R; ++r) {\n                const float* row",
+        "for (int64_t r = 0; r + 1 < R; ++r) {\n                const float* row"),
     "shifted_column": (
-        "                double v = (double)row[i];",
-        "                double v = (double)row[(i + 1) % inner];"),
+        "double v = (double)row[i];",
+        "double v = (double)row[(i + 1) % inner];"),
     "row_stride_R_instead_of_inner": (
         "const float* row = x + (o * R + r) * inner;",
         "const float* row = x + o * R * inner + r * (inner > 1 ? inner - 1 : 1);"),
     "signed_magnitude_axis": (
-        "                s[i] += v;\n                a[i] += fabs(v);",
-        "                s[i] += v;\n                a[i] += v;"),
+        "s[i] += v;\n                    a[i] += fabs(v);",
+        "s[i] += v;\n                    a[i] += v;"),
     # per-output entry point
     "at_reversed_column": (
         "double v = (double)x[(o * R + r) * inner + i];",

@@ -30,6 +30,7 @@ def check_invariants(p, outer, R, inner):
             assert p.workspace_bytes == (4 * outer * p.split if p.split > 1 else 0)
             groups = outer * p.split
             assert p.blocks == min(-(-groups // (256 // p.group)), MAX_BLOCKS)
+            assert d["combine"] == ("pass" if p.split > 1 else "none")
         assert p.passes == (2 if p.split > 1 else 1)
     if d["path"] in ("cols", "cols_narrow"):
         # the slabs tile [0, R) with none empty
@@ -56,6 +57,7 @@ def test_workload_plans():
     assert plans["normal_1e9"]["path"] == "rows"
     assert plans["normal_1e9"]["blocks"] == CU
     assert plans["normal_1e9"]["order"] == "blocked"
+    assert plans["normal_1e9"]["combine"] == "pass"
     assert plans["normal_1e9"]["passes"] == 2
     assert all(p["nontemporal"] == 1 for p in plans.values())
     # the [128, 4096, 4095] reduce fills the chip without a split along R:
