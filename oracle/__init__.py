@@ -16,6 +16,9 @@ What it computes (the plain definition of a sum, see ``oracle.c``):
   contiguous [outer, R, inner] array (POPCORNBENCH level-1 problem 47 trace,
   "sum over a dimension", reduce_dim = 1).
 * ``sum_dim_at(...)``      -> the same for a list of chosen outputs.
+* ``reduce_1d / reduce_dim / reduce_dim_at(..., op)`` -> the same for the
+  other reductions, op in {"sum", "sumsq", "max", "min"} ("Seven-step
+  reduction" page: sum, max, the L2 norm are the same primitive).
 * ``within_tolerance``     -> the acceptance rule |got - S| <= 1e-5*A + 1e-6,
   NaN-aware.
 """
@@ -71,6 +74,13 @@ class Oracle:
         lib.oracle_sum_dim_at.restype = None
         lib.oracle_default_threads.argtypes = []
         lib.oracle_default_threads.restype = ctypes.c_int
+        ci = ctypes.c_int
+        lib.oracle_reduce_1d.argtypes = [vp, i64, ci, dp, dp]
+        lib.oracle_reduce_1d.restype = None
+        lib.oracle_reduce_dim.argtypes = [vp, i64, i64, i64, ci, vp, vp, ci]
+        lib.oracle_reduce_dim.restype = None
+        lib.oracle_reduce_dim_at.argtypes = [vp, i64, i64, i64, ci, vp, vp, i64, vp, vp]
+        lib.oracle_reduce_dim_at.restype = None
         self.lib = lib
         self.path = library
 
@@ -116,6 +126,52 @@ class Oracle:
         return s, a
 
 
+    # ---- other reductions: op is "sum", "sumsq", "max" or "min"
+    def reduce_1d(self, x, op: str):
+        """(S, A) of the full reduce with ``op``."""
+        if op == "sum":
+            return self.sum_1d(x)
+        x = _as_f32(x).reshape(-1)
+        s = ctypes.c_double()
+        a = ctypes.c_double()
+        self.lib.oracle_reduce_1d(x.ctypes.data, x.size, OPS[op], ctypes.byref(s),
+                                  ctypes.byref(a))
+        return s.value, a.value
+
+    def reduce_dim(self, x, outer: int, R: int, inner: int, op: str, threads: int = 0):
+        """(S, A), each float64 [outer, inner], of the axis reduce with ``op``."""
+        if op == "sum":
+            return self.sum_dim(x, outer, R, inner, threads)
+        x = _as_f32(x).reshape(-1)
+        if x.size != outer * R * inner:
+            raise ValueError("size %d != %d*%d*%d" % (x.size, outer, R, inner))
+        s = np.empty((outer, inner), dtype=np.float64)
+        a = np.empty((outer, inner), dtype=np.float64)
+        self.lib.oracle_reduce_dim(x.ctypes.data, outer, R, inner, OPS[op], s.ctypes.data,
+                                   a.ctypes.data, int(threads))
+        return s, a
+
+    def reduce_dim_at(self, x, outer: int, R: int, inner: int, op: str, o_idx, i_idx):
+        if op == "sum":
+            return self.sum_dim_at(x, outer, R, inner, o_idx, i_idx)
+        x = _as_f32(x).reshape(-1)
+        o_idx = np.ascontiguousarray(o_idx, dtype=np.int64)
+        i_idx = np.ascontiguousarray(i_idx, dtype=np.int64)
+        if o_idx.size and (o_idx.min() < 0 or o_idx.max() >= outer
+                           or i_idx.min() < 0 or i_idx.max() >= inner):
+            raise IndexError("sample index out of range")
+        s = np.empty(o_idx.size, dtype=np.float64)
+        a = np.empty(o_idx.size, dtype=np.float64)
+        self.lib.oracle_reduce_dim_at(x.ctypes.data, outer, R, inner, OPS[op],
+                                      o_idx.ctypes.data, i_idx.ctypes.data, o_idx.size,
+                                      s.ctypes.data, a.ctypes.data)
+        return s, a
+
+
+# numbering of the reductions (the same as the library's rd_op)
+OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
+
+
 def default() -> Oracle:
     """The oracle built from ``oracle.c`` (compiled on first use if absent)."""
     global _default
@@ -140,6 +196,18 @@ def sum_dim(x, outer: int, R: int, inner: int, threads: int = 0):
 
 def sum_dim_at(x, outer: int, R: int, inner: int, o_idx, i_idx):
     return default().sum_dim_at(x, outer, R, inner, o_idx, i_idx)
+
+
+def reduce_1d(x, op: str):
+    return default().reduce_1d(x, op)
+
+
+def reduce_dim(x, outer: int, R: int, inner: int, op: str, threads: int = 0):
+    return default().reduce_dim(x, outer, R, inner, op, threads)
+
+
+def reduce_dim_at(x, outer: int, R: int, inner: int, op: str, o_idx, i_idx):
+    return default().reduce_dim_at(x, outer, R, inner, op, o_idx, i_idx)
 
 
 def tolerance(abs_sum):

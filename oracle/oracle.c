@@ -134,3 +134,130 @@ void oracle_sum_dim_at(const float* x, int64_t outer, int64_t R, int64_t inner,
         abs_out[k] = a;
     }
 }
+
+/*
+ * Other reductions on the same shapes ("Seven-step reduction: 30x from one
+ * kernel", opening section: sum, max, the softmax denominator, the L2 norm
+ * and the attention row-sum are all the same primitive):
+ *
+ *   op 1  sum of squares  S = sum x^2   (the L2 norm is its square root)
+ *   op 2  maximum         S = max x
+ *   op 3  minimum         S = min x
+ *
+ * (op 0, the sum itself, is oracle_sum_1d / oracle_sum_dim above.)  The
+ * square of a widened fp32 value is exact in fp64 (48 significant bits), so
+ * the sum of squares is accumulated like the sum, with A = S.  Maximum and
+ * minimum follow IEEE 754-2019 maximum / minimum: a NaN anywhere gives NaN,
+ * and -0 counts as less than +0, so the result does not depend on the order
+ * of the operands.  The maximum of nothing is -Inf, the minimum +Inf; for
+ * them A = |S|.  An op outside 1..3 gives NaN.
+ */
+static double maximum754(double m, double v)
+{
+    if (isnan(m) || isnan(v))
+        return NAN;
+    if (m == v)
+        return signbit(m) ? v : m; /* +0 over -0 */
+    return v > m ? v : m;
+}
+
+static double minimum754(double m, double v)
+{
+    if (isnan(m) || isnan(v))
+        return NAN;
+    if (m == v)
+        return signbit(m) ? m : v; /* -0 over +0 */
+    return v < m ? v : m;
+}
+
+static double reduce_start(int op)
+{
+    if (op == 2)
+        return -INFINITY;
+    if (op == 3)
+        return INFINITY;
+    return 0.0;
+}
+
+/* One term into (s, a) for op 1..3. */
+static void reduce_step(int op, double v, double* s, double* a)
+{
+    if (op == 1) {
+        *s += v * v;
+        *a += v * v;
+    } else if (op == 2) {
+        *s = maximum754(*s, v);
+    } else if (op == 3) {
+        *s = minimum754(*s, v);
+    } else {
+        *s = NAN;
+    }
+}
+
+static double reduce_magnitude(int op, double s, double a)
+{
+    return op == 1 ? a : fabs(s);
+}
+
+/* Full reduce of n floats with op 1..3, in index order. */
+void oracle_reduce_1d(const float* x, int64_t n, int op, double* res, double* abs_res)
+{
+    double s = reduce_start(op);
+    double a = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        reduce_step(op, (double)x[i], &s, &a);
+    *res = s;
+    *abs_res = reduce_magnitude(op, s, a);
+}
+
+/* Axis reduce with op 1..3; same layout and threading as oracle_sum_dim. */
+void oracle_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner, int op,
+                       double* out, double* abs_out, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = oracle_default_threads();
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* s = (double*)malloc((size_t)(inner > 0 ? inner : 1) * sizeof(double));
+        double* a = (double*)malloc((size_t)(inner > 0 ? inner : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t o = 0; o < outer; ++o) {
+            if (!s || !a) {
+                for (int64_t i = 0; i < inner; ++i)
+                    out[o * inner + i] = abs_out[o * inner + i] = NAN;
+                continue;
+            }
+            for (int64_t i = 0; i < inner; ++i) {
+                s[i] = reduce_start(op);
+                a[i] = 0.0;
+            }
+            for (int64_t r = 0; r < R; ++r) {
+                const float* row = x + (o * R + r) * inner;
+                for (int64_t i = 0; i < inner; ++i)
+                    reduce_step(op, (double)row[i], &s[i], &a[i]);
+            }
+            for (int64_t i = 0; i < inner; ++i) {
+                out[o * inner + i] = s[i];
+                abs_out[o * inner + i] = reduce_magnitude(op, s[i], a[i]);
+            }
+        }
+        free(s);
+        free(a);
+    }
+}
+
+/* The same for m chosen outputs, each straight from the definition. */
+void oracle_reduce_dim_at(const float* x, int64_t outer, int64_t R, int64_t inner, int op,
+                          const int64_t* o_idx, const int64_t* i_idx, int64_t m,
+                          double* out, double* abs_out)
+{
+    (void)outer;
+    for (int64_t k = 0; k < m; ++k) {
+        double s = reduce_start(op);
+        double a = 0.0;
+        for (int64_t r = 0; r < R; ++r)
+            reduce_step(op, (double)x[(o_idx[k] * R + r) * inner + i_idx[k]], &s, &a);
+        out[k] = s;
+        abs_out[k] = reduce_magnitude(op, s, a);
+    }
+}

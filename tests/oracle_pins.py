@@ -15,7 +15,10 @@ What the pins rest on (none of them re-types the oracle's own loop):
 * a correctly rounded library sum -- ``math.fsum`` (Shewchuk), with the
   sequential fp64 error bound (n-1) * 2^-53 * sum|x|;
 * a library axis routine -- numpy's ``sum(axis=1)`` on integer data (exact);
-* IEEE special cases -- NaN, +-Inf, signed zero, empty sums.
+* IEEE special cases -- NaN, +-Inf, signed zero, empty sums;
+* for the other reductions: sum of squares closed forms (n(n+1)(2n+1)/6),
+  exact integer sums of squares, numpy's max / min, IEEE 754-2019
+  maximum / minimum special cases, order independence.
 """
 from __future__ import annotations
 
@@ -229,9 +232,101 @@ def pin_page_shape_facts(orc):
     assert S.size == 2 * inner
 
 
+# ------------------------------------------------------ other reductions
+def pin_sumsq_closed_form(orc):
+    """x[i] = i + 1: sum of squares n(n+1)(2n+1)/6, exact in fp64 here; along
+    an axis with x[o, r, i] = r + 1 every output is R(R+1)(2R+1)/6."""
+    for n in (0, 1, 2, 7, 1000, 100_000):
+        x = np.arange(1, n + 1, dtype=np.float32)
+        S, A = orc.reduce_1d(x, "sumsq")
+        want = n * (n + 1) * (2 * n + 1) // 6
+        assert S == want and A == want, (n, S, want)
+    for outer, R, inner in ((3, 5, 7), (2, 1000, 1), (1, 33, 65)):
+        x = np.broadcast_to(np.arange(1, R + 1, dtype=np.float32)[None, :, None],
+                            (outer, R, inner)).copy()
+        S, _ = orc.reduce_dim(x, outer, R, inner, "sumsq")
+        assert np.all(S == R * (R + 1) * (2 * R + 1) // 6), (outer, R, inner)
+
+
+def pin_sumsq_exact_and_fsum(orc):
+    """Integer data: the exact int64 sum of squares; random data: math.fsum of
+    the (exact) fp64 squares within the sequential bound; axis brute force."""
+    x = workloads.small_ints(1_000_003, 41)
+    S, A = orc.reduce_1d(x, "sumsq")
+    assert S == int(np.sum(x.astype(np.int64) ** 2)) and A == S
+    y = workloads.random(200_000, 42, "normal")
+    S, A = orc.reduce_1d(y, "sumsq")
+    F = math.fsum((y.astype(np.float64) ** 2).tolist())
+    assert abs(S - F) <= len(y) * U53 * A
+    for k, (outer, R, inner) in enumerate(((3, 17, 63), (5, 4, 1), (2, 9, 4095))):
+        z = workloads.small_ints(outer * R * inner, 43 + k)
+        S, _ = orc.reduce_dim(z, outer, R, inner, "sumsq")
+        want = (z.astype(np.int64).reshape(outer, R, inner) ** 2).sum(axis=1)
+        assert np.array_equal(S, want.astype(np.float64)), (outer, R, inner)
+        oo, ii = np.meshgrid(np.arange(outer), np.arange(inner), indexing="ij")
+        s1, _ = orc.reduce_dim_at(z, outer, R, inner, "sumsq", oo.reshape(-1), ii.reshape(-1))
+        assert np.array_equal(s1, want.reshape(-1).astype(np.float64))
+
+
+def pin_max_min_library(orc):
+    """Maximum and minimum of random data equal numpy's, along any axis, and
+    do not depend on the order of the terms."""
+    rng = np.random.default_rng(44)
+    x = workloads.random(1_000_001, 45, "normal")
+    for op, f in (("max", np.max), ("min", np.min)):
+        S, A = orc.reduce_1d(x, op)
+        assert S == float(f(x)) and A == abs(S)
+        S2, _ = orc.reduce_1d(x[rng.permutation(x.size)], op)
+        assert S2 == S
+        assert orc.reduce_1d(-x, op)[0] == -orc.reduce_1d(x, "min" if op == "max" else "max")[0]
+    for outer, R, inner in ((3, 5, 7), (4, 1000, 1), (2, 64, 4095), (1, 1, 3)):
+        z = workloads.random(outer * R * inner, 46 + R, "uniform", -1.0, 1.0)
+        z3 = z.reshape(outer, R, inner)
+        for op, f in (("max", np.max), ("min", np.min)):
+            S, _ = orc.reduce_dim(z, outer, R, inner, op)
+            assert np.array_equal(S, f(z3, axis=1).astype(np.float64)), (op, outer, R, inner)
+            oo, ii = np.meshgrid(np.arange(outer), np.arange(inner), indexing="ij")
+            s1, _ = orc.reduce_dim_at(z, outer, R, inner, op, oo.reshape(-1), ii.reshape(-1))
+            assert np.array_equal(s1, S.reshape(-1))
+    # all-negative and all-positive data: the start values are -Inf / +Inf
+    neg = -np.abs(x) - 1.0
+    assert orc.reduce_1d(neg.astype(np.float32), "max")[0] == float(np.max(neg.astype(np.float32)))
+    pos = np.abs(x) + 1.0
+    assert orc.reduce_1d(pos.astype(np.float32), "min")[0] == float(np.min(pos.astype(np.float32)))
+
+
+def pin_max_min_special(orc):
+    """IEEE 754-2019 maximum / minimum: NaN propagates, -0 < +0 in either
+    order, Inf is a value; the max of nothing is -Inf, the min +Inf."""
+    f = lambda *v: np.array(v, dtype=np.float32)
+    for v in (f(-0.0, 0.0), f(0.0, -0.0), f(-0.0, 0.0, -0.0)):
+        S, _ = orc.reduce_1d(v, "max")
+        assert S == 0.0 and not math.copysign(1.0, S) < 0, v
+        S, _ = orc.reduce_1d(v, "min")
+        assert S == 0.0 and math.copysign(1.0, S) < 0, v
+    assert math.copysign(1.0, orc.reduce_1d(f(-0.0, -0.0), "max")[0]) < 0
+    for op in ("max", "min", "sumsq"):
+        for pos in (0, 3, 6):
+            v = f(1, 2, 3, 4, 5, 6, 7)
+            v[pos] = np.nan
+            assert math.isnan(orc.reduce_1d(v, op)[0]), (op, pos)
+    assert orc.reduce_1d(f(1, np.inf, 2), "max")[0] == math.inf
+    assert orc.reduce_1d(f(1, -np.inf, 2), "min")[0] == -math.inf
+    assert orc.reduce_1d(f(), "max")[0] == -math.inf
+    assert orc.reduce_1d(f(), "min")[0] == math.inf
+    assert orc.reduce_1d(f(), "sumsq")[0] == 0.0
+    z = np.ones((2, 3, 4), np.float32)
+    z[1, 2, 3] = np.nan
+    S, _ = orc.reduce_dim(z, 2, 3, 4, "max")
+    assert math.isnan(S[1, 3]) and np.isfinite(np.delete(S.reshape(-1), 7)).all()
+    S, _ = orc.reduce_dim(np.zeros(0, np.float32), 2, 0, 3, "min")
+    assert np.all(S == math.inf)
+
+
 ALL_PINS = [
     pin_harmonic, pin_constants_1d, pin_integers_1d, pin_fsum_1d,
     pin_special_values_1d, pin_index_closed_form, pin_constants_axis,
     pin_bruteforce_axis, pin_fsum_axis, pin_special_values_axis,
-    pin_page_shape_facts,
+    pin_page_shape_facts, pin_sumsq_closed_form, pin_sumsq_exact_and_fsum,
+    pin_max_min_library, pin_max_min_special,
 ]

@@ -32,20 +32,46 @@ MUTANTS = {
         "    double s = -0.0;\n    double a = 0.0;\n    for (int64_t i = 0; i < n;"),
     # axis reduce
     "transposed_outer_and_R": (
-        "const float* row = x + (o * R + r) * inner;",
-        "const float* row = x + (r * outer + o) * inner;"),
+        "const float* row = x + (o * R + r) * inner;\n                for (int64_t i = 0; i < inner; ++i) {",
+        "const float* row = x + (r * outer + o) * inner;\n                for (int64_t i = 0; i < inner; ++i) {"),
     "drops_last_row": (
-        "for (int64_t r = 0; r < R; ++r) {\n                const float* row",
-        "for (int64_t r = 0; r + 1 < R; ++r) {\n                const float* row"),
+        "for (int64_t r = 0; r < R; ++r) {\n                const float* row = x + (o * R + r) * inner;\n                for (int64_t i = 0; i < inner; ++i) {",
+        "for (int64_t r = 0; r + 1 < R; ++r) {\n                const float* row = x + (o * R + r) * inner;\n                for (int64_t i = 0; i < inner; ++i) {"),
     "shifted_column": (
         "double v = (double)row[i];",
         "double v = (double)row[(i + 1) % inner];"),
     "row_stride_R_instead_of_inner": (
-        "const float* row = x + (o * R + r) * inner;",
-        "const float* row = x + o * R * inner + r * (inner > 1 ? inner - 1 : 1);"),
+        "const float* row = x + (o * R + r) * inner;\n                for (int64_t i = 0; i < inner; ++i) {",
+        "const float* row = x + o * R * inner + r * (inner > 1 ? inner - 1 : 1);\n                for (int64_t i = 0; i < inner; ++i) {"),
     "signed_magnitude_axis": (
         "s[i] += v;\n                    a[i] += fabs(v);",
         "s[i] += v;\n                    a[i] += v;"),
+    # the other reductions
+    "max_starts_at_zero": (
+        "    if (op == 2)\n        return -INFINITY;", "    if (op == 2)\n        return 0.0;"),
+    "min_starts_at_zero": (
+        "    if (op == 3)\n        return INFINITY;", "    if (op == 3)\n        return 0.0;"),
+    "max_keeps_smaller": (
+        "    return v > m ? v : m;", "    return v < m ? v : m;"),
+    "max_prefers_negative_zero": (
+        "return signbit(m) ? v : m; /* +0 over -0 */", "return signbit(m) ? m : v; /* +0 over -0 */"),
+    "max_ignores_nan": (
+        "static double maximum754(double m, double v)\n{\n    if (isnan(m) || isnan(v))",
+        "static double maximum754(double m, double v)\n{\n    if (0)"),
+    "min_ignores_nan": (
+        "static double minimum754(double m, double v)\n{\n    if (isnan(m) || isnan(v))",
+        "static double minimum754(double m, double v)\n{\n    if (0)"),
+    "sumsq_adds_magnitude": (
+        "        *s += v * v;\n        *a += v * v;", "        *s += fabs(v);\n        *a += v * v;"),
+    "reduce_transposed_outer_and_R": (
+        "const float* row = x + (o * R + r) * inner;\n                for (int64_t i = 0; i < inner; ++i)\n                    reduce_step",
+        "const float* row = x + (r * outer + o) * inner;\n                for (int64_t i = 0; i < inner; ++i)\n                    reduce_step"),
+    "reduce_drops_last_row": (
+        "for (int64_t r = 0; r < R; ++r) {\n                const float* row = x + (o * R + r) * inner;\n                for (int64_t i = 0; i < inner; ++i)\n                    reduce_step",
+        "for (int64_t r = 0; r + 1 < R; ++r) {\n                const float* row = x + (o * R + r) * inner;\n                for (int64_t i = 0; i < inner; ++i)\n                    reduce_step"),
+    "reduce_at_reversed_column": (
+        "reduce_step(op, (double)x[(o_idx[k] * R + r) * inner + i_idx[k]], &s, &a);",
+        "reduce_step(op, (double)x[(o_idx[k] * R + r) * inner + (inner - 1 - i_idx[k])], &s, &a);"),
     # per-output entry point
     "at_reversed_column": (
         "double v = (double)x[(o * R + r) * inner + i];",
