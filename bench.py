@@ -71,11 +71,11 @@ def measured_traffic(workload: str):
 def kernel_name(plan: dict) -> str:
     """The main-pass kernel a plan launches, as the profiler names it."""
     nt = "true" if plan["nontemporal"] else "false"
-    if plan["path"] == "cols":
-        return "cols_kernel<%d, %d, %d, %s>" % (plan["col_waves"], plan["row_waves"],
-                                                plan["unroll"], nt)
+    if plan["path"] == "cols":  # first template argument: the operator (0 = sum)
+        return "cols_kernel<0, %d, %d, %d, %s>" % (plan["col_waves"], plan["row_waves"],
+                                                   plan["unroll"], nt)
     if plan["path"] == "rows":
-        return "rows_kernel<%d, %d, %s>" % (plan["group"], plan["unroll"], nt)
+        return "rows_kernel<0, %d, %d, %s>" % (plan["group"], plan["unroll"], nt)
     return plan["path"] + "_kernel"
 
 
@@ -101,6 +101,9 @@ def main(argv=None):
                     help="instead of the step line: one JSON line per workload (all five "
                          "unless --workload is given), warm and cold GPU times, the oracle's "
                          "CPU time and the parity check")
+    ap.add_argument("--op", action="append", default=None,
+                    choices=["sum", "sumsq", "max", "min"],
+                    help="with --report: the reductions to time (default: sum)")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="only run a device-to-device copy of this many bytes 3 times "
                          "(a known-size kernel for calibrating HBM byte counters)")
@@ -285,78 +288,96 @@ def report(args, dev, cu):
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     for name in (args.workload or list(workloads.WORKLOADS)):
         w = workloads.WORKLOADS[name]
-        log("report: %s" % name)
         host = workloads.generate(w)
         x = torch.from_numpy(host).to(dev)
         out = torch.empty(w.out_numel, dtype=torch.float32, device=dev)
-
-        def call():
-            if w.full_reduce:
-                rd.rd_sum_1d(x, out=out)
-            else:
-                rd.rd_sum_dim(x, w.outer, w.R, w.inner, out=out)
-
-        small = w.in_bytes < (1 << 30)
-        reps = 200 if small else 30
-        for _ in range(3):
-            call()
-        torch.cuda.synchronize()
-
-        def timed(cold: bool):
-            ms = []
-            for _ in range(reps):
-                if cold:
-                    flush.fill_(1.0)
-                # keep the GPU busy while the host enqueues the call, so the
-                # events see GPU time and not Python's enqueue latency
-                torch.cuda._sleep(200_000)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                call()
-                b.record()
-                b.synchronize()
-                ms.append(a.elapsed_time(b))
-            ms.sort()
-            return {"ms_median": round(ms[len(ms) // 2], 5), "ms_min": round(ms[0], 5),
-                    "ms_p90": round(ms[int(0.9 * (len(ms) - 1))], 5),
-                    "GBps_median": round(w.algorithmic_bytes / ms[len(ms) // 2] / 1e6, 1),
-                    "frac_of_peak": round(w.algorithmic_bytes / ms[len(ms) // 2] / 1e6
-                                          / PEAK_GBS, 4)}
-
-        warm = timed(False)
-        cold = timed(True)
-        got = out.cpu().numpy().reshape(-1)
-        t0 = time.perf_counter()
-        if w.full_reduce:
-            S, A = oracle.sum_1d(host)
-            S, A = np.array([S]), np.array([A])
-        else:
-            S, A = oracle.sum_dim(host, w.outer, w.R, w.inner, threads)
-        cpu_s = time.perf_counter() - t0
-        err = np.abs(got.astype(np.float64) - S.reshape(-1))
-        tol = oracle.tolerance(A.reshape(-1))
-        plan = (rd.rd_plan_1d(cu, w.numel) if w.full_reduce
-                else rd.rd_plan_dim(cu, w.outer, w.R, w.inner)).as_dict()
-        line = {
-            "workload": name, "shape": list(w.shape), "algorithmic_bytes": w.algorithmic_bytes,
-            "warm": warm, "cold": cold, "reps": reps, "plan": plan,
-            "cpu_oracle": {"s": round(cpu_s, 4), "GBps": round(w.algorithmic_bytes / cpu_s / 1e9, 3),
-                           "threads": 1 if w.full_reduce else threads},
-            "gpu_over_cpu": round(cpu_s * 1e3 / warm["ms_median"], 1),
-            "parity": {"ok": bool(oracle.within_tolerance(got, S.reshape(-1),
-                                                          A.reshape(-1)).all()),
-                       "max_err_over_tol": round(float((err / tol).max()), 5)},
-            "pages": PAGES_T4.get(name),
-        }
-        if w.name == "harmonic_1e6":
-            line["harmonic_closed_form"] = float(
-                np.log(w.numel) + 0.5772156649015329 + 1 / (2 * w.numel)
-                - 1 / (12 * w.numel ** 2))
-            line["gpu_value"] = float(got[0])
-        print(json.dumps(line), flush=True)
+        for op in (args.op or ["sum"]):
+            log("report: %s %s" % (name, op))
+            print(json.dumps(report_one(w, op, host, x, out, flush, threads, cu)), flush=True)
         del x, out, host
         torch.cuda.empty_cache()
     return 0
+
+
+def report_one(w, op, host, x, out, flush, threads, cu):
+    """One report line: workload `w` reduced with `op`, GPU warm and cold,
+    the oracle's host time, parity."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import sum_reduction_amd as rd
+
+    def call():
+        if w.full_reduce:
+            rd.rd_reduce_1d(x, op, out=out)
+        else:
+            rd.rd_reduce_dim(x, w.outer, w.R, w.inner, op, out=out)
+
+    small = w.in_bytes < (1 << 30)
+    reps = 200 if small else 30
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+
+    def timed(cold: bool):
+        ms = []
+        for _ in range(reps):
+            if cold:
+                flush.fill_(1.0)
+            # keep the GPU busy while the host enqueues the call, so the
+            # events see GPU time and not Python's enqueue latency
+            torch.cuda._sleep(200_000)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        ms.sort()
+        return {"ms_median": round(ms[len(ms) // 2], 5), "ms_min": round(ms[0], 5),
+                "ms_p90": round(ms[int(0.9 * (len(ms) - 1))], 5),
+                "GBps_median": round(w.algorithmic_bytes / ms[len(ms) // 2] / 1e6, 1),
+                "frac_of_peak": round(w.algorithmic_bytes / ms[len(ms) // 2] / 1e6
+                                      / PEAK_GBS, 4)}
+
+    warm = timed(False)
+    cold = timed(True)
+    got = out.cpu().numpy().reshape(-1)
+    t0 = time.perf_counter()
+    if w.full_reduce:
+        S, A = oracle.reduce_1d(host, op)
+        S, A = np.array([S]), np.array([A])
+    else:
+        S, A = oracle.reduce_dim(host, w.outer, w.R, w.inner, op, threads)
+    cpu_s = time.perf_counter() - t0
+    with np.errstate(invalid="ignore"):
+        err = np.abs(got.astype(np.float64) - S.reshape(-1))
+    tol = oracle.tolerance(A.reshape(-1))
+    plan = (rd.rd_plan_1d(cu, w.numel) if w.full_reduce
+            else rd.rd_plan_dim(cu, w.outer, w.R, w.inner)).as_dict()
+    line = {
+        "workload": w.name, "op": op, "shape": list(w.shape),
+        "algorithmic_bytes": w.algorithmic_bytes,
+        "warm": warm, "cold": cold, "reps": reps, "plan": plan,
+        "cpu_oracle": {"s": round(cpu_s, 4), "GBps": round(w.algorithmic_bytes / cpu_s / 1e9, 3),
+                       "threads": 1 if w.full_reduce else threads},
+        "gpu_over_cpu": round(cpu_s * 1e3 / warm["ms_median"], 1),
+        "parity": {"ok": bool(oracle.within_tolerance(got, S.reshape(-1),
+                                                      A.reshape(-1)).all()),
+                   "max_err_over_tol": round(float(np.nanmax(err / tol))
+                                             if np.isfinite(err).any() else 0.0, 5)},
+        "pages": PAGES_T4.get(w.name) if op == "sum" else None,
+    }
+    if op in ("max", "min"):  # exact reductions: the bits must match
+        line["parity"]["bit_exact"] = bool(np.array_equal(
+            got.view(np.uint32), S.reshape(-1).astype(np.float32).view(np.uint32)))
+    if w.name == "harmonic_1e6" and op == "sum":
+        line["harmonic_closed_form"] = float(
+            np.log(w.numel) + 0.5772156649015329 + 1 / (2 * w.numel)
+            - 1 / (12 * w.numel ** 2))
+        line["gpu_value"] = float(got[0])
+    return line
 
 
 if __name__ == "__main__":

@@ -66,6 +66,18 @@ extern "C" {
 #define RD_VERSION_MINOR 1
 #define RD_VERSION_PATCH 0
 
+/* The reductions.  The sum is the method; the others run on the same
+ * kernels ("Seven-step reduction: 30x from one kernel", opening section:
+ * sum, max and the L2 norm are one primitive). */
+typedef enum rd_op {
+    RD_OP_SUM = 0,   /* sum x                 empty: +0.0 */
+    RD_OP_SUMSQ = 1, /* sum x*x (one fused multiply-add per term; the L2 norm
+                        is its square root)   empty: +0.0 */
+    RD_OP_MAX = 2,   /* maximum, IEEE 754-2019: NaN propagates, -0 < +0
+                                              empty: -Inf */
+    RD_OP_MIN = 3    /* minimum, IEEE 754-2019 empty: +Inf */
+} rd_op;
+
 typedef enum rd_status {
     RD_OK = 0,
     RD_ERR_INVALID_ARG = 1, /* null/misaligned/overlapping pointer, negative or
@@ -103,6 +115,21 @@ rd_status rd_sum_1d(const float* x, int64_t n, float* out, hipStream_t stream);
  */
 rd_status rd_sum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
                      float* out, hipStream_t stream);
+
+/*
+ * The same two reductions with another operator: rd_reduce_1d(x, n, op, ...)
+ * and rd_reduce_dim(x, outer, R, inner, op, ...) take the arguments of
+ * rd_sum_1d / rd_sum_dim plus op, an rd_op (anything else is
+ * RD_ERR_INVALID_ARG).  An empty reduction (n == 0, R == 0) writes the
+ * operator's empty value.  The maximum and the minimum are exact (their
+ * result is one of the inputs, or NaN) and do not depend on the order of the
+ * terms; the sum of squares accumulates like the sum.  rd_sum_1d(...) is
+ * rd_reduce_1d(..., RD_OP_SUM, ...).
+ */
+rd_status rd_reduce_1d(const float* x, int64_t n, int32_t op, float* out,
+                       hipStream_t stream);
+rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
+                        int32_t op, float* out, hipStream_t stream);
 
 /* Static, NUL-terminated name of a status code ("RD_OK", ...). */
 const char* rd_status_string(rd_status status);
@@ -163,7 +190,8 @@ typedef struct rd_plan {
     int64_t workspace_bytes; /* stream-ordered scratch (0 if passes == 1) */
 } rd_plan;
 
-/* Plan of rd_sum_dim for that shape on a device with cu_count CUs. */
+/* Plan of rd_sum_dim for that shape on a device with cu_count CUs (the
+ * other operators use the same plan). */
 rd_status rd_plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
                       rd_plan* plan);
 
@@ -191,9 +219,11 @@ typedef struct rd_tune {
 
 rd_status rd_tune_set(const rd_tune* tune);
 
-/* 1 if this build has a kernel for (path, group|col_waves, row_waves,
- * unroll); path is RD_PATH_ROWS or RD_PATH_COLS, the unused field is 0. */
-int rd_tune_supported(int32_t path, int32_t group_or_col_waves,
+/* 1 if this build has a kernel for (op, path, group|col_waves, row_waves,
+ * unroll); path is RD_PATH_ROWS or RD_PATH_COLS, the unused field is 0.
+ * The sum has every shape; the other operators have the planner's default
+ * shapes (ROWS: U = 8 or 16; COLS: row_waves = 1, U = 4). */
+int rd_tune_supported(int32_t op, int32_t path, int32_t group_or_col_waves,
                       int32_t row_waves, int32_t unroll);
 
 #ifdef __cplusplus

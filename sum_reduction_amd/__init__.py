@@ -24,13 +24,15 @@ __all__ = [
     "RdError", "RdPlan", "RdTune", "library_path", "load", "rd_sum_1d", "rd_sum_dim",
     "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
     "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "sum", "tuning",
-    "PATH_NAMES",
+    "PATH_NAMES", "OPS", "rd_reduce_1d", "rd_reduce_dim", "reduce",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "librd.so")
 
 RD_OK = 0
+# rd_op: the reductions (the sum is the method; the others share its kernels)
+OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
 PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
               5: "cols_narrow"}
 ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
@@ -93,6 +95,10 @@ def load():
     lib.rd_sum_1d.restype = ctypes.c_int
     lib.rd_sum_dim.argtypes = [vp, i64, i64, i64, vp, vp]
     lib.rd_sum_dim.restype = ctypes.c_int
+    lib.rd_reduce_1d.argtypes = [vp, i64, i32, vp, vp]
+    lib.rd_reduce_1d.restype = ctypes.c_int
+    lib.rd_reduce_dim.argtypes = [vp, i64, i64, i64, i32, vp, vp]
+    lib.rd_reduce_dim.restype = ctypes.c_int
     lib.rd_status_string.argtypes = [ctypes.c_int]
     lib.rd_status_string.restype = ctypes.c_char_p
     lib.rd_last_hip_error.argtypes = []
@@ -105,7 +111,7 @@ def load():
     lib.rd_plan_1d.restype = ctypes.c_int
     lib.rd_tune_set.argtypes = [ctypes.POINTER(RdTune)]
     lib.rd_tune_set.restype = ctypes.c_int
-    lib.rd_tune_supported.argtypes = [i32, i32, i32, i32]
+    lib.rd_tune_supported.argtypes = [i32, i32, i32, i32, i32]
     lib.rd_tune_supported.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -147,9 +153,10 @@ def rd_tune_set(tune: Optional[RdTune]):
 
 
 def rd_tune_supported(path: str, group_or_col_waves: int, row_waves: int,
-                      unroll: int) -> bool:
+                      unroll: int, op: str = "sum") -> bool:
     code = {"rows": 2, "cols": 4}[path]
-    return bool(load().rd_tune_supported(code, group_or_col_waves, row_waves, unroll))
+    return bool(load().rd_tune_supported(OPS[op], code, group_or_col_waves, row_waves,
+                                         unroll))
 
 
 class tuning:
@@ -205,10 +212,40 @@ def _out_tensor(out, numel: int, device, shape):
     return out
 
 
+def _op_code(op) -> int:
+    if isinstance(op, str):
+        if op not in OPS:
+            raise ValueError("op must be one of %s" % sorted(OPS))
+        return OPS[op]
+    return int(op)
+
+
+def rd_reduce_1d(x, op="sum", out=None, stream=None):
+    """Reduction ``op`` ("sum", "sumsq", "max", "min") of all elements of the
+    float32 GPU tensor ``x`` into ``out`` (a 1-element tensor, allocated when
+    None).  Asynchronous on ``stream`` (default: torch's current stream)."""
+    _check_input(x, x.numel() if hasattr(x, "numel") else -1)
+    out = _out_tensor(out, 1, x.device, (1,))
+    ptr = x.data_ptr() if x.numel() else None
+    _check(load().rd_reduce_1d(ptr, x.numel(), _op_code(op), out.data_ptr(),
+                               _stream_handle(stream)), "rd_reduce_1d")
+    return out
+
+
+def rd_reduce_dim(x, outer: int, R: int, inner: int, op="sum", out=None, stream=None):
+    """out[o, i] = op over r of x[o, r, i] for x viewed as [outer, R, inner];
+    ``out`` is [outer, inner] (allocated when None)."""
+    _check_input(x, outer * R * inner)
+    out = _out_tensor(out, outer * inner, x.device, (outer, inner))
+    xp = x.data_ptr() if x.numel() else None
+    optr = out.data_ptr() if out.numel() else None
+    _check(load().rd_reduce_dim(xp, outer, R, inner, _op_code(op), optr,
+                                _stream_handle(stream)), "rd_reduce_dim")
+    return out
+
+
 def rd_sum_1d(x, out=None, stream=None):
-    """Sum of all elements of the float32 GPU tensor ``x`` into ``out`` (a
-    1-element tensor, allocated when None).  Asynchronous on ``stream``
-    (default: torch's current stream)."""
+    """Sum of all elements of the float32 GPU tensor ``x`` (rd_sum_1d)."""
     _check_input(x, x.numel() if hasattr(x, "numel") else -1)
     out = _out_tensor(out, 1, x.device, (1,))
     ptr = x.data_ptr() if x.numel() else None
@@ -219,21 +256,22 @@ def rd_sum_1d(x, out=None, stream=None):
 
 def rd_sum_dim(x, outer: int, R: int, inner: int, out=None, stream=None):
     """out[o, i] = sum_r x[o, r, i] for x viewed as [outer, R, inner]; ``out``
-    is [outer, inner] (allocated when None)."""
+    is [outer, inner] (allocated when None) (rd_sum_dim)."""
     _check_input(x, outer * R * inner)
     out = _out_tensor(out, outer * inner, x.device, (outer, inner))
     xp = x.data_ptr() if x.numel() else None
-    op = out.data_ptr() if out.numel() else None
-    _check(load().rd_sum_dim(xp, outer, R, inner, op, _stream_handle(stream)),
+    optr = out.data_ptr() if out.numel() else None
+    _check(load().rd_sum_dim(xp, outer, R, inner, optr, _stream_handle(stream)),
            "rd_sum_dim")
     return out
 
 
-def sum(x, dim: Optional[int] = None, out=None, stream=None):
-    """torch.sum(x) or torch.sum(x, dim) for a contiguous float32 GPU tensor,
-    through rd_sum_1d / rd_sum_dim.  Returns a 0-d tensor for dim=None."""
+def reduce(x, op="sum", dim: Optional[int] = None, out=None, stream=None):
+    """torch-style reduction of a contiguous float32 GPU tensor over all
+    elements (dim=None, a 0-d result) or over one dimension, through
+    rd_reduce_1d / rd_reduce_dim.  op: "sum", "sumsq", "max" or "min"."""
     if dim is None:
-        return rd_sum_1d(x, None if out is None else out.view(1), stream).view(())
+        return rd_reduce_1d(x, op, None if out is None else out.view(1), stream).view(())
     shape = tuple(x.shape)
     d = dim % len(shape)
     outer = 1
@@ -242,6 +280,11 @@ def sum(x, dim: Optional[int] = None, out=None, stream=None):
     inner = 1
     for s in shape[d + 1:]:
         inner *= s
-    res = rd_sum_dim(x, outer, shape[d], inner,
-                     None if out is None else out.view(outer, inner), stream)
+    res = rd_reduce_dim(x, outer, shape[d], inner, op,
+                        None if out is None else out.view(outer, inner), stream)
     return res.view(shape[:d] + shape[d + 1:])
+
+
+def sum(x, dim: Optional[int] = None, out=None, stream=None):
+    """torch.sum(x) or torch.sum(x, dim) for a contiguous float32 GPU tensor."""
+    return reduce(x, "sum", dim, out, stream)

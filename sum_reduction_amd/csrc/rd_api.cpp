@@ -133,9 +133,10 @@ rd_status current_device(Device** out) {
     return RD_OK;
 }
 
-rd_status make_plan(int cu, int64_t outer, int64_t R, int64_t inner, rd_plan* plan) {
+rd_status make_plan(int cu, int64_t outer, int64_t R, int64_t inner, int op,
+                    rd_plan* plan) {
     std::lock_guard<std::mutex> lock(g_tune_mu);
-    return rd::plan_dim(cu, outer, R, inner, g_tune_on ? &g_tune : nullptr, plan);
+    return rd::plan_dim(cu, outer, R, inner, op, g_tune_on ? &g_tune : nullptr, plan);
 }
 
 // Failure injection for tests of the error paths, read from the environment:
@@ -146,8 +147,8 @@ bool inject(const char* name) {
     return v && v[0] && v[0] != '0';
 }
 
-rd_status execute(const rd_plan& p, Device& dev, const float* x, int64_t outer, int64_t R,
-                  int64_t inner, float* out, hipStream_t s) {
+rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, int64_t outer,
+                  int64_t R, int64_t inner, float* out, hipStream_t s) {
     if (p.path == RD_PATH_NONE) return RD_OK;
     if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
@@ -160,29 +161,30 @@ rd_status execute(const rd_plan& p, Device& dev, const float* x, int64_t outer, 
     hipError_t e = hipSuccess;
     switch (p.path) {
         case RD_PATH_ZERO:
-            e = rd::launch_fill_zero(out, outer * inner, s);
+            e = rd::launch_fill_start(op, out, outer * inner, s);
             break;
         case RD_PATH_ROWS_SHORT:
-            e = rd::launch_rows_short(x, outer, R, out, s);
+            e = rd::launch_rows_short(op, x, outer, R, out, s);
             break;
         case RD_PATH_ROWS:
             if (p.split == 1) {
-                e = rd::launch_rows(p, x, outer, R, out, nullptr, nullptr, s);
+                e = rd::launch_rows(op, p, x, outer, R, out, nullptr, nullptr, s);
             } else {
                 uint32_t* ticket =
                     p.combine == RD_COMBINE_LAST_BLOCK ? stream_ticket(dev, s) : nullptr;
-                e = rd::launch_rows(p, x, outer, R, ws, ticket, out, s);
+                e = rd::launch_rows(op, p, x, outer, R, ws, ticket, out, s);
                 if (e == hipSuccess && !ticket)
-                    e = rd::launch_rows_combine(ws, outer, p.split, out, s);
+                    e = rd::launch_rows_combine(op, ws, outer, p.split, out, s);
             }
             break;
         case RD_PATH_COLS:
         case RD_PATH_COLS_NARROW: {
             float* dst = p.split == 1 ? out : ws;
-            e = p.path == RD_PATH_COLS ? rd::launch_cols(p, x, outer, R, inner, dst, s)
-                                       : rd::launch_cols_narrow(p, x, outer, R, inner, dst, s);
+            e = p.path == RD_PATH_COLS
+                    ? rd::launch_cols(op, p, x, outer, R, inner, dst, s)
+                    : rd::launch_cols_narrow(op, p, x, outer, R, inner, dst, s);
             if (e == hipSuccess && p.split > 1)
-                e = rd::launch_slab_combine(ws, p.split, outer * inner, out, s);
+                e = rd::launch_slab_combine(op, ws, p.split, outer * inner, out, s);
             break;
         }
         default:
@@ -196,30 +198,35 @@ rd_status execute(const rd_plan& p, Device& dev, const float* x, int64_t outer, 
     return RD_OK;
 }
 
-rd_status sum_dim_checked(const float* x, int64_t outer, int64_t R, int64_t inner,
-                          float* out, hipStream_t stream) {
+rd_status reduce_checked(const float* x, int64_t outer, int64_t R, int64_t inner, int op,
+                         float* out, hipStream_t stream) {
     Device* dev = nullptr;
     rd_status st = current_device(&dev);
     if (st != RD_OK) return st;
     rd_plan plan;
-    st = make_plan(dev->cu, outer, R, inner, &plan);
+    st = make_plan(dev->cu, outer, R, inner, op, &plan);
     if (st != RD_OK) return st;
-    return execute(plan, *dev, x, outer, R, inner, out, stream);
+    return execute(plan, op, *dev, x, outer, R, inner, out, stream);
 }
+
+bool op_valid(int32_t op) { return op >= RD_OP_SUM && op <= RD_OP_MIN; }
 
 }  // namespace
 
 extern "C" {
 
-rd_status rd_sum_1d(const float* x, int64_t n, float* out, hipStream_t stream) {
+rd_status rd_reduce_1d(const float* x, int64_t n, int32_t op, float* out,
+                       hipStream_t stream) {
+    if (!op_valid(op)) return RD_ERR_INVALID_ARG;
     if (n < 0 || n > INT64_MAX / 4 || !out || !aligned4(out)) return RD_ERR_INVALID_ARG;
     if (n > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
     if (overlap(x, n, out, 1)) return RD_ERR_INVALID_ARG;
-    return sum_dim_checked(x, 1, n, 1, out, stream);
+    return reduce_checked(x, 1, n, 1, op, out, stream);
 }
 
-rd_status rd_sum_dim(const float* x, int64_t outer, int64_t R, int64_t inner, float* out,
-                     hipStream_t stream) {
+rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner, int32_t op,
+                        float* out, hipStream_t stream) {
+    if (!op_valid(op)) return RD_ERR_INVALID_ARG;
     if (outer < 0 || R < 0 || inner < 0) return RD_ERR_INVALID_ARG;
     const int64_t lim = INT64_MAX / 4;
     if (outer && inner && inner > lim / outer) return RD_ERR_INVALID_ARG;
@@ -230,7 +237,16 @@ rd_status rd_sum_dim(const float* x, int64_t outer, int64_t R, int64_t inner, fl
     if (!out || !aligned4(out)) return RD_ERR_INVALID_ARG;
     if (nin > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
     if (overlap(x, nin, out, nout)) return RD_ERR_INVALID_ARG;
-    return sum_dim_checked(x, outer, R, inner, out, stream);
+    return reduce_checked(x, outer, R, inner, op, out, stream);
+}
+
+rd_status rd_sum_1d(const float* x, int64_t n, float* out, hipStream_t stream) {
+    return rd_reduce_1d(x, n, RD_OP_SUM, out, stream);
+}
+
+rd_status rd_sum_dim(const float* x, int64_t outer, int64_t R, int64_t inner, float* out,
+                     hipStream_t stream) {
+    return rd_reduce_dim(x, outer, R, inner, RD_OP_SUM, out, stream);
 }
 
 const char* rd_status_string(rd_status status) {
@@ -254,7 +270,8 @@ int rd_version(void) {
 rd_status rd_plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
                       rd_plan* plan) {
     std::lock_guard<std::mutex> lock(g_tune_mu);
-    return rd::plan_dim(cu_count, outer, R, inner, g_tune_on ? &g_tune : nullptr, plan);
+    return rd::plan_dim(cu_count, outer, R, inner, RD_OP_SUM, g_tune_on ? &g_tune : nullptr,
+                        plan);
 }
 
 rd_status rd_plan_1d(int cu_count, int64_t n, rd_plan* plan) {
@@ -276,11 +293,11 @@ rd_status rd_tune_set(const rd_tune* tune) {
     return RD_OK;
 }
 
-int rd_tune_supported(int32_t path, int32_t group_or_col_waves, int32_t row_waves,
-                      int32_t unroll) {
-    if (path == RD_PATH_ROWS) return rd::rows_shape_supported(group_or_col_waves, unroll);
+int rd_tune_supported(int32_t op, int32_t path, int32_t group_or_col_waves,
+                      int32_t row_waves, int32_t unroll) {
+    if (path == RD_PATH_ROWS) return rd::rows_shape_supported(op, group_or_col_waves, unroll);
     if (path == RD_PATH_COLS)
-        return rd::cols_shape_supported(group_or_col_waves, row_waves, unroll);
+        return rd::cols_shape_supported(op, group_or_col_waves, row_waves, unroll);
     return 0;
 }
 

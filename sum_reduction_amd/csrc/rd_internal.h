@@ -20,30 +20,31 @@ constexpr int64_t kShortRow = 64;
 // workgroups have up to 1024 threads).
 constexpr int64_t kMaxBlocks = int64_t(1) << 20;
 
-// Planner (rd_plan.cpp).  `tune` may be null.
-rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
+// Planner (rd_plan.cpp).  `tune` may be null; `op` is an rd_op (it only
+// decides which kernel shapes exist).
+rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op,
                    const rd_tune* tune, rd_plan* plan);
 
 // Kernel launchers (rd_kernels.hip).  Each enqueues on `s` and returns the
-// error hipLaunchKernel reports for the launch.
-hipError_t launch_fill_zero(float* out, int64_t n, hipStream_t s);
-// ticket == nullptr: dst receives the piece sums (or the row sums when
+// error hipLaunchKernel reports for the launch; `op` is an rd_op.
+hipError_t launch_fill_start(int op, float* out, int64_t n, hipStream_t s);
+// ticket == nullptr: dst receives the piece results (or the row results when
 // p.split == 1); otherwise the last workgroup also combines them into out.
-hipError_t launch_rows(const rd_plan& p, const float* x, int64_t outer, int64_t R,
+hipError_t launch_rows(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
                        float* dst, uint32_t* ticket, float* out, hipStream_t s);
-hipError_t launch_rows_short(const float* x, int64_t outer, int64_t R, float* out,
+hipError_t launch_rows_short(int op, const float* x, int64_t outer, int64_t R, float* out,
                              hipStream_t s);
-hipError_t launch_rows_combine(const float* part, int64_t outer, int64_t P,
+hipError_t launch_rows_combine(int op, const float* part, int64_t outer, int64_t P,
                                float* out, hipStream_t s);
-hipError_t launch_cols(const rd_plan& p, const float* x, int64_t outer, int64_t R,
+hipError_t launch_cols(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
                        int64_t inner, float* dst, hipStream_t s);
-hipError_t launch_cols_narrow(const rd_plan& p, const float* x, int64_t outer,
+hipError_t launch_cols_narrow(int op, const rd_plan& p, const float* x, int64_t outer,
                               int64_t R, int64_t inner, float* dst, hipStream_t s);
-hipError_t launch_slab_combine(const float* slab, int64_t S, int64_t n, float* out,
+hipError_t launch_slab_combine(int op, const float* slab, int64_t S, int64_t n, float* out,
                                hipStream_t s);
 
-// Which kernel shapes this build instantiates (rd_kernels.hip).
-bool rows_shape_supported(int group, int unroll);
-bool cols_shape_supported(int col_waves, int row_waves, int unroll);
+// Which kernel shapes this build instantiates for an operator (rd_kernels.hip).
+bool rows_shape_supported(int op, int group, int unroll);
+bool cols_shape_supported(int op, int col_waves, int row_waves, int unroll);
 
 }  // namespace rd

@@ -1,4 +1,4 @@
-// rd_kernels.hip -- gfx950 (CDNA4) kernels of the fp32 sum reduction.
+// rd_kernels.hip -- gfx950 (CDNA4) kernels of the fp32 reductions.
 //
 // Prior art on the pages, and what is kept of it here:
 //  * "Seven-step reduction: 30x from one kernel", V4/V6/V7: add while loading,
@@ -6,7 +6,9 @@
 //    warp staged in shared memory, one result per block.  Kept as structure;
 //    the warp is a 64-lane wavefront here and its reduction a DPP/swizzle
 //    butterfly, and the block results go to a second, fixed-order pass (no
-//    float atomics), so results are bitwise reproducible.
+//    float atomics), so results are bitwise reproducible.  The same page
+//    names sum, max and the L2 norm as one primitive: the kernels take the
+//    operator (sum, sum of squares, maximum, minimum) as a parameter.
 //  * "High-Performance Reduction Kernels" README, ILP4 section: several
 //    independent accumulators and several 128-bit loads in flight per thread.
 //    Kept as U loads in flight per lane.  What limits loads in flight on
@@ -19,29 +21,29 @@
 //    not apply, because CDNA's global_load_dwordx4 only needs dword alignment.
 //
 // Loads.  Every 16-byte load is issued from a 4-byte-aligned address through
-// a 4-byte-aligned vector type (memcpy), which the compiler emits as one
+// a 4-byte-aligned vector type, which the compiler emits as one
 // global_load_dwordx4.  No head peeling: element k of a row always lands in
 // the same lane and accumulator, whatever the base address modulo 16, which
 // keeps the result independent of the input's address.
 //
-// Summation order (fixed for a given plan; every add is IEEE fp32):
-//  ROWS      a lane adds its k-th 16-byte chunk (interleaved or blocked
+// Order of the operations (fixed for a given plan; "fold" adds a term,
+// "join" combines two partial results, see Op below):
+//  ROWS      a lane folds its k-th 16-byte chunk (interleaved or blocked
 //            order, see rows_kernel) into float4 accumulator (k mod 2); the
 //            R % 4 tail elements go to acc[0].x of the row's lanes 0..2;
-//            a = acc[0] + acc[1], lane total = (a.x + a.y) + (a.z + a.w); then
-//            the wave butterfly, then the wave sums in wave order; then (if
-//            the row has several pieces) combine_row over the piece sums, in
-//            a second kernel or in the last workgroup of the first.
-//  COLS      wave (cw, rw) adds its k-th row, r0 + rw + k*RW, into float4
-//            accumulator (k mod 2); acc[0] + acc[1]; then the row phases in
-//            rw order; then (if split) the slabs in slab order.
+//            a = join(acc[0], acc[1]), lane result = join(join(a.x, a.y),
+//            join(a.z, a.w)); then the wave butterfly, then the wave results
+//            in wave order; then (if the row has several pieces) combine_row
+//            over the piece results, in a second kernel or in the last
+//            workgroup of the first.
+//  COLS      wave (cw, rw) folds its k-th row, r0 + rw + k*RW, into float4
+//            accumulator (k mod 2); join(acc[0], acc[1]); then the row phases
+//            in rw order; then (if split) the slabs in slab order.
 // U, the number of 16-byte loads a lane keeps in flight, is even and does not
 // change the order.  Two accumulators rather than U keep the kernels within
 // 64 VGPRs (8 waves per SIMD) while all U loads are issued before the first
-// add waits on one.
+// fold waits on one.
 #include <hip/hip_runtime.h>
-
-#include <type_traits>
 
 #include "rd_internal.h"
 
@@ -49,7 +51,6 @@ namespace rd {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
-
 typedef float v4f_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // Four floats from a 4-byte-aligned address: one global_load_dwordx4, with
@@ -65,6 +66,80 @@ __device__ __forceinline__ v4f load4(const float* p) {
     }
 }
 
+// ------------------------------------------------------------- operators
+// start: the value of an empty reduction; fold: one more term into a
+// partial result; join: two partial results into one.
+//  sum      0,     a + v,           a + b
+//  sum sq   0,     fma(v, v, a),    a + b      (one rounding per term)
+//  max      -Inf,  maximum(a, v),   maximum(a, b)
+//  min      +Inf,  minimum(a, v),   minimum(a, b)
+// maximum / minimum are IEEE 754-2019 (v_maximum3_f32 / v_minimum3_f32 on
+// gfx950): a NaN operand gives NaN and -0 < +0, so their result does not
+// depend on the order of the terms.
+template <int OP>
+struct Op;
+
+template <>
+struct Op<RD_OP_SUM> {
+    static __device__ __forceinline__ float start() { return 0.f; }
+    static __device__ __forceinline__ v4f fold(v4f a, v4f v) { return a + v; }
+    static __device__ __forceinline__ float fold(float a, float v) { return a + v; }
+    static __device__ __forceinline__ v4f join(v4f a, v4f b) { return a + b; }
+    static __device__ __forceinline__ float join(float a, float b) { return a + b; }
+};
+
+template <>
+struct Op<RD_OP_SUMSQ> {
+    static __device__ __forceinline__ float start() { return 0.f; }
+    static __device__ __forceinline__ v4f fold(v4f a, v4f v) {
+        return __builtin_elementwise_fma(v, v, a);
+    }
+    static __device__ __forceinline__ float fold(float a, float v) {
+        return __builtin_fmaf(v, v, a);
+    }
+    static __device__ __forceinline__ v4f join(v4f a, v4f b) { return a + b; }
+    static __device__ __forceinline__ float join(float a, float b) { return a + b; }
+};
+
+template <>
+struct Op<RD_OP_MAX> {
+    static __device__ __forceinline__ float start() { return -__builtin_inff(); }
+    static __device__ __forceinline__ v4f fold(v4f a, v4f v) {
+        return __builtin_elementwise_maximum(a, v);
+    }
+    static __device__ __forceinline__ float fold(float a, float v) {
+        return __builtin_elementwise_maximum(a, v);
+    }
+    static __device__ __forceinline__ v4f join(v4f a, v4f b) { return fold(a, b); }
+    static __device__ __forceinline__ float join(float a, float b) { return fold(a, b); }
+};
+
+template <>
+struct Op<RD_OP_MIN> {
+    static __device__ __forceinline__ float start() { return __builtin_inff(); }
+    static __device__ __forceinline__ v4f fold(v4f a, v4f v) {
+        return __builtin_elementwise_minimum(a, v);
+    }
+    static __device__ __forceinline__ float fold(float a, float v) {
+        return __builtin_elementwise_minimum(a, v);
+    }
+    static __device__ __forceinline__ v4f join(v4f a, v4f b) { return fold(a, b); }
+    static __device__ __forceinline__ float join(float a, float b) { return fold(a, b); }
+};
+
+template <int OP>
+__device__ __forceinline__ v4f start4() {
+    const float s = Op<OP>::start();
+    return v4f{s, s, s, s};
+}
+
+// The four lanes of a float4 partial result joined in a fixed order.
+template <int OP>
+__device__ __forceinline__ float join_lanes(v4f a) {
+    return Op<OP>::join(Op<OP>::join(a.x, a.y), Op<OP>::join(a.z, a.w));
+}
+
+// ------------------------------------------------- wave and block steps
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(
@@ -72,37 +147,40 @@ __device__ __forceinline__ float dpp(float v) {
                                            0xF, 0xF, false));
 }
 
-// Sum of v over the 64 lanes of a wavefront; every lane must be active.
+// Join of v over the 64 lanes of a wavefront; every lane must be active.
 // Butterfly: lane pairs at distance 1 and 2 (DPP quad_perm), quads paired by
 // mirroring 8 lanes (row_half_mirror), 8-lane halves paired by mirroring 16
 // lanes (row_mirror), 16-lane rows paired by a swizzle swap of 16, and the
-// two 32-lane halves added through lanes 0 and 32.  Each step adds a lane's
-// value to an equal-rank partner's, so every lane ends with the same bits.
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);  // row_half_mirror
-    v += dpp<0x140>(v);  // row_mirror
-    v += __builtin_bit_cast(
-        float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+// two 32-lane halves joined through lanes 0 and 32.  Each step joins a
+// lane's value with an equal-rank partner's, and every join is commutative,
+// so every lane ends with the same bits.
+template <int OP>
+__device__ __forceinline__ float wave_reduce(float v) {
+    v = Op<OP>::join(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = Op<OP>::join(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = Op<OP>::join(v, dpp<0x141>(v));  // row_half_mirror
+    v = Op<OP>::join(v, dpp<0x140>(v));  // row_mirror
+    v = Op<OP>::join(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(
+                                                      __builtin_bit_cast(int, v), 0x401F)));
     const float lo = __builtin_bit_cast(
         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
     const float hi = __builtin_bit_cast(
         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    return lo + hi;
+    return Op<OP>::join(lo, hi);
 }
 
-// Sum over a kBlock-thread workgroup, valid in thread 0: wave butterflies,
-// then the wave sums in wave order.  The caller syncs before reusing `lds`.
-__device__ __forceinline__ float block_sum(float v, float* lds) {
-    v = wave_sum(v);
+// Join over a kBlock-thread workgroup, valid in thread 0: wave butterflies,
+// then the wave results in wave order.  The caller syncs before reusing lds.
+template <int OP>
+__device__ __forceinline__ float block_reduce(float v, float* lds) {
+    v = wave_reduce<OP>(v);
     if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = v;
     __syncthreads();
-    float t = 0.f;
+    float t = Op<OP>::start();
     if (threadIdx.x == 0) {
         t = lds[0];
 #pragma unroll
-        for (int k = 1; k < kBlock / kWave; ++k) t += lds[k];
+        for (int k = 1; k < kBlock / kWave; ++k) t = Op<OP>::join(t, lds[k]);
     }
     return t;
 }
@@ -119,15 +197,16 @@ __device__ __forceinline__ int64_t xcd_block(uint32_t nxcd) {
     return int64_t(x) * q + (x < r ? x : r) + i;
 }
 
-// out_o = the sum of the P piece sums of one row: lane t adds pieces t,
-// t + 256, ... in order, then the workgroup reduction.  Used by the second
-// pass and by the last workgroup of a fused first pass, so both give the same
-// bits.  Every thread of the workgroup must call it.
+// out_o = the join of the P piece results of one row: lane t joins pieces
+// t, t + 256, ... in order, then the workgroup reduction.  Used by the
+// second pass and by the last workgroup of a fused first pass, so both give
+// the same bits.  Every thread of the workgroup must call it.
+template <int OP>
 __device__ __forceinline__ void combine_row(const float* __restrict__ part, int64_t P,
                                             float* __restrict__ out_o, float* lds) {
-    float t = 0.f;
-    for (int64_t k = threadIdx.x; k < P; k += kBlock) t += part[k];
-    t = block_sum(t, lds);
+    float t = Op<OP>::start();
+    for (int64_t k = threadIdx.x; k < P; k += kBlock) t = Op<OP>::join(t, part[k]);
+    t = block_reduce<OP>(t, lds);
     if (threadIdx.x == 0) *out_o = t;
     __syncthreads();
 }
@@ -136,22 +215,22 @@ __device__ __forceinline__ void combine_row(const float* __restrict__ part, int6
 // Each group of G lanes (one wave, or the whole workgroup) reduces one row
 // piece: segment seg = (row o, piece p), o = seg / P, p = seg % P.  With
 // P == 1, dst is the output (one value per row); otherwise dst holds the
-// outer x P piece sums for rows_combine_kernel.  The full 1D reduce is the
-// case outer == 1.
+// outer x P piece results for rows_combine_kernel.  The full 1D reduce is
+// the case outer == 1.
 // Chunk order of the pieces of a row (16-byte chunks, nvec = R / 4 of them):
 //   interleaved  lane g = p * G + lane takes chunks g, g + P*G, g + 2*P*G, ...
 //   blocked      piece p owns the contiguous chunks [p*C, (p+1)*C) with
 //                C = ceil(nvec / P) rounded up to a multiple of G, and its
 //                lane takes p*C + lane, p*C + lane + G, ... (each group streams
 //                one contiguous stretch of memory)
-// Fused combine (ticket != null, P > 1): after storing its piece sums, each
-// workgroup publishes them (device-scope release) and takes a ticket from an
-// integer counter; the workgroup that draws the last ticket acquires, sums
-// every row's pieces with combine_row into out[0 .. outer), and resets the
-// counter to 0 for the next call on the same stream.  The counter must be 0
-// at launch.  No float atomics: only the ticket is atomic, and the combine
-// order is the second pass's.
-template <int G, int U, bool NT>
+// Fused combine (ticket != null, P > 1): after storing its piece results,
+// each workgroup publishes them (device-scope release) and takes a ticket
+// from an integer counter; the workgroup that draws the last ticket acquires,
+// joins every row's pieces with combine_row into out[0 .. outer), and resets
+// the counter to 0 for the next call on the same stream.  The counter must
+// be 0 at launch.  Only the ticket is atomic, and the combine order is the
+// second pass's.
+template <int OP, int G, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ x,
                                                       int64_t R, int64_t nseg,
                                                       int64_t P, int32_t blocked,
@@ -170,7 +249,7 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
     const int64_t gstride = int64_t(gridDim.x) * kGroups;
     for (int64_t first = xcd_block(nxcd) * kGroups; first < nseg; first += gstride) {
         const int64_t seg = first + threadIdx.x / G;  // uniform per group
-        float total = 0.f;
+        float total = Op<OP>::start();
         if (seg < nseg) {
             const int64_t o = seg / P;
             const int64_t piece = seg - o * P;
@@ -179,27 +258,27 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
             int64_t j = blocked ? piece * span + gl : g;
             int64_t end = nvec;
             if (blocked && piece * span + span < nvec) end = piece * span + span;
-            v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            v4f acc[2] = {start4<OP>(), start4<OP>()};
             for (; j + (U - 1) * L < end; j += U * L) {
                 v4f v[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) v[u] = load4<NT>(row + 4 * (j + u * L));
 #pragma unroll
-                for (int u = 0; u < U; ++u) acc[u & 1] += v[u];
+                for (int u = 0; u < U; ++u) acc[u & 1] = Op<OP>::fold(acc[u & 1], v[u]);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (j + u * L < end) acc[u & 1] += load4<NT>(row + 4 * (j + u * L));
-            if (g < tail) acc[0].x += row[4 * nvec + g];
-            const v4f a = acc[0] + acc[1];
-            total = (a.x + a.y) + (a.z + a.w);
+                if (j + u * L < end)
+                    acc[u & 1] = Op<OP>::fold(acc[u & 1], load4<NT>(row + 4 * (j + u * L)));
+            if (g < tail) acc[0].x = Op<OP>::fold(acc[0].x, row[4 * nvec + g]);
+            total = join_lanes<OP>(Op<OP>::join(acc[0], acc[1]));
         }
         if constexpr (G == kBlock) {
-            total = block_sum(total, lds);
+            total = block_reduce<OP>(total, lds);
             if (threadIdx.x == 0) dst[seg] = total;
             __syncthreads();
         } else {
-            total = wave_sum(total);
+            total = wave_reduce<OP>(total);
             if (gl == 0 && seg < nseg) dst[seg] = total;
         }
     }
@@ -208,7 +287,7 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
         // fence in every wave would write back and invalidate the L2 of
         // each XCD thousands of times under the still-running stream.
         __shared__ uint32_t last;
-        __syncthreads();  // the workgroup's piece sums are stored
+        __syncthreads();  // the workgroup's piece results are stored
         if (threadIdx.x == 0)
             last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELEASE,
                                           __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
@@ -216,7 +295,8 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
         if (last) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             const int64_t outer = nseg / P;
-            for (int64_t o = 0; o < outer; ++o) combine_row(dst + o * P, P, out + o, lds);
+            for (int64_t o = 0; o < outer; ++o)
+                combine_row<OP>(dst + o * P, P, out + o, lds);
             if (threadIdx.x == 0)
                 __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -225,28 +305,30 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
 
 // Rows shorter than a wave's worth of chunks: one lane per row, 16-byte
 // loads along the row, then the R % 4 tail in order.
+template <int OP>
 __global__ __launch_bounds__(kBlock) void rows_short_kernel(const float* __restrict__ x,
                                                             int64_t outer, int64_t R,
                                                             float* __restrict__ out) {
     const int64_t stride = int64_t(gridDim.x) * kBlock;
     for (int64_t o = int64_t(blockIdx.x) * kBlock + threadIdx.x; o < outer; o += stride) {
         const float* row = x + o * R;
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        v4f acc = start4<OP>();
         int64_t k = 0;
-        for (; k + 4 <= R; k += 4) acc += load4<false>(row + k);
-        float t = (acc.x + acc.y) + (acc.z + acc.w);
-        for (; k < R; ++k) t += row[k];
+        for (; k + 4 <= R; k += 4) acc = Op<OP>::fold(acc, load4<false>(row + k));
+        float t = join_lanes<OP>(acc);
+        for (; k < R; ++k) t = Op<OP>::fold(t, row[k]);
         out[o] = t;
     }
 }
 
-// Second pass of ROWS: out[o] = combine_row over the P piece sums of row o.
+// Second pass of ROWS: out[o] = combine_row over the P piece results of row o.
+template <int OP>
 __global__ __launch_bounds__(kBlock) void rows_combine_kernel(const float* __restrict__ part,
                                                               int64_t outer, int64_t P,
                                                               float* __restrict__ out) {
     __shared__ float lds[kBlock / kWave];
     for (int64_t o = blockIdx.x; o < outer; o += gridDim.x)
-        combine_row(part + o * P, P, out + o, lds);
+        combine_row<OP>(part + o * P, P, out + o, lds);
 }
 
 // ----------------------------------------------------------------- COLS
@@ -256,10 +338,10 @@ __global__ __launch_bounds__(kBlock) void rows_combine_kernel(const float* __res
 // that holds the last 1..3 columns of a row loads the row's last 4 floats
 // instead (start inner - 4) and keeps only its own, so no load leaves the
 // row and no lane diverges.  Wave (cw, rw) takes the rows r0 + rw + k*RW of
-// the slab, U rows in flight; the RW partial sums meet in LDS.  With S == 1,
-// dst is the output; otherwise dst is [S][outer][inner] for
+// the slab, U rows in flight; the RW partial results meet in LDS.  With
+// S == 1, dst is the output; otherwise dst is [S][outer][inner] for
 // slab_combine_kernel.  Needs inner >= 4.
-template <int CW, int RW, int U, bool NT>
+template <int OP, int CW, int RW, int U, bool NT>
 __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
     const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t ntiles,
     int64_t S, int64_t rps, float* __restrict__ dst, uint32_t nxcd) {
@@ -280,7 +362,7 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
         const int64_t r0 = s * rps + rw;
         const int64_t r1 = (s + 1) * rps < R ? (s + 1) * rps : R;
         const int64_t m = r0 < r1 ? (r1 - r0 + RW - 1) / RW : 0;
-        v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        v4f acc[2] = {start4<OP>(), start4<OP>()};
         if (active) {
             const float* p = x + (o * R + r0) * inner + cl;
             const int64_t step = RW * inner;
@@ -290,20 +372,21 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
 #pragma unroll
                 for (int u = 0; u < U; ++u) v[u] = load4<NT>(p + u * step);
 #pragma unroll
-                for (int u = 0; u < U; ++u) acc[u & 1] += v[u];
+                for (int u = 0; u < U; ++u) acc[u & 1] = Op<OP>::fold(acc[u & 1], v[u]);
                 p += U * step;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (k + u < m) acc[u & 1] += load4<NT>(p + u * step);
+                if (k + u < m) acc[u & 1] = Op<OP>::fold(acc[u & 1], load4<NT>(p + u * step));
         }
-        v4f a = acc[0] + acc[1];
+        v4f a = Op<OP>::join(acc[0], acc[1]);
         if constexpr (RW > 1) {
             if (rw > 0) lds[((rw - 1) * CW + cw) * kWave + lane] = a;
             __syncthreads();
             if (rw == 0) {
 #pragma unroll
-                for (int q = 1; q < RW; ++q) a += lds[((q - 1) * CW + cw) * kWave + lane];
+                for (int q = 1; q < RW; ++q)
+                    a = Op<OP>::join(a, lds[((q - 1) * CW + cw) * kWave + lane]);
             }
             __syncthreads();
         }
@@ -317,6 +400,7 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
 
 // inner in {2, 3} (or any inner): one lane per output of one slab, rows taken
 // round robin into 4 accumulators, the slab's last R % 4 rows into the first.
+template <int OP>
 __global__ __launch_bounds__(kBlock) void cols_narrow_kernel(const float* __restrict__ x,
                                                              int64_t outer, int64_t R,
                                                              int64_t inner, int64_t S,
@@ -333,40 +417,43 @@ __global__ __launch_bounds__(kBlock) void cols_narrow_kernel(const float* __rest
         const int64_t r0 = s * rps;
         const int64_t r1 = r0 + rps < R ? r0 + rps : R;
         const float* p = x + (o * R + r0) * inner + i;
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        float a0 = Op<OP>::start(), a1 = a0, a2 = a0, a3 = a0;
         int64_t r = r0;
         for (; r + 4 <= r1; r += 4) {
-            a0 += p[0];
-            a1 += p[inner];
-            a2 += p[2 * inner];
-            a3 += p[3 * inner];
+            a0 = Op<OP>::fold(a0, p[0]);
+            a1 = Op<OP>::fold(a1, p[inner]);
+            a2 = Op<OP>::fold(a2, p[2 * inner]);
+            a3 = Op<OP>::fold(a3, p[3 * inner]);
             p += 4 * inner;
         }
         for (; r < r1; ++r) {
-            a0 += p[0];
+            a0 = Op<OP>::fold(a0, p[0]);
             p += inner;
         }
-        dst[e] = (a0 + a1) + (a2 + a3);
+        dst[e] = Op<OP>::join(Op<OP>::join(a0, a1), Op<OP>::join(a2, a3));
     }
 }
 
-// Second pass of a split along R: out[e] = slab[0][e] + slab[1][e] + ...
+// Second pass of a split along R: out[e] = join of slab[0][e], slab[1][e], ...
+template <int OP>
 __global__ __launch_bounds__(kBlock) void slab_combine_kernel(const float* __restrict__ slab,
                                                               int64_t S, int64_t n,
                                                               float* __restrict__ out) {
     const int64_t stride = int64_t(gridDim.x) * kBlock;
     for (int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x; e < n; e += stride) {
         float t = slab[e];
-        for (int64_t s = 1; s < S; ++s) t += slab[s * n + e];
+        for (int64_t s = 1; s < S; ++s) t = Op<OP>::join(t, slab[s * n + e]);
         out[e] = t;
     }
 }
 
-__global__ __launch_bounds__(kBlock) void fill_zero_kernel(float* __restrict__ out,
-                                                           int64_t n) {
+// R == 0: every output is the operator's start value.
+template <int OP>
+__global__ __launch_bounds__(kBlock) void fill_start_kernel(float* __restrict__ out,
+                                                            int64_t n) {
     const int64_t stride = int64_t(gridDim.x) * kBlock;
     for (int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x; e < n; e += stride)
-        out[e] = 0.f;
+        out[e] = Op<OP>::start();
 }
 
 // ------------------------------------------------------------- launching
@@ -390,112 +477,113 @@ int64_t grid_for(int64_t items) {
     return b > kMaxBlocks ? kMaxBlocks : b;
 }
 
-// Instantiated kernel shapes.
-constexpr int kRowGroups[] = {64, 256};
-constexpr int kUnrolls[] = {2, 4, 8, 16};
-struct ColShape {
-    int cw, rw;
+// Instantiated kernel shapes.  The sum has every tuning shape; the other
+// operators have the shapes the planner picks by default (U = 8 or 16 on
+// ROWS, one row phase and U = 4 on COLS), each with and without the
+// streaming hint.
+constexpr bool unroll_built(int u) { return u == 2 || u == 4 || u == 8 || u == 16; }
+
+constexpr bool rows_built(int op, int g, int u) {
+    if (g != kWave && g != kBlock) return false;
+    return op == RD_OP_SUM ? unroll_built(u) : (u == 8 || u == 16);
+}
+
+constexpr bool col_shape_built(int cw, int rw) {
+    return (cw == 1 && (rw == 1 || rw == 2 || rw == 4 || rw == 8 || rw == 16)) ||
+           (cw == 2 && (rw == 1 || rw == 2 || rw == 4 || rw == 8)) ||
+           (cw == 4 && (rw == 1 || rw == 2 || rw == 4)) || (cw == 8 && (rw == 1 || rw == 2)) ||
+           (cw == 16 && rw == 1);
+}
+
+constexpr bool cols_built(int op, int cw, int rw, int u) {
+    if (op == RD_OP_SUM) return col_shape_built(cw, rw) && unroll_built(u);
+    return rw == 1 && (cw == 1 || cw == 2 || cw == 4 || cw == 8) && u == 4;
+}
+
+constexpr bool op_valid(int op) {
+    return op == RD_OP_SUM || op == RD_OP_SUMSQ || op == RD_OP_MAX || op == RD_OP_MIN;
+}
+
+struct RowsArgs {
+    const float* x;
+    int64_t outer, R;
+    float* dst;
+    uint32_t* ticket;
+    float* out;
 };
-constexpr ColShape kColShapes[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {1, 16}, {2, 1},
-                                   {2, 2}, {2, 4}, {2, 8}, {4, 1}, {4, 2}, {4, 4},
-                                   {8, 1}, {8, 2}, {16, 1}};
 
-template <int G, int U, bool NT>
-hipError_t rows_dispatch_u(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                           float* dst, uint32_t* ticket, float* out, hipStream_t s) {
-    return launch(rows_kernel<G, U, NT>, p.blocks, kBlock, s, x, R, outer * p.split,
-                  p.split, int32_t(p.order == RD_ORDER_BLOCKED), dst, uint32_t(p.nxcd),
-                  ticket, out);
+template <int OP, int G, int U, bool NT>
+hipError_t rows_go(const rd_plan& p, const RowsArgs& a, hipStream_t s) {
+    if constexpr (rows_built(OP, G, U)) {
+        return launch(rows_kernel<OP, G, U, NT>, p.blocks, kBlock, s, a.x, a.R,
+                      a.outer * p.split, p.split, int32_t(p.order == RD_ORDER_BLOCKED), a.dst,
+                      uint32_t(p.nxcd), a.ticket, a.out);
+    } else {
+        return hipErrorInvalidValue;
+    }
 }
 
-template <int G, bool NT>
-hipError_t rows_dispatch(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                         float* dst, uint32_t* ticket, float* out, hipStream_t s) {
+template <int OP, int G, bool NT>
+hipError_t rows_u(const rd_plan& p, const RowsArgs& a, hipStream_t s) {
     switch (p.unroll) {
-        case 2: return rows_dispatch_u<G, 2, NT>(p, x, outer, R, dst, ticket, out, s);
-        case 4: return rows_dispatch_u<G, 4, NT>(p, x, outer, R, dst, ticket, out, s);
-        case 8: return rows_dispatch_u<G, 8, NT>(p, x, outer, R, dst, ticket, out, s);
-        case 16: return rows_dispatch_u<G, 16, NT>(p, x, outer, R, dst, ticket, out, s);
+        case 2: return rows_go<OP, G, 2, NT>(p, a, s);
+        case 4: return rows_go<OP, G, 4, NT>(p, a, s);
+        case 8: return rows_go<OP, G, 8, NT>(p, a, s);
+        case 16: return rows_go<OP, G, 16, NT>(p, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int CW, int RW, int U, bool NT>
-hipError_t cols_dispatch_u(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                           int64_t inner, float* dst, hipStream_t s) {
-    const int64_t ntiles = ((inner + 3) / 4 + CW * kWave - 1) / (CW * kWave);
-    return launch(cols_kernel<CW, RW, U, NT>, p.blocks, kWave * CW * RW, s, x, outer, R,
-                  inner, ntiles, p.split, p.rows_per_split, dst, uint32_t(p.nxcd));
-}
-
-template <int CW, int RW, bool NT>
-hipError_t cols_dispatch_nt(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                            int64_t inner, float* dst, hipStream_t s) {
-    switch (p.unroll) {
-        case 2: return cols_dispatch_u<CW, RW, 2, NT>(p, x, outer, R, inner, dst, s);
-        case 4: return cols_dispatch_u<CW, RW, 4, NT>(p, x, outer, R, inner, dst, s);
-        case 8: return cols_dispatch_u<CW, RW, 8, NT>(p, x, outer, R, inner, dst, s);
-        case 16: return cols_dispatch_u<CW, RW, 16, NT>(p, x, outer, R, inner, dst, s);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <int CW, int RW>
-hipError_t cols_dispatch(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                         int64_t inner, float* dst, hipStream_t s) {
-    if (p.nontemporal) return cols_dispatch_nt<CW, RW, true>(p, x, outer, R, inner, dst, s);
-    return cols_dispatch_nt<CW, RW, false>(p, x, outer, R, inner, dst, s);
-}
-
-}  // namespace
-
-bool rows_shape_supported(int group, int unroll) {
-    bool g = false, u = false;
-    for (int v : kRowGroups) g |= v == group;
-    for (int v : kUnrolls) u |= v == unroll;
-    return g && u;
-}
-
-bool cols_shape_supported(int col_waves, int row_waves, int unroll) {
-    bool c = false, u = false;
-    for (const ColShape& v : kColShapes) c |= v.cw == col_waves && v.rw == row_waves;
-    for (int v : kUnrolls) u |= v == unroll;
-    return c && u;
-}
-
-hipError_t launch_fill_zero(float* out, int64_t n, hipStream_t s) {
-    return launch(fill_zero_kernel, grid_for(n), kBlock, s, out, n);
-}
-
-hipError_t launch_rows(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       float* dst, uint32_t* ticket, float* out, hipStream_t s) {
+template <int OP>
+hipError_t rows_op(const rd_plan& p, const RowsArgs& a, hipStream_t s) {
     if (p.group == kBlock)
-        return p.nontemporal
-                   ? rows_dispatch<kBlock, true>(p, x, outer, R, dst, ticket, out, s)
-                   : rows_dispatch<kBlock, false>(p, x, outer, R, dst, ticket, out, s);
+        return p.nontemporal ? rows_u<OP, kBlock, true>(p, a, s)
+                             : rows_u<OP, kBlock, false>(p, a, s);
     if (p.group == kWave)
-        return p.nontemporal
-                   ? rows_dispatch<kWave, true>(p, x, outer, R, dst, ticket, out, s)
-                   : rows_dispatch<kWave, false>(p, x, outer, R, dst, ticket, out, s);
+        return p.nontemporal ? rows_u<OP, kWave, true>(p, a, s)
+                             : rows_u<OP, kWave, false>(p, a, s);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_rows_short(const float* x, int64_t outer, int64_t R, float* out,
-                             hipStream_t s) {
-    return launch(rows_short_kernel, grid_for(outer), kBlock, s, x, outer, R, out);
+struct ColsArgs {
+    const float* x;
+    int64_t outer, R, inner;
+    float* dst;
+};
+
+template <int OP, int CW, int RW, int U, bool NT>
+hipError_t cols_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
+    if constexpr (cols_built(OP, CW, RW, U)) {
+        const int64_t ntiles = ((a.inner + 3) / 4 + CW * kWave - 1) / (CW * kWave);
+        return launch(cols_kernel<OP, CW, RW, U, NT>, p.blocks, kWave * CW * RW, s, a.x,
+                      a.outer, a.R, a.inner, ntiles, p.split, p.rows_per_split, a.dst,
+                      uint32_t(p.nxcd));
+    } else {
+        return hipErrorInvalidValue;
+    }
 }
 
-hipError_t launch_rows_combine(const float* part, int64_t outer, int64_t P, float* out,
-                               hipStream_t s) {
-    const int64_t blocks = outer < kMaxBlocks ? outer : kMaxBlocks;
-    return launch(rows_combine_kernel, blocks, kBlock, s, part, outer, P, out);
+template <int OP, int CW, int RW, bool NT>
+hipError_t cols_u(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
+    switch (p.unroll) {
+        case 2: return cols_go<OP, CW, RW, 2, NT>(p, a, s);
+        case 4: return cols_go<OP, CW, RW, 4, NT>(p, a, s);
+        case 8: return cols_go<OP, CW, RW, 8, NT>(p, a, s);
+        case 16: return cols_go<OP, CW, RW, 16, NT>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
-hipError_t launch_cols(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       int64_t inner, float* dst, hipStream_t s) {
+template <int OP, int CW, int RW>
+hipError_t cols_nt(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
+    return p.nontemporal ? cols_u<OP, CW, RW, true>(p, a, s)
+                         : cols_u<OP, CW, RW, false>(p, a, s);
+}
+
+template <int OP>
+hipError_t cols_op(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
 #define RD_COLS_CASE(CW, RW) \
-    if (p.col_waves == CW && p.row_waves == RW) \
-        return cols_dispatch<CW, RW>(p, x, outer, R, inner, dst, s);
+    if (p.col_waves == CW && p.row_waves == RW) return cols_nt<OP, CW, RW>(p, a, s);
     RD_COLS_CASE(1, 1)
     RD_COLS_CASE(1, 2)
     RD_COLS_CASE(1, 4)
@@ -515,15 +603,91 @@ hipError_t launch_cols(const rd_plan& p, const float* x, int64_t outer, int64_t 
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_cols_narrow(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                              int64_t inner, float* dst, hipStream_t s) {
-    return launch(cols_narrow_kernel, p.blocks, kBlock, s, x, outer, R, inner, p.split,
+// Calls F<OP>(args...) for the runtime operator op.
+#define RD_BY_OP(op, F, ...)                                  \
+    switch (op) {                                             \
+        case RD_OP_SUM: return F<RD_OP_SUM>(__VA_ARGS__);     \
+        case RD_OP_SUMSQ: return F<RD_OP_SUMSQ>(__VA_ARGS__); \
+        case RD_OP_MAX: return F<RD_OP_MAX>(__VA_ARGS__);     \
+        case RD_OP_MIN: return F<RD_OP_MIN>(__VA_ARGS__);     \
+        default: return hipErrorInvalidValue;                 \
+    }
+
+template <int OP>
+hipError_t fill_go(float* out, int64_t n, hipStream_t s) {
+    return launch(fill_start_kernel<OP>, grid_for(n), kBlock, s, out, n);
+}
+
+template <int OP>
+hipError_t rows_short_go(const float* x, int64_t outer, int64_t R, float* out,
+                         hipStream_t s) {
+    return launch(rows_short_kernel<OP>, grid_for(outer), kBlock, s, x, outer, R, out);
+}
+
+template <int OP>
+hipError_t rows_combine_go(const float* part, int64_t outer, int64_t P, float* out,
+                           hipStream_t s) {
+    const int64_t blocks = outer < kMaxBlocks ? outer : kMaxBlocks;
+    return launch(rows_combine_kernel<OP>, blocks, kBlock, s, part, outer, P, out);
+}
+
+template <int OP>
+hipError_t cols_narrow_go(const rd_plan& p, const float* x, int64_t outer, int64_t R,
+                          int64_t inner, float* dst, hipStream_t s) {
+    return launch(cols_narrow_kernel<OP>, p.blocks, kBlock, s, x, outer, R, inner, p.split,
                   p.rows_per_split, dst);
 }
 
-hipError_t launch_slab_combine(const float* slab, int64_t S, int64_t n, float* out,
+template <int OP>
+hipError_t slab_combine_go(const float* slab, int64_t S, int64_t n, float* out,
+                           hipStream_t s) {
+    return launch(slab_combine_kernel<OP>, grid_for(n), kBlock, s, slab, S, n, out);
+}
+
+}  // namespace
+
+bool rows_shape_supported(int op, int group, int unroll) {
+    return op_valid(op) && rows_built(op, group, unroll);
+}
+
+bool cols_shape_supported(int op, int col_waves, int row_waves, int unroll) {
+    return op_valid(op) && cols_built(op, col_waves, row_waves, unroll);
+}
+
+hipError_t launch_fill_start(int op, float* out, int64_t n, hipStream_t s) {
+    RD_BY_OP(op, fill_go, out, n, s)
+}
+
+hipError_t launch_rows(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
+                       float* dst, uint32_t* ticket, float* out, hipStream_t s) {
+    const RowsArgs a{x, outer, R, dst, ticket, out};
+    RD_BY_OP(op, rows_op, p, a, s)
+}
+
+hipError_t launch_rows_short(int op, const float* x, int64_t outer, int64_t R, float* out,
+                             hipStream_t s) {
+    RD_BY_OP(op, rows_short_go, x, outer, R, out, s)
+}
+
+hipError_t launch_rows_combine(int op, const float* part, int64_t outer, int64_t P,
+                               float* out, hipStream_t s) {
+    RD_BY_OP(op, rows_combine_go, part, outer, P, out, s)
+}
+
+hipError_t launch_cols(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
+                       int64_t inner, float* dst, hipStream_t s) {
+    const ColsArgs a{x, outer, R, inner, dst};
+    RD_BY_OP(op, cols_op, p, a, s)
+}
+
+hipError_t launch_cols_narrow(int op, const rd_plan& p, const float* x, int64_t outer,
+                              int64_t R, int64_t inner, float* dst, hipStream_t s) {
+    RD_BY_OP(op, cols_narrow_go, p, x, outer, R, inner, dst, s)
+}
+
+hipError_t launch_slab_combine(int op, const float* slab, int64_t S, int64_t n, float* out,
                                hipStream_t s) {
-    return launch(slab_combine_kernel, grid_for(n), kBlock, s, slab, S, n, out);
+    RD_BY_OP(op, slab_combine_go, slab, S, n, out, s)
 }
 
 }  // namespace rd

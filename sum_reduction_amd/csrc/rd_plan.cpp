@@ -45,7 +45,8 @@ int32_t nxcd_for(int cu_count) {
     return (cu_count >= 8 && cu_count % 8 == 0) ? 8 : 1;
 }
 
-rd_status plan_rows(int cu, int64_t outer, int64_t R, const rd_tune* t, rd_plan* p) {
+rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
+                    rd_plan* p) {
     const bool forced = t && (t->group || t->unroll || t->split || t->order || t->combine);
     if (R < kShortRow && !forced) {
         p->path = RD_PATH_ROWS_SHORT;
@@ -62,7 +63,7 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, const rd_tune* t, rd_plan*
     p->group = (t && t->group) ? t->group : (R >= 4096 ? kBlock : kWave);
     p->unroll = (t && t->unroll) ? t->unroll
                                  : (p->group == kBlock ? kRowsUnrollBlock : kRowsUnrollWave);
-    if (!rows_shape_supported(p->group, p->unroll)) return RD_ERR_INVALID_ARG;
+    if (!rows_shape_supported(op, p->group, p->unroll)) return RD_ERR_INVALID_ARG;
     p->order = (t && t->order) ? t->order : RD_ORDER_BLOCKED;
     if (p->order != RD_ORDER_INTERLEAVED && p->order != RD_ORDER_BLOCKED)
         return RD_ERR_INVALID_ARG;
@@ -113,8 +114,8 @@ void split_rows(int64_t R, int64_t S, rd_plan* p) {
     p->split = ceil_div(R, rps);
 }
 
-rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, const rd_tune* t,
-                    rd_plan* p) {
+rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
+                    const rd_tune* t, rd_plan* p) {
     if (inner < 4) {
         // one lane per output; only the split along R adds parallelism
         p->path = RD_PATH_COLS_NARROW;
@@ -154,7 +155,7 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, const rd_tu
     p->col_waves = (t && t->col_waves) ? t->col_waves : cw;
     p->row_waves = (t && t->row_waves) ? t->row_waves : 1;
     p->unroll = (t && t->unroll) ? t->unroll : kColsUnroll;
-    if (!cols_shape_supported(p->col_waves, p->row_waves, p->unroll))
+    if (!cols_shape_supported(op, p->col_waves, p->row_waves, p->unroll))
         return RD_ERR_INVALID_ARG;
     if (!nontemporal_choice(t, true, &p->nontemporal)) return RD_ERR_INVALID_ARG;
     p->block_threads = kWave * p->col_waves * p->row_waves;
@@ -192,10 +193,11 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, const rd_tu
 
 }  // namespace
 
-rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
+rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op,
                    const rd_tune* tune, rd_plan* plan) {
     if (!plan || cu_count < 1 || outer < 0 || R < 0 || inner < 0)
         return RD_ERR_INVALID_ARG;
+    if (op < RD_OP_SUM || op > RD_OP_MIN) return RD_ERR_INVALID_ARG;
     memset(plan, 0, sizeof(*plan));
     // outer * R * inner * 4 must be representable
     const int64_t lim = INT64_MAX / 4;
@@ -219,8 +221,8 @@ rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
         if (plan->blocks > kMaxBlocks) plan->blocks = kMaxBlocks;
         return RD_OK;
     }
-    if (inner == 1) return plan_rows(cu_count, outer, R, tune, plan);
-    return plan_cols(cu_count, outer, R, inner, tune, plan);
+    if (inner == 1) return plan_rows(cu_count, outer, R, op, tune, plan);
+    return plan_cols(cu_count, outer, R, inner, op, tune, plan);
 }
 
 }  // namespace rd

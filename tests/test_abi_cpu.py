@@ -24,9 +24,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("rd_sum_1d", "rd_sum_dim", "rd_status_string", "rd_last_hip_error",
-                 "rd_version", "rd_plan_dim", "rd_plan_1d", "rd_tune_set",
-                 "rd_tune_supported"):
+    for want in ("rd_sum_1d", "rd_sum_dim", "rd_reduce_1d", "rd_reduce_dim",
+                 "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
+                 "rd_plan_1d", "rd_tune_set", "rd_tune_supported"):
         assert want in names
 
 
@@ -87,6 +87,18 @@ def test_dim_invalid_arguments(lib, host_buf):
     ]
     for x, o_, R, i, out_ in cases:
         assert lib.rd_sum_dim(x, o_, R, i, out_, None) == INVALID, (o_, R, i)
+
+
+def test_reduce_rejects_unknown_operator(lib, host_buf):
+    base, _ = host_buf
+    out = base + 4 * 40
+    for op in (-1, 4, 99):
+        assert lib.rd_reduce_1d(base, 4, op, out, None) == INVALID
+        assert lib.rd_reduce_dim(base, 2, 2, 2, op, out, None) == INVALID
+    # and the other argument checks hold for every operator
+    for op in range(4):
+        assert lib.rd_reduce_1d(base, -1, op, out, None) == INVALID
+        assert lib.rd_reduce_dim(base + 1, 2, 2, 2, op, out, None) == INVALID
 
 
 def test_empty_output_needs_nothing(lib):

@@ -1,0 +1,216 @@
+"""GPU parity of the other reductions (sum of squares, maximum, minimum),
+through rd_reduce_1d / rd_reduce_dim, against the oracle.
+
+Maximum and minimum are exact, so they must match the oracle bit for bit on
+any data.  The sum of squares is bit-exact on small integers (values in
+[-2, 2]: every partial sum is an integer below 2^24) and within
+1e-5 * sum x^2 + 1e-6 on random data.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sum_reduction_amd as rd
+import workloads
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+OPS3 = ("sumsq", "max", "min")
+
+
+@pytest.fixture(autouse=True)
+def _clear_tuning():
+    rd.rd_tune_set(None)
+    yield
+    rd.rd_tune_set(None)
+
+
+def _data(n, seed, op):
+    # squares of [-2, 2] stay exact in fp32 sums of up to 4 million terms
+    return workloads.small_ints(n, seed, -2, 2) if op == "sumsq" else \
+        workloads.small_ints(n, seed)
+
+
+def _sweep_1d(op, ns, offsets, seed, tag):
+    data = _data(max(ns) + max(offsets) + 1, seed, op)
+    dev = H.upload(data)
+    lib = rd.load()
+    cases = [(n, off) for n in ns for off in offsets]
+    slots = H.OutSlots([1] * len(cases))
+    H.say("%s %s: %d calls of rd_reduce_1d" % (tag, op, len(cases)))
+    for k, (n, off) in enumerate(cases):
+        x = dev[off:off + n]
+        st = lib.rd_reduce_1d(x.data_ptr() if n else None, n, rd.OPS[op], slots.ptr(k),
+                              H.stream_handle())
+        assert st == 0, (op, n, off, rd.rd_status_string(st))
+    outs = slots.fetch()
+    for k, (n, off) in enumerate(cases):
+        S, _ = oracle.reduce_1d(data[off:off + n], op)
+        H.assert_bitwise_equal_oracle(outs[k], [S], "%s %s n=%d off=%d" % (tag, op, n, off))
+
+
+def _sweep_dim(op, shapes, offsets, seed, tag):
+    maxn = max(o * r * i for o, r, i in shapes)
+    data = _data(maxn + max(offsets) + 1, seed, op)
+    dev = H.upload(data)
+    lib = rd.load()
+    cases = [(s, off) for s in shapes for off in offsets]
+    slots = H.OutSlots([o * i for (o, r, i), _ in cases])
+    H.say("%s %s: %d calls of rd_reduce_dim" % (tag, op, len(cases)))
+    for k, ((o, r, i), off) in enumerate(cases):
+        x = dev[off:off + o * r * i]
+        st = lib.rd_reduce_dim(x.data_ptr() if x.numel() else None, o, r, i, rd.OPS[op],
+                               slots.ptr(k), H.stream_handle())
+        assert st == 0, (op, (o, r, i), off, rd.rd_status_string(st))
+    outs = slots.fetch()
+    for k, ((o, r, i), off) in enumerate(cases):
+        S, _ = oracle.reduce_dim(data[off:off + o * r * i], o, r, i, op, threads=1)
+        H.assert_bitwise_equal_oracle(outs[k], S, "%s %s shape=%s off=%d"
+                                      % (tag, op, (o, r, i), off))
+
+
+@pytest.mark.parametrize("op", OPS3)
+def test_every_small_n(op):
+    _sweep_1d(op, list(range(0, 1100)) + [4095, 4096, 4097, 65539, 1_000_003], [0, 1, 2, 3],
+              700 + rd.OPS[op], "1d")
+
+
+@pytest.mark.parametrize("op", OPS3)
+def test_small_and_wide_shapes(op):
+    shapes = [(o, r, i) for o in range(6) for r in range(6) for i in range(6)]
+    shapes += [(o, r, i) for i in (63, 64, 65, 255, 257, 1023, 4095)
+               for (o, r) in ((1, 1), (2, 5), (3, 17))]
+    shapes += [(1000, 3, 1), (300, 64, 1), (33, 4095, 1), (5, 12289, 1), (2, 4096, 4095),
+               (3, 100_003, 1), (5, 37, 2), (3, 1000, 3)]
+    _sweep_dim(op, shapes, [0, 1, 3], 710 + rd.OPS[op], "dim")
+
+
+ROW_SHAPES = [(op, g, u, p, nt, c) for op in OPS3 for (g, u) in ((64, 8), (64, 16), (256, 8),
+                                                                  (256, 16))
+              for p in (1, 3) for nt in (1, 2) for c in (1, 2) if not (p == 1 and c == 2)]
+
+
+@pytest.mark.parametrize("op,group,unroll,split,nt,combine", ROW_SHAPES,
+                         ids=["%s_g%d_u%d_p%d_nt%d_c%d" % t for t in ROW_SHAPES])
+def test_rows_kernel_shapes(op, group, unroll, split, nt, combine):
+    with rd.tuning(group=group, unroll=unroll, split=split, nontemporal=nt, combine=combine):
+        _sweep_1d(op, [0, 1, 5, 64, 65, 1000, 4097, 65539, 300_007], [0, 3],
+                  720 + group + unroll + split, "rows")
+        _sweep_dim(op, [(3, 1001, 1), (7, 4099, 1)], [0, 1], 730 + group + unroll, "rows")
+
+
+COL_SHAPES = [(op, cw, s, nt) for op in OPS3 for cw in (1, 2, 4, 8) for s in (1, 3)
+              for nt in (1, 2)]
+
+
+@pytest.mark.parametrize("op,cw,split,nt", COL_SHAPES,
+                         ids=["%s_cw%d_s%d_nt%d" % t for t in COL_SHAPES])
+def test_cols_kernel_shapes(op, cw, split, nt):
+    shapes = [(1, 1, 4), (2, 5, 4), (3, 17, 5), (2, 33, 63), (1, 64, 64), (2, 7, 65),
+              (1, 100, 255), (2, 9, 256), (1, 13, 257), (2, 37, 4095), (1, 19, 4 * 1024 + 3)]
+    with rd.tuning(col_waves=cw, row_waves=1, unroll=4, split=split, nontemporal=nt):
+        _sweep_dim(op, shapes, [0, 1, 2, 3], 740 + cw + split, "cols")
+
+
+@pytest.mark.parametrize("op", OPS3)
+def test_random_data(op):
+    """Non-integer data: max / min bit-exact, sum of squares within tolerance."""
+    a = workloads.random(3_000_001, 750, "normal")
+    got = rd.rd_reduce_1d(H.upload(a, 1), op).cpu().numpy()
+    S, A = oracle.reduce_1d(a, op)
+    check = H.assert_bitwise_equal_oracle if op != "sumsq" else None
+    if check:
+        check(got, [S], "1d " + op)
+    else:
+        H.assert_within_tolerance(got, [S], [A], "1d " + op)
+    for outer, R, inner in ((4, 1000, 4095), (300, 5000, 1), (2, 3000, 3), (64, 100, 100)):
+        b = workloads.random(outer * R * inner, 751 + R, "uniform", -3.0, 3.0)
+        got = rd.rd_reduce_dim(H.upload(b), outer, R, inner, op).cpu().numpy()
+        S, A = oracle.reduce_dim(b, outer, R, inner, op)
+        if op == "sumsq":
+            H.assert_within_tolerance(got, S, A, "dim %s %s" % (op, (outer, R, inner)))
+        else:
+            H.assert_bitwise_equal_oracle(got, S, "dim %s %s" % (op, (outer, R, inner)))
+
+
+def test_special_values():
+    """IEEE 754-2019 maximum / minimum on the GPU: NaN propagates, -0 < +0,
+    the empty reduction gives -Inf / +Inf (0 for the sum of squares), R == 0
+    fills the outputs with it."""
+    t = H.torch()
+    f = lambda *v: H.upload(np.array(v, dtype=np.float32))
+    bits = lambda tns: tns.cpu().numpy().view(np.uint32)[0]
+    pz, nz = np.float32(0.0).view(np.uint32), np.float32(-0.0).view(np.uint32)
+    for v in ((-0.0, 0.0), (0.0, -0.0), (-0.0, 0.0, -0.0, -0.0, 0.0)):
+        assert bits(rd.rd_reduce_1d(f(*v), "max")) == pz, v
+        assert bits(rd.rd_reduce_1d(f(*v), "min")) == nz, v
+    big = np.full(1_000_003, -0.0, np.float32)
+    big[777_777] = 0.0
+    assert bits(rd.rd_reduce_1d(H.upload(big), "max")) == pz
+    big = np.zeros(1_000_003, np.float32)
+    big[5] = -0.0
+    assert bits(rd.rd_reduce_1d(H.upload(big), "min")) == nz
+    for op in OPS3:
+        a = np.ones(1_000_003, np.float32)
+        a[500_001] = np.nan
+        assert np.isnan(rd.rd_reduce_1d(H.upload(a), op).item()), op
+    a = np.ones(1_000_003, np.float32)
+    a[3] = np.inf
+    assert rd.rd_reduce_1d(H.upload(a), "max").item() == np.inf
+    a[3] = -np.inf
+    assert rd.rd_reduce_1d(H.upload(a), "min").item() == -np.inf
+    e = H.upload(np.zeros(0, np.float32))
+    assert rd.rd_reduce_1d(e, "max").item() == -np.inf
+    assert rd.rd_reduce_1d(e, "min").item() == np.inf
+    assert bits(rd.rd_reduce_1d(e, "sumsq")) == pz
+    got = rd.rd_reduce_dim(e, 3, 0, 5, "max").cpu().numpy()
+    assert (got == -np.inf).all()
+    z = np.ones((3, 999, 70), np.float32)
+    z[1, 500, 69] = np.nan
+    got = rd.rd_reduce_dim(H.upload(z), 3, 999, 70, "min").cpu().numpy()
+    assert np.isnan(got[1, 69]) and np.isfinite(np.delete(got.reshape(-1), 139)).all()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("op", OPS3)
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_full_size(name, op):
+    """The five workloads at full size, default plan: max / min bit-exact,
+    sum of squares within tolerance; 5 repeats bitwise identical."""
+    w = workloads.WORKLOADS[name]
+    H.say("%s %s: generating" % (name, op))
+    host = workloads.generate(w)
+    if w.full_reduce:
+        S, A = oracle.reduce_1d(host, op)
+        S, A = np.array([S]), np.array([A])
+    else:
+        S, A = oracle.reduce_dim(host, w.outer, w.R, w.inner, op)
+    x = H.upload(host)
+    del host
+
+    def run():
+        if w.full_reduce:
+            return rd.rd_reduce_1d(x, op).cpu().numpy().reshape(-1)
+        return rd.rd_reduce_dim(x, w.outer, w.R, w.inner, op).cpu().numpy().reshape(-1)
+
+    first = run()
+    if op == "sumsq":
+        H.assert_within_tolerance(first, S, A, "%s %s" % (name, op))
+    else:
+        H.assert_bitwise_equal_oracle(first, S, "%s %s" % (name, op))
+    for _ in range(5):
+        assert np.array_equal(run().view(np.uint32), first.view(np.uint32))
+    del x
+    H.torch().cuda.empty_cache()
+
+
+def test_torch_style_reduce():
+    a = workloads.small_ints(6 * 7 * 8 * 9, 760).reshape(6, 7, 8, 9)
+    x = H.upload(a).view(6, 7, 8, 9)
+    for dim in range(4):
+        assert np.array_equal(rd.reduce(x, "max", dim).cpu().numpy(), a.max(axis=dim))
+        assert np.array_equal(rd.reduce(x, "min", dim).cpu().numpy(), a.min(axis=dim))
+        sq = (a.astype(np.int64) ** 2).sum(axis=dim).astype(np.float32)
+        assert np.array_equal(rd.reduce(x, "sumsq", dim).cpu().numpy(), sq)
+    assert rd.reduce(x, "max").item() == float(a.max())

@@ -153,3 +153,25 @@ def test_tuning_override():
     assert not rd.rd_tune_supported("rows", 256, 0, 6)
     assert rd.rd_tune_supported("cols", 1, 4, 8)
     assert not rd.rd_tune_supported("cols", 8, 4, 8)
+    # the other operators have the planner's default shapes
+    for op in ("sumsq", "max", "min"):
+        assert rd.rd_tune_supported("rows", 256, 0, 16, op)
+        assert rd.rd_tune_supported("rows", 64, 0, 8, op)
+        assert not rd.rd_tune_supported("rows", 256, 0, 4, op)
+        for cw in (1, 2, 4, 8):
+            assert rd.rd_tune_supported("cols", cw, 1, 4, op)
+        assert not rd.rd_tune_supported("cols", 1, 4, 8, op)
+
+
+def test_default_plans_are_built_for_every_operator():
+    """Whatever the planner picks by default exists for every operator."""
+    rng = np.random.default_rng(1)
+    ops = ("sum", "sumsq", "max", "min")
+    for _ in range(2000):
+        outer, R, inner = (int(v) for v in np.exp(rng.uniform(0, 12, 3)).astype(np.int64))
+        p = rd.rd_plan_dim(CU, outer, R, inner).as_dict()
+        if p["path"] == "rows":
+            assert all(rd.rd_tune_supported("rows", p["group"], 0, p["unroll"], op) for op in ops)
+        if p["path"] == "cols":
+            assert all(rd.rd_tune_supported("cols", p["col_waves"], p["row_waves"], p["unroll"], op)
+                       for op in ops)
