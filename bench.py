@@ -101,6 +101,9 @@ def main(argv=None):
                     help="instead of the step line: one JSON line per workload (all five "
                          "unless --workload is given), warm and cold GPU times, the oracle's "
                          "CPU time and the parity check")
+    ap.add_argument("--dim-shape", action="append", default=None, metavar="OxRxI",
+                    help="with --report: also an axis reduce of this [outer, R, inner] "
+                         "shape, U[0,1) data from seed 0")
     ap.add_argument("--op", action="append", default=None,
                     choices=["sum", "sumsq", "max", "min"],
                     help="with --report: the reductions to time (default: sum)")
@@ -286,13 +289,18 @@ def report(args, dev, cu):
 
     threads = oracle.default_threads()
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    for name in (args.workload or list(workloads.WORKLOADS)):
-        w = workloads.WORKLOADS[name]
+    todo = [workloads.WORKLOADS[n] for n in (args.workload or
+                                             ([] if args.dim_shape else list(workloads.WORKLOADS)))]
+    for spec in args.dim_shape or []:
+        o, r, i = (int(v) for v in spec.lower().split("x"))
+        todo.append(workloads.Workload("shape_%dx%dx%d" % (o, r, i), (o, r, i), o, r, i,
+                                       "uniform", seed=0))
+    for w in todo:
         host = workloads.generate(w)
         x = torch.from_numpy(host).to(dev)
         out = torch.empty(w.out_numel, dtype=torch.float32, device=dev)
         for op in (args.op or ["sum"]):
-            log("report: %s %s" % (name, op))
+            log("report: %s %s" % (w.name, op))
             print(json.dumps(report_one(w, op, host, x, out, flush, threads, cu)), flush=True)
         del x, out, host
         torch.cuda.empty_cache()

@@ -151,8 +151,9 @@ typedef enum rd_path {
     RD_PATH_ZERO = 1,        /* R == 0: fill out with +0.0 */
     RD_PATH_ROWS = 2,        /* inner == 1: a group of lanes per row piece */
     RD_PATH_ROWS_SHORT = 3,  /* inner == 1, R < 64: one lane per row */
-    RD_PATH_COLS = 4,        /* inner >= 4: a lane owns 4 adjacent columns */
-    RD_PATH_COLS_NARROW = 5  /* inner in {2, 3}: one lane per output */
+    RD_PATH_COLS = 4,        /* inner > 128: a lane owns 4 adjacent columns */
+    RD_PATH_COLS_SMALL = 5   /* 2 <= inner <= 128: a wave loads 64 / ceil(inner/4)
+                                adjacent rows per instruction */
 } rd_path;
 
 /* Chunk order of the pieces of one row on the ROWS path. */
@@ -214,15 +215,18 @@ typedef struct rd_tune {
     int32_t order;           /* ROWS: rd_order */
     int32_t nontemporal;     /* ROWS, COLS: 1 = off, 2 = on */
     int32_t combine;         /* ROWS: 1 = second pass, 2 = last workgroup */
+    int32_t path;            /* inner >= 4: RD_PATH_COLS or RD_PATH_COLS_SMALL
+                                (the latter for inner <= 256) */
     int64_t split;           /* ROWS: pieces per row; COLS*: slabs of R */
 } rd_tune;
 
 rd_status rd_tune_set(const rd_tune* tune);
 
 /* 1 if this build has a kernel for (op, path, group|col_waves, row_waves,
- * unroll); path is RD_PATH_ROWS or RD_PATH_COLS, the unused field is 0.
- * The sum has every shape; the other operators have the planner's default
- * shapes (ROWS: U = 8 or 16; COLS: row_waves = 1, U = 4). */
+ * unroll); path is RD_PATH_ROWS, RD_PATH_COLS or RD_PATH_COLS_SMALL, the
+ * unused fields are 0.  The sum has every shape; the other operators have
+ * the planner's default shapes (ROWS: U = 8 or 16; COLS: row_waves = 1,
+ * U = 4; COLS_SMALL: U = 4). */
 int rd_tune_supported(int32_t op, int32_t path, int32_t group_or_col_waves,
                       int32_t row_waves, int32_t unroll);
 

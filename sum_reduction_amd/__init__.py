@@ -34,7 +34,7 @@ RD_OK = 0
 # rd_op: the reductions (the sum is the method; the others share its kernels)
 OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
 PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
-              5: "cols_narrow"}
+              5: "cols_small"}
 ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
 COMBINE_NAMES = {0: "none", 1: "pass", 2: "last_block"}
 
@@ -71,7 +71,8 @@ class RdTune(ctypes.Structure):
     _fields_ = [("group", ctypes.c_int32), ("col_waves", ctypes.c_int32),
                 ("row_waves", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
-                ("combine", ctypes.c_int32), ("split", ctypes.c_int64)]
+                ("combine", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("split", ctypes.c_int64)]
 
 
 _lib = None
@@ -154,7 +155,7 @@ def rd_tune_set(tune: Optional[RdTune]):
 
 def rd_tune_supported(path: str, group_or_col_waves: int, row_waves: int,
                       unroll: int, op: str = "sum") -> bool:
-    code = {"rows": 2, "cols": 4}[path]
+    code = {"rows": 2, "cols": 4, "cols_small": 5}[path]
     return bool(load().rd_tune_supported(OPS[op], code, group_or_col_waves, row_waves,
                                          unroll))
 

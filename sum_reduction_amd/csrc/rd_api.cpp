@@ -178,11 +178,11 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, int64_t
             }
             break;
         case RD_PATH_COLS:
-        case RD_PATH_COLS_NARROW: {
+        case RD_PATH_COLS_SMALL: {
             float* dst = p.split == 1 ? out : ws;
             e = p.path == RD_PATH_COLS
                     ? rd::launch_cols(op, p, x, outer, R, inner, dst, s)
-                    : rd::launch_cols_narrow(op, p, x, outer, R, inner, dst, s);
+                    : rd::launch_cols_small(op, p, x, outer, R, inner, dst, s);
             if (e == hipSuccess && p.split > 1)
                 e = rd::launch_slab_combine(op, ws, p.split, outer * inner, out, s);
             break;
@@ -286,7 +286,8 @@ rd_status rd_tune_set(const rd_tune* tune) {
         return RD_OK;
     }
     if (tune->group < 0 || tune->col_waves < 0 || tune->row_waves < 0 || tune->unroll < 0 ||
-        tune->order < 0 || tune->nontemporal < 0 || tune->combine < 0 || tune->split < 0)
+        tune->order < 0 || tune->nontemporal < 0 || tune->combine < 0 || tune->path < 0 ||
+        tune->split < 0)
         return RD_ERR_INVALID_ARG;
     g_tune = *tune;
     g_tune_on = true;
@@ -298,6 +299,7 @@ int rd_tune_supported(int32_t op, int32_t path, int32_t group_or_col_waves,
     if (path == RD_PATH_ROWS) return rd::rows_shape_supported(op, group_or_col_waves, unroll);
     if (path == RD_PATH_COLS)
         return rd::cols_shape_supported(op, group_or_col_waves, row_waves, unroll);
+    if (path == RD_PATH_COLS_SMALL) return rd::small_shape_supported(op, unroll);
     return 0;
 }
 

@@ -15,6 +15,8 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 // Rows shorter than this take the lane-per-row path.
 constexpr int64_t kShortRow = 64;
+// Inner sizes up to this take the several-rows-per-load column path.
+constexpr int64_t kSmallInner = 128;
 // Upper bound on workgroups per launch; larger problems loop inside the
 // kernels (a grid's total thread count must stay below 2^32 on AMD, and
 // workgroups have up to 1024 threads).
@@ -38,13 +40,14 @@ hipError_t launch_rows_combine(int op, const float* part, int64_t outer, int64_t
                                float* out, hipStream_t s);
 hipError_t launch_cols(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
                        int64_t inner, float* dst, hipStream_t s);
-hipError_t launch_cols_narrow(int op, const rd_plan& p, const float* x, int64_t outer,
-                              int64_t R, int64_t inner, float* dst, hipStream_t s);
+hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, int64_t outer,
+                             int64_t R, int64_t inner, float* dst, hipStream_t s);
 hipError_t launch_slab_combine(int op, const float* slab, int64_t S, int64_t n, float* out,
                                hipStream_t s);
 
 // Which kernel shapes this build instantiates for an operator (rd_kernels.hip).
 bool rows_shape_supported(int op, int group, int unroll);
 bool cols_shape_supported(int op, int col_waves, int row_waves, int unroll);
+bool small_shape_supported(int op, int unroll);
 
 }  // namespace rd

@@ -66,6 +66,27 @@ __device__ __forceinline__ v4f load4(const float* p) {
     }
 }
 
+// V = 2 or 3 floats from a 4-byte-aligned address (global_load_dwordx2 /
+// dwordx3) into the first V lanes of a float4; the other lanes get `fill`.
+template <int V, bool NT>
+__device__ __forceinline__ v4f loadv(const float* p, float fill) {
+    if constexpr (V == 4) {
+        return load4<NT>(p);
+    } else {
+        typedef float vNf __attribute__((ext_vector_type(V), aligned(4)));
+        vNf w;
+        if constexpr (NT)
+            w = __builtin_nontemporal_load(reinterpret_cast<const vNf*>(p));
+        else
+            __builtin_memcpy(&w, p, sizeof(w));
+        v4f v = {fill, fill, fill, fill};
+        v.x = w.x;
+        v.y = w.y;
+        if constexpr (V == 3) v.z = w.z;
+        return v;
+    }
+}
+
 // ------------------------------------------------------------- operators
 // start: the value of an empty reduction; fold: one more term into a
 // partial result; join: two partial results into one.
@@ -398,39 +419,80 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
     }
 }
 
-// inner in {2, 3} (or any inner): one lane per output of one slab, rows taken
-// round robin into 4 accumulators, the slab's last R % 4 rows into the first.
-template <int OP>
-__global__ __launch_bounds__(kBlock) void cols_narrow_kernel(const float* __restrict__ x,
-                                                             int64_t outer, int64_t R,
-                                                             int64_t inner, int64_t S,
-                                                             int64_t rps,
-                                                             float* __restrict__ dst) {
-    const int64_t per_slab = outer * inner;
-    const int64_t total = S * per_slab;
-    const int64_t stride = int64_t(gridDim.x) * kBlock;
-    for (int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x; e < total; e += stride) {
-        const int64_t s = e / per_slab;
-        const int64_t oi = e - s * per_slab;
-        const int64_t o = oi / inner;
-        const int64_t i = oi - o * inner;
-        const int64_t r0 = s * rps;
-        const int64_t r1 = r0 + rps < R ? r0 + rps : R;
-        const float* p = x + (o * R + r0) * inner + i;
-        float a0 = Op<OP>::start(), a1 = a0, a2 = a0, a3 = a0;
-        int64_t r = r0;
-        for (; r + 4 <= r1; r += 4) {
-            a0 = Op<OP>::fold(a0, p[0]);
-            a1 = Op<OP>::fold(a1, p[inner]);
-            a2 = Op<OP>::fold(a2, p[2 * inner]);
-            a3 = Op<OP>::fold(a3, p[3 * inner]);
-            p += 4 * inner;
+// Small inner (2 <= inner <= 128): several rows of one outer index per load
+// instruction.  The rows of one outer index are adjacent in memory, so a wave
+// covers RPW consecutive rows at once: lane = (row phase rho, lane-column lc)
+// with LC = ceil(inner / 4) lane-columns per row and RPW = 64 / LC row
+// phases (lanes from RPW * LC on idle); each instruction reads RPW * inner
+// contiguous floats.  Lane-column lc owns columns 4*lc .. 4*lc + 3 (the
+// row's last lane-column loads the row's last 4 floats and keeps its own,
+// as in cols_kernel); with inner < 4 (V = inner) a lane loads its whole row.
+// Each wave works on one item (outer index o, slab s of R) at a time: row
+// phase rho folds rows r0 + rho + k*RPW into accumulator (k mod 2), U rows in
+// flight; then the row phases of each lane-column are joined through LDS in
+// rho order and the rho == 0 lanes write.  With S == 1, dst is the output;
+// otherwise dst is [S][outer][inner] for slab_combine_kernel.
+template <int OP, int V, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void cols_small_kernel(
+    const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t S,
+    int64_t rps, int32_t LC, float* __restrict__ dst, uint32_t nxcd) {
+    constexpr int kWaves = kBlock / kWave;
+    __shared__ v4f lds[kBlock];
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int RPW = kWave / LC;
+    const int rho = lane / LC;
+    const int lc = lane - rho * LC;
+    const bool active = rho < RPW;
+    const int64_t c = 4 * int64_t(lc);
+    const int64_t cl = (V == 4 && c + 4 > inner) ? inner - 4 : c;
+    const int keep = int(c - cl);  // 0, or 1..3 for the row's last lane-column
+    const int64_t nitems = S * outer;
+    const int64_t wstride = int64_t(gridDim.x) * kWaves;
+    v4f* my = lds + wave * kWave;
+    for (int64_t item = xcd_block(nxcd) * kWaves + wave; item < nitems; item += wstride) {
+        const int64_t o = item / S;
+        const int64_t s = item - o * S;
+        const int64_t r0 = s * rps + rho;
+        const int64_t r1 = (s + 1) * rps < R ? (s + 1) * rps : R;
+        const int64_t m = r0 < r1 ? (r1 - r0 + RPW - 1) / RPW : 0;
+        v4f acc[2] = {start4<OP>(), start4<OP>()};
+        if (active) {
+            const float* p = x + (o * R + r0) * inner + cl;
+            const int64_t step = int64_t(RPW) * inner;
+            const float fill = Op<OP>::start();
+            int64_t k = 0;
+            for (; k + U <= m; k += U) {
+                v4f v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u] = loadv<V, NT>(p + u * step, fill);
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc[u & 1] = Op<OP>::fold(acc[u & 1], v[u]);
+                p += U * step;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (k + u < m)
+                    acc[u & 1] = Op<OP>::fold(acc[u & 1], loadv<V, NT>(p + u * step, fill));
         }
-        for (; r < r1; ++r) {
-            a0 = Op<OP>::fold(a0, p[0]);
-            p += inner;
+        // join the row phases of each lane-column, in rho order
+        my[lane] = Op<OP>::join(acc[0], acc[1]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (rho == 0) {
+            v4f a = my[lc];
+            for (int q = 1; q < RPW; ++q) a = Op<OP>::join(a, my[q * LC + lc]);
+            float* d = dst + (s * outer + o) * inner + cl;
+            if constexpr (V == 4) {
+                for (int q = keep; q < 4; ++q) d[q] = a[q];
+            } else {
+                for (int q = 0; q < V; ++q) d[q] = a[q];
+            }
         }
-        dst[e] = Op<OP>::join(Op<OP>::join(a0, a1), Op<OP>::join(a2, a3));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -631,11 +693,42 @@ hipError_t rows_combine_go(const float* part, int64_t outer, int64_t P, float* o
     return launch(rows_combine_kernel<OP>, blocks, kBlock, s, part, outer, P, out);
 }
 
+constexpr bool small_built(int op, int v, int u) {
+    if (v != 2 && v != 3 && v != 4) return false;
+    return op == RD_OP_SUM ? (u == 2 || u == 4 || u == 8) : u == 4;
+}
+
+template <int OP, int V, int U, bool NT>
+hipError_t small_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
+    if constexpr (small_built(OP, V, U)) {
+        const int32_t lc = int32_t((a.inner + 3) / 4);
+        return launch(cols_small_kernel<OP, V, U, NT>, p.blocks, kBlock, s, a.x, a.outer, a.R,
+                      a.inner, p.split, p.rows_per_split, lc, a.dst, uint32_t(p.nxcd));
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int OP, int V, bool NT>
+hipError_t small_u(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
+    switch (p.unroll) {
+        case 2: return small_go<OP, V, 2, NT>(p, a, s);
+        case 4: return small_go<OP, V, 4, NT>(p, a, s);
+        case 8: return small_go<OP, V, 8, NT>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OP, int V>
+hipError_t small_nt(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
+    return p.nontemporal ? small_u<OP, V, true>(p, a, s) : small_u<OP, V, false>(p, a, s);
+}
+
 template <int OP>
-hipError_t cols_narrow_go(const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                          int64_t inner, float* dst, hipStream_t s) {
-    return launch(cols_narrow_kernel<OP>, p.blocks, kBlock, s, x, outer, R, inner, p.split,
-                  p.rows_per_split, dst);
+hipError_t cols_small_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
+    if (a.inner == 2) return small_nt<OP, 2>(p, a, s);
+    if (a.inner == 3) return small_nt<OP, 3>(p, a, s);
+    return small_nt<OP, 4>(p, a, s);
 }
 
 template <int OP>
@@ -652,6 +745,10 @@ bool rows_shape_supported(int op, int group, int unroll) {
 
 bool cols_shape_supported(int op, int col_waves, int row_waves, int unroll) {
     return op_valid(op) && cols_built(op, col_waves, row_waves, unroll);
+}
+
+bool small_shape_supported(int op, int unroll) {
+    return op_valid(op) && small_built(op, 4, unroll);
 }
 
 hipError_t launch_fill_start(int op, float* out, int64_t n, hipStream_t s) {
@@ -680,9 +777,10 @@ hipError_t launch_cols(int op, const rd_plan& p, const float* x, int64_t outer, 
     RD_BY_OP(op, cols_op, p, a, s)
 }
 
-hipError_t launch_cols_narrow(int op, const rd_plan& p, const float* x, int64_t outer,
-                              int64_t R, int64_t inner, float* dst, hipStream_t s) {
-    RD_BY_OP(op, cols_narrow_go, p, x, outer, R, inner, dst, s)
+hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, int64_t outer,
+                             int64_t R, int64_t inner, float* dst, hipStream_t s) {
+    const ColsArgs a{x, outer, R, inner, dst};
+    RD_BY_OP(op, cols_small_go, p, a, s)
 }
 
 hipError_t launch_slab_combine(int op, const float* slab, int64_t S, int64_t n, float* out,

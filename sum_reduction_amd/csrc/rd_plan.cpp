@@ -48,6 +48,7 @@ int32_t nxcd_for(int cu_count) {
 rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
                     rd_plan* p) {
     const bool forced = t && (t->group || t->unroll || t->split || t->order || t->combine);
+    if (t && t->path) return RD_ERR_INVALID_ARG;  // inner == 1 has no column path
     if (R < kShortRow && !forced) {
         p->path = RD_PATH_ROWS_SHORT;
         p->block_threads = kBlock;
@@ -116,29 +117,42 @@ void split_rows(int64_t R, int64_t S, rd_plan* p) {
 
 rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
                     const rd_tune* t, rd_plan* p) {
-    if (inner < 4) {
-        // one lane per output; only the split along R adds parallelism
-        p->path = RD_PATH_COLS_NARROW;
+    const int32_t forced = t ? t->path : 0;
+    if (forced && forced != RD_PATH_COLS && forced != RD_PATH_COLS_SMALL)
+        return RD_ERR_INVALID_ARG;
+    if (forced == RD_PATH_COLS && inner < 4) return RD_ERR_INVALID_ARG;
+    if (forced == RD_PATH_COLS_SMALL && inner > 2 * kSmallInner) return RD_ERR_INVALID_ARG;
+    if (forced == RD_PATH_COLS_SMALL || (!forced && inner <= kSmallInner)) {
+        // several adjacent rows per load instruction; a wave per item
+        // (outer index, slab of R), the split along R only for few items
+        p->path = RD_PATH_COLS_SMALL;
         p->block_threads = kBlock;
-        const int64_t lanes = outer * inner;
-        const int64_t target_lanes = int64_t(cu) * kLoadWavesPerCu * kWave;
+        p->unroll = (t && t->unroll) ? t->unroll : kColsUnroll;
+        if (!small_shape_supported(op, p->unroll)) return RD_ERR_INVALID_ARG;
+        if (!nontemporal_choice(t, true, &p->nontemporal)) return RD_ERR_INVALID_ARG;
+        const int64_t lc = ceil_div(inner, 4);
+        const int64_t rpw = kWave / lc;
+        const int64_t waves_per_block = kBlock / kWave;
+        const int64_t want = int64_t(cu) * kLoadWavesPerCu / p->unroll;  // waves
         int64_t S = 1;
         if (t && t->split) {
             S = t->split;
-        } else if (lanes < target_lanes) {
-            S = ceil_div(target_lanes, lanes);
-            int64_t cap = R / 16;
+        } else if (outer < want) {
+            S = ceil_div(want, outer);
+            // every lane keeps at least one full unrolled step of rows per slab
+            int64_t cap = R / (rpw * p->unroll);
             if (cap < 1) cap = 1;
             if (S > cap) S = cap;
         }
         if (S < 1) return RD_ERR_INVALID_ARG;
         split_rows(R, S, p);
-        if (p->split > INT64_MAX / 4 / lanes) return RD_ERR_INVALID_ARG;
-        p->blocks = ceil_div(p->split * lanes, kBlock);
+        if (p->split > INT64_MAX / 4 / (outer * inner)) return RD_ERR_INVALID_ARG;
+        p->blocks = ceil_div(p->split * outer, waves_per_block);
         if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
         p->passes = p->split > 1 ? 2 : 1;
         p->combine = p->split > 1 ? RD_COMBINE_PASS : RD_COMBINE_NONE;
-        p->workspace_bytes = p->split > 1 ? p->split * lanes * int64_t(sizeof(float)) : 0;
+        p->workspace_bytes =
+            p->split > 1 ? p->split * outer * inner * int64_t(sizeof(float)) : 0;
         return RD_OK;
     }
     p->path = RD_PATH_COLS;

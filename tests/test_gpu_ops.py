@@ -109,8 +109,20 @@ COL_SHAPES = [(op, cw, s, nt) for op in OPS3 for cw in (1, 2, 4, 8) for s in (1,
 def test_cols_kernel_shapes(op, cw, split, nt):
     shapes = [(1, 1, 4), (2, 5, 4), (3, 17, 5), (2, 33, 63), (1, 64, 64), (2, 7, 65),
               (1, 100, 255), (2, 9, 256), (1, 13, 257), (2, 37, 4095), (1, 19, 4 * 1024 + 3)]
-    with rd.tuning(col_waves=cw, row_waves=1, unroll=4, split=split, nontemporal=nt):
+    with rd.tuning(col_waves=cw, row_waves=1, unroll=4, split=split, nontemporal=nt, path=4):
         _sweep_dim(op, shapes, [0, 1, 2, 3], 740 + cw + split, "cols")
+
+
+SMALL = [(op, s, nt) for op in OPS3 for s in (1, 3) for nt in (1, 2)]
+
+
+@pytest.mark.parametrize("op,split,nt", SMALL, ids=["%s_s%d_nt%d" % t for t in SMALL])
+def test_cols_small_kernel_shapes(op, split, nt):
+    shapes = [(o, r, i) for i in (2, 3, 4, 5, 8, 17, 63, 64, 100, 128)
+              for (o, r) in ((1, 1), (3, 7), (2, 64), (5, 130))]
+    with rd.tuning(unroll=4, split=split, nontemporal=nt, path=5):
+        _sweep_dim(op, shapes + [(2, 33, 129), (1, 50, 256)], [0, 1, 3], 745 + split + nt,
+                   "cols_small")
 
 
 @pytest.mark.parametrize("op", OPS3)

@@ -129,7 +129,8 @@ def test_cols_kernel_shapes(cw, rw, unroll, split, nt):
     shapes = [(1, 1, 4), (2, 5, 4), (3, 17, 5), (2, 33, 63), (1, 64, 64), (2, 7, 65),
               (1, 100, 255), (2, 9, 256), (1, 13, 257), (1, 3, 1023), (2, 37, 4095),
               (1, 19, 4 * 1024 + 3)]
-    with rd.tuning(col_waves=cw, row_waves=rw, unroll=unroll, split=split, nontemporal=nt):
+    with rd.tuning(col_waves=cw, row_waves=rw, unroll=unroll, split=split, nontemporal=nt,
+                   path=4):
         _sweep_dim(shapes, [0, 1, 2, 3], 400 + cw * 100 + rw * 10 + unroll + split + nt,
                    "cols cw%d rw%d u%d s%d nt%d" % (cw, rw, unroll, split, nt))
 
@@ -186,12 +187,43 @@ def test_fused_combine_several_rows_and_streams():
         assert np.array_equal(o.cpu().numpy(), want)
 
 
-def test_cols_narrow_splits():
-    """inner in {2, 3}: one lane per output, with forced splits of R."""
-    shapes = [(5, 37, 2), (3, 1000, 3), (1, 4097, 2), (64, 9, 3)]
-    for split in (1, 2, 7):
-        with rd.tuning(split=split):
-            _sweep_dim(shapes, [0, 1], 500 + split, "cols narrow s%d" % split)
+SMALL_INNERS = [2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128]
+SMALL_TUNES = [(u, s, nt) for u in (2, 4, 8) for s in (1, 3) for nt in (1, 2)]
+
+
+@pytest.mark.parametrize("unroll,split,nt", SMALL_TUNES,
+                         ids=["u%d_s%d_nt%d" % t for t in SMALL_TUNES])
+def test_cols_small_kernel_shapes(unroll, split, nt):
+    """The several-rows-per-load column kernel: every inner up to 128 it
+    takes (and 129..256 when forced), row counts around its row phases,
+    forced splits of R."""
+    shapes = [(o, r, i) for i in SMALL_INNERS for (o, r) in ((1, 1), (3, 7), (2, 64), (5, 130))]
+    with rd.tuning(unroll=unroll, split=split, nontemporal=nt, path=5):
+        _sweep_dim(shapes + [(2, 33, 129), (3, 17, 200), (1, 50, 256)], [0, 1, 3],
+                   600 + unroll + split + nt, "cols_small u%d s%d nt%d" % (unroll, split, nt))
+
+
+def test_cols_small_default_plans():
+    """Small-inner shapes in the planner's own choice, splits included."""
+    shapes = [(1, 100_000, 4), (16, 20_000, 7), (2000, 40, 8), (300, 1000, 2), (7, 3000, 3),
+              (1, 1 << 18, 64), (40, 500, 100), (9, 9, 128)]
+    _sweep_dim(shapes, [0, 2], 650, "cols_small default")
+
+
+def test_cols_paths_agree():
+    """Both column kernels on the same inputs (inner 4..256): within the
+    integer data both are exact, so they agree bit for bit."""
+    shapes = [(3, 100, 4), (2, 50, 33), (4, 70, 100), (2, 65, 128), (1, 40, 256)]
+    maxn = max(o * r * i for o, r, i in shapes)
+    data = workloads.small_ints(maxn, 660)
+    dev = H.upload(data)
+    for o, r, i in shapes:
+        x = dev[:o * r * i]
+        with rd.tuning(path=4):
+            a = rd.rd_sum_dim(x, o, r, i).cpu().numpy()
+        with rd.tuning(path=5):
+            b = rd.rd_sum_dim(x, o, r, i).cpu().numpy()
+        assert np.array_equal(a, b), (o, r, i)
 
 
 def test_degenerate_shapes():

@@ -32,17 +32,18 @@ def check_invariants(p, outer, R, inner):
             assert p.blocks == min(-(-groups // (256 // p.group)), MAX_BLOCKS)
             assert d["combine"] == ("pass" if p.split > 1 else "none")
         assert p.passes == (2 if p.split > 1 else 1)
-    if d["path"] in ("cols", "cols_narrow"):
+    if d["path"] in ("cols", "cols_small"):
         # the slabs tile [0, R) with none empty
         assert p.split * p.rows_per_split >= R
         assert (p.split - 1) * p.rows_per_split < R
         assert p.workspace_bytes == (4 * p.split * outer * inner if p.split > 1 else 0)
         assert p.passes == (2 if p.split > 1 else 1)
         if d["path"] == "cols":
-            assert inner >= 4
+            assert inner > 128
             assert p.block_threads == 64 * p.col_waves * p.row_waves <= 1024
-    if d["path"] == "cols_narrow":
-        assert inner in (2, 3)
+    if d["path"] == "cols_small":
+        assert 2 <= inner <= 128
+        assert p.blocks == min(-(-(p.split * outer) // 4), MAX_BLOCKS)
 
 
 def test_workload_plans():
@@ -97,8 +98,9 @@ def test_degenerate_plans():
     assert rd.rd_plan_1d(CU, 0).as_dict()["path"] == "zero"
     assert rd.rd_plan_1d(CU, 63).as_dict()["path"] == "rows_short"
     assert rd.rd_plan_1d(CU, 64).as_dict()["path"] == "rows"
-    assert rd.rd_plan_dim(CU, 3, 9, 2).as_dict()["path"] == "cols_narrow"
-    assert rd.rd_plan_dim(CU, 3, 9, 4).as_dict()["path"] == "cols"
+    assert rd.rd_plan_dim(CU, 3, 9, 2).as_dict()["path"] == "cols_small"
+    assert rd.rd_plan_dim(CU, 3, 9, 128).as_dict()["path"] == "cols_small"
+    assert rd.rd_plan_dim(CU, 3, 9, 129).as_dict()["path"] == "cols"
 
 
 def test_random_shapes_keep_invariants():
@@ -116,10 +118,26 @@ def test_column_tile_width():
     """Widest tile that still gives every CU a workgroup."""
     assert rd.rd_plan_dim(CU, 128, 4096, 4095).col_waves == 8
     assert rd.rd_plan_dim(CU, 64, 4096, 4095).col_waves == 4
-    assert rd.rd_plan_dim(CU, 1000, 10, 100).col_waves == 1   # 25 lane-columns
+    assert rd.rd_plan_dim(CU, 1000, 10, 200).col_waves == 1   # 50 lane-columns
     assert rd.rd_plan_dim(CU, 1000, 10, 1000).col_waves == 4  # 250 lane-columns
     p = rd.rd_plan_dim(CU, 1, 1 << 16, 4095)                  # never reaches CU tiles
     assert p.col_waves == 8 and p.split > 1 and p.blocks >= CU
+
+
+def test_forced_column_path():
+    with rd.tuning(path=4):
+        assert rd.rd_plan_dim(CU, 3, 9, 64).as_dict()["path"] == "cols"
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 3, 9, 3)          # cols needs inner >= 4
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 3, 9, 1)          # no column path for rows
+    with rd.tuning(path=5):
+        assert rd.rd_plan_dim(CU, 3, 9, 256).as_dict()["path"] == "cols_small"
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 3, 9, 257)        # at most 64 lane-columns
+    with rd.tuning(path=2):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 3, 9, 64)
 
 
 def test_small_problems_still_spread():
@@ -175,3 +193,5 @@ def test_default_plans_are_built_for_every_operator():
         if p["path"] == "cols":
             assert all(rd.rd_tune_supported("cols", p["col_waves"], p["row_waves"], p["unroll"], op)
                        for op in ops)
+        if p["path"] == "cols_small":
+            assert all(rd.rd_tune_supported("cols_small", 0, 0, p["unroll"], op) for op in ops)
