@@ -19,6 +19,9 @@ What it computes (the plain definition of a sum, see ``oracle.c``):
 * ``reduce_1d / reduce_dim / reduce_dim_at(..., op)`` -> the same for the
   other reductions, op in {"sum", "sumsq", "max", "min"} ("Seven-step
   reduction" page: sum, max, the L2 norm are the same primitive).
+* ``cumsum_dim(x, o, R, i, reverse)`` -> (reverse) cumulative sums along the
+  middle axis (POPCORNBENCH level-1 problem 91 trace: cumsum of the flipped
+  row, flipped back).
 * ``within_tolerance``     -> the acceptance rule |got - S| <= 1e-5*A + 1e-6,
   NaN-aware.
 """
@@ -81,6 +84,8 @@ class Oracle:
         lib.oracle_reduce_dim.restype = None
         lib.oracle_reduce_dim_at.argtypes = [vp, i64, i64, i64, ci, vp, vp, i64, vp, vp]
         lib.oracle_reduce_dim_at.restype = None
+        lib.oracle_cumsum_dim.argtypes = [vp, i64, i64, i64, ci, vp, vp, ci]
+        lib.oracle_cumsum_dim.restype = None
         self.lib = lib
         self.path = library
 
@@ -167,6 +172,20 @@ class Oracle:
                                       s.ctypes.data, a.ctypes.data)
         return s, a
 
+    # ---- cumulative sum along the middle axis (same shape out)
+    def cumsum_dim(self, x, outer: int, R: int, inner: int, reverse: bool = True,
+                   threads: int = 0):
+        """(S, A), float64 [outer, R, inner]: the (reverse) cumulative sums of
+        x and of |x| along the middle axis."""
+        x = _as_f32(x).reshape(-1)
+        if x.size != outer * R * inner:
+            raise ValueError("size %d != %d*%d*%d" % (x.size, outer, R, inner))
+        s = np.empty((outer, R, inner), dtype=np.float64)
+        a = np.empty((outer, R, inner), dtype=np.float64)
+        self.lib.oracle_cumsum_dim(x.ctypes.data, outer, R, inner, int(bool(reverse)),
+                                   s.ctypes.data, a.ctypes.data, int(threads))
+        return s, a
+
 
 # numbering of the reductions (the same as the library's rd_op)
 OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
@@ -208,6 +227,10 @@ def reduce_dim(x, outer: int, R: int, inner: int, op: str, threads: int = 0):
 
 def reduce_dim_at(x, outer: int, R: int, inner: int, op: str, o_idx, i_idx):
     return default().reduce_dim_at(x, outer, R, inner, op, o_idx, i_idx)
+
+
+def cumsum_dim(x, outer: int, R: int, inner: int, reverse: bool = True, threads: int = 0):
+    return default().cumsum_dim(x, outer, R, inner, reverse, threads)
 
 
 def tolerance(abs_sum):

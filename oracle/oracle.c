@@ -261,3 +261,38 @@ void oracle_reduce_dim_at(const float* x, int64_t outer, int64_t R, int64_t inne
         abs_out[k] = reduce_magnitude(op, s, a);
     }
 }
+
+/*
+ * Cumulative sum along the middle axis of a contiguous [outer, R, inner]
+ * array, out having the same shape (POPCORNBENCH level-1 problem 91 trace:
+ * y = cumsum(x.flip(1), 1).flip(1), which it spells out as
+ * y[i][j] = x[i][j] + x[i][j+1] + ... + x[i][N-1]).
+ *   reverse != 0:  out[o][r][i] = sum_{k = r .. R-1} x[o][k][i]
+ *   reverse == 0:  out[o][r][i] = sum_{k = 0 .. r}   x[o][k][i]
+ * Each output is accumulated in fp64 in the order the definition walks:
+ * from the far end of the row (k = R-1 for the reverse sum, k = 0 for the
+ * forward one) toward r, one term at a time; abs_out gets the same sums of
+ * |x|.  Different (o, i) are independent and shared out over OpenMP threads.
+ */
+void oracle_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner, int reverse,
+                       double* out, double* abs_out, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = oracle_default_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t o = 0; o < outer; ++o) {
+        for (int64_t i = 0; i < inner; ++i) {
+            double s = 0.0;
+            double a = 0.0;
+            for (int64_t k = 0; k < R; ++k) {
+                const int64_t r = reverse ? R - 1 - k : k;
+                const int64_t e = (o * R + r) * inner + i;
+                double v = (double)x[e];
+                s += v;
+                a += fabs(v);
+                out[e] = s;
+                abs_out[e] = a;
+            }
+        }
+    }
+}

@@ -323,10 +323,73 @@ def pin_max_min_special(orc):
     assert np.all(S == math.inf)
 
 
+# ------------------------------------------------------ cumulative sums
+def pin_cumsum_page_example(orc):
+    """The problem-91 trace's worked row [a, b, c, d] -> [a+b+c+d, b+c+d,
+    c+d, d] (tests/golden/problem91_reverse_cumsum.json), in every layout
+    the row can take: alone, as one of several rows, as a column."""
+    with open(os.path.join(GOLDEN, "problem91_reverse_cumsum.json")) as f:
+        g = json.load(f)
+    row = np.array(g["row"], np.float32)
+    want = np.array(g["reverse_cumsum"])
+    S, A = orc.cumsum_dim(row, 1, row.size, 1, True)
+    assert np.array_equal(S.reshape(-1), want) and np.array_equal(A.reshape(-1), want)
+    rows = np.stack([row, 2 * row, -row]).astype(np.float32)
+    S, _ = orc.cumsum_dim(rows, 3, row.size, 1, True)
+    assert np.array_equal(S.reshape(3, -1), np.stack([want, 2 * want, -want]))
+    col = np.repeat(row[:, None], 5, axis=1).astype(np.float32)   # [R, inner]
+    S, _ = orc.cumsum_dim(col, 1, row.size, 5, True)
+    assert np.array_equal(S.reshape(row.size, 5), np.repeat(want[:, None], 5, axis=1))
+    # forward: the running sum from the front
+    S, _ = orc.cumsum_dim(row, 1, row.size, 1, False)
+    assert np.array_equal(S.reshape(-1), np.cumsum(g["row"]))
+
+
+def pin_cumsum_library(orc):
+    """Integer data: the trace's own formula cumsum(x.flip(1), 1).flip(1)
+    evaluated exactly by numpy in int64, and the forward cumsum; ones give
+    R - r and r + 1."""
+    for k, (outer, R, inner) in enumerate(((1, 1, 1), (3, 17, 1), (2, 64, 5), (4, 33, 4095),
+                                           (5, 1000, 1), (2, 0, 3))):
+        x = workloads.small_ints(outer * R * inner, 80 + k)
+        x3 = x.astype(np.int64).reshape(outer, R, inner)
+        rev = np.flip(np.cumsum(np.flip(x3, 1), 1), 1)
+        fwd = np.cumsum(x3, 1)
+        S, A = orc.cumsum_dim(x, outer, R, inner, True)
+        assert np.array_equal(S, rev.astype(np.float64)), (outer, R, inner)
+        absrev = np.flip(np.cumsum(np.flip(np.abs(x3), 1), 1), 1)
+        assert np.array_equal(A, absrev.astype(np.float64))
+        S, _ = orc.cumsum_dim(x, outer, R, inner, False)
+        assert np.array_equal(S, fwd.astype(np.float64)), (outer, R, inner)
+    ones = np.ones(3 * 50 * 2, np.float32)
+    S, _ = orc.cumsum_dim(ones, 3, 50, 2, True)
+    assert np.all(S == (50 - np.arange(50))[None, :, None])
+    S, _ = orc.cumsum_dim(ones, 3, 50, 2, False)
+    assert np.all(S == (1 + np.arange(50))[None, :, None])
+
+
+def pin_cumsum_fsum(orc):
+    """Random data: every output of a few rows against math.fsum of its terms
+    within the sequential fp64 bound; the reverse sum's first element is the
+    row sum."""
+    R = 3000
+    x = workloads.random(4 * R, 90, "normal").reshape(4, R)
+    S, A = orc.cumsum_dim(x, 4, R, 1, True)
+    S = S.reshape(4, R)
+    A = A.reshape(4, R)
+    for o in range(4):
+        for j in (0, 1, 7, R // 2, R - 2, R - 1):
+            F = math.fsum(x[o, j:].astype(np.float64).tolist())
+            assert abs(S[o, j] - F) <= (R - j) * U53 * A[o, j], (o, j)
+        Sr, _ = orc.sum_dim(x[o], 1, R, 1)
+        assert abs(S[o, 0] - Sr[0, 0]) <= 2 * R * U53 * A[o, 0]
+
+
 ALL_PINS = [
     pin_harmonic, pin_constants_1d, pin_integers_1d, pin_fsum_1d,
     pin_special_values_1d, pin_index_closed_form, pin_constants_axis,
     pin_bruteforce_axis, pin_fsum_axis, pin_special_values_axis,
     pin_page_shape_facts, pin_sumsq_closed_form, pin_sumsq_exact_and_fsum,
-    pin_max_min_library, pin_max_min_special,
+    pin_max_min_library, pin_max_min_special, pin_cumsum_page_example,
+    pin_cumsum_library, pin_cumsum_fsum,
 ]

@@ -72,6 +72,17 @@ MUTANTS = {
     "reduce_at_reversed_column": (
         "reduce_step(op, (double)x[(o_idx[k] * R + r) * inner + i_idx[k]], &s, &a);",
         "reduce_step(op, (double)x[(o_idx[k] * R + r) * inner + (inner - 1 - i_idx[k])], &s, &a);"),
+    # cumulative sums
+    "cumsum_wrong_direction": (
+        "const int64_t r = reverse ? R - 1 - k : k;", "const int64_t r = reverse ? k : R - 1 - k;"),
+    "cumsum_exclusive": (
+        "                s += v;\n                a += fabs(v);\n                out[e] = s;",
+        "                out[e] = s;\n                s += v;\n                a += fabs(v);"),
+    "cumsum_drops_far_end": (
+        "            for (int64_t k = 0; k < R; ++k) {\n                const int64_t r = reverse",
+        "            for (int64_t k = 1; k < R; ++k) {\n                const int64_t r = reverse"),
+    "cumsum_transposed": (
+        "const int64_t e = (o * R + r) * inner + i;", "const int64_t e = (r * outer + o) * inner + i;"),
     # per-output entry point
     "at_reversed_column": (
         "double v = (double)x[(o * R + r) * inner + i];",
