@@ -107,6 +107,11 @@ def main(argv=None):
     ap.add_argument("--op", action="append", default=None,
                     choices=["sum", "sumsq", "max", "min"],
                     help="with --report: the reductions to time (default: sum)")
+    ap.add_argument("--scan", action="store_true",
+                    help="with --report: the cumulative sums (problem 91's reverse "
+                    "cumsum of [32768, 32768], plus each --scan-shape) instead")
+    ap.add_argument("--scan-shape", action="append", default=None, metavar="OxRxI",
+                    help="with --report --scan: also a cumulative sum of this shape")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="only run a device-to-device copy of this many bytes 3 times "
                          "(a known-size kernel for calibrating HBM byte counters)")
@@ -141,7 +146,7 @@ def main(argv=None):
     props = torch.cuda.get_device_properties(dev)
     cu = props.multi_processor_count
     if args.report:
-        return report(args, dev, cu)
+        return report_scan(args, dev, cu) if args.scan else report(args, dev, cu)
     names = args.workload or STEP_WORKLOADS
     ws = [workloads.WORKLOADS[n] for n in names]
 
@@ -302,6 +307,92 @@ def report(args, dev, cu):
         for op in (args.op or ["sum"]):
             log("report: %s %s" % (w.name, op))
             print(json.dumps(report_one(w, op, host, x, out, flush, threads, cu)), flush=True)
+        del x, out, host
+        torch.cuda.empty_cache()
+    return 0
+
+
+def report_scan(args, dev, cu):
+    """One JSON line per cumulative sum (both directions): GPU time warm and
+    cold, GB/s over the algorithmic bytes (every element read once and written
+    once), the oracle's host time, parity on every output."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import sum_reduction_amd as rd
+    import workloads
+
+    threads = oracle.default_threads()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    todo = [] if args.scan_shape else list(workloads.SCAN_WORKLOADS.values())
+    for spec in args.scan_shape or []:
+        o, r, i = (int(v) for v in spec.lower().split("x"))
+        todo.append(workloads.Workload("scan_%dx%dx%d" % (o, r, i), (o, r, i), o, r, i,
+                                       "uniform", seed=0))
+    for w in todo:
+        host = workloads.generate(w)
+        x = torch.from_numpy(host).to(dev)
+        out = torch.empty_like(x)
+        nbytes = 8 * w.numel
+        for rev in (True, False):
+            log("report: cumsum %s reverse=%d" % (w.name, rev))
+
+            def call():
+                rd.rd_cumsum_dim(x, w.outer, w.R, w.inner, reverse=rev, out=out)
+
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            reps = 30 if nbytes >= (1 << 30) else 200
+
+            def timed(cold):
+                ms = []
+                for _ in range(reps):
+                    if cold:
+                        flush.fill_(1.0)
+                    torch.cuda._sleep(200_000)
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    call()
+                    b.record()
+                    b.synchronize()
+                    ms.append(a.elapsed_time(b))
+                ms.sort()
+                med = ms[len(ms) // 2]
+                return {"ms_median": round(med, 5), "ms_min": round(ms[0], 5),
+                        "GBps_median": round(nbytes / med / 1e6, 1),
+                        "frac_of_peak": round(nbytes / med / 1e6 / PEAK_GBS, 4)}
+
+            warm, cold = timed(False), timed(True)
+            got = out.cpu().numpy().reshape(w.outer, w.R * w.inner)
+            # the oracle in blocks of outer indices (its fp64 outputs of the
+            # whole array would not fit comfortably in host memory)
+            blk = max(1, (1 << 25) // max(1, w.R * w.inner))
+            ok, worst, cpu_s = True, 0.0, 0.0
+            for o0 in range(0, w.outer, blk):
+                o1 = min(w.outer, o0 + blk)
+                part = host[o0 * w.R * w.inner:o1 * w.R * w.inner]
+                t0 = time.perf_counter()
+                S, A = oracle.cumsum_dim(part, o1 - o0, w.R, w.inner, rev, threads)
+                cpu_s += time.perf_counter() - t0
+                g = got[o0:o1].reshape(-1)
+                ok &= bool(oracle.within_tolerance(g, S.reshape(-1), A.reshape(-1)).all())
+                with np.errstate(invalid="ignore"):
+                    r = np.abs(g.astype(np.float64) - S.reshape(-1)) / oracle.tolerance(
+                        A.reshape(-1))
+                worst = max(worst, float(np.nanmax(r)))
+            plan = rd.rd_plan_cumsum(cu, w.outer, w.R, w.inner).as_dict()
+            print(json.dumps({
+                "workload": w.name, "op": "cumsum", "reverse": rev, "shape": list(w.shape),
+                "algorithmic_bytes": nbytes, "warm": warm, "cold": cold, "reps": reps,
+                "plan": plan,
+                "cpu_oracle": {"s": round(cpu_s, 4), "GBps": round(nbytes / cpu_s / 1e9, 3),
+                               "threads": threads},
+                "gpu_over_cpu": round(cpu_s * 1e3 / warm["ms_median"], 1),
+                "parity": {"ok": ok, "max_err_over_tol": round(worst, 5)},
+            }), flush=True)
         del x, out, host
         torch.cuda.empty_cache()
     return 0

@@ -131,6 +131,22 @@ rd_status rd_reduce_1d(const float* x, int64_t n, int32_t op, float* out,
 rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
                         int32_t op, float* out, hipStream_t stream);
 
+/*
+ * Cumulative sum along the middle axis of a contiguous [outer, R, inner]
+ * array, out of the same shape:
+ *   reverse != 0:  out[o][r][i] = sum_{k = r .. R-1} x[o][k][i]
+ *   reverse == 0:  out[o][r][i] = sum_{k = 0 .. r}   x[o][k][i]
+ *   x, out  device pointers to outer*R*inner floats, 4-B aligned; out may be
+ *           x itself (in place) but must not overlap it otherwise
+ * fp32 adds in a fixed order (bitwise reproducible); each output is within
+ * the fp32 rounding of its terms, like the reductions.  Source: POPCORNBENCH
+ * Kimi-K2.6 level-1 problem 91 trace (reverse cumulative sum of a
+ * [32768, 32768] array along dim 1, y = cumsum(x.flip(1), 1).flip(1), spelled
+ * out as y[i][j] = x[i][j] + ... + x[i][N-1]).
+ */
+rd_status rd_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
+                        int32_t reverse, float* out, hipStream_t stream);
+
 /* Static, NUL-terminated name of a status code ("RD_OK", ...). */
 const char* rd_status_string(rd_status status);
 
@@ -152,8 +168,11 @@ typedef enum rd_path {
     RD_PATH_ROWS = 2,        /* inner == 1: a group of lanes per row piece */
     RD_PATH_ROWS_SHORT = 3,  /* inner == 1, R < 64: one lane per row */
     RD_PATH_COLS = 4,        /* inner > 128: a lane owns 4 adjacent columns */
-    RD_PATH_COLS_SMALL = 5   /* 2 <= inner <= 128: a wave loads 64 / ceil(inner/4)
+    RD_PATH_COLS_SMALL = 5,  /* 2 <= inner <= 128: a wave loads 64 / ceil(inner/4)
                                 adjacent rows per instruction */
+    RD_PATH_SCAN_ROWS = 6,   /* cumulative sum, inner == 1: a workgroup per row
+                                (piece) */
+    RD_PATH_SCAN_COLS = 7    /* cumulative sum, inner > 1: a lane per 4 columns */
 } rd_path;
 
 /* Chunk order of the pieces of one row on the ROWS path. */
@@ -198,6 +217,11 @@ rd_status rd_plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
 
 /* Plan of rd_sum_1d (the same as rd_plan_dim(cu_count, 1, n, 1, plan)). */
 rd_status rd_plan_1d(int cu_count, int64_t n, rd_plan* plan);
+
+/* Plan of rd_cumsum_dim for that shape (the tuning override's split and
+ * nontemporal fields apply). */
+rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                         rd_plan* plan);
 
 /*
  * Tuning override, process-wide, for measurement and tests: a field left at 0

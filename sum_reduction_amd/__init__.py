@@ -24,7 +24,8 @@ __all__ = [
     "RdError", "RdPlan", "RdTune", "library_path", "load", "rd_sum_1d", "rd_sum_dim",
     "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
     "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "sum", "tuning",
-    "PATH_NAMES", "OPS", "rd_reduce_1d", "rd_reduce_dim", "reduce",
+    "PATH_NAMES", "OPS", "rd_reduce_1d", "rd_reduce_dim", "reduce", "rd_cumsum_dim",
+    "rd_plan_cumsum", "cumsum",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +35,7 @@ RD_OK = 0
 # rd_op: the reductions (the sum is the method; the others share its kernels)
 OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
 PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
-              5: "cols_small"}
+              5: "cols_small", 6: "scan_rows", 7: "scan_cols"}
 ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
 COMBINE_NAMES = {0: "none", 1: "pass", 2: "last_block"}
 
@@ -100,6 +101,10 @@ def load():
     lib.rd_reduce_1d.restype = ctypes.c_int
     lib.rd_reduce_dim.argtypes = [vp, i64, i64, i64, i32, vp, vp]
     lib.rd_reduce_dim.restype = ctypes.c_int
+    lib.rd_cumsum_dim.argtypes = [vp, i64, i64, i64, i32, vp, vp]
+    lib.rd_cumsum_dim.restype = ctypes.c_int
+    lib.rd_plan_cumsum.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(RdPlan)]
+    lib.rd_plan_cumsum.restype = ctypes.c_int
     lib.rd_status_string.argtypes = [ctypes.c_int]
     lib.rd_status_string.restype = ctypes.c_char_p
     lib.rd_last_hip_error.argtypes = []
@@ -139,6 +144,13 @@ def rd_plan_dim(cu_count: int, outer: int, R: int, inner: int) -> RdPlan:
     plan = RdPlan()
     _check(load().rd_plan_dim(cu_count, outer, R, inner, ctypes.byref(plan)),
            "rd_plan_dim")
+    return plan
+
+
+def rd_plan_cumsum(cu_count: int, outer: int, R: int, inner: int) -> RdPlan:
+    plan = RdPlan()
+    _check(load().rd_plan_cumsum(cu_count, outer, R, inner, ctypes.byref(plan)),
+           "rd_plan_cumsum")
     return plan
 
 
@@ -284,6 +296,34 @@ def reduce(x, op="sum", dim: Optional[int] = None, out=None, stream=None):
     res = rd_reduce_dim(x, outer, shape[d], inner, op,
                         None if out is None else out.view(outer, inner), stream)
     return res.view(shape[:d] + shape[d + 1:])
+
+
+def rd_cumsum_dim(x, outer: int, R: int, inner: int, reverse: bool = True, out=None,
+                  stream=None):
+    """Cumulative sum along the middle axis of x viewed as [outer, R, inner]
+    (reverse: from the end, y[o, r, i] = sum_{k >= r} x[o, k, i]); ``out``
+    has x's shape (allocated when None; may be x itself)."""
+    _check_input(x, outer * R * inner)
+    out = _out_tensor(out, outer * R * inner, x.device, tuple(x.shape))
+    xp = x.data_ptr() if x.numel() else None
+    optr = out.data_ptr() if out.numel() else None
+    _check(load().rd_cumsum_dim(xp, outer, R, inner, int(bool(reverse)), optr,
+                                _stream_handle(stream)), "rd_cumsum_dim")
+    return out
+
+
+def cumsum(x, dim: int, reverse: bool = False, out=None, stream=None):
+    """torch.cumsum(x, dim) (reverse=False) or torch.cumsum(x.flip(dim),
+    dim).flip(dim) (reverse=True) for a contiguous float32 GPU tensor."""
+    shape = tuple(x.shape)
+    d = dim % len(shape)
+    outer = 1
+    for s in shape[:d]:
+        outer *= s
+    inner = 1
+    for s in shape[d + 1:]:
+        inner *= s
+    return rd_cumsum_dim(x, outer, shape[d], inner, reverse, out, stream)
 
 
 def sum(x, dim: Optional[int] = None, out=None, stream=None):

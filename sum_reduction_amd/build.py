@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "librd.so")
-SOURCES = ["rd_api.cpp", "rd_plan.cpp", "rd_kernels.hip"]
+SOURCES = ["rd_api.cpp", "rd_plan.cpp", "rd_kernels.hip", "rd_scan.hip"]
 ARCH = "gfx950"
 
 

@@ -240,6 +240,76 @@ rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
     return reduce_checked(x, outer, R, inner, op, out, stream);
 }
 
+rd_status rd_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
+                        int32_t reverse, float* out, hipStream_t stream) {
+    if (outer < 0 || R < 0 || inner < 0) return RD_ERR_INVALID_ARG;
+    const int64_t lim = INT64_MAX / 4;
+    if (outer && inner && inner > lim / outer) return RD_ERR_INVALID_ARG;
+    const int64_t nrow = outer * inner;
+    if (nrow && R && R > lim / nrow) return RD_ERR_INVALID_ARG;
+    const int64_t n = nrow * R;
+    if (n == 0) return RD_OK;  // nothing to write, no HIP call
+    if (!x || !out || !aligned4(x) || !aligned4(out)) return RD_ERR_INVALID_ARG;
+    if (out != x && overlap(x, n, out, n)) return RD_ERR_INVALID_ARG;
+    Device* dev = nullptr;
+    rd_status st = current_device(&dev);
+    if (st != RD_OK) return st;
+    rd_plan p;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        st = rd::plan_cumsum(dev->cu, outer, R, inner, g_tune_on ? &g_tune : nullptr, &p);
+    }
+    if (st != RD_OK) return st;
+    if (p.path == RD_PATH_NONE) return RD_OK;
+    if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
+    float* ws = nullptr;
+    if (p.workspace_bytes > 0) {
+        if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
+        hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
+                                              size_t(p.workspace_bytes), dev->pool, stream);
+        if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
+    }
+    const bool rev = reverse != 0;
+    hipError_t e = hipSuccess;
+    if (p.path == RD_PATH_SCAN_ROWS) {
+        if (p.split == 1) {
+            e = rd::launch_scan_rows(p, rev, x, out, outer, R, nullptr, nullptr, stream);
+        } else {
+            const int64_t m = outer * p.split;
+            float* totals = ws;
+            float* carries = ws + m;
+            e = rd::launch_scan_rows(p, rev, x, out, outer, R, nullptr, totals, stream);
+            if (e == hipSuccess) e = rd::launch_scan_carries(totals, carries, outer, p.split, stream);
+            if (e == hipSuccess)
+                e = rd::launch_scan_rows(p, rev, x, out, outer, R, carries, nullptr, stream);
+        }
+    } else {
+        if (p.split == 1) {
+            e = rd::launch_scan_cols(p, rev, x, out, outer, R, inner, nullptr, nullptr, stream);
+        } else {
+            const int64_t m = p.split * nrow;
+            float* totals = ws;
+            float* carries = ws + m;
+            e = rd::launch_scan_cols(p, rev, x, out, outer, R, inner, nullptr, totals, stream);
+            if (e == hipSuccess)
+                e = rd::launch_scan_slab_carries(rev, totals, carries, p.split, nrow, stream);
+            if (e == hipSuccess)
+                e = rd::launch_scan_cols(p, rev, x, out, outer, R, inner, carries, nullptr, stream);
+        }
+    }
+    if (ws) {
+        hipError_t f = hipFreeAsync(ws, stream);
+        if (e == hipSuccess && f != hipSuccess) return hip_fail(f, RD_ERR_HIP);
+    }
+    if (e != hipSuccess) return hip_fail(e, RD_ERR_LAUNCH);
+    return RD_OK;
+}
+
+rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner, rd_plan* plan) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return rd::plan_cumsum(cu_count, outer, R, inner, g_tune_on ? &g_tune : nullptr, plan);
+}
+
 rd_status rd_sum_1d(const float* x, int64_t n, float* out, hipStream_t stream) {
     return rd_reduce_1d(x, n, RD_OP_SUM, out, stream);
 }

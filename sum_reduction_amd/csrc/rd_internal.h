@@ -45,6 +45,32 @@ hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, int64_t o
 hipError_t launch_slab_combine(int op, const float* slab, int64_t S, int64_t n, float* out,
                                hipStream_t s);
 
+// Cumulative sums (rd_scan.hip).  Rows (inner == 1): item = (row, piece of
+// p.rows_per_split processing positions); totals != nullptr writes only the
+// piece totals, otherwise pieces are scanned from carry_in (nullptr: 0).
+hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, float* out,
+                            int64_t outer, int64_t R, const float* carry_in, float* totals,
+                            hipStream_t s);
+hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows, int64_t P,
+                               hipStream_t s);
+// Columns (inner >= 2): item = (64 lane-columns, slab of R, outer index).
+hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, float* out,
+                            int64_t outer, int64_t R, int64_t inner, const float* carry_in,
+                            float* totals, hipStream_t s);
+hipError_t launch_scan_slab_carries(bool reverse, const float* totals, float* carries, int64_t S,
+                                    int64_t n, hipStream_t s);
+
+// Planner of the cumulative sum (rd_plan.cpp).
+rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                      const rd_tune* tune, rd_plan* plan);
+// Row pieces of the row scan are whole multiples of kScanTile positions (a
+// multiple of every chunk size, 256 * slices).
+constexpr int64_t kScanTile = 4096;
+constexpr int kScanRowsChunkSlices = 4;   // 1024-element chunks by default
+constexpr int64_t kScanRowWavesMin = 4;   // rows per CU below which rows are cut
+constexpr int64_t kScanRowWavesSplit = 16;  // pieces per CU once they are cut
+constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan
+
 // Which kernel shapes this build instantiates for an operator (rd_kernels.hip).
 bool rows_shape_supported(int op, int group, int unroll);
 bool cols_shape_supported(int op, int col_waves, int row_waves, int unroll);

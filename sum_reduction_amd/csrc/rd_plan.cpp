@@ -239,4 +239,98 @@ rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op
     return plan_cols(cu_count, outer, R, inner, op, tune, plan);
 }
 
+rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                      const rd_tune* t, rd_plan* p) {
+    if (!p || cu_count < 1 || outer < 0 || R < 0 || inner < 0) return RD_ERR_INVALID_ARG;
+    memset(p, 0, sizeof(*p));
+    const int64_t lim = INT64_MAX / 4;
+    if (outer && R && inner) {
+        if (R > lim / outer || inner > lim / (outer * R)) return RD_ERR_INVALID_ARG;
+    }
+    p->nxcd = nxcd_for(cu_count);
+    p->split = 1;
+    if (outer == 0 || R == 0 || inner == 0) {
+        p->path = RD_PATH_NONE;
+        return RD_OK;
+    }
+    if (!nontemporal_choice(t, true, &p->nontemporal)) return RD_ERR_INVALID_ARG;
+    p->block_threads = kBlock;
+    p->passes = 1;
+    const int64_t cu = cu_count;
+    if (inner == 1) {
+        // one wave per row piece; pieces only when there are too few rows to
+        // keep kScanRowWavesMin waves per CU busy (then: piece totals, their
+        // scan, the scan from the carries -- x is read twice)
+        p->path = RD_PATH_SCAN_ROWS;
+        p->unroll = (t && t->unroll) ? t->unroll : kScanRowsChunkSlices;
+        if (p->unroll != 4 && p->unroll != 8) return RD_ERR_INVALID_ARG;
+        const int64_t tiles = ceil_div(R, kScanTile);
+        int64_t P = 1;
+        if (t && t->split) {
+            P = t->split;
+        } else if (outer < cu * kScanRowWavesMin) {
+            P = ceil_div(cu * kScanRowWavesSplit, outer);
+        }
+        if (P < 1) return RD_ERR_INVALID_ARG;
+        if (P > tiles) P = tiles;
+        const int64_t L = ceil_div(tiles, P) * kScanTile;
+        P = ceil_div(R, L);
+        p->split = P;
+        p->rows_per_split = L;
+        const int64_t b = ceil_div(outer * P, kBlock / kWave);
+        p->blocks = b < kMaxBlocks ? b : kMaxBlocks;
+        if (P > 1) {
+            p->passes = 3;
+            p->combine = RD_COMBINE_PASS;
+            p->workspace_bytes = 2 * outer * P * int64_t(sizeof(float));
+        }
+        return RD_OK;
+    }
+    // a lane per 4 columns (per row of 2 or 3), a wave per 64 lane-columns;
+    // slabs of R (totals, their scan, the scan from the carries) when there
+    // are fewer than 8 waves per CU
+    p->path = RD_PATH_SCAN_COLS;
+    p->unroll = (t && t->unroll) ? t->unroll : kScanColsUnroll;
+    if (p->unroll != 4 && p->unroll != 8 && p->unroll != 16) return RD_ERR_INVALID_ARG;
+    const int64_t lane_cols = inner >= 4 ? ceil_div(inner, 4) : 1;
+    const int64_t waves = ceil_div(lane_cols, kWave) * outer;
+    int64_t S = 1;
+    if (t && t->split) {
+        S = t->split;
+    } else if (waves < 8 * cu) {
+        S = ceil_div(8 * cu, waves);
+        int64_t cap = R / 64;
+        if (cap < 1) cap = 1;
+        if (S > cap) S = cap;
+    }
+    if (S < 1) return RD_ERR_INVALID_ARG;
+    split_rows(R, S, p);
+    // a block per (col_waves adjacent tiles, slab, outer index): the widest
+    // of 16, 8, 4 tiles that still gives every CU a block
+    const int64_t tiles = ceil_div(lane_cols, kWave);
+    if (t && t->col_waves) {
+        p->col_waves = t->col_waves;
+        if (p->col_waves != 4 && p->col_waves != 8 && p->col_waves != 16)
+            return RD_ERR_INVALID_ARG;
+    } else {
+        p->col_waves = 4;
+        for (int bw = 16; bw > 4; bw /= 2) {
+            if (tiles >= bw && ceil_div(tiles, bw) * p->split * outer >= cu) {
+                p->col_waves = bw;
+                break;
+            }
+        }
+    }
+    p->block_threads = p->col_waves * kWave;
+    const int64_t block_items = ceil_div(tiles, p->col_waves) * p->split * outer;
+    p->blocks = block_items < kMaxBlocks ? block_items : kMaxBlocks;
+    if (p->split > 1) {
+        if (p->split > INT64_MAX / 8 / (outer * inner)) return RD_ERR_INVALID_ARG;
+        p->passes = 3;
+        p->combine = RD_COMBINE_PASS;
+        p->workspace_bytes = 2 * p->split * outer * inner * int64_t(sizeof(float));
+    }
+    return RD_OK;
+}
+
 }  // namespace rd

@@ -1,0 +1,487 @@
+// rd_scan.hip -- gfx950 kernels of the fp32 cumulative sum along an axis.
+//
+// The POPCORNBENCH level-1 problem 91 trace computes a reverse cumulative sum
+// over the rows of a [32768, 32768] array, y = cumsum(x.flip(1), 1).flip(1),
+// i.e. y[i][j] = x[i][j] + ... + x[i][N-1], and notes that the flips of the
+// library formulation cost two extra passes; its own kernel gives each row to
+// one block that walks tiles from the right with a running carry and scans
+// each tile in the block.  Kept here: rows walked in processing order with a
+// running carry, each element read once and written once.  Changed for
+// wave64: a row (or row piece) belongs to one wave, not to a block, so there
+// is no barrier and no LDS -- the 64 lanes walk the row in chunks of
+// 256*K elements, every load and store a full 1 KB wave access, and the next
+// chunk's loads are issued before the current chunk is scanned and stored.
+// Positions are counted in processing order q (q = 0 is the first element
+// the sum takes: the row's last one for the reverse sum).
+//
+// Order of the adds within a chunk (fixed for a given plan): slice k of the
+// chunk holds q = 256k + 4l + j in lane l (j = 0..3);
+//   lane       s_j = ((x_0 + x_1) + ...) + x_j over its 4 elements
+//   wave       inclusive DPP scan of the lane totals s_3 (row_shr 1, 2, 4, 8,
+//              then row_bcast 15 and 31), shifted one lane for the exclusive e
+//   output     (carry + e) + s_j
+//   carry      carry + (the slice total, lane 63's inclusive value)
+// A row cut into pieces (few rows) runs in three kernels: the piece totals
+// (the same chunks, carry only), their exclusive scan in piece order, and the
+// scan of each piece from its carry.  The column scan (inner > 1) keeps one
+// running sum per column in a lane and walks R in processing order.
+#include <hip/hip_runtime.h>
+
+#include "rd_device.h"
+#include "rd_internal.h"
+
+namespace rd {
+namespace {
+
+// Inclusive scan of v over the 64 lanes of a wave (lane 0 first); every lane
+// must be active.
+__device__ __forceinline__ float wave_scan_inclusive(float v) {
+    v += dpp_or_zero<0x111>(v);         // row_shr:1
+    v += dpp_or_zero<0x112>(v);         // row_shr:2
+    v += dpp_or_zero<0x114>(v);         // row_shr:4
+    v += dpp_or_zero<0x118>(v);         // row_shr:8
+    v += dpp_or_zero<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
+    v += dpp_or_zero<0x143, 0xC>(v);    // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+__device__ __forceinline__ float lane63(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// The 4 elements at processing positions q .. q + 3 of a row of R, in
+// processing order, from one 16-byte load (REV: memory R - 4 - q .. R - 1 - q,
+// reversed).
+template <bool REV, bool NT>
+__device__ __forceinline__ v4f load_q4(const float* row, int64_t R, int64_t q) {
+    if constexpr (REV) {
+        const v4f m = load4<NT>(row + (R - 4 - q));
+        return v4f{m.w, m.z, m.y, m.x};
+    } else {
+        return load4<NT>(row + q);
+    }
+}
+
+template <bool REV>
+__device__ __forceinline__ void store_q4(float* row, int64_t R, int64_t q, v4f y) {
+    if constexpr (REV)
+        store4(row + (R - 4 - q), v4f{y.w, y.z, y.y, y.x});
+    else
+        store4(row + q, y);
+}
+
+// Positions q .. q + 3, those below q_end only (the others read as 0 / are
+// not written): the last chunk of a row.
+template <bool REV>
+__device__ __forceinline__ v4f load_q4_tail(const float* row, int64_t R, int64_t q,
+                                            int64_t q_end) {
+    v4f v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (q + j < q_end) v[j] = row[REV ? R - 1 - (q + j) : q + j];
+    return v;
+}
+
+template <bool REV>
+__device__ __forceinline__ void store_q4_tail(float* row, int64_t R, int64_t q, int64_t q_end,
+                                              v4f y) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (q + j < q_end) row[REV ? R - 1 - (q + j) : q + j] = y[j];
+}
+
+// Scan of one chunk held as K slices (v[k]: this lane's 4 elements of slice
+// k, processing order); y[k] receives the outputs.  Returns the new carry.
+template <int K, bool OUT>
+__device__ __forceinline__ float scan_chunk(const v4f (&v)[K], v4f (&y)[K], float carry) {
+    float e[K], tot[K];
+    v4f s[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        s[k].x = v[k].x;
+        s[k].y = s[k].x + v[k].y;
+        s[k].z = s[k].y + v[k].z;
+        s[k].w = s[k].z + v[k].w;
+        const float incl = wave_scan_inclusive(s[k].w);
+        e[k] = dpp_or_zero<0x138>(incl);  // wave_shr:1
+        tot[k] = lane63(incl);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if constexpr (OUT) {
+            const float pre = carry + e[k];
+            y[k] = v4f{pre + s[k].x, pre + s[k].y, pre + s[k].z, pre + s[k].w};
+        }
+        carry = carry + tot[k];
+    }
+    return carry;
+}
+
+// ------------------------------------------------------------ rows
+// One chunk step of a row: issue the loads of chunk q_load into `next`, then
+// scan chunk `cur` (already in flight) at q_cur and store it.  The two
+// buffers alternate between steps, so no register copy waits on a load.
+template <bool REV, int K, bool NT, bool OUT>
+__device__ __forceinline__ float rows_step(const float* row, float* orow, int64_t R,
+                                           int64_t q_cur, int64_t q_load, int64_t lq,
+                                           const v4f (&cur)[K], v4f (&next)[K], float carry) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) next[k] = load_q4<REV, NT>(row, R, q_load + 256 * k + lq);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before any of the scan
+    v4f y[K];
+    carry = scan_chunk<K, OUT>(cur, y, carry);
+    if constexpr (OUT) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) store_q4<REV>(orow, R, q_cur + 256 * k + lq, y[k]);
+    }
+    // keep the next step's scan below these stores: hoisted above them it
+    // would wait on the loads just issued
+    __builtin_amdgcn_sched_barrier(0);
+    return carry;
+}
+
+// The full chunks of [q_begin, q_end) (then the partial one), two buffers in
+// turn; the load issued during the last full chunk's step re-reads that chunk
+// (clamped index) and is not used.
+template <bool REV, int K, bool NT, bool OUT>
+__device__ __forceinline__ float rows_piece(const float* row, float* orow, int64_t R,
+                                            int64_t q_begin, int64_t q_end, int lane,
+                                            float carry) {
+    constexpr int64_t kChunk = 256 * K;
+    const int64_t lq = 4 * lane;
+    const int64_t nfull = q_end > q_begin ? (q_end - q_begin) / kChunk : 0;
+    const int64_t q_last = q_begin + (nfull - 1) * kChunk;
+    v4f a[K], b[K];
+    if (nfull > 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[k] = load_q4<REV, NT>(row, R, q_begin + 256 * k + lq);
+        int64_t c = 0;
+        for (; c + 2 <= nfull; c += 2) {
+            const int64_t q0 = q_begin + c * kChunk;
+            const int64_t q1 = q0 + kChunk;
+            const int64_t q2 = q1 + kChunk <= q_last ? q1 + kChunk : q_last;
+            carry = rows_step<REV, K, NT, OUT>(row, orow, R, q0, q1, lq, a, b, carry);
+            carry = rows_step<REV, K, NT, OUT>(row, orow, R, q1, q2, lq, b, a, carry);
+        }
+        if (c < nfull) {  // odd count: the last full chunk is in a
+            const int64_t q0 = q_begin + c * kChunk;
+            v4f y[K];
+            carry = scan_chunk<K, OUT>(a, y, carry);
+            if constexpr (OUT) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) store_q4<REV>(orow, R, q0 + 256 * k + lq, y[k]);
+            }
+        }
+    }
+    const int64_t qt = q_begin + nfull * kChunk;
+    if (qt < q_end) {  // the row's last, partial chunk
+        v4f y[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[k] = load_q4_tail<REV>(row, R, qt + 256 * k + lq, q_end);
+        carry = scan_chunk<K, OUT>(a, y, carry);
+        if constexpr (OUT) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) store_q4_tail<REV>(orow, R, qt + 256 * k + lq, q_end, y[k]);
+        }
+    }
+    return carry;
+}
+
+// Waves per SIMD the row scan is compiled for, 8 with 4-slice chunks (a
+// register budget of 512 / 8 = 64 VGPRs; the few spills sit outside the
+// chunk loop): the 32768 rows of the [32768, 32768] scan then fill the chip's
+// 256 * 4 * 8 wave slots in exactly 4 rounds.  8-slice chunks need 4.
+template <int K>
+constexpr int scan_rows_waves_per_simd() { return K <= 4 ? 8 : 4; }
+
+// Item = (row o, piece p): processing positions [p*L, min(R, (p+1)*L)), L a
+// multiple of the chunk.  One wave per item; the block's waves take
+// consecutive items.  totals != null: only the piece total (the final carry)
+// goes to totals[item]; otherwise the piece is scanned from carry
+// carry_in[item] (0 when carry_in is null) into out.  x and out may be the
+// same array: every element is loaded before it is stored, by the same lane,
+// and the re-read of a chunk (see rows_piece) happens before its store.
+template <bool REV, int K, bool NT>
+__global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_rows_kernel(
+    const float* x, float* out, int64_t outer, int64_t R,
+    int64_t P, int64_t L, const float* __restrict__ carry_in, float* __restrict__ totals) {
+    constexpr int kWaves = kBlock / kWave;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int64_t nitems = outer * P;
+    const int64_t wstride = int64_t(gridDim.x) * kWaves;
+    for (int64_t item = int64_t(blockIdx.x) * kWaves + wave; item < nitems; item += wstride) {
+        const int64_t o = item / P;
+        const int64_t p = item - o * P;
+        const int64_t q_begin = p * L;
+        const int64_t q_end = q_begin + L < R ? q_begin + L : R;
+        if (totals == nullptr) {
+            const float carry = carry_in != nullptr ? carry_in[item] : 0.f;
+            rows_piece<REV, K, NT, true>(x + o * R, out + o * R, R, q_begin, q_end, lane, carry);
+        } else {
+            const float t = rows_piece<REV, K, NT, false>(x + o * R, nullptr, R, q_begin, q_end,
+                                                          lane, 0.f);
+            if (lane == 0) totals[item] = t;
+        }
+    }
+}
+
+// Exclusive scan of the P piece totals of each row, in piece order:
+// carries[o*P + p] = totals[o*P] + ... + totals[o*P + p - 1].
+__global__ __launch_bounds__(kBlock) void scan_carries_kernel(const float* __restrict__ totals,
+                                                              float* __restrict__ carries,
+                                                              int64_t rows, int64_t P) {
+    const int64_t stride = int64_t(gridDim.x) * kBlock;
+    for (int64_t o = int64_t(blockIdx.x) * kBlock + threadIdx.x; o < rows; o += stride) {
+        float run = 0.f;
+        for (int64_t p = 0; p < P; ++p) {
+            carries[o * P + p] = run;
+            run = run + totals[o * P + p];
+        }
+    }
+}
+
+// ------------------------------------------------------------ columns
+// The running sums of a lane-column to one row: all 4 with one 16-byte store,
+// else only components keep .. V-1 (the row's last lane-column, or V < 4).
+template <int V>
+__device__ __forceinline__ void store_cols(float* q, int keep, v4f acc) {
+    if (V == 4 && keep == 0) {
+        store4(q, acc);
+    } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (j >= keep) q[j] = acc[j];
+    }
+}
+
+// One group step of a lane-column: issue the loads of the U rows at element
+// offset off_load into `next`, then add the U rows of `cur` (rows at off_cur)
+// to the running sums and store each; then meet the block's other waves.
+template <int V, int U, bool NT>
+__device__ __forceinline__ v4f cols_step(const float* p, float* q, int64_t off_cur,
+                                         int64_t off_load, int64_t dstep, int keep,
+                                         bool scan_out, const v4f (&cur)[U], v4f (&next)[U],
+                                         v4f acc) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) next[u] = loadv<V, NT>(p + off_load + u * dstep, 0.f);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the adds (as in rows_step)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        acc += cur[u];
+        if (scan_out) store_cols<V>(q + off_cur + u * dstep, keep, acc);
+    }
+    __syncthreads();
+    return acc;
+}
+
+// A lane owns lane-column lc: the V = min(4, inner) columns from 4*lc (the
+// row's last lane-column loads the row's last 4 floats and keeps only its
+// own, as the column reduction does).  A wave holds 64 lane-columns (a tile,
+// 1 KB of a row); a block holds BW adjacent tiles of one outer index o and one
+// slab s of R (block items are numbered tile group fastest, then slab, then
+// o), and its waves walk the slab's rows in processing order (REV: from the
+// last row) in lockstep, U rows per step with a barrier after each step.  In
+// lockstep, the cache lines two neighbouring tiles share at their edge (rows
+// need not be line-aligned) are written by both within one step, not rows
+// apart, so they leave the L2 whole.  Each step issues the next group's loads
+// before adding and storing the current group (two buffers in turn).
+// totals != null: only the slab totals go to totals[s][o][i]; otherwise the
+// slab is scanned from carry_in[s][o][i] (0 when null) into out.  x and out
+// may be the same array.
+template <bool REV, int V, int U, int BW, bool NT>
+__global__ __launch_bounds__(BW * kWave) void scan_cols_kernel(
+    const float* x, float* out, int64_t outer, int64_t R,
+    int64_t inner, int64_t ntiles, int64_t S, int64_t rps,
+    const float* __restrict__ carry_in, float* __restrict__ totals, uint32_t nxcd) {
+    constexpr int kWaves = BW;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const bool scan_out = totals == nullptr;
+    const int64_t ngt = (ntiles + kWaves - 1) / kWaves;  // tile groups per row
+    const int64_t nitems = ngt * S * outer;
+    for (int64_t item = xcd_block(nxcd); item < nitems; item += gridDim.x) {
+        const int64_t tg = item % ngt;
+        const int64_t rest = item / ngt;
+        const int64_t s = rest % S;
+        const int64_t o = rest / S;
+        const int64_t r_begin = s * rps;
+        const int64_t r_end = r_begin + rps < R ? r_begin + rps : R;
+        const int64_t m = r_end > r_begin ? r_end - r_begin : 0;
+        const int64_t ngroups = m / U;  // steps (and barriers) of every wave
+        const int64_t tile = tg * kWaves + wave;
+        if (tile >= ntiles) {  // a wave past the row's end only keeps step
+            for (int64_t g = 0; g < ngroups; ++g) __syncthreads();
+            continue;
+        }
+        // lanes past the row's end shadow the last lane-column and store nothing
+        const int64_t c = 4 * (tile * kWave + lane);
+        const bool live = c < inner;
+        const int64_t cl = V == 4 ? (c + 4 > inner ? inner - 4 : c) : 0;
+        const int keep = live ? int(c - cl) : V;
+        const int64_t cbase = (s * outer + o) * inner + cl;
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        if (live && scan_out && carry_in != nullptr) acc = loadv<V, false>(carry_in + cbase, 0.f);
+        // the k-th row in processing order is first + k*dstep (in elements)
+        const int64_t first = REV ? r_end - 1 : r_begin;
+        const int64_t dstep = REV ? -inner : inner;
+        const float* p = x + (o * R + first) * inner + cl;
+        float* q = out + (o * R + first) * inner + cl;
+        if (ngroups > 0) {
+            // the load issued during the last group's step re-reads that
+            // group (clamped) and is not used
+            const int64_t last = (ngroups - 1) * U * dstep;
+            v4f a[U], b[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) a[u] = loadv<V, NT>(p + u * dstep, 0.f);
+            int64_t g = 0;
+            for (; g + 2 <= ngroups; g += 2) {
+                const int64_t off0 = g * U * dstep;
+                const int64_t off1 = off0 + U * dstep;
+                const int64_t off2 = g + 2 < ngroups ? off1 + U * dstep : last;
+                acc = cols_step<V, U, NT>(p, q, off0, off1, dstep, keep, scan_out, a, b, acc);
+                acc = cols_step<V, U, NT>(p, q, off1, off2, dstep, keep, scan_out, b, a, acc);
+            }
+            if (g < ngroups) {
+                const int64_t off0 = g * U * dstep;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    acc += a[u];
+                    if (scan_out) store_cols<V>(q + off0 + u * dstep, keep, acc);
+                }
+                __syncthreads();
+            }
+            p += ngroups * U * dstep;
+            q += ngroups * U * dstep;
+        }
+        for (int64_t k = ngroups * U; k < m; ++k) {
+            acc += loadv<V, NT>(p, 0.f);
+            if (scan_out) store_cols<V>(q, keep, acc);
+            p += dstep;
+            q += dstep;
+        }
+        if (!scan_out)
+            for (int j = keep; j < V; ++j) totals[cbase + j] = acc[j];
+    }
+}
+
+// Exclusive scan over the S slabs of each (o, i), in processing order:
+// the reverse sum takes the last slab first.
+template <bool REV>
+__global__ __launch_bounds__(kBlock) void scan_slab_carries_kernel(
+    const float* __restrict__ totals, float* __restrict__ carries, int64_t S, int64_t n) {
+    const int64_t stride = int64_t(gridDim.x) * kBlock;
+    for (int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x; e < n; e += stride) {
+        float run = 0.f;
+        for (int64_t k = 0; k < S; ++k) {
+            const int64_t s = REV ? S - 1 - k : k;
+            carries[s * n + e] = run;
+            run = run + totals[s * n + e];
+        }
+    }
+}
+
+// ------------------------------------------------------------ launching
+template <typename T>
+struct same {
+    using type = T;
+};
+
+template <typename... K>
+hipError_t launch(void (*kernel)(K...), int64_t blocks, int threads, hipStream_t s,
+                  typename same<K>::type... args) {
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel),
+                           dim3(static_cast<uint32_t>(blocks)), dim3(threads), argv, 0, s);
+}
+
+int64_t grid_for(int64_t items) {
+    int64_t b = (items + kBlock - 1) / kBlock;
+    if (b < 1) b = 1;
+    return b > kMaxBlocks ? kMaxBlocks : b;
+}
+
+template <bool REV, int K>
+hipError_t rows_k(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
+                  const float* carry_in, float* totals, hipStream_t s) {
+    if (p.nontemporal)
+        return launch(scan_rows_kernel<REV, K, true>, p.blocks, kBlock, s, x, out, outer, R,
+                      p.split, p.rows_per_split, carry_in, totals);
+    return launch(scan_rows_kernel<REV, K, false>, p.blocks, kBlock, s, x, out, outer, R,
+                  p.split, p.rows_per_split, carry_in, totals);
+}
+
+template <bool REV>
+hipError_t rows_go(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
+                   const float* carry_in, float* totals, hipStream_t s) {
+    if (p.unroll == 8) return rows_k<REV, 8>(p, x, out, outer, R, carry_in, totals, s);
+    return rows_k<REV, 4>(p, x, out, outer, R, carry_in, totals, s);
+}
+
+template <bool REV, int V, int BW, bool NT>
+hipError_t cols_bw(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
+                   int64_t inner, int64_t ntiles, const float* carry_in, float* totals,
+                   hipStream_t s) {
+    const uint32_t nx = uint32_t(p.nxcd);
+    if (p.unroll == 16)
+        return launch(scan_cols_kernel<REV, V, 16, BW, NT>, p.blocks, BW * kWave, s, x, out,
+                      outer, R, inner, ntiles, p.split, p.rows_per_split, carry_in, totals, nx);
+    if (p.unroll == 8)
+        return launch(scan_cols_kernel<REV, V, 8, BW, NT>, p.blocks, BW * kWave, s, x, out,
+                      outer, R, inner, ntiles, p.split, p.rows_per_split, carry_in, totals, nx);
+    return launch(scan_cols_kernel<REV, V, 4, BW, NT>, p.blocks, BW * kWave, s, x, out, outer,
+                  R, inner, ntiles, p.split, p.rows_per_split, carry_in, totals, nx);
+}
+
+template <bool REV, int V, bool NT>
+hipError_t cols_go(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
+                   int64_t inner, const float* carry_in, float* totals, hipStream_t s) {
+    const int64_t lane_cols = inner >= 4 ? (inner + 3) / 4 : 1;
+    const int64_t ntiles = (lane_cols + kWave - 1) / kWave;
+    if (p.col_waves == 16)
+        return cols_bw<REV, V, 16, NT>(p, x, out, outer, R, inner, ntiles, carry_in, totals, s);
+    if (p.col_waves == 8)
+        return cols_bw<REV, V, 8, NT>(p, x, out, outer, R, inner, ntiles, carry_in, totals, s);
+    return cols_bw<REV, V, 4, NT>(p, x, out, outer, R, inner, ntiles, carry_in, totals, s);
+}
+
+template <bool REV, bool NT>
+hipError_t cols_v(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
+                  int64_t inner, const float* carry_in, float* totals, hipStream_t s) {
+    if (inner == 2) return cols_go<REV, 2, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
+    if (inner == 3) return cols_go<REV, 3, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
+    return cols_go<REV, 4, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
+}
+
+}  // namespace
+
+hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, float* out,
+                            int64_t outer, int64_t R, const float* carry_in, float* totals,
+                            hipStream_t s) {
+    return reverse ? rows_go<true>(p, x, out, outer, R, carry_in, totals, s)
+                   : rows_go<false>(p, x, out, outer, R, carry_in, totals, s);
+}
+
+hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows, int64_t P,
+                               hipStream_t s) {
+    return launch(scan_carries_kernel, grid_for(rows), kBlock, s, totals, carries, rows, P);
+}
+
+hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, float* out,
+                            int64_t outer, int64_t R, int64_t inner, const float* carry_in,
+                            float* totals, hipStream_t s) {
+    if (reverse)
+        return p.nontemporal ? cols_v<true, true>(p, x, out, outer, R, inner, carry_in, totals, s)
+                             : cols_v<true, false>(p, x, out, outer, R, inner, carry_in, totals, s);
+    return p.nontemporal ? cols_v<false, true>(p, x, out, outer, R, inner, carry_in, totals, s)
+                         : cols_v<false, false>(p, x, out, outer, R, inner, carry_in, totals, s);
+}
+
+hipError_t launch_scan_slab_carries(bool reverse, const float* totals, float* carries, int64_t S,
+                                    int64_t n, hipStream_t s) {
+    if (reverse)
+        return launch(scan_slab_carries_kernel<true>, grid_for(n), kBlock, s, totals, carries, S, n);
+    return launch(scan_slab_carries_kernel<false>, grid_for(n), kBlock, s, totals, carries, S, n);
+}
+
+}  // namespace rd

@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("rd_sum_1d", "rd_sum_dim", "rd_reduce_1d", "rd_reduce_dim",
                  "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
-                 "rd_plan_1d", "rd_tune_set", "rd_tune_supported"):
+                 "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "rd_cumsum_dim",
+                 "rd_plan_cumsum"):
         assert want in names
 
 
@@ -101,6 +102,28 @@ def test_reduce_rejects_unknown_operator(lib, host_buf):
         assert lib.rd_reduce_dim(base + 1, 2, 2, 2, op, out, None) == INVALID
 
 
+def test_cumsum_invalid_arguments(lib, host_buf):
+    base, _ = host_buf
+    out = base + 4 * 32
+    cases = [
+        (base, -1, 2, 2, out), (base, 2, -1, 2, out), (base, 2, 2, -1, out),
+        (base, 2 ** 40, 2 ** 40, 2, out),  # size overflow
+        (base, 2, 2, 2, None),             # null out
+        (None, 2, 2, 2, out),              # null x
+        (base + 1, 2, 2, 2, out),          # misaligned x
+        (base, 2, 2, 2, out + 2),          # misaligned out
+        (base, 2, 3, 4, base + 4 * 4),     # out partly over x (x holds 24 floats)
+        (base + 4 * 4, 2, 3, 4, base),     # x partly over out
+    ]
+    for x, o_, R, i, out_ in cases:
+        for rev in (0, 1):
+            assert lib.rd_cumsum_dim(x, o_, R, i, rev, out_, None) == INVALID, (o_, R, i, rev)
+    # nothing to write: RD_OK, no device needed, null pointers allowed
+    assert lib.rd_cumsum_dim(None, 0, 5, 3, 1, None, None) == OK
+    assert lib.rd_cumsum_dim(None, 4, 0, 3, 1, None, None) == OK
+    assert lib.rd_cumsum_dim(None, 4, 5, 0, 0, None, None) == OK
+
+
 def test_empty_output_needs_nothing(lib):
     # outer * inner == 0: nothing to write, RD_OK without a device, null ok
     assert lib.rd_sum_dim(None, 0, 5, 3, None, None) == OK
@@ -121,6 +144,8 @@ def test_no_device_is_reported(lib, host_buf):
     assert lib.rd_sum_1d(base, 8, base + 4 * 32, None) == NO_DEVICE
     assert lib.rd_sum_dim(base, 2, 2, 2, base + 4 * 32, None) == NO_DEVICE
     assert lib.rd_sum_1d(None, 0, base + 4 * 32, None) == NO_DEVICE
+    assert lib.rd_cumsum_dim(base, 2, 2, 2, 1, base + 4 * 32, None) == NO_DEVICE
+    assert lib.rd_cumsum_dim(base, 2, 2, 2, 1, base, None) == NO_DEVICE   # in place is valid
 
 
 def test_python_wrapper_rejects_cpu_tensors():
@@ -129,6 +154,8 @@ def test_python_wrapper_rejects_cpu_tensors():
         rd.rd_sum_1d(torch.ones(4))
     with pytest.raises(ValueError):
         rd.rd_sum_dim(torch.ones(4), 1, 4, 1)
+    with pytest.raises(ValueError):
+        rd.rd_cumsum_dim(torch.ones(4), 1, 4, 1)
 
 
 def test_wrapper_raises_with_status():

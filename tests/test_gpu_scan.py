@@ -1,0 +1,156 @@
+"""GPU parity of the cumulative sum (rd_cumsum_dim) against the oracle.
+
+Integer data (ints in [-8, 8]) keeps every running sum exact in fp32, so the
+GPU must match the oracle bit for bit, in both directions, for every shape
+here: rows around the 4096-element tile, columns around the 4-column lanes,
+forced splits into pieces / slabs, misaligned bases, in place.  Random data
+at the problem-91 size: every output within 1e-5 * (sum of |x| over its
+terms) + 1e-6, repeats bitwise identical.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sum_reduction_amd as rd
+import workloads
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _clear_tuning():
+    rd.rd_tune_set(None)
+    yield
+    rd.rd_tune_set(None)
+
+
+def _sweep(shapes, offsets, seed, tag, reverse_modes=(True, False)):
+    maxn = max(o * r * i for o, r, i in shapes)
+    data = workloads.small_ints(maxn + max(offsets) + 1, seed)
+    dev = H.upload(data)
+    lib = rd.load()
+    cases = [(s, off, rev) for s in shapes for off in offsets for rev in reverse_modes]
+    slots = H.OutSlots([o * r * i for (o, r, i), _, _ in cases])
+    H.say("%s: %d calls of rd_cumsum_dim" % (tag, len(cases)))
+    for k, ((o, r, i), off, rev) in enumerate(cases):
+        x = dev[off:off + o * r * i]
+        st = lib.rd_cumsum_dim(x.data_ptr() if x.numel() else None, o, r, i, int(rev),
+                               slots.ptr(k), H.stream_handle())
+        assert st == 0, ((o, r, i), off, rev, rd.rd_status_string(st))
+    outs = slots.fetch()
+    for k, ((o, r, i), off, rev) in enumerate(cases):
+        S, _ = oracle.cumsum_dim(data[off:off + o * r * i], o, r, i, rev, threads=2)
+        H.assert_bitwise_equal_oracle(outs[k], S, "%s shape=%s off=%d rev=%d"
+                                      % (tag, (o, r, i), off, rev))
+
+
+def test_small_shapes():
+    shapes = [(o, r, i) for o in range(5) for r in range(6) for i in range(6)]
+    _sweep(shapes, [0, 1, 3], 800, "scan small")
+
+
+def test_rows_around_tiles():
+    shapes = [(3, r, 1) for r in (15, 16, 17, 255, 4095, 4096, 4097, 8191, 8192, 12289)]
+    shapes += [(300, 5000, 1), (1, 100_003, 1), (2, 65536, 1)]
+    _sweep(shapes, [0, 1, 2, 3], 801, "scan rows")
+
+
+def test_columns():
+    shapes = [(o, r, i) for i in (2, 3, 4, 5, 7, 63, 64, 65, 255, 256, 257, 4095)
+              for (o, r) in ((1, 1), (3, 17), (2, 300))]
+    shapes += [(128, 64, 4095), (1, 5000, 5)]
+    _sweep(shapes, [0, 1, 3], 802, "scan cols")
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 7])
+def test_forced_splits(split):
+    """Rows cut into pieces and columns into slabs: totals, carries, scan."""
+    with rd.tuning(split=split):
+        _sweep([(1, 3 * 4096 + 5, 1), (3, 20000, 1), (1, 1000, 1), (2, 777, 9), (1, 5000, 4),
+                (3, 100, 2), (1, 64, 4095)], [0, 1], 810 + split, "scan split %d" % split)
+
+
+UNROLLS = [(4, 1, 4), (8, 1, 8), (4, 3, 16), (8, 3, 4), (16, 1, 16), (16, 5, 8)]
+
+
+@pytest.mark.parametrize("unroll,split,bw", UNROLLS, ids=["u%d_s%d_w%d" % t for t in UNROLLS])
+def test_unroll_variants(unroll, split, bw):
+    """Rows: 4- and 8-slice chunks (16 is a column-only depth); columns: 4, 8
+    and 16 rows per load group and 4, 8, 16 waves a block; around the chunk,
+    group and block-width boundaries (tiles of 256 columns)."""
+    rows = [(3, r, 1) for r in (1023, 1024, 1025, 2047, 2048, 2049, 3 * 2048 + 7, 5 * 4096 + 1)]
+    cols = [(2, r, i) for r in (7, 8, 9, 15, 16, 17, 33, 100) for i in (2, 3, 5, 300)]
+    cols += [(2, 37, i) for i in (1023, 1024, 1025, 2049, 4095, 4097)]
+    with rd.tuning(unroll=unroll, split=split, col_waves=bw):
+        _sweep(cols, [0, 1], 850 + unroll + split, "scan cols u%d s%d w%d" % (unroll, split, bw))
+    if unroll != 16:
+        with rd.tuning(unroll=unroll, split=split):
+            _sweep(rows, [0, 3], 860 + unroll + split, "scan rows u%d s%d" % (unroll, split))
+
+
+def test_default_splits():
+    """Few rows or columns: the planner cuts them itself."""
+    for shape in ((1, 1 << 20, 1), (7, 100_000, 1), (1, 100_000, 4), (2, 50_000, 33)):
+        p = rd.rd_plan_cumsum(256, *shape).as_dict()
+        assert p["split"] > 1 and p["passes"] == 3, (shape, p)
+    _sweep([(1, 1 << 20, 1), (7, 100_000, 1), (1, 100_000, 4), (2, 50_000, 33)], [0], 820,
+           "scan default splits")
+
+
+def test_in_place():
+    t = H.torch()
+    for shape in ((3, 10_000, 1), (2, 300, 17), (1, 1 << 18, 1)):
+        n = shape[0] * shape[1] * shape[2]
+        a = workloads.small_ints(n, 830)
+        x = H.upload(a)
+        rd.rd_cumsum_dim(x, *shape, reverse=True, out=x)
+        S, _ = oracle.cumsum_dim(a, *shape, True)
+        H.assert_bitwise_equal_oracle(x.cpu().numpy(), S, "in place %s" % (shape,))
+
+
+def test_special_values():
+    """A NaN or Inf reaches every output whose sum includes it, and no other."""
+    a = np.ones((3, 9000), np.float32)
+    a[1, 5000] = np.nan
+    a[2, 100] = np.inf
+    got = rd.rd_cumsum_dim(H.upload(a), 3, 9000, 1, reverse=True).cpu().numpy().reshape(3, 9000)
+    assert np.isnan(got[1, :5001]).all() and np.isfinite(got[1, 5001:]).all()
+    assert np.isinf(got[2, :101]).all() and np.isfinite(got[2, 101:]).all()
+    assert np.array_equal(got[0], np.arange(9000, 0, -1, dtype=np.float32))
+    got = rd.rd_cumsum_dim(H.upload(a), 3, 9000, 1, reverse=False).cpu().numpy().reshape(3, 9000)
+    assert np.isfinite(got[1, :5000]).all() and np.isnan(got[1, 5000:]).all()
+
+
+def test_torch_style_cumsum():
+    a = workloads.small_ints(4 * 5 * 6, 840).reshape(4, 5, 6)
+    x = H.upload(a).view(4, 5, 6)
+    for dim in range(3):
+        f = rd.cumsum(x, dim).cpu().numpy()
+        assert np.array_equal(f, np.cumsum(a.astype(np.int64), dim).astype(np.float32))
+        r = rd.cumsum(x, dim, reverse=True).cpu().numpy()
+        want = np.flip(np.cumsum(np.flip(a.astype(np.int64), dim), dim), dim)
+        assert np.array_equal(r, want.astype(np.float32))
+
+
+@pytest.mark.slow
+def test_problem91_full_size():
+    """[32768, 32768] reverse cumulative sum along dim 1, U[0, 1): every
+    output against the oracle (in row blocks), 3 repeats bitwise equal."""
+    w = workloads.SCAN_WORKLOADS["revcumsum_32768x32768"]
+    host = workloads.generate(w)
+    x = H.upload(host)
+    t = H.torch()
+    out = t.empty_like(x)
+    rd.rd_cumsum_dim(x, w.outer, w.R, w.inner, reverse=True, out=out)
+    got = out.cpu().numpy().reshape(w.outer, w.R)
+    for _ in range(3):
+        again = rd.rd_cumsum_dim(x, w.outer, w.R, w.inner, reverse=True)
+        assert t.equal(again, out)
+        del again
+    block = 1024
+    for o0 in range(0, w.outer, block):
+        rows = host[o0 * w.R:(o0 + block) * w.R]
+        S, A = oracle.cumsum_dim(rows, block, w.R, 1, True)
+        H.assert_within_tolerance(got[o0:o0 + block].reshape(-1), S.reshape(-1), A.reshape(-1),
+                                  "problem 91 rows %d.." % o0)

@@ -195,3 +195,67 @@ def test_default_plans_are_built_for_every_operator():
                        for op in ops)
         if p["path"] == "cols_small":
             assert all(rd.rd_tune_supported("cols_small", 0, 0, p["unroll"], op) for op in ops)
+
+
+def _scan_invariants(p, outer, R, inner):
+    d = p.as_dict()
+    assert d["path"] == ("scan_rows" if inner == 1 else "scan_cols")
+    # the pieces / slabs cover R exactly, none empty
+    assert p.split >= 1 and p.rows_per_split >= 1
+    assert p.split * p.rows_per_split >= R > (p.split - 1) * p.rows_per_split
+    if inner == 1:
+        assert p.rows_per_split % 4096 == 0           # whole tiles per piece
+        assert p.blocks == min(-(-outer * p.split // 4), 1 << 20)   # a wave per piece
+        ws = 2 * outer * p.split * 4 if p.split > 1 else 0
+    else:
+        tiles = -(-(-(-inner // 4) if inner >= 4 else 1) // 64)
+        bw = p.col_waves
+        assert bw in (4, 8, 16) and p.block_threads == 64 * bw
+        assert bw == 4 or tiles >= bw
+        assert p.blocks == min(-(-tiles // bw) * p.split * outer, 1 << 20)
+        ws = 2 * p.split * outer * inner * 4 if p.split > 1 else 0
+    assert p.workspace_bytes == ws
+    assert p.passes == (3 if p.split > 1 else 1)
+
+
+def test_cumsum_plans():
+    """Rows: a wave per row (problem 91: 32768 rows, no pieces, 4 rows per
+    block); few rows are cut into pieces of whole 4096-element tiles.
+    Columns: a wave per 64 lane-columns, slabs of R when there are too few
+    waves."""
+    p = rd.rd_plan_cumsum(CU, 32768, 32768, 1)
+    assert p.as_dict()["path"] == "scan_rows" and p.split == 1 and p.blocks == 8192
+    assert p.workspace_bytes == 0
+    p = rd.rd_plan_cumsum(CU, 1, 1 << 20, 1)
+    assert p.split == 256 and p.rows_per_split == 4096 and p.passes == 3
+    p = rd.rd_plan_cumsum(CU, 128, 4096, 4095)
+    assert p.as_dict()["path"] == "scan_cols" and p.split == 1
+    assert p.col_waves == 8 and p.blocks == 256         # 16 tiles a row: 2 blocks of 8
+    rng = np.random.default_rng(5)
+    for _ in range(3000):
+        outer, R, inner = (int(v) for v in rng.integers(1, [3000, 200_000, 5000]))
+        if rng.random() < 0.3:
+            inner = 1
+        if rng.random() < 0.2:
+            outer = int(rng.integers(1, 8))
+        _scan_invariants(rd.rd_plan_cumsum(int(rng.integers(1, 300)), outer, R, inner),
+                         outer, R, inner)
+
+
+def test_cumsum_forced_split():
+    with rd.tuning(split=5):
+        p = rd.rd_plan_cumsum(CU, 2, 3 * 4096 + 1, 1)   # 4 tiles: at most 4 pieces
+        assert p.split == 4 and p.rows_per_split == 4096
+        p = rd.rd_plan_cumsum(CU, 2, 100, 7)
+        assert p.split == 5 and p.rows_per_split == 20
+        p = rd.rd_plan_cumsum(CU, 2, 3, 7)              # at most R slabs
+        assert p.split == 3 and p.rows_per_split == 1
+
+
+def test_cumsum_degenerate_plans():
+    for shape in ((0, 5, 5), (5, 0, 5), (5, 5, 0)):
+        assert rd.rd_plan_cumsum(CU, *shape).as_dict()["path"] == "none"
+    with pytest.raises(rd.RdError):
+        rd.rd_plan_cumsum(0, 1, 1, 1)
+    with pytest.raises(rd.RdError):
+        rd.rd_plan_cumsum(CU, -1, 1, 1)

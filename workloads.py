@@ -94,6 +94,17 @@ WORKLOADS = {
     )
 }
 
+# The reverse cumulative sum of the POPCORNBENCH level-1 problem 91 trace:
+# [32768, 32768] along dim 1, torch.rand input (U[0, 1)); the trace names no
+# seed, 91 is ours.  A scan, kept apart from the reductions above.
+SCAN_WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("revcumsum_32768x32768", (32768, 32768), 32768, 32768, 1, "uniform",
+                 seed=91),
+    )
+}
+
 
 def _threads() -> int:
     try:
