@@ -41,19 +41,26 @@ METRIC = "HBM GB/s & % of peak: fp32 sum n=1e9; [128,4096,4095] dim-1 reduce"
 PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 STEP_WORKLOADS = ["normal_1e9", "cols_128x4096x4095"]
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCE = os.path.join(ROOT, "sum_reduction_amd", "csrc", "rd_kernels.hip")
+CSRC = os.path.join(ROOT, "sum_reduction_amd", "csrc")
+# the device code of the reductions and of the scans (a counter summary taken
+# on other sources no longer describes the kernels)
+KERNEL_SOURCES = {"reduce": ("rd_kernels.hip", "rd_device.h"),
+                  "scan": ("rd_scan.hip", "rd_device.h")}
 
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_digest(kind: str = "reduce") -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kind: str = "reduce"):
     """HBM bytes per launch of the workload's main kernel from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source
     (else None)."""
@@ -63,7 +70,7 @@ def measured_traffic(workload: str):
     text = open(path).read()
     digest = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     value = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not digest or not value or digest.group(1) != kernel_source_digest():
+    if not digest or not value or digest.group(1) != kernel_source_digest(kind):
         return None
     return float(value.group(1))
 
@@ -108,10 +115,16 @@ def main(argv=None):
                     choices=["sum", "sumsq", "max", "min"],
                     help="with --report: the reductions to time (default: sum)")
     ap.add_argument("--scan", action="store_true",
-                    help="with --report: the cumulative sums (problem 91's reverse "
-                    "cumsum of [32768, 32768], plus each --scan-shape) instead")
+                    help="with --report: the cumulative sums instead (problem 91's "
+                    "[32768, 32768] rows, then each --scan-shape)")
     ap.add_argument("--scan-shape", action="append", default=None, metavar="OxRxI",
                     help="with --report --scan: also a cumulative sum of this shape")
+    ap.add_argument("--reps", type=int, default=0,
+                    help="with --report: timed calls per measurement (default 200 "
+                    "under 1 GiB, else 30)")
+    ap.add_argument("--no-oracle", action="store_true",
+                    help="with --report: skip the oracle and the parity check "
+                    "(short runs under a profiler)")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="only run a device-to-device copy of this many bytes 3 times "
                          "(a known-size kernel for calibrating HBM byte counters)")
@@ -306,10 +319,31 @@ def report(args, dev, cu):
         out = torch.empty(w.out_numel, dtype=torch.float32, device=dev)
         for op in (args.op or ["sum"]):
             log("report: %s %s" % (w.name, op))
-            print(json.dumps(report_one(w, op, host, x, out, flush, threads, cu)), flush=True)
+            print(json.dumps(report_one(w, op, host, x, out, flush, threads, cu, args)),
+                  flush=True)
         del x, out, host
         torch.cuda.empty_cache()
     return 0
+
+
+def _median_ms(fn, reps):
+    """Median of `reps` event-timed calls of fn (the GPU kept busy while the
+    host enqueues each call)."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        torch.cuda._sleep(200_000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    return ms[len(ms) // 2]
 
 
 def report_scan(args, dev, cu):
@@ -325,7 +359,7 @@ def report_scan(args, dev, cu):
 
     threads = oracle.default_threads()
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    todo = [] if args.scan_shape else list(workloads.SCAN_WORKLOADS.values())
+    todo = list(workloads.SCAN_WORKLOADS.values())
     for spec in args.scan_shape or []:
         o, r, i = (int(v) for v in spec.lower().split("x"))
         todo.append(workloads.Workload("scan_%dx%dx%d" % (o, r, i), (o, r, i), o, r, i,
@@ -335,6 +369,18 @@ def report_scan(args, dev, cu):
         x = torch.from_numpy(host).to(dev)
         out = torch.empty_like(x)
         nbytes = 8 * w.numel
+        # context, same bytes: a plain device copy (the read + write stream's
+        # practical ceiling) and, for the problem 91 rows, the pages' library
+        # formulation, cumsum of the flipped rows flipped back
+        ctx = {"copy_ms": round(_median_ms(lambda: out.copy_(x), 20), 5)}
+        if w.name in workloads.SCAN_WORKLOADS:
+            xv = x.view(w.outer, w.R)
+            ctx["torch_flip_cumsum_flip_ms"] = round(
+                _median_ms(lambda: torch.cumsum(xv.flip(1), 1).flip(1), 5), 5)
+            ctx["torch_cumsum_ms"] = round(
+                _median_ms(lambda: torch.cumsum(xv, 1, out=out.view(w.outer, w.R)), 5), 5)
+        print(json.dumps({"workload": w.name, "op": "context", "algorithmic_bytes": nbytes,
+                          **ctx}), flush=True)
         for rev in (True, False):
             log("report: cumsum %s reverse=%d" % (w.name, rev))
 
@@ -344,7 +390,7 @@ def report_scan(args, dev, cu):
             for _ in range(3):
                 call()
             torch.cuda.synchronize()
-            reps = 30 if nbytes >= (1 << 30) else 200
+            reps = args.reps or (30 if nbytes >= (1 << 30) else 200)
 
             def timed(cold):
                 ms = []
@@ -366,6 +412,13 @@ def report_scan(args, dev, cu):
                         "frac_of_peak": round(nbytes / med / 1e6 / PEAK_GBS, 4)}
 
             warm, cold = timed(False), timed(True)
+            plan = rd.rd_plan_cumsum(cu, w.outer, w.R, w.inner).as_dict()
+            line = {"workload": w.name, "op": "cumsum", "reverse": rev, "shape": list(w.shape),
+                    "algorithmic_bytes": nbytes, "warm": warm, "cold": cold, "reps": reps,
+                    "plan": plan}
+            if args.no_oracle:
+                print(json.dumps(line), flush=True)
+                continue
             got = out.cpu().numpy().reshape(w.outer, w.R * w.inner)
             # the oracle in blocks of outer indices (its fp64 outputs of the
             # whole array would not fit comfortably in host memory)
@@ -383,22 +436,19 @@ def report_scan(args, dev, cu):
                     r = np.abs(g.astype(np.float64) - S.reshape(-1)) / oracle.tolerance(
                         A.reshape(-1))
                 worst = max(worst, float(np.nanmax(r)))
-            plan = rd.rd_plan_cumsum(cu, w.outer, w.R, w.inner).as_dict()
-            print(json.dumps({
-                "workload": w.name, "op": "cumsum", "reverse": rev, "shape": list(w.shape),
-                "algorithmic_bytes": nbytes, "warm": warm, "cold": cold, "reps": reps,
-                "plan": plan,
+            line.update({
                 "cpu_oracle": {"s": round(cpu_s, 4), "GBps": round(nbytes / cpu_s / 1e9, 3),
                                "threads": threads},
                 "gpu_over_cpu": round(cpu_s * 1e3 / warm["ms_median"], 1),
                 "parity": {"ok": ok, "max_err_over_tol": round(worst, 5)},
-            }), flush=True)
+            })
+            print(json.dumps(line), flush=True)
         del x, out, host
         torch.cuda.empty_cache()
     return 0
 
 
-def report_one(w, op, host, x, out, flush, threads, cu):
+def report_one(w, op, host, x, out, flush, threads, cu, args):
     """One report line: workload `w` reduced with `op`, GPU warm and cold,
     the oracle's host time, parity."""
     import numpy as np
@@ -414,7 +464,7 @@ def report_one(w, op, host, x, out, flush, threads, cu):
             rd.rd_reduce_dim(x, w.outer, w.R, w.inner, op, out=out)
 
     small = w.in_bytes < (1 << 30)
-    reps = 200 if small else 30
+    reps = args.reps or (200 if small else 30)
     for _ in range(3):
         call()
     torch.cuda.synchronize()
@@ -442,6 +492,12 @@ def report_one(w, op, host, x, out, flush, threads, cu):
 
     warm = timed(False)
     cold = timed(True)
+    plan = (rd.rd_plan_1d(cu, w.numel) if w.full_reduce
+            else rd.rd_plan_dim(cu, w.outer, w.R, w.inner)).as_dict()
+    if args.no_oracle:
+        return {"workload": w.name, "op": op, "shape": list(w.shape),
+                "algorithmic_bytes": w.algorithmic_bytes, "warm": warm, "cold": cold,
+                "reps": reps, "plan": plan}
     got = out.cpu().numpy().reshape(-1)
     t0 = time.perf_counter()
     if w.full_reduce:
@@ -453,8 +509,6 @@ def report_one(w, op, host, x, out, flush, threads, cu):
     with np.errstate(invalid="ignore"):
         err = np.abs(got.astype(np.float64) - S.reshape(-1))
     tol = oracle.tolerance(A.reshape(-1))
-    plan = (rd.rd_plan_1d(cu, w.numel) if w.full_reduce
-            else rd.rd_plan_dim(cu, w.outer, w.R, w.inner)).as_dict()
     line = {
         "workload": w.name, "op": op, "shape": list(w.shape),
         "algorithmic_bytes": w.algorithmic_bytes,

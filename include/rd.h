@@ -170,9 +170,10 @@ typedef enum rd_path {
     RD_PATH_COLS = 4,        /* inner > 128: a lane owns 4 adjacent columns */
     RD_PATH_COLS_SMALL = 5,  /* 2 <= inner <= 128: a wave loads 64 / ceil(inner/4)
                                 adjacent rows per instruction */
-    RD_PATH_SCAN_ROWS = 6,   /* cumulative sum, inner == 1: a workgroup per row
+    RD_PATH_SCAN_ROWS = 6,   /* cumulative sum, inner == 1: a wave per row
                                 (piece) */
-    RD_PATH_SCAN_COLS = 7    /* cumulative sum, inner > 1: a lane per 4 columns */
+    RD_PATH_SCAN_COLS = 7    /* cumulative sum, inner > 1: a lane per 4 columns,
+                                a workgroup of col_waves waves per tile group */
 } rd_path;
 
 /* Chunk order of the pieces of one row on the ROWS path. */
@@ -196,16 +197,22 @@ typedef struct rd_plan {
     int32_t path;            /* rd_path */
     int32_t block_threads;   /* threads per workgroup of the main pass */
     int32_t group;           /* ROWS: lanes that share one row piece (64|256) */
-    int32_t col_waves;       /* COLS: waves side by side across columns */
+    int32_t col_waves;       /* COLS, SCAN_COLS: waves side by side across
+                                columns */
     int32_t row_waves;       /* COLS: waves of one workgroup taking turns in R */
-    int32_t unroll;          /* 16-byte loads in flight per lane */
+    int32_t unroll;          /* 16-byte loads in flight per lane (SCAN_ROWS:
+                                1 KB slices per chunk; SCAN_COLS: rows per
+                                load group) */
     int32_t nxcd;            /* XCDs the workgroup numbering is spread over */
     int32_t passes;          /* kernel launches of the planned combine */
     int32_t combine;         /* rd_combine */
     int32_t order;           /* ROWS: rd_order; 0 elsewhere */
-    int32_t nontemporal;     /* 1: main-pass loads carry the streaming hint */
-    int64_t split;           /* ROWS: pieces per row; COLS*: slabs of R */
-    int64_t rows_per_split;  /* COLS*: rows per slab */
+    int32_t nontemporal;     /* 1: main-pass loads (and the scans' stores)
+                                carry the streaming hint */
+    int64_t split;           /* ROWS, SCAN_ROWS: pieces per row; COLS*,
+                                SCAN_COLS: slabs of R */
+    int64_t rows_per_split;  /* COLS*, SCAN_COLS: rows per slab; SCAN_ROWS:
+                                positions per piece */
     int64_t blocks;          /* workgroups of the main pass */
     int64_t workspace_bytes; /* stream-ordered scratch (0 if passes == 1) */
 } rd_plan;
@@ -218,8 +225,9 @@ rd_status rd_plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
 /* Plan of rd_sum_1d (the same as rd_plan_dim(cu_count, 1, n, 1, plan)). */
 rd_status rd_plan_1d(int cu_count, int64_t n, rd_plan* plan);
 
-/* Plan of rd_cumsum_dim for that shape (the tuning override's split and
- * nontemporal fields apply). */
+/* Plan of rd_cumsum_dim for that shape (the tuning override's split,
+ * unroll -- SCAN_ROWS 4 or 8, SCAN_COLS 4, 8 or 16 --, col_waves -- SCAN_COLS
+ * 4, 8 or 16 -- and nontemporal fields apply). */
 rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
                          rd_plan* plan);
 
@@ -233,11 +241,12 @@ rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
  */
 typedef struct rd_tune {
     int32_t group;           /* ROWS: 64 or 256 */
-    int32_t col_waves;       /* COLS */
+    int32_t col_waves;       /* COLS; SCAN_COLS: 4, 8 or 16 */
     int32_t row_waves;       /* COLS */
-    int32_t unroll;          /* ROWS, COLS: 2, 4, 8 or 16 */
+    int32_t unroll;          /* ROWS, COLS: 2, 4, 8 or 16 (scans: see
+                                rd_plan_cumsum) */
     int32_t order;           /* ROWS: rd_order */
-    int32_t nontemporal;     /* ROWS, COLS: 1 = off, 2 = on */
+    int32_t nontemporal;     /* every path: 1 = off, 2 = on */
     int32_t combine;         /* ROWS: 1 = second pass, 2 = last workgroup */
     int32_t path;            /* inner >= 4: RD_PATH_COLS or RD_PATH_COLS_SMALL
                                 (the latter for inner <= 256) */

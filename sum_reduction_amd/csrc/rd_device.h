@@ -46,8 +46,15 @@ __device__ __forceinline__ v4f loadv(const float* p, float fill) {
     }
 }
 
-// Four floats to a 4-byte-aligned address: one global_store_dwordx4.
-__device__ __forceinline__ void store4(float* p, v4f v) { __builtin_memcpy(p, &v, sizeof(v)); }
+// Four floats to a 4-byte-aligned address: one global_store_dwordx4, with
+// the nontemporal (streaming) hint when NT.
+template <bool NT>
+__device__ __forceinline__ void store4(float* p, v4f v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<v4f_a4*>(p));
+    else
+        __builtin_memcpy(p, &v, sizeof(v));
+}
 
 // v moved between lanes by a DPP control (gfx9 encoding); lanes whose source
 // is outside the pattern, or whose row is masked off, get 0.
