@@ -172,8 +172,12 @@ typedef enum rd_path {
                                 adjacent rows per instruction */
     RD_PATH_SCAN_ROWS = 6,   /* cumulative sum, inner == 1: a wave per row
                                 (piece) */
-    RD_PATH_SCAN_COLS = 7    /* cumulative sum, inner > 1: a lane per 4 columns,
-                                a workgroup of col_waves waves per tile group */
+    RD_PATH_SCAN_COLS = 7,   /* cumulative sum, inner > 128: a lane per 4
+                                columns, a workgroup of col_waves waves per
+                                tile group */
+    RD_PATH_SCAN_COLS_SMALL = 8  /* cumulative sum, 2 <= inner <= 128: several
+                                    rows per load instruction, scanned across
+                                    the wave */
 } rd_path;
 
 /* Chunk order of the pieces of one row on the ROWS path. */

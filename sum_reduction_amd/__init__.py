@@ -35,7 +35,7 @@ RD_OK = 0
 # rd_op: the reductions (the sum is the method; the others share its kernels)
 OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
 PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
-              5: "cols_small", 6: "scan_rows", 7: "scan_cols"}
+              5: "cols_small", 6: "scan_rows", 7: "scan_cols", 8: "scan_cols_small"}
 ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
 COMBINE_NAMES = {0: "none", 1: "pass", 2: "last_block"}
 

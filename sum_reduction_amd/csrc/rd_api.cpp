@@ -284,17 +284,23 @@ rd_status rd_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
                 e = rd::launch_scan_rows(p, rev, x, out, outer, R, carries, nullptr, stream);
         }
     } else {
+        const bool small = p.path == RD_PATH_SCAN_COLS_SMALL;
+        auto cols = [&](const float* carry_in, float* totals) {
+            return small ? rd::launch_scan_small(p, rev, x, out, outer, R, inner, carry_in, totals,
+                                                 stream)
+                         : rd::launch_scan_cols(p, rev, x, out, outer, R, inner, carry_in, totals,
+                                                stream);
+        };
         if (p.split == 1) {
-            e = rd::launch_scan_cols(p, rev, x, out, outer, R, inner, nullptr, nullptr, stream);
+            e = cols(nullptr, nullptr);
         } else {
             const int64_t m = p.split * nrow;
             float* totals = ws;
             float* carries = ws + m;
-            e = rd::launch_scan_cols(p, rev, x, out, outer, R, inner, nullptr, totals, stream);
+            e = cols(nullptr, totals);
             if (e == hipSuccess)
                 e = rd::launch_scan_slab_carries(rev, totals, carries, p.split, nrow, stream);
-            if (e == hipSuccess)
-                e = rd::launch_scan_cols(p, rev, x, out, outer, R, inner, carries, nullptr, stream);
+            if (e == hipSuccess) e = cols(carries, nullptr);
         }
     }
     if (ws) {

@@ -57,6 +57,9 @@ hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows
 hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, float* out,
                             int64_t outer, int64_t R, int64_t inner, const float* carry_in,
                             float* totals, hipStream_t s);
+hipError_t launch_scan_small(const rd_plan& p, bool reverse, const float* x, float* out,
+                             int64_t outer, int64_t R, int64_t inner, const float* carry_in,
+                             float* totals, hipStream_t s);
 hipError_t launch_scan_slab_carries(bool reverse, const float* totals, float* carries, int64_t S,
                                     int64_t n, hipStream_t s);
 
@@ -70,6 +73,8 @@ constexpr int kScanRowsChunkSlices = 4;   // 1024-element chunks by default
 constexpr int64_t kScanRowWavesMin = 4;   // rows per CU below which rows are cut
 constexpr int64_t kScanRowWavesSplit = 16;  // pieces per CU once they are cut
 constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan
+constexpr int kScanSmallUnroll = 8;       // load instructions per step, small inner
+constexpr int64_t kScanSmallWavesPerCu = 16;
 
 // Which kernel shapes this build instantiates for an operator (rd_kernels.hip).
 bool rows_shape_supported(int op, int group, int unroll);

@@ -257,6 +257,11 @@ rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
     p->block_threads = kBlock;
     p->passes = 1;
     const int64_t cu = cu_count;
+    const int32_t forced = t ? t->path : 0;
+    if (inner == 1 ? (forced && forced != RD_PATH_SCAN_ROWS)
+                   : (forced && forced != RD_PATH_SCAN_COLS && forced != RD_PATH_SCAN_COLS_SMALL))
+        return RD_ERR_INVALID_ARG;
+    if (forced == RD_PATH_SCAN_COLS_SMALL && inner > 2 * kSmallInner) return RD_ERR_INVALID_ARG;
     if (inner == 1) {
         // one wave per row piece; pieces only when there are too few rows to
         // keep kScanRowWavesMin waves per CU busy (then: piece totals, their
@@ -283,6 +288,37 @@ rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
             p->passes = 3;
             p->combine = RD_COMBINE_PASS;
             p->workspace_bytes = 2 * outer * P * int64_t(sizeof(float));
+        }
+        return RD_OK;
+    }
+    if (forced == RD_PATH_SCAN_COLS_SMALL || (!forced && inner <= kSmallInner)) {
+        // several rows per load instruction, a wave per (outer index, slab);
+        // slabs when there are fewer than kScanSmallWavesPerCu waves per CU
+        p->path = RD_PATH_SCAN_COLS_SMALL;
+        p->unroll = (t && t->unroll) ? t->unroll : kScanSmallUnroll;
+        if (p->unroll != 4 && p->unroll != 8) return RD_ERR_INVALID_ARG;
+        const int64_t lc = inner >= 4 ? ceil_div(inner, 4) : 1;
+        const int64_t rpw = kWave / lc;
+        const int64_t want = cu * kScanSmallWavesPerCu;
+        int64_t S = 1;
+        if (t && t->split) {
+            S = t->split;
+        } else if (outer < want) {
+            S = ceil_div(want, outer);
+            // every slab keeps at least two full steps of loads
+            int64_t cap = R / (2 * rpw * p->unroll);
+            if (cap < 1) cap = 1;
+            if (S > cap) S = cap;
+        }
+        if (S < 1) return RD_ERR_INVALID_ARG;
+        split_rows(R, S, p);
+        const int64_t b = ceil_div(p->split * outer, kBlock / kWave);
+        p->blocks = b < kMaxBlocks ? b : kMaxBlocks;
+        if (p->split > 1) {
+            if (p->split > INT64_MAX / 8 / (outer * inner)) return RD_ERR_INVALID_ARG;
+            p->passes = 3;
+            p->combine = RD_COMBINE_PASS;
+            p->workspace_bytes = 2 * p->split * outer * inner * int64_t(sizeof(float));
         }
         return RD_OK;
     }

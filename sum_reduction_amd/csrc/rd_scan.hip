@@ -234,16 +234,33 @@ __global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_ro
 }
 
 // Exclusive scan of the P piece totals of each row, in piece order:
-// carries[o*P + p] = totals[o*P] + ... + totals[o*P + p - 1].
+// carries[o*P + p] = totals[o*P] + ... + totals[o*P + p - 1] (summed as the
+// chunks are: lane-sequential within 4, DPP across the wave, a carry across
+// 256-total chunks).  One wave per row.
 __global__ __launch_bounds__(kBlock) void scan_carries_kernel(const float* __restrict__ totals,
                                                               float* __restrict__ carries,
                                                               int64_t rows, int64_t P) {
-    const int64_t stride = int64_t(gridDim.x) * kBlock;
-    for (int64_t o = int64_t(blockIdx.x) * kBlock + threadIdx.x; o < rows; o += stride) {
-        float run = 0.f;
-        for (int64_t p = 0; p < P; ++p) {
-            carries[o * P + p] = run;
-            run = run + totals[o * P + p];
+    constexpr int kWaves = kBlock / kWave;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int64_t wstride = int64_t(gridDim.x) * kWaves;
+    for (int64_t o = int64_t(blockIdx.x) * kWaves + wave; o < rows; o += wstride) {
+        const float* t = totals + o * P;
+        float* c = carries + o * P;
+        float carry = 0.f;
+        for (int64_t base = 0; base < P; base += 4 * kWave) {
+            const int64_t p0 = base + 4 * lane;
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = p0 + j < P ? t[p0 + j] : 0.f;
+            const float s0 = v[0], s1 = s0 + v[1], s2 = s1 + v[2], s3 = s2 + v[3];
+            const float incl = wave_scan_inclusive(s3);
+            const float pre = carry + dpp_or_zero<0x138>(incl);  // wave_shr:1
+            const float ex[4] = {pre, pre + s0, pre + s1, pre + s2};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (p0 + j < P) c[p0 + j] = ex[j];
+            carry = carry + lane63(incl);
         }
     }
 }
@@ -378,6 +395,165 @@ __global__ __launch_bounds__(BW * kWave) void scan_cols_kernel(
     }
 }
 
+// ------------------------------------------------------------ small inner
+// Inclusive scan over the row phases of a wave: lane l = rho*LC + lc receives
+// the sum of the lanes rho' <= rho of its lane-column lc (Hillis-Steele steps
+// of d*LC lanes through ds_bpermute; the sources of a lane with rho < RPW
+// all have rho' < RPW).  LC == 1 (inner <= 4) takes the DPP wave scan.
+__device__ __forceinline__ float phase_scan(float v, int lane, int rho, int LC, int RPW) {
+    if (LC == 1) return wave_scan_inclusive(v);
+    for (int d = 1; d < RPW; d *= 2) {
+        const int src = lane - d * LC;
+        const float t = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(4 * (src < 0 ? lane : src),
+                                                __builtin_bit_cast(int, v)));
+        v += rho >= d ? t : 0.f;
+    }
+    return v;
+}
+
+// The value lane (RPW - 1)*LC + lc holds, in every lane of lane-column lc.
+__device__ __forceinline__ float phase_last(float v, int lc, int LC, int RPW) {
+    if (LC == 1) return lane63(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                         4 * ((RPW - 1) * LC + lc), __builtin_bit_cast(int, v)));
+}
+
+// inner <= 128: a lane is (row phase rho, lane-column lc), LC = ceil(inner/4)
+// lane-columns per row and RPW = 64 / LC rows per load instruction, so one
+// instruction reads RPW adjacent rows of one outer index (RPW*inner
+// contiguous floats; inner 2-3: one row per lane, 8- or 12-byte loads).  A
+// wave owns one item (outer index, slab of R) at a time and walks it in
+// processing order, RPW rows per instruction and U instructions per step:
+// each instruction is scanned across its row phases (phase_scan) and added to
+// the running sums carried from the instruction before; the next step's loads
+// are issued before the current one is scanned and stored.  Lanes past RPW*LC
+// shadow the last row phase (valid loads) and store nothing.  Order of the
+// adds: Hillis-Steele over the phases, then carry + that.
+template <bool REV, int V, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void scan_small_kernel(
+    const float* x, float* out, int64_t outer, int64_t R, int64_t inner, int64_t S,
+    int64_t rps, int32_t LC, const float* __restrict__ carry_in, float* __restrict__ totals,
+    uint32_t nxcd) {
+    constexpr int kWaves = kBlock / kWave;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int RPW = kWave / LC;
+    const int rho_raw = lane / LC;
+    const bool active = rho_raw < RPW;
+    const int rho = active ? rho_raw : RPW - 1;
+    const int lc = lane - rho_raw * LC;
+    const int64_t c = 4 * int64_t(lc);
+    const int64_t cl = V == 4 ? (c + 4 > inner ? inner - 4 : c) : 0;
+    const int keep = active ? int(c - cl) : V;  // V: store nothing
+    const bool scan_out = totals == nullptr;
+    const int64_t nitems = S * outer;
+    const int64_t wstride = int64_t(gridDim.x) * kWaves;
+    for (int64_t item = xcd_block(nxcd) * kWaves + wave; item < nitems; item += wstride) {
+        const int64_t o = item / S;
+        const int64_t s = item - o * S;
+        const int64_t r_begin = s * rps;
+        const int64_t r_end = r_begin + rps < R ? r_begin + rps : R;
+        const int64_t m = r_end > r_begin ? r_end - r_begin : 0;
+        const int64_t cbase = (s * outer + o) * inner + cl;
+        v4f carry = {0.f, 0.f, 0.f, 0.f};
+        if (scan_out && carry_in != nullptr) carry = loadv<V, false>(carry_in + cbase, 0.f);
+        // processing position k of this lane in instruction g: g*RPW + rho;
+        // its row is first + k*dir
+        const int64_t first = REV ? r_end - 1 : r_begin;
+        const int64_t dstep = REV ? -inner : inner;
+        const float* p = x + (o * R + first) * inner + cl + int64_t(rho) * dstep;
+        float* q = out + (o * R + first) * inner + cl + int64_t(rho) * dstep;
+        const int64_t istep = int64_t(RPW) * dstep;  // elements per instruction
+        const int64_t nfull = m / RPW;               // instructions with every phase valid
+        const int64_t nsteps = nfull / U;
+
+        auto scan_one = [&](v4f v, float* qq, bool store) {
+            v4f y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < V; ++j) y[j] = carry[j] + phase_scan(v[j], lane, rho, LC, RPW);
+            if (scan_out && store) store_cols<V, NT>(qq, keep, y);
+#pragma unroll
+            for (int j = 0; j < V; ++j) carry[j] = phase_last(y[j], lc, LC, RPW);
+        };
+
+        if (nsteps > 0) {
+            v4f a[U], b[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) a[u] = loadv<V, NT>(p + u * istep, 0.f);
+            int64_t g = 0;
+            for (; g + 2 < nsteps; g += 2) {  // steps g, g + 1; loads g + 1, g + 2
+#pragma unroll
+                for (int u = 0; u < U; ++u) b[u] = loadv<V, NT>(p + ((g + 1) * U + u) * istep, 0.f);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) scan_one(a[u], q + (g * U + u) * istep, true);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) a[u] = loadv<V, NT>(p + ((g + 2) * U + u) * istep, 0.f);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) scan_one(b[u], q + ((g + 1) * U + u) * istep, true);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (g + 1 < nsteps) {  // two steps left
+#pragma unroll
+                for (int u = 0; u < U; ++u) b[u] = loadv<V, NT>(p + ((g + 1) * U + u) * istep, 0.f);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) scan_one(a[u], q + (g * U + u) * istep, true);
+#pragma unroll
+                for (int u = 0; u < U; ++u) scan_one(b[u], q + ((g + 1) * U + u) * istep, true);
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) scan_one(a[u], q + (g * U + u) * istep, true);
+            }
+        }
+        // the remaining instructions, the last one possibly partial
+        for (int64_t g = nsteps * U; g * RPW < m; ++g) {
+            const bool valid = g * RPW + rho < m;
+            const v4f v = valid ? loadv<V, NT>(p + g * istep, 0.f) : v4f{0.f, 0.f, 0.f, 0.f};
+            scan_one(v, q + g * istep, valid);
+        }
+        if (!scan_out && rho_raw == 0)
+            for (int j = keep; j < V; ++j) totals[cbase + j] = carry[j];
+    }
+}
+
+// The slab carries when there are many slabs: one wave per (o, i), the S
+// totals scanned in processing order in 256-total chunks (as
+// scan_carries_kernel), the reverse sum taking the last slab first.
+template <bool REV>
+__global__ __launch_bounds__(kBlock) void scan_slab_carries_wave_kernel(
+    const float* __restrict__ totals, float* __restrict__ carries, int64_t S, int64_t n) {
+    constexpr int kWaves = kBlock / kWave;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int64_t wstride = int64_t(gridDim.x) * kWaves;
+    for (int64_t e = int64_t(blockIdx.x) * kWaves + wave; e < n; e += wstride) {
+        float carry = 0.f;
+        for (int64_t base = 0; base < S; base += 4 * kWave) {
+            const int64_t k0 = base + 4 * lane;
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t k = k0 + j;
+                v[j] = k < S ? totals[(REV ? S - 1 - k : k) * n + e] : 0.f;
+            }
+            const float s0 = v[0], s1 = s0 + v[1], s2 = s1 + v[2], s3 = s2 + v[3];
+            const float incl = wave_scan_inclusive(s3);
+            const float pre = carry + dpp_or_zero<0x138>(incl);  // wave_shr:1
+            const float ex[4] = {pre, pre + s0, pre + s1, pre + s2};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t k = k0 + j;
+                if (k < S) carries[(REV ? S - 1 - k : k) * n + e] = ex[j];
+            }
+            carry = carry + lane63(incl);
+        }
+    }
+}
+
 // Exclusive scan over the S slabs of each (o, i), in processing order:
 // the reverse sum takes the last slab first.
 template <bool REV>
@@ -466,7 +642,37 @@ hipError_t cols_v(const rd_plan& p, const float* x, float* out, int64_t outer, i
     return cols_go<REV, 4, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
 }
 
+template <bool REV, int V, bool NT>
+hipError_t small_go(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
+                    int64_t inner, const float* carry_in, float* totals, hipStream_t s) {
+    const int32_t lc = inner >= 4 ? int32_t((inner + 3) / 4) : 1;
+    const uint32_t nx = uint32_t(p.nxcd);
+    if (p.unroll == 8)
+        return launch(scan_small_kernel<REV, V, 8, NT>, p.blocks, kBlock, s, x, out, outer, R,
+                      inner, p.split, p.rows_per_split, lc, carry_in, totals, nx);
+    return launch(scan_small_kernel<REV, V, 4, NT>, p.blocks, kBlock, s, x, out, outer, R, inner,
+                  p.split, p.rows_per_split, lc, carry_in, totals, nx);
+}
+
+template <bool REV, bool NT>
+hipError_t small_v(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
+                   int64_t inner, const float* carry_in, float* totals, hipStream_t s) {
+    if (inner == 2) return small_go<REV, 2, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
+    if (inner == 3) return small_go<REV, 3, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
+    return small_go<REV, 4, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
+}
+
 }  // namespace
+
+hipError_t launch_scan_small(const rd_plan& p, bool reverse, const float* x, float* out,
+                             int64_t outer, int64_t R, int64_t inner, const float* carry_in,
+                             float* totals, hipStream_t s) {
+    if (reverse)
+        return p.nontemporal ? small_v<true, true>(p, x, out, outer, R, inner, carry_in, totals, s)
+                             : small_v<true, false>(p, x, out, outer, R, inner, carry_in, totals, s);
+    return p.nontemporal ? small_v<false, true>(p, x, out, outer, R, inner, carry_in, totals, s)
+                         : small_v<false, false>(p, x, out, outer, R, inner, carry_in, totals, s);
+}
 
 hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, float* out,
                             int64_t outer, int64_t R, const float* carry_in, float* totals,
@@ -477,7 +683,9 @@ hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, floa
 
 hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows, int64_t P,
                                hipStream_t s) {
-    return launch(scan_carries_kernel, grid_for(rows), kBlock, s, totals, carries, rows, P);
+    int64_t blocks = (rows + kBlock / kWave - 1) / (kBlock / kWave);  // a wave per row
+    blocks = blocks > kMaxBlocks ? kMaxBlocks : blocks;
+    return launch(scan_carries_kernel, blocks, kBlock, s, totals, carries, rows, P);
 }
 
 hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, float* out,
@@ -492,6 +700,15 @@ hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, floa
 
 hipError_t launch_scan_slab_carries(bool reverse, const float* totals, float* carries, int64_t S,
                                     int64_t n, hipStream_t s) {
+    if (S > kWave) {  // many slabs: a wave per (o, i)
+        int64_t blocks = (n + kBlock / kWave - 1) / (kBlock / kWave);
+        blocks = blocks > kMaxBlocks ? kMaxBlocks : blocks;
+        if (reverse)
+            return launch(scan_slab_carries_wave_kernel<true>, blocks, kBlock, s, totals, carries,
+                          S, n);
+        return launch(scan_slab_carries_wave_kernel<false>, blocks, kBlock, s, totals, carries, S,
+                      n);
+    }
     if (reverse)
         return launch(scan_slab_carries_kernel<true>, grid_for(n), kBlock, s, totals, carries, S, n);
     return launch(scan_slab_carries_kernel<false>, grid_for(n), kBlock, s, totals, carries, S, n);

@@ -56,11 +56,20 @@ def test_rows_around_tiles():
     _sweep(shapes, [0, 1, 2, 3], 801, "scan rows")
 
 
-def test_columns():
-    shapes = [(o, r, i) for i in (2, 3, 4, 5, 7, 63, 64, 65, 255, 256, 257, 4095)
-              for (o, r) in ((1, 1), (3, 17), (2, 300))]
-    shapes += [(128, 64, 4095), (1, 5000, 5)]
-    _sweep(shapes, [0, 1, 3], 802, "scan cols")
+@pytest.mark.parametrize("path", [0, 7, 8], ids=["default", "scan_cols", "scan_cols_small"])
+def test_columns(path):
+    """inner > 1 on both column kernels: 4 columns a lane and 256 a wave
+    (scan_cols), or 64/LC rows a load instruction scanned across the wave
+    (scan_cols_small, LC = ceil(inner/4) lane-columns per row, inner <= 256)."""
+    inners = (2, 3, 4, 5, 7, 8, 12, 17, 31, 32, 33, 63, 64, 65, 100, 128, 129, 255, 256)
+    if path != 8:
+        inners += (257, 4095)
+    shapes = [(o, r, i) for i in inners for (o, r) in ((1, 1), (3, 17), (2, 300))]
+    shapes += [(1, 5000, 5), (3, 1000, 4), (2, 777, 2), (1, 4099, 3)]
+    if path != 8:
+        shapes += [(128, 64, 4095)]
+    with rd.tuning(path=path):
+        _sweep(shapes, [0, 1, 3], 802 + path, "scan cols path %d" % path)
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 7])
@@ -82,20 +91,37 @@ def test_unroll_variants(unroll, split, bw):
     rows = [(3, r, 1) for r in (1023, 1024, 1025, 2047, 2048, 2049, 3 * 2048 + 7, 5 * 4096 + 1)]
     cols = [(2, r, i) for r in (7, 8, 9, 15, 16, 17, 33, 100) for i in (2, 3, 5, 300)]
     cols += [(2, 37, i) for i in (1023, 1024, 1025, 2049, 4095, 4097)]
-    with rd.tuning(unroll=unroll, split=split, col_waves=bw):
+    with rd.tuning(unroll=unroll, split=split, col_waves=bw, path=7):
         _sweep(cols, [0, 1], 850 + unroll + split, "scan cols u%d s%d w%d" % (unroll, split, bw))
+    if unroll != 16:
+        small = [(2, r, i) for r in (63, 64, 65, 255, 256, 257, 600) for i in (2, 3, 4, 9, 40, 128)]
+        with rd.tuning(unroll=unroll, split=split, path=8):
+            _sweep(small, [0, 1], 855 + unroll + split, "scan small u%d s%d" % (unroll, split))
     if unroll != 16:
         with rd.tuning(unroll=unroll, split=split):
             _sweep(rows, [0, 3], 860 + unroll + split, "scan rows u%d s%d" % (unroll, split))
 
 
 def test_default_splits():
-    """Few rows or columns: the planner cuts them itself."""
-    for shape in ((1, 1 << 20, 1), (7, 100_000, 1), (1, 100_000, 4), (2, 50_000, 33)):
+    """Few rows or columns: the planner cuts them itself (many slabs: the slab
+    carries go one wave per column)."""
+    shapes = [(1, 1 << 20, 1), (7, 100_000, 1), (1, 100_000, 4), (2, 50_000, 33),
+              (1, 1 << 20, 4), (1, 200_000, 300)]
+    for shape in shapes:
         p = rd.rd_plan_cumsum(256, *shape).as_dict()
         assert p["split"] > 1 and p["passes"] == 3, (shape, p)
-    _sweep([(1, 1 << 20, 1), (7, 100_000, 1), (1, 100_000, 4), (2, 50_000, 33)], [0], 820,
-           "scan default splits")
+    assert rd.rd_plan_cumsum(256, 1, 1 << 20, 4).split > 64
+    _sweep(shapes, [0], 820, "scan default splits")
+
+
+def test_many_pieces():
+    """Thousands of pieces per row: the carries of the piece totals are scanned
+    in 256-total chunks by one wave per row."""
+    p = rd.rd_plan_cumsum(256, 1, 1 << 24, 1)
+    assert p.split == 4096 and p.passes == 3
+    _sweep([(1, 1 << 24, 1)], [0], 870, "scan 4096 pieces")
+    with rd.tuning(split=700):
+        _sweep([(2, 700 * 4096 + 3, 1), (1, 257 * 4096, 1)], [0, 1], 871, "scan 700 pieces")
 
 
 def test_in_place():
@@ -154,3 +180,25 @@ def test_problem91_full_size():
         S, A = oracle.cumsum_dim(rows, block, w.R, 1, True)
         H.assert_within_tolerance(got[o0:o0 + block].reshape(-1), S.reshape(-1), A.reshape(-1),
                                   "problem 91 rows %d.." % o0)
+
+
+@pytest.mark.slow
+def test_columns_full_size():
+    """[128, 4096, 4095] along dim 1 (the problem-47 shape) both ways, and a
+    small-inner [4096, 4096, 4]: every output against the oracle."""
+    t = H.torch()
+    for shape, seed in (((128, 4096, 4095), 92), ((4096, 4096, 4), 93)):
+        o, r, i = shape
+        host = workloads.random(o * r * i, seed, "uniform")
+        x = H.upload(host)
+        for rev in (True, False):
+            H.say("columns full size %s reverse=%d" % (shape, rev))
+            got = rd.rd_cumsum_dim(x, o, r, i, reverse=rev).cpu().numpy().reshape(o, r * i)
+            blk = max(1, (1 << 24) // (r * i))
+            for o0 in range(0, o, blk):
+                o1 = min(o, o0 + blk)
+                S, A = oracle.cumsum_dim(host[o0 * r * i:o1 * r * i], o1 - o0, r, i, rev)
+                H.assert_within_tolerance(got[o0:o1].reshape(-1), S.reshape(-1), A.reshape(-1),
+                                          "%s rev=%d outer %d.." % (shape, rev, o0))
+        del x
+        t.cuda.empty_cache()

@@ -199,7 +199,8 @@ def test_default_plans_are_built_for_every_operator():
 
 def _scan_invariants(p, outer, R, inner):
     d = p.as_dict()
-    assert d["path"] == ("scan_rows" if inner == 1 else "scan_cols")
+    assert d["path"] == ("scan_rows" if inner == 1 else
+                         "scan_cols_small" if inner <= 128 else "scan_cols")
     # the pieces / slabs cover R exactly, none empty
     assert p.split >= 1 and p.rows_per_split >= 1
     assert p.split * p.rows_per_split >= R > (p.split - 1) * p.rows_per_split
@@ -207,6 +208,10 @@ def _scan_invariants(p, outer, R, inner):
         assert p.rows_per_split % 4096 == 0           # whole tiles per piece
         assert p.blocks == min(-(-outer * p.split // 4), 1 << 20)   # a wave per piece
         ws = 2 * outer * p.split * 4 if p.split > 1 else 0
+    elif inner <= 128:
+        assert p.unroll in (4, 8)
+        assert p.blocks == min(-(-outer * p.split // 4), 1 << 20)   # a wave per slab
+        ws = 2 * p.split * outer * inner * 4 if p.split > 1 else 0
     else:
         tiles = -(-(-(-inner // 4) if inner >= 4 else 1) // 64)
         bw = p.col_waves
@@ -250,6 +255,29 @@ def test_cumsum_forced_split():
         assert p.split == 5 and p.rows_per_split == 20
         p = rd.rd_plan_cumsum(CU, 2, 3, 7)              # at most R slabs
         assert p.split == 3 and p.rows_per_split == 1
+
+
+def test_cumsum_small_inner_plans():
+    """inner <= 128: a wave per (outer index, slab); a forced path picks
+    either column kernel (the small one up to inner = 256)."""
+    p = rd.rd_plan_cumsum(CU, 4096, 4096, 4)
+    assert p.as_dict()["path"] == "scan_cols_small" and p.split == 1 and p.blocks == 1024
+    p = rd.rd_plan_cumsum(CU, 1, 1 << 24, 4)
+    assert p.split > 1 and p.passes == 3
+    with rd.tuning(path=7):
+        assert rd.rd_plan_cumsum(CU, 3, 9, 2).as_dict()["path"] == "scan_cols"
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum(CU, 3, 9, 1)       # rows have one path
+    with rd.tuning(path=8):
+        assert rd.rd_plan_cumsum(CU, 3, 9, 256).as_dict()["path"] == "scan_cols_small"
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum(CU, 3, 9, 257)
+    with rd.tuning(path=4):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum(CU, 3, 9, 64)      # a reduction path
+    with rd.tuning(unroll=16):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum(CU, 3, 9, 64)      # small scan: 4 or 8
 
 
 def test_cumsum_degenerate_plans():
