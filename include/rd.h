@@ -212,7 +212,9 @@ typedef struct rd_plan {
     int32_t combine;         /* rd_combine */
     int32_t order;           /* ROWS: rd_order; 0 elsewhere */
     int32_t nontemporal;     /* 1: main-pass loads (and the scans' stores)
-                                carry the streaming hint */
+                                carry the streaming hint (the totals pass
+                                of a split scan of at most 256 MB reads
+                                without it, to find x in the cache again) */
     int64_t split;           /* ROWS, SCAN_ROWS: pieces per row; COLS*,
                                 SCAN_COLS: slabs of R */
     int64_t rows_per_split;  /* COLS*, SCAN_COLS: rows per slab; SCAN_ROWS:

@@ -270,6 +270,11 @@ rd_status rd_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
         if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
     }
     const bool rev = reverse != 0;
+    // The totals pass of a split scan reads x without the streaming hint when
+    // x fits in the last-level cache, so that the scan pass re-reads it from
+    // there (measured: 5-11% faster up to 256 MB, 1% slower at 2 GB).
+    rd_plan pt = p;
+    if (uint64_t(n) * sizeof(float) <= rd::kScanCachedTotalsBytes) pt.nontemporal = 0;
     hipError_t e = hipSuccess;
     if (p.path == RD_PATH_SCAN_ROWS) {
         if (p.split == 1) {
@@ -278,29 +283,29 @@ rd_status rd_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
             const int64_t m = outer * p.split;
             float* totals = ws;
             float* carries = ws + m;
-            e = rd::launch_scan_rows(p, rev, x, out, outer, R, nullptr, totals, stream);
+            e = rd::launch_scan_rows(pt, rev, x, out, outer, R, nullptr, totals, stream);
             if (e == hipSuccess) e = rd::launch_scan_carries(totals, carries, outer, p.split, stream);
             if (e == hipSuccess)
                 e = rd::launch_scan_rows(p, rev, x, out, outer, R, carries, nullptr, stream);
         }
     } else {
         const bool small = p.path == RD_PATH_SCAN_COLS_SMALL;
-        auto cols = [&](const float* carry_in, float* totals) {
-            return small ? rd::launch_scan_small(p, rev, x, out, outer, R, inner, carry_in, totals,
+        auto cols = [&](const rd_plan& q, const float* carry_in, float* totals) {
+            return small ? rd::launch_scan_small(q, rev, x, out, outer, R, inner, carry_in, totals,
                                                  stream)
-                         : rd::launch_scan_cols(p, rev, x, out, outer, R, inner, carry_in, totals,
+                         : rd::launch_scan_cols(q, rev, x, out, outer, R, inner, carry_in, totals,
                                                 stream);
         };
         if (p.split == 1) {
-            e = cols(nullptr, nullptr);
+            e = cols(p, nullptr, nullptr);
         } else {
             const int64_t m = p.split * nrow;
             float* totals = ws;
             float* carries = ws + m;
-            e = cols(nullptr, totals);
+            e = cols(pt, nullptr, totals);
             if (e == hipSuccess)
                 e = rd::launch_scan_slab_carries(rev, totals, carries, p.split, nrow, stream);
-            if (e == hipSuccess) e = cols(carries, nullptr);
+            if (e == hipSuccess) e = cols(p, carries, nullptr);
         }
     }
     if (ws) {

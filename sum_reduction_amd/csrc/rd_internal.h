@@ -75,6 +75,9 @@ constexpr int64_t kScanRowWavesSplit = 16;  // pieces per CU once they are cut
 constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan
 constexpr int kScanSmallUnroll = 8;       // load instructions per step, small inner
 constexpr int64_t kScanSmallWavesPerCu = 16;
+// Inputs up to this size are read by a split scan's totals pass without the
+// streaming hint (MI355X has a 256 MB last-level cache).
+constexpr uint64_t kScanCachedTotalsBytes = uint64_t(256) << 20;
 
 // Which kernel shapes this build instantiates for an operator (rd_kernels.hip).
 bool rows_shape_supported(int op, int group, int unroll);
