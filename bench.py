@@ -119,6 +119,8 @@ def main(argv=None):
                     "[32768, 32768] rows, then each --scan-shape)")
     ap.add_argument("--scan-shape", action="append", default=None, metavar="OxRxI",
                     help="with --report --scan: also a cumulative sum of this shape")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the trivial read / copy kernels timed after the step")
     ap.add_argument("--reps", type=int, default=0,
                     help="with --report: timed calls per measurement (default 200 "
                     "under 1 GiB, else 30)")
@@ -244,6 +246,11 @@ def main(argv=None):
         "device": {"name": props.name, "cu": cu, "gcn_arch": getattr(props, "gcnArchName", "")},
     }
 
+    if not args.no_ceiling:
+        src = max(xs.values(), key=lambda t: t.numel())
+        log("ceiling probes on %d floats" % src.numel())
+        result["ceiling"] = measure_ceiling(src, achieved)
+
     if not args.no_cpu_baseline:
         import oracle
 
@@ -282,6 +289,56 @@ def main(argv=None):
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def measure_ceiling(src, achieved_gbs):
+    """Bandwidth of trivial kernels on this GPU (librd_ceiling.so): a
+    grid-stride read of `src` and a copy of it, each over a few grid sizes,
+    best median of 10 event-timed launches.  Context for the roofline
+    fraction, which stays relative to the published 8 TB/s."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "sum_reduction_amd", "librd_ceiling.so"))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.rd_ceiling_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.rd_ceiling_copy.argtypes = [vp, vp, i64, i32, vp]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream or None
+    n = src.numel() // 4 * 4
+    sink = torch.empty((1 << 15) * 256, dtype=torch.float32, device=src.device)
+    dst = torch.empty(n, dtype=torch.float32, device=src.device)
+
+    def best(fn, grids, nbytes):
+        out = (0.0, 0)
+        for g in grids:
+            assert fn(g) == 0
+            torch.cuda.synchronize()
+            ms = []
+            for _ in range(10):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn(g)
+                b.record(stream)
+                b.synchronize()
+                ms.append(a.elapsed_time(b))
+            gbs = nbytes / sorted(ms)[len(ms) // 2] / 1e6
+            out = max(out, (gbs, g))
+        return out
+
+    rd_gbs, rd_g = best(lambda g: lib.rd_ceiling_read(src.data_ptr(), n, g, sink.data_ptr(), sh),
+                        (256, 512, 1024, 2048, 4096, 8192), 4 * n)
+    cp_gbs, cp_g = best(lambda g: lib.rd_ceiling_copy(src.data_ptr(), dst.data_ptr(), n, g, sh),
+                        (2048, 8192, 32768), 8 * n)
+    del dst, sink
+    torch.cuda.empty_cache()
+    return {"read_GBps": round(rd_gbs, 1), "read_blocks": rd_g, "copy_GBps": round(cp_gbs, 1),
+            "copy_blocks": cp_g, "bytes_read": 4 * n,
+            "roofline_achieved_over_read": round(achieved_gbs / rd_gbs, 4),
+            "kind": "trivial grid-stride kernels, 16-byte nontemporal accesses "
+                    "(include/rd_ceiling.h)"}
 
 
 # Context figures printed by the pages for the same operation (another machine):
@@ -390,7 +447,7 @@ def report_scan(args, dev, cu):
             for _ in range(3):
                 call()
             torch.cuda.synchronize()
-            reps = args.reps or (30 if nbytes >= (1 << 30) else 200)
+            reps = args.reps or (50 if nbytes >= (1 << 30) else 500)
 
             def timed(cold):
                 ms = []
@@ -464,7 +521,7 @@ def report_one(w, op, host, x, out, flush, threads, cu, args):
             rd.rd_reduce_dim(x, w.outer, w.R, w.inner, op, out=out)
 
     small = w.in_bytes < (1 << 30)
-    reps = args.reps or (200 if small else 30)
+    reps = args.reps or (500 if small else 50)
     for _ in range(3):
         call()
     torch.cuda.synchronize()

@@ -1,4 +1,5 @@
-"""Build ``librd.so`` (the HIP kernels and the C ABI of include/rd.h) in-tree.
+"""Build ``librd.so`` (the HIP kernels and the C ABI of include/rd.h) in-tree,
+and ``librd_ceiling.so`` (the bandwidth probes of include/rd_ceiling.h).
 
     python -m sum_reduction_amd.build          # compile for gfx950
 
@@ -22,6 +23,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "librd.so")
 SOURCES = ["rd_api.cpp", "rd_plan.cpp", "rd_kernels.hip", "rd_scan.hip"]
+# the bandwidth probes bench.py reports beside the reductions (include/rd_ceiling.h)
+CEILING_LIBRARY = os.path.join(HERE, "librd_ceiling.so")
+CEILING_SOURCES = ["rd_ceiling.hip"]
 ARCH = "gfx950"
 
 
@@ -40,9 +44,15 @@ def flags():
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into ``librd.so`` (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIBRARY + ".tmp%d" % os.getpid()
+    """Compile ``librd.so`` and ``librd_ceiling.so`` (always recompiles)."""
+    _compile(SOURCES, LIBRARY, verbose)
+    _compile(CEILING_SOURCES, CEILING_LIBRARY, verbose)
+    return LIBRARY
+
+
+def _compile(sources, library: str, verbose: bool) -> None:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = library + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *flags(), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -54,8 +64,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, library)
 
 
 if __name__ == "__main__":

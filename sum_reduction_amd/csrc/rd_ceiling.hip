@@ -1,0 +1,70 @@
+// rd_ceiling.hip -- measurement probes, not part of the reduction library:
+// the bandwidth a trivial kernel reaches on this GPU, reported beside the
+// reductions' fraction of the published 8 TB/s.
+//
+//   read:  every lane streams 16-byte nontemporal loads in grid-stride
+//          order, 4 in flight, and writes one float (its sum) at the end so
+//          that the loads are not dead code;
+//   copy:  every lane copies 16-byte chunks with nontemporal loads and
+//          stores, grid-stride.
+// Only whole float4s are touched: n is rounded down to a multiple of 4.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rd_ceiling.h"
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void read_kernel(const v4f* __restrict__ x, int64_t n4,
+                                                   float* __restrict__ sink) {
+    const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    v4f a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    int64_t i = tid;
+    for (; i + 3 * stride < n4; i += 4 * stride) {
+        const v4f v0 = __builtin_nontemporal_load(x + i);
+        const v4f v1 = __builtin_nontemporal_load(x + i + stride);
+        const v4f v2 = __builtin_nontemporal_load(x + i + 2 * stride);
+        const v4f v3 = __builtin_nontemporal_load(x + i + 3 * stride);
+        a += v0 + v2;
+        b += v1 + v3;
+    }
+    for (; i < n4; i += stride) a += __builtin_nontemporal_load(x + i);
+    a += b;
+    sink[tid] = (a.x + a.y) + (a.z + a.w);
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const v4f* __restrict__ x, v4f* __restrict__ y,
+                                                   int64_t n4) {
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(x + i), y + i);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int rd_ceiling_read(const float* x, int64_t n, int32_t blocks, float* sink, hipStream_t stream) {
+    if (!x || !sink || n < 4 || blocks < 1 || blocks > (1 << 20) || !aligned16(x)) return 1;
+    read_kernel<<<dim3(uint32_t(blocks)), dim3(256), 0, stream>>>(
+        reinterpret_cast<const v4f*>(x), n / 4, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int rd_ceiling_copy(const float* x, float* y, int64_t n, int32_t blocks, hipStream_t stream) {
+    if (!x || !y || n < 4 || blocks < 1 || blocks > (1 << 20) || !aligned16(x) || !aligned16(y))
+        return 1;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t bytes = uintptr_t(n / 4) * 16u;
+    if (a < b + bytes && b < a + bytes) return 1;  // overlap
+    copy_kernel<<<dim3(uint32_t(blocks)), dim3(256), 0, stream>>>(
+        reinterpret_cast<const v4f*>(x), reinterpret_cast<v4f*>(y), n / 4);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"

@@ -37,6 +37,27 @@ def test_library_exports_every_declared_function():
     assert not missing, missing
 
 
+def test_ceiling_probes_export_their_header():
+    """include/rd_ceiling.h (bandwidth probes bench.py reports as context)
+    against librd_ceiling.so, and their argument checks (no GPU needed)."""
+    with open(os.path.join(ROOT, "include", "rd_ceiling.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(rd_ceiling_[a-z]+)\s*\(", text)))
+    assert names == ["rd_ceiling_copy", "rd_ceiling_read"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "sum_reduction_amd", "librd_ceiling.so"))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.rd_ceiling_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.rd_ceiling_copy.argtypes = [vp, vp, i64, i32, vp]
+    buf = (ctypes.c_float * 64)()
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    assert lib.rd_ceiling_read(None, 16, 1, base, None) == 1
+    assert lib.rd_ceiling_read(base, 3, 1, base, None) == 1
+    assert lib.rd_ceiling_read(base + 4, 16, 1, base, None) == 1     # not 16-B aligned
+    assert lib.rd_ceiling_read(base, 16, 0, base, None) == 1
+    assert lib.rd_ceiling_copy(base, base + 32, 16, 1, None) == 1    # overlap
+    assert lib.rd_ceiling_copy(base, None, 16, 1, None) == 1
+
+
 def test_version_and_status_strings():
     assert rd.rd_version() == 100
     names = [rd.rd_status_string(s) for s in range(6)]
