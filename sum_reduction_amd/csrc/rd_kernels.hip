@@ -39,6 +39,9 @@
 //  COLS      wave (cw, rw) folds its k-th row, r0 + rw + k*RW, into float4
 //            accumulator (k mod 2); join(acc[0], acc[1]); then the row phases
 //            in rw order; then (if split) the slabs in slab order.
+//  COLS_SMALL  row phase rho folds its k-th row into accumulator (k mod 2);
+//            join(acc[0], acc[1]); then the row phases by a fixed tree (see
+//            cols_small_kernel); then (if split) the slabs in slab order.
 // U, the number of 16-byte loads a lane keeps in flight, is even and does not
 // change the order.  Two accumulators rather than U keep the kernels within
 // 64 VGPRs (8 waves per SIMD) while all U loads are issued before the first
@@ -152,6 +155,14 @@ __device__ __forceinline__ float wave_reduce(float v) {
     const float hi = __builtin_bit_cast(
         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
     return Op<OP>::join(lo, hi);
+}
+
+// The value v of lane `src` (ds_bpermute).  v is taken by value: a bit cast
+// applied to a vector element in place was miscompiled into one permute of
+// element 0 for all four.
+__device__ __forceinline__ float lane_value(int src, float v) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, v)));
 }
 
 // Join over a kBlock-thread workgroup, valid in thread 0: wave butterflies,
@@ -381,15 +392,16 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
 // as in cols_kernel); with inner < 4 (V = inner) a lane loads its whole row.
 // Each wave works on one item (outer index o, slab s of R) at a time: row
 // phase rho folds rows r0 + rho + k*RPW into accumulator (k mod 2), U rows in
-// flight; then the row phases of each lane-column are joined through LDS in
-// rho order and the rho == 0 lanes write.  With S == 1, dst is the output;
-// otherwise dst is [S][outer][inner] for slab_combine_kernel.
+// flight; then the row phases of each lane-column are joined by a fixed
+// tree (LC == 1: the wave butterfly; else pairs rho, rho + d for d = 1, 2,
+// 4, ... through ds_bpermute) and the rho == 0 lanes write.  With S == 1,
+// dst is the output; otherwise dst is [S][outer][inner] for
+// slab_combine_kernel.
 template <int OP, int V, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void cols_small_kernel(
     const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t S,
     int64_t rps, int32_t LC, float* __restrict__ dst, uint32_t nxcd) {
     constexpr int kWaves = kBlock / kWave;
-    __shared__ v4f lds[kBlock];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int RPW = kWave / LC;
@@ -401,7 +413,6 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
     const int keep = int(c - cl);  // 0, or 1..3 for the row's last lane-column
     const int64_t nitems = S * outer;
     const int64_t wstride = int64_t(gridDim.x) * kWaves;
-    v4f* my = lds + wave * kWave;
     for (int64_t item = xcd_block(nxcd) * kWaves + wave; item < nitems; item += wstride) {
         const int64_t o = item / S;
         const int64_t s = item - o * S;
@@ -427,14 +438,21 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
                 if (k + u < m)
                     acc[u & 1] = Op<OP>::fold(acc[u & 1], loadv<V, NT>(p + u * step, fill));
         }
-        // join the row phases of each lane-column, in rho order
-        my[lane] = Op<OP>::join(acc[0], acc[1]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // join the row phases of each lane-column by a fixed tree
+        v4f a = Op<OP>::join(acc[0], acc[1]);
+        if (LC == 1) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) a[j] = wave_reduce<OP>(a[j]);
+        } else {
+            for (int d = 1; d < RPW; d *= 2) {
+                const int src = lane + d * LC < kWave ? lane + d * LC : lane;
+                v4f t;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) t[j] = lane_value(src, a[j]);
+                if ((rho & (2 * d - 1)) == 0 && rho + d < RPW) a = Op<OP>::join(a, t);
+            }
+        }
         if (rho == 0) {
-            v4f a = my[lc];
-            for (int q = 1; q < RPW; ++q) a = Op<OP>::join(a, my[q * LC + lc]);
             float* d = dst + (s * outer + o) * inner + cl;
             if constexpr (V == 4) {
                 for (int q = keep; q < 4; ++q) d[q] = a[q];
@@ -442,9 +460,6 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
                 for (int q = 0; q < V; ++q) d[q] = a[q];
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
