@@ -1,11 +1,15 @@
 /*
  * rd.h -- fp32 sum reduction on one AMD Instinct MI355X (gfx950).
  *
- * Two reductions, both fp32 in and fp32 out:
+ * The two sums, fp32 in and fp32 out:
  *
  *   rd_sum_1d   S = sum_{i<n} x[i]                        (a full 1D reduce)
  *   rd_sum_dim  out[o][i] = sum_{r<R} x[o][r][i]          (reduce the middle
  *               axis of a contiguous [outer, R, inner] array)
+ *
+ * the same with another operator (sum of squares, maximum, minimum) --
+ * rd_reduce_1d, rd_reduce_dim -- and the cumulative sum along the middle
+ * axis, forward or reverse -- rd_cumsum_dim.
  *
  * The full reduce is the 1D float32 sum of the "High-Performance Reduction
  * Kernels" README (its kernel ladder: float4 loads, per-block partials, a
@@ -21,16 +25,18 @@
  * Pointers.  x and out are device pointers owned by the caller (for example
  *   the data pointers of torch tensors); the library never frees or keeps
  *   them.  They must be 4-byte aligned -- no 16-byte alignment is required --
- *   and the output range must not overlap the input range.  x must hold
- *   outer*R*inner (or n) contiguous floats, out outer*inner (or 1).
+ *   and the output range must not overlap the input range (the cumulative
+ *   sum may also write in place, out == x).  x must hold outer*R*inner (or
+ *   n) contiguous floats, out outer*inner (or 1; the cumulative sum: as x).
  * Streams.  Work is enqueued on `stream` (0 = the null stream) of the current
  *   device and the call returns without waiting; out is valid once the
  *   stream is synchronised.  No device-to-host transfer happens inside a call.
- * Workspace.  Where a shape needs per-block partials, the library allocates
- *   them stream-ordered on `stream` from a pool of its own and frees them on
- *   the same stream, so concurrent calls on different streams never share
- *   memory.  The partials of a split reduce are summed by a second kernel
- *   in fixed order.  With the RD_COMBINE_LAST_BLOCK option the last
+ * Workspace.  Where a shape needs per-block partials (a split reduce, or
+ *   the piece / slab totals and carries of a split cumulative sum), the
+ *   library allocates them stream-ordered on `stream` from a pool of its own
+ *   and frees them on the same stream, so concurrent calls on different
+ *   streams never share memory.  The partials of a split reduce are summed by
+ *   a second kernel in fixed order.  With the RD_COMBINE_LAST_BLOCK option the last
  *   workgroup of the first kernel sums them instead; the integer ticket
  *   counter that elects it belongs to the stream (one per stream and device,
  *   reset by the kernel itself), so calls on one stream, which never overlap,
@@ -137,9 +143,17 @@ rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
  *   reverse != 0:  out[o][r][i] = sum_{k = r .. R-1} x[o][k][i]
  *   reverse == 0:  out[o][r][i] = sum_{k = 0 .. r}   x[o][k][i]
  *   x, out  device pointers to outer*R*inner floats, 4-B aligned; out may be
- *           x itself (in place) but must not overlap it otherwise
- * fp32 adds in a fixed order (bitwise reproducible); each output is within
- * the fp32 rounding of its terms, like the reductions.  Source: POPCORNBENCH
+ *           x itself (in place) but must not overlap it otherwise (both may
+ *           be NULL when outer*R*inner == 0, which writes nothing)
+ *   outer, R, inner  >= 0, with outer*R*inner*4 representable in int64
+ *   reverse 0 or not
+ *   stream  HIP stream of the current device, 0 for the null stream
+ * Returns RD_OK once the work is enqueued (one kernel, or three when there
+ * are too few rows or columns to fill the GPU: totals, their carries, the
+ * scan); RD_ERR_INVALID_ARG, RD_ERR_NO_DEVICE, RD_ERR_ALLOC (the totals of a
+ * split scan), RD_ERR_LAUNCH as for the reductions, out untouched.  fp32
+ * adds in a fixed order (bitwise reproducible); each output is within the
+ * fp32 rounding of its terms, like the reductions.  Source: POPCORNBENCH
  * Kimi-K2.6 level-1 problem 91 trace (reverse cumulative sum of a
  * [32768, 32768] array along dim 1, y = cumsum(x.flip(1), 1).flip(1), spelled
  * out as y[i][j] = x[i][j] + ... + x[i][N-1]).

@@ -11,8 +11,9 @@
 // is no barrier and no LDS -- the 64 lanes walk the row in chunks of
 // 256*K elements, every load and store a full 1 KB wave access, and the next
 // chunk's loads are issued before the current chunk is scanned and stored.
-// Loads and stores both carry the nontemporal hint (measured on MI355X: the
-// two together beat neither and beat either alone, by up to 10%).
+// Loads and stores both carry the nontemporal hint (measured on MI355X:
+// hinting both was the fastest of the four combinations, up to 10% ahead of
+// hinting the loads alone).
 // Positions are counted in processing order q (q = 0 is the first element
 // the sum takes: the row's last one for the reverse sum).
 //
@@ -25,8 +26,10 @@
 //   carry      carry + (the slice total, lane 63's inclusive value)
 // A row cut into pieces (few rows) runs in three kernels: the piece totals
 // (the same chunks, carry only), their exclusive scan in piece order, and the
-// scan of each piece from its carry.  The column scan (inner > 1) keeps one
-// running sum per column in a lane and walks R in processing order.
+// scan of each piece from its carry.  The column scans (inner > 1) keep the
+// running sums of 4 adjacent columns in a lane and walk R in processing
+// order: 256 columns a wave for wide rows (scan_cols_kernel), several whole
+// rows a load instruction for inner <= 128 (scan_small_kernel).
 #include <hip/hip_runtime.h>
 
 #include "rd_device.h"

@@ -124,6 +124,21 @@ def test_many_pieces():
         _sweep([(2, 700 * 4096 + 3, 1), (1, 257 * 4096, 1)], [0, 1], 871, "scan 700 pieces")
 
 
+def test_repeats_bitwise_equal():
+    """Random data, every path and split kind: 5 calls give identical bits
+    (the totals, their carries and the scan are summed in a fixed order)."""
+    t = H.torch()
+    for k, shape in enumerate(((3, 50_000, 1), (1, 1 << 21, 1), (2, 3000, 4095), (1, 200_000, 300),
+                               (1, 1 << 20, 4), (64, 1000, 33), (1, 100_000, 2))):
+        n = shape[0] * shape[1] * shape[2]
+        x = H.upload(workloads.random(n, 880 + k, "normal"))
+        for rev in (True, False):
+            first = rd.rd_cumsum_dim(x, *shape, reverse=rev)
+            for _ in range(4):
+                assert t.equal(rd.rd_cumsum_dim(x, *shape, reverse=rev).view(t.int32),
+                               first.view(t.int32)), (shape, rev)
+
+
 def test_in_place():
     t = H.torch()
     for shape in ((3, 10_000, 1), (2, 300, 17), (1, 1 << 18, 1)):
