@@ -22,6 +22,10 @@ What it computes (the plain definition of a sum, see ``oracle.c``):
 * ``cumsum_dim(x, o, R, i, reverse)`` -> (reverse) cumulative sums along the
   middle axis (POPCORNBENCH level-1 problem 91 trace: cumsum of the flipped
   row, flipped back).
+* ``softmax_denom_dim(x, o, R, i)`` -> (M, S): per output the maximum M and
+  S = sum exp(x - c), c = M when finite else 0, so the softmax denominator is
+  exp(c) * S ("Seven-step reduction" page: the softmax denominator is one of
+  the reductions it names); ``softmax_denom_dim_at`` for chosen outputs.
 * ``within_tolerance``     -> the acceptance rule |got - S| <= 1e-5*A + 1e-6,
   NaN-aware.
 """
@@ -86,6 +90,10 @@ class Oracle:
         lib.oracle_reduce_dim_at.restype = None
         lib.oracle_cumsum_dim.argtypes = [vp, i64, i64, i64, ci, vp, vp, ci]
         lib.oracle_cumsum_dim.restype = None
+        lib.oracle_softmax_denom_dim.argtypes = [vp, i64, i64, i64, vp, vp, ci]
+        lib.oracle_softmax_denom_dim.restype = None
+        lib.oracle_softmax_denom_dim_at.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp]
+        lib.oracle_softmax_denom_dim_at.restype = None
         self.lib = lib
         self.path = library
 
@@ -186,6 +194,38 @@ class Oracle:
                                    s.ctypes.data, a.ctypes.data, int(threads))
         return s, a
 
+    # ---- softmax denominator along the middle axis: (max, shifted sum of exp)
+    def softmax_denom_dim(self, x, outer: int, R: int, inner: int, threads: int = 0):
+        """(M, S), each float64 [outer, inner]: M = max over the middle axis,
+        S = sum exp(x - c) with c = M when M is finite, else 0."""
+        x = _as_f32(x).reshape(-1)
+        if x.size != outer * R * inner:
+            raise ValueError("size %d != %d*%d*%d" % (x.size, outer, R, inner))
+        m = np.empty((outer, inner), dtype=np.float64)
+        s = np.empty((outer, inner), dtype=np.float64)
+        self.lib.oracle_softmax_denom_dim(x.ctypes.data, outer, R, inner, m.ctypes.data,
+                                          s.ctypes.data, int(threads))
+        return m, s
+
+    def softmax_denom_dim_at(self, x, outer: int, R: int, inner: int, o_idx, i_idx):
+        """(M, S) for the outputs (o_idx[k], i_idx[k])."""
+        x = _as_f32(x).reshape(-1)
+        if x.size != outer * R * inner:
+            raise ValueError("size %d != %d*%d*%d" % (x.size, outer, R, inner))
+        o_idx = np.ascontiguousarray(o_idx, dtype=np.int64)
+        i_idx = np.ascontiguousarray(i_idx, dtype=np.int64)
+        if o_idx.shape != i_idx.shape:
+            raise ValueError("index arrays differ in shape")
+        if o_idx.size and (o_idx.min() < 0 or o_idx.max() >= outer
+                           or i_idx.min() < 0 or i_idx.max() >= inner):
+            raise IndexError("sample index out of range")
+        m = np.empty(o_idx.size, dtype=np.float64)
+        s = np.empty(o_idx.size, dtype=np.float64)
+        self.lib.oracle_softmax_denom_dim_at(x.ctypes.data, outer, R, inner, o_idx.ctypes.data,
+                                             i_idx.ctypes.data, o_idx.size, m.ctypes.data,
+                                             s.ctypes.data)
+        return m, s
+
 
 # numbering of the reductions (the same as the library's rd_op)
 OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
@@ -231,6 +271,14 @@ def reduce_dim_at(x, outer: int, R: int, inner: int, op: str, o_idx, i_idx):
 
 def cumsum_dim(x, outer: int, R: int, inner: int, reverse: bool = True, threads: int = 0):
     return default().cumsum_dim(x, outer, R, inner, reverse, threads)
+
+
+def softmax_denom_dim(x, outer: int, R: int, inner: int, threads: int = 0):
+    return default().softmax_denom_dim(x, outer, R, inner, threads)
+
+
+def softmax_denom_dim_at(x, outer: int, R: int, inner: int, o_idx, i_idx):
+    return default().softmax_denom_dim_at(x, outer, R, inner, o_idx, i_idx)
 
 
 def tolerance(abs_sum):

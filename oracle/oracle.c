@@ -296,3 +296,70 @@ void oracle_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner, 
         }
     }
 }
+
+/*
+ * Softmax denominator along the middle axis of a contiguous [outer, R, inner]
+ * array ("Seven-step reduction: 30x from one kernel", opening section: the
+ * softmax denominator is one of the reductions it names).  softmax(x)_r is
+ * exp(x_r) / sum_k exp(x_k); written with a shift c that keeps every
+ * exponent at or below zero, the denominator is exp(c) * s.  For each output
+ * (o, i), over its terms x_r = x[o][r][i], r < R:
+ *
+ *   m = max_r x_r         (IEEE 754-2019 maximum as above; -Inf for R = 0)
+ *   c = m when m is finite, else 0
+ *   s = sum_r exp(x_r - c)
+ *
+ * so that softmax(x)_r = exp(x_r - c) / s and log sum_r exp(x_r) = c + log s.
+ * Shifting by 0 when the maximum is infinite is the reading taken for the
+ * cases the softmax leaves open: all terms -Inf (or none) give s = 0, a +Inf
+ * term gives s = +Inf, a NaN gives NaN.  m_out receives m (exact), s_out
+ * receives s: the maximum in a first sweep over r, then exp() of libm in fp64
+ * on the exactly widened terms, added in increasing r.  All terms of s are
+ * non-negative, so s is also its own magnitude (the acceptance bound's A).
+ * Different o are shared out over OpenMP threads.
+ */
+static double softmax_shift(double m)
+{
+    return isfinite(m) ? m : 0.0;
+}
+
+void oracle_softmax_denom_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
+                              double* m_out, double* s_out, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = oracle_default_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t o = 0; o < outer; ++o) {
+        for (int64_t i = 0; i < inner; ++i) {
+            double m = -INFINITY;
+            for (int64_t r = 0; r < R; ++r)
+                m = maximum754(m, (double)x[(o * R + r) * inner + i]);
+            const double c = softmax_shift(m);
+            double s = 0.0;
+            for (int64_t r = 0; r < R; ++r)
+                s += exp((double)x[(o * R + r) * inner + i] - c);
+            m_out[o * inner + i] = m;
+            s_out[o * inner + i] = s;
+        }
+    }
+}
+
+/* The same for m chosen outputs (o_idx[k], i_idx[k]). */
+void oracle_softmax_denom_dim_at(const float* x, int64_t outer, int64_t R, int64_t inner,
+                                 const int64_t* o_idx, const int64_t* i_idx, int64_t cnt,
+                                 double* m_out, double* s_out)
+{
+    (void)outer;
+    for (int64_t k = 0; k < cnt; ++k) {
+        const float* col = x + o_idx[k] * R * inner + i_idx[k];
+        double m = -INFINITY;
+        for (int64_t r = 0; r < R; ++r)
+            m = maximum754(m, (double)col[r * inner]);
+        const double c = softmax_shift(m);
+        double s = 0.0;
+        for (int64_t r = 0; r < R; ++r)
+            s += exp((double)col[r * inner] - c);
+        m_out[k] = m;
+        s_out[k] = s;
+    }
+}

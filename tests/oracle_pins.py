@@ -18,7 +18,11 @@ What the pins rest on (none of them re-types the oracle's own loop):
 * IEEE special cases -- NaN, +-Inf, signed zero, empty sums;
 * for the other reductions: sum of squares closed forms (n(n+1)(2n+1)/6),
   exact integer sums of squares, numpy's max / min, IEEE 754-2019
-  maximum / minimum special cases, order independence.
+  maximum / minimum special cases, order independence;
+* for the softmax denominator: constant columns (every term exp(0) = 1),
+  a shuffled geometric series (closed form (1 - q^R) / (1 - q)), shift
+  invariance, scipy's and torch's log-sum-exp (independent library
+  routines, special values included), numpy's max.
 """
 from __future__ import annotations
 
@@ -385,11 +389,105 @@ def pin_cumsum_fsum(orc):
         assert abs(S[o, 0] - Sr[0, 0]) <= 2 * R * U53 * A[o, 0]
 
 
+# ------------------------------------------------------ softmax denominator
+def pin_softmax_constants(orc):
+    """A constant column x_r = c has maximum c and every shifted term
+    exp(c - c) = 1, so S = R exactly, for any c; no terms: (-Inf, 0)."""
+    for c in (0.0, 1.0, -1000.0, 1000.0, 3.5, -0.125):
+        for outer, R, inner in ((1, 1, 1), (2, 7, 3), (1, 1000, 1), (3, 5, 130)):
+            x = np.full(outer * R * inner, c, np.float32)
+            M, S = orc.softmax_denom_dim(x, outer, R, inner)
+            assert np.all(M == c) and np.all(S == R), (c, outer, R, inner)
+    M, S = orc.softmax_denom_dim(np.zeros(0, np.float32), 2, 0, 3)
+    assert np.all(M == -math.inf) and np.all(S == 0.0)
+
+
+def pin_softmax_geometric(orc):
+    """Column (o, i) holds k - delta * p for p = 0 .. R-1 in a shuffled order
+    (k an integer of either sign, delta exact in fp32): its maximum is k and
+    S = sum_p q^p = (1 - q^R) / (1 - q) with q = exp(-delta), whatever k."""
+    rng = np.random.default_rng(47)
+    for outer, R, inner, delta in ((2, 20, 3, 0.5), (1, 300, 1, 0.25), (3, 9, 70, 1.0),
+                                   (1, 1, 4, 0.5)):
+        x = np.empty((outer, R, inner), np.float32)
+        k = rng.integers(-60, 60, size=(outer, inner))
+        for o in range(outer):
+            for i in range(inner):
+                x[o, :, i] = k[o, i] - delta * rng.permutation(R)
+        M, S = orc.softmax_denom_dim(x, outer, R, inner)
+        q = math.exp(-delta)
+        want = (1.0 - q ** R) / (1.0 - q)
+        assert np.array_equal(M, k.astype(np.float64)), (outer, R, inner)
+        assert np.all(np.abs(S - want) <= 1e-13 * want), (outer, R, inner, S, want)
+        oo, ii = np.meshgrid(np.arange(outer), np.arange(inner), indexing="ij")
+        m1, s1 = orc.softmax_denom_dim_at(x, outer, R, inner, oo.reshape(-1), ii.reshape(-1))
+        assert np.array_equal(m1, M.reshape(-1)) and np.array_equal(s1, S.reshape(-1))
+
+
+def pin_softmax_library(orc):
+    """Random data: the maximum equals numpy's; c + log S equals scipy's
+    logsumexp along the same axis (an independent implementation); adding
+    an integer to every term moves the maximum by it and leaves S alone."""
+    from scipy.special import logsumexp
+    for k, (outer, R, inner, scale) in enumerate(((3, 5, 7, 1.0), (4, 1000, 1, 10.0),
+                                                  (2, 64, 4095, 3.0), (1, 1, 3, 1.0),
+                                                  (5, 333, 2, 30.0))):
+        x = workloads.random(outer * R * inner, 60 + k, "normal") * np.float32(scale)
+        x3 = x.reshape(outer, R, inner)
+        M, S = orc.softmax_denom_dim(x, outer, R, inner)
+        assert np.array_equal(M, np.max(x3, axis=1).astype(np.float64)), (outer, R, inner)
+        lse = logsumexp(x3.astype(np.float64), axis=1)
+        assert np.all(np.abs(M + np.log(S) - lse) <= 1e-12 * (1 + np.abs(lse))), (outer, R, inner)
+        assert np.all(S >= 1.0) and np.all(S <= R)
+        for shift in (7, -40):
+            M2, S2 = orc.softmax_denom_dim((x + np.float32(shift)).astype(np.float32), outer, R,
+                                           inner)
+            exact = (x + np.float32(shift)).astype(np.float64) == x.astype(np.float64) + shift
+            if exact.all():
+                assert np.array_equal(M2, M + shift)
+                assert np.all(np.abs(S2 - S) <= 1e-13 * S)
+        oo = np.array([0, outer - 1, outer // 2])
+        ii = np.array([inner - 1, 0, inner // 2])
+        m1, s1 = orc.softmax_denom_dim_at(x, outer, R, inner, oo, ii)
+        assert np.array_equal(m1, M[oo, ii]) and np.array_equal(s1, S[oo, ii])
+
+
+def pin_softmax_special(orc):
+    """IEEE special cases, checked against torch.logsumexp in float64 (which
+    also shifts by 0 where the maximum is infinite): -Inf terms add nothing,
+    an all -Inf column gives (-Inf, 0), a +Inf term gives (+Inf, +Inf), a NaN
+    gives NaN."""
+    import torch
+    inf, nan = math.inf, math.nan
+    cols = [[-inf, -inf, -inf], [1.0, -inf, 2.0], [-inf, 5.0, -inf], [inf, 1.0, -2.0],
+            [inf, -inf, 0.0], [inf, inf, 3.0], [nan, 1.0, 2.0], [1.0, 2.0, nan],
+            [-inf, nan, inf], [-0.0, -0.0, -0.0], [-30.0, 0.0, -0.0]]
+    x = np.array(cols, np.float32).T.copy()      # [R = 3, inner = len(cols)]
+    M, S = orc.softmax_denom_dim(x, 1, 3, len(cols))
+    M, S = M.reshape(-1), S.reshape(-1)
+    lse = torch.logsumexp(torch.from_numpy(x.astype(np.float64)), dim=0).numpy()
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ours = np.where(np.isfinite(M), M, 0.0) + np.log(S)
+    for j, col in enumerate(cols):
+        if math.isnan(lse[j]):
+            assert math.isnan(M[j]) and math.isnan(S[j]), col
+        elif math.isinf(lse[j]):
+            assert ours[j] == lse[j], (col, M[j], S[j])
+        else:
+            assert abs(ours[j] - lse[j]) <= 1e-15 * (1 + abs(lse[j])), (col, M[j], S[j])
+    assert M[0] == -inf and S[0] == 0.0
+    assert S[1] == 1.0 + math.exp(-1.0) and M[1] == 2.0
+    assert M[2] == 5.0 and S[2] == 1.0
+    assert M[3] == inf and S[3] == inf
+    assert M[9] == 0.0 and S[9] == 3.0
+
+
 ALL_PINS = [
     pin_harmonic, pin_constants_1d, pin_integers_1d, pin_fsum_1d,
     pin_special_values_1d, pin_index_closed_form, pin_constants_axis,
     pin_bruteforce_axis, pin_fsum_axis, pin_special_values_axis,
     pin_page_shape_facts, pin_sumsq_closed_form, pin_sumsq_exact_and_fsum,
     pin_max_min_library, pin_max_min_special, pin_cumsum_page_example,
-    pin_cumsum_library, pin_cumsum_fsum,
+    pin_cumsum_library, pin_cumsum_fsum, pin_softmax_constants, pin_softmax_geometric,
+    pin_softmax_library, pin_softmax_special,
 ]

@@ -83,6 +83,30 @@ MUTANTS = {
         "            for (int64_t k = 1; k < R; ++k) {\n                const int64_t r = reverse"),
     "cumsum_transposed": (
         "const int64_t e = (o * R + r) * inner + i;", "const int64_t e = (r * outer + o) * inner + i;"),
+    # softmax denominator
+    "softmax_exp_sign_flipped": (
+        "s += exp((double)x[(o * R + r) * inner + i] - c);",
+        "s += exp(c - (double)x[(o * R + r) * inner + i]);"),
+    "softmax_no_shift": (
+        "m = maximum754(m, (double)x[(o * R + r) * inner + i]);\n            const double c = softmax_shift(m);",
+        "m = maximum754(m, (double)x[(o * R + r) * inner + i]);\n            const double c = 0.0;"),
+    "softmax_shift_by_infinite_max": (
+        "return isfinite(m) ? m : 0.0;", "return m;"),
+    "softmax_max_starts_at_zero": (
+        "double m = -INFINITY;\n            for (int64_t r = 0; r < R; ++r)\n                m = maximum754(m, (double)x[",
+        "double m = 0.0;\n            for (int64_t r = 0; r < R; ++r)\n                m = maximum754(m, (double)x["),
+    "softmax_drops_last_term": (
+        "for (int64_t r = 0; r < R; ++r)\n                s += exp((double)x[",
+        "for (int64_t r = 0; r + 1 < R; ++r)\n                s += exp((double)x["),
+    "softmax_transposed": (
+        "s += exp((double)x[(o * R + r) * inner + i] - c);",
+        "s += exp((double)x[(r * outer + o) * inner + i] - c);"),
+    "softmax_shift_by_first_term": (
+        "m = maximum754(m, (double)x[(o * R + r) * inner + i]);\n            const double c = softmax_shift(m);",
+        "m = maximum754(m, (double)x[(o * R + r) * inner + i]);\n            const double c = R ? (double)x[o * R * inner + i] : 0.0;"),
+    "softmax_at_reversed_column": (
+        "const float* col = x + o_idx[k] * R * inner + i_idx[k];",
+        "const float* col = x + o_idx[k] * R * inner + (inner - 1 - i_idx[k]);"),
     # per-output entry point
     "at_reversed_column": (
         "double v = (double)x[(o * R + r) * inner + i];",
