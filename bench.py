@@ -112,8 +112,9 @@ def main(argv=None):
                     help="with --report: also an axis reduce of this [outer, R, inner] "
                          "shape, U[0,1) data from seed 0")
     ap.add_argument("--op", action="append", default=None,
-                    choices=["sum", "sumsq", "max", "min"],
-                    help="with --report: the reductions to time (default: sum)")
+                    choices=["sum", "sumsq", "max", "min", "softmax_denom"],
+                    help="with --report: the reductions to time (default: sum); "
+                    "softmax_denom writes the pair (max, shifted sum of exp)")
     ap.add_argument("--scan", action="store_true",
                     help="with --report: the cumulative sums instead (problem 91's "
                     "[32768, 32768] rows, then each --scan-shape)")
@@ -373,7 +374,7 @@ def report(args, dev, cu):
     for w in todo:
         host = workloads.generate(w)
         x = torch.from_numpy(host).to(dev)
-        out = torch.empty(w.out_numel, dtype=torch.float32, device=dev)
+        out = torch.empty(2 * w.out_numel, dtype=torch.float32, device=dev)
         for op in (args.op or ["sum"]):
             log("report: %s %s" % (w.name, op))
             print(json.dumps(report_one(w, op, host, x, out, flush, threads, cu, args)),
@@ -514,11 +515,21 @@ def report_one(w, op, host, x, out, flush, threads, cu, args):
     import oracle
     import sum_reduction_amd as rd
 
+    nout = w.out_numel
+    pair = op == "softmax_denom"
+    # the softmax denominator writes two outputs (max, sum) per reduced column
+    nbytes = w.in_bytes + 4 * nout * (2 if pair else 1)
+
     def call():
-        if w.full_reduce:
-            rd.rd_reduce_1d(x, op, out=out)
+        if pair:
+            if w.full_reduce:
+                rd.rd_softmax_denom_1d(x, out[:1], out[1:2])
+            else:
+                rd.rd_softmax_denom_dim(x, w.outer, w.R, w.inner, out[:nout], out[nout:])
+        elif w.full_reduce:
+            rd.rd_reduce_1d(x, op, out=out[:1])
         else:
-            rd.rd_reduce_dim(x, w.outer, w.R, w.inner, op, out=out)
+            rd.rd_reduce_dim(x, w.outer, w.R, w.inner, op, out=out[:nout])
 
     small = w.in_bytes < (1 << 30)
     reps = args.reps or (500 if small else 50)
@@ -543,9 +554,8 @@ def report_one(w, op, host, x, out, flush, threads, cu, args):
         ms.sort()
         return {"ms_median": round(ms[len(ms) // 2], 5), "ms_min": round(ms[0], 5),
                 "ms_p90": round(ms[int(0.9 * (len(ms) - 1))], 5),
-                "GBps_median": round(w.algorithmic_bytes / ms[len(ms) // 2] / 1e6, 1),
-                "frac_of_peak": round(w.algorithmic_bytes / ms[len(ms) // 2] / 1e6
-                                      / PEAK_GBS, 4)}
+                "GBps_median": round(nbytes / ms[len(ms) // 2] / 1e6, 1),
+                "frac_of_peak": round(nbytes / ms[len(ms) // 2] / 1e6 / PEAK_GBS, 4)}
 
     warm = timed(False)
     cold = timed(True)
@@ -553,11 +563,18 @@ def report_one(w, op, host, x, out, flush, threads, cu, args):
             else rd.rd_plan_dim(cu, w.outer, w.R, w.inner)).as_dict()
     if args.no_oracle:
         return {"workload": w.name, "op": op, "shape": list(w.shape),
-                "algorithmic_bytes": w.algorithmic_bytes, "warm": warm, "cold": cold,
+                "algorithmic_bytes": nbytes, "warm": warm, "cold": cold,
                 "reps": reps, "plan": plan}
-    got = out.cpu().numpy().reshape(-1)
+    got = out[:nout].cpu().numpy().reshape(-1)
     t0 = time.perf_counter()
-    if w.full_reduce:
+    if pair:
+        if w.full_reduce:
+            M, S = oracle.softmax_denom_dim(host, 1, w.numel, 1)
+        else:
+            M, S = oracle.softmax_denom_dim(host, w.outer, w.R, w.inner, threads)
+        A = S   # every term exp(x - c) is non-negative
+        got_m, got = got, out[nout:].cpu().numpy().reshape(-1)
+    elif w.full_reduce:
         S, A = oracle.reduce_1d(host, op)
         S, A = np.array([S]), np.array([A])
     else:
@@ -568,9 +585,9 @@ def report_one(w, op, host, x, out, flush, threads, cu, args):
     tol = oracle.tolerance(A.reshape(-1))
     line = {
         "workload": w.name, "op": op, "shape": list(w.shape),
-        "algorithmic_bytes": w.algorithmic_bytes,
+        "algorithmic_bytes": nbytes,
         "warm": warm, "cold": cold, "reps": reps, "plan": plan,
-        "cpu_oracle": {"s": round(cpu_s, 4), "GBps": round(w.algorithmic_bytes / cpu_s / 1e9, 3),
+        "cpu_oracle": {"s": round(cpu_s, 4), "GBps": round(nbytes / cpu_s / 1e9, 3),
                        "threads": 1 if w.full_reduce else threads},
         "gpu_over_cpu": round(cpu_s * 1e3 / warm["ms_median"], 1),
         "parity": {"ok": bool(oracle.within_tolerance(got, S.reshape(-1),
@@ -582,6 +599,10 @@ def report_one(w, op, host, x, out, flush, threads, cu, args):
     if op in ("max", "min"):  # exact reductions: the bits must match
         line["parity"]["bit_exact"] = bool(np.array_equal(
             got.view(np.uint32), S.reshape(-1).astype(np.float32).view(np.uint32)))
+    if pair:  # the maxima are exact
+        line["parity"]["max_bit_exact"] = bool(np.array_equal(
+            got_m.view(np.uint32), M.reshape(-1).astype(np.float32).view(np.uint32)))
+        line["parity"]["ok"] = line["parity"]["ok"] and line["parity"]["max_bit_exact"]
     if w.name == "harmonic_1e6" and op == "sum":
         line["harmonic_closed_form"] = float(
             np.log(w.numel) + 0.5772156649015329 + 1 / (2 * w.numel)

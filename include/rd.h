@@ -81,7 +81,10 @@ typedef enum rd_op {
                         is its square root)   empty: +0.0 */
     RD_OP_MAX = 2,   /* maximum, IEEE 754-2019: NaN propagates, -0 < +0
                                               empty: -Inf */
-    RD_OP_MIN = 3    /* minimum, IEEE 754-2019 empty: +Inf */
+    RD_OP_MIN = 3,   /* minimum, IEEE 754-2019 empty: +Inf */
+    RD_OP_SOFTMAX_DENOM = 4  /* the pair (max x, sum exp(x - c)); only for
+                                rd_softmax_denom_1d / rd_softmax_denom_dim
+                                and rd_tune_supported */
 } rd_op;
 
 typedef enum rd_status {
@@ -136,6 +139,39 @@ rd_status rd_reduce_1d(const float* x, int64_t n, int32_t op, float* out,
                        hipStream_t stream);
 rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
                         int32_t op, float* out, hipStream_t stream);
+
+/*
+ * Softmax denominator along the middle axis of a contiguous [outer, R, inner]
+ * array ("Seven-step reduction: 30x from one kernel", opening section: the
+ * softmax denominator is one of the reductions it lists with the sum and the
+ * maximum).  For each output e = o * inner + i, over its terms
+ * x_r = x[(o * R + r) * inner + i], r < R:
+ *   out_max[e] = m = max_r x_r        (IEEE 754-2019 maximum, exact)
+ *   out_sum[e] = s = sum_r exp(x_r - c),  c = m if m is finite, else 0
+ * so softmax(x)_r = exp(x_r - c) / s and log(sum_r exp(x_r)) = c + log(s).
+ * One pass over x: the maximum and the sum of exponentials are folded
+ * together, with the running sums re-centred on the running maxima.
+ *   x        device pointer to outer*R*inner floats, row-major, contiguous,
+ *            4-B aligned (may be NULL when outer*R*inner == 0)
+ *   outer, R, inner  >= 0, with outer*R*inner*8 representable in int64
+ *   out_max, out_sum  device pointers to outer*inner floats each, 4-B
+ *            aligned, overlapping neither x nor each other (may be NULL when
+ *            outer*inner == 0, which writes nothing)
+ *   stream   HIP stream of the current device, 0 for the null stream
+ * R == 0 writes (-Inf, 0).  A -Inf term adds nothing, a +Inf term gives
+ * (+Inf, +Inf), a NaN gives (NaN, NaN).  out_max is exact and out_sum is
+ * within fp32 rounding of its terms (each e^y evaluated as 2^(y log2 e) by
+ * the hardware's exp2); bitwise reproducible for a given device and shape.
+ * Returns RD_OK once the work is enqueued; RD_ERR_INVALID_ARG,
+ * RD_ERR_NO_DEVICE, RD_ERR_ALLOC (a split shape's pairs of partial results,
+ * 8 bytes each), RD_ERR_LAUNCH as for the reductions, outputs untouched.
+ * rd_softmax_denom_1d(x, n, ...) is the case outer = inner = 1, R = n, with
+ * one float at each of out_max and out_sum.
+ */
+rd_status rd_softmax_denom_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
+                               float* out_max, float* out_sum, hipStream_t stream);
+rd_status rd_softmax_denom_1d(const float* x, int64_t n, float* out_max, float* out_sum,
+                              hipStream_t stream);
 
 /*
  * Cumulative sum along the middle axis of a contiguous [outer, R, inner]

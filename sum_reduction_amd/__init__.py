@@ -25,7 +25,8 @@ __all__ = [
     "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
     "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "sum", "tuning",
     "PATH_NAMES", "OPS", "rd_reduce_1d", "rd_reduce_dim", "reduce", "rd_cumsum_dim",
-    "rd_plan_cumsum", "cumsum",
+    "rd_plan_cumsum", "cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim",
+    "softmax_denom",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +35,9 @@ LIBRARY = os.path.join(_HERE, "librd.so")
 RD_OK = 0
 # rd_op: the reductions (the sum is the method; the others share its kernels)
 OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
+# the softmax denominator's pair (maximum, shifted sum of exponentials) has
+# entry points of its own; its code is accepted by rd_tune_supported
+OP_SOFTMAX_DENOM = 4
 PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
               5: "cols_small", 6: "scan_rows", 7: "scan_cols", 8: "scan_cols_small"}
 ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
@@ -101,6 +105,10 @@ def load():
     lib.rd_reduce_1d.restype = ctypes.c_int
     lib.rd_reduce_dim.argtypes = [vp, i64, i64, i64, i32, vp, vp]
     lib.rd_reduce_dim.restype = ctypes.c_int
+    lib.rd_softmax_denom_1d.argtypes = [vp, i64, vp, vp, vp]
+    lib.rd_softmax_denom_1d.restype = ctypes.c_int
+    lib.rd_softmax_denom_dim.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    lib.rd_softmax_denom_dim.restype = ctypes.c_int
     lib.rd_cumsum_dim.argtypes = [vp, i64, i64, i64, i32, vp, vp]
     lib.rd_cumsum_dim.restype = ctypes.c_int
     lib.rd_plan_cumsum.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(RdPlan)]
@@ -168,8 +176,8 @@ def rd_tune_set(tune: Optional[RdTune]):
 def rd_tune_supported(path: str, group_or_col_waves: int, row_waves: int,
                       unroll: int, op: str = "sum") -> bool:
     code = {"rows": 2, "cols": 4, "cols_small": 5}[path]
-    return bool(load().rd_tune_supported(OPS[op], code, group_or_col_waves, row_waves,
-                                         unroll))
+    opc = OP_SOFTMAX_DENOM if op == "softmax_denom" else OPS[op]
+    return bool(load().rd_tune_supported(opc, code, group_or_col_waves, row_waves, unroll))
 
 
 class tuning:
@@ -296,6 +304,53 @@ def reduce(x, op="sum", dim: Optional[int] = None, out=None, stream=None):
     res = rd_reduce_dim(x, outer, shape[d], inner, op,
                         None if out is None else out.view(outer, inner), stream)
     return res.view(shape[:d] + shape[d + 1:])
+
+
+def rd_softmax_denom_dim(x, outer: int, R: int, inner: int, out_max=None, out_sum=None,
+                         stream=None):
+    """Softmax denominator over the middle axis of x viewed as [outer, R,
+    inner]: returns (m, s), each [outer, inner] (allocated when None), with
+    m = max over r and s = sum_r exp(x - c), c = m where m is finite, else 0;
+    so softmax(x) = exp(x - c) / s and logsumexp(x) = c + log(s)."""
+    _check_input(x, outer * R * inner)
+    out_max = _out_tensor(out_max, outer * inner, x.device, (outer, inner))
+    out_sum = _out_tensor(out_sum, outer * inner, x.device, (outer, inner))
+    xp = x.data_ptr() if x.numel() else None
+    mp = out_max.data_ptr() if out_max.numel() else None
+    sp = out_sum.data_ptr() if out_sum.numel() else None
+    _check(load().rd_softmax_denom_dim(xp, outer, R, inner, mp, sp, _stream_handle(stream)),
+           "rd_softmax_denom_dim")
+    return out_max, out_sum
+
+
+def rd_softmax_denom_1d(x, out_max=None, out_sum=None, stream=None):
+    """(m, s) of all elements of x: 1-element tensors (rd_softmax_denom_1d)."""
+    _check_input(x, x.numel() if hasattr(x, "numel") else -1)
+    out_max = _out_tensor(out_max, 1, x.device, (1,))
+    out_sum = _out_tensor(out_sum, 1, x.device, (1,))
+    ptr = x.data_ptr() if x.numel() else None
+    _check(load().rd_softmax_denom_1d(ptr, x.numel(), out_max.data_ptr(), out_sum.data_ptr(),
+                                      _stream_handle(stream)), "rd_softmax_denom_1d")
+    return out_max, out_sum
+
+
+def softmax_denom(x, dim: Optional[int] = None, stream=None):
+    """(m, s) over all elements (dim=None, 0-d results) or over one dimension
+    of a contiguous float32 GPU tensor; see rd_softmax_denom_dim."""
+    if dim is None:
+        m, s = rd_softmax_denom_1d(x, stream=stream)
+        return m.view(()), s.view(())
+    shape = tuple(x.shape)
+    d = dim % len(shape)
+    outer = 1
+    for k in shape[:d]:
+        outer *= k
+    inner = 1
+    for k in shape[d + 1:]:
+        inner *= k
+    m, s = rd_softmax_denom_dim(x, outer, shape[d], inner, stream=stream)
+    rest = shape[:d] + shape[d + 1:]
+    return m.view(rest), s.view(rest)
 
 
 def rd_cumsum_dim(x, outer: int, R: int, inner: int, reverse: bool = True, out=None,

@@ -148,7 +148,7 @@ bool inject(const char* name) {
 }
 
 rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, int64_t outer,
-                  int64_t R, int64_t inner, float* out, hipStream_t s) {
+                  int64_t R, int64_t inner, rd::Results out, hipStream_t s) {
     if (p.path == RD_PATH_NONE) return RD_OK;
     if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
@@ -158,6 +158,10 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, int64_t
                                               size_t(p.workspace_bytes), dev.pool, s);
         if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
     }
+    // partial results: one array, or the two halves of the pairs
+    rd::Results part{ws, nullptr};
+    if (ws && op == RD_OP_SOFTMAX_DENOM)
+        part.b = ws + p.workspace_bytes / int64_t(2 * sizeof(float));
     hipError_t e = hipSuccess;
     switch (p.path) {
         case RD_PATH_ZERO:
@@ -168,23 +172,23 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, int64_t
             break;
         case RD_PATH_ROWS:
             if (p.split == 1) {
-                e = rd::launch_rows(op, p, x, outer, R, out, nullptr, nullptr, s);
+                e = rd::launch_rows(op, p, x, outer, R, out, nullptr, rd::Results{}, s);
             } else {
                 uint32_t* ticket =
                     p.combine == RD_COMBINE_LAST_BLOCK ? stream_ticket(dev, s) : nullptr;
-                e = rd::launch_rows(op, p, x, outer, R, ws, ticket, out, s);
+                e = rd::launch_rows(op, p, x, outer, R, part, ticket, out, s);
                 if (e == hipSuccess && !ticket)
-                    e = rd::launch_rows_combine(op, ws, outer, p.split, out, s);
+                    e = rd::launch_rows_combine(op, part, outer, p.split, out, s);
             }
             break;
         case RD_PATH_COLS:
         case RD_PATH_COLS_SMALL: {
-            float* dst = p.split == 1 ? out : ws;
+            const rd::Results dst = p.split == 1 ? out : part;
             e = p.path == RD_PATH_COLS
                     ? rd::launch_cols(op, p, x, outer, R, inner, dst, s)
                     : rd::launch_cols_small(op, p, x, outer, R, inner, dst, s);
             if (e == hipSuccess && p.split > 1)
-                e = rd::launch_slab_combine(op, ws, p.split, outer * inner, out, s);
+                e = rd::launch_slab_combine(op, part, p.split, outer * inner, out, s);
             break;
         }
         default:
@@ -199,7 +203,7 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, int64_t
 }
 
 rd_status reduce_checked(const float* x, int64_t outer, int64_t R, int64_t inner, int op,
-                         float* out, hipStream_t stream) {
+                         rd::Results out, hipStream_t stream) {
     Device* dev = nullptr;
     rd_status st = current_device(&dev);
     if (st != RD_OK) return st;
@@ -221,7 +225,7 @@ rd_status rd_reduce_1d(const float* x, int64_t n, int32_t op, float* out,
     if (n < 0 || n > INT64_MAX / 4 || !out || !aligned4(out)) return RD_ERR_INVALID_ARG;
     if (n > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
     if (overlap(x, n, out, 1)) return RD_ERR_INVALID_ARG;
-    return reduce_checked(x, 1, n, 1, op, out, stream);
+    return reduce_checked(x, 1, n, 1, op, rd::Results{out, nullptr}, stream);
 }
 
 rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner, int32_t op,
@@ -237,7 +241,32 @@ rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
     if (!out || !aligned4(out)) return RD_ERR_INVALID_ARG;
     if (nin > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
     if (overlap(x, nin, out, nout)) return RD_ERR_INVALID_ARG;
-    return reduce_checked(x, outer, R, inner, op, out, stream);
+    return reduce_checked(x, outer, R, inner, op, rd::Results{out, nullptr}, stream);
+}
+
+rd_status rd_softmax_denom_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
+                               float* out_max, float* out_sum, hipStream_t stream) {
+    if (outer < 0 || R < 0 || inner < 0) return RD_ERR_INVALID_ARG;
+    const int64_t lim = INT64_MAX / 8;
+    if (outer && inner && inner > lim / outer) return RD_ERR_INVALID_ARG;
+    const int64_t nout = outer * inner;
+    if (nout && R && R > lim / nout) return RD_ERR_INVALID_ARG;
+    const int64_t nin = nout * R;
+    if (nout == 0) return RD_OK;  // nothing to write, no HIP call
+    if (!out_max || !out_sum || !aligned4(out_max) || !aligned4(out_sum))
+        return RD_ERR_INVALID_ARG;
+    if (nin > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
+    if (overlap(x, nin, out_max, nout) || overlap(x, nin, out_sum, nout) ||
+        overlap(out_max, nout, out_sum, nout))
+        return RD_ERR_INVALID_ARG;
+    return reduce_checked(x, outer, R, inner, RD_OP_SOFTMAX_DENOM,
+                          rd::Results{out_max, out_sum}, stream);
+}
+
+rd_status rd_softmax_denom_1d(const float* x, int64_t n, float* out_max, float* out_sum,
+                              hipStream_t stream) {
+    if (n < 0 || n > INT64_MAX / 8) return RD_ERR_INVALID_ARG;
+    return rd_softmax_denom_dim(x, 1, n, 1, out_max, out_sum, stream);
 }
 
 rd_status rd_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,

@@ -27,22 +27,30 @@ constexpr int64_t kMaxBlocks = int64_t(1) << 20;
 rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op,
                    const rd_tune* tune, rd_plan* plan);
 
+// Where a launch stores its results: `a` holds them (for the softmax
+// denominator, the maxima), `b` the softmax denominator's sums (null for the
+// other operators).  Workspaces of partial results are laid out the same way.
+struct Results {
+    float* a;
+    float* b;
+};
+
 // Kernel launchers (rd_kernels.hip).  Each enqueues on `s` and returns the
 // error hipLaunchKernel reports for the launch; `op` is an rd_op.
-hipError_t launch_fill_start(int op, float* out, int64_t n, hipStream_t s);
+hipError_t launch_fill_start(int op, Results out, int64_t n, hipStream_t s);
 // ticket == nullptr: dst receives the piece results (or the row results when
 // p.split == 1); otherwise the last workgroup also combines them into out.
 hipError_t launch_rows(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       float* dst, uint32_t* ticket, float* out, hipStream_t s);
-hipError_t launch_rows_short(int op, const float* x, int64_t outer, int64_t R, float* out,
+                       Results dst, uint32_t* ticket, Results out, hipStream_t s);
+hipError_t launch_rows_short(int op, const float* x, int64_t outer, int64_t R, Results out,
                              hipStream_t s);
-hipError_t launch_rows_combine(int op, const float* part, int64_t outer, int64_t P,
-                               float* out, hipStream_t s);
+hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, Results out,
+                               hipStream_t s);
 hipError_t launch_cols(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       int64_t inner, float* dst, hipStream_t s);
+                       int64_t inner, Results dst, hipStream_t s);
 hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, int64_t outer,
-                             int64_t R, int64_t inner, float* dst, hipStream_t s);
-hipError_t launch_slab_combine(int op, const float* slab, int64_t S, int64_t n, float* out,
+                             int64_t R, int64_t inner, Results dst, hipStream_t s);
+hipError_t launch_slab_combine(int op, Results slab, int64_t S, int64_t n, Results out,
                                hipStream_t s);
 
 // Cumulative sums (rd_scan.hip).  Rows (inner == 1): item = (row, piece of

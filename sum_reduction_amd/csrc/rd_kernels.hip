@@ -115,16 +115,229 @@ struct Op<RD_OP_MIN> {
     static __device__ __forceinline__ float join(float a, float b) { return fold(a, b); }
 };
 
-template <int OP>
-__device__ __forceinline__ v4f start4() {
-    const float s = Op<OP>::start();
-    return v4f{s, s, s, s};
+// The softmax denominator ("Seven-step reduction: 30x from one kernel",
+// opening section, lists it beside the sum and the maximum): per output the
+// maximum m of its terms and s = sum exp(x - c) with c = m when m is finite,
+// else 0, so that softmax(x) = exp(x - c) / s.  It is one pass over x: the
+// maximum and the sum of exponentials are folded together ("online"
+// softmax), e^y being computed as 2^(y log2 e) by the hardware exp2.
+//  * A lane's running state is (m, c, s) with s = sum exp(x - c) over the
+//    terms it has seen.  The shift c is moved only when the running maximum
+//    leaves [c, c + kLazy] (lazy re-centring): s is then multiplied by
+//    e^(c_old - c_new) <= e^-kLazy, so the rounding of each re-centring
+//    weighs on terms that the next one shrinks by e^-kLazy again, and the
+//    errors cannot pile up however slowly the maximum creeps up; every term
+//    stays at or below e^kLazy.
+//  * Joined states, and stored ones, are re-centred on their maximum
+//    exactly (c = m, or 0 when m is not finite), which the pair (m, s)
+//    implies; a join multiplies by e^(c - m) with the exponent's rounding
+//    compensated (2^(zh + zl) = 2^zh (1 + zl ln 2) with zh + zl = d log2 e
+//    to ~2^-48).  Joins of a finite maximum re-centre both sides; joins of
+//    an infinite or NaN maximum add the s values (+Inf, NaN propagate).
+//  * Terms x = -Inf add exp(-Inf) = 0; +Inf makes m = +Inf and s = +Inf; a
+//    NaN makes both NaN; no terms give (-Inf, 0).
+constexpr float kLog2e = 1.44269502f;        // log2(e) rounded to fp32
+constexpr float kLog2eLo = 1.925963e-8f;     // log2(e) - kLog2e
+constexpr float kLn2 = 0.693147182f;
+constexpr float kLazy = 8.f;
+
+__device__ __forceinline__ float sm_exp(float y) {
+    return __builtin_amdgcn_exp2f(y * kLog2e);
 }
 
-// The four lanes of a float4 partial result joined in a fixed order.
+__device__ __forceinline__ v4f sm_exp(v4f y) {
+    return v4f{sm_exp(y.x), sm_exp(y.y), sm_exp(y.z), sm_exp(y.w)};
+}
+
+__device__ __forceinline__ bool sm_finite(float m) { return __builtin_isfinite(m); }
+
+// The shift a maximum implies: m when finite, else 0.
+__device__ __forceinline__ float sm_shift(float m) { return sm_finite(m) ? m : 0.f; }
+
+// e^(a - b) for finite a, b, with the exponent's rounding compensated: the
+// difference is split exactly into dh + dl (two-sum), d log2 e into zh + zl,
+// and 2^(zh + zl) = 2^zh (1 + zl ln 2).
+__device__ __forceinline__ float sm_factor(float a, float b) {
+    const float dh = a - b;
+    const float bv = dh - a;
+    const float dl = (a - (dh - bv)) - (b + bv);
+    const float zh = dh * kLog2e;
+    const float zl = (__builtin_fmaf(dh, kLog2e, -zh) + dh * kLog2eLo) + dl * kLog2e;
+    const float e = __builtin_amdgcn_exp2f(zh);
+    return __builtin_fmaf(e, zl * kLn2, e);
+}
+
+// s * e^(a - b) for finite a, b; s == 0 stays 0 whatever the factor, and
+// a == b leaves s as it is.  No branch: both sides are computed.
+__device__ __forceinline__ float sm_rescale(float s, float a, float b) {
+    const float f = sm_factor(a, b);
+    return ((s == 0.f) | (a == b)) ? s : s * f;
+}
+
+struct SmPair {   // (m, s), s relative to sm_shift(m)
+    float m, s;
+};
+struct SmState4 {  // four independent running states
+    v4f m, c, s;
+};
+struct SmOut {    // where pairs are stored: the maxima, the sums
+    float* __restrict__ m;
+    float* __restrict__ s;
+};
+
+__device__ __forceinline__ SmPair sm_join(SmPair a, SmPair b) {
+    const float m = __builtin_elementwise_maximum(a.m, b.m);
+    if (!sm_finite(m)) return SmPair{m, a.s + b.s};
+    return SmPair{m, sm_rescale(a.s, sm_shift(a.m), m) + sm_rescale(b.s, sm_shift(b.m), m)};
+}
+
+// ------------------------------------------------------------- states
+// St<OP> is how the kernels hold, move and store partial results:
+//   S1 / S4   one partial result / four independent ones (float4 lanes)
+//   Out       where results are stored (an array, or a pair of arrays)
+//   start1/4  the empty result;  fold(S4, v4f) adds one term per lane;
+//   fold_x    adds one term to lane x only;  fold_all<U> adds U float4s of
+//   terms into acc[0..1];  join (S1 or S4);  lane / set_lane move one lane
+//   of an S4;  get / put / at read, write and offset an Out;  fill is the
+//   value of a load lane that holds no term (neutral for fold).
+// For sum, sum of squares, maximum and minimum a result is one float and
+// every step is the Op<OP> arithmetic above.
 template <int OP>
-__device__ __forceinline__ float join_lanes(v4f a) {
-    return Op<OP>::join(Op<OP>::join(a.x, a.y), Op<OP>::join(a.z, a.w));
+struct St {
+    typedef float S1;
+    typedef v4f S4;
+    typedef float* __restrict__ Out;
+    static __device__ __forceinline__ S1 start1() { return Op<OP>::start(); }
+    static __device__ __forceinline__ S4 start4() {
+        const float s = Op<OP>::start();
+        return v4f{s, s, s, s};
+    }
+    static __device__ __forceinline__ float fill() { return Op<OP>::start(); }
+    static __device__ __forceinline__ S4 fold(S4 a, v4f v) { return Op<OP>::fold(a, v); }
+    static __device__ __forceinline__ S1 fold(S1 a, float v) { return Op<OP>::fold(a, v); }
+    static __device__ __forceinline__ S4 fold_x(S4 a, float v) {
+        a.x = Op<OP>::fold(a.x, v);
+        return a;
+    }
+    template <int U>
+    static __device__ __forceinline__ void fold_all(S4 (&acc)[2], const v4f (&v)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u & 1] = Op<OP>::fold(acc[u & 1], v[u]);
+    }
+    static __device__ __forceinline__ S4 join(S4 a, S4 b) { return Op<OP>::join(a, b); }
+    static __device__ __forceinline__ S1 join(S1 a, S1 b) { return Op<OP>::join(a, b); }
+    static __device__ __forceinline__ S1 lane(S4 a, int q) { return a[q]; }
+    static __device__ __forceinline__ void set_lane(S4& a, int q, S1 v) { a[q] = v; }
+    static __device__ __forceinline__ S1 get(Out o, int64_t e) { return o[e]; }
+    static __device__ __forceinline__ void put(Out o, int64_t e, S1 v) { o[e] = v; }
+    static __device__ __forceinline__ Out at(Out o, int64_t e) { return o + e; }
+    static Out make_out(float* a, float*) { return a; }
+};
+
+template <>
+struct St<RD_OP_SOFTMAX_DENOM> {
+    typedef SmPair S1;
+    typedef SmState4 S4;
+    typedef SmOut Out;
+    static __device__ __forceinline__ S1 start1() { return SmPair{-__builtin_inff(), 0.f}; }
+    static __device__ __forceinline__ S4 start4() {
+        const float n = -__builtin_inff();
+        return SmState4{v4f{n, n, n, n}, v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    }
+    static __device__ __forceinline__ float fill() { return -__builtin_inff(); }
+    // U float4s of terms into acc[0]: the new maxima first, a lazy re-centring
+    // of the lanes whose finite maximum left [c, c + kLazy] (or that hold
+    // nothing yet, s == 0, where it costs no rounding), then the sum of the
+    // exponentials.
+    template <int U>
+    static __device__ __forceinline__ void fold_all(S4 (&acc)[2], const v4f (&v)[U]) {
+        S4& a = acc[0];
+        v4f mb = a.m;
+#pragma unroll
+        for (int u = 0; u < U; ++u) mb = __builtin_elementwise_maximum(mb, v[u]);
+        // A lane whose state holds a sum (s != 0) has c <= m: c was a
+        // maximum of its terms.  Re-centre where the maximum is finite and
+        // either nothing is held yet or it passed c + kLazy; the test takes
+        // no branch per lane, the (rare) re-centring one for all four.
+        bool need[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            need[q] = sm_finite(mb[q]) & ((a.s[q] == 0.f) | (mb[q] > a.c[q] + kLazy));
+        if (need[0] | need[1] | need[2] | need[3]) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float r = sm_rescale(a.s[q], a.c[q], mb[q]);
+                a.s[q] = need[q] ? r : a.s[q];
+                a.c[q] = need[q] ? mb[q] : a.c[q];
+            }
+        }
+        a.m = mb;
+        // the U exponentials summed by a pairwise tree, then added to s: the
+        // long-running sum takes one rounding per U terms
+        v4f t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) t[u] = sm_exp(v[u] - a.c);
+#pragma unroll
+        for (int w = 1; w < U; w *= 2)
+#pragma unroll
+            for (int u = 0; u + w < U; u += 2 * w) t[u] = t[u] + t[u + w];
+        a.s = a.s + t[0];
+    }
+    static __device__ __forceinline__ S4 fold(S4 a, v4f v) {
+        S4 acc[2] = {a, a};
+        const v4f w[1] = {v};
+        fold_all<1>(acc, w);
+        return acc[0];
+    }
+    static __device__ __forceinline__ S4 fold_x(S4 a, float v) {
+        const float n = -__builtin_inff();
+        return fold(a, v4f{v, n, n, n});
+    }
+    static __device__ __forceinline__ S1 fold(S1 a, float v) {
+        const bool f = sm_finite(v);
+        return sm_join(a, SmPair{v, f ? 1.f : sm_exp(v)});
+    }
+    // one lane of a running state, re-centred on its maximum
+    static __device__ __forceinline__ S1 lane(S4 a, int q) {
+        const float m = a.m[q];
+        return SmPair{m, sm_finite(m) ? sm_rescale(a.s[q], a.c[q], m) : a.s[q]};
+    }
+    static __device__ __forceinline__ void set_lane(S4& a, int q, S1 v) {
+        a.m[q] = v.m;
+        a.c[q] = sm_shift(v.m);
+        a.s[q] = v.s;
+    }
+    static __device__ __forceinline__ S4 join(S4 a, S4 b) {
+        S4 r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float m = __builtin_elementwise_maximum(a.m[q], b.m[q]);
+            r.m[q] = m;
+            if (sm_finite(m)) {
+                r.c[q] = m;
+                r.s[q] = sm_rescale(a.s[q], a.c[q], m) + sm_rescale(b.s[q], b.c[q], m);
+            } else {
+                r.c[q] = 0.f;
+                r.s[q] = a.s[q] + b.s[q];
+            }
+        }
+        return r;
+    }
+    static __device__ __forceinline__ S1 join(S1 a, S1 b) { return sm_join(a, b); }
+    static __device__ __forceinline__ S1 get(Out o, int64_t e) { return SmPair{o.m[e], o.s[e]}; }
+    static __device__ __forceinline__ void put(Out o, int64_t e, S1 v) {
+        o.m[e] = v.m;
+        o.s[e] = v.s;
+    }
+    static __device__ __forceinline__ Out at(Out o, int64_t e) { return SmOut{o.m + e, o.s + e}; }
+    static Out make_out(float* a, float* b) { return SmOut{a, b}; }
+};
+
+// The four lanes of an S4 joined in a fixed order.
+template <int OP>
+__device__ __forceinline__ typename St<OP>::S1 join_lanes(typename St<OP>::S4 a) {
+    typedef St<OP> T;
+    return T::join(T::join(T::lane(a, 0), T::lane(a, 1)), T::join(T::lane(a, 2), T::lane(a, 3)));
 }
 
 // ------------------------------------------------- wave and block steps
@@ -135,6 +348,27 @@ __device__ __forceinline__ float dpp(float v) {
                                            0xF, 0xF, false));
 }
 
+template <int kCtrl>
+__device__ __forceinline__ SmPair dpp(SmPair v) {
+    return SmPair{dpp<kCtrl>(v.m), dpp<kCtrl>(v.s)};
+}
+
+// ds_swizzle swap of 16 lanes, and v_readlane, for each kind of result
+__device__ __forceinline__ float swap16(float v) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+__device__ __forceinline__ SmPair swap16(SmPair v) { return SmPair{swap16(v.m), swap16(v.s)}; }
+
+__device__ __forceinline__ float read_lane(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+__device__ __forceinline__ SmPair read_lane(SmPair v, int l) {
+    return SmPair{read_lane(v.m, l), read_lane(v.s, l)};
+}
+
 // Join of v over the 64 lanes of a wavefront; every lane must be active.
 // Butterfly: lane pairs at distance 1 and 2 (DPP quad_perm), quads paired by
 // mirroring 8 lanes (row_half_mirror), 8-lane halves paired by mirroring 16
@@ -143,18 +377,14 @@ __device__ __forceinline__ float dpp(float v) {
 // lane's value with an equal-rank partner's, and every join is commutative,
 // so every lane ends with the same bits.
 template <int OP>
-__device__ __forceinline__ float wave_reduce(float v) {
-    v = Op<OP>::join(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
-    v = Op<OP>::join(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
-    v = Op<OP>::join(v, dpp<0x141>(v));  // row_half_mirror
-    v = Op<OP>::join(v, dpp<0x140>(v));  // row_mirror
-    v = Op<OP>::join(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(
-                                                      __builtin_bit_cast(int, v), 0x401F)));
-    const float lo = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    const float hi = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    return Op<OP>::join(lo, hi);
+__device__ __forceinline__ typename St<OP>::S1 wave_reduce(typename St<OP>::S1 v) {
+    typedef St<OP> T;
+    v = T::join(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = T::join(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = T::join(v, dpp<0x141>(v));  // row_half_mirror
+    v = T::join(v, dpp<0x140>(v));  // row_mirror
+    v = T::join(v, swap16(v));
+    return T::join(read_lane(v, 0), read_lane(v, 32));
 }
 
 // The value v of lane `src` (ds_bpermute).  v is taken by value: a bit cast
@@ -165,18 +395,32 @@ __device__ __forceinline__ float lane_value(int src, float v) {
                               __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, v)));
 }
 
+// All four lanes of lane `src`'s partial results, one permute per float.
+__device__ __forceinline__ v4f lane_value(int src, v4f a) {
+    v4f t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = lane_value(src, a[j]);
+    return t;
+}
+
+__device__ __forceinline__ SmState4 lane_value(int src, SmState4 a) {
+    return SmState4{lane_value(src, a.m), lane_value(src, a.c), lane_value(src, a.s)};
+}
+
 // Join over a kBlock-thread workgroup, valid in thread 0: wave butterflies,
 // then the wave results in wave order.  The caller syncs before reusing lds.
 template <int OP>
-__device__ __forceinline__ float block_reduce(float v, float* lds) {
+__device__ __forceinline__ typename St<OP>::S1 block_reduce(typename St<OP>::S1 v,
+                                                            typename St<OP>::S1* lds) {
+    typedef St<OP> T;
     v = wave_reduce<OP>(v);
     if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = v;
     __syncthreads();
-    float t = Op<OP>::start();
+    typename T::S1 t = T::start1();
     if (threadIdx.x == 0) {
         t = lds[0];
 #pragma unroll
-        for (int k = 1; k < kBlock / kWave; ++k) t = Op<OP>::join(t, lds[k]);
+        for (int k = 1; k < kBlock / kWave; ++k) t = T::join(t, lds[k]);
     }
     return t;
 }
@@ -186,12 +430,14 @@ __device__ __forceinline__ float block_reduce(float v, float* lds) {
 // second pass and by the last workgroup of a fused first pass, so both give
 // the same bits.  Every thread of the workgroup must call it.
 template <int OP>
-__device__ __forceinline__ void combine_row(const float* __restrict__ part, int64_t P,
-                                            float* __restrict__ out_o, float* lds) {
-    float t = Op<OP>::start();
-    for (int64_t k = threadIdx.x; k < P; k += kBlock) t = Op<OP>::join(t, part[k]);
+__device__ __forceinline__ void combine_row(typename St<OP>::Out part, int64_t P,
+                                            typename St<OP>::Out out_o,
+                                            typename St<OP>::S1* lds) {
+    typedef St<OP> T;
+    typename T::S1 t = T::start1();
+    for (int64_t k = threadIdx.x; k < P; k += kBlock) t = T::join(t, T::get(part, k));
     t = block_reduce<OP>(t, lds);
-    if (threadIdx.x == 0) *out_o = t;
+    if (threadIdx.x == 0) T::put(out_o, 0, t);
     __syncthreads();
 }
 
@@ -218,13 +464,14 @@ template <int OP, int G, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ x,
                                                       int64_t R, int64_t nseg,
                                                       int64_t P, int32_t blocked,
-                                                      float* __restrict__ dst,
+                                                      typename St<OP>::Out dst,
                                                       uint32_t nxcd,
                                                       uint32_t* __restrict__ ticket,
-                                                      float* __restrict__ out) {
+                                                      typename St<OP>::Out out) {
     static_assert(G == kWave || G == kBlock, "group is a wave or a workgroup");
+    typedef St<OP> T;
     constexpr int kGroups = kBlock / G;
-    __shared__ float lds[kBlock / kWave];
+    __shared__ typename T::S1 lds[kBlock / kWave];
     const int gl = threadIdx.x % G;
     const int64_t nvec = R >> 2;
     const int64_t tail = R & 3;
@@ -233,7 +480,7 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
     const int64_t gstride = int64_t(gridDim.x) * kGroups;
     for (int64_t first = xcd_block(nxcd) * kGroups; first < nseg; first += gstride) {
         const int64_t seg = first + threadIdx.x / G;  // uniform per group
-        float total = Op<OP>::start();
+        typename T::S1 total = T::start1();
         if (seg < nseg) {
             const int64_t o = seg / P;
             const int64_t piece = seg - o * P;
@@ -242,28 +489,27 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
             int64_t j = blocked ? piece * span + gl : g;
             int64_t end = nvec;
             if (blocked && piece * span + span < nvec) end = piece * span + span;
-            v4f acc[2] = {start4<OP>(), start4<OP>()};
+            typename T::S4 acc[2] = {T::start4(), T::start4()};
             for (; j + (U - 1) * L < end; j += U * L) {
                 v4f v[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) v[u] = load4<NT>(row + 4 * (j + u * L));
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc[u & 1] = Op<OP>::fold(acc[u & 1], v[u]);
+                T::template fold_all<U>(acc, v);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (j + u * L < end)
-                    acc[u & 1] = Op<OP>::fold(acc[u & 1], load4<NT>(row + 4 * (j + u * L)));
-            if (g < tail) acc[0].x = Op<OP>::fold(acc[0].x, row[4 * nvec + g]);
-            total = join_lanes<OP>(Op<OP>::join(acc[0], acc[1]));
+                    acc[u & 1] = T::fold(acc[u & 1], load4<NT>(row + 4 * (j + u * L)));
+            if (g < tail) acc[0] = T::fold_x(acc[0], row[4 * nvec + g]);
+            total = join_lanes<OP>(T::join(acc[0], acc[1]));
         }
         if constexpr (G == kBlock) {
             total = block_reduce<OP>(total, lds);
-            if (threadIdx.x == 0) dst[seg] = total;
+            if (threadIdx.x == 0) T::put(dst, seg, total);
             __syncthreads();
         } else {
             total = wave_reduce<OP>(total);
-            if (gl == 0 && seg < nseg) dst[seg] = total;
+            if (gl == 0 && seg < nseg) T::put(dst, seg, total);
         }
     }
     if (ticket != nullptr) {
@@ -280,7 +526,7 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             const int64_t outer = nseg / P;
             for (int64_t o = 0; o < outer; ++o)
-                combine_row<OP>(dst + o * P, P, out + o, lds);
+                combine_row<OP>(T::at(dst, o * P), P, T::at(out, o), lds);
             if (threadIdx.x == 0)
                 __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -292,27 +538,29 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
 template <int OP>
 __global__ __launch_bounds__(kBlock) void rows_short_kernel(const float* __restrict__ x,
                                                             int64_t outer, int64_t R,
-                                                            float* __restrict__ out) {
+                                                            typename St<OP>::Out out) {
+    typedef St<OP> T;
     const int64_t stride = int64_t(gridDim.x) * kBlock;
     for (int64_t o = int64_t(blockIdx.x) * kBlock + threadIdx.x; o < outer; o += stride) {
         const float* row = x + o * R;
-        v4f acc = start4<OP>();
+        typename T::S4 acc = T::start4();
         int64_t k = 0;
-        for (; k + 4 <= R; k += 4) acc = Op<OP>::fold(acc, load4<false>(row + k));
-        float t = join_lanes<OP>(acc);
-        for (; k < R; ++k) t = Op<OP>::fold(t, row[k]);
-        out[o] = t;
+        for (; k + 4 <= R; k += 4) acc = T::fold(acc, load4<false>(row + k));
+        typename T::S1 t = join_lanes<OP>(acc);
+        for (; k < R; ++k) t = T::fold(t, row[k]);
+        T::put(out, o, t);
     }
 }
 
 // Second pass of ROWS: out[o] = combine_row over the P piece results of row o.
 template <int OP>
-__global__ __launch_bounds__(kBlock) void rows_combine_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(kBlock) void rows_combine_kernel(typename St<OP>::Out part,
                                                               int64_t outer, int64_t P,
-                                                              float* __restrict__ out) {
-    __shared__ float lds[kBlock / kWave];
+                                                              typename St<OP>::Out out) {
+    typedef St<OP> T;
+    __shared__ typename T::S1 lds[kBlock / kWave];
     for (int64_t o = blockIdx.x; o < outer; o += gridDim.x)
-        combine_row<OP>(part + o * P, P, out + o, lds);
+        combine_row<OP>(T::at(part, o * P), P, T::at(out, o), lds);
 }
 
 // ----------------------------------------------------------------- COLS
@@ -328,8 +576,9 @@ __global__ __launch_bounds__(kBlock) void rows_combine_kernel(const float* __res
 template <int OP, int CW, int RW, int U, bool NT>
 __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
     const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t ntiles,
-    int64_t S, int64_t rps, float* __restrict__ dst, uint32_t nxcd) {
-    __shared__ v4f lds[RW > 1 ? (RW - 1) * CW * kWave : 1];
+    int64_t S, int64_t rps, typename St<OP>::Out dst, uint32_t nxcd) {
+    typedef St<OP> T;
+    __shared__ typename T::S4 lds[RW > 1 ? (RW - 1) * CW * kWave : 1];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int cw = wave % CW;
@@ -346,7 +595,7 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
         const int64_t r0 = s * rps + rw;
         const int64_t r1 = (s + 1) * rps < R ? (s + 1) * rps : R;
         const int64_t m = r0 < r1 ? (r1 - r0 + RW - 1) / RW : 0;
-        v4f acc[2] = {start4<OP>(), start4<OP>()};
+        typename T::S4 acc[2] = {T::start4(), T::start4()};
         if (active) {
             const float* p = x + (o * R + r0) * inner + cl;
             const int64_t step = RW * inner;
@@ -355,29 +604,28 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
                 v4f v[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) v[u] = load4<NT>(p + u * step);
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc[u & 1] = Op<OP>::fold(acc[u & 1], v[u]);
+                T::template fold_all<U>(acc, v);
                 p += U * step;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (k + u < m) acc[u & 1] = Op<OP>::fold(acc[u & 1], load4<NT>(p + u * step));
+                if (k + u < m) acc[u & 1] = T::fold(acc[u & 1], load4<NT>(p + u * step));
         }
-        v4f a = Op<OP>::join(acc[0], acc[1]);
+        typename T::S4 a = T::join(acc[0], acc[1]);
         if constexpr (RW > 1) {
             if (rw > 0) lds[((rw - 1) * CW + cw) * kWave + lane] = a;
             __syncthreads();
             if (rw == 0) {
 #pragma unroll
                 for (int q = 1; q < RW; ++q)
-                    a = Op<OP>::join(a, lds[((q - 1) * CW + cw) * kWave + lane]);
+                    a = T::join(a, lds[((q - 1) * CW + cw) * kWave + lane]);
             }
             __syncthreads();
         }
         if (rw == 0 && active) {
-            float* d = dst + (s * outer + o) * inner + cl;
+            const int64_t e = (s * outer + o) * inner + cl;
             const int keep = int(c - cl);  // 0, or 1..3 for the row's last lane
-            for (int q = keep; q < 4; ++q) d[q] = a[q];
+            for (int q = keep; q < 4; ++q) T::put(dst, e + q, T::lane(a, q));
         }
     }
 }
@@ -400,7 +648,8 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
 template <int OP, int V, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void cols_small_kernel(
     const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t S,
-    int64_t rps, int32_t LC, float* __restrict__ dst, uint32_t nxcd) {
+    int64_t rps, int32_t LC, typename St<OP>::Out dst, uint32_t nxcd) {
+    typedef St<OP> T;
     constexpr int kWaves = kBlock / kWave;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
@@ -419,45 +668,42 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
         const int64_t r0 = s * rps + rho;
         const int64_t r1 = (s + 1) * rps < R ? (s + 1) * rps : R;
         const int64_t m = r0 < r1 ? (r1 - r0 + RPW - 1) / RPW : 0;
-        v4f acc[2] = {start4<OP>(), start4<OP>()};
+        typename T::S4 acc[2] = {T::start4(), T::start4()};
         if (active) {
             const float* p = x + (o * R + r0) * inner + cl;
             const int64_t step = int64_t(RPW) * inner;
-            const float fill = Op<OP>::start();
+            const float fill = T::fill();
             int64_t k = 0;
             for (; k + U <= m; k += U) {
                 v4f v[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) v[u] = loadv<V, NT>(p + u * step, fill);
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc[u & 1] = Op<OP>::fold(acc[u & 1], v[u]);
+                T::template fold_all<U>(acc, v);
                 p += U * step;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (k + u < m)
-                    acc[u & 1] = Op<OP>::fold(acc[u & 1], loadv<V, NT>(p + u * step, fill));
+                    acc[u & 1] = T::fold(acc[u & 1], loadv<V, NT>(p + u * step, fill));
         }
         // join the row phases of each lane-column by a fixed tree
-        v4f a = Op<OP>::join(acc[0], acc[1]);
+        typename T::S4 a = T::join(acc[0], acc[1]);
         if (LC == 1) {
 #pragma unroll
-            for (int j = 0; j < V; ++j) a[j] = wave_reduce<OP>(a[j]);
+            for (int j = 0; j < V; ++j) T::set_lane(a, j, wave_reduce<OP>(T::lane(a, j)));
         } else {
             for (int d = 1; d < RPW; d *= 2) {
                 const int src = lane + d * LC < kWave ? lane + d * LC : lane;
-                v4f t;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) t[j] = lane_value(src, a[j]);
-                if ((rho & (2 * d - 1)) == 0 && rho + d < RPW) a = Op<OP>::join(a, t);
+                const typename T::S4 t = lane_value(src, a);
+                if ((rho & (2 * d - 1)) == 0 && rho + d < RPW) a = T::join(a, t);
             }
         }
         if (rho == 0) {
-            float* d = dst + (s * outer + o) * inner + cl;
+            const int64_t e = (s * outer + o) * inner + cl;
             if constexpr (V == 4) {
-                for (int q = keep; q < 4; ++q) d[q] = a[q];
+                for (int q = keep; q < 4; ++q) T::put(dst, e + q, T::lane(a, q));
             } else {
-                for (int q = 0; q < V; ++q) d[q] = a[q];
+                for (int q = 0; q < V; ++q) T::put(dst, e + q, T::lane(a, q));
             }
         }
     }
@@ -465,24 +711,26 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
 
 // Second pass of a split along R: out[e] = join of slab[0][e], slab[1][e], ...
 template <int OP>
-__global__ __launch_bounds__(kBlock) void slab_combine_kernel(const float* __restrict__ slab,
+__global__ __launch_bounds__(kBlock) void slab_combine_kernel(typename St<OP>::Out slab,
                                                               int64_t S, int64_t n,
-                                                              float* __restrict__ out) {
+                                                              typename St<OP>::Out out) {
+    typedef St<OP> T;
     const int64_t stride = int64_t(gridDim.x) * kBlock;
     for (int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x; e < n; e += stride) {
-        float t = slab[e];
-        for (int64_t s = 1; s < S; ++s) t = Op<OP>::join(t, slab[s * n + e]);
-        out[e] = t;
+        typename T::S1 t = T::get(slab, e);
+        for (int64_t s = 1; s < S; ++s) t = T::join(t, T::get(slab, s * n + e));
+        T::put(out, e, t);
     }
 }
 
 // R == 0: every output is the operator's start value.
 template <int OP>
-__global__ __launch_bounds__(kBlock) void fill_start_kernel(float* __restrict__ out,
+__global__ __launch_bounds__(kBlock) void fill_start_kernel(typename St<OP>::Out out,
                                                             int64_t n) {
+    typedef St<OP> T;
     const int64_t stride = int64_t(gridDim.x) * kBlock;
     for (int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x; e < n; e += stride)
-        out[e] = Op<OP>::start();
+        T::put(out, e, T::start1());
 }
 
 // ------------------------------------------------------------- launching
@@ -526,27 +774,35 @@ constexpr bool col_shape_built(int cw, int rw) {
 
 constexpr bool cols_built(int op, int cw, int rw, int u) {
     if (op == RD_OP_SUM) return col_shape_built(cw, rw) && unroll_built(u);
+    if (op == RD_OP_SOFTMAX_DENOM)
+        return rw == 1 && (cw == 1 || cw == 2 || cw == 4 || cw == 8) && (u == 4 || u == 8);
     return rw == 1 && (cw == 1 || cw == 2 || cw == 4 || cw == 8) && u == 4;
 }
 
 constexpr bool op_valid(int op) {
-    return op == RD_OP_SUM || op == RD_OP_SUMSQ || op == RD_OP_MAX || op == RD_OP_MIN;
+    return op == RD_OP_SUM || op == RD_OP_SUMSQ || op == RD_OP_MAX || op == RD_OP_MIN ||
+           op == RD_OP_SOFTMAX_DENOM;
+}
+
+template <int OP>
+typename St<OP>::Out out_of(Results r) {
+    return St<OP>::make_out(r.a, r.b);
 }
 
 struct RowsArgs {
     const float* x;
     int64_t outer, R;
-    float* dst;
+    Results dst;
     uint32_t* ticket;
-    float* out;
+    Results out;
 };
 
 template <int OP, int G, int U, bool NT>
 hipError_t rows_go(const rd_plan& p, const RowsArgs& a, hipStream_t s) {
     if constexpr (rows_built(OP, G, U)) {
         return launch(rows_kernel<OP, G, U, NT>, p.blocks, kBlock, s, a.x, a.R,
-                      a.outer * p.split, p.split, int32_t(p.order == RD_ORDER_BLOCKED), a.dst,
-                      uint32_t(p.nxcd), a.ticket, a.out);
+                      a.outer * p.split, p.split, int32_t(p.order == RD_ORDER_BLOCKED),
+                      out_of<OP>(a.dst), uint32_t(p.nxcd), a.ticket, out_of<OP>(a.out));
     } else {
         return hipErrorInvalidValue;
     }
@@ -577,7 +833,7 @@ hipError_t rows_op(const rd_plan& p, const RowsArgs& a, hipStream_t s) {
 struct ColsArgs {
     const float* x;
     int64_t outer, R, inner;
-    float* dst;
+    Results dst;
 };
 
 template <int OP, int CW, int RW, int U, bool NT>
@@ -585,8 +841,8 @@ hipError_t cols_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
     if constexpr (cols_built(OP, CW, RW, U)) {
         const int64_t ntiles = ((a.inner + 3) / 4 + CW * kWave - 1) / (CW * kWave);
         return launch(cols_kernel<OP, CW, RW, U, NT>, p.blocks, kWave * CW * RW, s, a.x,
-                      a.outer, a.R, a.inner, ntiles, p.split, p.rows_per_split, a.dst,
-                      uint32_t(p.nxcd));
+                      a.outer, a.R, a.inner, ntiles, p.split, p.rows_per_split,
+                      out_of<OP>(a.dst), uint32_t(p.nxcd));
     } else {
         return hipErrorInvalidValue;
     }
@@ -639,25 +895,29 @@ hipError_t cols_op(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
         case RD_OP_SUMSQ: return F<RD_OP_SUMSQ>(__VA_ARGS__); \
         case RD_OP_MAX: return F<RD_OP_MAX>(__VA_ARGS__);     \
         case RD_OP_MIN: return F<RD_OP_MIN>(__VA_ARGS__);     \
+        case RD_OP_SOFTMAX_DENOM:                             \
+            return F<RD_OP_SOFTMAX_DENOM>(__VA_ARGS__);       \
         default: return hipErrorInvalidValue;                 \
     }
 
 template <int OP>
-hipError_t fill_go(float* out, int64_t n, hipStream_t s) {
-    return launch(fill_start_kernel<OP>, grid_for(n), kBlock, s, out, n);
+hipError_t fill_go(Results out, int64_t n, hipStream_t s) {
+    return launch(fill_start_kernel<OP>, grid_for(n), kBlock, s, out_of<OP>(out), n);
 }
 
 template <int OP>
-hipError_t rows_short_go(const float* x, int64_t outer, int64_t R, float* out,
+hipError_t rows_short_go(const float* x, int64_t outer, int64_t R, Results out,
                          hipStream_t s) {
-    return launch(rows_short_kernel<OP>, grid_for(outer), kBlock, s, x, outer, R, out);
+    return launch(rows_short_kernel<OP>, grid_for(outer), kBlock, s, x, outer, R,
+                  out_of<OP>(out));
 }
 
 template <int OP>
-hipError_t rows_combine_go(const float* part, int64_t outer, int64_t P, float* out,
+hipError_t rows_combine_go(Results part, int64_t outer, int64_t P, Results out,
                            hipStream_t s) {
     const int64_t blocks = outer < kMaxBlocks ? outer : kMaxBlocks;
-    return launch(rows_combine_kernel<OP>, blocks, kBlock, s, part, outer, P, out);
+    return launch(rows_combine_kernel<OP>, blocks, kBlock, s, out_of<OP>(part), outer, P,
+                  out_of<OP>(out));
 }
 
 constexpr bool small_built(int op, int v, int u) {
@@ -670,7 +930,8 @@ hipError_t small_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
     if constexpr (small_built(OP, V, U)) {
         const int32_t lc = int32_t((a.inner + 3) / 4);
         return launch(cols_small_kernel<OP, V, U, NT>, p.blocks, kBlock, s, a.x, a.outer, a.R,
-                      a.inner, p.split, p.rows_per_split, lc, a.dst, uint32_t(p.nxcd));
+                      a.inner, p.split, p.rows_per_split, lc, out_of<OP>(a.dst),
+                      uint32_t(p.nxcd));
     } else {
         return hipErrorInvalidValue;
     }
@@ -699,9 +960,9 @@ hipError_t cols_small_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
 }
 
 template <int OP>
-hipError_t slab_combine_go(const float* slab, int64_t S, int64_t n, float* out,
-                           hipStream_t s) {
-    return launch(slab_combine_kernel<OP>, grid_for(n), kBlock, s, slab, S, n, out);
+hipError_t slab_combine_go(Results slab, int64_t S, int64_t n, Results out, hipStream_t s) {
+    return launch(slab_combine_kernel<OP>, grid_for(n), kBlock, s, out_of<OP>(slab), S, n,
+                  out_of<OP>(out));
 }
 
 }  // namespace
@@ -718,39 +979,39 @@ bool small_shape_supported(int op, int unroll) {
     return op_valid(op) && small_built(op, 4, unroll);
 }
 
-hipError_t launch_fill_start(int op, float* out, int64_t n, hipStream_t s) {
+hipError_t launch_fill_start(int op, Results out, int64_t n, hipStream_t s) {
     RD_BY_OP(op, fill_go, out, n, s)
 }
 
 hipError_t launch_rows(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       float* dst, uint32_t* ticket, float* out, hipStream_t s) {
+                       Results dst, uint32_t* ticket, Results out, hipStream_t s) {
     const RowsArgs a{x, outer, R, dst, ticket, out};
     RD_BY_OP(op, rows_op, p, a, s)
 }
 
-hipError_t launch_rows_short(int op, const float* x, int64_t outer, int64_t R, float* out,
+hipError_t launch_rows_short(int op, const float* x, int64_t outer, int64_t R, Results out,
                              hipStream_t s) {
     RD_BY_OP(op, rows_short_go, x, outer, R, out, s)
 }
 
-hipError_t launch_rows_combine(int op, const float* part, int64_t outer, int64_t P,
-                               float* out, hipStream_t s) {
+hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, Results out,
+                               hipStream_t s) {
     RD_BY_OP(op, rows_combine_go, part, outer, P, out, s)
 }
 
 hipError_t launch_cols(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       int64_t inner, float* dst, hipStream_t s) {
+                       int64_t inner, Results dst, hipStream_t s) {
     const ColsArgs a{x, outer, R, inner, dst};
     RD_BY_OP(op, cols_op, p, a, s)
 }
 
 hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, int64_t outer,
-                             int64_t R, int64_t inner, float* dst, hipStream_t s) {
+                             int64_t R, int64_t inner, Results dst, hipStream_t s) {
     const ColsArgs a{x, outer, R, inner, dst};
     RD_BY_OP(op, cols_small_go, p, a, s)
 }
 
-hipError_t launch_slab_combine(int op, const float* slab, int64_t S, int64_t n, float* out,
+hipError_t launch_slab_combine(int op, Results slab, int64_t S, int64_t n, Results out,
                                hipStream_t s) {
     RD_BY_OP(op, slab_combine_go, slab, S, n, out, s)
 }

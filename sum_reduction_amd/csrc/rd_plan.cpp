@@ -42,6 +42,11 @@ bool nontemporal_choice(const rd_tune* t, bool dflt, int32_t* out) {
     return true;
 }
 
+// Bytes of one partial result: a float, or the softmax denominator's pair.
+int64_t result_bytes(int op) {
+    return int64_t(sizeof(float)) * (op == RD_OP_SOFTMAX_DENOM ? 2 : 1);
+}
+
 int32_t nxcd_for(int cu_count) {
     // MI355X: 8 XCDs of 32 CUs.  Only used to spread the workgroup numbering,
     // so a wrong guess costs locality, never correctness.
@@ -93,12 +98,12 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
         if (cap < 1) cap = 1;
         if (P > cap) P = cap;
     }
-    if (P > INT64_MAX / 4 / outer) return RD_ERR_INVALID_ARG;
+    if (P > INT64_MAX / result_bytes(op) / outer) return RD_ERR_INVALID_ARG;
     p->split = P;
     const int64_t segs = outer * P;
     p->blocks = ceil_div(segs, groups_per_block);
     if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
-    p->workspace_bytes = P > 1 ? segs * int64_t(sizeof(float)) : 0;
+    p->workspace_bytes = P > 1 ? segs * result_bytes(op) : 0;
     p->combine = RD_COMBINE_NONE;
     if (P > 1) {
         // The second kernel is the default: measured on MI355X it is faster
@@ -155,13 +160,12 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
         }
         if (S < 1) return RD_ERR_INVALID_ARG;
         split_rows(R, S, p);
-        if (p->split > INT64_MAX / 4 / (outer * inner)) return RD_ERR_INVALID_ARG;
+        if (p->split > INT64_MAX / result_bytes(op) / (outer * inner)) return RD_ERR_INVALID_ARG;
         p->blocks = ceil_div(p->split * outer, waves_per_block);
         if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
         p->passes = p->split > 1 ? 2 : 1;
         p->combine = p->split > 1 ? RD_COMBINE_PASS : RD_COMBINE_NONE;
-        p->workspace_bytes =
-            p->split > 1 ? p->split * outer * inner * int64_t(sizeof(float)) : 0;
+        p->workspace_bytes = p->split > 1 ? p->split * outer * inner * result_bytes(op) : 0;
         return RD_OK;
     }
     p->path = RD_PATH_COLS;
@@ -204,13 +208,12 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
     }
     if (S < 1) return RD_ERR_INVALID_ARG;
     split_rows(R, S, p);
-    if (p->split > INT64_MAX / 4 / (outer * inner)) return RD_ERR_INVALID_ARG;
+    if (p->split > INT64_MAX / result_bytes(op) / (outer * inner)) return RD_ERR_INVALID_ARG;
     p->blocks = base * p->split;
     if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
     p->passes = p->split > 1 ? 2 : 1;
     p->combine = p->split > 1 ? RD_COMBINE_PASS : RD_COMBINE_NONE;
-    p->workspace_bytes =
-        p->split > 1 ? p->split * outer * inner * int64_t(sizeof(float)) : 0;
+    p->workspace_bytes = p->split > 1 ? p->split * outer * inner * result_bytes(op) : 0;
     return RD_OK;
 }
 
@@ -220,7 +223,7 @@ rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op
                    const rd_tune* tune, rd_plan* plan) {
     if (!plan || cu_count < 1 || outer < 0 || R < 0 || inner < 0)
         return RD_ERR_INVALID_ARG;
-    if (op < RD_OP_SUM || op > RD_OP_MIN) return RD_ERR_INVALID_ARG;
+    if (op < RD_OP_SUM || op > RD_OP_SOFTMAX_DENOM) return RD_ERR_INVALID_ARG;
     memset(plan, 0, sizeof(*plan));
     // outer * R * inner * 4 must be representable
     const int64_t lim = INT64_MAX / 4;

@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     for want in ("rd_sum_1d", "rd_sum_dim", "rd_reduce_1d", "rd_reduce_dim",
                  "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
                  "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "rd_cumsum_dim",
-                 "rd_plan_cumsum"):
+                 "rd_plan_cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim"):
         assert want in names
 
 
@@ -114,7 +114,7 @@ def test_dim_invalid_arguments(lib, host_buf):
 def test_reduce_rejects_unknown_operator(lib, host_buf):
     base, _ = host_buf
     out = base + 4 * 40
-    for op in (-1, 4, 99):
+    for op in (-1, 4, 5, 99):   # 4, the softmax denominator, has two outputs
         assert lib.rd_reduce_1d(base, 4, op, out, None) == INVALID
         assert lib.rd_reduce_dim(base, 2, 2, 2, op, out, None) == INVALID
     # and the other argument checks hold for every operator
@@ -145,6 +145,39 @@ def test_cumsum_invalid_arguments(lib, host_buf):
     assert lib.rd_cumsum_dim(None, 4, 5, 0, 0, None, None) == OK
 
 
+def test_softmax_denom_invalid_arguments(lib, host_buf):
+    base, _ = host_buf
+    m, s = base + 4 * 32, base + 4 * 48
+    cases = [
+        (base, -1, 2, 2, m, s), (base, 2, -1, 2, m, s), (base, 2, 2, -1, m, s),
+        (base, 2 ** 40, 2 ** 39, 2, m, s),  # size * 8 overflows
+        (base, 2, 2, 2, None, s),           # null maxima
+        (base, 2, 2, 2, m, None),           # null sums
+        (None, 2, 2, 2, m, s),              # null x, inputs exist
+        (base + 1, 2, 2, 2, m, s),          # misaligned x
+        (base, 2, 2, 2, m + 2, s),          # misaligned maxima
+        (base, 2, 2, 2, m, s + 1),          # misaligned sums
+        (base, 2, 3, 4, base + 4 * 20, s),  # maxima overlap x (24 floats)
+        (base, 2, 3, 4, m, base),           # sums overlap x
+        (base, 2, 3, 4, m, m + 4 * 7),      # sums overlap maxima (8 floats each)
+        (base, 2, 3, 4, m, m),              # the same array for both
+    ]
+    for x, o_, R, i, mm, ss in cases:
+        assert lib.rd_softmax_denom_dim(x, o_, R, i, mm, ss, None) == INVALID, (o_, R, i)
+    for x, n, mm, ss in ((base, -1, m, s), (base, 2 ** 61, m, s), (base, 4, None, s),
+                         (base, 4, m, None), (None, 4, m, s), (base, 4, base, s),
+                         (base, 4, m, m), (base + 2, 4, m, s)):
+        assert lib.rd_softmax_denom_1d(x, n, mm, ss, None) == INVALID, (n,)
+    assert lib.rd_softmax_denom_dim(None, 0, 5, 3, None, None, None) == OK
+    assert lib.rd_softmax_denom_dim(None, 4, 5, 0, None, None, None) == OK
+    # its kernel shapes are those of the maximum
+    for g, u in ((256, 16), (256, 8), (64, 8), (64, 16)):
+        assert rd.rd_tune_supported("rows", g, 1, u, "softmax_denom")
+    assert not rd.rd_tune_supported("rows", 256, 1, 4, "softmax_denom")
+    assert rd.rd_tune_supported("cols", 8, 1, 4, "softmax_denom")
+    assert not rd.rd_tune_supported("cols", 8, 2, 4, "softmax_denom")
+
+
 def test_empty_output_needs_nothing(lib):
     # outer * inner == 0: nothing to write, RD_OK without a device, null ok
     assert lib.rd_sum_dim(None, 0, 5, 3, None, None) == OK
@@ -167,6 +200,9 @@ def test_no_device_is_reported(lib, host_buf):
     assert lib.rd_sum_1d(None, 0, base + 4 * 32, None) == NO_DEVICE
     assert lib.rd_cumsum_dim(base, 2, 2, 2, 1, base + 4 * 32, None) == NO_DEVICE
     assert lib.rd_cumsum_dim(base, 2, 2, 2, 1, base, None) == NO_DEVICE   # in place is valid
+    assert lib.rd_softmax_denom_dim(base, 2, 2, 2, base + 4 * 32, base + 4 * 40,
+                                    None) == NO_DEVICE
+    assert lib.rd_softmax_denom_1d(base, 8, base + 4 * 32, base + 4 * 40, None) == NO_DEVICE
 
 
 def test_python_wrapper_rejects_cpu_tensors():
@@ -177,6 +213,10 @@ def test_python_wrapper_rejects_cpu_tensors():
         rd.rd_sum_dim(torch.ones(4), 1, 4, 1)
     with pytest.raises(ValueError):
         rd.rd_cumsum_dim(torch.ones(4), 1, 4, 1)
+    with pytest.raises(ValueError):
+        rd.rd_softmax_denom_dim(torch.ones(4), 1, 4, 1)
+    with pytest.raises(ValueError):
+        rd.softmax_denom(torch.ones(4))
 
 
 def test_wrapper_raises_with_status():
