@@ -141,6 +141,33 @@ rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
                         int32_t op, float* out, hipStream_t stream);
 
 /*
+ * Strided views: the reductions of rd_reduce_dim over a view whose elements
+ * need not be contiguous -- element (o, r, i) of the [outer, R, inner] view
+ * is x[o * stride_outer + r * stride_r + i * stride_inner] (strides in
+ * floats, >= 0; 0 repeats an element), as torch lays out a transposed,
+ * sliced or expanded tensor.  out is contiguous: out[o * inner + i].
+ *   x      device pointer, 4-B aligned; the view's furthest element, and
+ *          outer*R*inner floats, must be representable in bytes
+ *   out    device pointer to outer*inner floats, 4-B aligned, outside the
+ *          view's span [x, x + furthest element] (may be NULL when
+ *          outer*inner == 0)
+ *   op     an rd_op other than RD_OP_SOFTMAX_DENOM
+ * The kernel follows the unit stride: stride_inner == 1 reads columns with
+ * 16-byte loads as rd_reduce_dim does for inner > 1; stride_r == 1 reads each
+ * output's R terms as a row; a single kept axis of adjacent outputs
+ * (inner == 1, stride_outer == 1) is read as columns; any other layout takes
+ * one lane per output (correct, not fast).  A contiguous view
+ * (stride_outer = R*inner, stride_r = inner, stride_inner = 1) gives the bits
+ * rd_reduce_dim gives.  Status codes as for rd_reduce_dim.  Source: the
+ * POPCORNBENCH problem-47 trace reduces a torch tensor over one dimension
+ * (torch.sum(x, dim)), which accepts any strided tensor; the survey of the
+ * pages lists strided views beside small inner sizes.
+ */
+rd_status rd_reduce_strided(const float* x, int64_t outer, int64_t R, int64_t inner,
+                            int64_t stride_outer, int64_t stride_r, int64_t stride_inner,
+                            int32_t op, float* out, hipStream_t stream);
+
+/*
  * Softmax denominator along the middle axis of a contiguous [outer, R, inner]
  * array ("Seven-step reduction: 30x from one kernel", opening section: the
  * softmax denominator is one of the reductions it lists with the sum and the
@@ -225,9 +252,12 @@ typedef enum rd_path {
     RD_PATH_SCAN_COLS = 7,   /* cumulative sum, inner > 128: a lane per 4
                                 columns, a workgroup of col_waves waves per
                                 tile group */
-    RD_PATH_SCAN_COLS_SMALL = 8  /* cumulative sum, 2 <= inner <= 128: several
+    RD_PATH_SCAN_COLS_SMALL = 8, /* cumulative sum, 2 <= inner <= 128: several
                                     rows per load instruction, scanned across
                                     the wave */
+    RD_PATH_STRIDED = 9      /* a strided view with no unit stride along the
+                                reduced or the inner axis: one lane per
+                                output */
 } rd_path;
 
 /* Chunk order of the pieces of one row on the ROWS path. */
@@ -280,6 +310,13 @@ rd_status rd_plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
 
 /* Plan of rd_sum_1d (the same as rd_plan_dim(cu_count, 1, n, 1, plan)). */
 rd_status rd_plan_1d(int cu_count, int64_t n, rd_plan* plan);
+
+/* The plan rd_reduce_strided executes for the view (after the view is
+ * normalised: strides of length-1 axes ignored, a single kept axis of
+ * adjacent outputs read as columns). */
+rd_status rd_plan_strided(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                          int64_t stride_outer, int64_t stride_r, int64_t stride_inner,
+                          rd_plan* plan);
 
 /* Plan of rd_cumsum_dim for that shape (the tuning override's split,
  * unroll -- SCAN_ROWS 4 or 8, SCAN_COLS 4, 8 or 16 --, col_waves -- SCAN_COLS

@@ -26,7 +26,7 @@ __all__ = [
     "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "sum", "tuning",
     "PATH_NAMES", "OPS", "rd_reduce_1d", "rd_reduce_dim", "reduce", "rd_cumsum_dim",
     "rd_plan_cumsum", "cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim",
-    "softmax_denom",
+    "softmax_denom", "rd_reduce_strided", "rd_plan_strided",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +39,8 @@ OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
 # entry points of its own; its code is accepted by rd_tune_supported
 OP_SOFTMAX_DENOM = 4
 PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
-              5: "cols_small", 6: "scan_rows", 7: "scan_cols", 8: "scan_cols_small"}
+              5: "cols_small", 6: "scan_rows", 7: "scan_cols", 8: "scan_cols_small",
+              9: "strided"}
 ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
 COMBINE_NAMES = {0: "none", 1: "pass", 2: "last_block"}
 
@@ -109,6 +110,11 @@ def load():
     lib.rd_softmax_denom_1d.restype = ctypes.c_int
     lib.rd_softmax_denom_dim.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     lib.rd_softmax_denom_dim.restype = ctypes.c_int
+    lib.rd_reduce_strided.argtypes = [vp, i64, i64, i64, i64, i64, i64, i32, vp, vp]
+    lib.rd_reduce_strided.restype = ctypes.c_int
+    lib.rd_plan_strided.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                    ctypes.POINTER(RdPlan)]
+    lib.rd_plan_strided.restype = ctypes.c_int
     lib.rd_cumsum_dim.argtypes = [vp, i64, i64, i64, i32, vp, vp]
     lib.rd_cumsum_dim.restype = ctypes.c_int
     lib.rd_plan_cumsum.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(RdPlan)]
@@ -159,6 +165,14 @@ def rd_plan_cumsum(cu_count: int, outer: int, R: int, inner: int) -> RdPlan:
     plan = RdPlan()
     _check(load().rd_plan_cumsum(cu_count, outer, R, inner, ctypes.byref(plan)),
            "rd_plan_cumsum")
+    return plan
+
+
+def rd_plan_strided(cu_count: int, outer: int, R: int, inner: int, stride_outer: int,
+                    stride_r: int, stride_inner: int) -> RdPlan:
+    plan = RdPlan()
+    _check(load().rd_plan_strided(cu_count, outer, R, inner, stride_outer, stride_r,
+                                  stride_inner, ctypes.byref(plan)), "rd_plan_strided")
     return plan
 
 
@@ -265,6 +279,54 @@ def rd_reduce_dim(x, outer: int, R: int, inner: int, op="sum", out=None, stream=
     return out
 
 
+def _check_view(x):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor, got device %s" % x.device)
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32, got %s" % x.dtype)
+
+
+def rd_reduce_strided(x, outer: int, R: int, inner: int, stride_outer: int, stride_r: int,
+                      stride_inner: int, op="sum", out=None, stream=None):
+    """out[o, i] = op over r of x's storage at o*stride_outer + r*stride_r +
+    i*stride_inner (floats from x.data_ptr()); ``out`` is [outer, inner].
+    The caller guarantees the view lies inside x's storage."""
+    _check_view(x)
+    out = _out_tensor(out, outer * inner, x.device, (outer, inner))
+    xp = x.data_ptr() if outer * R * inner else None
+    optr = out.data_ptr() if out.numel() else None
+    _check(load().rd_reduce_strided(xp, outer, R, inner, stride_outer, stride_r, stride_inner,
+                                    _op_code(op), optr, _stream_handle(stream)),
+           "rd_reduce_strided")
+    return out
+
+
+def _collapse(sizes, strides):
+    """(size, stride) of dims that form one strided axis, or None."""
+    n, st = 1, 0
+    dims = [(a, b) for a, b in zip(sizes, strides) if a != 1]
+    if not dims:
+        return 1, 0
+    for k, (a, b) in enumerate(dims):
+        if k and dims[k - 1][1] != b * a:
+            return None
+        n *= a
+    return n, dims[-1][1]
+
+
+def _view3(x, d):
+    """x viewed as [outer, R, inner] with strides, reducing dim d, or None."""
+    shape, strides = tuple(x.shape), tuple(x.stride())
+    before = _collapse(shape[:d], strides[:d])
+    after = _collapse(shape[d + 1:], strides[d + 1:])
+    if before is None or after is None:
+        return None
+    return before[0], shape[d], after[0], before[1], strides[d], after[1]
+
+
 def rd_sum_1d(x, out=None, stream=None):
     """Sum of all elements of the float32 GPU tensor ``x`` (rd_sum_1d)."""
     _check_input(x, x.numel() if hasattr(x, "numel") else -1)
@@ -288,13 +350,25 @@ def rd_sum_dim(x, outer: int, R: int, inner: int, out=None, stream=None):
 
 
 def reduce(x, op="sum", dim: Optional[int] = None, out=None, stream=None):
-    """torch-style reduction of a contiguous float32 GPU tensor over all
-    elements (dim=None, a 0-d result) or over one dimension, through
-    rd_reduce_1d / rd_reduce_dim.  op: "sum", "sumsq", "max" or "min"."""
+    """torch-style reduction of a float32 GPU tensor over all elements
+    (dim=None, a 0-d result; x contiguous) or over one dimension, through
+    rd_reduce_1d / rd_reduce_dim, or rd_reduce_strided for a transposed,
+    sliced or expanded view.  op: "sum", "sumsq", "max" or "min"."""
     if dim is None:
         return rd_reduce_1d(x, op, None if out is None else out.view(1), stream).view(())
     shape = tuple(x.shape)
     d = dim % len(shape)
+    if not x.is_contiguous():
+        # a strided view: reduced in place through rd_reduce_strided
+        v = _view3(x, d)
+        if v is None:
+            raise ValueError("this view of x cannot be read as one [outer, R, inner] "
+                             "strided array; make it contiguous first")
+        outer, R, inner = v[:3]
+        res = rd_reduce_strided(x, *v, op=op,
+                                out=None if out is None else out.view(outer, inner),
+                                stream=stream)
+        return res.view(shape[:d] + shape[d + 1:])
     outer = 1
     for s in shape[:d]:
         outer *= s
@@ -382,5 +456,5 @@ def cumsum(x, dim: int, reverse: bool = False, out=None, stream=None):
 
 
 def sum(x, dim: Optional[int] = None, out=None, stream=None):
-    """torch.sum(x) or torch.sum(x, dim) for a contiguous float32 GPU tensor."""
+    """torch.sum(x) (x contiguous) or torch.sum(x, dim) for a float32 GPU tensor."""
     return reduce(x, "sum", dim, out, stream)

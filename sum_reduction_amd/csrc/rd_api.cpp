@@ -133,12 +133,6 @@ rd_status current_device(Device** out) {
     return RD_OK;
 }
 
-rd_status make_plan(int cu, int64_t outer, int64_t R, int64_t inner, int op,
-                    rd_plan* plan) {
-    std::lock_guard<std::mutex> lock(g_tune_mu);
-    return rd::plan_dim(cu, outer, R, inner, op, g_tune_on ? &g_tune : nullptr, plan);
-}
-
 // Failure injection for tests of the error paths, read from the environment:
 // RD_TEST_FAIL_ALLOC makes the workspace allocation fail, RD_TEST_FAIL_LAUNCH
 // makes the first launch fail; neither enqueues any work.
@@ -147,8 +141,8 @@ bool inject(const char* name) {
     return v && v[0] && v[0] != '0';
 }
 
-rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, int64_t outer,
-                  int64_t R, int64_t inner, rd::Results out, hipStream_t s) {
+rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const rd::Strides& v,
+                  rd::Results out, hipStream_t s) {
     if (p.path == RD_PATH_NONE) return RD_OK;
     if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
@@ -162,35 +156,38 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, int64_t
     rd::Results part{ws, nullptr};
     if (ws && op == RD_OP_SOFTMAX_DENOM)
         part.b = ws + p.workspace_bytes / int64_t(2 * sizeof(float));
+    const int64_t nout = v.outer * v.inner;
     hipError_t e = hipSuccess;
     switch (p.path) {
         case RD_PATH_ZERO:
-            e = rd::launch_fill_start(op, out, outer * inner, s);
+            e = rd::launch_fill_start(op, out, nout, s);
             break;
         case RD_PATH_ROWS_SHORT:
-            e = rd::launch_rows_short(op, x, outer, R, out, s);
+            e = rd::launch_rows_short(op, x, v, out, s);
             break;
         case RD_PATH_ROWS:
             if (p.split == 1) {
-                e = rd::launch_rows(op, p, x, outer, R, out, nullptr, rd::Results{}, s);
+                e = rd::launch_rows(op, p, x, v, out, nullptr, rd::Results{}, s);
             } else {
                 uint32_t* ticket =
                     p.combine == RD_COMBINE_LAST_BLOCK ? stream_ticket(dev, s) : nullptr;
-                e = rd::launch_rows(op, p, x, outer, R, part, ticket, out, s);
+                e = rd::launch_rows(op, p, x, v, part, ticket, out, s);
                 if (e == hipSuccess && !ticket)
-                    e = rd::launch_rows_combine(op, part, outer, p.split, out, s);
+                    e = rd::launch_rows_combine(op, part, nout, p.split, out, s);
             }
             break;
         case RD_PATH_COLS:
         case RD_PATH_COLS_SMALL: {
             const rd::Results dst = p.split == 1 ? out : part;
-            e = p.path == RD_PATH_COLS
-                    ? rd::launch_cols(op, p, x, outer, R, inner, dst, s)
-                    : rd::launch_cols_small(op, p, x, outer, R, inner, dst, s);
+            e = p.path == RD_PATH_COLS ? rd::launch_cols(op, p, x, v, dst, s)
+                                       : rd::launch_cols_small(op, p, x, v, dst, s);
             if (e == hipSuccess && p.split > 1)
-                e = rd::launch_slab_combine(op, part, p.split, outer * inner, out, s);
+                e = rd::launch_slab_combine(op, part, p.split, nout, out, s);
             break;
         }
+        case RD_PATH_STRIDED:
+            e = rd::launch_strided(op, x, v, out, s);
+            break;
         default:
             e = hipErrorInvalidValue;
     }
@@ -202,15 +199,29 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, int64_t
     return RD_OK;
 }
 
-rd_status reduce_checked(const float* x, int64_t outer, int64_t R, int64_t inner, int op,
-                         rd::Results out, hipStream_t stream) {
+// Plans and runs a reduction of the view v (sizes already validated).
+rd_status reduce_checked(const float* x, rd::Strides v, int op, rd::Results out,
+                         hipStream_t stream) {
     Device* dev = nullptr;
     rd_status st = current_device(&dev);
     if (st != RD_OK) return st;
     rd_plan plan;
-    st = make_plan(dev->cu, outer, R, inner, op, &plan);
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        st = rd::plan_view(dev->cu, &v, op, g_tune_on ? &g_tune : nullptr, &plan);
+    }
     if (st != RD_OK) return st;
-    return execute(plan, op, *dev, x, outer, R, inner, out, stream);
+    return execute(plan, op, *dev, x, v, out, stream);
+}
+
+rd::Strides contiguous(int64_t outer, int64_t R, int64_t inner) {
+    return rd::Strides{outer, R, inner, R * inner, inner, 1};
+}
+
+// Floats from x to one past the furthest element of the view (0 if empty).
+int64_t view_extent(const rd::Strides& v) {
+    if (v.outer == 0 || v.R == 0 || v.inner == 0) return 0;
+    return (v.outer - 1) * v.so + (v.R - 1) * v.sr + (v.inner - 1) * v.si + 1;
 }
 
 bool op_valid(int32_t op) { return op >= RD_OP_SUM && op <= RD_OP_MIN; }
@@ -225,7 +236,7 @@ rd_status rd_reduce_1d(const float* x, int64_t n, int32_t op, float* out,
     if (n < 0 || n > INT64_MAX / 4 || !out || !aligned4(out)) return RD_ERR_INVALID_ARG;
     if (n > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
     if (overlap(x, n, out, 1)) return RD_ERR_INVALID_ARG;
-    return reduce_checked(x, 1, n, 1, op, rd::Results{out, nullptr}, stream);
+    return reduce_checked(x, contiguous(1, n, 1), op, rd::Results{out, nullptr}, stream);
 }
 
 rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner, int32_t op,
@@ -241,7 +252,31 @@ rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
     if (!out || !aligned4(out)) return RD_ERR_INVALID_ARG;
     if (nin > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
     if (overlap(x, nin, out, nout)) return RD_ERR_INVALID_ARG;
-    return reduce_checked(x, outer, R, inner, op, rd::Results{out, nullptr}, stream);
+    return reduce_checked(x, contiguous(outer, R, inner), op, rd::Results{out, nullptr},
+                          stream);
+}
+
+rd_status rd_reduce_strided(const float* x, int64_t outer, int64_t R, int64_t inner,
+                            int64_t stride_outer, int64_t stride_r, int64_t stride_inner,
+                            int32_t op, float* out, hipStream_t stream) {
+    if (!op_valid(op)) return RD_ERR_INVALID_ARG;
+    const rd::Strides v{outer, R, inner, stride_outer, stride_r, stride_inner};
+    if (!rd::view_sizes_ok(v)) return RD_ERR_INVALID_ARG;
+    const int64_t nout = outer * inner;
+    if (nout == 0) return RD_OK;  // nothing to write, no HIP call
+    const int64_t span = view_extent(v);
+    if (!out || !aligned4(out)) return RD_ERR_INVALID_ARG;
+    if (span > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
+    if (overlap(x, span, out, nout)) return RD_ERR_INVALID_ARG;
+    return reduce_checked(x, v, op, rd::Results{out, nullptr}, stream);
+}
+
+rd_status rd_plan_strided(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                          int64_t stride_outer, int64_t stride_r, int64_t stride_inner,
+                          rd_plan* plan) {
+    rd::Strides v{outer, R, inner, stride_outer, stride_r, stride_inner};
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return rd::plan_view(cu_count, &v, RD_OP_SUM, g_tune_on ? &g_tune : nullptr, plan);
 }
 
 rd_status rd_softmax_denom_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
@@ -259,7 +294,7 @@ rd_status rd_softmax_denom_dim(const float* x, int64_t outer, int64_t R, int64_t
     if (overlap(x, nin, out_max, nout) || overlap(x, nin, out_sum, nout) ||
         overlap(out_max, nout, out_sum, nout))
         return RD_ERR_INVALID_ARG;
-    return reduce_checked(x, outer, R, inner, RD_OP_SOFTMAX_DENOM,
+    return reduce_checked(x, contiguous(outer, R, inner), RD_OP_SOFTMAX_DENOM,
                           rd::Results{out_max, out_sum}, stream);
 }
 

@@ -22,10 +22,6 @@ constexpr int64_t kSmallInner = 128;
 // workgroups have up to 1024 threads).
 constexpr int64_t kMaxBlocks = int64_t(1) << 20;
 
-// Planner (rd_plan.cpp).  `tune` may be null; `op` is an rd_op (it only
-// decides which kernel shapes exist).
-rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op,
-                   const rd_tune* tune, rd_plan* plan);
 
 // Where a launch stores its results: `a` holds them (for the softmax
 // denominator, the maxima), `b` the softmax denominator's sums (null for the
@@ -35,21 +31,48 @@ struct Results {
     float* b;
 };
 
+// The [outer, R, inner] view a reduction reads: element (o, r, i) at
+// x[o*so + r*sr + i*si] (strides in floats).  A contiguous array has
+// so = R*inner, sr = inner, si = 1.  The planner picks the kernel from the
+// unit stride: si == 1 (columns contiguous) -> the column kernels;
+// sr == 1 -> the row kernels over outer*inner rows; neither -> the
+// lane-per-output kernel.
+struct Strides {
+    int64_t outer, R, inner, so, sr, si;
+};
+
+// Planner (rd_plan.cpp).  `tune` may be null; `op` is an rd_op (it only
+// decides which kernel shapes exist).  plan_view first normalises *v (the
+// strides of length-1 axes; a strided reduction with adjacent outputs becomes
+// a column reduction), and the launch must use the normalised view.
+rd_status plan_view(int cu_count, Strides* v, int op, const rd_tune* tune, rd_plan* plan);
+// Non-negative sizes and strides whose furthest element, and outer*R*inner
+// floats, are representable in bytes.
+bool view_sizes_ok(const Strides& v);
+// A contiguous [outer, R, inner] array.
+rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op,
+                   const rd_tune* tune, rd_plan* plan);
+
 // Kernel launchers (rd_kernels.hip).  Each enqueues on `s` and returns the
 // error hipLaunchKernel reports for the launch; `op` is an rd_op.
 hipError_t launch_fill_start(int op, Results out, int64_t n, hipStream_t s);
-// ticket == nullptr: dst receives the piece results (or the row results when
-// p.split == 1); otherwise the last workgroup also combines them into out.
-hipError_t launch_rows(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
+// Rows (v.sr == 1): v.outer * v.inner rows.  ticket == nullptr: dst
+// receives the piece results (or the row results when p.split == 1);
+// otherwise the last workgroup also combines them into out.
+hipError_t launch_rows(int op, const rd_plan& p, const float* x, const Strides& v,
                        Results dst, uint32_t* ticket, Results out, hipStream_t s);
-hipError_t launch_rows_short(int op, const float* x, int64_t outer, int64_t R, Results out,
+hipError_t launch_rows_short(int op, const float* x, const Strides& v, Results out,
                              hipStream_t s);
 hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, Results out,
                                hipStream_t s);
-hipError_t launch_cols(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       int64_t inner, Results dst, hipStream_t s);
-hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, int64_t outer,
-                             int64_t R, int64_t inner, Results dst, hipStream_t s);
+// Columns (v.si == 1).
+hipError_t launch_cols(int op, const rd_plan& p, const float* x, const Strides& v,
+                       Results dst, hipStream_t s);
+hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, const Strides& v,
+                             Results dst, hipStream_t s);
+// Any strides: one lane per output.
+hipError_t launch_strided(int op, const float* x, const Strides& v, Results out,
+                          hipStream_t s);
 hipError_t launch_slab_combine(int op, Results slab, int64_t S, int64_t n, Results out,
                                hipStream_t s);
 

@@ -441,6 +441,20 @@ __device__ __forceinline__ void combine_row(typename St<OP>::Out part, int64_t P
     __syncthreads();
 }
 
+// Where the rows of the ROWS kernels start.  Row o (o < rows) is the pair
+// (o / ninner, o % ninner) of a view whose reduced axis is contiguous; it
+// starts at (o / ninner) * so + (o % ninner) * si floats from x.  A
+// contiguous [outer, R] array is ninner = 1, so = R.
+struct RowMap {
+    int64_t so, si, ninner;
+};
+
+__device__ __forceinline__ int64_t row_start(const RowMap& m, int64_t o) {
+    if (m.ninner == 1) return o * m.so;
+    const int64_t a = o / m.ninner;
+    return a * m.so + (o - a * m.ninner) * m.si;
+}
+
 // ----------------------------------------------------------------- ROWS
 // Each group of G lanes (one wave, or the whole workgroup) reduces one row
 // piece: segment seg = (row o, piece p), o = seg / P, p = seg % P.  With
@@ -460,9 +474,15 @@ __device__ __forceinline__ void combine_row(typename St<OP>::Out part, int64_t P
 // the counter to 0 for the next call on the same stream.  The counter must
 // be 0 at launch.  Only the ticket is atomic, and the combine order is the
 // second pass's.
+// At most 5 waves per SIMD: the U loads of a step are all issued before the
+// first fold waits (about 90 VGPRs at U = 16).  Left free to aim at 8 waves,
+// the compiler squeezed the kernel into 64 VGPRs by waiting after every
+// other load, and the 1D reduce of 1e9 floats -- 1 wave per SIMD -- lost
+// 1.2 % (measured on MI355X).
 template <int OP, int G, int U, bool NT>
-__global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ x,
-                                                      int64_t R, int64_t nseg,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 5)))
+void rows_kernel(const float* __restrict__ x,
+                                                      RowMap map, int64_t R, int64_t nseg,
                                                       int64_t P, int32_t blocked,
                                                       typename St<OP>::Out dst,
                                                       uint32_t nxcd,
@@ -485,7 +505,7 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
             const int64_t o = seg / P;
             const int64_t piece = seg - o * P;
             const int64_t g = piece * G + gl;
-            const float* row = x + o * R;
+            const float* row = x + row_start(map, o);
             int64_t j = blocked ? piece * span + gl : g;
             int64_t end = nvec;
             if (blocked && piece * span + span < nvec) end = piece * span + span;
@@ -537,12 +557,13 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(const float* __restrict__ 
 // loads along the row, then the R % 4 tail in order.
 template <int OP>
 __global__ __launch_bounds__(kBlock) void rows_short_kernel(const float* __restrict__ x,
-                                                            int64_t outer, int64_t R,
+                                                            RowMap map, int64_t outer,
+                                                            int64_t R,
                                                             typename St<OP>::Out out) {
     typedef St<OP> T;
     const int64_t stride = int64_t(gridDim.x) * kBlock;
     for (int64_t o = int64_t(blockIdx.x) * kBlock + threadIdx.x; o < outer; o += stride) {
-        const float* row = x + o * R;
+        const float* row = x + row_start(map, o);
         typename T::S4 acc = T::start4();
         int64_t k = 0;
         for (; k + 4 <= R; k += 4) acc = T::fold(acc, load4<false>(row + k));
@@ -572,11 +593,14 @@ __global__ __launch_bounds__(kBlock) void rows_combine_kernel(typename St<OP>::O
 // row and no lane diverges.  Wave (cw, rw) takes the rows r0 + rw + k*RW of
 // the slab, U rows in flight; the RW partial results meet in LDS.  With
 // S == 1, dst is the output; otherwise dst is [S][outer][inner] for
-// slab_combine_kernel.  Needs inner >= 4.
+// slab_combine_kernel.  Needs inner >= 4.  Element (o, r, c) is read at
+// x + o*so + r*sr + c: columns are contiguous, rows and outer indices may be
+// any distance apart (a contiguous array has so = R*inner, sr = inner).
 template <int OP, int CW, int RW, int U, bool NT>
 __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
-    const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t ntiles,
-    int64_t S, int64_t rps, typename St<OP>::Out dst, uint32_t nxcd) {
+    const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t so,
+    int64_t sr, int64_t ntiles, int64_t S, int64_t rps, typename St<OP>::Out dst,
+    uint32_t nxcd) {
     typedef St<OP> T;
     __shared__ typename T::S4 lds[RW > 1 ? (RW - 1) * CW * kWave : 1];
     const int wave = threadIdx.x / kWave;
@@ -597,8 +621,8 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
         const int64_t m = r0 < r1 ? (r1 - r0 + RW - 1) / RW : 0;
         typename T::S4 acc[2] = {T::start4(), T::start4()};
         if (active) {
-            const float* p = x + (o * R + r0) * inner + cl;
-            const int64_t step = RW * inner;
+            const float* p = x + o * so + r0 * sr + cl;
+            const int64_t step = RW * sr;
             int64_t k = 0;
             for (; k + U <= m; k += U) {
                 v4f v[U];
@@ -631,7 +655,9 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
 }
 
 // Small inner (2 <= inner <= 128): several rows of one outer index per load
-// instruction.  The rows of one outer index are adjacent in memory, so a wave
+// instruction.  Element (o, r, c) is at x + o*so + r*sr + c as in cols_kernel.
+// In a contiguous array (sr = inner) the rows of one outer index are
+// adjacent in memory, so a wave
 // covers RPW consecutive rows at once: lane = (row phase rho, lane-column lc)
 // with LC = ceil(inner / 4) lane-columns per row and RPW = 64 / LC row
 // phases (lanes from RPW * LC on idle); each instruction reads RPW * inner
@@ -647,8 +673,9 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
 // slab_combine_kernel.
 template <int OP, int V, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void cols_small_kernel(
-    const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t S,
-    int64_t rps, int32_t LC, typename St<OP>::Out dst, uint32_t nxcd) {
+    const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t so,
+    int64_t sr, int64_t S, int64_t rps, int32_t LC, typename St<OP>::Out dst,
+    uint32_t nxcd) {
     typedef St<OP> T;
     constexpr int kWaves = kBlock / kWave;
     const int wave = threadIdx.x / kWave;
@@ -670,8 +697,8 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
         const int64_t m = r0 < r1 ? (r1 - r0 + RPW - 1) / RPW : 0;
         typename T::S4 acc[2] = {T::start4(), T::start4()};
         if (active) {
-            const float* p = x + (o * R + r0) * inner + cl;
-            const int64_t step = int64_t(RPW) * inner;
+            const float* p = x + o * so + r0 * sr + cl;
+            const int64_t step = int64_t(RPW) * sr;
             const float fill = T::fill();
             int64_t k = 0;
             for (; k + U <= m; k += U) {
@@ -706,6 +733,27 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
                 for (int q = 0; q < V; ++q) T::put(dst, e + q, T::lane(a, q));
             }
         }
+    }
+}
+
+// Views with no unit stride along the reduced axis or the kept inner axis:
+// one lane per output (o, i), its R terms x[o*so + r*sr + i*si] folded one
+// after the other in r order.  Correct for any strides; not fast.
+template <int OP>
+__global__ __launch_bounds__(kBlock) void strided_kernel(const float* __restrict__ x,
+                                                         int64_t outer, int64_t R,
+                                                         int64_t inner, int64_t so,
+                                                         int64_t sr, int64_t si,
+                                                         typename St<OP>::Out out) {
+    typedef St<OP> T;
+    const int64_t n = outer * inner;
+    const int64_t stride = int64_t(gridDim.x) * kBlock;
+    for (int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x; e < n; e += stride) {
+        const int64_t o = e / inner;
+        const float* p = x + o * so + (e - o * inner) * si;
+        typename T::S1 t = T::start1();
+        for (int64_t r = 0; r < R; ++r) t = T::fold(t, p[r * sr]);
+        T::put(out, e, t);
     }
 }
 
@@ -791,6 +839,7 @@ typename St<OP>::Out out_of(Results r) {
 
 struct RowsArgs {
     const float* x;
+    RowMap map;
     int64_t outer, R;
     Results dst;
     uint32_t* ticket;
@@ -800,7 +849,7 @@ struct RowsArgs {
 template <int OP, int G, int U, bool NT>
 hipError_t rows_go(const rd_plan& p, const RowsArgs& a, hipStream_t s) {
     if constexpr (rows_built(OP, G, U)) {
-        return launch(rows_kernel<OP, G, U, NT>, p.blocks, kBlock, s, a.x, a.R,
+        return launch(rows_kernel<OP, G, U, NT>, p.blocks, kBlock, s, a.x, a.map, a.R,
                       a.outer * p.split, p.split, int32_t(p.order == RD_ORDER_BLOCKED),
                       out_of<OP>(a.dst), uint32_t(p.nxcd), a.ticket, out_of<OP>(a.out));
     } else {
@@ -832,7 +881,7 @@ hipError_t rows_op(const rd_plan& p, const RowsArgs& a, hipStream_t s) {
 
 struct ColsArgs {
     const float* x;
-    int64_t outer, R, inner;
+    int64_t outer, R, inner, so, sr;
     Results dst;
 };
 
@@ -841,7 +890,7 @@ hipError_t cols_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
     if constexpr (cols_built(OP, CW, RW, U)) {
         const int64_t ntiles = ((a.inner + 3) / 4 + CW * kWave - 1) / (CW * kWave);
         return launch(cols_kernel<OP, CW, RW, U, NT>, p.blocks, kWave * CW * RW, s, a.x,
-                      a.outer, a.R, a.inner, ntiles, p.split, p.rows_per_split,
+                      a.outer, a.R, a.inner, a.so, a.sr, ntiles, p.split, p.rows_per_split,
                       out_of<OP>(a.dst), uint32_t(p.nxcd));
     } else {
         return hipErrorInvalidValue;
@@ -906,10 +955,16 @@ hipError_t fill_go(Results out, int64_t n, hipStream_t s) {
 }
 
 template <int OP>
-hipError_t rows_short_go(const float* x, int64_t outer, int64_t R, Results out,
+hipError_t rows_short_go(const float* x, RowMap map, int64_t outer, int64_t R, Results out,
                          hipStream_t s) {
-    return launch(rows_short_kernel<OP>, grid_for(outer), kBlock, s, x, outer, R,
+    return launch(rows_short_kernel<OP>, grid_for(outer), kBlock, s, x, map, outer, R,
                   out_of<OP>(out));
+}
+
+template <int OP>
+hipError_t strided_go(const float* x, const Strides& v, Results out, hipStream_t s) {
+    return launch(strided_kernel<OP>, grid_for(v.outer * v.inner), kBlock, s, x, v.outer, v.R,
+                  v.inner, v.so, v.sr, v.si, out_of<OP>(out));
 }
 
 template <int OP>
@@ -930,7 +985,7 @@ hipError_t small_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
     if constexpr (small_built(OP, V, U)) {
         const int32_t lc = int32_t((a.inner + 3) / 4);
         return launch(cols_small_kernel<OP, V, U, NT>, p.blocks, kBlock, s, a.x, a.outer, a.R,
-                      a.inner, p.split, p.rows_per_split, lc, out_of<OP>(a.dst),
+                      a.inner, a.so, a.sr, p.split, p.rows_per_split, lc, out_of<OP>(a.dst),
                       uint32_t(p.nxcd));
     } else {
         return hipErrorInvalidValue;
@@ -983,15 +1038,26 @@ hipError_t launch_fill_start(int op, Results out, int64_t n, hipStream_t s) {
     RD_BY_OP(op, fill_go, out, n, s)
 }
 
-hipError_t launch_rows(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
+// The rows of a ROWS plan: v.outer * v.inner rows of v.R contiguous floats
+// (v.sr == 1), row (o, i) starting at o*so + i*si.
+RowMap row_map(const Strides& v) {
+    return v.inner == 1 ? RowMap{v.so, 0, 1} : RowMap{v.so, v.si, v.inner};
+}
+
+hipError_t launch_rows(int op, const rd_plan& p, const float* x, const Strides& v,
                        Results dst, uint32_t* ticket, Results out, hipStream_t s) {
-    const RowsArgs a{x, outer, R, dst, ticket, out};
+    const RowsArgs a{x, row_map(v), v.outer * v.inner, v.R, dst, ticket, out};
     RD_BY_OP(op, rows_op, p, a, s)
 }
 
-hipError_t launch_rows_short(int op, const float* x, int64_t outer, int64_t R, Results out,
+hipError_t launch_rows_short(int op, const float* x, const Strides& v, Results out,
                              hipStream_t s) {
-    RD_BY_OP(op, rows_short_go, x, outer, R, out, s)
+    RD_BY_OP(op, rows_short_go, x, row_map(v), v.outer * v.inner, v.R, out, s)
+}
+
+hipError_t launch_strided(int op, const float* x, const Strides& v, Results out,
+                          hipStream_t s) {
+    RD_BY_OP(op, strided_go, x, v, out, s)
 }
 
 hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, Results out,
@@ -999,15 +1065,15 @@ hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, R
     RD_BY_OP(op, rows_combine_go, part, outer, P, out, s)
 }
 
-hipError_t launch_cols(int op, const rd_plan& p, const float* x, int64_t outer, int64_t R,
-                       int64_t inner, Results dst, hipStream_t s) {
-    const ColsArgs a{x, outer, R, inner, dst};
+hipError_t launch_cols(int op, const rd_plan& p, const float* x, const Strides& v,
+                       Results dst, hipStream_t s) {
+    const ColsArgs a{x, v.outer, v.R, v.inner, v.so, v.sr, dst};
     RD_BY_OP(op, cols_op, p, a, s)
 }
 
-hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, int64_t outer,
-                             int64_t R, int64_t inner, Results dst, hipStream_t s) {
-    const ColsArgs a{x, outer, R, inner, dst};
+hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, const Strides& v,
+                             Results dst, hipStream_t s) {
+    const ColsArgs a{x, v.outer, v.R, v.inner, v.so, v.sr, dst};
     RD_BY_OP(op, cols_small_go, p, a, s)
 }
 

@@ -219,19 +219,49 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
 
 }  // namespace
 
-rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op,
-                   const rd_tune* tune, rd_plan* plan) {
-    if (!plan || cu_count < 1 || outer < 0 || R < 0 || inner < 0)
-        return RD_ERR_INVALID_ARG;
+// Sizes of a view are valid when its furthest element, in bytes, and the
+// outer*R*inner*4 bytes a contiguous copy would take are representable.
+bool view_sizes_ok(const Strides& v) {
+    if (v.outer < 0 || v.R < 0 || v.inner < 0 || v.so < 0 || v.sr < 0 || v.si < 0)
+        return false;
+    const int64_t lim = INT64_MAX / 4;
+    if (v.outer && v.R && v.inner) {
+        if (v.R > lim / v.outer || v.inner > lim / (v.outer * v.R)) return false;
+    } else if (v.outer && v.inner && v.inner > lim / v.outer) {
+        return false;
+    }
+    if (v.outer == 0 || v.R == 0 || v.inner == 0) return true;
+    // (outer-1)*so + (R-1)*sr + (inner-1)*si must stay below lim
+    int64_t left = lim;
+    const int64_t n[3] = {v.outer - 1, v.R - 1, v.inner - 1};
+    const int64_t st[3] = {v.so, v.sr, v.si};
+    for (int k = 0; k < 3; ++k) {
+        if (n[k] == 0 || st[k] == 0) continue;
+        if (st[k] > left / n[k]) return false;
+        left -= n[k] * st[k];
+    }
+    return true;
+}
+
+void normalize_view(Strides* v) {
+    // strides of axes of length 1 never move: give them the unit value
+    if (v->inner == 1) v->si = 1;
+    if (v->R == 1) v->sr = 1;
+    if (v->outer == 1) v->so = 0;
+    // a single kept axis whose elements are adjacent (outputs o at so == 1)
+    // and a strided reduced axis: the same as a column reduction of
+    // [1, R, outer], whose outputs keep their order
+    if (v->inner == 1 && v->sr != 1 && v->so == 1 && v->outer > 1) {
+        *v = Strides{1, v->R, v->outer, 0, v->sr, 1};
+    }
+}
+
+rd_status plan_view(int cu_count, Strides* v, int op, const rd_tune* tune, rd_plan* plan) {
+    if (!plan || !v || cu_count < 1 || !view_sizes_ok(*v)) return RD_ERR_INVALID_ARG;
     if (op < RD_OP_SUM || op > RD_OP_SOFTMAX_DENOM) return RD_ERR_INVALID_ARG;
     memset(plan, 0, sizeof(*plan));
-    // outer * R * inner * 4 must be representable
-    const int64_t lim = INT64_MAX / 4;
-    if (outer && R && inner) {
-        if (R > lim / outer || inner > lim / (outer * R)) return RD_ERR_INVALID_ARG;
-    } else if (outer && inner && inner > lim / outer) {
-        return RD_ERR_INVALID_ARG;
-    }
+    normalize_view(v);
+    const int64_t outer = v->outer, R = v->R, inner = v->inner;
     plan->nxcd = nxcd_for(cu_count);
     plan->split = 1;
     plan->passes = 1;
@@ -247,8 +277,31 @@ rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op
         if (plan->blocks > kMaxBlocks) plan->blocks = kMaxBlocks;
         return RD_OK;
     }
-    if (inner == 1) return plan_rows(cu_count, outer, R, op, tune, plan);
-    return plan_cols(cu_count, outer, R, inner, op, tune, plan);
+    if (inner == 1 && v->sr == 1) return plan_rows(cu_count, outer, R, op, tune, plan);
+    if (inner > 1 && v->si == 1) return plan_cols(cu_count, outer, R, inner, op, tune, plan);
+    // the reduced axis contiguous, the kept ones strided: outer*inner rows
+    if (v->sr == 1) return plan_rows(cu_count, outer * inner, R, op, tune, plan);
+    if (tune && tune->path) return RD_ERR_INVALID_ARG;
+    plan->path = RD_PATH_STRIDED;
+    plan->block_threads = kBlock;
+    plan->blocks = (outer * inner + kBlock - 1) / kBlock;
+    if (plan->blocks > kMaxBlocks) plan->blocks = kMaxBlocks;
+    return RD_OK;
+}
+
+rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op,
+                   const rd_tune* tune, rd_plan* plan) {
+    if (!plan || cu_count < 1 || outer < 0 || R < 0 || inner < 0)
+        return RD_ERR_INVALID_ARG;
+    // outer * R * inner * 4 must be representable
+    const int64_t lim = INT64_MAX / 4;
+    if (outer && R && inner) {
+        if (R > lim / outer || inner > lim / (outer * R)) return RD_ERR_INVALID_ARG;
+    } else if (outer && inner && inner > lim / outer) {
+        return RD_ERR_INVALID_ARG;
+    }
+    Strides v{outer, R, inner, R * inner, inner, 1};
+    return plan_view(cu_count, &v, op, tune, plan);
 }
 
 rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,

@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     for want in ("rd_sum_1d", "rd_sum_dim", "rd_reduce_1d", "rd_reduce_dim",
                  "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
                  "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "rd_cumsum_dim",
-                 "rd_plan_cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim"):
+                 "rd_plan_cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim",
+                 "rd_reduce_strided", "rd_plan_strided"):
         assert want in names
 
 
@@ -178,6 +179,29 @@ def test_softmax_denom_invalid_arguments(lib, host_buf):
     assert not rd.rd_tune_supported("cols", 8, 2, 4, "softmax_denom")
 
 
+def test_strided_invalid_arguments(lib, host_buf):
+    base, _ = host_buf
+    out = base + 4 * 48
+    cases = [
+        (base, -1, 2, 2, 4, 2, 1, out), (base, 2, 2, 2, -4, 2, 1, out),
+        (base, 2, 2, 2, 4, -2, 1, out), (base, 2, 2, 2, 4, 2, -1, out),
+        (base, 2, 2, 2, 2 ** 62, 2, 1, out),      # the furthest element overflows
+        (base, 2, 2, 2, 4, 2, 1, None),           # null out
+        (None, 2, 2, 2, 4, 2, 1, out),            # null x
+        (base + 1, 2, 2, 2, 4, 2, 1, out),        # misaligned x
+        (base, 2, 2, 2, 4, 2, 1, out + 2),        # misaligned out
+        (base, 2, 3, 2, 20, 2, 1, base + 4 * 20), # out inside the view's span (x[0..23])
+        (base, 2, 3, 2, 3, 10, 5, base + 4 * 28), # out at x[28], the furthest element (3 + 20 + 5)
+    ]
+    for x, o_, R, i, so, sr, si, out_ in cases:
+        assert lib.rd_reduce_strided(x, o_, R, i, so, sr, si, 0, out_, None) == INVALID, (
+            o_, R, i, so, sr, si)
+    for op in (-1, 4, 7):
+        assert lib.rd_reduce_strided(base, 2, 2, 2, 4, 2, 1, op, out, None) == INVALID
+    assert lib.rd_reduce_strided(None, 0, 5, 3, 15, 3, 1, 0, None, None) == OK
+    assert lib.rd_reduce_strided(None, 4, 5, 0, 0, 0, 1, 2, None, None) == OK
+
+
 def test_empty_output_needs_nothing(lib):
     # outer * inner == 0: nothing to write, RD_OK without a device, null ok
     assert lib.rd_sum_dim(None, 0, 5, 3, None, None) == OK
@@ -203,6 +227,7 @@ def test_no_device_is_reported(lib, host_buf):
     assert lib.rd_softmax_denom_dim(base, 2, 2, 2, base + 4 * 32, base + 4 * 40,
                                     None) == NO_DEVICE
     assert lib.rd_softmax_denom_1d(base, 8, base + 4 * 32, base + 4 * 40, None) == NO_DEVICE
+    assert lib.rd_reduce_strided(base, 2, 2, 2, 1, 4, 2, 0, base + 4 * 32, None) == NO_DEVICE
 
 
 def test_python_wrapper_rejects_cpu_tensors():

@@ -1,0 +1,147 @@
+"""GPU parity of reductions over strided views (rd_reduce_strided), against
+the oracle run on a contiguous copy of the same view.
+
+Integer data makes every summation order exact, so each result must equal
+the oracle's bit for bit.  The views cover each path the planner takes for
+a view: columns with a row stride (slices, every other row, broadcast rows
+of stride 0), rows with a row stride (slices, broadcast), a transposed
+array read as columns or as rows, and layouts with no unit stride (the
+lane-per-output kernel), each at base offsets 0-3 floats and with forced
+kernel shapes and splits.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sum_reduction_amd as rd
+import workloads
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+OPS = ("sum", "sumsq", "max", "min")
+
+
+@pytest.fixture(autouse=True)
+def _clear_tuning():
+    rd.rd_tune_set(None)
+    yield
+    rd.rd_tune_set(None)
+
+
+# (name, base length, outer, R, inner, so, sr, si, expected path)
+VIEWS = [
+    ("transpose_dim1", 257 * 300, 300, 257, 1, 1, 300, 1, "cols"),
+    ("transpose_dim0", 257 * 300, 1, 300, 257, 0, 1, 300, "rows"),
+    ("row_slice", 500 * 300, 500, 98, 1, 300, 1, 1, "rows"),
+    ("short_row_slice", 500 * 300, 500, 40, 1, 300, 1, 1, "rows_short"),
+    ("long_row_slice", 20 * 5000, 20, 4493, 1, 5000, 1, 1, "rows"),
+    ("inner_slice_small", 8 * 64 * 100, 8, 64, 4, 6400, 100, 1, "cols_small"),
+    ("inner_slice_3", 8 * 64 * 100, 8, 64, 3, 6400, 100, 1, "cols_small"),
+    ("inner_slice_17", 8 * 64 * 100, 8, 64, 17, 6400, 100, 1, "cols_small"),
+    ("inner_slice_wide", 2 * 64 * 3000, 2, 64, 1000, 64 * 3000, 3000, 1, "cols"),
+    ("every_other_row", 600 * 700, 1, 300, 700, 0, 1400, 1, "cols"),
+    ("broadcast_rows", 300, 1, 50, 300, 0, 0, 1, "cols"),
+    ("broadcast_row_sums", 300, 50, 300, 1, 0, 1, 1, "rows"),
+    ("rows_of_columns", 6 * 400 * 7, 6, 400, 7, 2800, 1, 400, "rows"),
+    ("every_third_column", 200 * 90, 1, 100, 30, 0, 180, 3, "strided"),
+    ("permuted_3d", 5 * 6 * 7, 7, 5, 6, 1, 42, 7, "strided"),
+    ("strided_long", 3 * 20000 * 2, 3, 20000, 2, 1, 6, 3, "strided"),
+]
+
+
+def _view_host(base, outer, R, inner, so, sr, si, off):
+    v = np.lib.stride_tricks.as_strided(base[off:], shape=(outer, R, inner),
+                                        strides=(4 * so, 4 * sr, 4 * si), writeable=False)
+    return np.ascontiguousarray(v)
+
+
+def _data(n, seed, op):
+    return workloads.small_ints(n, seed, -2, 2) if op == "sumsq" else workloads.small_ints(n, seed)
+
+
+def _run(op, views, offsets, seed, tag):
+    lib = rd.load()
+    cases = [(v, off) for v in views for off in offsets]
+    hosts, devs = [], []
+    slots = H.OutSlots([v[2] * v[4] for v, _ in cases])
+    H.say("%s %s: %d calls of rd_reduce_strided" % (tag, op, len(cases)))
+    for k, ((name, n, o, R, i, so, sr, si, _), off) in enumerate(cases):
+        base = _data(n + 4, seed + k, op)
+        dev = H.upload(base)
+        hosts.append(base)
+        devs.append(dev)
+        st = lib.rd_reduce_strided(dev.data_ptr() + 4 * off, o, R, i, so, sr, si, rd.OPS[op],
+                                   slots.ptr(k), H.stream_handle())
+        assert st == 0, (name, off, rd.rd_status_string(st))
+    outs = slots.fetch()
+    for k, ((name, n, o, R, i, so, sr, si, _), off) in enumerate(cases):
+        S, _ = oracle.reduce_dim(_view_host(hosts[k], o, R, i, so, sr, si, off), o, R, i, op,
+                                 threads=1)
+        H.assert_bitwise_equal_oracle(outs[k], S, "%s %s %s off=%d" % (tag, op, name, off))
+
+
+def test_view_paths():
+    for name, n, o, R, i, so, sr, si, path in VIEWS:
+        got = rd.rd_plan_strided(256, o, R, i, so, sr, si).as_dict()["path"]
+        assert got == path, (name, got, path)
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_views_default_plan(op):
+    _run(op, VIEWS, [0, 1, 2, 3], 900 + rd.OPS[op], "views")
+
+
+VIEW_COLS = [v for v in VIEWS if v[-1] in ("cols", "cols_small")]
+VIEW_ROWS = [v for v in VIEWS if v[-1] == "rows"]
+
+
+@pytest.mark.parametrize("split", [1, 3])
+def test_views_forced_column_shapes(split):
+    wide = [v for v in VIEW_COLS if v[4] >= 4]
+    for cw in (1, 2, 4, 8):
+        with rd.tuning(col_waves=cw, row_waves=1, unroll=4, split=split, path=4):
+            _run("sum", wide, [0, 3], 910 + cw, "cols cw%d s%d" % (cw, split))
+    small = [v for v in VIEW_COLS if v[-1] == "cols_small"]
+    with rd.tuning(unroll=4, split=split, path=5):
+        _run("max", small, [0, 1], 915, "cols_small s%d" % split)
+
+
+@pytest.mark.parametrize("group,unroll", [(64, 8), (256, 16)])
+def test_views_forced_row_shapes(group, unroll):
+    for split in (1, 3):
+        with rd.tuning(group=group, unroll=unroll, split=split):
+            _run("sum", VIEW_ROWS, [0, 2], 920 + group + split, "rows g%d p%d" % (group, split))
+            _run("min", VIEW_ROWS, [1], 925 + group + split, "rows g%d p%d" % (group, split))
+
+
+def test_contiguous_view_gives_the_same_bits():
+    """A contiguous view through rd_reduce_strided is rd_reduce_dim, bit for bit."""
+    for outer, R, inner in ((3, 5000, 1), (1, 1_000_003, 1), (4, 1000, 4095), (50, 300, 7)):
+        a = workloads.random(outer * R * inner, 930 + R, "normal")
+        x = H.upload(a, 1)
+        want = rd.rd_reduce_dim(x, outer, R, inner, "sum").cpu().numpy()
+        got = rd.rd_reduce_strided(x, outer, R, inner, R * inner, inner, 1, "sum").cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (outer, R, inner)
+
+
+def test_torch_style_views():
+    """rd.reduce on transposed, sliced and expanded torch tensors equals
+    torch's own reduction of the same view (integer data: exact)."""
+    t = H.torch()
+    a = workloads.small_ints(6 * 70 * 8 * 9, 940).reshape(6, 70, 8, 9)
+    x = H.upload(a).view(6, 70, 8, 9)
+    views = [(x.transpose(0, 1), 1), (x[1:5], 1), (x[:, 3:60], 1), (x[:, ::2], 1),
+             (x.permute(3, 0, 1, 2), 0), (x[:, :, 0, 0].t(), 0), (x[:, :, 0, 0].t(), 1),
+             (x[:1].expand(5, 70, 8, 9), 0), (x[:1].expand(5, 70, 8, 9), 1),
+             (x[:, :, :, 0], 1), (x[..., ::3], 3), (x.flatten(1).t(), 1)]
+    for v, d in views:
+        for op, f in (("sum", lambda z: z.sum(d)), ("max", lambda z: z.amax(d)),
+                      ("min", lambda z: z.amin(d))):
+            got = rd.reduce(v, op, d).cpu()
+            want = f(v).cpu()
+            assert t.equal(got, want), (tuple(v.shape), v.stride(), d, op)
+    # no single [outer, R, inner] view: refused, not silently copied
+    for v, d in ((x[:, :, :, 2:5], 1), (x.transpose(0, 1), 0), (x.transpose(2, 3), 1)):
+        with pytest.raises(ValueError):
+            rd.reduce(v, "sum", d)

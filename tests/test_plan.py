@@ -287,3 +287,70 @@ def test_cumsum_degenerate_plans():
         rd.rd_plan_cumsum(0, 1, 1, 1)
     with pytest.raises(rd.RdError):
         rd.rd_plan_cumsum(CU, -1, 1, 1)
+
+
+# ------------------------------------------------------------ strided views
+def test_strided_contiguous_view_plans_like_the_array():
+    for outer, R, inner in ((1, 10**9, 1), (128, 4096, 4095), (32768, 32768, 1), (3, 5, 7),
+                            (4096, 4096, 4), (1, 100, 130), (7, 0, 3), (0, 4, 4)):
+        a = rd.rd_plan_dim(CU, outer, R, inner).as_dict()
+        b = rd.rd_plan_strided(CU, outer, R, inner, R * inner, inner, 1).as_dict()
+        assert a == b, (outer, R, inner)
+
+
+def test_strided_path_follows_the_unit_stride():
+    P = lambda *v: rd.rd_plan_strided(CU, *v).as_dict()
+    # reducing dim 1 of a transposed [N, M] array: outputs adjacent (so = 1),
+    # terms M apart -> read as the columns of [1, R, outer]
+    p = P(4096, 1000, 1, 1, 4096, 0)
+    q = rd.rd_plan_dim(CU, 1, 1000, 4096).as_dict()
+    assert p == q
+    # reducing dim 0 of a transposed array: each output's terms contiguous
+    # (sr = 1), outputs M apart -> rows
+    p = P(1, 4096, 1000, 0, 1, 4096)
+    assert p["path"] == "rows" and p == rd.rd_plan_dim(CU, 1000, 4096, 1).as_dict()
+    # a row slice of a wider array: rows with a stride
+    assert P(500, 98, 1, 300, 1, 1)["path"] == "rows_short" or P(500, 98, 1, 300, 1, 1)["path"] == "rows"
+    # columns of an inner slice: the column kernels with a row stride
+    assert P(8, 64, 4, 64 * 100, 100, 1)["path"] == "cols_small"
+    assert P(2, 64, 1000, 10**6, 3000, 1)["path"] == "cols"
+    # broadcast rows (stride 0) still have a unit stride
+    assert P(1, 50, 300, 0, 0, 1)["path"] == "cols_small" or P(1, 50, 300, 0, 0, 1)["path"] == "cols"
+    # no unit stride: the lane-per-output kernel
+    p = P(3, 100, 50, 10**5, 700, 3)
+    assert p["path"] == "strided" and p["passes"] == 1 and p["workspace_bytes"] == 0
+    assert p["blocks"] == -(-150 // 256)
+    # length-1 axes lose their strides
+    assert P(1, 1000, 1, 999, 1, 77) == rd.rd_plan_dim(CU, 1, 1000, 1).as_dict()
+    assert P(5, 1, 6, 6, 12345, 1) == rd.rd_plan_dim(CU, 5, 1, 6).as_dict()
+
+
+def test_strided_invalid_views():
+    for v in ((-1, 2, 2, 4, 2, 1), (2, 2, 2, -4, 2, 1), (2, 2, 2, 4, -2, 1), (2, 2, 2, 4, 2, -1),
+              (2, 2, 2, 2 ** 62, 1, 1), (2, 2 ** 40, 2, 0, 2 ** 30, 1)):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_strided(CU, *v)
+    with rd.tuning(path=4):   # a column kernel cannot read a view without a unit stride
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_strided(CU, 3, 100, 50, 10**5, 700, 3)
+
+
+def test_view3_collapses_torch_layouts():
+    import torch
+    x = torch.empty(6, 7, 8, 9)
+    cases = {
+        (x, 1): (6, 7, 72, 504, 72, 1),
+        (x.transpose(0, 1), 1): (7, 6, 72, 72, 504, 1),
+        (x[:, :, 2:5, :], 1): (6, 7, 27, 504, 72, 1),   # rows 2..4 of each 8x9 block are adjacent
+        (x[:, :, :, 2:5], 1): (6, 7, None, None, None, None),   # 8 runs of 3, 9 apart: no collapse
+        (x[1:4], 2): (21, 8, 9, 72, 9, 1),
+        (x[:, 1:4], 2): (6, 8, None, None, None, None),   # outer strides 504 and 72: no collapse
+        (x.permute(3, 0, 1, 2), 0): (1, 9, 336, 0, 1, 9),
+        (x.expand(2, 6, 7, 8, 9), 1): (2, 6, 504, 0, 504, 1),
+    }
+    for (t, d), want in cases.items():
+        got = rd._view3(t, d)
+        if want[2] is None:
+            assert got is None, (t.shape, t.stride(), d)
+        else:
+            assert got == want, (t.shape, t.stride(), d, got)
