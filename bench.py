@@ -115,6 +115,9 @@ def main(argv=None):
                     choices=["sum", "sumsq", "max", "min", "softmax_denom"],
                     help="with --report: the reductions to time (default: sum); "
                     "softmax_denom writes the pair (max, shifted sum of exp)")
+    ap.add_argument("--strided", action="store_true",
+                    help="with --report: sums over strided views of a [32768, 32768] array "
+                    "(transposed, every other row, every third column) instead")
     ap.add_argument("--scan", action="store_true",
                     help="with --report: the cumulative sums instead (problem 91's "
                     "[32768, 32768] rows, then each --scan-shape)")
@@ -162,6 +165,8 @@ def main(argv=None):
     props = torch.cuda.get_device_properties(dev)
     cu = props.multi_processor_count
     if args.report:
+        if args.strided:
+            return report_strided(args, dev, cu)
         return report_scan(args, dev, cu) if args.scan else report(args, dev, cu)
     names = args.workload or STEP_WORKLOADS
     ws = [workloads.WORKLOADS[n] for n in names]
@@ -381,6 +386,63 @@ def report(args, dev, cu):
                   flush=True)
         del x, out, host
         torch.cuda.empty_cache()
+    return 0
+
+
+# Strided views of one [N, N] float array, N = 32768 (4.3 GB), seed 3 normal
+# data: (name, outer, R, inner, stride_outer, stride_r, stride_inner), the
+# torch expression it stands for, and the bytes the view holds.
+STRIDED_N = 32768
+STRIDED_VIEWS = [
+    ("rows_of_transpose", STRIDED_N, STRIDED_N, 1, 1, STRIDED_N, 1, "x.t().sum(1)"),
+    ("cols_of_transpose", 1, STRIDED_N, STRIDED_N, 0, 1, STRIDED_N, "x.t().sum(0)"),
+    ("every_other_row", 1, STRIDED_N // 2, STRIDED_N, 0, 2 * STRIDED_N, 1, "x[::2].sum(0)"),
+    ("row_halves", STRIDED_N, STRIDED_N // 2, 1, STRIDED_N, 1, 1, "x[:, :N/2].sum(1)"),
+    ("every_third_column", 1, STRIDED_N // 8, STRIDED_N // 3, 0, 8 * STRIDED_N, 3,
+     "x[::8, ::3].sum(0)"),
+]
+
+
+def report_strided(args, dev, cu):
+    """One JSON line per strided view: GPU time warm, GB/s over the bytes the
+    view holds, its plan, parity against the oracle on a contiguous copy."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import sum_reduction_amd as rd
+    import workloads
+
+    threads = oracle.default_threads()
+    n = STRIDED_N
+    host = workloads.random(n * n, 3, "normal")
+    x = torch.from_numpy(host).to(dev)
+    for name, o, R, i, so, sr, si, expr in STRIDED_VIEWS:
+        log("report: strided %s" % name)
+        out = torch.empty(o * i, dtype=torch.float32, device=dev)
+
+        def call():
+            rd.rd_reduce_strided(x, o, R, i, so, sr, si, "sum", out=out)
+
+        reps = args.reps or 30
+        ms = _median_ms(call, reps)
+        nbytes = 4 * (o * R * i + o * i)
+        plan = rd.rd_plan_strided(cu, o, R, i, so, sr, si).as_dict()
+        line = {"view": name, "torch": expr, "shape": [o, R, i], "strides": [so, sr, si],
+                "view_bytes": nbytes, "ms_median": round(ms, 5),
+                "GBps": round(nbytes / ms / 1e6, 1),
+                "frac_of_peak": round(nbytes / ms / 1e6 / PEAK_GBS, 4),
+                "plan": plan, "reps": reps}
+        if not args.no_oracle:
+            v = np.lib.stride_tricks.as_strided(host, shape=(o, R, i),
+                                                strides=(4 * so, 4 * sr, 4 * si),
+                                                writeable=False)
+            S, A = oracle.sum_dim(np.ascontiguousarray(v), o, R, i, threads)
+            got = out.cpu().numpy().reshape(-1)
+            line["parity"] = {"ok": bool(oracle.within_tolerance(got, S.reshape(-1),
+                                                                 A.reshape(-1)).all())}
+        print(json.dumps(line), flush=True)
+        del out
     return 0
 
 
