@@ -193,11 +193,13 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
     if (t && t->split) {
         S = t->split;
     } else {
-        // loads in flight over the chip without a split, in lane-waves x U
-        const int64_t inflight = base * p->col_waves * p->row_waves * p->unroll;
+        // loads in flight over the chip without a split, in lane-waves x U:
+        // base * per, compared as base < ceil(want / per) so that the
+        // product is only formed when it is small
+        const int64_t per = int64_t(p->col_waves) * p->row_waves * p->unroll;
         const int64_t want = int64_t(cu) * kLoadWavesPerCu;
-        if (inflight < want || base < cu) {
-            S = ceil_div(want, inflight);
+        if (base < ceil_div(want, per) || base < cu) {
+            S = base < ceil_div(want, per) ? ceil_div(want, base * per) : 1;
             const int64_t fill = ceil_div(cu, base);
             if (S < fill) S = fill;
             // every wave keeps at least one full unrolled step of rows per slab

@@ -1,0 +1,150 @@
+// Host-only fuzz of the launch planner (sum_reduction_amd/csrc/rd_plan.cpp),
+// built with g++ under AddressSanitizer and UndefinedBehaviorSanitizer by
+// tests/test_plan_sanitized.py.  Random shapes (zeros, ones, small, huge,
+// near the int64 limits), strides, operators and tuning overrides go
+// through plan_view and plan_cumsum; every accepted plan must satisfy the
+// invariants the launchers rely on.  Any signed overflow, out-of-bounds
+// access or failed invariant ends the run with a nonzero status.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <random>
+
+#include "rd_internal.h"
+
+// Kernel-shape tables live with the kernels (rd_kernels.hip, not built
+// here); every shape counts as built, so tuning requests reach the sizing.
+namespace rd {
+bool rows_shape_supported(int, int group, int unroll) {
+    return (group == 64 || group == 256) && unroll > 0 && unroll <= 16;
+}
+bool cols_shape_supported(int, int cw, int rw, int unroll) {
+    return cw > 0 && rw > 0 && cw * rw <= 16 && unroll > 0 && unroll <= 16;
+}
+bool small_shape_supported(int, int unroll) { return unroll > 0 && unroll <= 8; }
+}  // namespace rd
+
+namespace {
+
+std::mt19937_64 rng;
+
+int64_t pick_size() {
+    switch (rng() % 8) {
+        case 0: return 0;
+        case 1: return 1;
+        case 2: return int64_t(rng() % 8);
+        case 3: return int64_t(rng() % 5000);
+        case 4: return int64_t(1) << (rng() % 40);
+        case 5: return (int64_t(1) << (rng() % 62)) + int64_t(rng() % 3) - 1;
+        case 6: return int64_t(rng() >> 1);           // up to INT64_MAX
+        default: return int64_t(rng() % 100000000);
+    }
+}
+
+int64_t pick_stride(int64_t contiguous) {
+    switch (rng() % 6) {
+        case 0: return 0;
+        case 1: return 1;
+        case 2: return contiguous;
+        case 3: return int64_t(rng() % 70000);
+        case 4: return int64_t(rng() >> (1 + rng() % 62));
+        default:
+            return contiguous > 0 && contiguous < (int64_t(1) << 60)
+                       ? contiguous * int64_t(1 + rng() % 3)
+                       : 1;
+    }
+}
+
+void fail(const char* what, const rd::Strides& v, int op, const rd_plan& p) {
+    fprintf(stderr,
+            "invariant failed: %s; view [%lld, %lld, %lld] strides (%lld, %lld, %lld) op %d; "
+            "plan path %d split %lld rows_per_split %lld blocks %lld workspace %lld\n",
+            what, (long long)v.outer, (long long)v.R, (long long)v.inner, (long long)v.so,
+            (long long)v.sr, (long long)v.si, op, p.path, (long long)p.split,
+            (long long)p.rows_per_split, (long long)p.blocks, (long long)p.workspace_bytes);
+    exit(3);
+}
+
+void check_reduce_plan(const rd::Strides& v, int op, const rd_plan& p) {
+    const int64_t max_blocks = rd::kMaxBlocks;
+    if (p.path == RD_PATH_NONE) {
+        if (v.outer * v.inner != 0) fail("NONE with outputs", v, op, p);
+        return;
+    }
+    if (p.blocks < 1 || p.blocks > max_blocks) fail("blocks out of range", v, op, p);
+    if (p.split < 1) fail("split < 1", v, op, p);
+    if (p.workspace_bytes < 0) fail("negative workspace", v, op, p);
+    if (p.passes != (p.split > 1 && p.combine != RD_COMBINE_LAST_BLOCK ? 2 : 1) &&
+        p.path != RD_PATH_ZERO && p.path != RD_PATH_STRIDED && p.path != RD_PATH_ROWS_SHORT)
+        fail("passes", v, op, p);
+    const int64_t bytes = op == RD_OP_SOFTMAX_DENOM ? 8 : 4;
+    switch (p.path) {
+        case RD_PATH_ROWS:
+            if (v.inner != 1 && v.sr != 1) fail("rows path without unit stride", v, op, p);
+            if (p.group != 64 && p.group != 256) fail("group", v, op, p);
+            if (p.split > 1 && p.workspace_bytes / bytes != v.outer * v.inner * p.split)
+                fail("rows workspace", v, op, p);
+            break;
+        case RD_PATH_COLS:
+        case RD_PATH_COLS_SMALL:
+            if (v.si != 1) fail("column path without unit inner stride", v, op, p);
+            if (p.rows_per_split < 1 || p.split * p.rows_per_split < v.R ||
+                (p.split - 1) * p.rows_per_split >= v.R)
+                fail("slabs do not tile R", v, op, p);
+            if (p.split > 1 && p.workspace_bytes / bytes != p.split * v.outer * v.inner)
+                fail("slab workspace", v, op, p);
+            break;
+        default:
+            break;
+    }
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+    const long iters = argc > 1 ? atol(argv[1]) : 200000;
+    rng.seed(argc > 2 ? strtoull(argv[2], nullptr, 10) : 12345);
+    long accepted = 0;
+    for (long it = 0; it < iters; ++it) {
+        const int cu = (rng() % 4 == 0) ? int(1 + rng() % 512) : 256;
+        rd::Strides v;
+        v.outer = pick_size();
+        v.R = pick_size();
+        v.inner = pick_size();
+        const bool contiguous = rng() % 2 == 0;
+        // contiguous strides only when they are representable
+        const bool fits = v.inner < (int64_t(1) << 31) && v.R < (int64_t(1) << 31);
+        v.so = contiguous && fits ? v.R * v.inner : pick_stride(v.R);
+        v.sr = contiguous && fits ? v.inner : pick_stride(v.inner);
+        v.si = contiguous ? 1 : pick_stride(1);
+        const int op = int(rng() % 5);
+        rd_tune t{};
+        const bool tuned = rng() % 3 == 0;
+        if (tuned) {
+            t.group = (rng() % 3 == 0) ? 0 : (rng() % 2 ? 64 : 256);
+            t.col_waves = int32_t(rng() % 5 == 0 ? 0 : 1 << (rng() % 5));
+            t.row_waves = int32_t(rng() % 3 == 0 ? 0 : 1 << (rng() % 4));
+            t.unroll = int32_t(rng() % 3 == 0 ? 0 : 1 << (rng() % 5));
+            t.order = int32_t(rng() % 3);
+            t.nontemporal = int32_t(rng() % 3);
+            t.combine = int32_t(rng() % 3);
+            t.path = int32_t(rng() % 4 == 0 ? (rng() % 2 ? RD_PATH_COLS : RD_PATH_COLS_SMALL) : 0);
+            t.split = rng() % 2 ? 0 : int64_t(rng() % 5000);
+        }
+        rd::Strides w = v;
+        rd_plan p;
+        if (rd::plan_view(cu, &w, op, tuned ? &t : nullptr, &p) == RD_OK) {
+            ++accepted;
+            check_reduce_plan(w, op, p);
+        }
+        if (contiguous && fits) {
+            rd_plan q;
+            if (rd::plan_cumsum(cu, v.outer, v.R, v.inner, tuned ? &t : nullptr, &q) == RD_OK) {
+                if (q.path != RD_PATH_NONE && (q.blocks < 1 || q.split < 1 || q.workspace_bytes < 0))
+                    fail("cumsum plan", v, -1, q);
+            }
+        }
+    }
+    printf("plan_fuzz: %ld iterations, %ld accepted plans, no finding\n", iters, accepted);
+    return 0;
+}

@@ -248,3 +248,16 @@ def test_wrapper_raises_with_status():
     with pytest.raises(rd.RdError) as e:
         rd.rd_plan_dim(0, 1, 1, 1)
     assert e.value.status == INVALID
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No silent fallback: without librd.so every entry point raises."""
+    import torch
+    monkeypatch.setattr(rd, "_lib", None)
+    monkeypatch.setattr(rd, "LIBRARY", "/nonexistent/librd.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        rd.load()
+    with pytest.raises(RuntimeError):
+        rd.rd_plan_dim(256, 1, 10, 1)
+    with pytest.raises((RuntimeError, ValueError)):
+        rd.rd_sum_1d(torch.ones(4))
