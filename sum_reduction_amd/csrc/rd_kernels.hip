@@ -624,12 +624,36 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
             const float* p = x + o * so + r0 * sr + cl;
             const int64_t step = RW * sr;
             int64_t k = 0;
-            for (; k + U <= m; k += U) {
-                v4f v[U];
+            if constexpr (OP == RD_OP_SOFTMAX_DENOM) {
+                // Software-pipelined: the next U rows are loaded before the
+                // exponentials of the current U are taken, so the loads stay
+                // in flight across the arithmetic (two waves per SIMD do not
+                // hide it otherwise).  Same order of the folds.
+                if (k + U <= m) {
+                    v4f cur[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = load4<NT>(p + u * step);
-                T::template fold_all<U>(acc, v);
-                p += U * step;
+                    for (int u = 0; u < U; ++u) cur[u] = load4<NT>(p + u * step);
+                    p += U * step;
+                    for (; k + 2 * U <= m; k += U) {
+                        v4f nxt[U];
+#pragma unroll
+                        for (int u = 0; u < U; ++u) nxt[u] = load4<NT>(p + u * step);
+                        T::template fold_all<U>(acc, cur);
+#pragma unroll
+                        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+                        p += U * step;
+                    }
+                    T::template fold_all<U>(acc, cur);
+                    k += U;
+                }
+            } else {
+                for (; k + U <= m; k += U) {
+                    v4f v[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) v[u] = load4<NT>(p + u * step);
+                    T::template fold_all<U>(acc, v);
+                    p += U * step;
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
