@@ -186,7 +186,9 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
             break;
         }
         case RD_PATH_STRIDED:
-            e = rd::launch_strided(op, x, v, out, s);
+            e = rd::launch_strided(op, p, x, v, p.split == 1 ? out : part, s);
+            if (e == hipSuccess && p.split > 1)
+                e = rd::launch_slab_combine(op, part, p.split, nout, out, s);
             break;
         default:
             e = hipErrorInvalidValue;

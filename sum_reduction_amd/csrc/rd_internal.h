@@ -70,9 +70,10 @@ hipError_t launch_cols(int op, const rd_plan& p, const float* x, const Strides& 
                        Results dst, hipStream_t s);
 hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, const Strides& v,
                              Results dst, hipStream_t s);
-// Any strides: one lane per output.
-hipError_t launch_strided(int op, const float* x, const Strides& v, Results out,
-                          hipStream_t s);
+// Any strides: one lane per (slab, output); dst is the output when
+// p.split == 1, else [p.split][outer*inner] partial results.
+hipError_t launch_strided(int op, const rd_plan& p, const float* x, const Strides& v,
+                          Results dst, hipStream_t s);
 hipError_t launch_slab_combine(int op, Results slab, int64_t S, int64_t n, Results out,
                                hipStream_t s);
 

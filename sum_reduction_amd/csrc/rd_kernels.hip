@@ -761,23 +761,43 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
 }
 
 // Views with no unit stride along the reduced axis or the kept inner axis:
-// one lane per output (o, i), its R terms x[o*so + r*sr + i*si] folded one
-// after the other in r order.  Correct for any strides; not fast.
+// one lane per (slab s, output e), e fastest, so a wave's lanes read
+// neighbouring outputs.  Lane (s, e) folds the terms x[o*so + r*sr + i*si]
+// of rows r in [s*rps, min(R, (s+1)*rps)) in r order, 8 loads in flight.
+// With S == 1 dst is the output; otherwise dst is [S][outer*inner] for
+// slab_combine_kernel.  Correct for any strides; as fast as scattered
+// 4-byte loads allow.
 template <int OP>
 __global__ __launch_bounds__(kBlock) void strided_kernel(const float* __restrict__ x,
                                                          int64_t outer, int64_t R,
                                                          int64_t inner, int64_t so,
-                                                         int64_t sr, int64_t si,
-                                                         typename St<OP>::Out out) {
+                                                         int64_t sr, int64_t si, int64_t S,
+                                                         int64_t rps,
+                                                         typename St<OP>::Out dst) {
     typedef St<OP> T;
+    constexpr int kIn = 8;
     const int64_t n = outer * inner;
+    const int64_t items = n * S;
     const int64_t stride = int64_t(gridDim.x) * kBlock;
-    for (int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x; e < n; e += stride) {
+    for (int64_t it = int64_t(blockIdx.x) * kBlock + threadIdx.x; it < items; it += stride) {
+        const int64_t s = it / n;
+        const int64_t e = it - s * n;
         const int64_t o = e / inner;
-        const float* p = x + o * so + (e - o * inner) * si;
+        const int64_t r0 = s * rps;
+        const int64_t r1 = r0 + rps < R ? r0 + rps : R;
+        const float* p = x + o * so + (e - o * inner) * si + r0 * sr;
         typename T::S1 t = T::start1();
-        for (int64_t r = 0; r < R; ++r) t = T::fold(t, p[r * sr]);
-        T::put(out, e, t);
+        int64_t r = r0;
+        for (; r + kIn <= r1; r += kIn) {
+            float v[kIn];
+#pragma unroll
+            for (int u = 0; u < kIn; ++u) v[u] = p[u * sr];
+#pragma unroll
+            for (int u = 0; u < kIn; ++u) t = T::fold(t, v[u]);
+            p += kIn * sr;
+        }
+        for (; r < r1; ++r, p += sr) t = T::fold(t, *p);
+        T::put(dst, it, t);
     }
 }
 
@@ -986,9 +1006,10 @@ hipError_t rows_short_go(const float* x, RowMap map, int64_t outer, int64_t R, R
 }
 
 template <int OP>
-hipError_t strided_go(const float* x, const Strides& v, Results out, hipStream_t s) {
-    return launch(strided_kernel<OP>, grid_for(v.outer * v.inner), kBlock, s, x, v.outer, v.R,
-                  v.inner, v.so, v.sr, v.si, out_of<OP>(out));
+hipError_t strided_go(const rd_plan& p, const float* x, const Strides& v, Results dst,
+                      hipStream_t s) {
+    return launch(strided_kernel<OP>, p.blocks, kBlock, s, x, v.outer, v.R, v.inner, v.so, v.sr,
+                  v.si, p.split, p.rows_per_split, out_of<OP>(dst));
 }
 
 template <int OP>
@@ -1079,9 +1100,9 @@ hipError_t launch_rows_short(int op, const float* x, const Strides& v, Results o
     RD_BY_OP(op, rows_short_go, x, row_map(v), v.outer * v.inner, v.R, out, s)
 }
 
-hipError_t launch_strided(int op, const float* x, const Strides& v, Results out,
-                          hipStream_t s) {
-    RD_BY_OP(op, strided_go, x, v, out, s)
+hipError_t launch_strided(int op, const rd_plan& p, const float* x, const Strides& v,
+                          Results dst, hipStream_t s) {
+    RD_BY_OP(op, strided_go, p, x, v, dst, s)
 }
 
 hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, Results out,

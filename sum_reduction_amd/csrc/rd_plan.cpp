@@ -219,6 +219,43 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
     return RD_OK;
 }
 
+// No unit stride: a lane per (slab, output).  Few outputs are split along R
+// into slabs until about kStridedLanesPerCu lanes per CU are busy, each slab
+// keeping at least kStridedMinRows rows.
+constexpr int64_t kStridedLanesPerCu = 1024;
+constexpr int64_t kStridedMinRows = 32;
+
+rd_status plan_strided(int cu, int64_t outer, int64_t R, int64_t inner, int op,
+                       const rd_tune* t, rd_plan* p) {
+    if (t && (t->path || t->group || t->col_waves || t->row_waves || t->unroll || t->order ||
+              t->combine))
+        return RD_ERR_INVALID_ARG;
+    const int64_t n = outer * inner;
+    int64_t S = 1;
+    if (t && t->split) {
+        S = t->split;
+    } else {
+        const int64_t want = int64_t(cu) * kStridedLanesPerCu;
+        if (n < want) {
+            S = ceil_div(want, n);
+            int64_t cap = R / kStridedMinRows;
+            if (cap < 1) cap = 1;
+            if (S > cap) S = cap;
+        }
+    }
+    if (S < 1) return RD_ERR_INVALID_ARG;
+    split_rows(R, S, p);
+    if (p->split > INT64_MAX / result_bytes(op) / n) return RD_ERR_INVALID_ARG;
+    p->path = RD_PATH_STRIDED;
+    p->block_threads = kBlock;
+    p->blocks = ceil_div(p->split * n, kBlock);
+    if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
+    p->passes = p->split > 1 ? 2 : 1;
+    p->combine = p->split > 1 ? RD_COMBINE_PASS : RD_COMBINE_NONE;
+    p->workspace_bytes = p->split > 1 ? p->split * n * result_bytes(op) : 0;
+    return RD_OK;
+}
+
 }  // namespace
 
 // Sizes of a view are valid when its furthest element, in bytes, and the
@@ -283,12 +320,7 @@ rd_status plan_view(int cu_count, Strides* v, int op, const rd_tune* tune, rd_pl
     if (inner > 1 && v->si == 1) return plan_cols(cu_count, outer, R, inner, op, tune, plan);
     // the reduced axis contiguous, the kept ones strided: outer*inner rows
     if (v->sr == 1) return plan_rows(cu_count, outer * inner, R, op, tune, plan);
-    if (tune && tune->path) return RD_ERR_INVALID_ARG;
-    plan->path = RD_PATH_STRIDED;
-    plan->block_threads = kBlock;
-    plan->blocks = (outer * inner + kBlock - 1) / kBlock;
-    if (plan->blocks > kMaxBlocks) plan->blocks = kMaxBlocks;
-    return RD_OK;
+    return plan_strided(cu_count, outer, R, inner, op, tune, plan);
 }
 
 rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op,

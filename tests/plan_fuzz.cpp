@@ -75,7 +75,7 @@ void check_reduce_plan(const rd::Strides& v, int op, const rd_plan& p) {
     if (p.split < 1) fail("split < 1", v, op, p);
     if (p.workspace_bytes < 0) fail("negative workspace", v, op, p);
     if (p.passes != (p.split > 1 && p.combine != RD_COMBINE_LAST_BLOCK ? 2 : 1) &&
-        p.path != RD_PATH_ZERO && p.path != RD_PATH_STRIDED && p.path != RD_PATH_ROWS_SHORT)
+        p.path != RD_PATH_ZERO && p.path != RD_PATH_ROWS_SHORT)
         fail("passes", v, op, p);
     const int64_t bytes = op == RD_OP_SOFTMAX_DENOM ? 8 : 4;
     switch (p.path) {
@@ -93,6 +93,14 @@ void check_reduce_plan(const rd::Strides& v, int op, const rd_plan& p) {
                 fail("slabs do not tile R", v, op, p);
             if (p.split > 1 && p.workspace_bytes / bytes != p.split * v.outer * v.inner)
                 fail("slab workspace", v, op, p);
+            break;
+        case RD_PATH_STRIDED:
+            if (v.sr == 1 || (v.si == 1 && v.inner > 1)) fail("strided path with a unit stride", v, op, p);
+            if (p.rows_per_split < 1 || p.split * p.rows_per_split < v.R ||
+                (p.split - 1) * p.rows_per_split >= v.R)
+                fail("strided slabs do not tile R", v, op, p);
+            if (p.split > 1 && p.workspace_bytes / bytes != p.split * v.outer * v.inner)
+                fail("strided workspace", v, op, p);
             break;
         default:
             break;

@@ -145,3 +145,12 @@ def test_torch_style_views():
     for v, d in ((x[:, :, :, 2:5], 1), (x.transpose(0, 1), 0), (x.transpose(2, 3), 1)):
         with pytest.raises(ValueError):
             rd.reduce(v, "sum", d)
+
+
+@pytest.mark.parametrize("split", [1, 2, 7, 40])
+def test_views_forced_strided_splits(split):
+    """The lane-per-output kernel with R cut into slabs (and their combine)."""
+    strided = [v for v in VIEWS if v[-1] == "strided"]
+    with rd.tuning(split=split):
+        for op in OPS:
+            _run(op, strided, [0, 1, 3], 950 + split, "strided s%d" % split)

@@ -318,8 +318,16 @@ def test_strided_path_follows_the_unit_stride():
     assert P(1, 50, 300, 0, 0, 1)["path"] == "cols_small" or P(1, 50, 300, 0, 0, 1)["path"] == "cols"
     # no unit stride: the lane-per-output kernel
     p = P(3, 100, 50, 10**5, 700, 3)
-    assert p["path"] == "strided" and p["passes"] == 1 and p["workspace_bytes"] == 0
-    assert p["blocks"] == -(-150 // 256)
+    # 150 outputs: split along R into slabs of at least 32 rows (here 3)
+    assert p["path"] == "strided" and p["split"] == 3 and p["rows_per_split"] == 34
+    assert p["passes"] == 2 and p["workspace_bytes"] == 4 * 3 * 150
+    assert p["blocks"] == -(-450 // 256)
+    # many outputs: one slab, one pass
+    p = P(1, 4096, 10922, 0, 262144, 3)
+    assert p["path"] == "strided" and p["split"] == 25 and p["passes"] == 2   # ceil(256*1024 / 10922)
+    p = P(300, 64, 1000, 10**6, 3000, 7)
+    assert p["path"] == "strided" and p["split"] == 1 and p["passes"] == 1
+    assert p["workspace_bytes"] == 0 and p["blocks"] == -(-300000 // 256)
     # length-1 axes lose their strides
     assert P(1, 1000, 1, 999, 1, 77) == rd.rd_plan_dim(CU, 1, 1000, 1).as_dict()
     assert P(5, 1, 6, 6, 12345, 1) == rd.rd_plan_dim(CU, 5, 1, 6).as_dict()
