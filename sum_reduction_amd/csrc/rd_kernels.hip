@@ -376,9 +376,38 @@ __device__ __forceinline__ SmPair read_lane(SmPair v, int l) {
 // two 32-lane halves joined through lanes 0 and 32.  Each step joins a
 // lane's value with an equal-rank partner's, and every join is commutative,
 // so every lane ends with the same bits.
+// The softmax pair takes the same butterfly twice instead of joining pairs:
+// first the maximum m, then every lane's sum re-centred on m once and the
+// sums added -- one exp2 per lane rather than a rescale at every step.
+__device__ __forceinline__ float wave_max(float m) {
+    m = __builtin_elementwise_maximum(m, dpp<0xB1>(m));
+    m = __builtin_elementwise_maximum(m, dpp<0x4E>(m));
+    m = __builtin_elementwise_maximum(m, dpp<0x141>(m));
+    m = __builtin_elementwise_maximum(m, dpp<0x140>(m));
+    m = __builtin_elementwise_maximum(m, swap16(m));
+    return __builtin_elementwise_maximum(read_lane(m, 0), read_lane(m, 32));
+}
+
+__device__ __forceinline__ float wave_add(float s) {
+    s = s + dpp<0xB1>(s);
+    s = s + dpp<0x4E>(s);
+    s = s + dpp<0x141>(s);
+    s = s + dpp<0x140>(s);
+    s = s + swap16(s);
+    return read_lane(s, 0) + read_lane(s, 32);
+}
+
 template <int OP>
 __device__ __forceinline__ typename St<OP>::S1 wave_reduce(typename St<OP>::S1 v) {
     typedef St<OP> T;
+    if constexpr (OP == RD_OP_SOFTMAX_DENOM) {
+        const float m = wave_max(v.m);
+        // a finite maximum: each sum re-centred on it (a lane that holds
+        // nothing has s = 0 and stays 0); otherwise the sums are added as
+        // they are (+Inf, NaN propagate; all -Inf gives 0)
+        const float s = sm_finite(m) ? sm_rescale(v.s, sm_shift(v.m), m) : v.s;
+        return SmPair{m, wave_add(s)};
+    }
     v = T::join(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
     v = T::join(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
     v = T::join(v, dpp<0x141>(v));  // row_half_mirror
