@@ -602,6 +602,85 @@ __global__ __launch_bounds__(kBlock) void rows_short_kernel(const float* __restr
     }
 }
 
+// Short rows that are adjacent in memory (row o at o*R, R < 64): a lane per
+// row reads 16 bytes from each of 64 rows R floats apart per load, so a
+// workgroup instead stages 256 rows at a time through LDS.  The tile's 256*R
+// floats are read with coalesced 16-byte loads (thread t takes float4s
+// t, t + 256, ...) and each float is put at (row, column) of an LDS tile
+// whose pitch is odd (R, or R + 1 for even R), so that thread t then reads
+// row t without bank conflicts.  Thread t folds its row in the order of
+// rows_short_kernel (float4 groups into four accumulators, their join, the
+// R % 4 tail), so both give the same bits.  The (row, column) of a float is
+// the same in every tile and is advanced incrementally (1024 floats per
+// step), with no division per element.  Dynamic LDS: 256 * pitch floats.
+template <int OP>
+__global__ __launch_bounds__(kBlock) void rows_short_tile_kernel(const float* __restrict__ x,
+                                                                 int64_t outer, int32_t R,
+                                                                 int32_t pitch, int32_t TR,
+                                                                 typename St<OP>::Out out) {
+    typedef St<OP> T;
+    extern __shared__ float tile[];
+    const int t = threadIdx.x;
+    // the float4 a thread loads first starts at float 4t of the tile
+    const int row0 = (4 * t) / R;
+    const int col0 = 4 * t - row0 * R;
+    const int drow = (4 * kBlock) / R;  // one step: 1024 floats further
+    const int dcol = 4 * kBlock - drow * R;
+    const int64_t ntiles = (outer + TR - 1) / TR;
+    for (int64_t tb = blockIdx.x; tb < ntiles; tb += gridDim.x) {
+        const int64_t o0 = tb * TR;
+        const int rows = outer - o0 < TR ? int(outer - o0) : TR;
+        const int nf = rows * R;  // floats of this tile (< 16384)
+        const float* base = x + o0 * R;
+        __syncthreads();  // the previous tile's rows have been read
+        int row = row0, col = col0;
+        for (int j = t; 4 * j + 3 < nf; j += kBlock) {
+            const v4f v = load4<true>(base + 4 * j);
+            int r = row, c = col;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tile[r * pitch + c] = v[q];
+                if (++c == R) {
+                    c = 0;
+                    ++r;
+                }
+            }
+            row += drow;
+            col += dcol;
+            if (col >= R) {
+                col -= R;
+                ++row;
+            }
+        }
+        for (int g = (nf & ~3) + t; g < nf; g += kBlock) {  // nf % 4 last floats
+            const int r = g / R;
+            tile[r * pitch + (g - r * R)] = base[g];
+        }
+        __syncthreads();
+        if (t < rows) {
+            const float* rw = tile + t * pitch;
+            typename T::S4 acc = T::start4();
+            int k = 0;
+            for (; k + 4 <= R; k += 4) acc = T::fold(acc, v4f{rw[k], rw[k + 1], rw[k + 2], rw[k + 3]});
+            typename T::S1 v = join_lanes<OP>(acc);
+            for (; k < R; ++k) v = T::fold(v, rw[k]);
+            T::put(out, o0 + t, v);
+        }
+    }
+}
+
+// Rows per LDS tile of rows_short_tile_kernel: 256, 128 or 64, the most
+// whose tile fits 22 KB.  Measured on MI355X, the tile size is what matters
+// (smaller tiles, more workgroups per CU): [4194304, 8] 62 % of peak with 256
+// rows vs 46 % with 128; [2097152, 40] 80 % with 128 vs 54 % with 256;
+// [1048576, 63] 81 % with 64 vs 41 % with 256.
+int32_t short_tile_rows(int64_t R) {
+    const int64_t pitch = R | 1;
+    for (int32_t tr = kBlock; tr > 64; tr /= 2)
+        if (tr * pitch * int64_t(sizeof(float)) <= 22528) return tr;
+    return 64;
+}
+
 // Second pass of ROWS: out[o] = combine_row over the P piece results of row o.
 template <int OP>
 __global__ __launch_bounds__(kBlock) void rows_combine_kernel(typename St<OP>::Out part,
@@ -869,6 +948,15 @@ hipError_t launch(void (*kernel)(K...), int64_t blocks, int threads, hipStream_t
                            dim3(static_cast<uint32_t>(blocks)), dim3(threads), argv, 0, s);
 }
 
+// The same with `lds` bytes of dynamic LDS.
+template <typename... K>
+hipError_t launch_lds(void (*kernel)(K...), int64_t blocks, int threads, size_t lds,
+                      hipStream_t s, typename same<K>::type... args) {
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel),
+                           dim3(static_cast<uint32_t>(blocks)), dim3(threads), argv, lds, s);
+}
+
 int64_t grid_for(int64_t items) {
     int64_t b = (items + kBlock - 1) / kBlock;
     if (b < 1) b = 1;
@@ -1030,6 +1118,15 @@ hipError_t fill_go(Results out, int64_t n, hipStream_t s) {
 template <int OP>
 hipError_t rows_short_go(const float* x, RowMap map, int64_t outer, int64_t R, Results out,
                          hipStream_t s) {
+    if (map.ninner == 1 && map.so == R && R >= 1 && R < kShortRow) {
+        // adjacent rows: staged through LDS, TR rows per tile
+        const int32_t pitch = int32_t(R | 1);
+        const int32_t TR = short_tile_rows(R);
+        const int64_t tiles = (outer + TR - 1) / TR;
+        return launch_lds(rows_short_tile_kernel<OP>, tiles < kMaxBlocks ? tiles : kMaxBlocks,
+                          kBlock, size_t(TR) * pitch * sizeof(float), s, x, outer, int32_t(R),
+                          pitch, TR, out_of<OP>(out));
+    }
     return launch(rows_short_kernel<OP>, grid_for(outer), kBlock, s, x, map, outer, R,
                   out_of<OP>(out));
 }
