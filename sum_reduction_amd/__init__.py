@@ -293,8 +293,16 @@ def rd_reduce_strided(x, outer: int, R: int, inner: int, stride_outer: int, stri
                       stride_inner: int, op="sum", out=None, stream=None):
     """out[o, i] = op over r of x's storage at o*stride_outer + r*stride_r +
     i*stride_inner (floats from x.data_ptr()); ``out`` is [outer, inner].
-    The caller guarantees the view lies inside x's storage."""
+    The view must lie inside x's storage (checked here)."""
     _check_view(x)
+    if min(outer, R, inner) > 0:
+        if min(stride_outer, stride_r, stride_inner) < 0:
+            raise ValueError("strides must be >= 0")
+        last = (outer - 1) * stride_outer + (R - 1) * stride_r + (inner - 1) * stride_inner
+        avail = x.untyped_storage().nbytes() // 4 - x.storage_offset()
+        if last >= avail:
+            raise ValueError("the view reaches float %d past x's start; its storage holds %d"
+                             % (last, avail))
     out = _out_tensor(out, outer * inner, x.device, (outer, inner))
     xp = x.data_ptr() if outer * R * inner else None
     optr = out.data_ptr() if out.numel() else None

@@ -261,3 +261,4 @@ def test_missing_library_fails_loudly(monkeypatch):
         rd.rd_plan_dim(256, 1, 10, 1)
     with pytest.raises((RuntimeError, ValueError)):
         rd.rd_sum_1d(torch.ones(4))
+

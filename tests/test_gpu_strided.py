@@ -154,3 +154,15 @@ def test_views_forced_strided_splits(split):
     with rd.tuning(split=split):
         for op in OPS:
             _run(op, strided, [0, 1, 3], 950 + split, "strided s%d" % split)
+
+
+def test_binding_refuses_views_past_the_storage():
+    """rd_reduce_strided from Python checks the view against the tensor's
+    storage (an offset view included) before calling the library."""
+    t = H.torch()
+    x = t.zeros(1000, device="cuda")[10:]          # 990 floats from x's start
+    rd.rd_reduce_strided(x, 2, 10, 5, 900, 5, 1)   # last = 900 + 45 + 4 = 949: fine
+    with pytest.raises(ValueError):
+        rd.rd_reduce_strided(x, 2, 10, 5, 941, 5, 1)   # last = 990: one past
+    with pytest.raises(ValueError):
+        rd.rd_reduce_strided(x, 2, 10, 5, -1, 5, 1)
