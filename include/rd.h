@@ -199,6 +199,15 @@ rd_status rd_softmax_denom_dim(const float* x, int64_t outer, int64_t R, int64_t
                                float* out_max, float* out_sum, hipStream_t stream);
 rd_status rd_softmax_denom_1d(const float* x, int64_t n, float* out_max, float* out_sum,
                               hipStream_t stream);
+/* The softmax denominator over a strided view: element (o, r, i) at
+ * x[o * stride_outer + r * stride_r + i * stride_inner], with the view rules
+ * of rd_reduce_strided and the outputs and status codes of
+ * rd_softmax_denom_dim (both outputs contiguous [outer, inner], outside the
+ * view's span and each other). */
+rd_status rd_softmax_denom_strided(const float* x, int64_t outer, int64_t R, int64_t inner,
+                                   int64_t stride_outer, int64_t stride_r,
+                                   int64_t stride_inner, float* out_max, float* out_sum,
+                                   hipStream_t stream);
 
 /*
  * Cumulative sum along the middle axis of a contiguous [outer, R, inner]

@@ -26,7 +26,7 @@ __all__ = [
     "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "sum", "tuning",
     "PATH_NAMES", "OPS", "rd_reduce_1d", "rd_reduce_dim", "reduce", "rd_cumsum_dim",
     "rd_plan_cumsum", "cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim",
-    "softmax_denom", "rd_reduce_strided", "rd_plan_strided",
+    "softmax_denom", "rd_reduce_strided", "rd_plan_strided", "rd_softmax_denom_strided",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -110,6 +110,8 @@ def load():
     lib.rd_softmax_denom_1d.restype = ctypes.c_int
     lib.rd_softmax_denom_dim.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     lib.rd_softmax_denom_dim.restype = ctypes.c_int
+    lib.rd_softmax_denom_strided.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, vp, vp]
+    lib.rd_softmax_denom_strided.restype = ctypes.c_int
     lib.rd_reduce_strided.argtypes = [vp, i64, i64, i64, i64, i64, i64, i32, vp, vp]
     lib.rd_reduce_strided.restype = ctypes.c_int
     lib.rd_plan_strided.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64,
@@ -289,12 +291,8 @@ def _check_view(x):
         raise ValueError("x must be float32, got %s" % x.dtype)
 
 
-def rd_reduce_strided(x, outer: int, R: int, inner: int, stride_outer: int, stride_r: int,
-                      stride_inner: int, op="sum", out=None, stream=None):
-    """out[o, i] = op over r of x's storage at o*stride_outer + r*stride_r +
-    i*stride_inner (floats from x.data_ptr()); ``out`` is [outer, inner].
-    The view must lie inside x's storage (checked here)."""
-    _check_view(x)
+def _check_view_span(x, outer, R, inner, stride_outer, stride_r, stride_inner):
+    """The view must lie inside x's storage."""
     if min(outer, R, inner) > 0:
         if min(stride_outer, stride_r, stride_inner) < 0:
             raise ValueError("strides must be >= 0")
@@ -303,6 +301,33 @@ def rd_reduce_strided(x, outer: int, R: int, inner: int, stride_outer: int, stri
         if last >= avail:
             raise ValueError("the view reaches float %d past x's start; its storage holds %d"
                              % (last, avail))
+
+
+def rd_softmax_denom_strided(x, outer: int, R: int, inner: int, stride_outer: int,
+                             stride_r: int, stride_inner: int, out_max=None, out_sum=None,
+                             stream=None):
+    """(m, s) of rd_softmax_denom_dim over a strided view of x's storage
+    (strides in floats from x.data_ptr(); checked against the storage)."""
+    _check_view(x)
+    _check_view_span(x, outer, R, inner, stride_outer, stride_r, stride_inner)
+    out_max = _out_tensor(out_max, outer * inner, x.device, (outer, inner))
+    out_sum = _out_tensor(out_sum, outer * inner, x.device, (outer, inner))
+    xp = x.data_ptr() if outer * R * inner else None
+    mp = out_max.data_ptr() if out_max.numel() else None
+    sp = out_sum.data_ptr() if out_sum.numel() else None
+    _check(load().rd_softmax_denom_strided(xp, outer, R, inner, stride_outer, stride_r,
+                                           stride_inner, mp, sp, _stream_handle(stream)),
+           "rd_softmax_denom_strided")
+    return out_max, out_sum
+
+
+def rd_reduce_strided(x, outer: int, R: int, inner: int, stride_outer: int, stride_r: int,
+                      stride_inner: int, op="sum", out=None, stream=None):
+    """out[o, i] = op over r of x's storage at o*stride_outer + r*stride_r +
+    i*stride_inner (floats from x.data_ptr()); ``out`` is [outer, inner].
+    The view must lie inside x's storage (checked here)."""
+    _check_view(x)
+    _check_view_span(x, outer, R, inner, stride_outer, stride_r, stride_inner)
     out = _out_tensor(out, outer * inner, x.device, (outer, inner))
     xp = x.data_ptr() if outer * R * inner else None
     optr = out.data_ptr() if out.numel() else None
@@ -417,13 +442,22 @@ def rd_softmax_denom_1d(x, out_max=None, out_sum=None, stream=None):
 
 
 def softmax_denom(x, dim: Optional[int] = None, stream=None):
-    """(m, s) over all elements (dim=None, 0-d results) or over one dimension
-    of a contiguous float32 GPU tensor; see rd_softmax_denom_dim."""
+    """(m, s) over all elements (dim=None, 0-d results; x contiguous) or over
+    one dimension of a float32 GPU tensor (a strided view too); see
+    rd_softmax_denom_dim."""
     if dim is None:
         m, s = rd_softmax_denom_1d(x, stream=stream)
         return m.view(()), s.view(())
     shape = tuple(x.shape)
     d = dim % len(shape)
+    if not x.is_contiguous():
+        v = _view3(x, d)
+        if v is None:
+            raise ValueError("this view of x cannot be read as one [outer, R, inner] "
+                             "strided array; make it contiguous first")
+        m, s = rd_softmax_denom_strided(x, *v, stream=stream)
+        rest = shape[:d] + shape[d + 1:]
+        return m.view(rest), s.view(rest)
     outer = 1
     for k in shape[:d]:
         outer *= k

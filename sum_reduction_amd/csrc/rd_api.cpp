@@ -300,6 +300,25 @@ rd_status rd_softmax_denom_dim(const float* x, int64_t outer, int64_t R, int64_t
                           rd::Results{out_max, out_sum}, stream);
 }
 
+rd_status rd_softmax_denom_strided(const float* x, int64_t outer, int64_t R, int64_t inner,
+                                   int64_t stride_outer, int64_t stride_r,
+                                   int64_t stride_inner, float* out_max, float* out_sum,
+                                   hipStream_t stream) {
+    const rd::Strides v{outer, R, inner, stride_outer, stride_r, stride_inner};
+    if (!rd::view_sizes_ok(v)) return RD_ERR_INVALID_ARG;
+    const int64_t nout = outer * inner;
+    if (nout == 0) return RD_OK;  // nothing to write, no HIP call
+    if (nout > INT64_MAX / 8) return RD_ERR_INVALID_ARG;
+    const int64_t span = view_extent(v);
+    if (!out_max || !out_sum || !aligned4(out_max) || !aligned4(out_sum))
+        return RD_ERR_INVALID_ARG;
+    if (span > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
+    if (overlap(x, span, out_max, nout) || overlap(x, span, out_sum, nout) ||
+        overlap(out_max, nout, out_sum, nout))
+        return RD_ERR_INVALID_ARG;
+    return reduce_checked(x, v, RD_OP_SOFTMAX_DENOM, rd::Results{out_max, out_sum}, stream);
+}
+
 rd_status rd_softmax_denom_1d(const float* x, int64_t n, float* out_max, float* out_sum,
                               hipStream_t stream) {
     if (n < 0 || n > INT64_MAX / 8) return RD_ERR_INVALID_ARG;

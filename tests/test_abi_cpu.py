@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
                  "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
                  "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "rd_cumsum_dim",
                  "rd_plan_cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim",
-                 "rd_reduce_strided", "rd_plan_strided"):
+                 "rd_reduce_strided", "rd_plan_strided", "rd_softmax_denom_strided"):
         assert want in names
 
 
@@ -199,6 +199,13 @@ def test_strided_invalid_arguments(lib, host_buf):
     for op in (-1, 4, 7):
         assert lib.rd_reduce_strided(base, 2, 2, 2, 4, 2, 1, op, out, None) == INVALID
     assert lib.rd_reduce_strided(None, 0, 5, 3, 15, 3, 1, 0, None, None) == OK
+    m, s2 = base + 4 * 32, base + 4 * 40
+    for v in ((base, -1, 2, 2, 4, 2, 1, m, s2), (base, 2, 2, 2, 4, -2, 1, m, s2),
+              (base, 2, 2, 2, 4, 2, 1, None, s2), (base, 2, 2, 2, 4, 2, 1, m, None),
+              (base, 2, 2, 2, 4, 2, 1, m, m), (base, 2, 3, 2, 20, 2, 1, base + 4 * 20, s2),
+              (base + 1, 2, 2, 2, 4, 2, 1, m, s2)):
+        assert lib.rd_softmax_denom_strided(*v, None) == INVALID, v
+    assert lib.rd_softmax_denom_strided(None, 0, 5, 3, 15, 3, 1, None, None, None) == OK
     assert lib.rd_reduce_strided(None, 4, 5, 0, 0, 0, 1, 2, None, None) == OK
 
 

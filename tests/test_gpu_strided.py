@@ -166,3 +166,39 @@ def test_binding_refuses_views_past_the_storage():
         rd.rd_reduce_strided(x, 2, 10, 5, 941, 5, 1)   # last = 990: one past
     with pytest.raises(ValueError):
         rd.rd_reduce_strided(x, 2, 10, 5, -1, 5, 1)
+
+
+def test_softmax_denominator_over_views():
+    """rd_softmax_denom_strided on every view: terms 0 / -Inf make both
+    outputs exact (bit-exact against the oracle on a contiguous copy); random
+    data within 1e-5 * s + 1e-6, maxima exact."""
+    lib = rd.load()
+    t = H.torch()
+    for k, (name, n, o, R, i, so, sr, si, _) in enumerate(VIEWS):
+        for kind in ("mask", "normal"):
+            if kind == "mask":
+                bits = workloads.small_ints(n + 4, 960 + k, 0, 1)
+                base = np.where(bits > 0, np.float32(0), np.float32(-np.inf)).astype(np.float32)
+            else:
+                base = workloads.random(n + 4, 970 + k, "normal") * np.float32(6)
+            dev = H.upload(base)
+            slots = H.OutSlots([o * i, o * i])
+            st = lib.rd_softmax_denom_strided(dev.data_ptr() + 4, o, R, i, so, sr, si,
+                                              slots.ptr(0), slots.ptr(1), H.stream_handle())
+            assert st == 0, (name, rd.rd_status_string(st))
+            gm, gs = slots.fetch()
+            M, S = oracle.softmax_denom_dim(_view_host(base, o, R, i, so, sr, si, 1), o, R, i)
+            what = "softmax %s %s" % (kind, name)
+            H.assert_bitwise_equal_oracle(gm, M, what + " (max)")
+            if kind == "mask":
+                H.assert_bitwise_equal_oracle(gs, S, what + " (sum)")
+            else:
+                H.assert_within_tolerance(gs, S, S, what + " (sum)")
+    # torch-style: softmax and log-sum-exp from the pair of a transposed view
+    a = (workloads.random(300 * 500, 980, "normal") * np.float32(3)).reshape(300, 500)
+    x = H.upload(a).view(300, 500)
+    for d in (0, 1):
+        m, s = rd.softmax_denom(x.t(), d)
+        lse = (m + t.log(s)).cpu().numpy()
+        ref = t.logsumexp(t.from_numpy(a.T.astype(np.float64)), d).numpy()
+        assert np.abs(lse - ref).max() <= 1e-5 * (1 + np.abs(ref).max()), d
