@@ -7,8 +7,9 @@
 //    the warp is a 64-lane wavefront here and its reduction a DPP/swizzle
 //    butterfly, and the block results go to a second, fixed-order pass (no
 //    float atomics), so results are bitwise reproducible.  The same page
-//    names sum, max and the L2 norm as one primitive: the kernels take the
-//    operator (sum, sum of squares, maximum, minimum) as a parameter.
+//    names sum, max, the L2 norm and the softmax denominator as one
+//    primitive: the kernels take the operator (sum, sum of squares, maximum,
+//    minimum, the softmax pair) as a parameter, through the state layer St.
 //  * "High-Performance Reduction Kernels" README, ILP4 section: several
 //    independent accumulators and several 128-bit loads in flight per thread.
 //    Kept as U loads in flight per lane.  What limits loads in flight on
@@ -42,10 +43,18 @@
 //  COLS_SMALL  row phase rho folds its k-th row into accumulator (k mod 2);
 //            join(acc[0], acc[1]); then the row phases by a fixed tree (see
 //            cols_small_kernel); then (if split) the slabs in slab order.
+//  ROWS_SHORT  a thread folds its row's float4 groups into one float4
+//            accumulator, joins its lanes, then folds the R % 4 tail
+//            (rows_short_tile_kernel reads the row from LDS, rows_short_kernel
+//            from memory: the same order).
+//  STRIDED   lane (slab, output) folds its terms in r order; then the slabs
+//            in slab order.
 // U, the number of 16-byte loads a lane keeps in flight, is even and does not
 // change the order.  Two accumulators rather than U keep the kernels within
 // 64 VGPRs (8 waves per SIMD) while all U loads are issued before the first
-// fold waits on one.
+// fold waits on one.  (The softmax pair folds a step's U loads at once into
+// accumulator 0: the group's maximum, a lazy re-centring, then the group's
+// exponentials summed by a pairwise tree -- see St<RD_OP_SOFTMAX_DENOM>.)
 #include <hip/hip_runtime.h>
 
 #include "rd_device.h"
