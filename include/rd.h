@@ -232,6 +232,23 @@ rd_status rd_softmax_denom_strided(const float* x, int64_t outer, int64_t R, int
  */
 rd_status rd_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
                         int32_t reverse, float* out, hipStream_t stream);
+/* The cumulative sum of a strided view: term (o, r, i) at
+ * x[o * stride_outer + r * stride_r + i * stride_inner] (strides in floats,
+ * >= 0, the view's furthest element representable in bytes), out the
+ * contiguous [outer, R, inner] array of rd_cumsum_dim.  out must lie outside
+ * the view's span [x, x + furthest element], except out == x when the view
+ * is out's own layout (strides R*inner, inner, 1; those of length-1 axes
+ * ignored).  The kernel follows the unit stride: stride_inner == 1 (inner >
+ * 1) scans columns as rd_cumsum_dim does, with any stride_outer and stride_r;
+ * inner == 1 with stride_r == 1 scans rows; any other view takes one lane per
+ * output column (a slab of it when there are few columns), each term a
+ * 4-byte access (correct, not fast).  A contiguous view gives the bits
+ * rd_cumsum_dim gives.  Status codes as for rd_cumsum_dim.  Source: the
+ * POPCORNBENCH problem-91 trace scans a torch tensor along one dimension
+ * (torch.cumsum over x.flip(1)), which accepts any strided tensor. */
+rd_status rd_cumsum_strided(const float* x, int64_t outer, int64_t R, int64_t inner,
+                            int64_t stride_outer, int64_t stride_r, int64_t stride_inner,
+                            int32_t reverse, float* out, hipStream_t stream);
 
 /* Static, NUL-terminated name of a status code ("RD_OK", ...). */
 const char* rd_status_string(rd_status status);
@@ -264,9 +281,12 @@ typedef enum rd_path {
     RD_PATH_SCAN_COLS_SMALL = 8, /* cumulative sum, 2 <= inner <= 128: several
                                     rows per load instruction, scanned across
                                     the wave */
-    RD_PATH_STRIDED = 9      /* a strided view with no unit stride along the
+    RD_PATH_STRIDED = 9,     /* a strided view with no unit stride along the
                                 reduced or the inner axis: one lane per
                                 output */
+    RD_PATH_SCAN_STRIDED = 10 /* cumulative sum of a view with no unit stride
+                                 along the inner axis (nor, inner == 1, along
+                                 R): one lane per (slab, output column) */
 } rd_path;
 
 /* Chunk order of the pieces of one row on the ROWS path. */
@@ -332,6 +352,13 @@ rd_status rd_plan_strided(int cu_count, int64_t outer, int64_t R, int64_t inner,
  * 4, 8 or 16 -- and nontemporal fields apply). */
 rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
                          rd_plan* plan);
+
+/* The plan rd_cumsum_strided executes for the view (the tuning override's
+ * fields as for rd_plan_cumsum; its path may also force RD_PATH_SCAN_STRIDED,
+ * valid for every view, whose only other field is split). */
+rd_status rd_plan_cumsum_strided(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                                 int64_t stride_outer, int64_t stride_r, int64_t stride_inner,
+                                 rd_plan* plan);
 
 /*
  * Tuning override, process-wide, for measurement and tests: a field left at 0

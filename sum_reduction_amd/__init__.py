@@ -25,8 +25,9 @@ __all__ = [
     "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
     "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "sum", "tuning",
     "PATH_NAMES", "OPS", "rd_reduce_1d", "rd_reduce_dim", "reduce", "rd_cumsum_dim",
-    "rd_plan_cumsum", "cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim",
-    "softmax_denom", "rd_reduce_strided", "rd_plan_strided", "rd_softmax_denom_strided",
+    "rd_plan_cumsum", "cumsum", "rd_cumsum_strided", "rd_plan_cumsum_strided",
+    "rd_softmax_denom_1d", "rd_softmax_denom_dim", "softmax_denom", "rd_reduce_strided",
+    "rd_plan_strided", "rd_softmax_denom_strided",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +41,7 @@ OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
 OP_SOFTMAX_DENOM = 4
 PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
               5: "cols_small", 6: "scan_rows", 7: "scan_cols", 8: "scan_cols_small",
-              9: "strided"}
+              9: "strided", 10: "scan_strided"}
 ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
 COMBINE_NAMES = {0: "none", 1: "pass", 2: "last_block"}
 
@@ -121,6 +122,11 @@ def load():
     lib.rd_cumsum_dim.restype = ctypes.c_int
     lib.rd_plan_cumsum.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(RdPlan)]
     lib.rd_plan_cumsum.restype = ctypes.c_int
+    lib.rd_cumsum_strided.argtypes = [vp, i64, i64, i64, i64, i64, i64, i32, vp, vp]
+    lib.rd_cumsum_strided.restype = ctypes.c_int
+    lib.rd_plan_cumsum_strided.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                           ctypes.POINTER(RdPlan)]
+    lib.rd_plan_cumsum_strided.restype = ctypes.c_int
     lib.rd_status_string.argtypes = [ctypes.c_int]
     lib.rd_status_string.restype = ctypes.c_char_p
     lib.rd_last_hip_error.argtypes = []
@@ -167,6 +173,15 @@ def rd_plan_cumsum(cu_count: int, outer: int, R: int, inner: int) -> RdPlan:
     plan = RdPlan()
     _check(load().rd_plan_cumsum(cu_count, outer, R, inner, ctypes.byref(plan)),
            "rd_plan_cumsum")
+    return plan
+
+
+def rd_plan_cumsum_strided(cu_count: int, outer: int, R: int, inner: int, stride_outer: int,
+                           stride_r: int, stride_inner: int) -> RdPlan:
+    plan = RdPlan()
+    _check(load().rd_plan_cumsum_strided(cu_count, outer, R, inner, stride_outer, stride_r,
+                                         stride_inner, ctypes.byref(plan)),
+           "rd_plan_cumsum_strided")
     return plan
 
 
@@ -483,11 +498,39 @@ def rd_cumsum_dim(x, outer: int, R: int, inner: int, reverse: bool = True, out=N
     return out
 
 
+def rd_cumsum_strided(x, outer: int, R: int, inner: int, stride_outer: int, stride_r: int,
+                      stride_inner: int, reverse: bool = True, out=None, stream=None):
+    """Cumulative sum along R of the view of x's storage with element (o, r, i)
+    at o*stride_outer + r*stride_r + i*stride_inner floats from x.data_ptr()
+    (checked against the storage); ``out`` is the contiguous [outer, R, inner]
+    result (allocated when None)."""
+    _check_view(x)
+    _check_view_span(x, outer, R, inner, stride_outer, stride_r, stride_inner)
+    n = outer * R * inner
+    out = _out_tensor(out, n, x.device, (outer, R, inner))
+    xp = x.data_ptr() if n else None
+    optr = out.data_ptr() if n else None
+    _check(load().rd_cumsum_strided(xp, outer, R, inner, stride_outer, stride_r, stride_inner,
+                                    int(bool(reverse)), optr, _stream_handle(stream)),
+           "rd_cumsum_strided")
+    return out
+
+
 def cumsum(x, dim: int, reverse: bool = False, out=None, stream=None):
     """torch.cumsum(x, dim) (reverse=False) or torch.cumsum(x.flip(dim),
-    dim).flip(dim) (reverse=True) for a contiguous float32 GPU tensor."""
+    dim).flip(dim) (reverse=True) for a float32 GPU tensor; a transposed,
+    sliced or expanded view is read in place (rd_cumsum_strided), the result
+    is contiguous."""
     shape = tuple(x.shape)
     d = dim % len(shape)
+    if not x.is_contiguous():
+        v = _view3(x, d)
+        if v is None:
+            raise ValueError("this view of x cannot be read as one [outer, R, inner] "
+                             "strided array; make it contiguous first")
+        res = rd_cumsum_strided(x, *v, reverse=reverse,
+                                out=None if out is None else out.view(v[:3]), stream=stream)
+        return res.view(shape)
     outer = 1
     for s in shape[:d]:
         outer *= s

@@ -226,6 +226,75 @@ int64_t view_extent(const rd::Strides& v) {
     return (v.outer - 1) * v.so + (v.R - 1) * v.sr + (v.inner - 1) * v.si + 1;
 }
 
+// The cumulative sum of the view v (sizes and pointers already checked, at
+// least one element): plan, workspace, one or three launches.
+rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
+                         hipStream_t stream) {
+    Device* dev = nullptr;
+    rd_status st = current_device(&dev);
+    if (st != RD_OK) return st;
+    rd_plan p;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        st = rd::plan_cumsum_view(dev->cu, &v, g_tune_on ? &g_tune : nullptr, &p);
+    }
+    if (st != RD_OK) return st;
+    if (p.path == RD_PATH_NONE) return RD_OK;
+    if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
+    float* ws = nullptr;
+    if (p.workspace_bytes > 0) {
+        if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
+        hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
+                                              size_t(p.workspace_bytes), dev->pool, stream);
+        if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
+    }
+    const int64_t nrow = v.outer * v.inner;
+    // The totals pass of a split scan reads x without the streaming hint when
+    // x fits in the last-level cache, so that the scan pass re-reads it from
+    // there (measured: 5-11% faster up to 256 MB, 1% slower at 2 GB).
+    rd_plan pt = p;
+    if (uint64_t(nrow * v.R) * sizeof(float) <= rd::kScanCachedTotalsBytes) pt.nontemporal = 0;
+    hipError_t e = hipSuccess;
+    if (p.path == RD_PATH_SCAN_ROWS) {
+        if (p.split == 1) {
+            e = rd::launch_scan_rows(p, rev, x, out, v, nullptr, nullptr, stream);
+        } else {
+            const int64_t m = v.outer * p.split;
+            float* totals = ws;
+            float* carries = ws + m;
+            e = rd::launch_scan_rows(pt, rev, x, out, v, nullptr, totals, stream);
+            if (e == hipSuccess)
+                e = rd::launch_scan_carries(totals, carries, v.outer, p.split, stream);
+            if (e == hipSuccess) e = rd::launch_scan_rows(p, rev, x, out, v, carries, nullptr, stream);
+        }
+    } else {
+        auto cols = [&](const rd_plan& q, const float* carry_in, float* totals) {
+            if (p.path == RD_PATH_SCAN_COLS_SMALL)
+                return rd::launch_scan_small(q, rev, x, out, v, carry_in, totals, stream);
+            if (p.path == RD_PATH_SCAN_COLS)
+                return rd::launch_scan_cols(q, rev, x, out, v, carry_in, totals, stream);
+            return rd::launch_scan_strided(q, rev, x, out, v, carry_in, totals, stream);
+        };
+        if (p.split == 1) {
+            e = cols(p, nullptr, nullptr);
+        } else {
+            const int64_t m = p.split * nrow;
+            float* totals = ws;
+            float* carries = ws + m;
+            e = cols(pt, nullptr, totals);
+            if (e == hipSuccess)
+                e = rd::launch_scan_slab_carries(rev, totals, carries, p.split, nrow, stream);
+            if (e == hipSuccess) e = cols(p, carries, nullptr);
+        }
+    }
+    if (ws) {
+        hipError_t f = hipFreeAsync(ws, stream);
+        if (e == hipSuccess && f != hipSuccess) return hip_fail(f, RD_ERR_HIP);
+    }
+    if (e != hipSuccess) return hip_fail(e, RD_ERR_LAUNCH);
+    return RD_OK;
+}
+
 bool op_valid(int32_t op) { return op >= RD_OP_SUM && op <= RD_OP_MIN; }
 
 }  // namespace
@@ -336,74 +405,37 @@ rd_status rd_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
     if (n == 0) return RD_OK;  // nothing to write, no HIP call
     if (!x || !out || !aligned4(x) || !aligned4(out)) return RD_ERR_INVALID_ARG;
     if (out != x && overlap(x, n, out, n)) return RD_ERR_INVALID_ARG;
-    Device* dev = nullptr;
-    rd_status st = current_device(&dev);
-    if (st != RD_OK) return st;
-    rd_plan p;
-    {
-        std::lock_guard<std::mutex> lock(g_tune_mu);
-        st = rd::plan_cumsum(dev->cu, outer, R, inner, g_tune_on ? &g_tune : nullptr, &p);
-    }
-    if (st != RD_OK) return st;
-    if (p.path == RD_PATH_NONE) return RD_OK;
-    if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
-    float* ws = nullptr;
-    if (p.workspace_bytes > 0) {
-        if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
-        hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
-                                              size_t(p.workspace_bytes), dev->pool, stream);
-        if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
-    }
-    const bool rev = reverse != 0;
-    // The totals pass of a split scan reads x without the streaming hint when
-    // x fits in the last-level cache, so that the scan pass re-reads it from
-    // there (measured: 5-11% faster up to 256 MB, 1% slower at 2 GB).
-    rd_plan pt = p;
-    if (uint64_t(n) * sizeof(float) <= rd::kScanCachedTotalsBytes) pt.nontemporal = 0;
-    hipError_t e = hipSuccess;
-    if (p.path == RD_PATH_SCAN_ROWS) {
-        if (p.split == 1) {
-            e = rd::launch_scan_rows(p, rev, x, out, outer, R, nullptr, nullptr, stream);
-        } else {
-            const int64_t m = outer * p.split;
-            float* totals = ws;
-            float* carries = ws + m;
-            e = rd::launch_scan_rows(pt, rev, x, out, outer, R, nullptr, totals, stream);
-            if (e == hipSuccess) e = rd::launch_scan_carries(totals, carries, outer, p.split, stream);
-            if (e == hipSuccess)
-                e = rd::launch_scan_rows(p, rev, x, out, outer, R, carries, nullptr, stream);
-        }
-    } else {
-        const bool small = p.path == RD_PATH_SCAN_COLS_SMALL;
-        auto cols = [&](const rd_plan& q, const float* carry_in, float* totals) {
-            return small ? rd::launch_scan_small(q, rev, x, out, outer, R, inner, carry_in, totals,
-                                                 stream)
-                         : rd::launch_scan_cols(q, rev, x, out, outer, R, inner, carry_in, totals,
-                                                stream);
-        };
-        if (p.split == 1) {
-            e = cols(p, nullptr, nullptr);
-        } else {
-            const int64_t m = p.split * nrow;
-            float* totals = ws;
-            float* carries = ws + m;
-            e = cols(pt, nullptr, totals);
-            if (e == hipSuccess)
-                e = rd::launch_scan_slab_carries(rev, totals, carries, p.split, nrow, stream);
-            if (e == hipSuccess) e = cols(p, carries, nullptr);
-        }
-    }
-    if (ws) {
-        hipError_t f = hipFreeAsync(ws, stream);
-        if (e == hipSuccess && f != hipSuccess) return hip_fail(f, RD_ERR_HIP);
-    }
-    if (e != hipSuccess) return hip_fail(e, RD_ERR_LAUNCH);
-    return RD_OK;
+    return cumsum_checked(x, contiguous(outer, R, inner), reverse != 0, out, stream);
+}
+
+rd_status rd_cumsum_strided(const float* x, int64_t outer, int64_t R, int64_t inner,
+                            int64_t stride_outer, int64_t stride_r, int64_t stride_inner,
+                            int32_t reverse, float* out, hipStream_t stream) {
+    const rd::Strides v{outer, R, inner, stride_outer, stride_r, stride_inner};
+    if (!rd::view_sizes_ok(v)) return RD_ERR_INVALID_ARG;
+    const int64_t n = outer * R * inner;
+    if (n == 0) return RD_OK;  // nothing to write, no HIP call
+    if (!x || !out || !aligned4(x) || !aligned4(out)) return RD_ERR_INVALID_ARG;
+    // in place only where the view is the output's own layout
+    const bool same_layout = (inner == 1 || stride_inner == 1) &&
+                             (R == 1 || stride_r == inner) &&
+                             (outer == 1 || stride_outer == R * inner);
+    if (!(out == x && same_layout) && overlap(x, view_extent(v), out, n))
+        return RD_ERR_INVALID_ARG;
+    return cumsum_checked(x, v, reverse != 0, out, stream);
 }
 
 rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner, rd_plan* plan) {
     std::lock_guard<std::mutex> lock(g_tune_mu);
     return rd::plan_cumsum(cu_count, outer, R, inner, g_tune_on ? &g_tune : nullptr, plan);
+}
+
+rd_status rd_plan_cumsum_strided(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                                 int64_t stride_outer, int64_t stride_r, int64_t stride_inner,
+                                 rd_plan* plan) {
+    rd::Strides v{outer, R, inner, stride_outer, stride_r, stride_inner};
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return rd::plan_cumsum_view(cu_count, &v, g_tune_on ? &g_tune : nullptr, plan);
 }
 
 rd_status rd_sum_1d(const float* x, int64_t n, float* out, hipStream_t stream) {

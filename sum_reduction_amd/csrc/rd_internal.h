@@ -77,25 +77,37 @@ hipError_t launch_strided(int op, const rd_plan& p, const float* x, const Stride
 hipError_t launch_slab_combine(int op, Results slab, int64_t S, int64_t n, Results out,
                                hipStream_t s);
 
-// Cumulative sums (rd_scan.hip).  Rows (inner == 1): item = (row, piece of
-// p.rows_per_split processing positions); totals != nullptr writes only the
-// piece totals, otherwise pieces are scanned from carry_in (nullptr: 0).
+// Cumulative sums (rd_scan.hip).  The input is a view (Strides: element
+// (o, r, i) at x[o*so + r*sr + i*si]; a contiguous array has so = R*inner,
+// sr = inner, si = 1); the output is the contiguous [outer, R, inner] array.
+// Rows (inner == 1, sr == 1): item = (row, piece of p.rows_per_split
+// processing positions); totals != nullptr writes only the piece totals,
+// otherwise pieces are scanned from carry_in (nullptr: 0).
 hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, float* out,
-                            int64_t outer, int64_t R, const float* carry_in, float* totals,
+                            const Strides& v, const float* carry_in, float* totals,
                             hipStream_t s);
 hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows, int64_t P,
                                hipStream_t s);
-// Columns (inner >= 2): item = (64 lane-columns, slab of R, outer index).
+// Columns (inner >= 2, si == 1): item = (64 lane-columns, slab of R, outer index).
 hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, float* out,
-                            int64_t outer, int64_t R, int64_t inner, const float* carry_in,
-                            float* totals, hipStream_t s);
+                            const Strides& v, const float* carry_in, float* totals,
+                            hipStream_t s);
 hipError_t launch_scan_small(const rd_plan& p, bool reverse, const float* x, float* out,
-                             int64_t outer, int64_t R, int64_t inner, const float* carry_in,
-                             float* totals, hipStream_t s);
+                             const Strides& v, const float* carry_in, float* totals,
+                             hipStream_t s);
 hipError_t launch_scan_slab_carries(bool reverse, const float* totals, float* carries, int64_t S,
                                     int64_t n, hipStream_t s);
+// Any strides: a lane per (slab, output column); slab totals and carries
+// laid out as those of launch_scan_cols.
+hipError_t launch_scan_strided(const rd_plan& p, bool reverse, const float* x, float* out,
+                               const Strides& v, const float* carry_in, float* totals,
+                               hipStream_t s);
 
-// Planner of the cumulative sum (rd_plan.cpp).
+// Planner of the cumulative sum (rd_plan.cpp): plan_cumsum_view normalises
+// the strides of length-1 axes in *v, then picks the rows scan (inner == 1,
+// sr == 1), the column scans (inner > 1, si == 1) or the lane-per-column
+// kernel; the launches must use the normalised view.
+rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* tune, rd_plan* plan);
 rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
                       const rd_tune* tune, rd_plan* plan);
 // Row pieces of the row scan are whole multiples of kScanTile positions (a

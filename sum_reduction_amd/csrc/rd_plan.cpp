@@ -338,14 +338,52 @@ rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op
     return plan_view(cu_count, &v, op, tune, plan);
 }
 
-rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
-                      const rd_tune* t, rd_plan* p) {
-    if (!p || cu_count < 1 || outer < 0 || R < 0 || inner < 0) return RD_ERR_INVALID_ARG;
-    memset(p, 0, sizeof(*p));
-    const int64_t lim = INT64_MAX / 4;
-    if (outer && R && inner) {
-        if (R > lim / outer || inner > lim / (outer * R)) return RD_ERR_INVALID_ARG;
+namespace {
+
+// The lane-per-column scan: columns split along R into slabs as the strided
+// reduction's outputs are (about kStridedLanesPerCu lanes per CU, at least
+// kStridedMinRows rows per slab); then slab totals, their scan, the scan from
+// the carries.
+rd_status plan_scan_strided(int64_t cu, int64_t outer, int64_t R, int64_t inner,
+                            const rd_tune* t, rd_plan* p) {
+    if (t && (t->group || t->col_waves || t->row_waves || t->unroll || t->order || t->combine))
+        return RD_ERR_INVALID_ARG;
+    const int64_t n = outer * inner;
+    int64_t S = 1;
+    if (t && t->split) {
+        S = t->split;
+    } else if (n < cu * kStridedLanesPerCu) {
+        S = ceil_div(cu * kStridedLanesPerCu, n);
+        int64_t cap = R / kStridedMinRows;
+        if (cap < 1) cap = 1;
+        if (S > cap) S = cap;
     }
+    if (S < 1) return RD_ERR_INVALID_ARG;
+    split_rows(R, S, p);
+    if (p->split > INT64_MAX / 8 / n) return RD_ERR_INVALID_ARG;
+    p->path = RD_PATH_SCAN_STRIDED;
+    p->nontemporal = 0;  // neighbouring lanes and rows share lines: keep them cached
+    p->blocks = ceil_div(p->split * n, kBlock);
+    if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
+    if (p->split > 1) {
+        p->passes = 3;
+        p->combine = RD_COMBINE_PASS;
+        p->workspace_bytes = 2 * p->split * n * int64_t(sizeof(float));
+    }
+    return RD_OK;
+}
+
+}  // namespace
+
+rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* p) {
+    if (!p || !v || cu_count < 1 || !view_sizes_ok(*v)) return RD_ERR_INVALID_ARG;
+    memset(p, 0, sizeof(*p));
+    // strides of axes of length 1 never move (the output is laid out in the
+    // view's own order, so no axes are exchanged as for reductions)
+    if (v->inner == 1) v->si = 1;
+    if (v->R == 1) v->sr = 1;
+    if (v->outer == 1) v->so = 0;
+    const int64_t outer = v->outer, R = v->R, inner = v->inner;
     p->nxcd = nxcd_for(cu_count);
     p->split = 1;
     if (outer == 0 || R == 0 || inner == 0) {
@@ -357,6 +395,12 @@ rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
     p->passes = 1;
     const int64_t cu = cu_count;
     const int32_t forced = t ? t->path : 0;
+    const bool rows_ok = inner == 1 && v->sr == 1;
+    const bool cols_ok = inner > 1 && v->si == 1;
+    if (forced == RD_PATH_SCAN_STRIDED || (!rows_ok && !cols_ok))
+        return forced && forced != RD_PATH_SCAN_STRIDED
+                   ? RD_ERR_INVALID_ARG
+                   : plan_scan_strided(cu, outer, R, inner, t, p);
     if (inner == 1 ? (forced && forced != RD_PATH_SCAN_ROWS)
                    : (forced && forced != RD_PATH_SCAN_COLS && forced != RD_PATH_SCAN_COLS_SMALL))
         return RD_ERR_INVALID_ARG;
@@ -466,6 +510,20 @@ rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
         p->workspace_bytes = 2 * p->split * outer * inner * int64_t(sizeof(float));
     }
     return RD_OK;
+}
+
+rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
+                      const rd_tune* t, rd_plan* p) {
+    if (!p || cu_count < 1 || outer < 0 || R < 0 || inner < 0) return RD_ERR_INVALID_ARG;
+    // outer * R * inner * 4 must be representable
+    const int64_t lim = INT64_MAX / 4;
+    if (outer && R && inner) {
+        if (R > lim / outer || inner > lim / (outer * R)) return RD_ERR_INVALID_ARG;
+    } else if (outer && inner && inner > lim / outer) {
+        return RD_ERR_INVALID_ARG;
+    }
+    Strides v{outer, R, inner, R * inner, inner, 1};
+    return plan_cumsum_view(cu_count, &v, t, p);
 }
 
 }  // namespace rd

@@ -209,11 +209,13 @@ constexpr int scan_rows_waves_per_simd() { return K <= 4 ? 8 : 4; }
 // multiple of the chunk.  One wave per item; the block's waves take
 // consecutive items.  totals != null: only the piece total (the final carry)
 // goes to totals[item]; otherwise the piece is scanned from carry
-// carry_in[item] (0 when carry_in is null) into out.  x and out may be the
-// same array: every element is loaded, then stored, by the same lane.
+// carry_in[item] (0 when carry_in is null) into out.  Row o of x starts at
+// x + o*so (so = R for a contiguous array), row o of out at out + o*R.  x and
+// out may be the same array: every element is loaded, then stored, by the
+// same lane.
 template <bool REV, int K, bool NT>
 __global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_rows_kernel(
-    const float* x, float* out, int64_t outer, int64_t R,
+    const float* x, float* out, int64_t outer, int64_t R, int64_t so,
     int64_t P, int64_t L, const float* __restrict__ carry_in, float* __restrict__ totals) {
     constexpr int kWaves = kBlock / kWave;
     const int wave = threadIdx.x / kWave;
@@ -227,9 +229,9 @@ __global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_ro
         const int64_t q_end = q_begin + L < R ? q_begin + L : R;
         if (totals == nullptr) {
             const float carry = carry_in != nullptr ? carry_in[item] : 0.f;
-            rows_piece<REV, K, NT, true>(x + o * R, out + o * R, R, q_begin, q_end, lane, carry);
+            rows_piece<REV, K, NT, true>(x + o * so, out + o * R, R, q_begin, q_end, lane, carry);
         } else {
-            const float t = rows_piece<REV, K, NT, false>(x + o * R, nullptr, R, q_begin, q_end,
+            const float t = rows_piece<REV, K, NT, false>(x + o * so, nullptr, R, q_begin, q_end,
                                                           lane, 0.f);
             if (lane == 0) totals[item] = t;
         }
@@ -285,18 +287,19 @@ __device__ __forceinline__ void store_cols(float* q, int keep, v4f acc) {
 // One group step of a lane-column: issue the loads of the U rows at element
 // offset off_load into `next`, then add the U rows of `cur` (rows at off_cur)
 // to the running sums and store each; then meet the block's other waves.
+// pl: the first row of the group to load (rows pstep floats apart in x);
+// qc: the first output row of the group in `cur` (qstep floats apart in out).
 template <int V, int U, bool NT>
-__device__ __forceinline__ v4f cols_step(const float* p, float* q, int64_t off_cur,
-                                         int64_t off_load, int64_t dstep, int keep,
-                                         bool scan_out, const v4f (&cur)[U], v4f (&next)[U],
-                                         v4f acc) {
+__device__ __forceinline__ v4f cols_step(const float* pl, float* qc, int64_t pstep,
+                                         int64_t qstep, int keep, bool scan_out,
+                                         const v4f (&cur)[U], v4f (&next)[U], v4f acc) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) next[u] = loadv<V, NT>(p + off_load + u * dstep, 0.f);
+    for (int u = 0; u < U; ++u) next[u] = loadv<V, NT>(pl + u * pstep, 0.f);
     __builtin_amdgcn_sched_barrier(0);  // the loads go out before the adds (as in rows_step)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         acc += cur[u];
-        if (scan_out) store_cols<V, NT>(q + off_cur + u * dstep, keep, acc);
+        if (scan_out) store_cols<V, NT>(qc + u * qstep, keep, acc);
     }
     __syncthreads();
     return acc;
@@ -314,12 +317,13 @@ __device__ __forceinline__ v4f cols_step(const float* p, float* q, int64_t off_c
 // apart, so they leave the L2 whole.  Each step issues the next group's loads
 // before adding and storing the current group (two buffers in turn).
 // totals != null: only the slab totals go to totals[s][o][i]; otherwise the
-// slab is scanned from carry_in[s][o][i] (0 when null) into out.  x and out
-// may be the same array.
+// slab is scanned from carry_in[s][o][i] (0 when null) into out.  Element
+// (o, r, c) of x is at x + o*so + r*sr + c (a contiguous array: so = R*inner,
+// sr = inner); out is contiguous.  x and out may be the same array.
 template <bool REV, int V, int U, int BW, bool NT>
 __global__ __launch_bounds__(BW * kWave) void scan_cols_kernel(
     const float* x, float* out, int64_t outer, int64_t R,
-    int64_t inner, int64_t ntiles, int64_t S, int64_t rps,
+    int64_t inner, int64_t so, int64_t sr, int64_t ntiles, int64_t S, int64_t rps,
     const float* __restrict__ carry_in, float* __restrict__ totals, uint32_t nxcd) {
     constexpr int kWaves = BW;
     const int wave = threadIdx.x / kWave;
@@ -349,49 +353,51 @@ __global__ __launch_bounds__(BW * kWave) void scan_cols_kernel(
         const int64_t cbase = (s * outer + o) * inner + cl;
         v4f acc = {0.f, 0.f, 0.f, 0.f};
         if (live && scan_out && carry_in != nullptr) acc = loadv<V, false>(carry_in + cbase, 0.f);
-        // the k-th row in processing order is first + k*dstep (in elements)
+        // the k-th row in processing order is x row first + k*dir: pstep
+        // floats apart in x, qstep in out
         const int64_t first = REV ? r_end - 1 : r_begin;
-        const int64_t dstep = REV ? -inner : inner;
-        const float* p = x + (o * R + first) * inner + cl;
+        const int64_t pstep = REV ? -sr : sr;
+        const int64_t qstep = REV ? -inner : inner;
+        const float* p = x + o * so + first * sr + cl;
         float* q = out + (o * R + first) * inner + cl;
         if (ngroups > 0) {
             v4f a[U], b[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) a[u] = loadv<V, NT>(p + u * dstep, 0.f);
+            for (int u = 0; u < U; ++u) a[u] = loadv<V, NT>(p + u * pstep, 0.f);
             int64_t g = 0;
             for (; g + 2 < ngroups; g += 2) {  // groups g, g + 1; loads g + 1, g + 2
-                const int64_t off0 = g * U * dstep;
-                const int64_t off1 = off0 + U * dstep;
-                acc = cols_step<V, U, NT>(p, q, off0, off1, dstep, keep, scan_out, a, b, acc);
-                acc = cols_step<V, U, NT>(p, q, off1, off1 + U * dstep, dstep, keep, scan_out, b,
-                                          a, acc);
+                const float* p1 = p + (g + 1) * U * pstep;
+                float* q0 = q + g * U * qstep;
+                acc = cols_step<V, U, NT>(p1, q0, pstep, qstep, keep, scan_out, a, b, acc);
+                acc = cols_step<V, U, NT>(p1 + U * pstep, q0 + U * qstep, pstep, qstep, keep,
+                                          scan_out, b, a, acc);
             }
             // one or two groups left, the first in a (a barrier after each)
-            const int64_t off0 = g * U * dstep;
+            float* q0 = q + g * U * qstep;
             if (g + 1 < ngroups) {
-                acc = cols_step<V, U, NT>(p, q, off0, off0 + U * dstep, dstep, keep, scan_out, a,
-                                          b, acc);
+                acc = cols_step<V, U, NT>(p + (g + 1) * U * pstep, q0, pstep, qstep, keep,
+                                          scan_out, a, b, acc);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     acc += b[u];
-                    if (scan_out) store_cols<V, NT>(q + off0 + (U + u) * dstep, keep, acc);
+                    if (scan_out) store_cols<V, NT>(q0 + (U + u) * qstep, keep, acc);
                 }
             } else {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     acc += a[u];
-                    if (scan_out) store_cols<V, NT>(q + off0 + u * dstep, keep, acc);
+                    if (scan_out) store_cols<V, NT>(q0 + u * qstep, keep, acc);
                 }
             }
             __syncthreads();
-            p += ngroups * U * dstep;
-            q += ngroups * U * dstep;
+            p += ngroups * U * pstep;
+            q += ngroups * U * qstep;
         }
         for (int64_t k = ngroups * U; k < m; ++k) {
             acc += loadv<V, NT>(p, 0.f);
             if (scan_out) store_cols<V, NT>(q, keep, acc);
-            p += dstep;
-            q += dstep;
+            p += pstep;
+            q += qstep;
         }
         if (!scan_out)
             for (int j = keep; j < V; ++j) totals[cbase + j] = acc[j];
@@ -433,11 +439,14 @@ __device__ __forceinline__ float phase_last(float v, int lc, int LC, int RPW) {
 // are issued before the current one is scanned and stored.  Lanes past RPW*LC
 // shadow the last row phase (valid loads) and store nothing.  Order of the
 // adds: Hillis-Steele over the phases, then carry + that.
+// Element (o, r, c) of x is at x + o*so + r*sr + c (a contiguous array: so =
+// R*inner, sr = inner, when each instruction reads RPW*inner contiguous
+// floats); out is contiguous.
 template <bool REV, int V, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void scan_small_kernel(
-    const float* x, float* out, int64_t outer, int64_t R, int64_t inner, int64_t S,
-    int64_t rps, int32_t LC, const float* __restrict__ carry_in, float* __restrict__ totals,
-    uint32_t nxcd) {
+    const float* x, float* out, int64_t outer, int64_t R, int64_t inner, int64_t so,
+    int64_t sr, int64_t S, int64_t rps, int32_t LC, const float* __restrict__ carry_in,
+    float* __restrict__ totals, uint32_t nxcd) {
     constexpr int kWaves = kBlock / kWave;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
@@ -464,10 +473,12 @@ __global__ __launch_bounds__(kBlock) void scan_small_kernel(
         // processing position k of this lane in instruction g: g*RPW + rho;
         // its row is first + k*dir
         const int64_t first = REV ? r_end - 1 : r_begin;
-        const int64_t dstep = REV ? -inner : inner;
-        const float* p = x + (o * R + first) * inner + cl + int64_t(rho) * dstep;
-        float* q = out + (o * R + first) * inner + cl + int64_t(rho) * dstep;
-        const int64_t istep = int64_t(RPW) * dstep;  // elements per instruction
+        const int64_t pstep = REV ? -sr : sr;        // rows apart in x
+        const int64_t qstep = REV ? -inner : inner;  // rows apart in out
+        const float* p = x + o * so + first * sr + cl + int64_t(rho) * pstep;
+        float* q = out + (o * R + first) * inner + cl + int64_t(rho) * qstep;
+        const int64_t istep = int64_t(RPW) * pstep;  // x elements per instruction
+        const int64_t ostep = int64_t(RPW) * qstep;  // out elements per instruction
         const int64_t nfull = m / RPW;               // instructions with every phase valid
         const int64_t nsteps = nfull / U;
 
@@ -490,13 +501,13 @@ __global__ __launch_bounds__(kBlock) void scan_small_kernel(
                 for (int u = 0; u < U; ++u) b[u] = loadv<V, NT>(p + ((g + 1) * U + u) * istep, 0.f);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < U; ++u) scan_one(a[u], q + (g * U + u) * istep, true);
+                for (int u = 0; u < U; ++u) scan_one(a[u], q + (g * U + u) * ostep, true);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < U; ++u) a[u] = loadv<V, NT>(p + ((g + 2) * U + u) * istep, 0.f);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < U; ++u) scan_one(b[u], q + ((g + 1) * U + u) * istep, true);
+                for (int u = 0; u < U; ++u) scan_one(b[u], q + ((g + 1) * U + u) * ostep, true);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (g + 1 < nsteps) {  // two steps left
@@ -504,19 +515,19 @@ __global__ __launch_bounds__(kBlock) void scan_small_kernel(
                 for (int u = 0; u < U; ++u) b[u] = loadv<V, NT>(p + ((g + 1) * U + u) * istep, 0.f);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < U; ++u) scan_one(a[u], q + (g * U + u) * istep, true);
+                for (int u = 0; u < U; ++u) scan_one(a[u], q + (g * U + u) * ostep, true);
 #pragma unroll
-                for (int u = 0; u < U; ++u) scan_one(b[u], q + ((g + 1) * U + u) * istep, true);
+                for (int u = 0; u < U; ++u) scan_one(b[u], q + ((g + 1) * U + u) * ostep, true);
             } else {
 #pragma unroll
-                for (int u = 0; u < U; ++u) scan_one(a[u], q + (g * U + u) * istep, true);
+                for (int u = 0; u < U; ++u) scan_one(a[u], q + (g * U + u) * ostep, true);
             }
         }
         // the remaining instructions, the last one possibly partial
         for (int64_t g = nsteps * U; g * RPW < m; ++g) {
             const bool valid = g * RPW + rho < m;
             const v4f v = valid ? loadv<V, NT>(p + g * istep, 0.f) : v4f{0.f, 0.f, 0.f, 0.f};
-            scan_one(v, q + g * istep, valid);
+            scan_one(v, q + g * ostep, valid);
         }
         if (!scan_out && rho_raw == 0)
             for (int j = keep; j < V; ++j) totals[cbase + j] = carry[j];
@@ -573,6 +584,63 @@ __global__ __launch_bounds__(kBlock) void scan_slab_carries_kernel(
     }
 }
 
+// Views with no unit stride along the columns (nor, when inner == 1, along
+// R): a lane per (slab s, output column e = o*inner + i), columns fastest.
+// The lane adds the slab's terms x[o*so + r*sr + i*si] one after the other in
+// processing order (REV: from the slab's last row), 8 loads in flight, and
+// stores each prefix at out[(o*R + r)*inner + i].  totals != null: only the
+// slab total goes to totals[s*n + e]; otherwise the slab is scanned from
+// carry_in[s*n + e] (0 when null).  Plain loads and stores: the lines a lane
+// touches are often the ones its neighbours touch next, or itself at the
+// next row, and are found again in the cache.
+template <bool REV>
+__global__ __launch_bounds__(kBlock) void scan_strided_kernel(
+    const float* x, float* out, int64_t outer, int64_t R,
+    int64_t inner, int64_t so, int64_t sr, int64_t si, int64_t S, int64_t rps,
+    const float* __restrict__ carry_in, float* __restrict__ totals) {
+    constexpr int kLoads = 8;
+    const bool scan_out = totals == nullptr;
+    const int64_t n = outer * inner;
+    const int64_t nitems = S * n;
+    const int64_t stride = int64_t(gridDim.x) * kBlock;
+    for (int64_t item = int64_t(blockIdx.x) * kBlock + threadIdx.x; item < nitems;
+         item += stride) {
+        const int64_t s = item / n;
+        const int64_t e = item - s * n;
+        const int64_t o = e / inner;
+        const int64_t i = e - o * inner;
+        const int64_t r_begin = s * rps;
+        const int64_t r_end = r_begin + rps < R ? r_begin + rps : R;
+        const int64_t m = r_end > r_begin ? r_end - r_begin : 0;
+        const int64_t first = REV ? r_end - 1 : r_begin;
+        const int64_t pstep = REV ? -sr : sr;
+        const int64_t qstep = REV ? -inner : inner;
+        const float* p = x + o * so + first * sr + i * si;
+        float* q = out + (o * R + first) * inner + i;
+        float acc = scan_out && carry_in != nullptr ? carry_in[item] : 0.f;
+        int64_t k = 0;
+        for (; k + kLoads <= m; k += kLoads) {
+            float v[kLoads];
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) v[u] = p[u * pstep];
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) {
+                acc += v[u];
+                if (scan_out) q[u * qstep] = acc;
+            }
+            p += kLoads * pstep;
+            q += kLoads * qstep;
+        }
+        for (; k < m; ++k) {
+            acc += *p;
+            if (scan_out) *q = acc;
+            p += pstep;
+            q += qstep;
+        }
+        if (!scan_out) totals[item] = acc;
+    }
+}
+
 // ------------------------------------------------------------ launching
 template <typename T>
 struct same {
@@ -594,94 +662,95 @@ int64_t grid_for(int64_t items) {
 }
 
 template <bool REV, int K>
-hipError_t rows_k(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
+hipError_t rows_k(const rd_plan& p, const float* x, float* out, const Strides& v,
                   const float* carry_in, float* totals, hipStream_t s) {
     if (p.nontemporal)
-        return launch(scan_rows_kernel<REV, K, true>, p.blocks, kBlock, s, x, out, outer, R,
-                      p.split, p.rows_per_split, carry_in, totals);
-    return launch(scan_rows_kernel<REV, K, false>, p.blocks, kBlock, s, x, out, outer, R,
-                  p.split, p.rows_per_split, carry_in, totals);
+        return launch(scan_rows_kernel<REV, K, true>, p.blocks, kBlock, s, x, out, v.outer, v.R,
+                      v.so, p.split, p.rows_per_split, carry_in, totals);
+    return launch(scan_rows_kernel<REV, K, false>, p.blocks, kBlock, s, x, out, v.outer, v.R,
+                  v.so, p.split, p.rows_per_split, carry_in, totals);
 }
 
 template <bool REV>
-hipError_t rows_go(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
+hipError_t rows_go(const rd_plan& p, const float* x, float* out, const Strides& v,
                    const float* carry_in, float* totals, hipStream_t s) {
-    if (p.unroll == 8) return rows_k<REV, 8>(p, x, out, outer, R, carry_in, totals, s);
-    return rows_k<REV, 4>(p, x, out, outer, R, carry_in, totals, s);
+    if (p.unroll == 8) return rows_k<REV, 8>(p, x, out, v, carry_in, totals, s);
+    return rows_k<REV, 4>(p, x, out, v, carry_in, totals, s);
 }
 
 template <bool REV, int V, int BW, bool NT>
-hipError_t cols_bw(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
-                   int64_t inner, int64_t ntiles, const float* carry_in, float* totals,
-                   hipStream_t s) {
+hipError_t cols_bw(const rd_plan& p, const float* x, float* out, const Strides& v,
+                   int64_t ntiles, const float* carry_in, float* totals, hipStream_t s) {
     const uint32_t nx = uint32_t(p.nxcd);
     if (p.unroll == 16)
         return launch(scan_cols_kernel<REV, V, 16, BW, NT>, p.blocks, BW * kWave, s, x, out,
-                      outer, R, inner, ntiles, p.split, p.rows_per_split, carry_in, totals, nx);
+                      v.outer, v.R, v.inner, v.so, v.sr, ntiles, p.split, p.rows_per_split,
+                      carry_in, totals, nx);
     if (p.unroll == 8)
         return launch(scan_cols_kernel<REV, V, 8, BW, NT>, p.blocks, BW * kWave, s, x, out,
-                      outer, R, inner, ntiles, p.split, p.rows_per_split, carry_in, totals, nx);
-    return launch(scan_cols_kernel<REV, V, 4, BW, NT>, p.blocks, BW * kWave, s, x, out, outer,
-                  R, inner, ntiles, p.split, p.rows_per_split, carry_in, totals, nx);
+                      v.outer, v.R, v.inner, v.so, v.sr, ntiles, p.split, p.rows_per_split,
+                      carry_in, totals, nx);
+    return launch(scan_cols_kernel<REV, V, 4, BW, NT>, p.blocks, BW * kWave, s, x, out, v.outer,
+                  v.R, v.inner, v.so, v.sr, ntiles, p.split, p.rows_per_split, carry_in, totals,
+                  nx);
 }
 
 template <bool REV, int V, bool NT>
-hipError_t cols_go(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
-                   int64_t inner, const float* carry_in, float* totals, hipStream_t s) {
-    const int64_t lane_cols = inner >= 4 ? (inner + 3) / 4 : 1;
+hipError_t cols_go(const rd_plan& p, const float* x, float* out, const Strides& v,
+                   const float* carry_in, float* totals, hipStream_t s) {
+    const int64_t lane_cols = v.inner >= 4 ? (v.inner + 3) / 4 : 1;
     const int64_t ntiles = (lane_cols + kWave - 1) / kWave;
     if (p.col_waves == 16)
-        return cols_bw<REV, V, 16, NT>(p, x, out, outer, R, inner, ntiles, carry_in, totals, s);
-    if (p.col_waves == 8)
-        return cols_bw<REV, V, 8, NT>(p, x, out, outer, R, inner, ntiles, carry_in, totals, s);
-    return cols_bw<REV, V, 4, NT>(p, x, out, outer, R, inner, ntiles, carry_in, totals, s);
+        return cols_bw<REV, V, 16, NT>(p, x, out, v, ntiles, carry_in, totals, s);
+    if (p.col_waves == 8) return cols_bw<REV, V, 8, NT>(p, x, out, v, ntiles, carry_in, totals, s);
+    return cols_bw<REV, V, 4, NT>(p, x, out, v, ntiles, carry_in, totals, s);
 }
 
 template <bool REV, bool NT>
-hipError_t cols_v(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
-                  int64_t inner, const float* carry_in, float* totals, hipStream_t s) {
-    if (inner == 2) return cols_go<REV, 2, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
-    if (inner == 3) return cols_go<REV, 3, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
-    return cols_go<REV, 4, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
+hipError_t cols_v(const rd_plan& p, const float* x, float* out, const Strides& v,
+                  const float* carry_in, float* totals, hipStream_t s) {
+    if (v.inner == 2) return cols_go<REV, 2, NT>(p, x, out, v, carry_in, totals, s);
+    if (v.inner == 3) return cols_go<REV, 3, NT>(p, x, out, v, carry_in, totals, s);
+    return cols_go<REV, 4, NT>(p, x, out, v, carry_in, totals, s);
 }
 
 template <bool REV, int V, bool NT>
-hipError_t small_go(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
-                    int64_t inner, const float* carry_in, float* totals, hipStream_t s) {
-    const int32_t lc = inner >= 4 ? int32_t((inner + 3) / 4) : 1;
+hipError_t small_go(const rd_plan& p, const float* x, float* out, const Strides& v,
+                    const float* carry_in, float* totals, hipStream_t s) {
+    const int32_t lc = v.inner >= 4 ? int32_t((v.inner + 3) / 4) : 1;
     const uint32_t nx = uint32_t(p.nxcd);
     if (p.unroll == 8)
-        return launch(scan_small_kernel<REV, V, 8, NT>, p.blocks, kBlock, s, x, out, outer, R,
-                      inner, p.split, p.rows_per_split, lc, carry_in, totals, nx);
-    return launch(scan_small_kernel<REV, V, 4, NT>, p.blocks, kBlock, s, x, out, outer, R, inner,
-                  p.split, p.rows_per_split, lc, carry_in, totals, nx);
+        return launch(scan_small_kernel<REV, V, 8, NT>, p.blocks, kBlock, s, x, out, v.outer, v.R,
+                      v.inner, v.so, v.sr, p.split, p.rows_per_split, lc, carry_in, totals, nx);
+    return launch(scan_small_kernel<REV, V, 4, NT>, p.blocks, kBlock, s, x, out, v.outer, v.R,
+                  v.inner, v.so, v.sr, p.split, p.rows_per_split, lc, carry_in, totals, nx);
 }
 
 template <bool REV, bool NT>
-hipError_t small_v(const rd_plan& p, const float* x, float* out, int64_t outer, int64_t R,
-                   int64_t inner, const float* carry_in, float* totals, hipStream_t s) {
-    if (inner == 2) return small_go<REV, 2, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
-    if (inner == 3) return small_go<REV, 3, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
-    return small_go<REV, 4, NT>(p, x, out, outer, R, inner, carry_in, totals, s);
+hipError_t small_v(const rd_plan& p, const float* x, float* out, const Strides& v,
+                   const float* carry_in, float* totals, hipStream_t s) {
+    if (v.inner == 2) return small_go<REV, 2, NT>(p, x, out, v, carry_in, totals, s);
+    if (v.inner == 3) return small_go<REV, 3, NT>(p, x, out, v, carry_in, totals, s);
+    return small_go<REV, 4, NT>(p, x, out, v, carry_in, totals, s);
 }
 
 }  // namespace
 
 hipError_t launch_scan_small(const rd_plan& p, bool reverse, const float* x, float* out,
-                             int64_t outer, int64_t R, int64_t inner, const float* carry_in,
-                             float* totals, hipStream_t s) {
+                             const Strides& v, const float* carry_in, float* totals,
+                             hipStream_t s) {
     if (reverse)
-        return p.nontemporal ? small_v<true, true>(p, x, out, outer, R, inner, carry_in, totals, s)
-                             : small_v<true, false>(p, x, out, outer, R, inner, carry_in, totals, s);
-    return p.nontemporal ? small_v<false, true>(p, x, out, outer, R, inner, carry_in, totals, s)
-                         : small_v<false, false>(p, x, out, outer, R, inner, carry_in, totals, s);
+        return p.nontemporal ? small_v<true, true>(p, x, out, v, carry_in, totals, s)
+                             : small_v<true, false>(p, x, out, v, carry_in, totals, s);
+    return p.nontemporal ? small_v<false, true>(p, x, out, v, carry_in, totals, s)
+                         : small_v<false, false>(p, x, out, v, carry_in, totals, s);
 }
 
 hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, float* out,
-                            int64_t outer, int64_t R, const float* carry_in, float* totals,
+                            const Strides& v, const float* carry_in, float* totals,
                             hipStream_t s) {
-    return reverse ? rows_go<true>(p, x, out, outer, R, carry_in, totals, s)
-                   : rows_go<false>(p, x, out, outer, R, carry_in, totals, s);
+    return reverse ? rows_go<true>(p, x, out, v, carry_in, totals, s)
+                   : rows_go<false>(p, x, out, v, carry_in, totals, s);
 }
 
 hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows, int64_t P,
@@ -692,13 +761,23 @@ hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows
 }
 
 hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, float* out,
-                            int64_t outer, int64_t R, int64_t inner, const float* carry_in,
-                            float* totals, hipStream_t s) {
+                            const Strides& v, const float* carry_in, float* totals,
+                            hipStream_t s) {
     if (reverse)
-        return p.nontemporal ? cols_v<true, true>(p, x, out, outer, R, inner, carry_in, totals, s)
-                             : cols_v<true, false>(p, x, out, outer, R, inner, carry_in, totals, s);
-    return p.nontemporal ? cols_v<false, true>(p, x, out, outer, R, inner, carry_in, totals, s)
-                         : cols_v<false, false>(p, x, out, outer, R, inner, carry_in, totals, s);
+        return p.nontemporal ? cols_v<true, true>(p, x, out, v, carry_in, totals, s)
+                             : cols_v<true, false>(p, x, out, v, carry_in, totals, s);
+    return p.nontemporal ? cols_v<false, true>(p, x, out, v, carry_in, totals, s)
+                         : cols_v<false, false>(p, x, out, v, carry_in, totals, s);
+}
+
+hipError_t launch_scan_strided(const rd_plan& p, bool reverse, const float* x, float* out,
+                               const Strides& v, const float* carry_in, float* totals,
+                               hipStream_t s) {
+    if (reverse)
+        return launch(scan_strided_kernel<true>, p.blocks, kBlock, s, x, out, v.outer, v.R,
+                      v.inner, v.so, v.sr, v.si, p.split, p.rows_per_split, carry_in, totals);
+    return launch(scan_strided_kernel<false>, p.blocks, kBlock, s, x, out, v.outer, v.R, v.inner,
+                  v.so, v.sr, v.si, p.split, p.rows_per_split, carry_in, totals);
 }
 
 hipError_t launch_scan_slab_carries(bool reverse, const float* totals, float* carries, int64_t S,

@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
                  "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
                  "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "rd_cumsum_dim",
                  "rd_plan_cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim",
-                 "rd_reduce_strided", "rd_plan_strided", "rd_softmax_denom_strided"):
+                 "rd_reduce_strided", "rd_plan_strided", "rd_softmax_denom_strided",
+                 "rd_cumsum_strided", "rd_plan_cumsum_strided"):
         assert want in names
 
 
@@ -209,6 +210,31 @@ def test_strided_invalid_arguments(lib, host_buf):
     assert lib.rd_reduce_strided(None, 4, 5, 0, 0, 0, 1, 2, None, None) == OK
 
 
+def test_cumsum_strided_invalid_arguments(lib, host_buf):
+    base, _ = host_buf
+    out = base + 4 * 40
+    cases = [
+        (base, -1, 2, 2, 4, 2, 1, out), (base, 2, 2, 2, -4, 2, 1, out),
+        (base, 2, 2, 2, 4, -2, 1, out), (base, 2, 2, 2, 4, 2, -1, out),
+        (base, 2, 2, 2, 2 ** 62, 2, 1, out),      # the furthest element overflows
+        (base, 2, 2, 2, 4, 2, 1, None),           # null out
+        (None, 2, 2, 2, 4, 2, 1, out),            # null x
+        (base + 1, 2, 2, 2, 4, 2, 1, out),        # misaligned x
+        (base, 2, 2, 2, 4, 2, 1, out + 2),        # misaligned out
+        (base, 2, 3, 2, 20, 2, 1, base + 4 * 20), # out over the view's span (x[0..23])
+        (base + 4 * 8, 2, 3, 2, 6, 2, 1, base),   # the view (x[8..19]) over out[0..11]
+        (base, 2, 3, 2, 1, 4, 2, base),           # in place, but not out's layout
+        (base, 3, 1, 4, 8, 4, 2, base),           # in place, stride_inner 2
+    ]
+    for x, o_, R, i, so, sr, si, out_ in cases:
+        for rev in (0, 1):
+            assert lib.rd_cumsum_strided(x, o_, R, i, so, sr, si, rev, out_,
+                                         None) == INVALID, (o_, R, i, so, sr, si, rev)
+    # nothing to write: RD_OK, no device needed, null pointers allowed
+    assert lib.rd_cumsum_strided(None, 0, 5, 3, 15, 3, 1, 1, None, None) == OK
+    assert lib.rd_cumsum_strided(None, 4, 0, 3, 0, 0, 1, 0, None, None) == OK
+
+
 def test_empty_output_needs_nothing(lib):
     # outer * inner == 0: nothing to write, RD_OK without a device, null ok
     assert lib.rd_sum_dim(None, 0, 5, 3, None, None) == OK
@@ -235,6 +261,12 @@ def test_no_device_is_reported(lib, host_buf):
                                     None) == NO_DEVICE
     assert lib.rd_softmax_denom_1d(base, 8, base + 4 * 32, base + 4 * 40, None) == NO_DEVICE
     assert lib.rd_reduce_strided(base, 2, 2, 2, 1, 4, 2, 0, base + 4 * 32, None) == NO_DEVICE
+    assert lib.rd_cumsum_strided(base, 2, 2, 2, 1, 4, 2, 1, base + 4 * 32, None) == NO_DEVICE
+    # in place where the view is out's layout (the strides of length-1 axes ignored)
+    assert lib.rd_cumsum_strided(base, 2, 3, 4, 12, 4, 1, 0, base, None) == NO_DEVICE
+    assert lib.rd_cumsum_strided(base, 1, 3, 4, 99, 4, 1, 0, base, None) == NO_DEVICE
+    assert lib.rd_cumsum_strided(base, 2, 1, 4, 4, 77, 1, 0, base, None) == NO_DEVICE
+    assert lib.rd_cumsum_strided(base, 2, 3, 1, 3, 1, 5, 0, base, None) == NO_DEVICE
 
 
 def test_python_wrapper_rejects_cpu_tensors():
@@ -249,6 +281,8 @@ def test_python_wrapper_rejects_cpu_tensors():
         rd.rd_softmax_denom_dim(torch.ones(4), 1, 4, 1)
     with pytest.raises(ValueError):
         rd.softmax_denom(torch.ones(4))
+    with pytest.raises(ValueError):
+        rd.rd_cumsum_strided(torch.ones(4), 1, 4, 1, 4, 1, 1)
 
 
 def test_wrapper_raises_with_status():

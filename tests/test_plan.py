@@ -289,6 +289,83 @@ def test_cumsum_degenerate_plans():
         rd.rd_plan_cumsum(CU, -1, 1, 1)
 
 
+def test_cumsum_contiguous_view_plans_like_the_array():
+    for outer, R, inner in ((32768, 32768, 1), (128, 4096, 4095), (1, 1 << 20, 1),
+                            (4096, 4096, 4), (3, 5, 7), (1, 100, 130), (7, 0, 3)):
+        a = rd.rd_plan_cumsum(CU, outer, R, inner).as_dict()
+        b = rd.rd_plan_cumsum_strided(CU, outer, R, inner, R * inner, inner, 1).as_dict()
+        assert a == b, (outer, R, inner)
+
+
+def test_cumsum_strided_view_plans():
+    """The unit stride decides: inner axis -> column scans (any outer and R
+    strides), R with inner == 1 -> row scan (any row stride), none -> a lane
+    per output column, split into slabs of >= 32 rows when there are few."""
+    # the [4096, 4096] array transposed: [4096, 4096], strides (1, 4096)
+    p = rd.rd_plan_cumsum_strided(CU, 4096, 4096, 1, 1, 4096, 1).as_dict()
+    assert p["path"] == "scan_strided" and p["split"] == 64 and p["rows_per_split"] == 64
+    assert p["workspace_bytes"] == 2 * 64 * 4096 * 4 and p["passes"] == 3
+    assert p["nontemporal"] == 0
+    # columns 0..1023 of [64, 512, 4096]: the column scan with sr = 4096
+    p = rd.rd_plan_cumsum_strided(CU, 64, 512, 1024, 512 * 4096, 4096, 1).as_dict()
+    assert p["path"] == "scan_cols"
+    assert p == rd.rd_plan_cumsum(CU, 64, 512, 1024).as_dict()
+    # every other row of a [8192, 8192] array: rows with so = 2*8192
+    p = rd.rd_plan_cumsum_strided(CU, 4096, 8192, 1, 2 * 8192, 1, 1).as_dict()
+    assert p == rd.rd_plan_cumsum(CU, 4096, 8192, 1).as_dict()
+    # the inner axis strided: a lane per column, enough columns for no slabs
+    p = rd.rd_plan_cumsum_strided(CU, 512, 100, 1024, 1024 * 100, 1, 100).as_dict()
+    assert p["path"] == "scan_strided" and p["split"] == 1 and p["passes"] == 1
+    assert p["blocks"] == 512 * 1024 // 256 and p["workspace_bytes"] == 0
+    # one strided column: as many slabs as keep 32 rows each
+    p = rd.rd_plan_cumsum_strided(CU, 1, 100_000, 1, 0, 7, 1).as_dict()
+    assert p["path"] == "scan_strided" and p["split"] == 3125 and p["rows_per_split"] == 32
+    # length-1 axes: their strides are ignored
+    assert rd.rd_plan_cumsum_strided(CU, 1, 9, 4, 12345, 4, 1).as_dict()["path"] == \
+        "scan_cols_small"
+    assert rd.rd_plan_cumsum_strided(CU, 9, 1, 1, 5, 3, 77).as_dict()["path"] == "scan_rows"
+    rng = np.random.default_rng(9)
+    for _ in range(2000):
+        outer, R, inner = (int(v) for v in rng.integers(1, [500, 50_000, 600]))
+        so, sr, si = (int(v) for v in rng.integers(0, [10**6, 5000, 40]))
+        cu = int(rng.integers(1, 300))
+        p = rd.rd_plan_cumsum_strided(cu, outer, R, inner, so, sr, si)
+        d = p.as_dict()
+        assert p.split * p.rows_per_split >= R > (p.split - 1) * p.rows_per_split
+        unit_rows = inner == 1 and (sr == 1 or R == 1)
+        unit_cols = inner > 1 and si == 1
+        if not (unit_rows or unit_cols):
+            assert d["path"] == "scan_strided"
+            assert p.blocks == min(-(-p.split * outer * inner // 256), 1 << 20)
+            assert p.split == 1 or p.rows_per_split >= 32
+            assert p.workspace_bytes == (2 * p.split * outer * inner * 4 if p.split > 1 else 0)
+        else:
+            assert d == rd.rd_plan_cumsum(cu, outer, R, inner).as_dict()
+
+
+def test_cumsum_strided_forced_path():
+    """path = RD_PATH_SCAN_STRIDED is valid for every view (with split);
+    a row or column path is refused where its unit stride is missing."""
+    with rd.tuning(path=10):
+        p = rd.rd_plan_cumsum_strided(CU, 3, 100, 5, 500, 5, 1).as_dict()
+        assert p["path"] == "scan_strided"
+        assert rd.rd_plan_cumsum(CU, 32768, 32768, 1).as_dict()["path"] == "scan_strided"
+    with rd.tuning(path=10, split=3):
+        p = rd.rd_plan_cumsum_strided(CU, 3, 100, 5, 500, 5, 1)
+        assert p.split == 3 and p.rows_per_split == 34 and p.passes == 3
+    with rd.tuning(path=10, unroll=4):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum_strided(CU, 3, 100, 5, 500, 5, 1)
+    with rd.tuning(path=6):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum_strided(CU, 3, 100, 1, 1, 3, 1)   # rows, R strided
+    with rd.tuning(path=7):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum_strided(CU, 3, 100, 5, 500, 1, 100)  # inner strided
+    with pytest.raises(rd.RdError):
+        rd.rd_plan_cumsum_strided(CU, 2, 2, 2, -1, 2, 1)
+
+
 # ------------------------------------------------------------ strided views
 def test_strided_contiguous_view_plans_like_the_array():
     for outer, R, inner in ((1, 10**9, 1), (128, 4096, 4095), (32768, 32768, 1), (3, 5, 7),
