@@ -241,9 +241,11 @@ rd_status rd_cumsum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
  * ignored).  The kernel follows the unit stride: stride_inner == 1 (inner >
  * 1) scans columns as rd_cumsum_dim does, with any stride_outer and stride_r;
  * inner == 1 with stride_r == 1 scans rows; any other view takes one lane per
- * output column (a slab of it when there are few columns), each term a
- * 4-byte access (correct, not fast).  A contiguous view gives the bits
- * rd_cumsum_dim gives.  Status codes as for rd_cumsum_dim.  Source: the
+ * output column (a slab of it when there are few columns) adding its terms
+ * one after the other, with the outputs staged through LDS when inner == 1
+ * (a transposed array: lanes on adjacent columns, each column's outputs
+ * contiguous) and the inputs staged when stride_r == 1.  A contiguous view
+ * gives the bits rd_cumsum_dim gives.  Status codes as for rd_cumsum_dim.  Source: the
  * POPCORNBENCH problem-91 trace scans a torch tensor along one dimension
  * (torch.cumsum over x.flip(1)), which accepts any strided tensor. */
 rd_status rd_cumsum_strided(const float* x, int64_t outer, int64_t R, int64_t inner,

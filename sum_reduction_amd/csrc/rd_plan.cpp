@@ -363,7 +363,8 @@ rd_status plan_scan_strided(int64_t cu, int64_t outer, int64_t R, int64_t inner,
     if (p->split > INT64_MAX / 8 / n) return RD_ERR_INVALID_ARG;
     p->path = RD_PATH_SCAN_STRIDED;
     p->nontemporal = 0;  // neighbouring lanes and rows share lines: keep them cached
-    p->blocks = ceil_div(p->split * n, kBlock);
+    // a workgroup per (slab, kBlock columns): the staged variants' item
+    p->blocks = p->split * ceil_div(n, kBlock);
     if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
     if (p->split > 1) {
         p->passes = 3;

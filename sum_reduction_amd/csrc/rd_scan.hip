@@ -641,6 +641,165 @@ __global__ __launch_bounds__(kBlock) void scan_strided_kernel(
     }
 }
 
+// Two layouts of scan_strided_kernel's lanes have one unit-stride side that
+// the lanes do not follow; a block then stages that side through an LDS tile
+// of kTileRows rows x kBlock columns (an odd pitch: thread t touching element
+// (t, j), and 32 threads touching 32 consecutive elements of one column, both
+// hit distinct banks).  Every column is still added one term after the other
+// in processing order from the same carry, so the bits are those of
+// scan_strided_kernel.  Block items: (slab s, block of kBlock columns),
+// columns fastest.
+constexpr int kTileRows = 32;
+constexpr int kTilePitch = kTileRows + 1;
+
+// The rows [lo, lo + kc) of chunk c (c0 = c*kTileRows processing positions
+// into a slab [r_begin, r_end)): REV walks the slab from its end.
+template <bool REV>
+__device__ __forceinline__ int64_t chunk_lo(int64_t r_begin, int64_t r_end, int64_t c0, int kc) {
+    return REV ? r_end - c0 - kc : r_begin + c0;
+}
+
+// inner == 1: the outputs of column o are out[o*R + r], R floats apart from
+// the next column's, so lanes storing their own prefixes would each write
+// 4 bytes of a different line.  Thread t keeps column o0 + t: it loads its
+// chunk's terms x[o*so + r*sr] (adjacent across lanes when so == 1), adds
+// them, and parks each prefix at tile[t][r - lo]; then the block writes the
+// tile out row by row of out (kTileRows consecutive floats of one column per
+// 32 threads).
+template <bool REV>
+__global__ __launch_bounds__(kBlock) void scan_tile_out_kernel(
+    const float* x, float* out, int64_t outer, int64_t R, int64_t so, int64_t sr, int64_t S,
+    int64_t rps, const float* __restrict__ carry_in) {
+    __shared__ float tile[kBlock * kTilePitch];
+    const int t = threadIdx.x;
+    const int64_t nblk = (outer + kBlock - 1) / kBlock;
+    const int64_t nitems = nblk * S;
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const int64_t s = item / nblk;
+        const int64_t o0 = (item - s * nblk) * kBlock;
+        const int ncols = outer - o0 < kBlock ? int(outer - o0) : kBlock;
+        const bool live = t < ncols;
+        const int64_t r_begin = s * rps;
+        const int64_t r_end = r_begin + rps < R ? r_begin + rps : R;
+        const int64_t m = r_end - r_begin;  // >= 1: no slab is empty
+        const float* p = x + (live ? (o0 + t) * so : 0);
+        float acc = live && carry_in != nullptr ? carry_in[s * outer + o0 + t] : 0.f;
+        float* row = tile + t * kTilePitch;
+        for (int64_t c0 = 0; c0 < m; c0 += kTileRows) {
+            const int kc = m - c0 < kTileRows ? int(m - c0) : kTileRows;
+            const int64_t lo = chunk_lo<REV>(r_begin, r_end, c0, kc);
+            if (live) {
+                if (kc == kTileRows) {
+                    float v[kTileRows];
+#pragma unroll
+                    for (int j = 0; j < kTileRows; ++j)
+                        v[j] = p[(lo + (REV ? kTileRows - 1 - j : j)) * sr];
+#pragma unroll
+                    for (int j = 0; j < kTileRows; ++j) {
+                        acc += v[j];
+                        row[REV ? kTileRows - 1 - j : j] = acc;
+                    }
+                } else {
+                    for (int j = 0; j < kc; ++j) {
+                        const int k = REV ? kc - 1 - j : j;
+                        acc += p[(lo + k) * sr];
+                        row[k] = acc;
+                    }
+                }
+            }
+            __syncthreads();
+            if (kc == kTileRows) {
+#pragma unroll 8
+                for (int mm = 0; mm < kTileRows; ++mm) {
+                    const int col = mm * (kBlock / kTileRows) + t / kTileRows;
+                    const int k = t % kTileRows;
+                    if (col < ncols) out[(o0 + col) * R + lo + k] = tile[col * kTilePitch + k];
+                }
+            } else {
+                for (int f = t; f < ncols * kc; f += kBlock) {
+                    const int col = f / kc;
+                    const int k = f - col * kc;
+                    out[(o0 + col) * R + lo + k] = tile[col * kTilePitch + k];
+                }
+            }
+            __syncthreads();  // the tile is refilled next
+        }
+    }
+}
+
+// stride_r == 1, inner > 1 (columns e = o*inner + i at x[o*so + i*si], their
+// terms adjacent): lanes own adjacent outputs, so their stores are adjacent,
+// but their loads are si floats apart.  The block first reads a chunk of
+// kTileRows terms of its kBlock columns, 32 threads per column run
+// (128 contiguous bytes), into tile[col][r - lo]; then thread t adds column
+// e0 + t's terms from the tile and stores each prefix at
+// out[(o*R + r)*inner + i].  totals != null: only the slab totals, at
+// totals[s*n + e].
+template <bool REV>
+__global__ __launch_bounds__(kBlock) void scan_tile_in_kernel(
+    const float* x, float* out, int64_t outer, int64_t R, int64_t inner, int64_t so,
+    int64_t si, int64_t S, int64_t rps, const float* __restrict__ carry_in,
+    float* __restrict__ totals) {
+    __shared__ float tile[kBlock * kTilePitch];
+    __shared__ int64_t base[kBlock];  // where each column's terms start in x
+    const int t = threadIdx.x;
+    const bool scan_out = totals == nullptr;
+    const int64_t n = outer * inner;
+    const int64_t nblk = (n + kBlock - 1) / kBlock;
+    const int64_t nitems = nblk * S;
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const int64_t s = item / nblk;
+        const int64_t e0 = (item - s * nblk) * kBlock;
+        const int ncols = n - e0 < kBlock ? int(n - e0) : kBlock;
+        const bool live = t < ncols;
+        const int64_t e = e0 + t;
+        const int64_t o = live ? e / inner : 0;
+        const int64_t i = live ? e - o * inner : 0;
+        const int64_t r_begin = s * rps;
+        const int64_t r_end = r_begin + rps < R ? r_begin + rps : R;
+        const int64_t m = r_end - r_begin;  // >= 1: no slab is empty
+        float* q = out + o * R * inner + i;
+        float acc = live && scan_out && carry_in != nullptr ? carry_in[s * n + e] : 0.f;
+        const float* row = tile + t * kTilePitch;
+        __syncthreads();  // the previous item is done with base
+        base[t] = o * so + i * si;
+        __syncthreads();
+        for (int64_t c0 = 0; c0 < m; c0 += kTileRows) {
+            const int kc = m - c0 < kTileRows ? int(m - c0) : kTileRows;
+            const int64_t lo = chunk_lo<REV>(r_begin, r_end, c0, kc);
+            if (kc == kTileRows) {  // all kTileRows loads in flight, then the tile
+                float v[kTileRows];
+#pragma unroll
+                for (int mm = 0; mm < kTileRows; ++mm) {
+                    const int col = mm * (kBlock / kTileRows) + t / kTileRows;
+                    v[mm] = col < ncols ? x[base[col] + lo + t % kTileRows] : 0.f;
+                }
+#pragma unroll
+                for (int mm = 0; mm < kTileRows; ++mm) {
+                    const int col = mm * (kBlock / kTileRows) + t / kTileRows;
+                    tile[col * kTilePitch + t % kTileRows] = v[mm];
+                }
+            } else {
+                for (int f = t; f < ncols * kc; f += kBlock) {
+                    const int col = f / kc;
+                    const int k = f - col * kc;
+                    tile[col * kTilePitch + k] = x[base[col] + lo + k];
+                }
+            }
+            __syncthreads();
+            if (live) {
+                for (int j = 0; j < kc; ++j) {
+                    const int k = REV ? kc - 1 - j : j;
+                    acc += row[k];
+                    if (scan_out) q[(lo + k) * inner] = acc;
+                }
+            }
+            __syncthreads();  // the tile is refilled next
+        }
+        if (live && !scan_out) totals[s * n + e] = acc;
+    }
+}
+
 // ------------------------------------------------------------ launching
 template <typename T>
 struct same {
@@ -773,10 +932,25 @@ hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, floa
 hipError_t launch_scan_strided(const rd_plan& p, bool reverse, const float* x, float* out,
                                const Strides& v, const float* carry_in, float* totals,
                                hipStream_t s) {
+    const int64_t blocks = p.blocks;  // a lane per (slab, column) in every variant
+    if (v.inner == 1 && totals == nullptr) {  // stage the outputs
+        if (reverse)
+            return launch(scan_tile_out_kernel<true>, blocks, kBlock, s, x, out, v.outer, v.R,
+                          v.so, v.sr, p.split, p.rows_per_split, carry_in);
+        return launch(scan_tile_out_kernel<false>, blocks, kBlock, s, x, out, v.outer, v.R, v.so,
+                      v.sr, p.split, p.rows_per_split, carry_in);
+    }
+    if (v.inner > 1 && v.sr == 1) {  // stage the inputs
+        if (reverse)
+            return launch(scan_tile_in_kernel<true>, blocks, kBlock, s, x, out, v.outer, v.R,
+                          v.inner, v.so, v.si, p.split, p.rows_per_split, carry_in, totals);
+        return launch(scan_tile_in_kernel<false>, blocks, kBlock, s, x, out, v.outer, v.R,
+                      v.inner, v.so, v.si, p.split, p.rows_per_split, carry_in, totals);
+    }
     if (reverse)
-        return launch(scan_strided_kernel<true>, p.blocks, kBlock, s, x, out, v.outer, v.R,
+        return launch(scan_strided_kernel<true>, blocks, kBlock, s, x, out, v.outer, v.R,
                       v.inner, v.so, v.sr, v.si, p.split, p.rows_per_split, carry_in, totals);
-    return launch(scan_strided_kernel<false>, p.blocks, kBlock, s, x, out, v.outer, v.R, v.inner,
+    return launch(scan_strided_kernel<false>, blocks, kBlock, s, x, out, v.outer, v.R, v.inner,
                   v.so, v.sr, v.si, p.split, p.rows_per_split, carry_in, totals);
 }
 

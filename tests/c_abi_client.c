@@ -114,6 +114,21 @@ int main(void) {
     oracle_cumsum_dim(h, outer, R, inner, 1, w, a, 0);
     ok &= same_bits(g, w, n, "rd_cumsum_dim");
 
+    /* the forward cumulative sum over the transposed view [R*inner, outer]
+       (stride 1 between outputs, R*inner along the scan), contiguous out */
+    {
+        const int64_t P = R * inner;
+        float* ht = (float*)malloc((size_t)n * sizeof(float));
+        for (int64_t o = 0; o < outer; ++o)
+            for (int64_t p = 0; p < P; ++p) ht[p * outer + o] = h[o * P + p];
+        RD_OK_(rd_cumsum_strided(x, P, outer, 1, 1, P, 1, 0, out, s));
+        HIP_OK(hipStreamSynchronize(s));
+        HIP_OK(hipMemcpy(g, out, (size_t)n * sizeof(float), hipMemcpyDeviceToHost));
+        oracle_cumsum_dim(ht, P, outer, 1, 0, w, a, 0);
+        ok &= same_bits(g, w, n, "rd_cumsum_strided");
+        free(ht);
+    }
+
     /* the softmax denominator on terms 0 / -Inf: s counts the zeros exactly */
     for (int64_t k = 0; k < n; ++k) h[k] = h[k] > 0 ? 0.f : -__builtin_inff();
     HIP_OK(hipMemcpy(x, h, (size_t)n * sizeof(float), hipMemcpyHostToDevice));

@@ -2,12 +2,15 @@
 // built with g++ under AddressSanitizer and UndefinedBehaviorSanitizer by
 // tests/test_plan_sanitized.py.  Random shapes (zeros, ones, small, huge,
 // near the int64 limits), strides, operators and tuning overrides go
-// through plan_view and plan_cumsum; every accepted plan must satisfy the
+// through plan_view, plan_cumsum and plan_cumsum_view; every accepted plan
+// must satisfy the
 // invariants the launchers rely on.  Any signed overflow, out-of-bounds
 // access or failed invariant ends the run with a nonzero status.
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
+#include <algorithm>
 #include <random>
 
 #include "rd_internal.h"
@@ -107,6 +110,42 @@ void check_reduce_plan(const rd::Strides& v, int op, const rd_plan& p) {
     }
 }
 
+bool tiles(int64_t R, int64_t split, int64_t per) {
+    return per >= 1 && split >= 1 && split * per >= R && (split - 1) * per < R;
+}
+
+void check_scan_plan(const rd::Strides& v, const rd_plan& p) {
+    if (p.path == RD_PATH_NONE) {
+        if (v.outer != 0 && v.R != 0 && v.inner != 0) fail("scan NONE with elements", v, -1, p);
+        return;
+    }
+    if (p.blocks < 1 || p.blocks > rd::kMaxBlocks) fail("scan blocks out of range", v, -1, p);
+    if (p.passes != (p.split > 1 ? 3 : 1)) fail("scan passes", v, -1, p);
+    const int64_t n = v.outer * v.inner;
+    switch (p.path) {
+        case RD_PATH_SCAN_ROWS:
+            if (v.inner != 1 || v.sr != 1) fail("scan rows without unit row stride", v, -1, p);
+            if (!tiles(v.R, p.split, p.rows_per_split)) fail("pieces do not tile R", v, -1, p);
+            if (p.workspace_bytes != (p.split > 1 ? 8 * v.outer * p.split : 0))
+                fail("scan rows workspace", v, -1, p);
+            break;
+        case RD_PATH_SCAN_COLS:
+        case RD_PATH_SCAN_COLS_SMALL:
+        case RD_PATH_SCAN_STRIDED:
+            if (p.path != RD_PATH_SCAN_STRIDED && (v.inner < 2 || v.si != 1))
+                fail("column scan without unit inner stride", v, -1, p);
+            if (!tiles(v.R, p.split, p.rows_per_split)) fail("scan slabs do not tile R", v, -1, p);
+            if (p.workspace_bytes != (p.split > 1 ? 8 * p.split * n : 0))
+                fail("scan slab workspace", v, -1, p);
+            if (p.path == RD_PATH_SCAN_STRIDED &&
+                p.blocks != std::min(rd::kMaxBlocks, p.split * ((n + rd::kBlock - 1) / rd::kBlock)))
+                fail("scan strided blocks", v, -1, p);
+            break;
+        default:
+            fail("unknown scan path", v, -1, p);
+    }
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -136,7 +175,10 @@ int main(int argc, char** argv) {
             t.order = int32_t(rng() % 3);
             t.nontemporal = int32_t(rng() % 3);
             t.combine = int32_t(rng() % 3);
-            t.path = int32_t(rng() % 4 == 0 ? (rng() % 2 ? RD_PATH_COLS : RD_PATH_COLS_SMALL) : 0);
+            static const int32_t paths[] = {RD_PATH_COLS, RD_PATH_COLS_SMALL, RD_PATH_SCAN_ROWS,
+                                            RD_PATH_SCAN_COLS, RD_PATH_SCAN_COLS_SMALL,
+                                            RD_PATH_SCAN_STRIDED};
+            t.path = rng() % 4 == 0 ? paths[rng() % 6] : 0;
             t.split = rng() % 2 ? 0 : int64_t(rng() % 5000);
         }
         rd::Strides w = v;
@@ -145,12 +187,20 @@ int main(int argc, char** argv) {
             ++accepted;
             check_reduce_plan(w, op, p);
         }
+        rd::Strides u = v;
+        rd_plan q;
+        if (rd::plan_cumsum_view(cu, &u, tuned ? &t : nullptr, &q) == RD_OK) {
+            ++accepted;
+            check_scan_plan(u, q);
+        }
         if (contiguous && fits) {
-            rd_plan q;
-            if (rd::plan_cumsum(cu, v.outer, v.R, v.inner, tuned ? &t : nullptr, &q) == RD_OK) {
-                if (q.path != RD_PATH_NONE && (q.blocks < 1 || q.split < 1 || q.workspace_bytes < 0))
-                    fail("cumsum plan", v, -1, q);
-            }
+            rd_plan c;
+            const rd_status a = rd::plan_cumsum(cu, v.outer, v.R, v.inner, tuned ? &t : nullptr, &c);
+            rd::Strides cv{v.outer, v.R, v.inner, v.R * v.inner, v.inner, 1};
+            rd_plan d;
+            const rd_status b = rd::plan_cumsum_view(cu, &cv, tuned ? &t : nullptr, &d);
+            if (a != b || (a == RD_OK && memcmp(&c, &d, sizeof(c)) != 0))
+                fail("contiguous view plans unlike the array", v, -1, c);
         }
     }
     printf("plan_fuzz: %ld iterations, %ld accepted plans, no finding\n", iters, accepted);

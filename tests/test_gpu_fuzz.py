@@ -128,3 +128,47 @@ def test_random_strided(seed):
                                             strides=(4 * so, 4 * sr, 4 * si), writeable=False)
         S, _ = _expected(np.ascontiguousarray(v), o, R, i, op)
         H.assert_bitwise_equal_oracle(got, S, what)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_strided_cumsum(seed):
+    """rd_cumsum_strided on random views, both directions, sometimes with the
+    lane-per-column kernel forced and a random slab count; integer data, so
+    every prefix is exact and must equal the oracle's bit for bit."""
+    rng = np.random.default_rng(8500 + seed)
+    lib = rd.load()
+    for case in range(40):
+        while True:
+            o, R, i = _size(rng, 300), _size(rng, 3000), _size(rng, 300)
+            if o * R * i <= 600_000:
+                break
+
+        def pick(contig):
+            return int(rng.choice([0, 1, contig, contig + int(rng.integers(1, 9)),
+                                   int(rng.integers(1, 40))]))
+        si = pick(1)
+        sr = pick(max(i, 1) * max(si, 1))
+        so = pick(max(R, 1) * max(sr, 1))
+        rev = int(rng.integers(0, 2))
+        off = int(rng.integers(0, 4))
+        tune = dict(path=10, split=int(rng.choice([1, 2, 7, 50]))) if rng.random() < 0.3 else {}
+        n = o * R * i
+        ext = 0 if n == 0 else (o - 1) * so + (R - 1) * sr + (i - 1) * si + 1
+        host = workloads.small_ints(ext + off + 1, 8600 + 100 * seed + case)
+        dev = H.upload(host)
+        slots = H.OutSlots([n])
+        what = "seed %d case %d view %s strides %s rev %d off %d tune %s" % (
+            seed, case, (o, R, i), (so, sr, si), rev, off, tune)
+        H.say(what)
+        xp = dev.data_ptr() + 4 * off if ext else None
+        with rd.tuning(**tune):
+            st = lib.rd_cumsum_strided(xp, o, R, i, so, sr, si, rev, slots.ptr(0) if n else None,
+                                       H.stream_handle())
+        assert st == 0, (what, rd.rd_status_string(st))
+        (got,) = slots.fetch()
+        if n == 0:
+            continue
+        v = np.lib.stride_tricks.as_strided(host[off:], shape=(o, R, i),
+                                            strides=(4 * so, 4 * sr, 4 * si), writeable=False)
+        S, _ = oracle.cumsum_dim(np.ascontiguousarray(v), o, R, i, bool(rev), threads=1)
+        H.assert_bitwise_equal_oracle(got, S, what)

@@ -5,10 +5,12 @@ Integer data (ints in [-8, 8]) keeps every running sum exact in fp32, so each
 output must equal the oracle's bit for bit, in both directions.  The views
 cover each path the planner takes: rows with a row stride (slices, broadcast
 rows, pieces), columns with outer and row strides (slices, every other row,
-broadcast), and views with no unit stride (a transposed array, permuted
-axes, a strided inner axis: the lane-per-column kernel, with slabs), each at
-base offsets 0-3 floats, with the lane-per-column kernel also forced on
-every view and cut into forced slab counts.
+broadcast), and views with no unit stride along the lanes' side: a
+transposed array scanned along its rows (outputs staged through LDS) or its
+columns (inputs staged), permuted axes and a strided inner axis (one lane
+per column), short and ragged chunks and column blocks, slabs; each at base
+offsets 0-3 floats, with the lane-per-column scan also forced on every view
+and cut into forced slab counts.
 """
 import numpy as np
 import pytest
@@ -47,6 +49,9 @@ VIEWS = [
     ("every_third_column", 200 * 90, 1, 100, 30, 0, 180, 3, "scan_strided"),
     ("permuted_3d", 5 * 6 * 7, 7, 5, 6, 1, 42, 7, "scan_strided"),
     ("strided_long", 3 * 20000 * 2, 3, 20000, 2, 1, 6, 3, "scan_strided"),
+    ("transpose_short_rows", 5 * 1000, 1000, 5, 1, 1, 1000, 1, "scan_strided"),
+    ("transpose_short_cols", 7 * 300, 1, 7, 300, 0, 1, 7, "scan_strided"),
+    ("transpose_every_third", 70 * 900, 300, 70, 1, 3, 900, 1, "scan_strided"),
 ]
 
 

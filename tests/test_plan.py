@@ -336,7 +336,7 @@ def test_cumsum_strided_view_plans():
         unit_cols = inner > 1 and si == 1
         if not (unit_rows or unit_cols):
             assert d["path"] == "scan_strided"
-            assert p.blocks == min(-(-p.split * outer * inner // 256), 1 << 20)
+            assert p.blocks == min(p.split * -(-outer * inner // 256), 1 << 20)
             assert p.split == 1 or p.rows_per_split >= 32
             assert p.workspace_bytes == (2 * p.split * outer * inner * 4 if p.split > 1 else 0)
         else:
