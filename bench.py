@@ -116,8 +116,9 @@ def main(argv=None):
                     help="with --report: the reductions to time (default: sum); "
                     "softmax_denom writes the pair (max, shifted sum of exp)")
     ap.add_argument("--strided", action="store_true",
-                    help="with --report: sums over strided views of a [32768, 32768] array "
-                    "(transposed, every other row, every third column) instead")
+                    help="with --report: sums, then cumulative sums, over strided views of "
+                    "a [32768, 32768] array (transposed, every other row, every third "
+                    "column) instead")
     ap.add_argument("--scan", action="store_true",
                     help="with --report: the cumulative sums instead (problem 91's "
                     "[32768, 32768] rows, then each --scan-shape)")
@@ -403,6 +404,18 @@ STRIDED_VIEWS = [
 ]
 
 
+# the same views scanned (rd_cumsum_strided, forward): the output is the
+# contiguous array of the view's shape
+STRIDED_SCAN_VIEWS = [
+    ("rows_of_transpose", STRIDED_N, STRIDED_N, 1, 1, STRIDED_N, 1, "x.t().cumsum(1)"),
+    ("cols_of_transpose", 1, STRIDED_N, STRIDED_N, 0, 1, STRIDED_N, "x.t().cumsum(0)"),
+    ("every_other_row", 1, STRIDED_N // 2, STRIDED_N, 0, 2 * STRIDED_N, 1, "x[::2].cumsum(0)"),
+    ("row_halves", STRIDED_N, STRIDED_N // 2, 1, STRIDED_N, 1, 1, "x[:, :N/2].cumsum(1)"),
+    ("every_third_column", 1, STRIDED_N // 8, STRIDED_N // 3, 0, 8 * STRIDED_N, 3,
+     "x[::8, ::3].cumsum(0)"),
+]
+
+
 def report_strided(args, dev, cu):
     """One JSON line per strided view: GPU time warm, GB/s over the bytes the
     view holds, its plan, parity against the oracle on a contiguous copy."""
@@ -441,6 +454,33 @@ def report_strided(args, dev, cu):
             got = out.cpu().numpy().reshape(-1)
             line["parity"] = {"ok": bool(oracle.within_tolerance(got, S.reshape(-1),
                                                                  A.reshape(-1)).all())}
+        print(json.dumps(line), flush=True)
+        del out
+    for name, o, R, i, so, sr, si, expr in STRIDED_SCAN_VIEWS:
+        log("report: strided cumsum %s" % name)
+        out = torch.empty(o * R * i, dtype=torch.float32, device=dev)
+
+        def call():
+            rd.rd_cumsum_strided(x, o, R, i, so, sr, si, False, out=out)
+
+        reps = args.reps or 30
+        ms = _median_ms(call, reps)
+        nbytes = 8 * o * R * i
+        plan = rd.rd_plan_cumsum_strided(cu, o, R, i, so, sr, si).as_dict()
+        line = {"op": "cumsum", "view": name, "torch": expr, "shape": [o, R, i],
+                "strides": [so, sr, si], "view_bytes": nbytes, "ms_median": round(ms, 5),
+                "GBps": round(nbytes / ms / 1e6, 1),
+                "frac_of_peak": round(nbytes / ms / 1e6 / PEAK_GBS, 4), "plan": plan,
+                "reps": reps}
+        if not args.no_oracle:
+            v = np.lib.stride_tricks.as_strided(host, shape=(o, R, i),
+                                                strides=(4 * so, 4 * sr, 4 * si),
+                                                writeable=False)
+            S, A = oracle.cumsum_dim(np.ascontiguousarray(v), o, R, i, False, threads)
+            got = out.cpu().numpy().reshape(-1)
+            line["parity"] = {"ok": bool(oracle.within_tolerance(got, S.reshape(-1),
+                                                                 A.reshape(-1)).all())}
+            del S, A, got
         print(json.dumps(line), flush=True)
         del out
     return 0
