@@ -37,8 +37,11 @@ def kernels(tmp_path_factory):
     """{symbol: [instruction text]} for every gfx950 function in librd.so."""
     bundler, objdump = _tools()
     tmp = tmp_path_factory.mktemp("isa")
-    fat = str(tmp / "fatbin")
-    subprocess.run(["objcopy", "--dump-section", ".hip_fatbin=" + fat, rd.library_path()],
+    # work on a copy: objcopy rewrites its input file unless given an output
+    # file, and this process has the library mapped
+    lib, fat = str(tmp / "librd.so"), str(tmp / "fatbin")
+    shutil.copyfile(rd.library_path(), lib)
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", lib, fat],
                    check=True, capture_output=True)
     data = open(fat, "rb").read()
     starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)] + [len(data)]
