@@ -207,8 +207,9 @@ __device__ __forceinline__ SmPair sm_join(SmPair a, SmPair b) {
 //   start1/4  the empty result;  fold(S4, v4f) adds one term per lane;
 //   fold_x    adds one term to lane x only;  fold_all<U> adds U float4s of
 //   terms into acc[0..1];  join (S1 or S4);  lane / set_lane move one lane
-//   of an S4;  get / put / at read, write and offset an Out;  fill is the
-//   value of a load lane that holds no term (neutral for fold).
+//   of an S4;  get / put / at read, write and offset an Out, get4 reads
+//   four consecutive results as an S4;  fill is the value of a load lane
+//   that holds no term (neutral for fold).
 // For sum, sum of squares, maximum and minimum a result is one float and
 // every step is the Op<OP> arithmetic above.
 template <int OP>
@@ -238,6 +239,7 @@ struct St {
     static __device__ __forceinline__ S1 lane(S4 a, int q) { return a[q]; }
     static __device__ __forceinline__ void set_lane(S4& a, int q, S1 v) { a[q] = v; }
     static __device__ __forceinline__ S1 get(Out o, int64_t e) { return o[e]; }
+    static __device__ __forceinline__ S4 get4(Out o, int64_t e) { return load4<false>(o + e); }
     static __device__ __forceinline__ void put(Out o, int64_t e, S1 v) { o[e] = v; }
     static __device__ __forceinline__ Out at(Out o, int64_t e) { return o + e; }
     static Out make_out(float* a, float*) { return a; }
@@ -334,6 +336,16 @@ struct St<RD_OP_SOFTMAX_DENOM> {
     }
     static __device__ __forceinline__ S1 join(S1 a, S1 b) { return sm_join(a, b); }
     static __device__ __forceinline__ S1 get(Out o, int64_t e) { return SmPair{o.m[e], o.s[e]}; }
+    // four stored pairs as running states: each sum is relative to its
+    // pair's shift
+    static __device__ __forceinline__ S4 get4(Out o, int64_t e) {
+        S4 r;
+        r.m = load4<false>(o.m + e);
+        r.s = load4<false>(o.s + e);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.c[q] = sm_shift(r.m[q]);
+        return r;
+    }
     static __device__ __forceinline__ void put(Out o, int64_t e, S1 v) {
         o.m[e] = v.m;
         o.s[e] = v.s;
@@ -463,17 +475,34 @@ __device__ __forceinline__ typename St<OP>::S1 block_reduce(typename St<OP>::S1 
     return t;
 }
 
-// out_o = the join of the P piece results of one row: lane t joins pieces
-// t, t + 256, ... in order, then the workgroup reduction.  Used by the
-// second pass and by the last workgroup of a fused first pass, so both give
-// the same bits.  Every thread of the workgroup must call it.
+// out_o = the join of the P piece results of one row.  Lane t keeps four
+// running results, the pieces 4q .. 4q + 3 for q = t, t + 256, ... joined
+// lane-wise in that order (16-byte loads, kCombineLoads of them issued before
+// the first join, so tens of thousands of pieces cost a few memory round
+// trips); its four lanes are then joined (join_lanes), the P % 4 last pieces
+// joined by threads 0 .. 2, then the workgroup reduction.  Used by the second
+// pass and by the last workgroup of a fused first pass, so both give the same
+// bits.  Every thread of the workgroup must call it.
+constexpr int kCombineLoads = 16;
+
 template <int OP>
 __device__ __forceinline__ void combine_row(typename St<OP>::Out part, int64_t P,
                                             typename St<OP>::Out out_o,
                                             typename St<OP>::S1* lds) {
     typedef St<OP> T;
-    typename T::S1 t = T::start1();
-    for (int64_t k = threadIdx.x; k < P; k += kBlock) t = T::join(t, T::get(part, k));
+    const int64_t nq = P >> 2;
+    typename T::S4 acc = T::start4();
+    for (int64_t q = threadIdx.x; q < nq; q += kCombineLoads * kBlock) {
+        typename T::S4 v[kCombineLoads];
+#pragma unroll
+        for (int u = 0; u < kCombineLoads; ++u)
+            if (q + u * kBlock < nq) v[u] = T::get4(part, 4 * (q + u * kBlock));
+#pragma unroll
+        for (int u = 0; u < kCombineLoads; ++u)
+            if (q + u * kBlock < nq) acc = T::join(acc, v[u]);
+    }
+    typename T::S1 t = join_lanes<OP>(acc);
+    if (threadIdx.x < (P & 3)) t = T::join(t, T::get(part, 4 * nq + threadIdx.x));
     t = block_reduce<OP>(t, lds);
     if (threadIdx.x == 0) T::put(out_o, 0, t);
     __syncthreads();

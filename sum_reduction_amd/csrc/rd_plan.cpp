@@ -5,14 +5,15 @@
 // max_blocks_per_SM) and worry that a grid of a few hundred blocks is too
 // small for the chip (POPCORNBENCH problem-47 trace, grid sizing discussion).
 //
-// Measured on MI355X (256 CUs, HBM3E), a read stream runs fastest with every
-// CU busy but few waves per CU: about 8 MB of 16-byte loads in flight over
-// the chip (32 KB per CU) saturates HBM, and more concurrent streams cost
-// DRAM locality.  So the planner aims for at least one workgroup per CU and
-// about 32 * CU 16-byte loads in flight per lane-wave, splits a reduction
-// along R only when its natural parallelism is below that, and turns on the
-// streaming hint, which keeps a once-read stream from allocating in the
-// caches (it was worth 10-15% on every path).
+// Measured on MI355X (256 CUs, HBM3E): a column reduction saturates HBM with
+// every CU busy and a few waves per CU (about 8 MB of 16-byte loads in flight
+// over the chip), so it is split along R only when its natural parallelism is
+// below that.  Long rows read fastest as many short-lived workgroups, each
+// streaming one piece of about 128 KB, rather than as a few long streams far
+// apart in memory: the row planner cuts them into such pieces (and combines
+// the piece results in a second pass).  Every path takes the streaming hint,
+// which keeps a once-read stream from allocating in the caches (it was worth
+// 10-15% on every path).
 #include <string.h>
 
 #include "rd_internal.h"
@@ -27,6 +28,16 @@ constexpr int64_t kMidInputLo = int64_t(256) << 20;
 constexpr int64_t kMidInputHi = int64_t(1) << 30;
 // Defaults measured on MI355X for the two kernels.
 constexpr int kRowsUnrollBlock = 16;  // 256-lane groups
+// Row pieces of about kPieceFloats floats (128 KB): long rows read by many
+// workgroups of one such piece each, five resident per CU, move faster than
+// by a few workgroups streaming far apart (measured on MI355X: the 1D sum of
+// 1e9 floats 1.6 % faster than with one piece per CU, [100, 1e7] rows 27 %,
+// [8192, 131072] 27 %; neutral at 1e8, where the pieces were already that
+// short).  Rows that already give every CU a workgroup are cut only when the
+// input reaches kPieceSplitBytes (at [1000, 100000], 400 MB, the second pass
+// costs more than the pieces gain).
+constexpr int64_t kPieceFloats = 32768;
+constexpr int64_t kPieceSplitBytes = int64_t(1) << 30;
 constexpr int kRowsUnrollWave = 8;    // 64-lane groups
 constexpr int kColsUnroll = 4;
 constexpr int kColsMaxColWaves = 8;
@@ -80,23 +91,27 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
 
     const int64_t nvec = R / 4;
     const int64_t groups_per_block = kBlock / p->group;
+    // every lane gets at least one full unrolled step of loads
+    int64_t cap = nvec / (int64_t(p->group) * p->unroll);
+    if (cap < 1) cap = 1;
+    const int64_t pieces = ceil_div(R, kPieceFloats);
     int64_t P = 1;
     if (t && t->split) {
         P = t->split;
         if (P < 1) return RD_ERR_INVALID_ARG;
     } else if (outer < int64_t(cu) * groups_per_block) {
         // fewer rows than one workgroup per CU: cut each row into pieces,
-        // one per CU -- or eight per CU for inputs between the last-level
-        // cache's 256 MB and 1 GB, where the uneven finish of 256 long
-        // streams is a visible share of the time (measured: n = 1e8 and 2e8
-        // floats 6-9% faster with 2048 pieces; 4e8 and 1e9 fastest with 256)
+        // at least one per CU -- eight per CU for inputs between the
+        // last-level cache's 256 MB and 1 GB, where the uneven finish of a
+        // few long streams showed (n = 1e8 and 2e8 floats 6-9% faster with
+        // 2048 pieces than 256) -- and pieces of at most about kPieceFloats
         const int64_t bytes = outer * R * int64_t(sizeof(float));
         const int64_t per_cu = (bytes > kMidInputLo && bytes <= kMidInputHi) ? 8 : 1;
         P = ceil_div(int64_t(cu) * per_cu * groups_per_block, outer);
-        // every lane gets at least one full unrolled step of loads
-        int64_t cap = nvec / (int64_t(p->group) * p->unroll);
-        if (cap < 1) cap = 1;
+        if (P < pieces) P = pieces;
         if (P > cap) P = cap;
+    } else if (pieces > 1 && outer * R >= kPieceSplitBytes / int64_t(sizeof(float))) {
+        P = pieces < cap ? pieces : cap;
     }
     if (P > INT64_MAX / result_bytes(op) / outer) return RD_ERR_INVALID_ARG;
     p->split = P;

@@ -53,10 +53,11 @@ def test_workload_plans():
              else rd.rd_plan_dim(CU, w.outer, w.R, w.inner))
         check_invariants(p, w.outer, w.R, w.inner)
         plans[name] = p.as_dict()
-    # the 1D reduce of 1e9: one workgroup per CU, each streaming one
-    # contiguous piece, one partial each
+    # the 1D reduce of 1e9: pieces of 32768 floats (8192 16-byte chunks, two
+    # unrolled steps of a 256-lane group), one workgroup and one partial each
     assert plans["normal_1e9"]["path"] == "rows"
-    assert plans["normal_1e9"]["blocks"] == CU
+    assert plans["normal_1e9"]["split"] == -(-10**9 // 32768) == 30518
+    assert plans["normal_1e9"]["blocks"] == 30518
     assert plans["normal_1e9"]["order"] == "blocked"
     assert plans["normal_1e9"]["combine"] == "pass"
     assert plans["normal_1e9"]["passes"] == 2
@@ -75,6 +76,27 @@ def test_workload_plans():
     assert plans["rows_32768x32768"]["group"] == 256
     assert plans["rows_32768x32768"]["split"] == 1
     assert plans["rows_32768x32768"]["blocks"] == 32768
+
+
+def test_row_pieces():
+    """Long rows are cut into pieces of about 32768 floats: always when there
+    are fewer rows than CUs, otherwise from 1 GB of input on; never below one
+    full unrolled step (16 x 16 bytes) per lane."""
+    def P(outer, R):
+        return rd.rd_plan_dim(CU, outer, R, 1).split
+    assert P(1, 10**6) == 61                 # one step per lane caps it
+    assert P(1, 10**7) == 306                # ceil(1e7 / 32768) > one per CU
+    assert P(1, 10**8) == 3052
+    assert P(100, 10**7) == 306
+    assert P(1000, 100_000) == 1             # 400 MB, a row per workgroup already
+    assert P(300, 10**6) == 31               # 1.2 GB
+    assert P(8192, 131072) == 4
+    assert P(32768, 32768) == 1              # the problem-91 rows are one piece each
+    assert P(256, 1 << 22) == 128
+    for outer, R in ((1, 3 * 10**9 // 4), (7, 10**8), (2000, 1 << 20)):
+        p = rd.rd_plan_dim(CU, outer, R, 1)
+        span = -(-(-(-(R // 4) // p.split)) // 256) * 256   # chunks per piece
+        assert span * 4 <= 32768 and span >= 4096, (outer, R, p.split)
 
 
 def test_problem47_lane_columns():
