@@ -8,8 +8,11 @@
  *               axis of a contiguous [outer, R, inner] array)
  *
  * the same with another operator (sum of squares, maximum, minimum) --
- * rd_reduce_1d, rd_reduce_dim -- and the cumulative sum along the middle
- * axis, forward or reverse -- rd_cumsum_dim.
+ * rd_reduce_1d, rd_reduce_dim --, the softmax denominator's pair (maximum,
+ * shifted sum of exponentials) -- rd_softmax_denom_1d, rd_softmax_denom_dim
+ * --, the cumulative sum along the middle axis, forward or reverse --
+ * rd_cumsum_dim --, and each axis operation over a strided view read in
+ * place -- rd_reduce_strided, rd_softmax_denom_strided, rd_cumsum_strided.
  *
  * The full reduce is the 1D float32 sum of the "High-Performance Reduction
  * Kernels" README (its kernel ladder: float4 loads, per-block partials, a
@@ -27,7 +30,9 @@
  *   them.  They must be 4-byte aligned -- no 16-byte alignment is required --
  *   and the output range must not overlap the input range (the cumulative
  *   sum may also write in place, out == x).  x must hold outer*R*inner (or
- *   n) contiguous floats, out outer*inner (or 1; the cumulative sum: as x).
+ *   n) contiguous floats -- a strided entry point: every element of its view
+ *   --, out outer*inner (or 1; the cumulative sum: outer*R*inner) contiguous
+ *   floats.
  * Streams.  Work is enqueued on `stream` (0 = the null stream) of the current
  *   device and the call returns without waiting; out is valid once the
  *   stream is synchronised.  No device-to-host transfer happens inside a call.
@@ -83,8 +88,8 @@ typedef enum rd_op {
                                               empty: -Inf */
     RD_OP_MIN = 3,   /* minimum, IEEE 754-2019 empty: +Inf */
     RD_OP_SOFTMAX_DENOM = 4  /* the pair (max x, sum exp(x - c)); only for
-                                rd_softmax_denom_1d / rd_softmax_denom_dim
-                                and rd_tune_supported */
+                                rd_softmax_denom_1d / _dim / _strided and
+                                rd_tune_supported */
 } rd_op;
 
 typedef enum rd_status {
