@@ -165,8 +165,9 @@ rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
  * (stride_outer = R*inner, stride_r = inner, stride_inner = 1) gives the bits
  * rd_reduce_dim gives.  Status codes as for rd_reduce_dim.  Source: the
  * POPCORNBENCH problem-47 trace reduces a torch tensor over one dimension
- * (torch.sum(x, dim)), which accepts any strided tensor; the survey of the
- * pages lists strided views beside small inner sizes.
+ * (torch.sum(x, dim)), which accepts any strided tensor, and its discussion
+ * of thread-to-element mappings weighs reads strided along the reduced axis
+ * against reads along the contiguous one.
  */
 rd_status rd_reduce_strided(const float* x, int64_t outer, int64_t R, int64_t inner,
                             int64_t stride_outer, int64_t stride_r, int64_t stride_inner,
