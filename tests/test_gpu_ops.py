@@ -226,3 +226,44 @@ def test_torch_style_reduce():
         sq = (a.astype(np.int64) ** 2).sum(axis=dim).astype(np.float32)
         assert np.array_equal(rd.reduce(x, "sumsq", dim).cpu().numpy(), sq)
     assert rd.reduce(x, "max").item() == float(a.max())
+
+
+@pytest.mark.parametrize("combine", [1, 2], ids=["pass", "last_block"])
+def test_many_pieces(combine):
+    """Tens of thousands of row pieces (most of them empty past the data's
+    end): the piece results are joined four per 16-byte load, 16 loads in
+    flight per lane, over several rounds and a ragged tail of 1-3 pieces;
+    every operator and the softmax pair, bit-exact on integer (0 / -Inf)
+    data, with the second pass and with the fused last-workgroup combine."""
+    n = (1 << 22) + 7
+    pieces = [4095, 4096, 4097, 16385, 65537]
+    lib = rd.load()
+    for op in ("sum", "sumsq", "max", "min"):
+        with rd.tuning(group=256, unroll=16, split=pieces[0], combine=combine):
+            assert rd.rd_plan_1d(256, n).split == pieces[0]
+        _data_op = _data(n + 1, 760 + rd.OPS[op], op)
+        dev = H.upload(_data_op)
+        slots = H.OutSlots([1] * len(pieces))
+        for k, P in enumerate(pieces):
+            with rd.tuning(group=256, unroll=16, split=P, combine=combine):
+                st = lib.rd_reduce_1d(dev.data_ptr(), n, rd.OPS[op], slots.ptr(k),
+                                      H.stream_handle())
+            assert st == 0, (op, P, rd.rd_status_string(st))
+        outs = slots.fetch()
+        S, _ = oracle.reduce_1d(_data_op[:n], op)
+        for k, P in enumerate(pieces):
+            H.assert_bitwise_equal_oracle(outs[k], [S], "%s P=%d combine=%d" % (op, P, combine))
+    bits = workloads.small_ints(n, 770, 0, 1)
+    mask = np.where(bits > 0, np.float32(0), np.float32(-np.inf)).astype(np.float32)
+    dev = H.upload(mask)
+    slots = H.OutSlots([1, 1] * len(pieces))
+    for k, P in enumerate(pieces):
+        with rd.tuning(group=256, unroll=16, split=P, combine=combine):
+            st = lib.rd_softmax_denom_1d(dev.data_ptr(), n, slots.ptr(2 * k),
+                                         slots.ptr(2 * k + 1), H.stream_handle())
+        assert st == 0, ("softmax", P, rd.rd_status_string(st))
+    outs = slots.fetch()
+    M, Ssm = oracle.softmax_denom_dim(mask, 1, n, 1)
+    for k, P in enumerate(pieces):
+        H.assert_bitwise_equal_oracle(outs[2 * k], M.reshape(-1), "softmax max P=%d" % P)
+        H.assert_bitwise_equal_oracle(outs[2 * k + 1], Ssm.reshape(-1), "softmax sum P=%d" % P)
