@@ -661,8 +661,8 @@ def report_one(w, op, host, x, out, flush, threads, cu, args):
 
     warm = timed(False)
     cold = timed(True)
-    plan = (rd.rd_plan_1d(cu, w.numel) if w.full_reduce
-            else rd.rd_plan_dim(cu, w.outer, w.R, w.inner)).as_dict()
+    plan = (rd.rd_plan_reduce(cu, 1, w.numel, 1, op) if w.full_reduce
+            else rd.rd_plan_reduce(cu, w.outer, w.R, w.inner, op)).as_dict()
     if args.no_oracle:
         return {"workload": w.name, "op": op, "shape": list(w.shape),
                 "algorithmic_bytes": nbytes, "warm": warm, "cold": cold,

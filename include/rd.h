@@ -340,10 +340,16 @@ typedef struct rd_plan {
     int64_t workspace_bytes; /* stream-ordered scratch (0 if passes == 1) */
 } rd_plan;
 
-/* Plan of rd_sum_dim for that shape on a device with cu_count CUs (the
- * other operators use the same plan). */
+/* Plan of rd_sum_dim for that shape on a device with cu_count CUs (the sum
+ * of squares, maximum and minimum use the same plan). */
 rd_status rd_plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
                       rd_plan* plan);
+
+/* Plan of rd_reduce_dim with operator op, or of rd_softmax_denom_dim for
+ * op = RD_OP_SOFTMAX_DENOM (whose long rows are cut into pieces twice as
+ * long as the others'). */
+rd_status rd_plan_reduce(int cu_count, int64_t outer, int64_t R, int64_t inner, int32_t op,
+                         rd_plan* plan);
 
 /* Plan of rd_sum_1d (the same as rd_plan_dim(cu_count, 1, n, 1, plan)). */
 rd_status rd_plan_1d(int cu_count, int64_t n, rd_plan* plan);

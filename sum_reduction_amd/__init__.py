@@ -23,7 +23,7 @@ from typing import Optional
 __all__ = [
     "RdError", "RdPlan", "RdTune", "library_path", "load", "rd_sum_1d", "rd_sum_dim",
     "rd_status_string", "rd_last_hip_error", "rd_version", "rd_plan_dim",
-    "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "sum", "tuning",
+    "rd_plan_1d", "rd_plan_reduce", "rd_tune_set", "rd_tune_supported", "sum", "tuning",
     "PATH_NAMES", "OPS", "rd_reduce_1d", "rd_reduce_dim", "reduce", "rd_cumsum_dim",
     "rd_plan_cumsum", "cumsum", "rd_cumsum_strided", "rd_plan_cumsum_strided",
     "rd_softmax_denom_1d", "rd_softmax_denom_dim", "softmax_denom", "rd_reduce_strided",
@@ -135,6 +135,8 @@ def load():
     lib.rd_version.restype = ctypes.c_int
     lib.rd_plan_dim.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(RdPlan)]
     lib.rd_plan_dim.restype = ctypes.c_int
+    lib.rd_plan_reduce.argtypes = [ctypes.c_int, i64, i64, i64, i32, ctypes.POINTER(RdPlan)]
+    lib.rd_plan_reduce.restype = ctypes.c_int
     lib.rd_plan_1d.argtypes = [ctypes.c_int, i64, ctypes.POINTER(RdPlan)]
     lib.rd_plan_1d.restype = ctypes.c_int
     lib.rd_tune_set.argtypes = [ctypes.POINTER(RdTune)]
@@ -166,6 +168,16 @@ def rd_plan_dim(cu_count: int, outer: int, R: int, inner: int) -> RdPlan:
     plan = RdPlan()
     _check(load().rd_plan_dim(cu_count, outer, R, inner, ctypes.byref(plan)),
            "rd_plan_dim")
+    return plan
+
+
+def rd_plan_reduce(cu_count: int, outer: int, R: int, inner: int, op="sum") -> RdPlan:
+    """Plan of rd_reduce_dim with ``op`` ("sum", "sumsq", "max", "min") or of
+    rd_softmax_denom_dim (op="softmax_denom")."""
+    plan = RdPlan()
+    code = OP_SOFTMAX_DENOM if op == "softmax_denom" else _op_code(op)
+    _check(load().rd_plan_reduce(cu_count, outer, R, inner, code, ctypes.byref(plan)),
+           "rd_plan_reduce")
     return plan
 
 

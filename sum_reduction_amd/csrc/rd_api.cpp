@@ -472,6 +472,13 @@ rd_status rd_plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner,
                         plan);
 }
 
+rd_status rd_plan_reduce(int cu_count, int64_t outer, int64_t R, int64_t inner, int32_t op,
+                         rd_plan* plan) {
+    if (op < RD_OP_SUM || op > RD_OP_SOFTMAX_DENOM) return RD_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return rd::plan_dim(cu_count, outer, R, inner, op, g_tune_on ? &g_tune : nullptr, plan);
+}
+
 rd_status rd_plan_1d(int cu_count, int64_t n, rd_plan* plan) {
     return rd_plan_dim(cu_count, 1, n, 1, plan);
 }

@@ -35,8 +35,12 @@ constexpr int kRowsUnrollBlock = 16;  // 256-lane groups
 // [8192, 131072] 27 %; neutral at 1e8, where the pieces were already that
 // short).  Rows that already give every CU a workgroup are cut only when the
 // input reaches kPieceSplitBytes (at [1000, 100000], 400 MB, the second pass
-// costs more than the pieces gain).
+// costs more than the pieces gain).  The softmax denominator's pieces are
+// twice as long: its per-piece epilogue joins pairs, and 65536-float pieces
+// measured best for it (1e9 floats: 576 us against 583 us with 32768; its
+// [100, 1e7] rows 563 against 566 us).
 constexpr int64_t kPieceFloats = 32768;
+constexpr int64_t kPieceFloatsSoftmax = 65536;
 constexpr int64_t kPieceSplitBytes = int64_t(1) << 30;
 constexpr int kRowsUnrollWave = 8;    // 64-lane groups
 constexpr int kColsUnroll = 4;
@@ -94,7 +98,8 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
     // every lane gets at least one full unrolled step of loads
     int64_t cap = nvec / (int64_t(p->group) * p->unroll);
     if (cap < 1) cap = 1;
-    const int64_t pieces = ceil_div(R, kPieceFloats);
+    const int64_t pieces =
+        ceil_div(R, op == RD_OP_SOFTMAX_DENOM ? kPieceFloatsSoftmax : kPieceFloats);
     int64_t P = 1;
     if (t && t->split) {
         P = t->split;

@@ -99,6 +99,19 @@ def test_row_pieces():
         assert span * 4 <= 32768 and span >= 4096, (outer, R, p.split)
 
 
+def test_softmax_row_pieces_are_twice_as_long():
+    for outer, R in ((1, 10**9), (100, 10**7), (8192, 131072), (3, 5000)):
+        s = rd.rd_plan_reduce(CU, outer, R, 1, "sum").as_dict()
+        for op in ("sumsq", "max", "min"):
+            assert rd.rd_plan_reduce(CU, outer, R, 1, op).as_dict() == s
+        assert s == rd.rd_plan_dim(CU, outer, R, 1).as_dict()
+    assert rd.rd_plan_reduce(CU, 1, 10**9, 1, "softmax_denom").split == -(-10**9 // 65536)
+    assert rd.rd_plan_reduce(CU, 100, 10**7, 1, "softmax_denom").split == 153
+    assert rd.rd_plan_reduce(CU, 8192, 131072, 1, "softmax_denom").split == 2
+    with pytest.raises(ValueError):
+        rd.rd_plan_reduce(CU, 1, 10, 1, "mean")
+
+
 def test_problem47_lane_columns():
     """The trace's count: 4095 = 1023 * 4 + 3, so 1024 lane-columns per row,
     the last holding 3 columns; 128 * 4095 = 524160 outputs."""
