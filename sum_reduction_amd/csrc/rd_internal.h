@@ -111,9 +111,17 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* tune, rd_pla
 rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
                       const rd_tune* tune, rd_plan* plan);
 // Row pieces of the row scan are whole multiples of kScanTile positions (a
-// multiple of every chunk size, 256 * slices).
+// multiple of every wave chunk, 256 * slices, and of a workgroup's 4-slice
+// chunk; a piece that is no multiple of the chunk ends with a partial one).
 constexpr int64_t kScanTile = 4096;
-constexpr int kScanRowsChunkSlices = 4;   // 1024-element chunks by default
+// Row scans: 8-slice chunks (2048 positions a wave), and a workgroup per
+// row from kScanRowsBlockMinR positions on when rows are not cut into
+// pieces.  Measured on MI355X, same box, interleaved: [32768, 32768] 1666 us
+// (wave, 4 slices) -> 1629 (wave, 8) -> 1570 (workgroup, 8); [1024, 2^20]
+// 1833 -> 1675 -> 1657; rows of 10000, and rows cut into pieces, are faster
+// by waves (a workgroup's barrier per chunk does not pay for itself there).
+constexpr int kScanRowsChunkSlices = 8;
+constexpr int64_t kScanRowsBlockMinR = 32768;
 constexpr int64_t kScanRowWavesMin = 4;   // rows per CU below which rows are cut
 constexpr int64_t kScanRowWavesSplit = 16;  // pieces per CU once they are cut
 constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan

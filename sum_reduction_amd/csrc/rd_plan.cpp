@@ -433,6 +433,7 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         p->path = RD_PATH_SCAN_ROWS;
         p->unroll = (t && t->unroll) ? t->unroll : kScanRowsChunkSlices;
         if (p->unroll != 4 && p->unroll != 8) return RD_ERR_INVALID_ARG;
+        if (t && t->group && t->group != kWave && t->group != kBlock) return RD_ERR_INVALID_ARG;
         const int64_t tiles = ceil_div(R, kScanTile);
         int64_t P = 1;
         if (t && t->split) {
@@ -446,7 +447,11 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         P = ceil_div(R, L);
         p->split = P;
         p->rows_per_split = L;
-        const int64_t b = ceil_div(outer * P, kBlock / kWave);
+        // a workgroup per item for long uncut rows (adjacent waves on adjacent
+        // stretches of one row), else a wave per item
+        p->group = (t && t->group) ? t->group
+                                   : (P == 1 && R >= kScanRowsBlockMinR ? kBlock : kWave);
+        const int64_t b = ceil_div(outer * P, kBlock / p->group);
         p->blocks = b < kMaxBlocks ? b : kMaxBlocks;
         if (P > 1) {
             p->passes = 3;

@@ -238,6 +238,143 @@ __global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_ro
     }
 }
 
+// The row scan with a workgroup per item instead of a wave.  The item's
+// positions are walked in block chunks of 4 waves x K slices: wave w scans
+// the K slices [c0 + w*256K, c0 + (w+1)*256K) of chunk c0 as a wave does
+// above (in-lane sums of 4, DPP across the wave), the four wave totals meet
+// in LDS (two slot sets in turn, so one barrier per chunk suffices), and
+// wave w's outputs start from the block carry plus the totals of the waves
+// before it; the block carry then grows by the four totals in wave order.
+// Adjacent waves stream adjacent 1-4 KB of one row, which HBM serves faster
+// than four rows apart (a copy of 128 KB pieces measured 5.5 TB/s by
+// workgroups against 5.0-5.2 by waves).  The next chunk's loads are issued
+// before the current chunk is scanned (a barrier does not wait for them).
+template <bool REV, int K, bool NT, bool OUT>
+__device__ __forceinline__ float block_chunk(const float* row, float* orow, int64_t R,
+                                             int64_t qw, int64_t q_end, bool tail,
+                                             int64_t lq, const v4f (&v)[K], float carry,
+                                             float* slots, int wave) {
+    constexpr int kWaves = kBlock / kWave;
+    float e[K], tot[K];
+    v4f s[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        s[k].x = v[k].x;
+        s[k].y = s[k].x + v[k].y;
+        s[k].z = s[k].y + v[k].z;
+        s[k].w = s[k].z + v[k].w;
+        const float incl = wave_scan_inclusive(s[k].w);
+        e[k] = dpp_or_zero<0x138>(incl);  // wave_shr:1
+        tot[k] = lane63(incl);
+    }
+    float wt = tot[0];
+#pragma unroll
+    for (int k = 1; k < K; ++k) wt = wt + tot[k];
+    if (threadIdx.x % kWave == 0) slots[wave] = wt;
+    __syncthreads();
+    float mine = carry, next = carry;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const float t = slots[w];
+        if (w < wave) mine = mine + t;
+        next = next + t;
+    }
+    if constexpr (OUT) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float pre = mine + e[k];
+            const v4f y = v4f{pre + s[k].x, pre + s[k].y, pre + s[k].z, pre + s[k].w};
+            mine = mine + tot[k];
+            if (tail)
+                store_q4_tail<REV>(orow, R, qw + 256 * k + lq, q_end, y);
+            else
+                store_q4<REV, NT>(orow, R, qw + 256 * k + lq, y);
+        }
+    }
+    return next;
+}
+
+// One item's positions [q_begin, q_end) from carry (OUT: outputs stored;
+// otherwise only the total is computed).  Every thread of the block calls it.
+template <bool REV, int K, bool NT, bool OUT>
+__device__ __forceinline__ float block_piece(const float* row, float* orow, int64_t R,
+                                             int64_t q_begin, int64_t q_end, float carry,
+                                             float (&slots)[2][kBlock / kWave], int& parity) {
+    constexpr int64_t kSpan = 256 * K;                     // a wave's positions per chunk
+    constexpr int64_t kChunk = (kBlock / kWave) * kSpan;   // the block's positions per chunk
+    const int wave = threadIdx.x / kWave;
+    const int64_t lq = 4 * (threadIdx.x % kWave);
+    const int64_t nfull = (q_end - q_begin) / kChunk;
+    const int64_t qw = q_begin + wave * kSpan;  // this wave's window in chunk 0
+    v4f a[K], b[K];
+    if (nfull > 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[k] = load_q4<REV, NT>(row, R, qw + 256 * k + lq);
+    }
+    // full chunks two at a time (a, then b), the next chunk's loads first
+    int64_t c = 0;
+    for (; c + 2 <= nfull; c += 2) {
+        const int64_t q0 = qw + c * kChunk;
+#pragma unroll
+        for (int k = 0; k < K; ++k) b[k] = load_q4<REV, NT>(row, R, q0 + kChunk + 256 * k + lq);
+        __builtin_amdgcn_sched_barrier(0);
+        carry = block_chunk<REV, K, NT, OUT>(row, orow, R, q0, q_end, false, lq, a, carry,
+                                             slots[parity], wave);
+        parity ^= 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 2 < nfull) {
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                a[k] = load_q4<REV, NT>(row, R, q0 + 2 * kChunk + 256 * k + lq);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        carry = block_chunk<REV, K, NT, OUT>(row, orow, R, q0 + kChunk, q_end, false, lq, b,
+                                             carry, slots[parity], wave);
+        parity ^= 1;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (c < nfull) {  // one full chunk left, in a
+        carry = block_chunk<REV, K, NT, OUT>(row, orow, R, qw + c * kChunk, q_end, false, lq, a,
+                                             carry, slots[parity], wave);
+        parity ^= 1;
+    }
+    const int64_t qt = q_begin + nfull * kChunk;
+    if (qt < q_end) {  // the last, partial chunk
+        const int64_t q0 = qt + wave * kSpan;
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[k] = load_q4_tail<REV>(row, R, q0 + 256 * k + lq, q_end);
+        carry = block_chunk<REV, K, NT, OUT>(row, orow, R, q0, q_end, true, lq, a, carry,
+                                             slots[parity], wave);
+        parity ^= 1;
+    }
+    return carry;
+}
+
+// Item = (row o, piece p) as in scan_rows_kernel, one workgroup per item.
+template <bool REV, int K, bool NT>
+__global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_rows_block_kernel(
+    const float* x, float* out, int64_t outer, int64_t R, int64_t so,
+    int64_t P, int64_t L, const float* __restrict__ carry_in, float* __restrict__ totals) {
+    __shared__ float slots[2][kBlock / kWave];
+    const int64_t nitems = outer * P;
+    int parity = 0;
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const int64_t o = item / P;
+        const int64_t p = item - o * P;
+        const int64_t q_begin = p * L;
+        const int64_t q_end = q_begin + L < R ? q_begin + L : R;
+        if (totals == nullptr) {
+            const float carry = carry_in != nullptr ? carry_in[item] : 0.f;
+            block_piece<REV, K, NT, true>(x + o * so, out + o * R, R, q_begin, q_end, carry,
+                                          slots, parity);
+        } else {
+            const float t = block_piece<REV, K, NT, false>(x + o * so, nullptr, R, q_begin,
+                                                           q_end, 0.f, slots, parity);
+            if (threadIdx.x == 0) totals[item] = t;
+        }
+    }
+}
+
 // Exclusive scan of the P piece totals of each row, in piece order:
 // carries[o*P + p] = totals[o*P] + ... + totals[o*P + p - 1] (summed as the
 // chunks are: lane-sequential within 4, DPP across the wave, a carry across
@@ -823,6 +960,13 @@ int64_t grid_for(int64_t items) {
 template <bool REV, int K>
 hipError_t rows_k(const rd_plan& p, const float* x, float* out, const Strides& v,
                   const float* carry_in, float* totals, hipStream_t s) {
+    if (p.group == kBlock) {  // a workgroup per item
+        if (p.nontemporal)
+            return launch(scan_rows_block_kernel<REV, K, true>, p.blocks, kBlock, s, x, out,
+                          v.outer, v.R, v.so, p.split, p.rows_per_split, carry_in, totals);
+        return launch(scan_rows_block_kernel<REV, K, false>, p.blocks, kBlock, s, x, out,
+                      v.outer, v.R, v.so, p.split, p.rows_per_split, carry_in, totals);
+    }
     if (p.nontemporal)
         return launch(scan_rows_kernel<REV, K, true>, p.blocks, kBlock, s, x, out, v.outer, v.R,
                       v.so, p.split, p.rows_per_split, carry_in, totals);

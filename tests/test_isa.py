@@ -6,7 +6,7 @@ Checked: no packed-FP32 arithmetic anywhere (the library is compiled with
 that feature off; with it on, hipcc -O3 turns the reduce kernels' float4
 adds into some 17,000 packed instructions), and the hot loops keep the loads in flight that their
 kernel shapes promise -- the 1D / row reduce 16 16-byte loads per lane, the
-column reduce 4, the row scan a chunk of 4 slices, the column scan 8 rows --
+column reduce 4, the row scan a chunk of 8 slices, the column scan 8 rows --
 issued back to back before the first wait on them, with the streaming hint.
 """
 import os
@@ -86,7 +86,8 @@ def _load_runs(body):
 
 def test_the_library_has_the_kernels(kernels):
     for part in ("rows_kernel", "cols_kernel", "cols_small_kernel", "rows_short_tile_kernel",
-                 "strided_kernel", "scan_rows_kernel", "scan_cols_kernel", "scan_small_kernel",
+                 "strided_kernel", "scan_rows_kernel", "scan_rows_block_kernel",
+                 "scan_cols_kernel", "scan_small_kernel",
                  "scan_tile_out_kernel", "scan_tile_in_kernel", "scan_strided_kernel"):
         assert any(part in n for n in kernels), part
 
@@ -101,7 +102,7 @@ def test_no_packed_fp32_arithmetic(kernels):
 @pytest.mark.parametrize("parts,loads", [
     (("rows_kernelILi0ELi256ELi16ELb1E",), 16),          # 1D / row sum, U = 16
     (("cols_kernelILi0ELi8ELi1ELi4ELb1E",), 4),          # column sum, U = 4
-    (("scan_rows_kernelILb1ELi4ELb1E",), 4),             # reverse row scan, 4 slices
+    (("scan_rows_block_kernelILb1ELi8ELb1E",), 8),       # reverse row scan, 8 slices
     (("scan_cols_kernelILb1ELi4ELi8ELi8ELb1E",), 8),     # column scan, 8 rows
 ], ids=["rows_sum", "cols_sum", "scan_rows", "scan_cols"])
 def test_hot_loops_keep_their_loads_in_flight(kernels, parts, loads):
