@@ -427,9 +427,10 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         return RD_ERR_INVALID_ARG;
     if (forced == RD_PATH_SCAN_COLS_SMALL && inner > 2 * kSmallInner) return RD_ERR_INVALID_ARG;
     if (inner == 1) {
-        // one wave per row piece; pieces only when there are too few rows to
-        // keep kScanRowWavesMin waves per CU busy (then: piece totals, their
-        // scan, the scan from the carries -- x is read twice)
+        // a wave or a workgroup per row piece; pieces only when there are
+        // too few rows to keep kScanRowWavesMin waves per CU busy (then:
+        // piece totals, their scan, the scan from the carries -- x is read
+        // twice)
         p->path = RD_PATH_SCAN_ROWS;
         p->unroll = (t && t->unroll) ? t->unroll : kScanRowsChunkSlices;
         if (p->unroll != 4 && p->unroll != 8) return RD_ERR_INVALID_ARG;
