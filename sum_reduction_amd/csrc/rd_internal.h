@@ -124,7 +124,11 @@ constexpr int kScanRowsChunkSlices = 8;
 constexpr int64_t kScanRowsBlockMinR = 32768;
 constexpr int64_t kScanRowWavesMin = 4;   // rows per CU below which rows are cut
 constexpr int64_t kScanRowWavesSplit = 16;  // pieces per CU once they are cut
-constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan
+constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan,
+// 16 for slabs of kScanColsDeepRows rows or more (same box, interleaved:
+// [128, 4096, 4095] 3369 -> 3285 us, [16, 8192, 4096] 1073 -> 1055; short
+// slabs -- [64, 512, 1024], 64 rows -- lose 3-5 % with 16)
+constexpr int64_t kScanColsDeepRows = 1024;
 constexpr int kScanSmallUnroll = 8;       // load instructions per step, small inner
 constexpr int64_t kScanSmallWavesPerCu = 16;
 // Inputs up to this size are read by a split scan's totals pass without the

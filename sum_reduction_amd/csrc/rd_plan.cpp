@@ -511,6 +511,8 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
     }
     if (S < 1) return RD_ERR_INVALID_ARG;
     split_rows(R, S, p);
+    // slabs of at least kScanColsDeepRows rows keep 16 rows in flight
+    if (!(t && t->unroll) && p->rows_per_split >= kScanColsDeepRows) p->unroll = 16;
     // a block per (col_waves adjacent tiles, slab, outer index): the widest
     // of 16, 8, 4 tiles that still gives every CU a block
     const int64_t tiles = ceil_div(lane_cols, kWave);

@@ -6,7 +6,7 @@ Checked: no packed-FP32 arithmetic anywhere (the library is compiled with
 that feature off; with it on, hipcc -O3 turns the reduce kernels' float4
 adds into some 17,000 packed instructions), and the hot loops keep the loads in flight that their
 kernel shapes promise -- the 1D / row reduce 16 16-byte loads per lane, the
-column reduce 4, the row scan a chunk of 8 slices, the column scan 8 rows --
+column reduce 4, the row scan a chunk of 8 slices, the column scan 16 rows --
 issued back to back before the first wait on them, with the streaming hint.
 """
 import os
@@ -103,7 +103,7 @@ def test_no_packed_fp32_arithmetic(kernels):
     (("rows_kernelILi0ELi256ELi16ELb1E",), 16),          # 1D / row sum, U = 16
     (("cols_kernelILi0ELi8ELi1ELi4ELb1E",), 4),          # column sum, U = 4
     (("scan_rows_block_kernelILb1ELi8ELb1E",), 8),       # reverse row scan, 8 slices
-    (("scan_cols_kernelILb1ELi4ELi8ELi8ELb1E",), 8),     # column scan, 8 rows
+    (("scan_cols_kernelILb1ELi4ELi16ELi8ELb1E",), 16),   # column scan, 16 rows
 ], ids=["rows_sum", "cols_sum", "scan_rows", "scan_cols"])
 def test_hot_loops_keep_their_loads_in_flight(kernels, parts, loads):
     # per run: the 16-byte loads with the streaming hint
