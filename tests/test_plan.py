@@ -217,19 +217,21 @@ def test_tuning_override():
 
 
 def test_default_plans_are_built_for_every_operator():
-    """Whatever the planner picks by default exists for every operator."""
+    """Whatever the planner picks by default for an operator is built for it
+    (the sum's small-inner slabs may take a depth the others do not have)."""
     rng = np.random.default_rng(1)
-    ops = ("sum", "sumsq", "max", "min")
-    for _ in range(2000):
+    ops = ("sum", "sumsq", "max", "min", "softmax_denom")
+    for _ in range(1000):
         outer, R, inner = (int(v) for v in np.exp(rng.uniform(0, 12, 3)).astype(np.int64))
-        p = rd.rd_plan_dim(CU, outer, R, inner).as_dict()
-        if p["path"] == "rows":
-            assert all(rd.rd_tune_supported("rows", p["group"], 0, p["unroll"], op) for op in ops)
-        if p["path"] == "cols":
-            assert all(rd.rd_tune_supported("cols", p["col_waves"], p["row_waves"], p["unroll"], op)
-                       for op in ops)
-        if p["path"] == "cols_small":
-            assert all(rd.rd_tune_supported("cols_small", 0, 0, p["unroll"], op) for op in ops)
+        for op in ops:
+            p = rd.rd_plan_reduce(CU, outer, R, inner, op).as_dict()
+            if p["path"] == "rows":
+                assert rd.rd_tune_supported("rows", p["group"], 0, p["unroll"], op)
+            if p["path"] == "cols":
+                assert rd.rd_tune_supported("cols", p["col_waves"], p["row_waves"], p["unroll"],
+                                            op)
+            if p["path"] == "cols_small":
+                assert rd.rd_tune_supported("cols_small", 0, 0, p["unroll"], op), (op, p)
 
 
 def _scan_invariants(p, outer, R, inner):
