@@ -859,31 +859,13 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
     const int keep = int(c - cl);  // 0, or 1..3 for the row's last lane-column
     const int64_t nitems = S * outer;
     const int64_t wstride = int64_t(gridDim.x) * kWaves;
-    for (int64_t item = xcd_block(nxcd) * kWaves + wave; item < nitems; item += wstride) {
+    const int64_t step = int64_t(RPW) * sr;
+    const float fill = T::fill();
+
+    // the row phases of each lane-column joined by a fixed tree, then stored
+    auto finish = [&](int64_t item, typename T::S4 (&acc)[2]) {
         const int64_t o = item / S;
         const int64_t s = item - o * S;
-        const int64_t r0 = s * rps + rho;
-        const int64_t r1 = (s + 1) * rps < R ? (s + 1) * rps : R;
-        const int64_t m = r0 < r1 ? (r1 - r0 + RPW - 1) / RPW : 0;
-        typename T::S4 acc[2] = {T::start4(), T::start4()};
-        if (active) {
-            const float* p = x + o * so + r0 * sr + cl;
-            const int64_t step = int64_t(RPW) * sr;
-            const float fill = T::fill();
-            int64_t k = 0;
-            for (; k + U <= m; k += U) {
-                v4f v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = loadv<V, NT>(p + u * step, fill);
-                T::template fold_all<U>(acc, v);
-                p += U * step;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (k + u < m)
-                    acc[u & 1] = T::fold(acc[u & 1], loadv<V, NT>(p + u * step, fill));
-        }
-        // join the row phases of each lane-column by a fixed tree
         typename T::S4 a = T::join(acc[0], acc[1]);
         if (LC == 1) {
 #pragma unroll
@@ -903,6 +885,68 @@ __global__ __launch_bounds__(kBlock) void cols_small_kernel(
                 for (int q = 0; q < V; ++q) T::put(dst, e + q, T::lane(a, q));
             }
         }
+    };
+
+    if (rps <= int64_t(RPW) * U && nitems > wstride) {
+        // Every item is one step of at most U load instructions and a wave
+        // has several: it issues the next item's loads before it folds,
+        // joins and stores the current one, so short items (a few KB) do not
+        // each wait out a memory round trip.  Instructions past the item's
+        // rows load the neutral fill, which every fold leaves unchanged.
+        auto load_item = [&](int64_t item, v4f (&v)[U]) {
+            const int64_t o = item / S;
+            const int64_t s = item - o * S;
+            const int64_t r0 = s * rps + rho;
+            const int64_t r1 = (s + 1) * rps < R ? (s + 1) * rps : R;
+            const int64_t m = active && r0 < r1 ? (r1 - r0 + RPW - 1) / RPW : 0;
+            const float* p = x + o * so + r0 * sr + cl;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = u < m ? loadv<V, NT>(p + u * step, fill) : v4f{fill, fill, fill, fill};
+        };
+        int64_t item = xcd_block(nxcd) * kWaves + wave;
+        if (item >= nitems) return;
+        v4f cur[U], nxt[U];
+        load_item(item, cur);
+        for (;;) {
+            const int64_t next = item + wstride;
+            const bool more = next < nitems;
+            if (more) load_item(next, nxt);
+            __builtin_amdgcn_sched_barrier(0);  // the next item's loads go out first
+            typename T::S4 acc[2] = {T::start4(), T::start4()};
+            T::template fold_all<U>(acc, cur);
+            finish(item, acc);
+            if (!more) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+            item = next;
+        }
+        return;
+    }
+
+    for (int64_t item = xcd_block(nxcd) * kWaves + wave; item < nitems; item += wstride) {
+        const int64_t o = item / S;
+        const int64_t s = item - o * S;
+        const int64_t r0 = s * rps + rho;
+        const int64_t r1 = (s + 1) * rps < R ? (s + 1) * rps : R;
+        const int64_t m = r0 < r1 ? (r1 - r0 + RPW - 1) / RPW : 0;
+        typename T::S4 acc[2] = {T::start4(), T::start4()};
+        if (active) {
+            const float* p = x + o * so + r0 * sr + cl;
+            int64_t k = 0;
+            for (; k + U <= m; k += U) {
+                v4f v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u] = loadv<V, NT>(p + u * step, fill);
+                T::template fold_all<U>(acc, v);
+                p += U * step;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (k + u < m)
+                    acc[u & 1] = T::fold(acc[u & 1], loadv<V, NT>(p + u * step, fill));
+        }
+        finish(item, acc);
     }
 }
 

@@ -44,6 +44,12 @@ constexpr int64_t kPieceFloatsSoftmax = 65536;
 constexpr int64_t kPieceSplitBytes = int64_t(1) << 30;
 constexpr int kRowsUnrollWave = 8;    // 64-lane groups
 constexpr int kColsUnroll = 4;
+// Workgroups per CU for small-inner items of a single load step (a wave
+// prefetches its next item).  Same box, A/B of 4, 8, 16, 64 and no cap:
+// 64 was fastest on every such shape measured ([1048576, 256, 2] 408 ->
+// 328 us, [2097152, 128, 2] 698 -> 514, [524288, 128, 4] 218 -> 182,
+// [262144, 64, 8] 128 -> 115 against a wave per item).
+constexpr int64_t kTinyItemBlocksPerCu = 64;
 constexpr int kColsMaxColWaves = 8;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -188,6 +194,15 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
         split_rows(R, S, p);
         if (p->split > INT64_MAX / result_bytes(op) / (outer * inner)) return RD_ERR_INVALID_ARG;
         p->blocks = ceil_div(p->split * outer, waves_per_block);
+        // items of one load step each: a wave takes many in turn, each
+        // item's loads issued while the one before is joined and stored --
+        // except full single steps of 12-byte rows, which measured faster
+        // a wave per item ([1048576, 256, 3]: 434 us against 503; yet
+        // [4194304, 32, 3], a partial step, 1209 -> 1031 us)
+        const bool one_step = p->rows_per_split <= rpw * p->unroll;
+        const bool full_step_of_3 = inner == 3 && p->rows_per_split == rpw * p->unroll;
+        if (one_step && !full_step_of_3 && p->blocks > int64_t(cu) * kTinyItemBlocksPerCu)
+            p->blocks = int64_t(cu) * kTinyItemBlocksPerCu;
         if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
         p->passes = p->split > 1 ? 2 : 1;
         p->combine = p->split > 1 ? RD_COMBINE_PASS : RD_COMBINE_NONE;

@@ -20,7 +20,7 @@ def _clear_tuning():
     rd.rd_tune_set(None)
 
 
-def check_invariants(p, outer, R, inner):
+def check_invariants(p, outer, R, inner, cu=CU):
     d = p.as_dict()
     assert 1 <= p.blocks <= MAX_BLOCKS or d["path"] == "none", d
     if d["path"] in ("rows", "rows_short"):
@@ -43,7 +43,12 @@ def check_invariants(p, outer, R, inner):
             assert p.block_threads == 64 * p.col_waves * p.row_waves <= 1024
     if d["path"] == "cols_small":
         assert 2 <= inner <= 128
-        assert p.blocks == min(-(-(p.split * outer) // 4), MAX_BLOCKS)
+        blocks = -(-(p.split * outer) // 4)              # a wave per item
+        rpw = 64 // -(-inner // 4)
+        full_step_of_3 = inner == 3 and p.rows_per_split == rpw * p.unroll
+        if p.rows_per_split <= rpw * p.unroll and not full_step_of_3:   # one load step per
+            blocks = min(blocks, 64 * cu)                 # item: waves take several in turn
+        assert p.blocks == min(blocks, MAX_BLOCKS)
 
 
 def test_workload_plans():
@@ -146,7 +151,7 @@ def test_random_shapes_keep_invariants():
             continue
         for cu in (1, 32, 80, 256, 304):
             p = rd.rd_plan_dim(cu, outer, R, inner)
-            check_invariants(p, outer, R, inner)
+            check_invariants(p, outer, R, inner, cu)
 
 
 def test_column_tile_width():
