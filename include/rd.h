@@ -45,9 +45,11 @@
  *   workgroup of the first kernel sums them instead; the integer ticket
  *   counter that elects it belongs to the stream (one per stream and device,
  *   reset by the kernel itself), so calls on one stream, which never overlap,
- *   never share it with calls on another, and a call made while its stream
- *   is being captured into a graph falls back to the second kernel: same
- *   bits either way.
+ *   never share it with calls on another.  A call that needs a workspace is
+ *   refused with RD_ERR_CAPTURE while its stream is being captured into a
+ *   graph (a replay of such a capture faulted in the second kernel, reading
+ *   the graph-allocated workspace; the cause is not established); calls
+ *   whose plan needs no workspace (one kernel) can be captured.
  * Semantics.  IEEE fp32 adds, round to nearest even, no flush of denormals,
  *   NaN and Inf propagate.  Accumulators start at +0.0, so the empty sum is
  *   +0.0 and an all -0.0 input sums to +0.0.  R == 0 writes outer*inner zeros;
@@ -99,7 +101,9 @@ typedef enum rd_status {
     RD_ERR_NO_DEVICE = 2,   /* no usable HIP device */
     RD_ERR_ALLOC = 3,       /* the stream-ordered workspace could not be had */
     RD_ERR_LAUNCH = 4,      /* a kernel launch was rejected */
-    RD_ERR_HIP = 5          /* another HIP runtime call failed */
+    RD_ERR_HIP = 5,         /* another HIP runtime call failed */
+    RD_ERR_CAPTURE = 6      /* the call needs a stream-ordered workspace and
+                               its stream is being captured into a graph */
 } rd_status;
 
 /*

@@ -53,6 +53,16 @@ uint32_t* make_tickets() {
     return t;
 }
 
+// True when `stream` is being captured into a graph (or its state cannot be
+// read).  A call whose plan needs a workspace is refused then: a replay of a
+// captured stream-ordered workspace faulted in the second kernel that reads
+// it, and the cause is not established.
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &cap) != hipSuccess ||
+           cap != hipStreamCaptureStatusNone;
+}
+
 // The ticket counter of `stream`, or null for the two-kernel combine (stream
 // being captured, or every counter taken).
 uint32_t* stream_ticket(Device& d, hipStream_t stream) {
@@ -147,6 +157,7 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
     if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
     if (p.workspace_bytes > 0) {
+        if (capturing(s)) return RD_ERR_CAPTURE;
         if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
         hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
                                               size_t(p.workspace_bytes), dev.pool, s);
@@ -243,6 +254,7 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
     if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
     if (p.workspace_bytes > 0) {
+        if (capturing(stream)) return RD_ERR_CAPTURE;
         if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
         hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
                                               size_t(p.workspace_bytes), dev->pool, stream);
@@ -455,6 +467,7 @@ const char* rd_status_string(rd_status status) {
         case RD_ERR_ALLOC: return "RD_ERR_ALLOC";
         case RD_ERR_LAUNCH: return "RD_ERR_LAUNCH";
         case RD_ERR_HIP: return "RD_ERR_HIP";
+        case RD_ERR_CAPTURE: return "RD_ERR_CAPTURE";
     }
     return "RD_ERR_UNKNOWN";
 }

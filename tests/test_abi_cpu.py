@@ -62,9 +62,9 @@ def test_ceiling_probes_export_their_header():
 
 def test_version_and_status_strings():
     assert rd.rd_version() == 100
-    names = [rd.rd_status_string(s) for s in range(6)]
+    names = [rd.rd_status_string(s) for s in range(7)]
     assert names == ["RD_OK", "RD_ERR_INVALID_ARG", "RD_ERR_NO_DEVICE", "RD_ERR_ALLOC",
-                     "RD_ERR_LAUNCH", "RD_ERR_HIP"]
+                     "RD_ERR_LAUNCH", "RD_ERR_HIP", "RD_ERR_CAPTURE"]
     assert rd.rd_status_string(99) == "RD_ERR_UNKNOWN"
 
 

@@ -6,6 +6,14 @@ denominator and a split cumulative sum -- and is replayed several times with
 eager work in between that changes the inputs; every replay must give the
 bits of an eager call on the same inputs.  No call inside the library clears
 memory with a memset node: the workspaces are written before they are read.
+
+Skipped: the first replay of this graph once faulted (a memory aperture
+violation in slab_combine_kernel, the second kernel of the [3, 50000, 70]
+axis reduce, reading its graph-allocated workspace) after the plan of that
+call changed; the same calls run eagerly are in bounds and pass, and the
+cause was not established.  Until it is, the library refuses a call that
+needs a workspace on a capturing stream (RD_ERR_CAPTURE), and these tests
+stay off the GPU.
 """
 import numpy as np
 import pytest
@@ -24,6 +32,11 @@ def _eager(xs):
             rd.rd_cumsum_dim(x4, 1, 3 << 20, 1, reverse=True)]
 
 
+SKIP_REASON = ("a replay of a captured workspace faulted on the GPU; cause not established, "
+               "capture of workspace plans is refused (RD_ERR_CAPTURE) until it is")
+
+
+@pytest.mark.skip(reason=SKIP_REASON)
 def test_graph_replays_match_eager_calls():
     t = H.torch()
     rng = [workloads.random(n, 1000 + k, "normal") for k, n in
