@@ -286,8 +286,8 @@ typedef enum rd_path {
     RD_PATH_COLS_SMALL = 5,  /* 2 <= inner <= 128: a wave loads 64 / ceil(inner/4)
                                 adjacent rows per instruction */
     RD_PATH_SCAN_ROWS = 6,   /* cumulative sum, inner == 1: a wave (group
-                                64) or a workgroup (group 256) per row
-                                (piece) */
+                                64) or a workgroup of group threads (256,
+                                512 or 1024) per row (piece) */
     RD_PATH_SCAN_COLS = 7,   /* cumulative sum, inner > 128: a lane per 4
                                 columns, a workgroup of col_waves waves per
                                 tile group */
@@ -323,7 +323,8 @@ typedef struct rd_plan {
     int32_t path;            /* rd_path */
     int32_t block_threads;   /* threads per workgroup of the main pass */
     int32_t group;           /* ROWS, SCAN_ROWS: lanes that share one row
-                                piece (64|256) */
+                                piece (ROWS 64|256, SCAN_ROWS 64|256|512|
+                                1024) */
     int32_t col_waves;       /* COLS, SCAN_COLS: waves side by side across
                                 columns */
     int32_t row_waves;       /* COLS: waves of one workgroup taking turns in R */
@@ -368,9 +369,9 @@ rd_status rd_plan_strided(int cu_count, int64_t outer, int64_t R, int64_t inner,
                           rd_plan* plan);
 
 /* Plan of rd_cumsum_dim for that shape (the tuning override's split,
- * unroll -- SCAN_ROWS 4 or 8, SCAN_COLS 4, 8 or 16 --, group -- SCAN_ROWS 64
- * or 256 --, col_waves -- SCAN_COLS 4, 8 or 16 -- and nontemporal fields
- * apply). */
+ * unroll -- SCAN_ROWS 4 or 8, SCAN_COLS 4, 8 or 16 --, group -- SCAN_ROWS 64,
+ * 256, 512 or 1024 --, col_waves -- SCAN_COLS 4, 8 or 16 -- and nontemporal
+ * fields apply). */
 rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
                          rd_plan* plan);
 
@@ -390,7 +391,8 @@ rd_status rd_plan_cumsum_strided(int cu_count, int64_t outer, int64_t R, int64_t
  * respect to concurrent reductions; pass NULL to clear.
  */
 typedef struct rd_tune {
-    int32_t group;           /* ROWS, SCAN_ROWS: 64 or 256 */
+    int32_t group;           /* ROWS: 64 or 256; SCAN_ROWS: 64, 256, 512
+                                or 1024 */
     int32_t col_waves;       /* COLS; SCAN_COLS: 4, 8 or 16 */
     int32_t row_waves;       /* COLS */
     int32_t unroll;          /* ROWS, COLS: 2, 4, 8 or 16 (scans: see

@@ -114,14 +114,25 @@ rd_status plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
 // multiple of every wave chunk, 256 * slices, and of a workgroup's 4-slice
 // chunk; a piece that is no multiple of the chunk ends with a partial one).
 constexpr int64_t kScanTile = 4096;
-// Row scans: 8-slice chunks (2048 positions a wave), and a workgroup per
-// row from kScanRowsBlockMinR positions on when rows are not cut into
-// pieces.  Measured on MI355X, same box, interleaved: [32768, 32768] 1666 us
-// (wave, 4 slices) -> 1629 (wave, 8) -> 1570 (workgroup, 8); [1024, 2^20]
-// 1833 -> 1675 -> 1657; rows of 10000, and rows cut into pieces, are faster
-// by waves (a workgroup's barrier per chunk does not pay for itself there).
+// Row scans: 8-slice chunks (2048 positions a wave); rows longer than
+// kScanRowsBlockMinR positions that are not cut into pieces take a workgroup
+// of 8 waves (chunks of 16384 positions), from kScanRowsWideMinR on one of
+// 16 (chunks of 32768).  A workgroup's chunk is 8 or 16 times a wave's, so
+// a row of a chunk or less leaves no next chunk to load while one is
+// scanned; 16 waves fill a CU alone, so they need rows of two chunks.
+// Measured on MI355X (each line on one box, interleaved), forward / reverse,
+// us:
+//   R        wave        4 waves     8 waves     16 waves
+//   4096     1580/1507   1396/1436   1820/2157   5542/6069
+//   16384    1591/1571   1652/1604   1668/1675   1918/2037
+//   20000    1511/1513   1487/1506   1446/1394   1589/1649
+//   32768    1685/1669   1556/1566   1510/1539   1598/1679
+//   68559    --          1550/1570   1512/1525   1434/1460
+//   262144   1654/1638   1588/1580   1556/1554   1507/1503
+// (1 GiB of input each; rows cut into pieces are faster by waves).
 constexpr int kScanRowsChunkSlices = 8;
-constexpr int64_t kScanRowsBlockMinR = 32768;
+constexpr int64_t kScanRowsBlockMinR = 16384;
+constexpr int64_t kScanRowsWideMinR = 65536;
 constexpr int64_t kScanRowWavesMin = 4;   // rows per CU below which rows are cut
 constexpr int64_t kScanRowWavesSplit = 16;  // pieces per CU once they are cut
 constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan,

@@ -455,7 +455,9 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         p->path = RD_PATH_SCAN_ROWS;
         p->unroll = (t && t->unroll) ? t->unroll : kScanRowsChunkSlices;
         if (p->unroll != 4 && p->unroll != 8) return RD_ERR_INVALID_ARG;
-        if (t && t->group && t->group != kWave && t->group != kBlock) return RD_ERR_INVALID_ARG;
+        if (t && t->group && t->group != kWave && t->group != kBlock &&
+            t->group != 2 * kBlock && t->group != 4 * kBlock)
+            return RD_ERR_INVALID_ARG;
         const int64_t tiles = ceil_div(R, kScanTile);
         int64_t P = 1;
         if (t && t->split) {
@@ -469,12 +471,19 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         P = ceil_div(R, L);
         p->split = P;
         p->rows_per_split = L;
-        // a workgroup per item for long uncut rows (adjacent waves on adjacent
-        // stretches of one row), else a wave per item
-        p->group = (t && t->group) ? t->group
-                                   : (P == 1 && R >= kScanRowsBlockMinR ? kBlock : kWave);
-        const int64_t b = ceil_div(outer * P, kBlock / p->group);
+        // long uncut rows: a workgroup per row (adjacent waves on adjacent
+        // stretches of it) -- 8 waves, 16 for rows of two of their chunks or
+        // more; with 4-slice chunks (kernels built for 8 waves a SIMD, where
+        // wider workgroups spill) 4 waves --; else a wave per item
+        int32_t group = kWave;
+        if (P == 1 && R > kScanRowsBlockMinR)
+            group = p->unroll == 4 ? kBlock : R >= kScanRowsWideMinR ? 16 * kWave : 8 * kWave;
+        p->group = (t && t->group) ? t->group : group;
+        // a workgroup of 256 threads holds 4 wave items; a wider group is one
+        // workgroup per item
+        const int64_t b = p->group == kWave ? ceil_div(outer * P, kBlock / kWave) : outer * P;
         p->blocks = b < kMaxBlocks ? b : kMaxBlocks;
+        p->block_threads = p->group == kWave ? kBlock : p->group;
         if (P > 1) {
             p->passes = 3;
             p->combine = RD_COMBINE_PASS;

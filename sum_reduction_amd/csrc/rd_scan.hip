@@ -76,10 +76,13 @@ __device__ __forceinline__ void store_q4(float* row, int64_t R, int64_t q, v4f y
 }
 
 // Positions q .. q + 3, those below q_end only (the others read as 0 / are
-// not written): the last chunk of a row.
-template <bool REV>
-__device__ __forceinline__ v4f load_q4_tail(const float* row, int64_t R, int64_t q,
+// not written): the partial chunk of a row piece.  A lane whose 4 positions
+// are all below q_end makes one 16-byte access, the lane across q_end one
+// access per position.
+template <bool REV, bool NT>
+__device__ __forceinline__ v4f load_q4_part(const float* row, int64_t R, int64_t q,
                                             int64_t q_end) {
+    if (q + 4 <= q_end) return load_q4<REV, NT>(row, R, q);
     v4f v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -87,9 +90,13 @@ __device__ __forceinline__ v4f load_q4_tail(const float* row, int64_t R, int64_t
     return v;
 }
 
-template <bool REV>
-__device__ __forceinline__ void store_q4_tail(float* row, int64_t R, int64_t q, int64_t q_end,
+template <bool REV, bool NT>
+__device__ __forceinline__ void store_q4_part(float* row, int64_t R, int64_t q, int64_t q_end,
                                               v4f y) {
+    if (q + 4 <= q_end) {
+        store_q4<REV, NT>(row, R, q, y);
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         if (q + j < q_end) row[REV ? R - 1 - (q + j) : q + j] = y[j];
@@ -145,55 +152,76 @@ __device__ __forceinline__ float rows_step(const float* row, float* orow, int64_
     return carry;
 }
 
-// The full chunks of [q_begin, q_end) (then the partial one), two buffers in
-// turn; every load fetches a chunk that is then scanned.
+// nfull full chunks from position qf, the first already loaded into a; two
+// buffers in turn, every load fetches a chunk that is then scanned.
+template <bool REV, int K, bool NT, bool OUT>
+__device__ __forceinline__ float rows_full(const float* row, float* orow, int64_t R, int64_t qf,
+                                           int64_t nfull, int64_t lq, v4f (&a)[K], v4f (&b)[K],
+                                           float carry) {
+    constexpr int64_t kChunk = 256 * K;
+    int64_t c = 0;
+    for (; c + 2 < nfull; c += 2) {  // chunks c, c + 1; loads c + 1, c + 2
+        const int64_t q0 = qf + c * kChunk;
+        carry = rows_step<REV, K, NT, OUT>(row, orow, R, q0, q0 + kChunk, lq, a, b, carry);
+        carry = rows_step<REV, K, NT, OUT>(row, orow, R, q0 + kChunk, q0 + 2 * kChunk, lq, b, a,
+                                           carry);
+    }
+    // one or two chunks left, the first in a
+    const int64_t q0 = qf + c * kChunk;
+    v4f y[K];
+    if (c + 1 < nfull) {
+        carry = rows_step<REV, K, NT, OUT>(row, orow, R, q0, q0 + kChunk, lq, a, b, carry);
+        carry = scan_chunk<K, OUT>(b, y, carry);
+        if constexpr (OUT) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) store_q4<REV, NT>(orow, R, q0 + kChunk + 256 * k + lq, y[k]);
+        }
+    } else {
+        carry = scan_chunk<K, OUT>(a, y, carry);
+        if constexpr (OUT) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) store_q4<REV, NT>(orow, R, q0 + 256 * k + lq, y[k]);
+        }
+    }
+    return carry;
+}
+
+// The positions [q_begin, q_end) of a row piece, walked by one wave.  When
+// the piece is no whole number of chunks, its partial chunk comes first: its
+// loads go out together with those of the first full chunk, and the piece
+// ends on a full chunk (a partial chunk at the end would wait for its loads
+// after all the others, one memory latency per piece).
 template <bool REV, int K, bool NT, bool OUT>
 __device__ __forceinline__ float rows_piece(const float* row, float* orow, int64_t R,
                                             int64_t q_begin, int64_t q_end, int lane,
                                             float carry) {
     constexpr int64_t kChunk = 256 * K;
     const int64_t lq = 4 * lane;
-    const int64_t nfull = q_end > q_begin ? (q_end - q_begin) / kChunk : 0;
+    const int64_t n = q_end > q_begin ? q_end - q_begin : 0;
+    const int64_t nfull = n / kChunk;
+    const int64_t qf = q_begin + (n - nfull * kChunk);  // the first full chunk
     v4f a[K], b[K];
-    if (nfull > 0) {
+    if (qf > q_begin) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) a[k] = load_q4<REV, NT>(row, R, q_begin + 256 * k + lq);
-        int64_t c = 0;
-        for (; c + 2 < nfull; c += 2) {  // chunks c, c + 1; loads c + 1, c + 2
-            const int64_t q0 = q_begin + c * kChunk;
-            carry = rows_step<REV, K, NT, OUT>(row, orow, R, q0, q0 + kChunk, lq, a, b, carry);
-            carry = rows_step<REV, K, NT, OUT>(row, orow, R, q0 + kChunk, q0 + 2 * kChunk, lq, b,
-                                               a, carry);
+        for (int k = 0; k < K; ++k) a[k] = load_q4_part<REV, NT>(row, R, q_begin + 256 * k + lq, qf);
+        if (nfull > 0) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) b[k] = load_q4<REV, NT>(row, R, qf + 256 * k + lq);
         }
-        // one or two chunks left, the first in a
-        const int64_t q0 = q_begin + c * kChunk;
+        __builtin_amdgcn_sched_barrier(0);
         v4f y[K];
-        if (c + 1 < nfull) {
-            carry = rows_step<REV, K, NT, OUT>(row, orow, R, q0, q0 + kChunk, lq, a, b, carry);
-            carry = scan_chunk<K, OUT>(b, y, carry);
-            if constexpr (OUT) {
-#pragma unroll
-                for (int k = 0; k < K; ++k)
-                    store_q4<REV, NT>(orow, R, q0 + kChunk + 256 * k + lq, y[k]);
-            }
-        } else {
-            carry = scan_chunk<K, OUT>(a, y, carry);
-            if constexpr (OUT) {
-#pragma unroll
-                for (int k = 0; k < K; ++k) store_q4<REV, NT>(orow, R, q0 + 256 * k + lq, y[k]);
-            }
-        }
-    }
-    const int64_t qt = q_begin + nfull * kChunk;
-    if (qt < q_end) {  // the row's last, partial chunk
-        v4f y[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) a[k] = load_q4_tail<REV>(row, R, qt + 256 * k + lq, q_end);
         carry = scan_chunk<K, OUT>(a, y, carry);
         if constexpr (OUT) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) store_q4_tail<REV>(orow, R, qt + 256 * k + lq, q_end, y[k]);
+            for (int k = 0; k < K; ++k)
+                store_q4_part<REV, NT>(orow, R, q_begin + 256 * k + lq, qf, y[k]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (nfull > 0) carry = rows_full<REV, K, NT, OUT>(row, orow, R, qf, nfull, lq, b, a, carry);
+    } else if (nfull > 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[k] = load_q4<REV, NT>(row, R, qf + 256 * k + lq);
+        carry = rows_full<REV, K, NT, OUT>(row, orow, R, qf, nfull, lq, a, b, carry);
     }
     return carry;
 }
@@ -238,23 +266,24 @@ __global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_ro
     }
 }
 
-// The row scan with a workgroup per item instead of a wave.  The item's
-// positions are walked in block chunks of 4 waves x K slices: wave w scans
-// the K slices [c0 + w*256K, c0 + (w+1)*256K) of chunk c0 as a wave does
-// above (in-lane sums of 4, DPP across the wave), the four wave totals meet
-// in LDS (two slot sets in turn, so one barrier per chunk suffices), and
+// The row scan with a workgroup of NW waves per item instead of a wave.  The
+// item's positions are walked in block chunks of NW waves x K slices: wave w
+// scans the K slices [c0 + w*256K, c0 + (w+1)*256K) of chunk c0 as a wave
+// does above (in-lane sums of 4, DPP across the wave), the NW wave totals
+// meet in LDS (two slot sets in turn, so one barrier per chunk suffices), and
 // wave w's outputs start from the block carry plus the totals of the waves
-// before it; the block carry then grows by the four totals in wave order.
-// Adjacent waves stream adjacent 1-4 KB of one row, which HBM serves faster
-// than four rows apart (a copy of 128 KB pieces measured 5.5 TB/s by
-// workgroups against 5.0-5.2 by waves).  The next chunk's loads are issued
-// before the current chunk is scanned (a barrier does not wait for them).
-template <bool REV, int K, bool NT, bool OUT>
+// before it; the block carry then grows by the NW totals in wave order.
+// Adjacent waves stream adjacent 1-8 KB of one row, which HBM serves faster
+// than rows apart, and the wider the block chunk the faster (copies of
+// 128 KB rows, a workgroup per row, measured on MI355X: 4 waves x 8 KB
+// steps 5.57 TB/s, 16 waves taking the whole row at once 6.0 TB/s).  The
+// next chunk's loads are issued before the current chunk is scanned (a
+// barrier does not wait for them).
+template <bool REV, int NW, int K, bool NT, bool OUT>
 __device__ __forceinline__ float block_chunk(const float* row, float* orow, int64_t R,
-                                             int64_t qw, int64_t q_end, bool tail,
+                                             int64_t qw, int64_t q_end, bool part,
                                              int64_t lq, const v4f (&v)[K], float carry,
                                              float* slots, int wave) {
-    constexpr int kWaves = kBlock / kWave;
     float e[K], tot[K];
     v4f s[K];
 #pragma unroll
@@ -274,7 +303,7 @@ __device__ __forceinline__ float block_chunk(const float* row, float* orow, int6
     __syncthreads();
     float mine = carry, next = carry;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const float t = slots[w];
         if (w < wave) mine = mine + t;
         next = next + t;
@@ -285,8 +314,8 @@ __device__ __forceinline__ float block_chunk(const float* row, float* orow, int6
             const float pre = mine + e[k];
             const v4f y = v4f{pre + s[k].x, pre + s[k].y, pre + s[k].z, pre + s[k].w};
             mine = mine + tot[k];
-            if (tail)
-                store_q4_tail<REV>(orow, R, qw + 256 * k + lq, q_end, y);
+            if (part)
+                store_q4_part<REV, NT>(orow, R, qw + 256 * k + lq, q_end, y);
             else
                 store_q4<REV, NT>(orow, R, qw + 256 * k + lq, y);
         }
@@ -294,23 +323,18 @@ __device__ __forceinline__ float block_chunk(const float* row, float* orow, int6
     return next;
 }
 
-// One item's positions [q_begin, q_end) from carry (OUT: outputs stored;
-// otherwise only the total is computed).  Every thread of the block calls it.
-template <bool REV, int K, bool NT, bool OUT>
-__device__ __forceinline__ float block_piece(const float* row, float* orow, int64_t R,
-                                             int64_t q_begin, int64_t q_end, float carry,
-                                             float (&slots)[2][kBlock / kWave], int& parity) {
-    constexpr int64_t kSpan = 256 * K;                     // a wave's positions per chunk
-    constexpr int64_t kChunk = (kBlock / kWave) * kSpan;   // the block's positions per chunk
+// nfull full block chunks from position qf, the first already loaded into a
+// (this wave's window of it); two buffers in turn.
+template <bool REV, int NW, int K, bool NT, bool OUT>
+__device__ __forceinline__ float block_full(const float* row, float* orow, int64_t R,
+                                            int64_t qf, int64_t nfull, float carry,
+                                            v4f (&a)[K], v4f (&b)[K], float (&slots)[2][NW],
+                                            int& parity) {
+    constexpr int64_t kSpan = 256 * K;         // a wave's positions per chunk
+    constexpr int64_t kChunk = NW * kSpan;     // the block's positions per chunk
     const int wave = threadIdx.x / kWave;
     const int64_t lq = 4 * (threadIdx.x % kWave);
-    const int64_t nfull = (q_end - q_begin) / kChunk;
-    const int64_t qw = q_begin + wave * kSpan;  // this wave's window in chunk 0
-    v4f a[K], b[K];
-    if (nfull > 0) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) a[k] = load_q4<REV, NT>(row, R, qw + 256 * k + lq);
-    }
+    const int64_t qw = qf + wave * kSpan;  // this wave's window in the first chunk
     // full chunks two at a time (a, then b), the next chunk's loads first
     int64_t c = 0;
     for (; c + 2 <= nfull; c += 2) {
@@ -318,8 +342,8 @@ __device__ __forceinline__ float block_piece(const float* row, float* orow, int6
 #pragma unroll
         for (int k = 0; k < K; ++k) b[k] = load_q4<REV, NT>(row, R, q0 + kChunk + 256 * k + lq);
         __builtin_amdgcn_sched_barrier(0);
-        carry = block_chunk<REV, K, NT, OUT>(row, orow, R, q0, q_end, false, lq, a, carry,
-                                             slots[parity], wave);
+        carry = block_chunk<REV, NW, K, NT, OUT>(row, orow, R, q0, 0, false, lq, a, carry,
+                                                 slots[parity], wave);
         parity ^= 1;
         __builtin_amdgcn_sched_barrier(0);
         if (c + 2 < nfull) {
@@ -328,34 +352,69 @@ __device__ __forceinline__ float block_piece(const float* row, float* orow, int6
                 a[k] = load_q4<REV, NT>(row, R, q0 + 2 * kChunk + 256 * k + lq);
         }
         __builtin_amdgcn_sched_barrier(0);
-        carry = block_chunk<REV, K, NT, OUT>(row, orow, R, q0 + kChunk, q_end, false, lq, b,
-                                             carry, slots[parity], wave);
+        carry = block_chunk<REV, NW, K, NT, OUT>(row, orow, R, q0 + kChunk, 0, false, lq, b,
+                                                 carry, slots[parity], wave);
         parity ^= 1;
         __builtin_amdgcn_sched_barrier(0);
     }
     if (c < nfull) {  // one full chunk left, in a
-        carry = block_chunk<REV, K, NT, OUT>(row, orow, R, qw + c * kChunk, q_end, false, lq, a,
-                                             carry, slots[parity], wave);
-        parity ^= 1;
-    }
-    const int64_t qt = q_begin + nfull * kChunk;
-    if (qt < q_end) {  // the last, partial chunk
-        const int64_t q0 = qt + wave * kSpan;
-#pragma unroll
-        for (int k = 0; k < K; ++k) a[k] = load_q4_tail<REV>(row, R, q0 + 256 * k + lq, q_end);
-        carry = block_chunk<REV, K, NT, OUT>(row, orow, R, q0, q_end, true, lq, a, carry,
-                                             slots[parity], wave);
+        carry = block_chunk<REV, NW, K, NT, OUT>(row, orow, R, qw + c * kChunk, 0, false, lq, a,
+                                                 carry, slots[parity], wave);
         parity ^= 1;
     }
     return carry;
 }
 
-// Item = (row o, piece p) as in scan_rows_kernel, one workgroup per item.
-template <bool REV, int K, bool NT>
-__global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_rows_block_kernel(
-    const float* x, float* out, int64_t outer, int64_t R, int64_t so,
-    int64_t P, int64_t L, const float* __restrict__ carry_in, float* __restrict__ totals) {
-    __shared__ float slots[2][kBlock / kWave];
+// One item's positions [q_begin, q_end) from carry (OUT: outputs stored;
+// otherwise only the total is computed).  Every thread of the block calls it.
+// As in rows_piece, a partial chunk comes first, loaded together with the
+// first full chunk.
+template <bool REV, int NW, int K, bool NT, bool OUT>
+__device__ __forceinline__ float block_piece(const float* row, float* orow, int64_t R,
+                                             int64_t q_begin, int64_t q_end, float carry,
+                                             float (&slots)[2][NW], int& parity) {
+    constexpr int64_t kSpan = 256 * K;         // a wave's positions per chunk
+    constexpr int64_t kChunk = NW * kSpan;     // the block's positions per chunk
+    const int wave = threadIdx.x / kWave;
+    const int64_t lq = 4 * (threadIdx.x % kWave);
+    const int64_t n = q_end - q_begin;
+    const int64_t nfull = n / kChunk;
+    const int64_t qf = q_begin + (n - nfull * kChunk);  // the first full chunk
+    v4f a[K], b[K];
+    if (qf > q_begin) {
+        const int64_t qh = q_begin + wave * kSpan;  // this wave's window of the partial chunk
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[k] = load_q4_part<REV, NT>(row, R, qh + 256 * k + lq, qf);
+        if (nfull > 0) {
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                b[k] = load_q4<REV, NT>(row, R, qf + wave * kSpan + 256 * k + lq);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        carry = block_chunk<REV, NW, K, NT, OUT>(row, orow, R, qh, qf, true, lq, a, carry,
+                                                 slots[parity], wave);
+        parity ^= 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (nfull > 0)
+            carry = block_full<REV, NW, K, NT, OUT>(row, orow, R, qf, nfull, carry, b, a, slots,
+                                                    parity);
+    } else if (nfull > 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[k] = load_q4<REV, NT>(row, R, qf + wave * kSpan + 256 * k + lq);
+        carry = block_full<REV, NW, K, NT, OUT>(row, orow, R, qf, nfull, carry, a, b, slots,
+                                                parity);
+    }
+    return carry;
+}
+
+// Item = (row o, piece p) as in scan_rows_kernel, one workgroup of NW waves
+// per item.
+template <bool REV, int NW, int K, bool NT>
+__global__ __launch_bounds__(NW * kWave, scan_rows_waves_per_simd<K>()) void
+scan_rows_block_kernel(const float* x, float* out, int64_t outer, int64_t R, int64_t so,
+                       int64_t P, int64_t L, const float* __restrict__ carry_in,
+                       float* __restrict__ totals) {
+    __shared__ float slots[2][NW];
     const int64_t nitems = outer * P;
     int parity = 0;
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
@@ -365,10 +424,10 @@ __global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_ro
         const int64_t q_end = q_begin + L < R ? q_begin + L : R;
         if (totals == nullptr) {
             const float carry = carry_in != nullptr ? carry_in[item] : 0.f;
-            block_piece<REV, K, NT, true>(x + o * so, out + o * R, R, q_begin, q_end, carry,
+            block_piece<REV, NW, K, NT, true>(x + o * so, out + o * R, R, q_begin, q_end, carry,
                                           slots, parity);
         } else {
-            const float t = block_piece<REV, K, NT, false>(x + o * so, nullptr, R, q_begin,
+            const float t = block_piece<REV, NW, K, NT, false>(x + o * so, nullptr, R, q_begin,
                                                            q_end, 0.f, slots, parity);
             if (threadIdx.x == 0) totals[item] = t;
         }
@@ -957,15 +1016,26 @@ int64_t grid_for(int64_t items) {
     return b > kMaxBlocks ? kMaxBlocks : b;
 }
 
+template <bool REV, int NW, int K>
+hipError_t rows_block_k(const rd_plan& p, const float* x, float* out, const Strides& v,
+                        const float* carry_in, float* totals, hipStream_t s) {
+    if (p.nontemporal)
+        return launch(scan_rows_block_kernel<REV, NW, K, true>, p.blocks, NW * kWave, s, x, out,
+                      v.outer, v.R, v.so, p.split, p.rows_per_split, carry_in, totals);
+    return launch(scan_rows_block_kernel<REV, NW, K, false>, p.blocks, NW * kWave, s, x, out,
+                  v.outer, v.R, v.so, p.split, p.rows_per_split, carry_in, totals);
+}
+
 template <bool REV, int K>
 hipError_t rows_k(const rd_plan& p, const float* x, float* out, const Strides& v,
                   const float* carry_in, float* totals, hipStream_t s) {
-    if (p.group == kBlock) {  // a workgroup per item
-        if (p.nontemporal)
-            return launch(scan_rows_block_kernel<REV, K, true>, p.blocks, kBlock, s, x, out,
-                          v.outer, v.R, v.so, p.split, p.rows_per_split, carry_in, totals);
-        return launch(scan_rows_block_kernel<REV, K, false>, p.blocks, kBlock, s, x, out,
-                      v.outer, v.R, v.so, p.split, p.rows_per_split, carry_in, totals);
+    // a workgroup of group / 64 waves per item, or a wave per item
+    switch (p.group) {
+        case 4 * kWave: return rows_block_k<REV, 4, K>(p, x, out, v, carry_in, totals, s);
+        case 8 * kWave: return rows_block_k<REV, 8, K>(p, x, out, v, carry_in, totals, s);
+        case 16 * kWave: return rows_block_k<REV, 16, K>(p, x, out, v, carry_in, totals, s);
+        case kWave: break;
+        default: return hipErrorInvalidValue;
     }
     if (p.nontemporal)
         return launch(scan_rows_kernel<REV, K, true>, p.blocks, kBlock, s, x, out, v.outer, v.R,

@@ -128,6 +128,19 @@ void check_scan_plan(const rd::Strides& v, const rd_plan& p) {
             if (!tiles(v.R, p.split, p.rows_per_split)) fail("pieces do not tile R", v, -1, p);
             if (p.workspace_bytes != (p.split > 1 ? 8 * v.outer * p.split : 0))
                 fail("scan rows workspace", v, -1, p);
+            // a wave per item (4 to a 256-thread workgroup) or a workgroup of
+            // `group` threads per item
+            if (p.group == 64) {
+                if (p.block_threads != rd::kBlock ||
+                    p.blocks != std::min(rd::kMaxBlocks, (v.outer * p.split + 3) / 4))
+                    fail("scan rows wave grid", v, -1, p);
+            } else if (p.group == 256 || p.group == 512 || p.group == 1024) {
+                if (p.block_threads != p.group ||
+                    p.blocks != std::min(rd::kMaxBlocks, v.outer * p.split))
+                    fail("scan rows workgroup grid", v, -1, p);
+            } else {
+                fail("scan rows group", v, -1, p);
+            }
             break;
         case RD_PATH_SCAN_COLS:
         case RD_PATH_SCAN_COLS_SMALL:
@@ -168,7 +181,8 @@ int main(int argc, char** argv) {
         rd_tune t{};
         const bool tuned = rng() % 3 == 0;
         if (tuned) {
-            t.group = (rng() % 3 == 0) ? 0 : (rng() % 2 ? 64 : 256);
+            static const int32_t groups[] = {0, 64, 256, 512, 1024};
+            t.group = groups[rng() % 5];
             t.col_waves = int32_t(rng() % 5 == 0 ? 0 : 1 << (rng() % 5));
             t.row_waves = int32_t(rng() % 3 == 0 ? 0 : 1 << (rng() % 4));
             t.unroll = int32_t(rng() % 3 == 0 ? 0 : 1 << (rng() % 5));

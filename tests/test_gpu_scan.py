@@ -102,25 +102,29 @@ def test_unroll_variants(unroll, split, bw):
             _sweep(rows, [0, 3], 860 + unroll + split, "scan rows u%d s%d" % (unroll, split))
 
 
-BLOCK_ROWS = [(4, 1), (4, 3), (8, 1), (8, 7)]
+BLOCK_ROWS = [(g, u, s) for g in (256, 512, 1024) for (u, s) in ((4, 1), (4, 3), (8, 1), (8, 7))]
 
 
-@pytest.mark.parametrize("unroll,split", BLOCK_ROWS, ids=["u%d_s%d" % t for t in BLOCK_ROWS])
-def test_rows_by_workgroup(unroll, split):
-    """The row scan with a workgroup per item (group 256): four waves per
-    chunk of 4 x 256 x unroll positions, their totals joined in LDS, around
-    the chunk boundaries, with pieces, both directions, and in place."""
+@pytest.mark.parametrize("group,unroll,split", BLOCK_ROWS,
+                         ids=["g%d_u%d_s%d" % t for t in BLOCK_ROWS])
+def test_rows_by_workgroup(group, unroll, split):
+    """The row scan with a workgroup per item (group 256, 512 or 1024: 4, 8 or
+    16 waves per chunk of waves x 256 x unroll positions, their totals joined
+    in LDS), around the chunk boundaries, with pieces, both directions, and in
+    place."""
     rows = [(o, r, 1) for o in (1, 3) for r in (1, 63, 255, 256, 1023, 1025, 4095, 4096,
                                                 4097, 8191, 8192, 8193, 3 * 4096 + 5, 20000)]
-    rows += [(5, 65537, 1), (2, 1 << 17, 1)]
-    with rd.tuning(group=256, unroll=unroll, split=split):
-        assert rd.rd_plan_cumsum(256, 3, 20000, 1).group == 256
-        _sweep(rows, [0, 3], 880 + unroll + split, "scan rows wg u%d s%d" % (unroll, split))
-        a = workloads.small_ints(3 * 30001, 890 + unroll + split)
+    rows += [(5, 65537, 1), (2, 1 << 17, 1), (1, 32767, 1), (2, 32769, 1), (2, 98305, 1)]
+    tag = "g%d u%d s%d" % (group, unroll, split)
+    with rd.tuning(group=group, unroll=unroll, split=split):
+        p = rd.rd_plan_cumsum(256, 3, 20000, 1)
+        assert p.group == group and p.block_threads == group
+        _sweep(rows, [0, 3], 880 + group + unroll + split, "scan rows wg " + tag)
+        a = workloads.small_ints(3 * 30001, 890 + group + unroll + split)
         x = H.upload(a)
         rd.rd_cumsum_dim(x, 3, 30001, 1, reverse=True, out=x)
         S, _ = oracle.cumsum_dim(a, 3, 30001, 1, True)
-        H.assert_bitwise_equal_oracle(x.cpu().numpy(), S, "wg in place u%d s%d" % (unroll, split))
+        H.assert_bitwise_equal_oracle(x.cpu().numpy(), S, "wg in place " + tag)
 
 
 def test_default_splits():

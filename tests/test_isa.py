@@ -102,9 +102,10 @@ def test_no_packed_fp32_arithmetic(kernels):
 @pytest.mark.parametrize("parts,loads", [
     (("rows_kernelILi0ELi256ELi16ELb1E",), 16),          # 1D / row sum, U = 16
     (("cols_kernelILi0ELi8ELi1ELi4ELb1E",), 4),          # column sum, U = 4
-    (("scan_rows_block_kernelILb1ELi8ELb1E",), 8),       # reverse row scan, 8 slices
+    (("scan_rows_block_kernelILb1ELi8ELi8ELb1E",), 8),   # reverse row scan, 8 waves x 8 slices
+    (("scan_rows_block_kernelILb1ELi16ELi8ELb1E",), 8),  # the same, 16 waves
     (("scan_cols_kernelILb1ELi4ELi16ELi8ELb1E",), 16),   # column scan, 16 rows
-], ids=["rows_sum", "cols_sum", "scan_rows", "scan_cols"])
+], ids=["rows_sum", "cols_sum", "scan_rows", "scan_rows_wide", "scan_cols"])
 def test_hot_loops_keep_their_loads_in_flight(kernels, parts, loads):
     # per run: the 16-byte loads with the streaming hint
     streamed = [sum(1 for i in r if i.split()[0] == "global_load_dwordx4" and

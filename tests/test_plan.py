@@ -248,9 +248,16 @@ def _scan_invariants(p, outer, R, inner):
     assert p.split * p.rows_per_split >= R > (p.split - 1) * p.rows_per_split
     if inner == 1:
         assert p.rows_per_split % 4096 == 0           # whole tiles per piece
-        # a workgroup per uncut row of 32768 or more, else a wave per piece
-        assert p.group == (256 if p.split == 1 and R >= 32768 else 64)
-        assert p.blocks == min(-(-outer * p.split // (256 // p.group)), 1 << 20)
+        # a workgroup per uncut row of more than 16384 -- 16 waves from 65536
+        # on, else 8 --, else a wave per piece (4 to a workgroup)
+        want = 64 if p.split > 1 or R <= 16384 else 1024 if R >= 65536 else 512
+        assert p.group == want
+        if p.group == 64:
+            assert p.block_threads == 256
+            assert p.blocks == min(-(-outer * p.split // 4), 1 << 20)
+        else:
+            assert p.block_threads == p.group
+            assert p.blocks == min(outer * p.split, 1 << 20)
         ws = 2 * outer * p.split * 4 if p.split > 1 else 0
     elif inner <= 128:
         assert p.unroll in (4, 8)
@@ -268,13 +275,14 @@ def _scan_invariants(p, outer, R, inner):
 
 
 def test_cumsum_plans():
-    """Rows: a workgroup per row (problem 91: 32768 rows, no pieces); few rows
+    """Rows: a workgroup of 8 waves per row (problem 91: 32768 rows, no pieces,
+    two 16384-position chunks a row); few rows
     are cut into pieces of whole 4096-element tiles, a wave each.
     Columns: a wave per 64 lane-columns, slabs of R when there are too few
     waves."""
     p = rd.rd_plan_cumsum(CU, 32768, 32768, 1)
     assert p.as_dict()["path"] == "scan_rows" and p.split == 1 and p.blocks == 32768
-    assert p.group == 256 and p.unroll == 8
+    assert p.group == 512 and p.block_threads == 512 and p.unroll == 8
     assert p.workspace_bytes == 0
     p = rd.rd_plan_cumsum(CU, 1, 1 << 20, 1)
     assert p.split == 256 and p.rows_per_split == 4096 and p.passes == 3
