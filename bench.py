@@ -300,9 +300,10 @@ def main(argv=None):
 
 def measure_ceiling(src, achieved_gbs):
     """Bandwidth of trivial kernels on this GPU (librd_ceiling.so): a
-    grid-stride read of `src` and a copy of it, each over a few grid sizes,
-    best median of 10 event-timed launches.  Context for the roofline
-    fraction, which stays relative to the published 8 TB/s."""
+    grid-stride read of `src` over a few grid sizes, and a copy of it, grid-
+    stride or one 16-byte chunk per thread over a few workgroup sizes; best
+    median of 10 event-timed launches.  Context for the roofline fraction,
+    which stays relative to the published 8 TB/s."""
     import ctypes
 
     import torch
@@ -311,6 +312,7 @@ def measure_ceiling(src, achieved_gbs):
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.rd_ceiling_read.argtypes = [vp, i64, i32, vp, vp]
     lib.rd_ceiling_copy.argtypes = [vp, vp, i64, i32, vp]
+    lib.rd_ceiling_copy_flat.argtypes = [vp, vp, i64, i32, vp]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream or None
     n = src.numel() // 4 * 4
@@ -339,13 +341,18 @@ def measure_ceiling(src, achieved_gbs):
                         (256, 512, 1024, 2048, 4096, 8192), 4 * n)
     cp_gbs, cp_g = best(lambda g: lib.rd_ceiling_copy(src.data_ptr(), dst.data_ptr(), n, g, sh),
                         (2048, 8192, 32768), 8 * n)
+    fl_gbs, fl_t = best(lambda t: lib.rd_ceiling_copy_flat(src.data_ptr(), dst.data_ptr(), n, t,
+                                                           sh),
+                        (64, 256, 1024), 8 * n)
     del dst, sink
     torch.cuda.empty_cache()
-    return {"read_GBps": round(rd_gbs, 1), "read_blocks": rd_g, "copy_GBps": round(cp_gbs, 1),
-            "copy_blocks": cp_g, "bytes_read": 4 * n,
+    copy_shape = ("grid-stride, %d workgroups of 256" % cp_g if cp_gbs >= fl_gbs else
+                  "one 16-byte chunk per thread, workgroups of %d" % fl_t)
+    return {"read_GBps": round(rd_gbs, 1), "read_blocks": rd_g,
+            "copy_GBps": round(max(cp_gbs, fl_gbs), 1), "copy_shape": copy_shape,
+            "copy_grid_stride_GBps": round(cp_gbs, 1), "bytes_read": 4 * n,
             "roofline_achieved_over_read": round(achieved_gbs / rd_gbs, 4),
-            "kind": "trivial grid-stride kernels, 16-byte nontemporal accesses "
-                    "(include/rd_ceiling.h)"}
+            "kind": "trivial kernels, 16-byte nontemporal accesses (include/rd_ceiling.h)"}
 
 
 # Context figures printed by the pages for the same operation (another machine):

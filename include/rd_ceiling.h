@@ -11,7 +11,11 @@
  *   blocks workgroups of 256 threads, 1 .. 2^20; grid-stride order
  *   sink   device pointer to blocks*256 floats, written (one per thread)
  * rd_ceiling_copy(x, y, n, blocks, stream)
- *   x, y   device pointers to n floats each, 16-byte aligned, disjoint
+ *   x, y   device pointers to n floats each, 16-byte aligned, disjoint;
+ *          blocks as for rd_ceiling_read (grid-stride)
+ * rd_ceiling_copy_flat(x, y, n, threads, stream)
+ *   x, y   as for rd_ceiling_copy; one 16-byte chunk per thread, workgroups
+ *          of `threads` (64, 256 or 1024), ceil(n/4 / threads) of them
  * Enqueued on `stream`; return 0 on success, 1 for an invalid argument
  * (nothing enqueued), 2 if the launch failed.  Caller-owned memory only.
  */
@@ -27,6 +31,8 @@ extern "C" {
 
 int rd_ceiling_read(const float* x, int64_t n, int32_t blocks, float* sink, hipStream_t stream);
 int rd_ceiling_copy(const float* x, float* y, int64_t n, int32_t blocks, hipStream_t stream);
+int rd_ceiling_copy_flat(const float* x, float* y, int64_t n, int32_t threads,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

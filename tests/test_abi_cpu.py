@@ -44,8 +44,8 @@ def test_ceiling_probes_export_their_header():
     against librd_ceiling.so, and their argument checks (no GPU needed)."""
     with open(os.path.join(ROOT, "include", "rd_ceiling.h")) as f:
         text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
-    names = sorted(set(re.findall(r"\b(rd_ceiling_[a-z]+)\s*\(", text)))
-    assert names == ["rd_ceiling_copy", "rd_ceiling_read"]
+    names = sorted(set(re.findall(r"\b(rd_ceiling_[a-z_]+)\s*\(", text)))
+    assert names == ["rd_ceiling_copy", "rd_ceiling_copy_flat", "rd_ceiling_read"]
     lib = ctypes.CDLL(os.path.join(ROOT, "sum_reduction_amd", "librd_ceiling.so"))
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.rd_ceiling_read.argtypes = [vp, i64, i32, vp, vp]
@@ -58,6 +58,10 @@ def test_ceiling_probes_export_their_header():
     assert lib.rd_ceiling_read(base, 16, 0, base, None) == 1
     assert lib.rd_ceiling_copy(base, base + 32, 16, 1, None) == 1    # overlap
     assert lib.rd_ceiling_copy(base, None, 16, 1, None) == 1
+    lib.rd_ceiling_copy_flat.argtypes = [vp, vp, i64, i32, vp]
+    assert lib.rd_ceiling_copy_flat(base, base + 32, 16, 64, None) == 1   # overlap
+    assert lib.rd_ceiling_copy_flat(base, base + 64, 16, 100, None) == 1  # no such workgroup
+    assert lib.rd_ceiling_copy_flat(base + 4, base + 64, 16, 64, None) == 1
 
 
 def test_version_and_status_strings():
