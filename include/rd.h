@@ -334,7 +334,11 @@ typedef struct rd_plan {
     int32_t nxcd;            /* XCDs the workgroup numbering is spread over */
     int32_t passes;          /* kernel launches of the planned combine */
     int32_t combine;         /* rd_combine */
-    int32_t order;           /* ROWS: rd_order; 0 elsewhere */
+    int32_t order;           /* ROWS: rd_order; SCAN_ROWS: 0 = a workgroup
+                                (or wave) per item, RD_ORDER_INTERLEAVED =
+                                persistent workgroups, each streaming the
+                                chunks of rows b, b + blocks, ... (tuning
+                                only); 0 elsewhere */
     int32_t nontemporal;     /* 1: main-pass loads (and the scans' stores)
                                 carry the streaming hint (the totals pass
                                 of a split scan of at most 256 MB reads
@@ -397,7 +401,8 @@ typedef struct rd_tune {
     int32_t row_waves;       /* COLS */
     int32_t unroll;          /* ROWS, COLS: 2, 4, 8 or 16 (scans: see
                                 rd_plan_cumsum) */
-    int32_t order;           /* ROWS: rd_order */
+    int32_t order;           /* ROWS: rd_order; SCAN_ROWS with a workgroup
+                                per row and no pieces: RD_ORDER_INTERLEAVED */
     int32_t nontemporal;     /* every path: 1 = off, 2 = on */
     int32_t combine;         /* ROWS: 1 = second pass, 2 = last workgroup */
     int32_t path;            /* inner >= 4: RD_PATH_COLS or RD_PATH_COLS_SMALL

@@ -479,9 +479,21 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         if (P == 1 && R > kScanRowsBlockMinR)
             group = p->unroll == 4 ? kBlock : R >= kScanRowsWideMinR ? 16 * kWave : 8 * kWave;
         p->group = (t && t->group) ? t->group : group;
+        // interleaved: persistent workgroups, each streaming the chunks of
+        // rows b, b + blocks, ... (whole rows, a workgroup per row only)
+        p->order = (t && t->order) ? t->order : 0;
+        if (p->order && (p->order != RD_ORDER_INTERLEAVED || p->group == kWave || P != 1))
+            return RD_ERR_INVALID_ARG;
         // a workgroup of 256 threads holds 4 wave items; a wider group is one
         // workgroup per item
-        const int64_t b = p->group == kWave ? ceil_div(outer * P, kBlock / kWave) : outer * P;
+        int64_t b = p->group == kWave ? ceil_div(outer * P, kBlock / kWave) : outer * P;
+        if (p->order == RD_ORDER_INTERLEAVED) {
+            // as many workgroups as the CUs hold at once: 4 SIMDs x the
+            // waves a SIMD the kernel is built for, over the workgroup's waves
+            const int64_t per_cu = 4 * int64_t(p->unroll == 4 ? 8 : 4) / (p->group / kWave);
+            const int64_t resident = cu * (per_cu > 0 ? per_cu : 1);
+            if (resident < b) b = resident;
+        }
         p->blocks = b < kMaxBlocks ? b : kMaxBlocks;
         p->block_threads = p->group == kWave ? kBlock : p->group;
         if (P > 1) {

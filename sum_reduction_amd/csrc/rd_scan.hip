@@ -434,6 +434,72 @@ scan_rows_block_kernel(const float* x, float* out, int64_t outer, int64_t R, int
     }
 }
 
+// Whole rows (no pieces) by persistent workgroups of NW waves: workgroup b
+// takes rows b, b + G, b + 2G, ... (G = gridDim.x) and walks their chunks as
+// one stream -- each row's partial chunk, if any, then its full chunks, the
+// order of block_piece -- loading chunk g + 1 (the next row's first one
+// included) while chunk g is scanned, so no row starts on a memory latency
+// of its own.  Same chunks, same order, same bits as scan_rows_block_kernel.
+template <bool REV, int NW, int K, bool NT>
+__device__ __forceinline__ void stream_load(const float* xr, int64_t R, int64_t c0, int64_t c1,
+                                            bool part, int64_t lq, int wave, v4f (&v)[K]) {
+    const int64_t q0 = c0 + int64_t(wave) * 256 * K;
+    if (part) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = load_q4_part<REV, NT>(xr, R, q0 + 256 * k + lq, c1);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = load_q4<REV, NT>(xr, R, q0 + 256 * k + lq);
+    }
+}
+
+template <bool REV, int NW, int K, bool NT>
+__global__ __launch_bounds__(NW * kWave, scan_rows_waves_per_simd<K>()) void
+scan_rows_stream_kernel(const float* x, float* out, int64_t outer, int64_t R, int64_t so) {
+    __shared__ float slots[2][NW];
+    constexpr int64_t kChunk = NW * 256 * K;
+    const int wave = threadIdx.x / kWave;
+    const int64_t lq = 4 * (threadIdx.x % kWave);
+    const int64_t G = gridDim.x;
+    const int64_t o0 = blockIdx.x;
+    if (o0 >= outer || R <= 0) return;
+    const int64_t nfull = R / kChunk;
+    const int64_t h = R - nfull * kChunk;              // the partial chunk's length
+    const int64_t hp = h > 0 ? 1 : 0;
+    const int64_t nch = nfull + hp;                     // chunks per row
+    const int64_t total = ((outer - 1 - o0) / G + 1) * nch;
+    // chunk j of a row covers [c0(j), c1(j)); only j == 0 can be partial
+    auto c0 = [&](int64_t jj) { return jj == 0 ? int64_t(0) : h + (jj - hp) * kChunk; };
+    auto c1 = [&](int64_t jj) { return hp ? h + jj * kChunk : (jj + 1) * kChunk; };
+    int64_t o = o0, j = 0;  // the chunk being scanned: row o, chunk j
+    v4f a[K], b[K];
+    stream_load<REV, NW, K, NT>(x + o * so, R, c0(0), c1(0), hp != 0, lq, wave, a);
+    float carry = 0.f;
+    int parity = 0;
+    // one step: load chunk g + 1 into nxt, scan chunk g (held in cur)
+    auto step = [&](int64_t g, v4f (&cur)[K], v4f (&nxt)[K]) {
+        const int64_t jn = j + 1 == nch ? 0 : j + 1;
+        const int64_t on = j + 1 == nch ? o + G : o;
+        if (g + 1 < total)
+            stream_load<REV, NW, K, NT>(x + on * so, R, c0(jn), c1(jn), jn == 0 && hp != 0, lq,
+                                        wave, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j == 0) carry = 0.f;
+        carry = block_chunk<REV, NW, K, NT, true>(x + o * so, out + o * R, R,
+                                                  c0(j) + int64_t(wave) * 256 * K, c1(j),
+                                                  j == 0 && hp != 0, lq, cur, carry,
+                                                  slots[parity], wave);
+        parity ^= 1;
+        __builtin_amdgcn_sched_barrier(0);
+        o = on;
+        j = jn;
+    };
+    for (int64_t g = 0; g < total; g += 2) {
+        step(g, a, b);
+        if (g + 1 < total) step(g + 1, b, a);
+    }
+}
+
 // Exclusive scan of the P piece totals of each row, in piece order:
 // carries[o*P + p] = totals[o*P] + ... + totals[o*P + p - 1] (summed as the
 // chunks are: lane-sequential within 4, DPP across the wave, a carry across
@@ -1019,6 +1085,14 @@ int64_t grid_for(int64_t items) {
 template <bool REV, int NW, int K>
 hipError_t rows_block_k(const rd_plan& p, const float* x, float* out, const Strides& v,
                         const float* carry_in, float* totals, hipStream_t s) {
+    if (p.order == RD_ORDER_INTERLEAVED) {  // persistent workgroups streaming whole rows
+        if (p.split != 1 || carry_in || totals) return hipErrorInvalidValue;
+        if (p.nontemporal)
+            return launch(scan_rows_stream_kernel<REV, NW, K, true>, p.blocks, NW * kWave, s, x,
+                          out, v.outer, v.R, v.so);
+        return launch(scan_rows_stream_kernel<REV, NW, K, false>, p.blocks, NW * kWave, s, x,
+                      out, v.outer, v.R, v.so);
+    }
     if (p.nontemporal)
         return launch(scan_rows_block_kernel<REV, NW, K, true>, p.blocks, NW * kWave, s, x, out,
                       v.outer, v.R, v.so, p.split, p.rows_per_split, carry_in, totals);

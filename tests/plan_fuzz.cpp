@@ -135,8 +135,13 @@ void check_scan_plan(const rd::Strides& v, const rd_plan& p) {
                     p.blocks != std::min(rd::kMaxBlocks, (v.outer * p.split + 3) / 4))
                     fail("scan rows wave grid", v, -1, p);
             } else if (p.group == 256 || p.group == 512 || p.group == 1024) {
+                // persistent workgroups (interleaved rows) take at most one
+                // row each at a time; otherwise one workgroup per item
+                const bool streamed = p.order == RD_ORDER_INTERLEAVED;
                 if (p.block_threads != p.group ||
-                    p.blocks != std::min(rd::kMaxBlocks, v.outer * p.split))
+                    (streamed ? p.split != 1 || p.blocks > std::min(rd::kMaxBlocks, v.outer)
+                              : p.order != 0 ||
+                                    p.blocks != std::min(rd::kMaxBlocks, v.outer * p.split)))
                     fail("scan rows workgroup grid", v, -1, p);
             } else {
                 fail("scan rows group", v, -1, p);

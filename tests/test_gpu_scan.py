@@ -127,6 +127,44 @@ def test_rows_by_workgroup(group, unroll, split):
         H.assert_bitwise_equal_oracle(x.cpu().numpy(), S, "wg in place " + tag)
 
 
+STREAM_ROWS = [(256, 8), (512, 8), (1024, 8), (512, 4)]
+
+
+@pytest.mark.parametrize("group,unroll", STREAM_ROWS, ids=["g%d_u%d" % t for t in STREAM_ROWS])
+def test_rows_streamed_by_persistent_workgroups(group, unroll):
+    """Whole rows by persistent workgroups that walk their rows' chunks as one
+    stream (order = interleaved): bit-exact against the oracle on integer
+    data, bitwise equal to a workgroup per row (the same chunks in the same
+    order), in place; rows of less than a chunk, of a chunk, with and without
+    a partial chunk, fewer rows than workgroups and a ragged last round."""
+    chunk = group // 64 * 256 * unroll
+    shapes = [(o, r, 1) for o in (1, 3, 700) for r in (1, 5, chunk - 1, chunk, chunk + 1,
+                                                       2 * chunk, 2 * chunk + 3, 3 * chunk - 4)]
+    shapes += [(2100, 5, 1), (2100, chunk + 1, 1)]
+    shapes = [sh for sh in shapes if sh[0] * sh[1] <= 20_000_000]
+    tag = "stream g%d u%d" % (group, unroll)
+    with rd.tuning(group=group, unroll=unroll, order=1, split=1):
+        p = rd.rd_plan_cumsum(256, 700, 2 * chunk, 1)
+        assert p.group == group and p.order == 1 and p.split == 1
+        assert p.blocks == min(700, 256 * 16 // (group // 64) * (2 if unroll == 4 else 1))
+        _sweep(shapes, [0, 1], 1880 + group + unroll, tag)
+    t = H.torch()
+    rng = np.random.default_rng(group + unroll)
+    for o, r in ((700, 2 * chunk + 3), (5, 3 * chunk - 4)):
+        a = rng.standard_normal(o * r).astype(np.float32)
+        x = H.upload(a)
+        for rev in (True, False):
+            with rd.tuning(group=group, unroll=unroll, split=1):
+                want = rd.rd_cumsum_dim(x, o, r, 1, rev)
+            with rd.tuning(group=group, unroll=unroll, order=1, split=1):
+                got = rd.rd_cumsum_dim(x, o, r, 1, rev)
+                y = x.clone()
+                rd.rd_cumsum_dim(y, o, r, 1, rev, out=y)
+            t.cuda.synchronize()
+            assert t.equal(got.view(t.int32), want.view(t.int32)), (tag, o, r, rev)
+            assert t.equal(y.view(t.int32), want.view(t.int32)), (tag, "in place", o, r, rev)
+
+
 def test_default_splits():
     """Few rows or columns: the planner cuts them itself (many slabs: the slab
     carries go one wave per column)."""

@@ -87,6 +87,7 @@ def _load_runs(body):
 def test_the_library_has_the_kernels(kernels):
     for part in ("rows_kernel", "cols_kernel", "cols_small_kernel", "rows_short_tile_kernel",
                  "strided_kernel", "scan_rows_kernel", "scan_rows_block_kernel",
+                 "scan_rows_stream_kernel",
                  "scan_cols_kernel", "scan_small_kernel",
                  "scan_tile_out_kernel", "scan_tile_in_kernel", "scan_strided_kernel"):
         assert any(part in n for n in kernels), part

@@ -274,6 +274,31 @@ def _scan_invariants(p, outer, R, inner):
     assert p.passes == (3 if p.split > 1 else 1)
 
 
+def test_cumsum_rows_streamed():
+    """order = interleaved on the row scan: persistent workgroups (as many as
+    the CUs hold at once), whole rows only, a workgroup per row only."""
+    for group, unroll, per_cu in ((256, 8, 4), (512, 8, 2), (1024, 8, 1), (512, 4, 4)):
+        with rd.tuning(group=group, unroll=unroll, order=1):
+            p = rd.rd_plan_cumsum(CU, 32768, 32768, 1)
+            assert (p.group, p.order, p.split) == (group, 1, 1)
+            assert p.blocks == CU * per_cu and p.block_threads == group
+        with rd.tuning(group=group, unroll=unroll, order=1, split=1):
+            assert rd.rd_plan_cumsum(CU, 3, 50_000, 1).blocks == 3  # fewer rows than CUs
+        with rd.tuning(group=group, unroll=unroll, order=1):
+            with pytest.raises(rd.RdError):  # few rows are cut into pieces
+                rd.rd_plan_cumsum(CU, 3, 50_000, 1)
+    with rd.tuning(group=64, order=1):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum(CU, 32768, 32768, 1)
+    with rd.tuning(group=512, order=1, split=2):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum(CU, 32768, 32768, 1)
+    with rd.tuning(group=512, order=2):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_cumsum(CU, 32768, 32768, 1)
+    assert rd.rd_plan_cumsum(CU, 32768, 32768, 1).order == 0
+
+
 def test_cumsum_plans():
     """Rows: a workgroup of 8 waves per row (problem 91: 32768 rows, no pieces,
     two 16384-position chunks a row); few rows
