@@ -10,6 +10,15 @@ namespace rd {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v4f_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
+// The calling wave's index in its workgroup (64-lane waves) as a scalar.
+// threadIdx.x / 64 is the same on every lane of a wave, but the compiler
+// cannot tell, and otherwise keeps whatever is computed from it -- a wave's
+// row pointer, its window of positions -- in vector registers, one copy per
+// lane (in the row scans, enough to spill them to scratch memory).
+__device__ __forceinline__ int wave_in_block() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
+}
+
 // Four floats from a 4-byte-aligned address: one global_load_dwordx4, with
 // the nontemporal (streaming) hint when NT.  CDNA's multi-dword global loads
 // need only dword alignment.

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kBlock, scan_rows_waves_per_simd<K>()) void scan_ro
     const float* x, float* out, int64_t outer, int64_t R, int64_t so,
     int64_t P, int64_t L, const float* __restrict__ carry_in, float* __restrict__ totals) {
     constexpr int kWaves = kBlock / kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_in_block();
     const int lane = threadIdx.x % kWave;
     const int64_t nitems = outer * P;
     const int64_t wstride = int64_t(gridDim.x) * kWaves;
@@ -332,7 +332,7 @@ __device__ __forceinline__ float block_full(const float* row, float* orow, int64
                                             int& parity) {
     constexpr int64_t kSpan = 256 * K;         // a wave's positions per chunk
     constexpr int64_t kChunk = NW * kSpan;     // the block's positions per chunk
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_in_block();
     const int64_t lq = 4 * (threadIdx.x % kWave);
     const int64_t qw = qf + wave * kSpan;  // this wave's window in the first chunk
     // full chunks two at a time (a, then b), the next chunk's loads first
@@ -375,7 +375,7 @@ __device__ __forceinline__ float block_piece(const float* row, float* orow, int6
                                              float (&slots)[2][NW], int& parity) {
     constexpr int64_t kSpan = 256 * K;         // a wave's positions per chunk
     constexpr int64_t kChunk = NW * kSpan;     // the block's positions per chunk
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_in_block();
     const int64_t lq = 4 * (threadIdx.x % kWave);
     const int64_t n = q_end - q_begin;
     const int64_t nfull = n / kChunk;
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(NW * kWave, scan_rows_waves_per_simd<K>()) void
 scan_rows_stream_kernel(const float* x, float* out, int64_t outer, int64_t R, int64_t so) {
     __shared__ float slots[2][NW];
     constexpr int64_t kChunk = NW * 256 * K;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_in_block();
     const int64_t lq = 4 * (threadIdx.x % kWave);
     const int64_t G = gridDim.x;
     const int64_t o0 = blockIdx.x;
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(kBlock) void scan_carries_kernel(const float* __res
                                                               float* __restrict__ carries,
                                                               int64_t rows, int64_t P) {
     constexpr int kWaves = kBlock / kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_in_block();
     const int lane = threadIdx.x % kWave;
     const int64_t wstride = int64_t(gridDim.x) * kWaves;
     for (int64_t o = int64_t(blockIdx.x) * kWaves + wave; o < rows; o += wstride) {
@@ -588,7 +588,7 @@ __global__ __launch_bounds__(BW * kWave) void scan_cols_kernel(
     int64_t inner, int64_t so, int64_t sr, int64_t ntiles, int64_t S, int64_t rps,
     const float* __restrict__ carry_in, float* __restrict__ totals, uint32_t nxcd) {
     constexpr int kWaves = BW;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_in_block();
     const int lane = threadIdx.x % kWave;
     const bool scan_out = totals == nullptr;
     const int64_t ngt = (ntiles + kWaves - 1) / kWaves;  // tile groups per row
@@ -710,7 +710,7 @@ __global__ __launch_bounds__(kBlock) void scan_small_kernel(
     int64_t sr, int64_t S, int64_t rps, int32_t LC, const float* __restrict__ carry_in,
     float* __restrict__ totals, uint32_t nxcd) {
     constexpr int kWaves = kBlock / kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_in_block();
     const int lane = threadIdx.x % kWave;
     const int RPW = kWave / LC;
     const int rho_raw = lane / LC;
@@ -803,7 +803,7 @@ template <bool REV>
 __global__ __launch_bounds__(kBlock) void scan_slab_carries_wave_kernel(
     const float* __restrict__ totals, float* __restrict__ carries, int64_t S, int64_t n) {
     constexpr int kWaves = kBlock / kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_in_block();
     const int lane = threadIdx.x % kWave;
     const int64_t wstride = int64_t(gridDim.x) * kWaves;
     for (int64_t e = int64_t(blockIdx.x) * kWaves + wave; e < n; e += wstride) {
