@@ -53,14 +53,19 @@ uint32_t* make_tickets() {
     return t;
 }
 
-// True when `stream` is being captured into a graph (or its state cannot be
-// read).  A call whose plan needs a workspace is refused then: a replay of a
-// captured stream-ordered workspace faulted in the second kernel that reads
-// it, and the cause is not established.
-bool capturing(hipStream_t stream) {
+// RD_OK when `stream` is not being captured into a graph, RD_ERR_CAPTURE
+// when it is, RD_ERR_HIP when its state cannot be read.  A call whose plan
+// needs a workspace is refused while capturing: a replay of a captured
+// stream-ordered workspace faulted in the second kernel that reads it, and
+// the cause is not established.
+rd_status capture_check(hipStream_t stream) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    return hipStreamIsCapturing(stream, &cap) != hipSuccess ||
-           cap != hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) {
+        t_last_hip = static_cast<int>(e);
+        return RD_ERR_HIP;
+    }
+    return cap == hipStreamCaptureStatusNone ? RD_OK : RD_ERR_CAPTURE;
 }
 
 // The ticket counter of `stream`, or null for the two-kernel combine (stream
@@ -157,7 +162,8 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
     if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
     if (p.workspace_bytes > 0) {
-        if (capturing(s)) return RD_ERR_CAPTURE;
+        const rd_status cs = capture_check(s);
+        if (cs != RD_OK) return cs;
         if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
         hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
                                               size_t(p.workspace_bytes), dev.pool, s);
@@ -254,7 +260,8 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
     if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
     if (p.workspace_bytes > 0) {
-        if (capturing(stream)) return RD_ERR_CAPTURE;
+        const rd_status cs = capture_check(stream);
+        if (cs != RD_OK) return cs;
         if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
         hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
                                               size_t(p.workspace_bytes), dev->pool, stream);
