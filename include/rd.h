@@ -49,7 +49,11 @@
  *   refused with RD_ERR_CAPTURE while its stream is being captured into a
  *   graph (a replay of such a capture faulted in the second kernel, reading
  *   the graph-allocated workspace; the cause is not established); calls
- *   whose plan needs no workspace (one kernel) can be captured.
+ *   whose plan needs no workspace (one kernel) can be captured, once the
+ *   device has been set up by an earlier call outside the capture (the
+ *   first call on a device allocates and synchronizes, so on a capturing
+ *   stream it is refused with RD_ERR_CAPTURE and the capture is left
+ *   intact).
  * Semantics.  IEEE fp32 adds, round to nearest even, no flush of denormals,
  *   NaN and Inf propagate.  Accumulators start at +0.0, so the empty sum is
  *   +0.0 and an all -0.0 input sums to +0.0.  R == 0 writes outer*inner zeros;
@@ -102,8 +106,9 @@ typedef enum rd_status {
     RD_ERR_ALLOC = 3,       /* the stream-ordered workspace could not be had */
     RD_ERR_LAUNCH = 4,      /* a kernel launch was rejected */
     RD_ERR_HIP = 5,         /* another HIP runtime call failed */
-    RD_ERR_CAPTURE = 6      /* the call needs a stream-ordered workspace and
-                               its stream is being captured into a graph */
+    RD_ERR_CAPTURE = 6      /* the call needs a stream-ordered workspace, or
+                               is the first on its device, and its stream is
+                               being captured into a graph */
 } rd_status;
 
 /*

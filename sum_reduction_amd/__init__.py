@@ -27,13 +27,21 @@ __all__ = [
     "PATH_NAMES", "OPS", "rd_reduce_1d", "rd_reduce_dim", "reduce", "rd_cumsum_dim",
     "rd_plan_cumsum", "cumsum", "rd_cumsum_strided", "rd_plan_cumsum_strided",
     "rd_softmax_denom_1d", "rd_softmax_denom_dim", "softmax_denom", "rd_reduce_strided",
-    "rd_plan_strided", "rd_softmax_denom_strided",
+    "rd_plan_strided", "rd_softmax_denom_strided", "RD_OK", "RD_ERR_INVALID_ARG",
+    "RD_ERR_NO_DEVICE", "RD_ERR_ALLOC", "RD_ERR_LAUNCH", "RD_ERR_HIP", "RD_ERR_CAPTURE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "librd.so")
 
+# rd_status codes (include/rd.h)
 RD_OK = 0
+RD_ERR_INVALID_ARG = 1
+RD_ERR_NO_DEVICE = 2
+RD_ERR_ALLOC = 3
+RD_ERR_LAUNCH = 4
+RD_ERR_HIP = 5
+RD_ERR_CAPTURE = 6
 # rd_op: the reductions (the sum is the method; the others share its kernels)
 OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
 # the softmax denominator's pair (maximum, shifted sum of exponentials) has

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <unordered_map>
 
@@ -26,6 +27,7 @@ constexpr int kMaxDevices = 64;
 constexpr int kTicketSlots = 4096;
 struct Device {
     std::once_flag once;
+    std::atomic<bool> ready{false};  // set once the setup below has run
     int cu = 0;
     hipMemPool_t pool = nullptr;
     hipError_t err = hipSuccess;
@@ -103,7 +105,11 @@ bool overlap(const float* a, int64_t na, const float* b, int64_t nb) {
     return a0 < b1 && b0 < a1;
 }
 
-rd_status current_device(Device** out) {
+// The calling thread's current device, set up on its first use: CU count,
+// workspace pool, ticket counters.  The set-up allocates and synchronizes,
+// which would invalidate a graph being captured, so a first call on a
+// capturing `stream` is refused with RD_ERR_CAPTURE before any of it.
+rd_status current_device(Device** out, hipStream_t stream) {
     int count = 0;
     hipError_t e = hipGetDeviceCount(&count);
     if (e != hipSuccess || count < 1) {
@@ -115,6 +121,10 @@ rd_status current_device(Device** out) {
     if (e != hipSuccess) return hip_fail(e, RD_ERR_NO_DEVICE);
     if (dev < 0 || dev >= kMaxDevices) return RD_ERR_NO_DEVICE;
     Device& d = g_devices[dev];
+    if (!d.ready.load(std::memory_order_acquire)) {
+        const rd_status cs = capture_check(stream);
+        if (cs != RD_OK) return cs;
+    }
     std::call_once(d.once, [&d, dev] {
         int cu = 0;
         hipError_t err =
@@ -142,6 +152,7 @@ rd_status current_device(Device** out) {
         }
         d.tickets = make_tickets();
         d.cu = cu;
+        d.ready.store(true, std::memory_order_release);
     });
     if (d.err != hipSuccess) return hip_fail(d.err, RD_ERR_HIP);
     *out = &d;
@@ -222,7 +233,7 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
 rd_status reduce_checked(const float* x, rd::Strides v, int op, rd::Results out,
                          hipStream_t stream) {
     Device* dev = nullptr;
-    rd_status st = current_device(&dev);
+    rd_status st = current_device(&dev, stream);
     if (st != RD_OK) return st;
     rd_plan plan;
     {
@@ -248,7 +259,7 @@ int64_t view_extent(const rd::Strides& v) {
 rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
                          hipStream_t stream) {
     Device* dev = nullptr;
-    rd_status st = current_device(&dev);
+    rd_status st = current_device(&dev, stream);
     if (st != RD_OK) return st;
     rd_plan p;
     {

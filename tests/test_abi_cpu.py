@@ -70,6 +70,9 @@ def test_version_and_status_strings():
     assert names == ["RD_OK", "RD_ERR_INVALID_ARG", "RD_ERR_NO_DEVICE", "RD_ERR_ALLOC",
                      "RD_ERR_LAUNCH", "RD_ERR_HIP", "RD_ERR_CAPTURE"]
     assert rd.rd_status_string(99) == "RD_ERR_UNKNOWN"
+    consts = [rd.RD_OK, rd.RD_ERR_INVALID_ARG, rd.RD_ERR_NO_DEVICE, rd.RD_ERR_ALLOC,
+              rd.RD_ERR_LAUNCH, rd.RD_ERR_HIP, rd.RD_ERR_CAPTURE]
+    assert [rd.rd_status_string(c) for c in consts] == names
 
 
 @pytest.fixture(scope="module")

@@ -1,19 +1,19 @@
 """The entry points under HIP graph capture (torch.cuda.graph).
 
-A graph records the kernels of several calls -- a split full reduce (two
-kernels and a stream-ordered workspace), an axis reduce, a softmax
-denominator and a split cumulative sum -- and is replayed several times with
-eager work in between that changes the inputs; every replay must give the
-bits of an eager call on the same inputs.  No call inside the library clears
-memory with a memset node: the workspaces are written before they are read.
+Run: a call whose plan needs a workspace is refused on a capturing stream
+(RD_ERR_CAPTURE) and records nothing; calls whose plan is one kernel with no
+workspace are captured and replayed several times, with eager work in
+between that changes the inputs, and every replay gives the bits of an
+eager call on the same inputs.
 
-Skipped: the first replay of this graph once faulted (a memory aperture
-violation in slab_combine_kernel, the second kernel of the [3, 50000, 70]
-axis reduce, reading its graph-allocated workspace) after the plan of that
-call changed; the same calls run eagerly are in bounds and pass, and the
-cause was not established.  Until it is, the library refuses a call that
-needs a workspace on a capturing stream (RD_ERR_CAPTURE), and these tests
-stay off the GPU.
+Skipped: a graph of calls with workspaces (a split full reduce -- two
+kernels and a stream-ordered workspace --, a split axis reduce, a softmax
+denominator, a split cumulative sum).  Its first replay once faulted (a
+memory aperture violation in slab_combine_kernel, the second kernel of the
+[3, 50000, 70] axis reduce, reading its graph-allocated workspace) after the
+plan of that call changed; the same calls run eagerly are in bounds and
+pass, and the cause was not established.  Until it is, the library refuses
+such calls while capturing, and that test stays off the GPU.
 """
 import numpy as np
 import pytest
@@ -71,3 +71,104 @@ def test_graph_replays_match_eager_calls():
         t.cuda.synchronize()
         for k, (a, b) in enumerate(zip(outs, want)):
             assert t.equal(a.reshape(-1).view(t.int32), b.reshape(-1).view(t.int32)), (rep, k)
+
+
+def test_capture_refuses_workspace_plans():
+    """A call whose plan needs a workspace returns RD_ERR_CAPTURE while its
+    stream is being captured, and records nothing; the capture goes on."""
+    t = H.torch()
+    x = H.upload(workloads.random(1_000_000, 2001, "normal"))
+    y = t.zeros(16, device="cuda")
+    assert rd.rd_plan_1d(256, 1_000_000).workspace_bytes > 0
+    rd.rd_sum_1d(x)  # the device's set-up happens outside the capture
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    statuses = []
+    with t.cuda.graph(g):
+        try:
+            rd.rd_sum_1d(x)
+        except rd.RdError as e:
+            statuses.append(e.status)
+        y.add_(1.0)
+    assert statuses == [rd.RD_ERR_CAPTURE]
+    for _ in range(3):
+        g.replay()
+    t.cuda.synchronize()
+    assert float(y.sum()) == 3.0 * 16
+
+
+def test_single_kernel_plans_replay():
+    """Calls whose plan is one kernel and no workspace (a column reduce, a row
+    reduce with a workgroup per row, a cumulative sum of uncut rows) capture
+    and replay: every replay, with eager work changing the inputs in between,
+    gives the bits of an eager call."""
+    t = H.torch()
+    shapes = [(128, 256, 4095), (4096, 2048, 1)]
+    for o, r, i in shapes:
+        p = rd.rd_plan_dim(256, o, r, i)
+        assert p.split == 1 and p.workspace_bytes == 0, (o, r, i)
+    assert rd.rd_plan_cumsum(256, 2048, 5000, 1).workspace_bytes == 0
+    xs = [H.upload(workloads.random(o * r * i, 2100 + k, "normal"))
+          for k, (o, r, i) in enumerate(shapes)]
+    xc = H.upload(workloads.random(2048 * 5000, 2110, "normal"))
+    outs = [t.empty(o * i, device="cuda") for o, r, i in shapes]
+    oc = t.empty(2048 * 5000, device="cuda")
+    for (o, r, i), x, out in zip(shapes, xs, outs):  # warm-up outside the capture
+        rd.rd_sum_dim(x, o, r, i, out=out)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        for (o, r, i), x, out in zip(shapes, xs, outs):
+            rd.rd_sum_dim(x, o, r, i, out=out)
+        rd.rd_cumsum_dim(xc, 2048, 5000, 1, reverse=True, out=oc)
+    for rep in range(4):
+        for x in xs + [xc]:
+            x.mul_(1.25).add_(0.5)
+        g.replay()
+        t.cuda.synchronize()
+        for (o, r, i), x, out in zip(shapes, xs, outs):
+            want = rd.rd_sum_dim(x, o, r, i)
+            assert t.equal(out.view(t.int32), want.reshape(-1).view(t.int32)), (rep, o, r, i)
+        want = rd.rd_cumsum_dim(xc, 2048, 5000, 1, reverse=True)
+        assert t.equal(oc.view(t.int32), want.reshape(-1).view(t.int32)), (rep, "cumsum")
+
+
+_FIRST_CALL = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import torch
+import sum_reduction_amd as rd
+x = torch.ones(128 * 256 * 4095, device="cuda")
+y = torch.zeros(16, device="cuda")
+y.add_(0.0)                      # torch's own set-up, outside the capture
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+st = []
+with torch.cuda.graph(g):
+    try:
+        rd.rd_sum_dim(x, 128, 256, 4095)   # the library's first call on the device
+    except rd.RdError as e:
+        st.append(e.status)
+    y.add_(1.0)
+g.replay()
+torch.cuda.synchronize()
+assert st == [rd.RD_ERR_CAPTURE], st
+assert float(y.sum()) == 16.0
+out = rd.rd_sum_dim(x, 128, 256, 4095)     # set up now, outside the capture
+assert float(out.min()) == 256.0 and float(out.max()) == 256.0
+print("first-call-ok")
+"""
+
+
+def test_first_call_under_capture_is_refused():
+    """The library's first call on a device sets the device up (it allocates
+    and synchronizes); on a capturing stream it returns RD_ERR_CAPTURE before
+    any of that, and the capture stays valid.  Needs a process whose library
+    has not been used yet: one child process."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", _FIRST_CALL, root], capture_output=True,
+                         text=True, timeout=240)
+    assert res.returncode == 0 and "first-call-ok" in res.stdout, res.stdout + res.stderr[-3000:]
