@@ -274,6 +274,21 @@ def _scan_invariants(p, outer, R, inner):
     assert p.passes == (3 if p.split > 1 else 1)
 
 
+def test_cumsum_row_widths_at_their_edges():
+    """Uncut rows: a wave per row up to 16384 positions, a workgroup of 8
+    waves above, of 16 from 65536 on (two of its 32768-position chunks);
+    rows cut into pieces stay a wave per piece."""
+    for R, group in ((4096, 64), (16384, 64), (16385, 512), (32768, 512), (65535, 512),
+                     (65536, 1024), (1 << 20, 1024)):
+        p = rd.rd_plan_cumsum(CU, 4096, R, 1)
+        assert p.split == 1 and p.group == group, (R, p.as_dict())
+        assert p.block_threads == max(group, 256)
+    p = rd.rd_plan_cumsum(CU, 16, 1 << 20, 1)   # 16 rows: cut into pieces
+    assert p.split > 1 and p.group == 64
+    with rd.tuning(unroll=4):                    # 4-slice chunks: 4 waves
+        assert rd.rd_plan_cumsum(CU, 4096, 65536, 1).group == 256
+
+
 def test_cumsum_rows_streamed():
     """order = interleaved on the row scan: persistent workgroups (as many as
     the CUs hold at once), whole rows only, a workgroup per row only."""
