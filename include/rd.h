@@ -45,15 +45,18 @@
  *   workgroup of the first kernel sums them instead; the integer ticket
  *   counter that elects it belongs to the stream (one per stream and device,
  *   reset by the kernel itself), so calls on one stream, which never overlap,
- *   never share it with calls on another.  A call that needs a workspace is
- *   refused with RD_ERR_CAPTURE while its stream is being captured into a
- *   graph (a replay of such a capture faulted in the second kernel, reading
- *   the graph-allocated workspace; the cause is not established); calls
- *   whose plan needs no workspace (one kernel) can be captured, once the
- *   device has been set up by an earlier call outside the capture (the
- *   first call on a device allocates and synchronizes, so on a capturing
- *   stream it is refused with RD_ERR_CAPTURE and the capture is left
- *   intact).
+ *   never share it with calls on another (calls on the per-thread default
+ *   stream, whose handle stands for a different stream in each thread, take
+ *   the second kernel instead).  The pool and the counters are created by
+ *   the first call on a device that needs a workspace.  A call that needs a
+ *   workspace is refused with RD_ERR_CAPTURE while its stream is being
+ *   captured into a graph (a replay of such a capture faulted in the second
+ *   kernel, reading the graph-allocated workspace; the cause is not
+ *   established); calls whose plan needs no workspace (one kernel) can be
+ *   captured, once the device has been set up by an earlier call outside
+ *   the capture (the first call on a device reads its properties and may
+ *   load the library's code onto it, so on a capturing stream it is refused
+ *   with RD_ERR_CAPTURE and the capture is left intact).
  * Semantics.  IEEE fp32 adds, round to nearest even, no flush of denormals,
  *   NaN and Inf propagate.  Accumulators start at +0.0, so the empty sum is
  *   +0.0 and an all -0.0 input sums to +0.0.  R == 0 writes outer*inner zeros;

@@ -16,6 +16,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -37,7 +38,7 @@ def hipcc() -> str:
 
 
 def flags():
-    return ["-O3", "-std=c++17", "--offload-arch=%s" % ARCH, "-fPIC", "-shared",
+    return ["-O3", "-std=c++17", "--offload-arch=%s" % ARCH, "-fPIC",
             "-ffp-contract=off", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", CSRC]
@@ -50,10 +51,7 @@ def build(verbose: bool = False) -> str:
     return LIBRARY
 
 
-def _compile(sources, library: str, verbose: bool) -> None:
-    srcs = [os.path.join(CSRC, s) for s in sources]
-    tmp = library + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *flags(), "-o", tmp, *srcs]
+def _run(cmd, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,7 +62,28 @@ def _compile(sources, library: str, verbose: bool) -> None:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, library)
+
+
+def _compile(sources, library: str, verbose: bool) -> None:
+    """Each source to an object file (in parallel: the kernel files take a
+    minute or more each), then one shared library."""
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(os.path.dirname(library),
+                         "_%s.%s.o" % (os.path.splitext(s)[0], tag)) for s in sources]
+    jobs = [[hipcc(), *flags(), "-c", "-o", o, os.path.join(CSRC, s)]
+            for s, o in zip(sources, objs)]
+    try:
+        with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as pool:
+            for f in [pool.submit(_run, j, verbose) for j in jobs]:
+                f.result()
+        tmp = library + ".tmp%s" % tag
+        _run([hipcc(), "--offload-arch=%s" % ARCH, "-shared", "-fPIC", "-o", tmp, *objs],
+             verbose)
+        os.replace(tmp, library)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
 
 
 if __name__ == "__main__":

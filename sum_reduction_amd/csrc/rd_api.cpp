@@ -16,26 +16,29 @@ namespace {
 
 thread_local int t_last_hip = 0;
 
-// Per-device state, created once on first use of the device: its CU count
-// (which fixes the plan, hence the summation order) and a memory pool of the
-// library's own for workspaces, which keeps its memory between calls.
-constexpr int kMaxDevices = 64;
+// Per-device state.  The first call on a device reads its CU count (which
+// fixes the plan, hence the summation order); the first call that needs a
+// workspace also creates the library's memory pool for workspaces, which
+// keeps its memory between calls, and the ticket counters of the fused
+// combine.  Calls whose plan needs no workspace never allocate.
 // Ticket counters for the fused (last-workgroup) combine: one per stream that
-// has made such a call on the device, zeroed once when the device is set up
-// and left at zero by every kernel that uses one.  Calls on one stream never
+// has made such a call on the device, zeroed once when they are created and
+// left at zero by every kernel that uses one.  Calls on one stream never
 // overlap, so a stream's counter is always 0 when its next kernel starts.
 constexpr int kTicketSlots = 4096;
 struct Device {
     std::once_flag once;
-    std::atomic<bool> ready{false};  // set once the setup below has run
+    std::atomic<bool> ready{false};  // set once the CU count is known
     int cu = 0;
-    hipMemPool_t pool = nullptr;
     hipError_t err = hipSuccess;
+    std::once_flag mem_once;  // pool and tickets, on the first workspace plan
+    hipMemPool_t pool = nullptr;
+    hipError_t mem_err = hipSuccess;
     uint32_t* tickets = nullptr;  // null: the fused combine is not used
     std::mutex ticket_mu;
     std::unordered_map<hipStream_t, int> ticket_of;
 };
-Device g_devices[kMaxDevices];
+Device g_devices[rd::kMaxDevices];
 
 // Zeroed ticket counters, or null if they cannot be had (then every split
 // reduce takes the two-kernel combine, with the same results).
@@ -70,13 +73,13 @@ rd_status capture_check(hipStream_t stream) {
     return cap == hipStreamCaptureStatusNone ? RD_OK : RD_ERR_CAPTURE;
 }
 
-// The ticket counter of `stream`, or null for the two-kernel combine (stream
-// being captured, or every counter taken).
+// The ticket counter of `stream` (not being captured: such calls are
+// refused before this), or null for the two-kernel combine: every counter
+// taken, or the per-thread default stream, whose one handle stands for a
+// different stream in each host thread -- calls from two threads could run
+// at once and share the counter.
 uint32_t* stream_ticket(Device& d, hipStream_t stream) {
-    if (!d.tickets) return nullptr;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
-        return nullptr;
+    if (!d.tickets || stream == hipStreamPerThread) return nullptr;
     std::lock_guard<std::mutex> lock(d.ticket_mu);
     auto it = d.ticket_of.find(stream);
     if (it != d.ticket_of.end()) return d.tickets + it->second;
@@ -105,11 +108,12 @@ bool overlap(const float* a, int64_t na, const float* b, int64_t nb) {
     return a0 < b1 && b0 < a1;
 }
 
-// The calling thread's current device, set up on its first use: CU count,
-// workspace pool, ticket counters.  The set-up allocates and synchronizes,
-// which would invalidate a graph being captured, so a first call on a
-// capturing `stream` is refused with RD_ERR_CAPTURE before any of it.
-rd_status current_device(Device** out, hipStream_t stream) {
+// The calling thread's current device (its index in *index), its CU count
+// read on its first use.  The first use of a device may load the library's
+// code objects onto it, which must not happen inside a graph being
+// captured, so a first call on a capturing `stream` is refused with
+// RD_ERR_CAPTURE before any of it.
+rd_status current_device(Device** out, int* index, hipStream_t stream) {
     int count = 0;
     hipError_t e = hipGetDeviceCount(&count);
     if (e != hipSuccess || count < 1) {
@@ -119,7 +123,7 @@ rd_status current_device(Device** out, hipStream_t stream) {
     int dev = -1;
     e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, RD_ERR_NO_DEVICE);
-    if (dev < 0 || dev >= kMaxDevices) return RD_ERR_NO_DEVICE;
+    if (dev < 0 || dev >= rd::kMaxDevices) return RD_ERR_NO_DEVICE;
     Device& d = g_devices[dev];
     if (!d.ready.load(std::memory_order_acquire)) {
         const rd_status cs = capture_check(stream);
@@ -127,10 +131,30 @@ rd_status current_device(Device** out, hipStream_t stream) {
     }
     std::call_once(d.once, [&d, dev] {
         int cu = 0;
-        hipError_t err =
+        const hipError_t err =
             hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess || cu < 1) {
             d.err = err != hipSuccess ? err : hipErrorInvalidDevice;
+            return;
+        }
+        d.cu = cu;
+        d.ready.store(true, std::memory_order_release);
+    });
+    if (d.err != hipSuccess) return hip_fail(d.err, RD_ERR_HIP);
+    *out = &d;
+    if (index) *index = dev;
+    return RD_OK;
+}
+
+// The device's workspace pool and ticket counters, created by the first call
+// that needs a workspace (never while capturing: such calls are refused
+// first).  The calling thread's current device is d's.
+rd_status device_memory(Device& d) {
+    std::call_once(d.mem_once, [&d] {
+        int dev = -1;
+        hipError_t err = hipGetDevice(&dev);
+        if (err != hipSuccess) {
+            d.mem_err = err;
             return;
         }
         hipMemPoolProps props;
@@ -141,44 +165,62 @@ rd_status current_device(Device** out, hipStream_t stream) {
         props.location.id = dev;
         err = hipMemPoolCreate(&d.pool, &props);
         if (err != hipSuccess) {
-            d.err = err;
+            d.mem_err = err;
             return;
         }
         uint64_t keep = UINT64_MAX;  // hold freed workspace for the next call
         err = hipMemPoolSetAttribute(d.pool, hipMemPoolAttrReleaseThreshold, &keep);
         if (err != hipSuccess) {
-            d.err = err;
+            d.mem_err = err;
             return;
         }
         d.tickets = make_tickets();
-        d.cu = cu;
-        d.ready.store(true, std::memory_order_release);
     });
-    if (d.err != hipSuccess) return hip_fail(d.err, RD_ERR_HIP);
-    *out = &d;
+    if (d.mem_err != hipSuccess) return hip_fail(d.mem_err, RD_ERR_HIP);
     return RD_OK;
 }
 
-// Failure injection for tests of the error paths, read from the environment:
-// RD_TEST_FAIL_ALLOC makes the workspace allocation fail, RD_TEST_FAIL_LAUNCH
-// makes the first launch fail; neither enqueues any work.
-bool inject(const char* name) {
+// Failure injection for tests of the error paths, read from the environment
+// once per process (at the first call that looks): RD_TEST_FAIL_ALLOC makes
+// the workspace allocation fail, RD_TEST_FAIL_LAUNCH makes the first launch
+// fail; neither enqueues any work.
+bool env_on(const char* name) {
     const char* v = getenv(name);
     return v && v[0] && v[0] != '0';
 }
 
+struct Injected {
+    bool alloc, launch;
+};
+
+const Injected& injected() {
+    static const Injected f{env_on("RD_TEST_FAIL_ALLOC"), env_on("RD_TEST_FAIL_LAUNCH")};
+    return f;
+}
+
+// Runs plan p.  fixed == nullptr: the workspace (if any) is allocated
+// stream-ordered from the device's pool and freed after the last kernel,
+// which is refused while `s` is being captured.  fixed != nullptr: it is the
+// workspace, at least p.workspace_bytes long, and nothing is allocated (the
+// partial results are combined by the second kernel).
 rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const rd::Strides& v,
-                  rd::Results out, hipStream_t s) {
+                  rd::Results out, hipStream_t s, float* fixed) {
     if (p.path == RD_PATH_NONE) return RD_OK;
-    if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
+    if (injected().launch) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
-    if (p.workspace_bytes > 0) {
-        const rd_status cs = capture_check(s);
-        if (cs != RD_OK) return cs;
-        if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
+    bool pooled = false;
+    if (p.workspace_bytes > 0 && fixed) {
+        ws = fixed;
+    } else if (p.workspace_bytes > 0) {
+        rd_status st = capture_check(s);
+        if (st != RD_OK) return st;
+        st = device_memory(dev);
+        if (st != RD_OK) return st;
+        if (injected().alloc) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
         hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
                                               size_t(p.workspace_bytes), dev.pool, s);
         if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
+        pooled = true;
     }
     // partial results: one array, or the two halves of the pairs
     rd::Results part{ws, nullptr};
@@ -197,8 +239,9 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
             if (p.split == 1) {
                 e = rd::launch_rows(op, p, x, v, out, nullptr, rd::Results{}, s);
             } else {
-                uint32_t* ticket =
-                    p.combine == RD_COMBINE_LAST_BLOCK ? stream_ticket(dev, s) : nullptr;
+                uint32_t* ticket = p.combine == RD_COMBINE_LAST_BLOCK && pooled
+                                       ? stream_ticket(dev, s)
+                                       : nullptr;
                 e = rd::launch_rows(op, p, x, v, part, ticket, out, s);
                 if (e == hipSuccess && !ticket)
                     e = rd::launch_rows_combine(op, part, nout, p.split, out, s);
@@ -221,7 +264,7 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
         default:
             e = hipErrorInvalidValue;
     }
-    if (ws) {
+    if (pooled) {
         hipError_t f = hipFreeAsync(ws, s);
         if (e == hipSuccess && f != hipSuccess) return hip_fail(f, RD_ERR_HIP);
     }
@@ -233,7 +276,7 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
 rd_status reduce_checked(const float* x, rd::Strides v, int op, rd::Results out,
                          hipStream_t stream) {
     Device* dev = nullptr;
-    rd_status st = current_device(&dev, stream);
+    rd_status st = current_device(&dev, nullptr, stream);
     if (st != RD_OK) return st;
     rd_plan plan;
     {
@@ -241,7 +284,7 @@ rd_status reduce_checked(const float* x, rd::Strides v, int op, rd::Results out,
         st = rd::plan_view(dev->cu, &v, op, g_tune_on ? &g_tune : nullptr, &plan);
     }
     if (st != RD_OK) return st;
-    return execute(plan, op, *dev, x, v, out, stream);
+    return execute(plan, op, *dev, x, v, out, stream, nullptr);
 }
 
 rd::Strides contiguous(int64_t outer, int64_t R, int64_t inner) {
@@ -259,7 +302,7 @@ int64_t view_extent(const rd::Strides& v) {
 rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
                          hipStream_t stream) {
     Device* dev = nullptr;
-    rd_status st = current_device(&dev, stream);
+    rd_status st = current_device(&dev, nullptr, stream);
     if (st != RD_OK) return st;
     rd_plan p;
     {
@@ -268,12 +311,14 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
     }
     if (st != RD_OK) return st;
     if (p.path == RD_PATH_NONE) return RD_OK;
-    if (inject("RD_TEST_FAIL_LAUNCH")) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
+    if (injected().launch) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
     if (p.workspace_bytes > 0) {
-        const rd_status cs = capture_check(stream);
-        if (cs != RD_OK) return cs;
-        if (inject("RD_TEST_FAIL_ALLOC")) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
+        st = capture_check(stream);
+        if (st != RD_OK) return st;
+        st = device_memory(*dev);
+        if (st != RD_OK) return st;
+        if (injected().alloc) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
         hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
                                               size_t(p.workspace_bytes), dev->pool, stream);
         if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
@@ -325,6 +370,27 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
     return RD_OK;
 }
 
+// The arguments of an axis reduce of a contiguous [outer, R, inner] array:
+// RD_OK with *empty set when there is nothing to write (outer*inner == 0).
+rd_status dim_args(const float* x, int64_t outer, int64_t R, int64_t inner, const float* out,
+                   bool* empty) {
+    *empty = false;
+    if (outer < 0 || R < 0 || inner < 0) return RD_ERR_INVALID_ARG;
+    const int64_t lim = INT64_MAX / 4;
+    if (outer && inner && inner > lim / outer) return RD_ERR_INVALID_ARG;
+    const int64_t nout = outer * inner;
+    if (nout && R && R > lim / nout) return RD_ERR_INVALID_ARG;
+    const int64_t nin = nout * R;
+    if (nout == 0) {
+        *empty = true;
+        return RD_OK;
+    }
+    if (!out || !aligned4(out)) return RD_ERR_INVALID_ARG;
+    if (nin > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
+    if (overlap(x, nin, out, nout)) return RD_ERR_INVALID_ARG;
+    return RD_OK;
+}
+
 bool op_valid(int32_t op) { return op >= RD_OP_SUM && op <= RD_OP_MIN; }
 
 }  // namespace
@@ -343,16 +409,9 @@ rd_status rd_reduce_1d(const float* x, int64_t n, int32_t op, float* out,
 rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner, int32_t op,
                         float* out, hipStream_t stream) {
     if (!op_valid(op)) return RD_ERR_INVALID_ARG;
-    if (outer < 0 || R < 0 || inner < 0) return RD_ERR_INVALID_ARG;
-    const int64_t lim = INT64_MAX / 4;
-    if (outer && inner && inner > lim / outer) return RD_ERR_INVALID_ARG;
-    const int64_t nout = outer * inner;
-    if (nout && R && R > lim / nout) return RD_ERR_INVALID_ARG;
-    const int64_t nin = nout * R;
-    if (nout == 0) return RD_OK;  // nothing to write, no HIP call
-    if (!out || !aligned4(out)) return RD_ERR_INVALID_ARG;
-    if (nin > 0 && (!x || !aligned4(x))) return RD_ERR_INVALID_ARG;
-    if (overlap(x, nin, out, nout)) return RD_ERR_INVALID_ARG;
+    bool empty = false;
+    const rd_status st = dim_args(x, outer, R, inner, out, &empty);
+    if (st != RD_OK || empty) return st;  // empty: nothing to write, no HIP call
     return reduce_checked(x, contiguous(outer, R, inner), op, rd::Results{out, nullptr},
                           stream);
 }

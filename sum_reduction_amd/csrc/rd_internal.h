@@ -21,6 +21,8 @@ constexpr int64_t kSmallInner = 128;
 // kernels (a grid's total thread count must stay below 2^32 on AMD, and
 // workgroups have up to 1024 threads).
 constexpr int64_t kMaxBlocks = int64_t(1) << 20;
+// Devices the library keeps state for (indices 0 .. kMaxDevices - 1).
+constexpr int kMaxDevices = 64;
 
 
 // Where a launch stores its results: `a` holds them (for the softmax

@@ -300,22 +300,43 @@ def test_address_independence_random():
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), off
 
 
-def test_failure_injection_leaves_out_untouched(monkeypatch):
+_INJECT = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import torch
+import sum_reduction_amd as rd
+from tests import gpu_helpers as H
+want = int(sys.argv[2])
+x = H.upload(np.ones(1_000_000, np.float32))
+slots = H.OutSlots([1])
+assert rd.rd_plan_1d(256, 1_000_000).workspace_bytes > 0
+st = H.call_1d(x, slots.ptr(0))
+assert st == want, (st, want)
+out = slots.fetch()[0]
+assert out.view(np.uint32)[0] == H.GUARD_BITS
+print("inject-ok", st)
+"""
+
+
+def test_failure_injection_leaves_out_untouched():
     """Forced allocation and launch failures return their status codes and
-    enqueue nothing."""
+    enqueue nothing.  The library reads the failure switches once per
+    process, so each runs in a child process of its own."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for var, status in (("RD_TEST_FAIL_ALLOC", 3), ("RD_TEST_FAIL_LAUNCH", 4)):
+        H.say("failure injection: %s" % var)
+        env = dict(os.environ, **{var: "1"})
+        res = subprocess.run([sys.executable, "-c", _INJECT, root, str(status)], env=env,
+                             capture_output=True, text=True, timeout=240, cwd=root)
+        assert res.returncode == 0 and "inject-ok %d" % status in res.stdout, (
+            var, res.stdout + res.stderr[-3000:])
+    # and the library of this process (no switch set) works
     t = H.torch()
     x = H.upload(np.ones(1_000_000, np.float32))
-    slots = H.OutSlots([1, 1])
-    monkeypatch.setenv("RD_TEST_FAIL_ALLOC", "1")
-    assert rd.rd_plan_1d(256, 1_000_000).workspace_bytes > 0
-    assert H.call_1d(x, slots.ptr(0)) == 3  # RD_ERR_ALLOC
-    monkeypatch.delenv("RD_TEST_FAIL_ALLOC")
-    monkeypatch.setenv("RD_TEST_FAIL_LAUNCH", "1")
-    assert H.call_1d(x, slots.ptr(1)) == 4  # RD_ERR_LAUNCH
-    monkeypatch.delenv("RD_TEST_FAIL_LAUNCH")
-    outs = slots.fetch()
-    assert all(o.view(np.uint32)[0] == H.GUARD_BITS for o in outs)
-    # and the library still works afterwards
     assert rd.rd_sum_1d(x).item() == 1_000_000.0
 
 
