@@ -52,11 +52,12 @@
  *   workspace is refused with RD_ERR_CAPTURE while its stream is being
  *   captured into a graph (a replay of such a capture faulted in the second
  *   kernel, reading the graph-allocated workspace; the cause is not
- *   established); calls whose plan needs no workspace (one kernel) can be
- *   captured, once the device has been set up by an earlier call outside
- *   the capture (the first call on a device reads its properties and may
- *   load the library's code onto it, so on a capturing stream it is refused
- *   with RD_ERR_CAPTURE and the capture is left intact).
+ *   established); calls whose plan needs no workspace (one kernel), and
+ *   rd_sum_dim_noalloc, can be captured, once the device has been set up by
+ *   an earlier call outside the capture (the first call on a device reads
+ *   its properties and may load the library's code onto it, so on a
+ *   capturing stream it is refused with RD_ERR_CAPTURE and the capture is
+ *   left intact).
  * Semantics.  IEEE fp32 adds, round to nearest even, no flush of denormals,
  *   NaN and Inf propagate.  Accumulators start at +0.0, so the empty sum is
  *   +0.0 and an all -0.0 input sums to +0.0.  R == 0 writes outer*inner zeros;
@@ -109,9 +110,12 @@ typedef enum rd_status {
     RD_ERR_ALLOC = 3,       /* the stream-ordered workspace could not be had */
     RD_ERR_LAUNCH = 4,      /* a kernel launch was rejected */
     RD_ERR_HIP = 5,         /* another HIP runtime call failed */
-    RD_ERR_CAPTURE = 6      /* the call needs a stream-ordered workspace, or
+    RD_ERR_CAPTURE = 6,     /* the call needs a stream-ordered workspace, or
                                is the first on its device, and its stream is
                                being captured into a graph */
+    RD_ERR_WORKSPACE = 7    /* rd_sum_dim_noalloc: the shape's plan needs more
+                               partial results than its fixed scratch buffer
+                               (RD_NOALLOC_SCRATCH_BYTES) holds */
 } rd_status;
 
 /*
@@ -141,6 +145,33 @@ rd_status rd_sum_1d(const float* x, int64_t n, float* out, hipStream_t stream);
  */
 rd_status rd_sum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
                      float* out, hipStream_t stream);
+
+/*
+ * rd_sum_dim without any allocation, for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results (bitwise: the same plan and
+ * kernels) and status codes as rd_sum_dim, plus RD_ERR_WORKSPACE; the full
+ * reduce of n floats is rd_sum_dim_noalloc(x, 1, n, 1, out, stream).
+ * Where the shape's plan needs partial results (rd_plan_dim(...).
+ * workspace_bytes > 0), they go to a scratch buffer of
+ * RD_NOALLOC_SCRATCH_BYTES bytes that the library holds in device memory of
+ * each GPU it runs on until the process ends; a plan that needs more is
+ * refused with RD_ERR_WORKSPACE before any work is enqueued (8 MiB holds
+ * the partial sums of a full reduce of up to about 68e9 floats, and the
+ * slabs of every column plan of MI355X's default planner up to a few MB).
+ * Nothing in the buffer needs to start at zero: the first kernel writes
+ * every partial result the second one reads.  Every call on one GPU shares
+ * that GPU's buffer, so calls that may overlap on one GPU -- on different
+ * streams, or from different host threads, without an ordering between
+ * them -- race and give wrong results; calls in one stream's order are
+ * safe.  The partials are always combined by a second kernel (the
+ * RD_COMBINE_LAST_BLOCK tuning option is ignored here).  Set-up: the
+ * library's first call on a device (of any entry point) must not be made
+ * while its stream is being captured (RD_ERR_CAPTURE).
+ */
+#define RD_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+rd_status rd_sum_dim_noalloc(const float* x, int64_t outer, int64_t R, int64_t inner,
+                             float* out, hipStream_t stream);
 
 /*
  * The same two reductions with another operator: rd_reduce_1d(x, n, op, ...)

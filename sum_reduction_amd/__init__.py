@@ -29,6 +29,7 @@ __all__ = [
     "rd_softmax_denom_1d", "rd_softmax_denom_dim", "softmax_denom", "rd_reduce_strided",
     "rd_plan_strided", "rd_softmax_denom_strided", "RD_OK", "RD_ERR_INVALID_ARG",
     "RD_ERR_NO_DEVICE", "RD_ERR_ALLOC", "RD_ERR_LAUNCH", "RD_ERR_HIP", "RD_ERR_CAPTURE",
+    "RD_ERR_WORKSPACE", "RD_NOALLOC_SCRATCH_BYTES", "rd_sum_dim_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +43,9 @@ RD_ERR_ALLOC = 3
 RD_ERR_LAUNCH = 4
 RD_ERR_HIP = 5
 RD_ERR_CAPTURE = 6
+RD_ERR_WORKSPACE = 7
+# bytes of the fixed scratch buffer of rd_sum_dim_noalloc (include/rd.h)
+RD_NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024
 # rd_op: the reductions (the sum is the method; the others share its kernels)
 OPS = {"sum": 0, "sumsq": 1, "max": 2, "min": 3}
 # the softmax denominator's pair (maximum, shifted sum of exponentials) has
@@ -111,6 +115,8 @@ def load():
     lib.rd_sum_1d.restype = ctypes.c_int
     lib.rd_sum_dim.argtypes = [vp, i64, i64, i64, vp, vp]
     lib.rd_sum_dim.restype = ctypes.c_int
+    lib.rd_sum_dim_noalloc.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.rd_sum_dim_noalloc.restype = ctypes.c_int
     lib.rd_reduce_1d.argtypes = [vp, i64, i32, vp, vp]
     lib.rd_reduce_1d.restype = ctypes.c_int
     lib.rd_reduce_dim.argtypes = [vp, i64, i64, i64, i32, vp, vp]
@@ -414,6 +420,21 @@ def rd_sum_dim(x, outer: int, R: int, inner: int, out=None, stream=None):
     optr = out.data_ptr() if out.numel() else None
     _check(load().rd_sum_dim(xp, outer, R, inner, optr, _stream_handle(stream)),
            "rd_sum_dim")
+    return out
+
+
+def rd_sum_dim_noalloc(x, outer: int, R: int, inner: int, out=None, stream=None):
+    """rd_sum_dim without any allocation inside the library: the partial
+    results of a split plan go to its fixed device scratch buffer
+    (RD_NOALLOC_SCRATCH_BYTES; RdError RD_ERR_WORKSPACE when the plan needs
+    more).  Calls that may overlap on one GPU share that buffer and race.
+    Pass ``out`` to allocate nothing at all on the Python side either."""
+    _check_input(x, outer * R * inner)
+    out = _out_tensor(out, outer * inner, x.device, (outer, inner))
+    xp = x.data_ptr() if x.numel() else None
+    optr = out.data_ptr() if out.numel() else None
+    _check(load().rd_sum_dim_noalloc(xp, outer, R, inner, optr, _stream_handle(stream)),
+           "rd_sum_dim_noalloc")
     return out
 
 

@@ -23,7 +23,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "librd.so")
-SOURCES = ["rd_api.cpp", "rd_plan.cpp", "rd_kernels.hip", "rd_scan.hip"]
+SOURCES = ["rd_api.cpp", "rd_plan.cpp", "rd_kernels.hip", "rd_scan.hip", "rd_noalloc.hip"]
 # the bandwidth probes bench.py reports beside the reductions (include/rd_ceiling.h)
 CEILING_LIBRARY = os.path.join(HERE, "librd_ceiling.so")
 CEILING_SOURCES = ["rd_ceiling.hip"]

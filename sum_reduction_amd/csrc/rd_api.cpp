@@ -20,7 +20,8 @@ thread_local int t_last_hip = 0;
 // fixes the plan, hence the summation order); the first call that needs a
 // workspace also creates the library's memory pool for workspaces, which
 // keeps its memory between calls, and the ticket counters of the fused
-// combine.  Calls whose plan needs no workspace never allocate.
+// combine.  Calls whose plan needs no workspace, and rd_sum_dim_noalloc,
+// never allocate.
 // Ticket counters for the fused (last-workgroup) combine: one per stream that
 // has made such a call on the device, zeroed once when they are created and
 // left at zero by every kernel that uses one.  Calls on one stream never
@@ -395,6 +396,35 @@ bool op_valid(int32_t op) { return op >= RD_OP_SUM && op <= RD_OP_MIN; }
 
 }  // namespace
 
+namespace rd {
+
+rd_status sum_dim_fixed(const float* x, int64_t outer, int64_t R, int64_t inner, float* out,
+                        ScratchFn scratch, int64_t scratch_bytes, hipStream_t stream) {
+    bool empty = false;
+    rd_status st = dim_args(x, outer, R, inner, out, &empty);
+    if (st != RD_OK || empty) return st;  // empty: nothing to write, no HIP call
+    Device* dev = nullptr;
+    int index = -1;
+    st = current_device(&dev, &index, stream);
+    if (st != RD_OK) return st;
+    float* ws = nullptr;
+    st = scratch(index, &ws);
+    if (st != RD_OK) return st;
+    Strides v = contiguous(outer, R, inner);
+    rd_plan plan;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        st = plan_view(dev->cu, &v, RD_OP_SUM, g_tune_on ? &g_tune : nullptr, &plan);
+    }
+    if (st != RD_OK) return st;
+    if (plan.workspace_bytes > scratch_bytes) return RD_ERR_WORKSPACE;
+    return execute(plan, RD_OP_SUM, *dev, x, v, Results{out, nullptr}, stream, ws);
+}
+
+void set_last_hip_error(hipError_t e) { t_last_hip = static_cast<int>(e); }
+
+}  // namespace rd
+
 extern "C" {
 
 rd_status rd_reduce_1d(const float* x, int64_t n, int32_t op, float* out,
@@ -545,6 +575,7 @@ const char* rd_status_string(rd_status status) {
         case RD_ERR_LAUNCH: return "RD_ERR_LAUNCH";
         case RD_ERR_HIP: return "RD_ERR_HIP";
         case RD_ERR_CAPTURE: return "RD_ERR_CAPTURE";
+        case RD_ERR_WORKSPACE: return "RD_ERR_WORKSPACE";
     }
     return "RD_ERR_UNKNOWN";
 }

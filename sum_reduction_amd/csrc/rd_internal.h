@@ -148,6 +148,18 @@ constexpr int64_t kScanSmallWavesPerCu = 16;
 // streaming hint (MI355X has a 256 MB last-level cache).
 constexpr uint64_t kScanCachedTotalsBytes = uint64_t(256) << 20;
 
+// The no-allocation sum (rd_api.cpp; its scratch buffer is in rd_noalloc.hip).
+// ScratchFn gives the device's scratch buffer (device index in, pointer out);
+// it is called once the arguments are valid and the device is set up, with
+// that device current.  sum_dim_fixed is rd_sum_dim with that buffer, of
+// scratch_bytes bytes, as the workspace: RD_ERR_WORKSPACE if the plan needs
+// more; nothing allocated, the partial results combined by the second kernel.
+typedef rd_status (*ScratchFn)(int device, float** ptr);
+rd_status sum_dim_fixed(const float* x, int64_t outer, int64_t R, int64_t inner, float* out,
+                        ScratchFn scratch, int64_t scratch_bytes, hipStream_t stream);
+// Keeps e for rd_last_hip_error() on the calling thread.
+void set_last_hip_error(hipError_t e);
+
 // Which kernel shapes this build instantiates for an operator (rd_kernels.hip).
 bool rows_shape_supported(int op, int group, int unroll);
 bool cols_shape_supported(int op, int col_waves, int row_waves, int unroll);

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
                  "rd_plan_1d", "rd_tune_set", "rd_tune_supported", "rd_cumsum_dim",
                  "rd_plan_cumsum", "rd_softmax_denom_1d", "rd_softmax_denom_dim",
                  "rd_reduce_strided", "rd_plan_strided", "rd_softmax_denom_strided",
-                 "rd_cumsum_strided", "rd_plan_cumsum_strided"):
+                 "rd_cumsum_strided", "rd_plan_cumsum_strided", "rd_sum_dim_noalloc"):
         assert want in names
 
 
@@ -66,12 +66,12 @@ def test_ceiling_probes_export_their_header():
 
 def test_version_and_status_strings():
     assert rd.rd_version() == 100
-    names = [rd.rd_status_string(s) for s in range(7)]
+    names = [rd.rd_status_string(s) for s in range(8)]
     assert names == ["RD_OK", "RD_ERR_INVALID_ARG", "RD_ERR_NO_DEVICE", "RD_ERR_ALLOC",
-                     "RD_ERR_LAUNCH", "RD_ERR_HIP", "RD_ERR_CAPTURE"]
+                     "RD_ERR_LAUNCH", "RD_ERR_HIP", "RD_ERR_CAPTURE", "RD_ERR_WORKSPACE"]
     assert rd.rd_status_string(99) == "RD_ERR_UNKNOWN"
     consts = [rd.RD_OK, rd.RD_ERR_INVALID_ARG, rd.RD_ERR_NO_DEVICE, rd.RD_ERR_ALLOC,
-              rd.RD_ERR_LAUNCH, rd.RD_ERR_HIP, rd.RD_ERR_CAPTURE]
+              rd.RD_ERR_LAUNCH, rd.RD_ERR_HIP, rd.RD_ERR_CAPTURE, rd.RD_ERR_WORKSPACE]
     assert [rd.rd_status_string(c) for c in consts] == names
 
 
@@ -118,6 +118,22 @@ def test_dim_invalid_arguments(lib, host_buf):
     ]
     for x, o_, R, i, out_ in cases:
         assert lib.rd_sum_dim(x, o_, R, i, out_, None) == INVALID, (o_, R, i)
+        assert lib.rd_sum_dim_noalloc(x, o_, R, i, out_, None) == INVALID, (o_, R, i)
+    # nothing to write: RD_OK before any HIP call, for both
+    for o_, R, i in ((0, 5, 3), (3, 5, 0), (0, 0, 0)):
+        assert lib.rd_sum_dim(base, o_, R, i, out, None) == OK
+        assert lib.rd_sum_dim_noalloc(base, o_, R, i, out, None) == OK
+
+
+def test_noalloc_scratch_size_is_the_header_constant():
+    """The binding's RD_NOALLOC_SCRATCH_BYTES is the header's, and the
+    default plans of the pages' full reduces fit it (the 1D sum of 1e9
+    floats has 30518 partial sums)."""
+    with open(HEADER) as f:
+        m = re.search(r"#define RD_NOALLOC_SCRATCH_BYTES \((\d+) \* 1024 \* 1024\)", f.read())
+    assert m and int(m.group(1)) * 1024 * 1024 == rd.RD_NOALLOC_SCRATCH_BYTES
+    for n in (1_000_000, 100_000_000, 1_000_000_000):
+        assert 0 < rd.rd_plan_1d(256, n).workspace_bytes <= rd.RD_NOALLOC_SCRATCH_BYTES
 
 
 def test_reduce_rejects_unknown_operator(lib, host_buf):
