@@ -299,11 +299,13 @@ def main(argv=None):
 
 
 def measure_ceiling(src, achieved_gbs):
-    """Bandwidth of trivial kernels on this GPU (librd_ceiling.so): a
-    grid-stride read of `src` over a few grid sizes, and a copy of it, grid-
-    stride or one 16-byte chunk per thread over a few workgroup sizes; best
-    median of 10 event-timed launches.  Context for the roofline fraction,
-    which stays relative to the published 8 TB/s."""
+    """Bandwidth of trivial kernels on this GPU (librd_ceiling.so): reads of
+    `src` -- grid-stride over a few grid sizes, and pieces of a few lengths,
+    one per workgroup, 16 loads in flight per lane -- and a copy of it,
+    grid-stride or one 16-byte chunk per thread over a few workgroup sizes;
+    best median of 10 event-timed launches.  The best read is the achievable
+    read rate the dominant kernel is compared with; the roofline fraction
+    stays relative to the published 8 TB/s."""
     import ctypes
 
     import torch
@@ -311,12 +313,16 @@ def measure_ceiling(src, achieved_gbs):
     lib = ctypes.CDLL(os.path.join(ROOT, "sum_reduction_amd", "librd_ceiling.so"))
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.rd_ceiling_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.rd_ceiling_read_pieces.argtypes = [vp, i64, i32, vp, vp]
     lib.rd_ceiling_copy.argtypes = [vp, vp, i64, i32, vp]
     lib.rd_ceiling_copy_flat.argtypes = [vp, vp, i64, i32, vp]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream or None
     n = src.numel() // 4 * 4
-    sink = torch.empty((1 << 15) * 256, dtype=torch.float32, device=src.device)
+    # one float per grid-stride thread (at most 8192 x 256) or per piece
+    # (at most ceil(n/4 / 4096))
+    sink = torch.empty(max((1 << 13) * 256, n // 4 // 4096 + 1), dtype=torch.float32,
+                       device=src.device)
     dst = torch.empty(n, dtype=torch.float32, device=src.device)
 
     def best(fn, grids, nbytes):
@@ -339,6 +345,9 @@ def measure_ceiling(src, achieved_gbs):
 
     rd_gbs, rd_g = best(lambda g: lib.rd_ceiling_read(src.data_ptr(), n, g, sink.data_ptr(), sh),
                         (256, 512, 1024, 2048, 4096, 8192), 4 * n)
+    pc_gbs, pc_s = best(lambda s: lib.rd_ceiling_read_pieces(src.data_ptr(), n, s,
+                                                             sink.data_ptr(), sh),
+                        (1, 2, 4, 8), 4 * n)
     cp_gbs, cp_g = best(lambda g: lib.rd_ceiling_copy(src.data_ptr(), dst.data_ptr(), n, g, sh),
                         (2048, 8192, 32768), 8 * n)
     fl_gbs, fl_t = best(lambda t: lib.rd_ceiling_copy_flat(src.data_ptr(), dst.data_ptr(), n, t,
@@ -348,10 +357,15 @@ def measure_ceiling(src, achieved_gbs):
     torch.cuda.empty_cache()
     copy_shape = ("grid-stride, %d workgroups of 256" % cp_g if cp_gbs >= fl_gbs else
                   "one 16-byte chunk per thread, workgroups of %d" % fl_t)
-    return {"read_GBps": round(rd_gbs, 1), "read_blocks": rd_g,
+    read = max(rd_gbs, pc_gbs)
+    read_shape = ("grid-stride, %d workgroups of 256" % rd_g if rd_gbs >= pc_gbs else
+                  "a piece of %d KB per workgroup of 256, 16 loads in flight per lane"
+                  % (pc_s * 64))
+    return {"read_GBps": round(read, 1), "read_shape": read_shape,
+            "read_grid_stride_GBps": round(rd_gbs, 1), "read_pieces_GBps": round(pc_gbs, 1),
             "copy_GBps": round(max(cp_gbs, fl_gbs), 1), "copy_shape": copy_shape,
             "copy_grid_stride_GBps": round(cp_gbs, 1), "bytes_read": 4 * n,
-            "roofline_achieved_over_read": round(achieved_gbs / rd_gbs, 4),
+            "roofline_achieved_over_read": round(achieved_gbs / read, 4),
             "kind": "trivial kernels, 16-byte nontemporal accesses (include/rd_ceiling.h)"}
 
 

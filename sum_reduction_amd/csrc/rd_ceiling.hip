@@ -5,6 +5,12 @@
 //   read:  every lane streams 16-byte nontemporal loads in grid-stride
 //          order, 4 in flight, and writes one float (its sum) at the end so
 //          that the loads are not dead code;
+//   read_pieces: workgroup b reads the b-th piece of steps x 4096 chunks
+//          (16 loads in flight per lane, each load instruction of the
+//          workgroup 4 KB of adjacent chunks), then writes one float --
+//          many short-lived workgroups each streaming one contiguous piece,
+//          the shape of the library's row reduction; steps = 1 is one
+//          16-load step per lane;
 //   copy:  every lane copies 16-byte chunks with nontemporal loads and
 //          stores, grid-stride; or (copy_flat) one chunk per lane, a grid of
 //          as many lanes as chunks -- on MI355X the faster of the two by far
@@ -46,6 +52,34 @@ __global__ __launch_bounds__(256) void copy_kernel(const v4f* __restrict__ x, v4
         __builtin_nontemporal_store(__builtin_nontemporal_load(x + i), y + i);
 }
 
+// workgroup b: chunks [b*P, (b+1)*P), P = steps * 16 * 256, 16 loads in
+// flight per lane; every load is checked against n4
+__global__ __launch_bounds__(256) void read_pieces_kernel(const v4f* __restrict__ x, int64_t n4,
+                                                          int32_t steps,
+                                                          float* __restrict__ sink) {
+    constexpr int U = 16;
+    const int64_t base = int64_t(blockIdx.x) * steps * (U * 256) + threadIdx.x;
+    v4f a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < steps; ++s) {
+        const int64_t i0 = base + int64_t(s) * (U * 256);
+        v4f v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = i0 + u * 256;
+            v[u] = i < n4 ? __builtin_nontemporal_load(x + i) : v4f{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+            a += v[u];
+            b += v[u + 1];
+        }
+    }
+    a += b;
+    float t = (a.x + a.y) + (a.z + a.w);
+    // one value per workgroup (any lane's would do; lane 0's keeps it simple)
+    if (threadIdx.x == 0) sink[blockIdx.x] = t;
+}
+
 // one 16-byte chunk per lane; the grid covers n4 chunks
 template <int T>
 __global__ __launch_bounds__(T) void copy_flat_kernel(const v4f* __restrict__ x,
@@ -64,6 +98,18 @@ int rd_ceiling_read(const float* x, int64_t n, int32_t blocks, float* sink, hipS
     if (!x || !sink || n < 4 || blocks < 1 || blocks > (1 << 20) || !aligned16(x)) return 1;
     read_kernel<<<dim3(uint32_t(blocks)), dim3(256), 0, stream>>>(
         reinterpret_cast<const v4f*>(x), n / 4, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int rd_ceiling_read_pieces(const float* x, int64_t n, int32_t steps, float* sink,
+                           hipStream_t stream) {
+    if (!x || !sink || n < 4 || steps < 1 || steps > 1024 || !aligned16(x)) return 1;
+    const int64_t n4 = n / 4;
+    const int64_t piece = int64_t(steps) * 16 * 256;
+    const int64_t blocks = (n4 + piece - 1) / piece;
+    if (blocks > int64_t(UINT32_MAX) / 256) return 1;
+    read_pieces_kernel<<<dim3(uint32_t(blocks)), dim3(256), 0, stream>>>(
+        reinterpret_cast<const v4f*>(x), n4, steps, sink);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

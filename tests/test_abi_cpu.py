@@ -45,7 +45,8 @@ def test_ceiling_probes_export_their_header():
     with open(os.path.join(ROOT, "include", "rd_ceiling.h")) as f:
         text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(rd_ceiling_[a-z_]+)\s*\(", text)))
-    assert names == ["rd_ceiling_copy", "rd_ceiling_copy_flat", "rd_ceiling_read"]
+    assert names == ["rd_ceiling_copy", "rd_ceiling_copy_flat", "rd_ceiling_read",
+                     "rd_ceiling_read_pieces"]
     lib = ctypes.CDLL(os.path.join(ROOT, "sum_reduction_amd", "librd_ceiling.so"))
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.rd_ceiling_read.argtypes = [vp, i64, i32, vp, vp]
@@ -56,6 +57,11 @@ def test_ceiling_probes_export_their_header():
     assert lib.rd_ceiling_read(base, 3, 1, base, None) == 1
     assert lib.rd_ceiling_read(base + 4, 16, 1, base, None) == 1     # not 16-B aligned
     assert lib.rd_ceiling_read(base, 16, 0, base, None) == 1
+    lib.rd_ceiling_read_pieces.argtypes = [vp, i64, i32, vp, vp]
+    assert lib.rd_ceiling_read_pieces(None, 16, 1, base, None) == 1
+    assert lib.rd_ceiling_read_pieces(base + 4, 16, 1, base, None) == 1   # not 16-B aligned
+    assert lib.rd_ceiling_read_pieces(base, 16, 0, base, None) == 1       # no steps
+    assert lib.rd_ceiling_read_pieces(base, 16, 2000, base, None) == 1    # too many steps
     assert lib.rd_ceiling_copy(base, base + 32, 16, 1, None) == 1    # overlap
     assert lib.rd_ceiling_copy(base, None, 16, 1, None) == 1
     lib.rd_ceiling_copy_flat.argtypes = [vp, vp, i64, i32, vp]
