@@ -203,8 +203,13 @@ rd_status rd_reduce_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
  * The kernel follows the unit stride: stride_inner == 1 reads columns with
  * 16-byte loads as rd_reduce_dim does for inner > 1; stride_r == 1 reads each
  * output's R terms as a row; a single kept axis of adjacent outputs
- * (inner == 1, stride_outer == 1) is read as columns; any other layout takes
- * one lane per output (correct, not fast).  A contiguous view
+ * (inner == 1, stride_outer == 1) is read as columns; a kept inner axis of
+ * terms 2 .. 32 floats apart whose rows span more than 128 floats and do not
+ * overlap (stride_r at least the span) is read as the dense span of each row
+ * (every 128-byte line there holds a term, so the same lines are fetched)
+ * with every stride_inner-th column kept -- the floats in between are read
+ * but never reach a result; any other layout
+ * takes one lane per output (correct, not fast).  A contiguous view
  * (stride_outer = R*inner, stride_r = inner, stride_inner = 1) gives the bits
  * rd_reduce_dim gives.  Status codes as for rd_reduce_dim.  Source: the
  * POPCORNBENCH problem-47 trace reduces a torch tensor over one dimension

@@ -17,6 +17,11 @@ constexpr int kBlock = 256;
 constexpr int64_t kShortRow = 64;
 // Inner sizes up to this take the several-rows-per-load column path.
 constexpr int64_t kSmallInner = 128;
+// A strided view whose kept inner axis is 2 .. kDenseColumnStride floats apart
+// (every 128-byte line of a row's span then holds one of its terms) and whose
+// rows span more than kSmallInner floats is reduced by the column kernel over
+// the dense span of its rows, keeping every si-th column (dense_columns).
+constexpr int64_t kDenseColumnStride = 32;
 // Upper bound on workgroups per launch; larger problems loop inside the
 // kernels (a grid's total thread count must stay below 2^32 on AMD, and
 // workgroups have up to 1024 threads).
@@ -51,6 +56,11 @@ rd_status plan_view(int cu_count, Strides* v, int op, const rd_tune* tune, rd_pl
 // Non-negative sizes and strides whose furthest element, and outer*R*inner
 // floats, are representable in bytes.
 bool view_sizes_ok(const Strides& v);
+// A view the column kernel reads as the dense span of its rows (see
+// kDenseColumnStride): inner > 1, 2 <= si <= kDenseColumnStride, span wider
+// than kSmallInner, rows that do not overlap (sr >= span, or R == 1).
+// plan_view gives it a COLS plan; launch_cols keeps every si-th column.
+bool dense_columns(const Strides& v);
 // A contiguous [outer, R, inner] array.
 rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op,
                    const rd_tune* tune, rd_plan* plan);
@@ -67,7 +77,7 @@ hipError_t launch_rows_short(int op, const float* x, const Strides& v, Results o
                              hipStream_t s);
 hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, Results out,
                                hipStream_t s);
-// Columns (v.si == 1).
+// Columns (v.si == 1, or a dense_columns view).
 hipError_t launch_cols(int op, const rd_plan& p, const float* x, const Strides& v,
                        Results dst, hipStream_t s);
 hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, const Strides& v,

@@ -742,11 +742,17 @@ __global__ __launch_bounds__(kBlock) void rows_combine_kernel(typename St<OP>::O
 // slab_combine_kernel.  Needs inner >= 4.  Element (o, r, c) is read at
 // x + o*so + r*sr + c: columns are contiguous, rows and outer indices may be
 // any distance apart (a contiguous array has so = R*inner, sr = inner).
+// Column c goes to output c / cstride of its outer index (inner_out per outer
+// index) when c % cstride == 0: cstride == 1 for an array; a strided view whose
+// terms are cstride floats apart along its kept inner axis is read as the dense
+// span of its rows and only every cstride-th column is kept (each column has
+// accumulator lanes of its own, so the floats in between never reach a kept
+// result).
 template <int OP, int CW, int RW, int U, bool NT>
 __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
     const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t so,
-    int64_t sr, int64_t ntiles, int64_t S, int64_t rps, typename St<OP>::Out dst,
-    uint32_t nxcd) {
+    int64_t sr, int64_t ntiles, int64_t S, int64_t rps, int64_t cstride, int64_t inner_out,
+    typename St<OP>::Out dst, uint32_t nxcd) {
     typedef St<OP> T;
     __shared__ typename T::S4 lds[RW > 1 ? (RW - 1) * CW * kWave : 1];
     const int wave = threadIdx.x / kWave;
@@ -817,9 +823,18 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
             __syncthreads();
         }
         if (rw == 0 && active) {
-            const int64_t e = (s * outer + o) * inner + cl;
             const int keep = int(c - cl);  // 0, or 1..3 for the row's last lane
-            for (int q = keep; q < 4; ++q) T::put(dst, e + q, T::lane(a, q));
+            if (cstride == 1) {
+                const int64_t e = (s * outer + o) * inner + cl;
+                for (int q = keep; q < 4; ++q) T::put(dst, e + q, T::lane(a, q));
+            } else {
+                const int64_t e = (s * outer + o) * inner_out;
+                for (int q = keep; q < 4; ++q) {
+                    const int64_t col = cl + q;
+                    const int64_t k = col / cstride;
+                    if (k * cstride == col) T::put(dst, e + k, T::lane(a, q));
+                }
+            }
         }
     }
 }
@@ -1122,10 +1137,13 @@ hipError_t rows_op(const rd_plan& p, const RowsArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+// inner: the floats read per row; cstride, inner_out: see cols_kernel (1 and
+// inner for an array).
 struct ColsArgs {
     const float* x;
     int64_t outer, R, inner, so, sr;
     Results dst;
+    int64_t cstride, inner_out;
 };
 
 template <int OP, int CW, int RW, int U, bool NT>
@@ -1134,7 +1152,7 @@ hipError_t cols_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
         const int64_t ntiles = ((a.inner + 3) / 4 + CW * kWave - 1) / (CW * kWave);
         return launch(cols_kernel<OP, CW, RW, U, NT>, p.blocks, kWave * CW * RW, s, a.x,
                       a.outer, a.R, a.inner, a.so, a.sr, ntiles, p.split, p.rows_per_split,
-                      out_of<OP>(a.dst), uint32_t(p.nxcd));
+                      a.cstride, a.inner_out, out_of<OP>(a.dst), uint32_t(p.nxcd));
     } else {
         return hipErrorInvalidValue;
     }
@@ -1320,13 +1338,16 @@ hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, R
 
 hipError_t launch_cols(int op, const rd_plan& p, const float* x, const Strides& v,
                        Results dst, hipStream_t s) {
-    const ColsArgs a{x, v.outer, v.R, v.inner, v.so, v.sr, dst};
+    if (v.si != 1 && !dense_columns(v)) return hipErrorInvalidValue;
+    const int64_t span = (v.inner - 1) * v.si + 1;  // v.inner for an array
+    const ColsArgs a{x, v.outer, v.R, span, v.so, v.sr, dst, v.si, v.inner};
     RD_BY_OP(op, cols_op, p, a, s)
 }
 
 hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, const Strides& v,
                              Results dst, hipStream_t s) {
-    const ColsArgs a{x, v.outer, v.R, v.inner, v.so, v.sr, dst};
+    if (v.si != 1) return hipErrorInvalidValue;
+    const ColsArgs a{x, v.outer, v.R, v.inner, v.so, v.sr, dst, 1, v.inner};
     RD_BY_OP(op, cols_small_go, p, a, s)
 }
 

@@ -155,10 +155,16 @@ void split_rows(int64_t R, int64_t S, rd_plan* p) {
     p->split = ceil_div(R, rps);
 }
 
-rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
-                    const rd_tune* t, rd_plan* p) {
+// Columns: lanes along the contiguous inner axis.  inner is the width read
+// per row and inner_out the outputs per outer index: the same for an array;
+// a view whose kept inner axis has a small stride is read as the dense span
+// of its rows (inner = (inner_out - 1) * stride + 1, the COLS kernel only).
+rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int64_t inner_out,
+                    int op, const rd_tune* t, rd_plan* p) {
     const int32_t forced = t ? t->path : 0;
     if (forced && forced != RD_PATH_COLS && forced != RD_PATH_COLS_SMALL)
+        return RD_ERR_INVALID_ARG;
+    if (inner != inner_out && (forced == RD_PATH_COLS_SMALL || inner <= kSmallInner))
         return RD_ERR_INVALID_ARG;
     if (forced == RD_PATH_COLS && inner < 4) return RD_ERR_INVALID_ARG;
     if (forced == RD_PATH_COLS_SMALL && inner > 2 * kSmallInner) return RD_ERR_INVALID_ARG;
@@ -251,12 +257,12 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int op,
     }
     if (S < 1) return RD_ERR_INVALID_ARG;
     split_rows(R, S, p);
-    if (p->split > INT64_MAX / result_bytes(op) / (outer * inner)) return RD_ERR_INVALID_ARG;
+    if (p->split > INT64_MAX / result_bytes(op) / (outer * inner_out)) return RD_ERR_INVALID_ARG;
     p->blocks = base * p->split;
     if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
     p->passes = p->split > 1 ? 2 : 1;
     p->combine = p->split > 1 ? RD_COMBINE_PASS : RD_COMBINE_NONE;
-    p->workspace_bytes = p->split > 1 ? p->split * outer * inner * result_bytes(op) : 0;
+    p->workspace_bytes = p->split > 1 ? p->split * outer * inner_out * result_bytes(op) : 0;
     return RD_OK;
 }
 
@@ -323,6 +329,14 @@ bool view_sizes_ok(const Strides& v) {
     return true;
 }
 
+bool dense_columns(const Strides& v) {
+    if (!(v.inner > 1 && v.si >= 2 && v.si <= kDenseColumnStride)) return false;
+    const int64_t span = (v.inner - 1) * v.si + 1;
+    // rows whose spans overlap (a transposed array, stride_r < span) would
+    // read the same lines once per row: those keep the lane-per-output kernels
+    return span > kSmallInner && (v.R == 1 || v.sr >= span);
+}
+
 void normalize_view(Strides* v) {
     // strides of axes of length 1 never move: give them the unit value
     if (v->inner == 1) v->si = 1;
@@ -358,9 +372,18 @@ rd_status plan_view(int cu_count, Strides* v, int op, const rd_tune* tune, rd_pl
         return RD_OK;
     }
     if (inner == 1 && v->sr == 1) return plan_rows(cu_count, outer, R, op, tune, plan);
-    if (inner > 1 && v->si == 1) return plan_cols(cu_count, outer, R, inner, op, tune, plan);
+    if (inner > 1 && v->si == 1)
+        return plan_cols(cu_count, outer, R, inner, inner, op, tune, plan);
     // the reduced axis contiguous, the kept ones strided: outer*inner rows
     if (v->sr == 1) return plan_rows(cu_count, outer * inner, R, op, tune, plan);
+    // the kept inner axis a few floats apart: every cache line of a row's
+    // span holds a term, so the dense span is read with the column kernel
+    // (the same lines, in 16-byte loads) and every si-th column kept
+    if (dense_columns(*v)) {
+        const int64_t span = (inner - 1) * v->si + 1;
+        if (!(tune && tune->path == RD_PATH_COLS_SMALL))
+            return plan_cols(cu_count, outer, R, span, inner, op, tune, plan);
+    }
     return plan_strided(cu_count, outer, R, inner, op, tune, plan);
 }
 
@@ -384,7 +407,10 @@ namespace {
 // The lane-per-column scan: columns split along R into slabs as the strided
 // reduction's outputs are (about kStridedLanesPerCu lanes per CU, at least
 // kStridedMinRows rows per slab); then slab totals, their scan, the scan from
-// the carries.
+// the carries.  (Measured on MI355X for the transposed [32768, 32768] array,
+// 32768 columns: 8 slabs of 256-column workgroups, x read twice, took 2.4 /
+// 2.5 ms for the row / column scan; one pass of 512 single-wave workgroups
+// took 2.8 / 3.8 ms.)
 rd_status plan_scan_strided(int64_t cu, int64_t outer, int64_t R, int64_t inner,
                             const rd_tune* t, rd_plan* p) {
     if (t && (t->group || t->col_waves || t->row_waves || t->unroll || t->order || t->combine))
@@ -439,6 +465,10 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
     const int32_t forced = t ? t->path : 0;
     const bool rows_ok = inner == 1 && v->sr == 1;
     const bool cols_ok = inner > 1 && v->si == 1;
+    // (a kept inner axis of terms a few floats apart is not scanned over the
+    // dense span of its rows as the reductions do: x[::8, ::3] of [32768,
+    // 32768], whose 128 tiles need slabs, took 0.39 ms so against 0.30 ms
+    // with a lane per column)
     if (forced == RD_PATH_SCAN_STRIDED || (!rows_ok && !cols_ok))
         return forced && forced != RD_PATH_SCAN_STRIDED
                    ? RD_ERR_INVALID_ARG
@@ -535,18 +565,23 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         return RD_OK;
     }
     // a lane per 4 columns (per row of 2 or 3), a wave per 64 lane-columns;
-    // slabs of R (totals, their scan, the scan from the carries) when there
-    // are fewer than 8 waves per CU
+    // slabs of R (totals, their scan, the scan from the carries: x is read
+    // twice) only when there are fewer waves than CUs.  Measured on MI355X:
+    // [16, 8192, 4096] (256 waves) 1074 us cut into 8 slabs of 8-wave
+    // blocks, 713 us in one pass of single-wave blocks; [64, 512, 1024] 75 ->
+    // 65 us; [1, 65536, 8192] (32 waves) 1171 -> 991 us in 8 slabs of
+    // single-wave blocks.
     p->path = RD_PATH_SCAN_COLS;
     p->unroll = (t && t->unroll) ? t->unroll : kScanColsUnroll;
     if (p->unroll != 4 && p->unroll != 8 && p->unroll != 16) return RD_ERR_INVALID_ARG;
     const int64_t lane_cols = inner >= 4 ? ceil_div(inner, 4) : 1;
-    const int64_t waves = ceil_div(lane_cols, kWave) * outer;
+    const int64_t tiles = ceil_div(lane_cols, kWave);
+    const int64_t waves = tiles * outer;
     int64_t S = 1;
     if (t && t->split) {
         S = t->split;
-    } else if (waves < 8 * cu) {
-        S = ceil_div(8 * cu, waves);
+    } else if (waves < cu) {
+        S = ceil_div(cu, waves);
         int64_t cap = R / 64;
         if (cap < 1) cap = 1;
         if (S > cap) S = cap;
@@ -556,15 +591,17 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
     // slabs of at least kScanColsDeepRows rows keep 16 rows in flight
     if (!(t && t->unroll) && p->rows_per_split >= kScanColsDeepRows) p->unroll = 16;
     // a block per (col_waves adjacent tiles, slab, outer index): the widest
-    // of 16, 8, 4 tiles that still gives every CU a block
-    const int64_t tiles = ceil_div(lane_cols, kWave);
+    // of 16, 8, 4, 2, 1 tiles that still gives every CU a block (wide blocks
+    // share fewer tile edges; [128, 4096, 4095]: 8 tiles, 3322 us against
+    // 3960 with single-wave blocks)
     if (t && t->col_waves) {
         p->col_waves = t->col_waves;
-        if (p->col_waves != 4 && p->col_waves != 8 && p->col_waves != 16)
+        if (p->col_waves != 4 && p->col_waves != 8 && p->col_waves != 16 &&
+            !((p->col_waves == 1 || p->col_waves == 2) && inner >= 4))
             return RD_ERR_INVALID_ARG;
     } else {
-        p->col_waves = 4;
-        for (int bw = 16; bw > 4; bw /= 2) {
+        p->col_waves = inner >= 4 ? 1 : 4;
+        for (int bw = 16; bw > p->col_waves; bw /= 2) {
             if (tiles >= bw && ceil_div(tiles, bw) * p->split * outer >= cu) {
                 p->col_waves = bw;
                 break;

@@ -1149,13 +1149,22 @@ hipError_t cols_go(const rd_plan& p, const float* x, float* out, const Strides& 
     const int64_t ntiles = (lane_cols + kWave - 1) / kWave;
     if (p.col_waves == 16)
         return cols_bw<REV, V, 16, NT>(p, x, out, v, ntiles, carry_in, totals, s);
-    if (p.col_waves == 8) return cols_bw<REV, V, 8, NT>(p, x, out, v, ntiles, carry_in, totals, s);
+    if (p.col_waves == 8)
+        return cols_bw<REV, V, 8, NT>(p, x, out, v, ntiles, carry_in, totals, s);
+    if constexpr (V == 4) {
+        if (p.col_waves == 2)
+            return cols_bw<REV, V, 2, NT>(p, x, out, v, ntiles, carry_in, totals, s);
+        if (p.col_waves == 1)
+            return cols_bw<REV, V, 1, NT>(p, x, out, v, ntiles, carry_in, totals, s);
+    }
+    if (p.col_waves != 4) return hipErrorInvalidValue;
     return cols_bw<REV, V, 4, NT>(p, x, out, v, ntiles, carry_in, totals, s);
 }
 
 template <bool REV, bool NT>
 hipError_t cols_v(const rd_plan& p, const float* x, float* out, const Strides& v,
                   const float* carry_in, float* totals, hipStream_t s) {
+    if (v.si != 1) return hipErrorInvalidValue;
     if (v.inner == 2) return cols_go<REV, 2, NT>(p, x, out, v, carry_in, totals, s);
     if (v.inner == 3) return cols_go<REV, 3, NT>(p, x, out, v, carry_in, totals, s);
     return cols_go<REV, 4, NT>(p, x, out, v, carry_in, totals, s);

@@ -90,7 +90,12 @@ void check_reduce_plan(const rd::Strides& v, int op, const rd_plan& p) {
             break;
         case RD_PATH_COLS:
         case RD_PATH_COLS_SMALL:
-            if (v.si != 1) fail("column path without unit inner stride", v, op, p);
+            // a strided kept inner axis only as a dense span (every
+            // si-th column of it kept), and only on the wide column path
+            if (v.si != 1 && !(rd::dense_columns(v) && p.path == RD_PATH_COLS))
+                fail("column path without unit inner stride", v, op, p);
+            if (v.si != 1 && (v.inner - 1) * v.si + 1 <= rd::kSmallInner)
+                fail("dense span too narrow for the column kernel", v, op, p);
             if (p.rows_per_split < 1 || p.split * p.rows_per_split < v.R ||
                 (p.split - 1) * p.rows_per_split >= v.R)
                 fail("slabs do not tile R", v, op, p);
@@ -158,6 +163,7 @@ void check_scan_plan(const rd::Strides& v, const rd_plan& p) {
             if (p.path == RD_PATH_SCAN_STRIDED &&
                 p.blocks != std::min(rd::kMaxBlocks, p.split * ((n + rd::kBlock - 1) / rd::kBlock)))
                 fail("scan strided blocks", v, -1, p);
+            break;
             break;
         default:
             fail("unknown scan path", v, -1, p);

@@ -52,6 +52,13 @@ VIEWS = [
     ("transpose_short_rows", 5 * 1000, 1000, 5, 1, 1, 1000, 1, "scan_strided"),
     ("transpose_short_cols", 7 * 300, 1, 7, 300, 0, 1, 7, "scan_strided"),
     ("transpose_every_third", 70 * 900, 300, 70, 1, 3, 900, 1, "scan_strided"),
+    # a strided kept inner axis with a wide span, with and without slabs, and
+    # transposes with enough columns for several workgroups per CU
+    ("every_third_column_wide", 200 * 900, 1, 100, 300, 0, 1800, 3, "scan_strided"),
+    ("every_fifth_3d", 4 * 50 * 1000, 4, 50, 200, 50 * 1000, 1000, 5, "scan_strided"),
+    ("every_seventh_slabs", 3000 * 1400, 1, 3000, 200, 0, 1400, 7, "scan_strided"),
+    ("transpose_rows_wide", 40 * 20000, 20000, 40, 1, 1, 20000, 1, "scan_strided"),
+    ("transpose_cols_wide", 40 * 20000, 1, 40, 20000, 0, 1, 40, "scan_strided"),
 ]
 
 

@@ -45,6 +45,14 @@ VIEWS = [
     ("broadcast_row_sums", 300, 50, 300, 1, 0, 1, 1, "rows"),
     ("rows_of_columns", 6 * 400 * 7, 6, 400, 7, 2800, 1, 400, "rows"),
     ("every_third_column", 200 * 90, 1, 100, 30, 0, 180, 3, "strided"),
+    # the kept inner axis 2..32 floats apart and a wide span: the column
+    # kernel over the dense span of each row, every si-th column kept
+    ("every_third_column_wide", 200 * 900, 1, 100, 300, 0, 1800, 3, "cols"),
+    ("every_fifth_3d", 4 * 50 * 1000, 4, 50, 200, 50 * 1000, 1000, 5, "cols"),
+    ("every_other_column_rows", 300 * 700, 1, 300, 350, 0, 700, 2, "cols"),
+    ("every_32nd_column", 64 * 32 * 200, 1, 64, 200, 0, 32 * 200, 32, "cols"),
+    ("every_33rd_column", 64 * 33 * 200, 1, 64, 200, 0, 33 * 200, 33, "strided"),
+    ("every_seventh_split", 2 * 3000 * 1400, 2, 3000, 200, 3000 * 1400, 1400, 7, "cols"),
     ("permuted_3d", 5 * 6 * 7, 7, 5, 6, 1, 42, 7, "strided"),
     ("strided_long", 3 * 20000 * 2, 3, 20000, 2, 1, 6, 3, "strided"),
 ]

@@ -239,7 +239,7 @@ def test_default_plans_are_built_for_every_operator():
                 assert rd.rd_tune_supported("cols_small", 0, 0, p["unroll"], op), (op, p)
 
 
-def _scan_invariants(p, outer, R, inner):
+def _scan_invariants(p, outer, R, inner, cu=CU):
     d = p.as_dict()
     assert d["path"] == ("scan_rows" if inner == 1 else
                          "scan_cols_small" if inner <= 128 else "scan_cols")
@@ -266,9 +266,15 @@ def _scan_invariants(p, outer, R, inner):
     else:
         tiles = -(-(-(-inner // 4) if inner >= 4 else 1) // 64)
         bw = p.col_waves
-        assert bw in (4, 8, 16) and p.block_threads == 64 * bw
-        assert bw == 4 or tiles >= bw
-        assert p.blocks == min(-(-tiles // bw) * p.split * outer, 1 << 20)
+        assert bw in (1, 2, 4, 8, 16) and p.block_threads == 64 * bw
+        assert tiles >= bw
+        # slabs only when there are fewer waves (tiles x outer) than CUs;
+        # then the widest block that still gives every CU one
+        assert (p.split > 1) == (tiles * outer < cu and R >= 128)
+        blocks = -(-tiles // bw) * p.split * outer
+        assert blocks >= cu or bw == 1
+        assert bw == 16 or -(-tiles // (2 * bw)) * p.split * outer < cu or tiles < 2 * bw
+        assert p.blocks == min(blocks, 1 << 20)
         ws = 2 * p.split * outer * inner * 4 if p.split > 1 else 0
     assert p.workspace_bytes == ws
     assert p.passes == (3 if p.split > 1 else 1)
@@ -336,8 +342,8 @@ def test_cumsum_plans():
             inner = 1
         if rng.random() < 0.2:
             outer = int(rng.integers(1, 8))
-        _scan_invariants(rd.rd_plan_cumsum(int(rng.integers(1, 300)), outer, R, inner),
-                         outer, R, inner)
+        cu = int(rng.integers(1, 300))
+        _scan_invariants(rd.rd_plan_cumsum(cu, outer, R, inner), outer, R, inner, cu)
 
 
 def test_cumsum_forced_split():
@@ -486,18 +492,29 @@ def test_strided_path_follows_the_unit_stride():
     assert P(2, 64, 1000, 10**6, 3000, 1)["path"] == "cols"
     # broadcast rows (stride 0) still have a unit stride
     assert P(1, 50, 300, 0, 0, 1)["path"] == "cols_small" or P(1, 50, 300, 0, 0, 1)["path"] == "cols"
-    # no unit stride: the lane-per-output kernel
-    p = P(3, 100, 50, 10**5, 700, 3)
+    # no unit stride, terms more than 32 floats apart along the kept inner
+    # axis (or a narrow span): the lane-per-output kernel
+    p = P(3, 100, 50, 10**5, 700, 33)
     # 150 outputs: split along R into slabs of at least 32 rows (here 3)
     assert p["path"] == "strided" and p["split"] == 3 and p["rows_per_split"] == 34
     assert p["passes"] == 2 and p["workspace_bytes"] == 4 * 3 * 150
     assert p["blocks"] == -(-450 // 256)
+    assert P(3, 100, 40, 10**5, 700, 3)["path"] == "strided"   # span 118 floats
     # many outputs: one slab, one pass
-    p = P(1, 4096, 10922, 0, 262144, 3)
-    assert p["path"] == "strided" and p["split"] == 25 and p["passes"] == 2   # ceil(256*1024 / 10922)
-    p = P(300, 64, 1000, 10**6, 3000, 7)
+    p = P(300, 64, 1000, 10**6, 3000, 40)
     assert p["path"] == "strided" and p["split"] == 1 and p["passes"] == 1
     assert p["workspace_bytes"] == 0 and p["blocks"] == -(-300000 // 256)
+    # the kept inner axis 2..32 floats apart, a span wider than 128 floats:
+    # the column kernel over the dense span of each row, planned as the
+    # columns of that span, with workspaces sized by the outputs
+    p = P(1, 4096, 10923, 0, 262144, 3)          # x[::8, ::3] of [32768, 32768]
+    q = rd.rd_plan_dim(CU, 1, 4096, 32767).as_dict()
+    assert p["path"] == "cols" and p["split"] == q["split"] and p["blocks"] == q["blocks"]
+    assert p["workspace_bytes"] == q["split"] * 10923 * 4 * (q["split"] > 1)
+    p = P(3, 100, 50, 10**5, 700, 3)             # span 148 floats
+    assert p["path"] == "cols" and p["col_waves"] == rd.rd_plan_dim(CU, 3, 100, 148).col_waves
+    p = P(300, 64, 1000, 10**6, 32000, 32)
+    assert p["path"] == "cols" and p["split"] == 1 and p["workspace_bytes"] == 0
     # length-1 axes lose their strides
     assert P(1, 1000, 1, 999, 1, 77) == rd.rd_plan_dim(CU, 1, 1000, 1).as_dict()
     assert P(5, 1, 6, 6, 12345, 1) == rd.rd_plan_dim(CU, 5, 1, 6).as_dict()
@@ -509,6 +526,9 @@ def test_strided_invalid_views():
         with pytest.raises(rd.RdError):
             rd.rd_plan_strided(CU, *v)
     with rd.tuning(path=4):   # a column kernel cannot read a view without a unit stride
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_strided(CU, 3, 100, 50, 10**5, 700, 33)
+    with rd.tuning(path=5):   # nor the small-inner one a dense span
         with pytest.raises(rd.RdError):
             rd.rd_plan_strided(CU, 3, 100, 50, 10**5, 700, 3)
 
