@@ -371,7 +371,10 @@ typedef struct rd_plan {
                                 1024) */
     int32_t col_waves;       /* COLS, SCAN_COLS: waves side by side across
                                 columns */
-    int32_t row_waves;       /* COLS: waves of one workgroup taking turns in R */
+    int32_t row_waves;       /* COLS, SCAN_COLS: waves of one workgroup taking
+                                turns in R (SCAN_COLS: on one tile, over the
+                                whole of R, when there are fewer tiles x outer
+                                than CUs) */
     int32_t unroll;          /* 16-byte loads in flight per lane (SCAN_ROWS:
                                 1 KB slices per chunk; SCAN_COLS: rows per
                                 load group) */
@@ -418,7 +421,8 @@ rd_status rd_plan_strided(int cu_count, int64_t outer, int64_t R, int64_t inner,
 
 /* Plan of rd_cumsum_dim for that shape (the tuning override's split,
  * unroll -- SCAN_ROWS 4 or 8, SCAN_COLS 4, 8 or 16 --, group -- SCAN_ROWS 64,
- * 256, 512 or 1024 --, col_waves -- SCAN_COLS 4, 8 or 16 -- and nontemporal
+ * 256, 512 or 1024 --, col_waves -- SCAN_COLS 1, 2, 4, 8 or 16 (1 and 2 for
+ * inner >= 4) --, row_waves -- SCAN_COLS, see rd_tune -- and nontemporal
  * fields apply). */
 rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
                          rd_plan* plan);
@@ -442,7 +446,8 @@ typedef struct rd_tune {
     int32_t group;           /* ROWS: 64 or 256; SCAN_ROWS: 64, 256, 512
                                 or 1024 */
     int32_t col_waves;       /* COLS; SCAN_COLS: 4, 8 or 16 */
-    int32_t row_waves;       /* COLS */
+    int32_t row_waves;       /* COLS; SCAN_COLS: 1, 2, 4, 8 or 16 (above 1:
+                                col_waves 1, no slabs, unroll 4 or 8) */
     int32_t unroll;          /* ROWS, COLS: 2, 4, 8 or 16 (scans: see
                                 rd_plan_cumsum) */
     int32_t order;           /* ROWS: rd_order; SCAN_ROWS with a workgroup

@@ -152,6 +152,11 @@ constexpr int kScanColsUnroll = 8;        // rows per load group of the column s
 // [128, 4096, 4095] 3369 -> 3285 us, [16, 8192, 4096] 1073 -> 1055; short
 // slabs -- [64, 512, 1024], 64 rows -- lose 3-5 % with 16)
 constexpr int64_t kScanColsDeepRows = 1024;
+// Column scans with between half and twice as many tiles (x outer) as CUs:
+// a block per tile whose waves take turns on its row groups, at most
+// kScanColsMaxRowWaves of them, aiming at kScanColsRoundWavesPerCu waves per CU.
+constexpr int32_t kScanColsMaxRowWaves = 8;
+constexpr int64_t kScanColsRoundWavesPerCu = 4;
 constexpr int kScanSmallUnroll = 8;       // load instructions per step, small inner
 constexpr int64_t kScanSmallWavesPerCu = 16;
 // Inputs up to this size are read by a split scan's totals pass without the

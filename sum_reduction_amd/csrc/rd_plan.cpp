@@ -404,24 +404,33 @@ rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op
 
 namespace {
 
-// The lane-per-column scan: columns split along R into slabs as the strided
-// reduction's outputs are (about kStridedLanesPerCu lanes per CU, at least
-// kStridedMinRows rows per slab); then slab totals, their scan, the scan from
-// the carries.  (Measured on MI355X for the transposed [32768, 32768] array,
-// 32768 columns: 8 slabs of 256-column workgroups, x read twice, took 2.4 /
-// 2.5 ms for the row / column scan; one pass of 512 single-wave workgroups
-// took 2.8 / 3.8 ms.)
-rd_status plan_scan_strided(int64_t cu, int64_t outer, int64_t R, int64_t inner,
-                            const rd_tune* t, rd_plan* p) {
+// The lane-per-column scan.  Views whose unit-stride side the lanes do not
+// follow (inner == 1: the outputs are staged; stride_r == 1: the inputs) run
+// in blocks of kStageWaves waves on kStageCols columns, which take turns on a
+// slab's row chunks; columns are split along R into slabs (totals, their
+// scan, the scan from the carries: x read twice) only when there are fewer
+// than two such blocks per CU, with slabs of at least one round of the block
+// (kStageWaves x 32 rows).  (The transposed [32768, 32768] array, 32768
+// columns: 512 blocks, one pass.)  Other views take a lane per (slab,
+// column), 256 columns a workgroup, split until about kStridedLanesPerCu
+// lanes per CU are busy, each slab keeping at least kStridedMinRows rows.
+constexpr int64_t kStageCols = 64;
+constexpr int64_t kStageRound = 4 * 32;
+
+rd_status plan_scan_strided(int64_t cu, const Strides& v, const rd_tune* t, rd_plan* p) {
     if (t && (t->group || t->col_waves || t->row_waves || t->unroll || t->order || t->combine))
         return RD_ERR_INVALID_ARG;
+    const int64_t outer = v.outer, R = v.R, inner = v.inner;
     const int64_t n = outer * inner;
+    const bool staged = inner == 1 || v.sr == 1;
+    const int64_t cols = staged ? kStageCols : kBlock;  // columns per workgroup
+    const int64_t nblk = ceil_div(n, cols);
     int64_t S = 1;
     if (t && t->split) {
         S = t->split;
-    } else if (n < cu * kStridedLanesPerCu) {
-        S = ceil_div(cu * kStridedLanesPerCu, n);
-        int64_t cap = R / kStridedMinRows;
+    } else if (staged ? nblk < 2 * cu : n < cu * kStridedLanesPerCu) {
+        S = staged ? ceil_div(2 * cu, nblk) : ceil_div(cu * kStridedLanesPerCu, n);
+        int64_t cap = R / (staged ? kStageRound : kStridedMinRows);
         if (cap < 1) cap = 1;
         if (S > cap) S = cap;
     }
@@ -430,8 +439,8 @@ rd_status plan_scan_strided(int64_t cu, int64_t outer, int64_t R, int64_t inner,
     if (p->split > INT64_MAX / 8 / n) return RD_ERR_INVALID_ARG;
     p->path = RD_PATH_SCAN_STRIDED;
     p->nontemporal = 0;  // neighbouring lanes and rows share lines: keep them cached
-    // a workgroup per (slab, kBlock columns): the staged variants' item
-    p->blocks = p->split * ceil_div(n, kBlock);
+    p->block_threads = kBlock;
+    p->blocks = p->split * nblk;  // a workgroup per (slab, columns)
     if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
     if (p->split > 1) {
         p->passes = 3;
@@ -468,11 +477,11 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
     // (a kept inner axis of terms a few floats apart is not scanned over the
     // dense span of its rows as the reductions do: x[::8, ::3] of [32768,
     // 32768], whose 128 tiles need slabs, took 0.39 ms so against 0.30 ms
-    // with a lane per column)
+    // with a lane per column, measured on MI355X)
     if (forced == RD_PATH_SCAN_STRIDED || (!rows_ok && !cols_ok))
         return forced && forced != RD_PATH_SCAN_STRIDED
                    ? RD_ERR_INVALID_ARG
-                   : plan_scan_strided(cu, outer, R, inner, t, p);
+                   : plan_scan_strided(cu, *v, t, p);
     if (inner == 1 ? (forced && forced != RD_PATH_SCAN_ROWS)
                    : (forced && forced != RD_PATH_SCAN_COLS && forced != RD_PATH_SCAN_COLS_SMALL))
         return RD_ERR_INVALID_ARG;
@@ -577,10 +586,29 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
     const int64_t lane_cols = inner >= 4 ? ceil_div(inner, 4) : 1;
     const int64_t tiles = ceil_div(lane_cols, kWave);
     const int64_t waves = tiles * outer;
+    // Between half and twice as many tiles (x outer) as CUs: a block per
+    // tile whose rw waves take turns on its row groups (one pass), the fewest
+    // that make about kScanColsRoundWavesPerCu waves per CU, at most
+    // kScanColsMaxRowWaves (each block runs on one CU, so fewer tiles than
+    // half the CUs would leave most of them idle: slabs then).  Measured on
+    // MI355X: [1, 16384, 32768] (128 tiles) 1063 us in 2 slabs, 849 us with 8
+    // row waves; [3, 16384, 16384] 1552 -> 1060 us (8); [64, 512, 1024] 64 ->
+    // 50 us (4); [16, 8192, 4096] 707 us with single waves, 704 with 4.
+    int32_t rw = 1;
+    if (t && t->row_waves) {
+        rw = t->row_waves;
+        if (rw != 1 && rw != 2 && rw != 4 && rw != 8 && rw != 16) return RD_ERR_INVALID_ARG;
+        if (rw > 1 && (inner < 4 || (t->split && t->split != 1) ||
+                       (t->col_waves && t->col_waves != 1)))
+            return RD_ERR_INVALID_ARG;
+    } else if (2 * waves >= cu && waves < 2 * cu && inner >= 4 &&
+               !(t && (t->split || t->col_waves))) {
+        while (rw < kScanColsMaxRowWaves && waves * rw < kScanColsRoundWavesPerCu * cu) rw *= 2;
+    }
     int64_t S = 1;
     if (t && t->split) {
         S = t->split;
-    } else if (waves < cu) {
+    } else if (waves < cu && rw == 1) {
         S = ceil_div(cu, waves);
         int64_t cap = R / 64;
         if (cap < 1) cap = 1;
@@ -588,13 +616,18 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
     }
     if (S < 1) return RD_ERR_INVALID_ARG;
     split_rows(R, S, p);
-    // slabs of at least kScanColsDeepRows rows keep 16 rows in flight
-    if (!(t && t->unroll) && p->rows_per_split >= kScanColsDeepRows) p->unroll = 16;
+    // slabs of at least kScanColsDeepRows rows keep 16 rows in flight (the
+    // row-round blocks take groups of 8)
+    if (!(t && t->unroll) && rw == 1 && p->rows_per_split >= kScanColsDeepRows) p->unroll = 16;
+    if (rw > 1 && p->unroll != 4 && p->unroll != 8) return RD_ERR_INVALID_ARG;
+    p->row_waves = rw;
     // a block per (col_waves adjacent tiles, slab, outer index): the widest
     // of 16, 8, 4, 2, 1 tiles that still gives every CU a block (wide blocks
     // share fewer tile edges; [128, 4096, 4095]: 8 tiles, 3322 us against
     // 3960 with single-wave blocks)
-    if (t && t->col_waves) {
+    if (rw > 1) {
+        p->col_waves = 1;
+    } else if (t && t->col_waves) {
         p->col_waves = t->col_waves;
         if (p->col_waves != 4 && p->col_waves != 8 && p->col_waves != 16 &&
             !((p->col_waves == 1 || p->col_waves == 2) && inner >= 4))
@@ -608,7 +641,7 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
             }
         }
     }
-    p->block_threads = p->col_waves * kWave;
+    p->block_threads = p->col_waves * rw * kWave;
     const int64_t block_items = ceil_div(tiles, p->col_waves) * p->split * outer;
     p->blocks = block_items < kMaxBlocks ? block_items : kMaxBlocks;
     if (p->split > 1) {

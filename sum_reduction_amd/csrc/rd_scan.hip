@@ -666,6 +666,89 @@ __global__ __launch_bounds__(BW * kWave) void scan_cols_kernel(
     }
 }
 
+// Few tiles, tall columns: a block of RW waves on one tile (64 lane-columns,
+// 256 columns) of one outer index, over the whole of R (one pass, x read
+// once, where slabs would read it twice).  Wave w takes the groups of U rows
+// w, w + RW, w + 2RW, ... in processing order; per round of RW groups each
+// wave adds its group up (running sums pre_u in processing order, group
+// total t_w), the totals meet in LDS (two slot sets in turn: one barrier a
+// round), wave w's outputs are (carry + t_0 + ... + t_{w-1}) + pre_u, and the
+// carry of the next round is carry + t_0 + ... + t_{RW-1} -- a fixed order, so
+// the results do not depend on timing.  The next round's loads go out before
+// the current round is added up.  inner >= 4; element (o, r, c) at
+// x + o*so + r*sr + c as in scan_cols_kernel, out contiguous.
+template <bool REV, int U, int RW, bool NT>
+__global__ __launch_bounds__(RW * kWave) void scan_cols_rounds_kernel(
+    const float* x, float* out, int64_t outer, int64_t R, int64_t inner, int64_t so,
+    int64_t sr, int64_t ntiles, uint32_t nxcd) {
+    __shared__ v4f slots[2][RW][kWave];
+    const int wave = wave_in_block();
+    const int lane = threadIdx.x % kWave;
+    const int64_t nitems = ntiles * outer;
+    const int64_t per_round = int64_t(RW) * U;
+    const int64_t nrounds = (R + per_round - 1) / per_round;
+    int parity = 0;
+    for (int64_t item = xcd_block(nxcd); item < nitems; item += gridDim.x) {
+        const int64_t tile = item % ntiles;
+        const int64_t o = item / ntiles;
+        const int64_t c = 4 * (tile * kWave + lane);
+        const bool live = c < inner;
+        const int64_t cl = c + 4 > inner ? inner - 4 : c;
+        const int keep = live ? int(c - cl) : 4;
+        const int64_t first = REV ? R - 1 : 0;
+        const int64_t pstep = REV ? -sr : sr;
+        const int64_t qstep = REV ? -inner : inner;
+        const float* p = x + o * so + first * sr + cl;
+        float* q = out + (o * R + first) * inner + cl;
+        // the group of round g: processing positions g*per_round + wave*U + u
+        auto load_group = [&](int64_t g, v4f (&v)[U]) {
+            const int64_t k0 = g * per_round + int64_t(wave) * U;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = live && k0 + u < R ? load4<NT>(p + (k0 + u) * pstep) : v4f{0.f, 0.f, 0.f, 0.f};
+        };
+        auto round = [&](int64_t g, v4f (&v)[U], v4f& carry) {
+            const int64_t k0 = g * per_round + int64_t(wave) * U;
+            v4f t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                t += v[u];
+                v[u] = t;
+            }
+            slots[parity][wave][lane] = t;
+            __syncthreads();
+            v4f mine = carry, next = carry;
+#pragma unroll
+            for (int w = 0; w < RW; ++w) {
+                const v4f sw = slots[parity][w][lane];
+                if (w < wave) mine += sw;
+                next += sw;
+            }
+            carry = next;
+            parity ^= 1;
+            if (live) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (k0 + u < R) store_cols<4, NT>(q + (k0 + u) * qstep, keep, mine + v[u]);
+            }
+        };
+        v4f carry = {0.f, 0.f, 0.f, 0.f};
+        v4f a[U], b[U];
+        load_group(0, a);
+        for (int64_t g = 0; g < nrounds; g += 2) {
+            if (g + 1 < nrounds) load_group(g + 1, b);
+            __builtin_amdgcn_sched_barrier(0);  // the next round's loads go out first
+            round(g, a, carry);
+            __builtin_amdgcn_sched_barrier(0);
+            if (g + 1 >= nrounds) break;
+            if (g + 2 < nrounds) load_group(g + 2, a);
+            __builtin_amdgcn_sched_barrier(0);
+            round(g + 1, b, carry);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // ------------------------------------------------------------ small inner
 // Inclusive scan over the row phases of a wave: lane l = rho*LC + lc receives
 // the sum of the lanes rho' <= rho of its lane-column lc (Hillis-Steele steps
@@ -904,15 +987,26 @@ __global__ __launch_bounds__(kBlock) void scan_strided_kernel(
 }
 
 // Two layouts of scan_strided_kernel's lanes have one unit-stride side that
-// the lanes do not follow; a block then stages that side through an LDS tile
-// of kTileRows rows x kBlock columns (an odd pitch: thread t touching element
-// (t, j), and 32 threads touching 32 consecutive elements of one column, both
-// hit distinct banks).  Every column is still added one term after the other
-// in processing order from the same carry, so the bits are those of
-// scan_strided_kernel.  Block items: (slab s, block of kBlock columns),
-// columns fastest.
+// the lanes do not follow; a block then stages that side through LDS.  A
+// block is kStageWaves waves on kStageCols adjacent columns (lane l of every
+// wave keeps column c0 + l), so a [32768, 32768] transpose has 512 blocks and
+// needs no slabs (x read once).  The block walks its slab in rounds of
+// kStageWaves chunks of kTileRows rows, in processing order; wave w takes the
+// round's w-th chunk:
+//   - it loads its chunk's terms and adds them up in processing order into
+//     running sums pre_j (chunk-local prefixes) and the chunk total t_w;
+//   - the totals meet in LDS (two slot sets in turn: one barrier a round);
+//   - its outputs are (carry + t_0 + ... + t_{w-1}) + pre_j, the brackets
+//     summed left to right, and the next round's carry is carry + t_0 + ... +
+//     t_{kStageWaves-1}, the same sum in every wave;
+// so a column's results do not depend on timing (a different, equally fixed
+// order from scan_strided_kernel's one term after the other).  Items: (slab
+// s, block of kStageCols columns), columns fastest.  totals != null: only the
+// slab totals (the final carries) go to totals[s*n + e].
 constexpr int kTileRows = 32;
-constexpr int kTilePitch = kTileRows + 1;
+constexpr int kTilePitch = kTileRows + 1;  // odd: column-wise and row-wise LDS walks hit distinct banks
+constexpr int kStageWaves = 4;
+constexpr int kStageCols = kWave;
 
 // The rows [lo, lo + kc) of chunk c (c0 = c*kTileRows processing positions
 // into a slab [r_begin, r_end)): REV walks the slab from its end.
@@ -921,144 +1015,199 @@ __device__ __forceinline__ int64_t chunk_lo(int64_t r_begin, int64_t r_end, int6
     return REV ? r_end - c0 - kc : r_begin + c0;
 }
 
-// inner == 1: the outputs of column o are out[o*R + r], R floats apart from
-// the next column's, so lanes storing their own prefixes would each write
-// 4 bytes of a different line.  Thread t keeps column o0 + t: it loads its
+// The round's chunk totals t (this lane's column, this wave's chunk) joined:
+// returns carry + t_0 + ... + t_{w-1} and sets carry to the sum over every
+// wave.  Every thread of the block calls it once a round.
+__device__ __forceinline__ float stage_carry(float t, float& carry,
+                                             float (&slots)[2][kStageWaves][kStageCols],
+                                             int& parity, int wave, int lane) {
+    slots[parity][wave][lane] = t;
+    __syncthreads();
+    float mine = carry, next = carry;
+#pragma unroll
+    for (int w = 0; w < kStageWaves; ++w) {
+        const float v = slots[parity][w][lane];
+        if (w < wave) mine = mine + v;
+        next = next + v;
+    }
+    carry = next;
+    parity ^= 1;
+    return mine;
+}
+
+// inner == 1: column o's outputs are out[o*R + r], R floats apart from the
+// next column's, so lanes storing their own prefixes would each write 4
+// bytes of a different line.  Lane l keeps column o = o0 + l: it loads its
 // chunk's terms x[o*so + r*sr] (adjacent across lanes when so == 1), adds
-// them, and parks each prefix at tile[t][r - lo]; then the block writes the
-// tile out row by row of out (kTileRows consecutive floats of one column per
-// 32 threads).
+// them, and parks each output at tile[l][r - lo] of its wave's tile; then the
+// wave writes the tile out row by row of out (kTileRows consecutive floats of
+// one column per 32 lanes).
 template <bool REV>
-__global__ __launch_bounds__(kBlock) void scan_tile_out_kernel(
+__global__ __launch_bounds__(kStageWaves * kWave) void scan_tile_out_kernel(
     const float* x, float* out, int64_t outer, int64_t R, int64_t so, int64_t sr, int64_t S,
-    int64_t rps, const float* __restrict__ carry_in) {
-    __shared__ float tile[kBlock * kTilePitch];
-    const int t = threadIdx.x;
-    const int64_t nblk = (outer + kBlock - 1) / kBlock;
+    int64_t rps, const float* __restrict__ carry_in, float* __restrict__ totals) {
+    __shared__ float tile[kStageWaves][kStageCols * kTilePitch];
+    __shared__ float slots[2][kStageWaves][kStageCols];
+    const int wave = wave_in_block();
+    const int lane = threadIdx.x % kWave;
+    const bool scan_out = totals == nullptr;
+    float* wt = tile[wave];
+    const int64_t nblk = (outer + kStageCols - 1) / kStageCols;
     const int64_t nitems = nblk * S;
+    int parity = 0;
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
         const int64_t s = item / nblk;
-        const int64_t o0 = (item - s * nblk) * kBlock;
-        const int ncols = outer - o0 < kBlock ? int(outer - o0) : kBlock;
-        const bool live = t < ncols;
+        const int64_t o0 = (item - s * nblk) * kStageCols;
+        const int ncols = outer - o0 < kStageCols ? int(outer - o0) : kStageCols;
+        const bool live = lane < ncols;
         const int64_t r_begin = s * rps;
         const int64_t r_end = r_begin + rps < R ? r_begin + rps : R;
         const int64_t m = r_end - r_begin;  // >= 1: no slab is empty
-        const float* p = x + (live ? (o0 + t) * so : 0);
-        float acc = live && carry_in != nullptr ? carry_in[s * outer + o0 + t] : 0.f;
-        float* row = tile + t * kTilePitch;
-        for (int64_t c0 = 0; c0 < m; c0 += kTileRows) {
-            const int kc = m - c0 < kTileRows ? int(m - c0) : kTileRows;
-            const int64_t lo = chunk_lo<REV>(r_begin, r_end, c0, kc);
-            if (live) {
-                if (kc == kTileRows) {
-                    float v[kTileRows];
+        const float* p = x + (live ? (o0 + lane) * so : 0);
+        float carry = live && scan_out && carry_in != nullptr ? carry_in[s * outer + o0 + lane] : 0.f;
+        for (int64_t c0 = 0; c0 < m; c0 += kStageWaves * kTileRows) {
+            const int64_t cw = c0 + int64_t(wave) * kTileRows;  // this wave's chunk
+            const int kc = cw >= m ? 0 : (m - cw < kTileRows ? int(m - cw) : kTileRows);
+            const int64_t lo = chunk_lo<REV>(r_begin, r_end, cw, kc);
+            float v[kTileRows];
+            float t = 0.f;
+            if (live && kc == kTileRows) {
+#pragma unroll
+                for (int j = 0; j < kTileRows; ++j)
+                    v[j] = p[(lo + (REV ? kTileRows - 1 - j : j)) * sr];
+#pragma unroll
+                for (int j = 0; j < kTileRows; ++j) {
+                    t += v[j];
+                    v[j] = t;
+                }
+            } else if (live) {
+#pragma unroll
+                for (int j = 0; j < kTileRows; ++j) {
+                    if (j < kc) {
+                        t += p[(lo + (REV ? kc - 1 - j : j)) * sr];
+                        v[j] = t;
+                    }
+                }
+            }
+            const float mine = stage_carry(t, carry, slots, parity, wave, lane);
+            if (scan_out && kc > 0) {
+                if (live) {
 #pragma unroll
                     for (int j = 0; j < kTileRows; ++j)
-                        v[j] = p[(lo + (REV ? kTileRows - 1 - j : j)) * sr];
-#pragma unroll
-                    for (int j = 0; j < kTileRows; ++j) {
-                        acc += v[j];
-                        row[REV ? kTileRows - 1 - j : j] = acc;
+                        if (j < kc) wt[lane * kTilePitch + (REV ? kc - 1 - j : j)] = mine + v[j];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if (kc == kTileRows) {
+#pragma unroll 8
+                    for (int mm = 0; mm < kStageCols / 2; ++mm) {
+                        const int col = 2 * mm + lane / kTileRows;
+                        const int k = lane % kTileRows;
+                        if (col < ncols) out[(o0 + col) * R + lo + k] = wt[col * kTilePitch + k];
                     }
                 } else {
-                    for (int j = 0; j < kc; ++j) {
-                        const int k = REV ? kc - 1 - j : j;
-                        acc += p[(lo + k) * sr];
-                        row[k] = acc;
+                    for (int f = lane; f < ncols * kc; f += kWave) {
+                        const int col = f / kc;
+                        const int k = f - col * kc;
+                        out[(o0 + col) * R + lo + k] = wt[col * kTilePitch + k];
                     }
                 }
+                // the wave's tile is refilled next round only after these
+                // reads: its own later LDS writes follow them in order
+                __builtin_amdgcn_wave_barrier();
             }
-            __syncthreads();
-            if (kc == kTileRows) {
-#pragma unroll 8
-                for (int mm = 0; mm < kTileRows; ++mm) {
-                    const int col = mm * (kBlock / kTileRows) + t / kTileRows;
-                    const int k = t % kTileRows;
-                    if (col < ncols) out[(o0 + col) * R + lo + k] = tile[col * kTilePitch + k];
-                }
-            } else {
-                for (int f = t; f < ncols * kc; f += kBlock) {
-                    const int col = f / kc;
-                    const int k = f - col * kc;
-                    out[(o0 + col) * R + lo + k] = tile[col * kTilePitch + k];
-                }
-            }
-            __syncthreads();  // the tile is refilled next
         }
+        if (!scan_out && live && wave == 0) totals[s * outer + o0 + lane] = carry;
     }
 }
 
 // stride_r == 1, inner > 1 (columns e = o*inner + i at x[o*so + i*si], their
 // terms adjacent): lanes own adjacent outputs, so their stores are adjacent,
-// but their loads are si floats apart.  The block first reads a chunk of
-// kTileRows terms of its kBlock columns, 32 threads per column run
-// (128 contiguous bytes), into tile[col][r - lo]; then thread t adds column
-// e0 + t's terms from the tile and stores each prefix at
-// out[(o*R + r)*inner + i].  totals != null: only the slab totals, at
-// totals[s*n + e].
+// but their loads are si floats apart.  Each wave first reads its chunk's
+// kTileRows terms of the block's columns, 32 lanes per column run (128
+// contiguous bytes), into its tile[col][r - lo]; then lane l adds column
+// e0 + l's terms from the tile and stores each output at
+// out[(o*R + r)*inner + i].
 template <bool REV>
-__global__ __launch_bounds__(kBlock) void scan_tile_in_kernel(
+__global__ __launch_bounds__(kStageWaves * kWave) void scan_tile_in_kernel(
     const float* x, float* out, int64_t outer, int64_t R, int64_t inner, int64_t so,
     int64_t si, int64_t S, int64_t rps, const float* __restrict__ carry_in,
     float* __restrict__ totals) {
-    __shared__ float tile[kBlock * kTilePitch];
-    __shared__ int64_t base[kBlock];  // where each column's terms start in x
-    const int t = threadIdx.x;
+    __shared__ float tile[kStageWaves][kStageCols * kTilePitch];
+    __shared__ float slots[2][kStageWaves][kStageCols];
+    __shared__ int64_t base[kStageCols];  // where each column's terms start in x
+    const int wave = wave_in_block();
+    const int lane = threadIdx.x % kWave;
     const bool scan_out = totals == nullptr;
+    float* wt = tile[wave];
     const int64_t n = outer * inner;
-    const int64_t nblk = (n + kBlock - 1) / kBlock;
+    const int64_t nblk = (n + kStageCols - 1) / kStageCols;
     const int64_t nitems = nblk * S;
+    int parity = 0;
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
         const int64_t s = item / nblk;
-        const int64_t e0 = (item - s * nblk) * kBlock;
-        const int ncols = n - e0 < kBlock ? int(n - e0) : kBlock;
-        const bool live = t < ncols;
-        const int64_t e = e0 + t;
+        const int64_t e0 = (item - s * nblk) * kStageCols;
+        const int ncols = n - e0 < kStageCols ? int(n - e0) : kStageCols;
+        const bool live = lane < ncols;
+        const int64_t e = e0 + lane;
         const int64_t o = live ? e / inner : 0;
         const int64_t i = live ? e - o * inner : 0;
         const int64_t r_begin = s * rps;
         const int64_t r_end = r_begin + rps < R ? r_begin + rps : R;
         const int64_t m = r_end - r_begin;  // >= 1: no slab is empty
         float* q = out + o * R * inner + i;
-        float acc = live && scan_out && carry_in != nullptr ? carry_in[s * n + e] : 0.f;
-        const float* row = tile + t * kTilePitch;
+        float carry = live && scan_out && carry_in != nullptr ? carry_in[s * n + e] : 0.f;
         __syncthreads();  // the previous item is done with base
-        base[t] = o * so + i * si;
+        if (wave == 0) base[lane] = o * so + i * si;
         __syncthreads();
-        for (int64_t c0 = 0; c0 < m; c0 += kTileRows) {
-            const int kc = m - c0 < kTileRows ? int(m - c0) : kTileRows;
-            const int64_t lo = chunk_lo<REV>(r_begin, r_end, c0, kc);
-            if (kc == kTileRows) {  // all kTileRows loads in flight, then the tile
-                float v[kTileRows];
+        const float* wr = wt + lane * kTilePitch;
+        for (int64_t c0 = 0; c0 < m; c0 += kStageWaves * kTileRows) {
+            const int64_t cw = c0 + int64_t(wave) * kTileRows;  // this wave's chunk
+            const int kc = cw >= m ? 0 : (m - cw < kTileRows ? int(m - cw) : kTileRows);
+            const int64_t lo = chunk_lo<REV>(r_begin, r_end, cw, kc);
+            if (kc == kTileRows) {  // all loads in flight, then the tile
+                float v[kStageCols / 2];
 #pragma unroll
-                for (int mm = 0; mm < kTileRows; ++mm) {
-                    const int col = mm * (kBlock / kTileRows) + t / kTileRows;
-                    v[mm] = col < ncols ? x[base[col] + lo + t % kTileRows] : 0.f;
+                for (int mm = 0; mm < kStageCols / 2; ++mm) {
+                    const int col = 2 * mm + lane / kTileRows;
+                    v[mm] = col < ncols ? x[base[col] + lo + lane % kTileRows] : 0.f;
                 }
 #pragma unroll
-                for (int mm = 0; mm < kTileRows; ++mm) {
-                    const int col = mm * (kBlock / kTileRows) + t / kTileRows;
-                    tile[col * kTilePitch + t % kTileRows] = v[mm];
+                for (int mm = 0; mm < kStageCols / 2; ++mm) {
+                    const int col = 2 * mm + lane / kTileRows;
+                    wt[col * kTilePitch + lane % kTileRows] = v[mm];
                 }
             } else {
-                for (int f = t; f < ncols * kc; f += kBlock) {
+                for (int f = lane; f < ncols * kc; f += kWave) {
                     const int col = f / kc;
                     const int k = f - col * kc;
-                    tile[col * kTilePitch + k] = x[base[col] + lo + k];
+                    wt[col * kTilePitch + k] = x[base[col] + lo + k];
                 }
             }
-            __syncthreads();
-            if (live) {
-                for (int j = 0; j < kc; ++j) {
-                    const int k = REV ? kc - 1 - j : j;
-                    acc += row[k];
-                    if (scan_out) q[(lo + k) * inner] = acc;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float v[kTileRows];
+            float t = 0.f;
+#pragma unroll
+            for (int j = 0; j < kTileRows; ++j) {
+                if (j < kc) {
+                    t += wr[REV ? kc - 1 - j : j];
+                    v[j] = t;
                 }
             }
-            __syncthreads();  // the tile is refilled next
+            if (!live) t = 0.f;
+            const float mine = stage_carry(t, carry, slots, parity, wave, lane);
+            if (scan_out && live) {
+#pragma unroll
+                for (int j = 0; j < kTileRows; ++j)
+                    if (j < kc) q[(lo + (REV ? kc - 1 - j : j)) * inner] = mine + v[j];
+            }
+            // the wave's tile is refilled next round only after these reads
+            __builtin_amdgcn_wave_barrier();
         }
-        if (live && !scan_out) totals[s * n + e] = acc;
+        if (!scan_out && live && wave == 0) totals[s * n + e] = carry;
     }
 }
 
@@ -1142,11 +1291,37 @@ hipError_t cols_bw(const rd_plan& p, const float* x, float* out, const Strides& 
                   nx);
 }
 
+template <bool REV, int RW, bool NT>
+hipError_t rounds_go(const rd_plan& p, const float* x, float* out, const Strides& v,
+                     int64_t ntiles, hipStream_t s) {
+    const uint32_t nx = uint32_t(p.nxcd);
+    if (p.unroll == 8)
+        return launch(scan_cols_rounds_kernel<REV, 8, RW, NT>, p.blocks, RW * kWave, s, x, out,
+                      v.outer, v.R, v.inner, v.so, v.sr, ntiles, nx);
+    if (p.unroll == 4)
+        return launch(scan_cols_rounds_kernel<REV, 4, RW, NT>, p.blocks, RW * kWave, s, x, out,
+                      v.outer, v.R, v.inner, v.so, v.sr, ntiles, nx);
+    return hipErrorInvalidValue;
+}
+
 template <bool REV, int V, bool NT>
 hipError_t cols_go(const rd_plan& p, const float* x, float* out, const Strides& v,
                    const float* carry_in, float* totals, hipStream_t s) {
     const int64_t lane_cols = v.inner >= 4 ? (v.inner + 3) / 4 : 1;
     const int64_t ntiles = (lane_cols + kWave - 1) / kWave;
+    if (p.row_waves > 1) {  // waves of a block taking turns in R: one pass only
+        if constexpr (V == 4) {
+            if (p.split != 1 || p.col_waves != 1 || carry_in || totals) return hipErrorInvalidValue;
+            switch (p.row_waves) {
+                case 2: return rounds_go<REV, 2, NT>(p, x, out, v, ntiles, s);
+                case 4: return rounds_go<REV, 4, NT>(p, x, out, v, ntiles, s);
+                case 8: return rounds_go<REV, 8, NT>(p, x, out, v, ntiles, s);
+                case 16: return rounds_go<REV, 16, NT>(p, x, out, v, ntiles, s);
+                default: return hipErrorInvalidValue;
+            }
+        }
+        return hipErrorInvalidValue;
+    }
     if (p.col_waves == 16)
         return cols_bw<REV, V, 16, NT>(p, x, out, v, ntiles, carry_in, totals, s);
     if (p.col_waves == 8)
@@ -1229,21 +1404,23 @@ hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, floa
 hipError_t launch_scan_strided(const rd_plan& p, bool reverse, const float* x, float* out,
                                const Strides& v, const float* carry_in, float* totals,
                                hipStream_t s) {
-    const int64_t blocks = p.blocks;  // a lane per (slab, column) in every variant
-    if (v.inner == 1 && totals == nullptr) {  // stage the outputs
+    const int64_t blocks = p.blocks;
+    if (v.inner == 1) {  // stage the outputs: a block per (slab, kStageCols columns)
         if (reverse)
-            return launch(scan_tile_out_kernel<true>, blocks, kBlock, s, x, out, v.outer, v.R,
-                          v.so, v.sr, p.split, p.rows_per_split, carry_in);
-        return launch(scan_tile_out_kernel<false>, blocks, kBlock, s, x, out, v.outer, v.R, v.so,
-                      v.sr, p.split, p.rows_per_split, carry_in);
+            return launch(scan_tile_out_kernel<true>, blocks, kStageWaves * kWave, s, x, out,
+                          v.outer, v.R, v.so, v.sr, p.split, p.rows_per_split, carry_in, totals);
+        return launch(scan_tile_out_kernel<false>, blocks, kStageWaves * kWave, s, x, out, v.outer,
+                      v.R, v.so, v.sr, p.split, p.rows_per_split, carry_in, totals);
     }
-    if (v.inner > 1 && v.sr == 1) {  // stage the inputs
+    if (v.sr == 1) {  // stage the inputs: a block per (slab, kStageCols columns)
         if (reverse)
-            return launch(scan_tile_in_kernel<true>, blocks, kBlock, s, x, out, v.outer, v.R,
-                          v.inner, v.so, v.si, p.split, p.rows_per_split, carry_in, totals);
-        return launch(scan_tile_in_kernel<false>, blocks, kBlock, s, x, out, v.outer, v.R,
-                      v.inner, v.so, v.si, p.split, p.rows_per_split, carry_in, totals);
+            return launch(scan_tile_in_kernel<true>, blocks, kStageWaves * kWave, s, x, out,
+                          v.outer, v.R, v.inner, v.so, v.si, p.split, p.rows_per_split, carry_in,
+                          totals);
+        return launch(scan_tile_in_kernel<false>, blocks, kStageWaves * kWave, s, x, out, v.outer,
+                      v.R, v.inner, v.so, v.si, p.split, p.rows_per_split, carry_in, totals);
     }
+    // a lane per (slab, column)
     if (reverse)
         return launch(scan_strided_kernel<true>, blocks, kBlock, s, x, out, v.outer, v.R,
                       v.inner, v.so, v.sr, v.si, p.split, p.rows_per_split, carry_in, totals);

@@ -102,6 +102,47 @@ def test_unroll_variants(unroll, split, bw):
             _sweep(rows, [0, 3], 860 + unroll + split, "scan rows u%d s%d" % (unroll, split))
 
 
+ROUNDS = [(rw, u) for rw in (2, 4, 8, 16) for u in (4, 8)]
+
+
+@pytest.mark.parametrize("rw,unroll", ROUNDS, ids=["rw%d_u%d" % t for t in ROUNDS])
+def test_columns_by_row_rounds(rw, unroll):
+    """Column scans whose block's rw waves take turns on one tile's groups
+    of `unroll` rows: R around the round (rw * unroll rows) and group
+    boundaries, ragged and partial tiles (inner % 4 != 0, lanes past the
+    row's end), several tiles and outer indices."""
+    per = rw * unroll
+    shapes = [(2, r, i) for r in (1, unroll - 1, unroll, unroll + 1, per - 1, per, per + 1,
+                                  2 * per + 3, 3 * per)
+              for i in (4, 5, 300)]
+    shapes += [(3, 5 * per + 7, 1023), (1, 4 * per, 4095), (2, per + 1, 1025)]
+    with rd.tuning(row_waves=rw, unroll=unroll, path=7):
+        for o, r, i in shapes[:3]:
+            p = rd.rd_plan_cumsum(256, o, r, i)
+            assert (p.row_waves, p.col_waves, p.split) == (rw, 1, 1), p.as_dict()
+        _sweep(shapes, [0, 1, 3], 870 + rw + unroll, "scan rounds rw%d u%d" % (rw, unroll))
+
+
+def test_columns_by_row_rounds_default_plans():
+    """Shapes whose default plan takes row rounds (between half and twice as
+    many tiles as CUs), random data: within tolerance of the oracle, and
+    bitwise equal from call to call."""
+    t = H.torch()
+    for o, r, i in ((1, 3000, 32768), (3, 1500, 16384), (64, 512, 1024)):
+        p = rd.rd_plan_cumsum(256, o, r, i)
+        assert p.row_waves > 1 and p.split == 1, p.as_dict()
+        a = workloads.random(o * r * i, 890 + o, "normal")
+        x = H.upload(a, 1)
+        for rev in (True, False):
+            H.say("scan rounds default plan %s rev=%d" % ((o, r, i), rev))
+            got = rd.rd_cumsum_dim(x, o, r, i, rev)
+            again = rd.rd_cumsum_dim(x, o, r, i, rev)
+            assert t.equal(got.view(t.int32), again.view(t.int32))
+            S, A = oracle.cumsum_dim(a, o, r, i, rev)
+            H.assert_within_tolerance(got.cpu().numpy().reshape(-1), S.reshape(-1),
+                                      A.reshape(-1), "rounds %s rev=%d" % ((o, r, i), rev))
+
+
 BLOCK_ROWS = [(g, u, s) for g in (256, 512, 1024) for (u, s) in ((4, 1), (4, 3), (8, 1), (8, 7))]
 
 

@@ -265,16 +265,27 @@ def _scan_invariants(p, outer, R, inner, cu=CU):
         ws = 2 * p.split * outer * inner * 4 if p.split > 1 else 0
     else:
         tiles = -(-(-(-inner // 4) if inner >= 4 else 1) // 64)
-        bw = p.col_waves
-        assert bw in (1, 2, 4, 8, 16) and p.block_threads == 64 * bw
+        bw, rw = p.col_waves, p.row_waves
+        waves = tiles * outer
+        assert bw in (1, 2, 4, 8, 16) and p.block_threads == 64 * bw * rw
         assert tiles >= bw
-        # slabs only when there are fewer waves (tiles x outer) than CUs;
-        # then the widest block that still gives every CU one
-        assert (p.split > 1) == (tiles * outer < cu and R >= 128)
-        blocks = -(-tiles // bw) * p.split * outer
-        assert blocks >= cu or bw == 1
-        assert bw == 16 or -(-tiles // (2 * bw)) * p.split * outer < cu or tiles < 2 * bw
-        assert p.blocks == min(blocks, 1 << 20)
+        if 2 * waves >= cu and waves < 2 * cu and inner >= 4:
+            # between half and twice as many tiles as CUs: rw waves of a
+            # block take turns on one tile's row groups, one pass, the
+            # fewest (at most 8) that make 4 waves per CU
+            assert p.split == 1 and bw == 1 and rw in (1, 2, 4, 8)
+            assert waves * rw >= 4 * cu or rw == 8
+            assert rw == 1 or waves * (rw // 2) < 4 * cu
+            assert p.unroll in (4, 8) and p.blocks == min(waves, 1 << 20)
+        else:
+            # slabs only when fewer tiles than half the CUs; then the widest
+            # block that still gives every CU one
+            assert rw == 1
+            assert (p.split > 1) == (waves < cu and R >= 128)
+            blocks = -(-tiles // bw) * p.split * outer
+            assert blocks >= cu or bw == 1
+            assert bw == 16 or -(-tiles // (2 * bw)) * p.split * outer < cu or tiles < 2 * bw
+            assert p.blocks == min(blocks, 1 << 20)
         ws = 2 * p.split * outer * inner * 4 if p.split > 1 else 0
     assert p.workspace_bytes == ws
     assert p.passes == (3 if p.split > 1 else 1)
@@ -400,11 +411,16 @@ def test_cumsum_strided_view_plans():
     """The unit stride decides: inner axis -> column scans (any outer and R
     strides), R with inner == 1 -> row scan (any row stride), none -> a lane
     per output column, split into slabs of >= 32 rows when there are few."""
-    # the [4096, 4096] array transposed: [4096, 4096], strides (1, 4096)
+    # the [4096, 4096] array transposed: [4096, 4096], strides (1, 4096):
+    # 64 blocks of 64 columns, cut into 8 slabs of 512 rows
     p = rd.rd_plan_cumsum_strided(CU, 4096, 4096, 1, 1, 4096, 1).as_dict()
-    assert p["path"] == "scan_strided" and p["split"] == 64 and p["rows_per_split"] == 64
-    assert p["workspace_bytes"] == 2 * 64 * 4096 * 4 and p["passes"] == 3
-    assert p["nontemporal"] == 0
+    assert p["path"] == "scan_strided" and p["split"] == 8 and p["rows_per_split"] == 512
+    assert p["workspace_bytes"] == 2 * 8 * 4096 * 4 and p["passes"] == 3
+    assert p["nontemporal"] == 0 and p["blocks"] == 8 * 64
+    # [32768, 32768] transposed: 512 blocks, one pass
+    for v in ((32768, 32768, 1, 1, 32768, 1), (1, 32768, 32768, 0, 1, 32768)):
+        p = rd.rd_plan_cumsum_strided(CU, *v).as_dict()
+        assert p["path"] == "scan_strided" and p["split"] == 1 and p["blocks"] == 512
     # columns 0..1023 of [64, 512, 4096]: the column scan with sr = 4096
     p = rd.rd_plan_cumsum_strided(CU, 64, 512, 1024, 512 * 4096, 4096, 1).as_dict()
     assert p["path"] == "scan_cols"
@@ -412,13 +428,18 @@ def test_cumsum_strided_view_plans():
     # every other row of a [8192, 8192] array: rows with so = 2*8192
     p = rd.rd_plan_cumsum_strided(CU, 4096, 8192, 1, 2 * 8192, 1, 1).as_dict()
     assert p == rd.rd_plan_cumsum(CU, 4096, 8192, 1).as_dict()
-    # the inner axis strided: a lane per column, enough columns for no slabs
+    # the inner axis strided, terms adjacent along R: inputs staged, enough
+    # columns for no slabs
     p = rd.rd_plan_cumsum_strided(CU, 512, 100, 1024, 1024 * 100, 1, 100).as_dict()
     assert p["path"] == "scan_strided" and p["split"] == 1 and p["passes"] == 1
-    assert p["blocks"] == 512 * 1024 // 256 and p["workspace_bytes"] == 0
-    # one strided column: as many slabs as keep 32 rows each
+    assert p["blocks"] == 512 * 1024 // 64 and p["workspace_bytes"] == 0
+    # one strided column (outputs staged): as many slabs as keep 128 rows each
     p = rd.rd_plan_cumsum_strided(CU, 1, 100_000, 1, 0, 7, 1).as_dict()
-    assert p["path"] == "scan_strided" and p["split"] == 3125 and p["rows_per_split"] == 32
+    assert p["path"] == "scan_strided" and p["rows_per_split"] == 196 and p["split"] == 511
+    # neither side contiguous: a lane per column, slabs of at least 32 rows
+    p = rd.rd_plan_cumsum_strided(CU, 100, 1000, 3, 7000, 7, 2).as_dict()
+    assert p["path"] == "scan_strided" and p["rows_per_split"] >= 32 and p["split"] > 1
+    assert p["blocks"] == p["split"] * -(-300 // 256)
     # length-1 axes: their strides are ignored
     assert rd.rd_plan_cumsum_strided(CU, 1, 9, 4, 12345, 4, 1).as_dict()["path"] == \
         "scan_cols_small"
@@ -435,8 +456,13 @@ def test_cumsum_strided_view_plans():
         unit_cols = inner > 1 and si == 1
         if not (unit_rows or unit_cols):
             assert d["path"] == "scan_strided"
-            assert p.blocks == min(p.split * -(-outer * inner // 256), 1 << 20)
-            assert p.split == 1 or p.rows_per_split >= 32
+            n = outer * inner
+            staged = inner == 1 or sr == 1 or R == 1
+            cols = 64 if staged else 256
+            assert p.blocks == min(p.split * -(-n // cols), 1 << 20)
+            assert p.split == 1 or p.rows_per_split >= (128 if staged else 32)
+            if staged and -(-n // 64) >= 2 * cu:
+                assert p.split == 1   # enough blocks: one pass, x read once
             assert p.workspace_bytes == (2 * p.split * outer * inner * 4 if p.split > 1 else 0)
         else:
             assert d == rd.rd_plan_cumsum(cu, outer, R, inner).as_dict()
