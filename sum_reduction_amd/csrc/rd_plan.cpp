@@ -132,12 +132,13 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
     p->workspace_bytes = P > 1 ? segs * result_bytes(op) : 0;
     p->combine = RD_COMBINE_NONE;
     if (P > 1) {
-        // The second kernel is the default: measured on MI355X it is faster
-        // than the fused last-workgroup combine at every size (1e6: 12.8 vs
-        // 13.1 us, 1e7: 17.6 vs 22.3, 1e8: 71.8 vs 76.8, 1e9: 573 vs 581),
-        // whose cross-XCD publication (one L2 write-back per workgroup, an L2
-        // invalidate and a memory round trip in the last one) costs more than
-        // a queued launch.
+        // The second kernel is the default: the fused last-workgroup
+        // combine needs every workgroup to publish its results with a
+        // device-scope release, which on MI355X (an L2 per XCD) writes back
+        // the L2 and costs about 47 ns per workgroup, serialized -- measured
+        // with 128 KB pieces: 1e8 floats 59.7 us with no ticket, 67.4 with a
+        // relaxed one, 200 with a release; 1e9 566 / 663 / 2037 us -- where
+        // a queued second launch costs a few microseconds.
         const int32_t c = (t && t->combine) ? t->combine : RD_COMBINE_PASS;
         if (c != RD_COMBINE_PASS && c != RD_COMBINE_LAST_BLOCK) return RD_ERR_INVALID_ARG;
         p->combine = c;

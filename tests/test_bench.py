@@ -63,4 +63,8 @@ def test_json_line():
     assert "traffic" in rf and rf["workload"] == "uniform_1e8"
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    # each leg reported with the threads it ran on: both are full reduces,
+    # the oracle's sequential loop
+    assert set(cb["legs"]) == {"harmonic_1e6", "uniform_1e8"}
+    assert all(leg["threads"] == 1 and leg["GBps"] > 0 for leg in cb["legs"].values())
     assert d["parity"]["ok"] is True

@@ -578,3 +578,48 @@ def test_view3_collapses_torch_layouts():
             assert got is None, (t.shape, t.stride(), d)
         else:
             assert got == want, (t.shape, t.stride(), d, got)
+
+
+def _workspace_extent(outer, R, inner, p):
+    """Host-side index arithmetic of a split reduce: the largest float index
+    the first kernel writes and the second one reads in the workspace, as
+    the kernels compute them (rows: piece results at row * P + piece;
+    columns: slab results at (s * outer + o) * inner + column), against the
+    workspace's size in floats."""
+    d = p.as_dict()
+    if d["path"] == "rows":
+        written = outer * p.split - 1                  # dst[seg], seg < outer * P
+        read = (outer - 1) * p.split + p.split - 1      # combine_row: part[o * P + k], k < P
+    else:
+        # pass 1: the last slab (its first row r0 = s * rps < R), last outer
+        # index, last column; pass 2 (slab_combine): slab[s * n + e]
+        s_last = p.split - 1
+        assert s_last * p.rows_per_split < R
+        written = (s_last * outer + outer - 1) * inner + inner - 1
+        read = s_last * (outer * inner) + outer * inner - 1
+    return written, read, p.workspace_bytes // 4
+
+
+def test_split_workspace_indices_stay_inside():
+    """Every index the two kernels of a split plan touch lies inside its
+    workspace -- among them the [3, 50000, 70] axis reduce (341 slabs of
+    147 rows, 286,440 bytes: highest index 71,609 of 71,610 floats), whose
+    graph-captured workspace once faulted on replay; the same arithmetic
+    holds for every default split plan of a sweep of shapes."""
+    p = rd.rd_plan_dim(CU, 3, 50_000, 70)
+    assert p.as_dict()["path"] == "cols_small"
+    assert (p.split, p.rows_per_split, p.workspace_bytes) == (341, 147, 286_440)
+    assert _workspace_extent(3, 50_000, 70, p) == (71_609, 71_609, 71_610)
+    rng = np.random.default_rng(77)
+    checked = 0
+    for _ in range(4000):
+        outer, R, inner = (int(v) for v in np.exp(rng.uniform(0, 11, 3)).astype(np.int64))
+        p = rd.rd_plan_dim(CU, outer, R, inner)
+        if p.split == 1 or p.as_dict()["path"] not in ("rows", "cols", "cols_small"):
+            continue
+        if p.as_dict()["path"] == "rows" and inner != 1:
+            continue
+        written, read, floats = _workspace_extent(outer, R, inner, p)
+        assert written < floats and read < floats, (outer, R, inner, p.as_dict())
+        checked += 1
+    assert checked > 100
