@@ -44,7 +44,8 @@
  *   a second kernel in fixed order.  With the RD_COMBINE_LAST_BLOCK option the last
  *   workgroup of the first kernel sums them instead; the integer ticket
  *   counter that elects it belongs to the stream (one per stream and device,
- *   reset by the kernel itself), so calls on one stream, which never overlap,
+ *   zeroed in stream order before each such launch and reset by the kernel
+ *   itself), so calls on one stream, which never overlap,
  *   never share it with calls on another (calls on the per-thread default
  *   stream, whose handle stands for a different stream in each thread, take
  *   the second kernel instead).  The pool and the counters are created by

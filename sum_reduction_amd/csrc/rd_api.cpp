@@ -23,9 +23,10 @@ thread_local int t_last_hip = 0;
 // combine.  Calls whose plan needs no workspace, and rd_sum_dim_noalloc,
 // never allocate.
 // Ticket counters for the fused (last-workgroup) combine: one per stream that
-// has made such a call on the device, zeroed once when they are created and
-// left at zero by every kernel that uses one.  Calls on one stream never
-// overlap, so a stream's counter is always 0 when its next kernel starts.
+// has made such a call on the device, zeroed when they are created, before
+// every fused launch (in stream order) and by every kernel that uses one.
+// Calls on one stream never overlap, so a stream's counter is 0 when its next
+// kernel starts.
 constexpr int kTicketSlots = 4096;
 struct Device {
     std::once_flag once;
@@ -243,7 +244,13 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
                 uint32_t* ticket = p.combine == RD_COMBINE_LAST_BLOCK && pooled
                                        ? stream_ticket(dev, s)
                                        : nullptr;
-                e = rd::launch_rows(op, p, x, v, part, ticket, out, s);
+                // the election needs the counter at 0 when the kernel starts:
+                // the kernel leaves it there, and it is zeroed in stream order
+                // before every fused launch as well, so that no earlier launch
+                // (one that did not run to its end) can make a later one elect
+                // the wrong workgroup
+                if (ticket) e = hipMemsetAsync(ticket, 0, sizeof(uint32_t), s);
+                if (e == hipSuccess) e = rd::launch_rows(op, p, x, v, part, ticket, out, s);
                 if (e == hipSuccess && !ticket)
                     e = rd::launch_rows_combine(op, part, nout, p.split, out, s);
             }
