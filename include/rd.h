@@ -357,11 +357,15 @@ typedef enum rd_order {
 typedef enum rd_combine {
     RD_COMBINE_NONE = 0,       /* one pass, no partial sums */
     RD_COMBINE_PASS = 1,       /* a second kernel sums them in fixed order */
-    RD_COMBINE_LAST_BLOCK = 2  /* the last workgroup of the first kernel sums
+    RD_COMBINE_LAST_BLOCK = 2, /* the last workgroup of the first kernel sums
                                   them in the same order (one launch; an
                                   option: slower than RD_COMBINE_PASS on
                                   MI355X); calls on a capturing stream use
                                   RD_COMBINE_PASS, with identical results */
+    RD_COMBINE_LOOKBACK = 3    /* row scans: one launch, a workgroup per row
+                                  piece, each piece's carry summed in a fixed
+                                  order from totals that earlier pieces
+                                  publish (see rd_plan_cumsum) */
 } rd_combine;
 
 typedef struct rd_plan {

@@ -55,7 +55,7 @@ PATH_NAMES = {0: "none", 1: "zero", 2: "rows", 3: "rows_short", 4: "cols",
               5: "cols_small", 6: "scan_rows", 7: "scan_cols", 8: "scan_cols_small",
               9: "strided", 10: "scan_strided"}
 ORDER_NAMES = {0: "-", 1: "interleaved", 2: "blocked"}
-COMBINE_NAMES = {0: "none", 1: "pass", 2: "last_block"}
+COMBINE_NAMES = {0: "none", 1: "pass", 2: "last_block", 3: "lookback"}
 
 
 class RdError(RuntimeError):

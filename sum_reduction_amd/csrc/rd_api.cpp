@@ -185,7 +185,9 @@ rd_status device_memory(Device& d) {
 // Failure injection for tests of the error paths, read from the environment
 // once per process (at the first call that looks): RD_TEST_FAIL_ALLOC makes
 // the workspace allocation fail, RD_TEST_FAIL_LAUNCH makes the first launch
-// fail; neither enqueues any work.
+// fail; neither enqueues any work.  RD_TEST_SPIN_LIMIT=n caps the polls of a
+// look-back wait at n (the kernel still runs to its end; a piece whose wait
+// gives up writes NaN).
 bool env_on(const char* name) {
     const char* v = getenv(name);
     return v && v[0] && v[0] != '0';
@@ -193,10 +195,19 @@ bool env_on(const char* name) {
 
 struct Injected {
     bool alloc, launch;
+    uint32_t spin_limit;  // polls of a look-back wait before it gives up
 };
 
+uint32_t env_spin_limit() {
+    const char* v = getenv("RD_TEST_SPIN_LIMIT");
+    if (!v || !*v) return rd::kLookSpinLimit;
+    const unsigned long n = strtoul(v, nullptr, 10);
+    return n < rd::kLookSpinLimit ? uint32_t(n) : rd::kLookSpinLimit;
+}
+
 const Injected& injected() {
-    static const Injected f{env_on("RD_TEST_FAIL_ALLOC"), env_on("RD_TEST_FAIL_LAUNCH")};
+    static const Injected f{env_on("RD_TEST_FAIL_ALLOC"), env_on("RD_TEST_FAIL_LAUNCH"),
+                            env_spin_limit()};
     return f;
 }
 
@@ -338,7 +349,9 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
     rd_plan pt = p;
     if (uint64_t(nrow * v.R) * sizeof(float) <= rd::kScanCachedTotalsBytes) pt.nontemporal = 0;
     hipError_t e = hipSuccess;
-    if (p.path == RD_PATH_SCAN_ROWS) {
+    if (p.path == RD_PATH_SCAN_ROWS && p.combine == RD_COMBINE_LOOKBACK) {
+        e = rd::launch_scan_rows_lookback(p, rev, x, out, v, ws, injected().spin_limit, stream);
+    } else if (p.path == RD_PATH_SCAN_ROWS) {
         if (p.split == 1) {
             e = rd::launch_scan_rows(p, rev, x, out, v, nullptr, nullptr, stream);
         } else {

@@ -100,6 +100,21 @@ hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, floa
                             hipStream_t s);
 hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows, int64_t P,
                                hipStream_t s);
+// Rows in one pass by a fixed-order look-back (p.combine RD_COMBINE_LOOKBACK):
+// p.split pieces of one block chunk per row, a workgroup each; ws holds
+// p.workspace_bytes, which the call zeroes (in stream order) and the kernel
+// uses for its ticket and the published totals.  A wait of the kernel ends
+// after spin_limit polls (the piece's outputs are then NaN).
+constexpr int64_t kLookGroup = 64;          // chunk totals per group total
+constexpr int64_t kLookTicketBytes = 256;   // the ticket, padded
+constexpr uint32_t kLookSpinLimit = 1u << 18;
+inline int64_t lookback_groups(int64_t P) { return (P + kLookGroup - 1) / kLookGroup; }
+inline int64_t lookback_workspace_bytes(int64_t outer, int64_t P) {
+    return kLookTicketBytes + 8 * outer * (P + lookback_groups(P));
+}
+hipError_t launch_scan_rows_lookback(const rd_plan& p, bool reverse, const float* x, float* out,
+                                     const Strides& v, void* ws, uint32_t spin_limit,
+                                     hipStream_t s);
 // Columns (inner >= 2, si == 1): item = (64 lane-columns, slab of R, outer index).
 hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, float* out,
                             const Strides& v, const float* carry_in, float* totals,
@@ -145,7 +160,30 @@ constexpr int64_t kScanTile = 4096;
 constexpr int kScanRowsChunkSlices = 8;
 constexpr int64_t kScanRowsBlockMinR = 16384;
 constexpr int64_t kScanRowsWideMinR = 65536;
-constexpr int64_t kScanRowWavesMin = 4;   // rows per CU below which rows are cut
+// Few rows.  Rows are cut into pieces (piece totals, their scan, the scan
+// from the carries: three launches, x read twice) only when there are fewer
+// than a third as many rows as CUs and the rows hold at least
+// kScanRowsCutMinR positions; otherwise every row is scanned in one pass,
+// and with fewer than kScanRowWavesMin rows per CU a row of more than one
+// tile takes a workgroup of 4 waves or more.  Measured on MI355X (one box,
+// interleaved), us, pieces / one pass: [64, 65536] 18.9 / 14.4, [256, 65536]
+// 39.7 / 24.7, [512, 16384] 21.8 / 14.6, [128, 131072] 39.8 / 29.0,
+// [100, 1048576] 235.8 / 206.3; the other way round [64, 131072] 21.6 /
+// 27.8, [64, 262144] 39.7 / 46.5, [64, 1048576] 131.9 / 179.8 (one
+// workgroup streams a row at ~60 GB/s).  Rows of 4096 < R <= 16384 among
+// few: a wave 7.5 -> 4 waves 6.2 us ([64, 8192]), 15.8 -> 9.2 ([256, 16384]).
+// Longer rows among few -- at least kScanRowsLookMinR positions and
+// kScanRowsLookMinN elements in all -- take the one-pass look-back instead
+// (launch_scan_rows_lookback), pieces of 32768 positions: us, before -> after,
+// [1, 2^28] 590.3 -> 397.5, [2, 2^26] 299.4 -> 206.5, [4, 2.5e7] 220.7 ->
+// 161.9, [64, 2^20] 133.8 -> 110.6, [85, 2^20] 198.0 -> 142.4, [256, 2^20]
+// 398.5 -> 381.0, [16, 2^20] 40.4 -> 39.6; shorter rows or smaller arrays
+// lose the zeroing of its workspace (one more dispatch): [1, 2^22] 19.4 ->
+// 21.1, [64, 2^17] 21.8 -> 25.3, [256, 2^18] 95.9 -> 104.7.
+constexpr int64_t kScanRowWavesMin = 4;
+constexpr int64_t kScanRowsCutMinR = 131072;
+constexpr int64_t kScanRowsLookMinR = int64_t(1) << 20;
+constexpr int64_t kScanRowsLookMinN = int64_t(1) << 24;
 constexpr int64_t kScanRowWavesSplit = 16;  // pieces per CU once they are cut
 constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan,
 // 16 for slabs of kScanColsDeepRows rows or more (same box, interleaved:

@@ -488,11 +488,42 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         return RD_ERR_INVALID_ARG;
     if (forced == RD_PATH_SCAN_COLS_SMALL && inner > 2 * kSmallInner) return RD_ERR_INVALID_ARG;
     if (inner == 1) {
-        // a wave or a workgroup per row piece; pieces only when there are
-        // too few rows to keep kScanRowWavesMin waves per CU busy (then:
-        // piece totals, their scan, the scan from the carries -- x is read
-        // twice)
+        // a wave or a workgroup per row piece; pieces only for few long rows
+        // (then: piece totals, their scan, the scan from the carries -- x is
+        // read twice)
         p->path = RD_PATH_SCAN_ROWS;
+        const int32_t comb = t ? t->combine : 0;
+        if (comb != 0 && comb != RD_COMBINE_PASS && comb != RD_COMBINE_LOOKBACK)
+            return RD_ERR_INVALID_ARG;
+        // Long rows among few (at least kScanRowsLookMinR positions, fewer
+        // than kScanRowWavesMin rows per CU, kScanRowsLookMinN elements in
+        // all) take the look-back: one launch, x read once.
+        const int64_t look_len = int64_t(16) * kWave * 4 * kScanRowsChunkSlices;
+        const bool tuned = t && (t->split || t->order || t->group || t->unroll);
+        const bool look = comb == RD_COMBINE_LOOKBACK ||
+                          (comb == 0 && !tuned && outer < cu * kScanRowWavesMin &&
+                           R >= kScanRowsLookMinR && outer * R >= kScanRowsLookMinN &&
+                           ceil_div(R, look_len) <= kMaxBlocks / outer);
+        if (look) {
+            // one launch, a workgroup of 8 or 16 waves per piece of one block
+            // chunk (8 slices a wave), the carries by look-back
+            if (t && (t->split || t->order || (t->unroll && t->unroll != 8)))
+                return RD_ERR_INVALID_ARG;
+            const int32_t group = (t && t->group) ? t->group : 16 * kWave;
+            if (group != 8 * kWave && group != 16 * kWave) return RD_ERR_INVALID_ARG;
+            const int64_t L = int64_t(group / kWave) * kWave * 4 * kScanRowsChunkSlices;
+            const int64_t P = ceil_div(R, L);
+            if (P > kMaxBlocks / outer) return RD_ERR_INVALID_ARG;
+            p->unroll = kScanRowsChunkSlices;
+            p->group = group;
+            p->block_threads = group;
+            p->split = P;
+            p->rows_per_split = L;
+            p->blocks = outer * P;
+            p->combine = RD_COMBINE_LOOKBACK;
+            p->workspace_bytes = lookback_workspace_bytes(outer, P);
+            return RD_OK;
+        }
         p->unroll = (t && t->unroll) ? t->unroll : kScanRowsChunkSlices;
         if (p->unroll != 4 && p->unroll != 8) return RD_ERR_INVALID_ARG;
         if (t && t->group && t->group != kWave && t->group != kBlock &&
@@ -502,7 +533,7 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         int64_t P = 1;
         if (t && t->split) {
             P = t->split;
-        } else if (outer < cu * kScanRowWavesMin) {
+        } else if (3 * outer < cu && R >= kScanRowsCutMinR) {
             P = ceil_div(cu * kScanRowWavesSplit, outer);
         }
         if (P < 1) return RD_ERR_INVALID_ARG;
@@ -514,10 +545,13 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         // long uncut rows: a workgroup per row (adjacent waves on adjacent
         // stretches of it) -- 8 waves, 16 for rows of two of their chunks or
         // more; with 4-slice chunks (kernels built for 8 waves a SIMD, where
-        // wider workgroups spill) 4 waves --; else a wave per item
+        // wider workgroups spill) 4 waves --; uncut rows of more than a tile
+        // among few rows: 4 waves; else a wave per item
         int32_t group = kWave;
         if (P == 1 && R > kScanRowsBlockMinR)
             group = p->unroll == 4 ? kBlock : R >= kScanRowsWideMinR ? 16 * kWave : 8 * kWave;
+        else if (P == 1 && R > kScanTile && outer < cu * kScanRowWavesMin)
+            group = kBlock;
         p->group = (t && t->group) ? t->group : group;
         // interleaved: persistent workgroups, each streaming the chunks of
         // rows b, b + blocks, ... (whole rows, a workgroup per row only)

@@ -434,6 +434,130 @@ scan_rows_block_kernel(const float* x, float* out, int64_t outer, int64_t R, int
     }
 }
 
+// Few long rows in one pass: a decoupled look-back in a fixed order.  Row o
+// is cut into P pieces of one block chunk each (L = NW*256*K processing
+// positions, the row's last piece partial), a workgroup per piece.  A
+// workgroup takes piece t = o*P + j by a ticket drawn at its start, so every
+// piece it waits for belongs to a workgroup that started before it (and is
+// resident or done), and none of those waits for a later piece: no wait can
+// close a cycle.  The workgroup loads its chunk, adds it up in the order of
+// block_chunk, publishes the chunk total a_j, then forms its carry from what
+// earlier pieces of the row published.  Pieces form groups of kLookGroup;
+// the last piece of a group that has a successor also publishes the group
+// total T_g = (a_gG + ... + a_{j-1}) + a_j, and piece j of group g takes
+//   carry = (T_0 + ... + T_{g-1}) + (a_gG + ... + a_{j-1}),
+// each run of terms summed by a wave scan in index order (T's 64 at a time,
+// the batches added in order).  The terms and their order depend on the
+// plan and the data alone, never on which piece finished first, so every
+// run gives the same bits.  A published value is one 64-bit word, 1 in the
+// high half and the float's bits in the low half, stored and loaded by
+// relaxed device-scope atomics: the value travels with its flag, so no fence
+// is needed.  The workspace (ticket, chunk totals, group totals) is zeroed
+// before every launch.  A wait gives up after spin_limit polls and returns
+// NaN, so a piece that could not get its carry writes NaN, never a wrong
+// finite sum.  x and out may be the same array (each element is loaded and
+// stored by the same lane).
+__device__ __forceinline__ void look_publish(uint64_t* slot, float v) {
+    const uint64_t w = (uint64_t(1) << 32) | uint64_t(__builtin_bit_cast(uint32_t, v));
+    __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float look_await(uint64_t* slot, uint32_t spin_limit) {
+    for (uint32_t it = 0;; ++it) {
+        const uint64_t w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (w >> 32) return __builtin_bit_cast(float, uint32_t(w));
+        if (it >= spin_limit) return __builtin_nanf("");
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+template <bool REV, int NW, int K, bool NT>
+__global__ __launch_bounds__(NW * kWave, scan_rows_waves_per_simd<K>()) void
+scan_rows_lookback_kernel(const float* x, float* out, int64_t outer, int64_t R, int64_t so,
+                          int64_t P, int64_t NG, uint32_t* __restrict__ ticket, uint64_t* agg,
+                          uint64_t* gsum, uint32_t spin_limit) {
+    constexpr int64_t kSpan = 256 * K;      // a wave's positions
+    constexpr int64_t kChunk = NW * kSpan;  // the piece's positions
+    __shared__ float slots[NW];
+    __shared__ uint32_t s_item;
+    __shared__ float s_carry;
+    const int wave = wave_in_block();
+    const int lane = threadIdx.x % kWave;
+    if (threadIdx.x == 0)
+        s_item = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t item = s_item;
+    if (item >= outer * P) return;  // only if the ticket was not zeroed: never wait on it
+    const int64_t o = item / P;
+    const int64_t j = item - o * P;
+    const float* row = x + o * so;
+    float* orow = out + o * R;
+    const int64_t q_begin = j * kChunk;
+    const int64_t q_end = q_begin + kChunk < R ? q_begin + kChunk : R;
+    const bool part = q_end - q_begin < kChunk;
+    const int64_t lq = 4 * lane;
+    const int64_t qw = q_begin + wave * kSpan;  // this wave's window
+    v4f v[K];
+    if (part) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = load_q4_part<REV, NT>(row, R, qw + 256 * k + lq, q_end);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = load_q4<REV, NT>(row, R, qw + 256 * k + lq);
+    }
+    float e[K], tot[K];
+    v4f sv[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        sv[k].x = v[k].x;
+        sv[k].y = sv[k].x + v[k].y;
+        sv[k].z = sv[k].y + v[k].z;
+        sv[k].w = sv[k].z + v[k].w;
+        const float incl = wave_scan_inclusive(sv[k].w);
+        e[k] = dpp_or_zero<0x138>(incl);  // wave_shr:1
+        tot[k] = lane63(incl);
+    }
+    float wt = tot[0];
+#pragma unroll
+    for (int k = 1; k < K; ++k) wt = wt + tot[k];
+    if (lane == 0) slots[wave] = wt;
+    __syncthreads();
+    if (wave == 0) {
+        float a = 0.f;  // the chunk total, 0 + t_0 + ... + t_{NW-1}
+#pragma unroll
+        for (int w = 0; w < NW; ++w) a = a + slots[w];
+        if (lane == 0) look_publish(agg + item, a);
+        const int64_t g = j / kLookGroup;
+        const int64_t first = g * kLookGroup;
+        // this group's earlier chunk totals, lane i <- piece first + i
+        const float ai = first + lane < j ? look_await(agg + o * P + first + lane, spin_limit) : 0.f;
+        const float in_group = lane63(wave_scan_inclusive(ai));
+        if (j == first + kLookGroup - 1 && j + 1 < P && lane == 0)
+            look_publish(gsum + o * NG + g, in_group + a);
+        float before = 0.f;  // the earlier groups' totals
+        for (int64_t h0 = 0; h0 < g; h0 += kWave) {
+            const float th = h0 + lane < g ? look_await(gsum + o * NG + h0 + lane, spin_limit) : 0.f;
+            before = before + lane63(wave_scan_inclusive(th));
+        }
+        if (lane == 0) s_carry = before + in_group;
+    }
+    __syncthreads();
+    float mine = s_carry;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        if (w < wave) mine = mine + slots[w];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float pre = mine + e[k];
+        const v4f y = v4f{pre + sv[k].x, pre + sv[k].y, pre + sv[k].z, pre + sv[k].w};
+        mine = mine + tot[k];
+        if (part)
+            store_q4_part<REV, NT>(orow, R, qw + 256 * k + lq, q_end, y);
+        else
+            store_q4<REV, NT>(orow, R, qw + 256 * k + lq, y);
+    }
+}
+
 // Whole rows (no pieces) by persistent workgroups of NW waves: workgroup b
 // takes rows b, b + G, b + 2G, ... (G = gridDim.x) and walks their chunks as
 // one stream -- each row's partial chunk, if any, then its full chunks, the
@@ -1382,6 +1506,39 @@ hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, floa
                             hipStream_t s) {
     return reverse ? rows_go<true>(p, x, out, v, carry_in, totals, s)
                    : rows_go<false>(p, x, out, v, carry_in, totals, s);
+}
+
+template <bool REV, int NW>
+hipError_t lookback_go(const rd_plan& p, const float* x, float* out, const Strides& v,
+                       uint32_t* ticket, uint64_t* agg, uint64_t* gsum, int64_t NG,
+                       uint32_t spin_limit, hipStream_t s) {
+    if (p.nontemporal)
+        return launch(scan_rows_lookback_kernel<REV, NW, 8, true>, p.blocks, NW * kWave, s, x,
+                      out, v.outer, v.R, v.so, p.split, NG, ticket, agg, gsum, spin_limit);
+    return launch(scan_rows_lookback_kernel<REV, NW, 8, false>, p.blocks, NW * kWave, s, x, out,
+                  v.outer, v.R, v.so, p.split, NG, ticket, agg, gsum, spin_limit);
+}
+
+hipError_t launch_scan_rows_lookback(const rd_plan& p, bool reverse, const float* x, float* out,
+                                     const Strides& v, void* ws, uint32_t spin_limit,
+                                     hipStream_t s) {
+    const int64_t NG = lookback_groups(p.split);
+    const int nw = p.group / kWave;
+    if (p.combine != RD_COMBINE_LOOKBACK || p.unroll != 8 || (nw != 8 && nw != 16) ||
+        p.rows_per_split != int64_t(nw) * 256 * 8 || p.blocks != v.outer * p.split ||
+        p.workspace_bytes != lookback_workspace_bytes(v.outer, p.split) || ws == nullptr)
+        return hipErrorInvalidValue;
+    hipError_t e = hipMemsetAsync(ws, 0, size_t(p.workspace_bytes), s);
+    if (e != hipSuccess) return e;
+    char* base = static_cast<char*>(ws);
+    uint32_t* ticket = reinterpret_cast<uint32_t*>(base);
+    uint64_t* agg = reinterpret_cast<uint64_t*>(base + kLookTicketBytes);
+    uint64_t* gsum = agg + v.outer * p.split;
+    if (reverse)
+        return nw == 8 ? lookback_go<true, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s)
+                       : lookback_go<true, 16>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+    return nw == 8 ? lookback_go<false, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s)
+                   : lookback_go<false, 16>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
 }
 
 hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows, int64_t P,

@@ -125,8 +125,21 @@ void check_scan_plan(const rd::Strides& v, const rd_plan& p) {
         return;
     }
     if (p.blocks < 1 || p.blocks > rd::kMaxBlocks) fail("scan blocks out of range", v, -1, p);
-    if (p.passes != (p.split > 1 ? 3 : 1)) fail("scan passes", v, -1, p);
+    const bool look = p.combine == RD_COMBINE_LOOKBACK;
+    if (p.passes != (p.split > 1 && !look ? 3 : 1)) fail("scan passes", v, -1, p);
     const int64_t n = v.outer * v.inner;
+    if (look) {
+        // one launch, a workgroup of 8 or 16 waves per piece of one block
+        // chunk; workspace: ticket, chunk totals, group totals
+        if (p.path != RD_PATH_SCAN_ROWS || v.inner != 1 || v.sr != 1)
+            fail("look-back off the row path", v, -1, p);
+        if ((p.group != 512 && p.group != 1024) || p.block_threads != p.group || p.unroll != 8 ||
+            p.rows_per_split != p.group / 64 * 2048 || !tiles(v.R, p.split, p.rows_per_split) ||
+            p.blocks != v.outer * p.split ||
+            p.workspace_bytes != rd::lookback_workspace_bytes(v.outer, p.split))
+            fail("look-back plan", v, -1, p);
+        return;
+    }
     switch (p.path) {
         case RD_PATH_SCAN_ROWS:
             if (v.inner != 1 || v.sr != 1) fail("scan rows without unit row stride", v, -1, p);

@@ -56,6 +56,18 @@ def test_rows_around_tiles():
     _sweep(shapes, [0, 1, 2, 3], 801, "scan rows")
 
 
+def test_few_rows_one_pass_plans():
+    """Few rows that are not cut: a workgroup per row in one pass -- 4 waves
+    for rows of 2-4 tiles, 8 past 16384 positions, 16 from 65536 -- up to
+    the longest rows the planner leaves uncut."""
+    shapes = [(40, 16384, 1), (5, 16385, 1), (64, 65536, 1), (2, 131071, 1),
+              (86, 131072, 1), (300, 4097, 1)]
+    for (o, r, i), group in zip(shapes, (256, 512, 1024, 1024, 1024, 256)):
+        p = rd.rd_plan_cumsum(256, o, r, i)
+        assert (p.split, p.group, p.passes) == (1, group, 1), ((o, r, i), p.as_dict())
+    _sweep(shapes, [0, 1], 802, "scan few rows")
+
+
 @pytest.mark.parametrize("path", [0, 7, 8], ids=["default", "scan_cols", "scan_cols_small"])
 def test_columns(path):
     """inner > 1 on both column kernels: 4 columns a lane and 256 a wave
@@ -207,9 +219,9 @@ def test_rows_streamed_by_persistent_workgroups(group, unroll):
 
 
 def test_default_splits():
-    """Few rows or columns: the planner cuts them itself (many slabs: the slab
-    carries go one wave per column)."""
-    shapes = [(1, 1 << 20, 1), (7, 100_000, 1), (1, 100_000, 4), (2, 50_000, 33),
+    """Few long rows or few columns: the planner cuts them itself (many slabs:
+    the slab carries go one wave per column)."""
+    shapes = [(1, 1 << 20, 1), (7, 200_000, 1), (1, 100_000, 4), (2, 50_000, 33),
               (1, 1 << 20, 4), (1, 200_000, 300)]
     for shape in shapes:
         p = rd.rd_plan_cumsum(256, *shape).as_dict()
@@ -221,9 +233,10 @@ def test_default_splits():
 def test_many_pieces():
     """Thousands of pieces per row: the carries of the piece totals are scanned
     in 256-total chunks by one wave per row."""
-    p = rd.rd_plan_cumsum(256, 1, 1 << 24, 1)
-    assert p.split == 4096 and p.passes == 3
-    _sweep([(1, 1 << 24, 1)], [0], 870, "scan 4096 pieces")
+    with rd.tuning(combine=1):  # this row would take the look-back by default
+        p = rd.rd_plan_cumsum(256, 1, 1 << 24, 1)
+        assert p.split == 4096 and p.passes == 3
+        _sweep([(1, 1 << 24, 1)], [0], 870, "scan 4096 pieces")
     with rd.tuning(split=700):
         _sweep([(2, 700 * 4096 + 3, 1), (1, 257 * 4096, 1)], [0, 1], 871, "scan 700 pieces")
 
@@ -321,3 +334,108 @@ def test_columns_full_size():
                                           "%s rev=%d outer %d.." % (shape, rev, o0))
         del x
         t.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("group", [512, 1024])
+def test_rows_lookback(group):
+    """Rows in one launch, a workgroup per piece of one block chunk, each
+    piece's carry formed from the totals earlier pieces publish: rows of one
+    and of several pieces, around the chunk, more pieces than a group of 64
+    (group totals), misaligned bases, both directions; integer data, bit for
+    bit."""
+    L = group // 64 * 2048
+    shapes = [(3, 1, 1), (3, 5, 1), (2, 4096, 1), (2, L - 1, 1), (2, L, 1), (2, L + 1, 1),
+              (5, 3 * L + 17, 1), (1, 64 * L, 1), (1, 65 * L + 7, 1), (2, 130 * L + 3, 1)]
+    with rd.tuning(combine=3, group=group):
+        for o, r, i in shapes:
+            p = rd.rd_plan_cumsum(256, o, r, i)
+            assert (p.combine, p.split, p.passes, p.rows_per_split) == (3, -(-r // L), 1, L)
+        _sweep(shapes, [0, 3], 900 + group, "scan lookback g%d" % group)
+
+
+def test_rows_lookback_default_plans():
+    """Long rows among few take the look-back by default."""
+    shapes = [(1, 1 << 24, 1), (5, (1 << 22) + 3, 1), (16, 1 << 20, 1)]
+    for shape in shapes:
+        p = rd.rd_plan_cumsum(256, *shape)
+        assert p.as_dict()["combine"] == "lookback" and p.group == 1024, (shape, p.as_dict())
+    _sweep(shapes, [0, 1], 905, "scan lookback default")
+
+
+def test_rows_lookback_many_groups():
+    """More than 64 group totals before a piece: they are read 64 at a time."""
+    shape = (1, 4097 * 16384 + 3, 1)
+    with rd.tuning(combine=3, group=512):
+        p = rd.rd_plan_cumsum(256, *shape)
+        assert p.split == 4098
+        _sweep([shape], [0], 910, "scan lookback 65 groups")
+
+
+def test_rows_lookback_in_place_strided_repeats():
+    t = H.torch()
+    with rd.tuning(combine=3, group=1024):
+        a = workloads.small_ints(3 * 100_000, 911)
+        x = H.upload(a)
+        rd.rd_cumsum_dim(x, 3, 100_000, 1, reverse=True, out=x)
+        S, _ = oracle.cumsum_dim(a, 3, 100_000, 1, True)
+        H.assert_bitwise_equal_oracle(x.cpu().numpy(), S, "lookback in place")
+        # rows 100_007 floats apart: the first 100_000 of each
+        b = workloads.small_ints(3 * 100_007, 912)
+        view = H.upload(b).view(3, 100_007)[:, :100_000]
+        got = rd.cumsum(view, 1).cpu().numpy()
+        S, _ = oracle.cumsum_dim(np.ascontiguousarray(b.reshape(3, 100_007)[:, :100_000]).ravel(),
+                                 3, 100_000, 1, False)
+        H.assert_bitwise_equal_oracle(got.ravel(), S, "lookback row stride")
+        # random data: the carries are summed in a fixed order, so repeats agree
+        xr = H.upload(workloads.random(2 * 3_000_000, 913, "normal"))
+        for rev in (True, False):
+            first = rd.rd_cumsum_dim(xr, 2, 3_000_000, 1, reverse=rev)
+            for _ in range(4):
+                assert t.equal(rd.rd_cumsum_dim(xr, 2, 3_000_000, 1, reverse=rev).view(t.int32),
+                               first.view(t.int32)), rev
+
+
+_SPIN = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import torch
+import oracle
+import workloads
+import sum_reduction_amd as rd
+from tests import gpu_helpers as H
+o, r, L = 4, 40 * 16384 + 5, 16384
+a = workloads.small_ints(o * r, 915)
+x = H.upload(a)
+S, _ = oracle.cumsum_dim(a, o, r, 1, True)
+S = np.asarray(S).reshape(o, r)
+with rd.tuning(combine=3, group=512):
+    y = rd.rd_cumsum_dim(x, o, r, 1, reverse=True).cpu().numpy().reshape(o, r)
+nan_pieces = 0
+for i in range(o):
+    yr, sr = y[i, ::-1], S[i, ::-1]  # processing order of the reverse sum
+    for j in range(0, r, L):
+        seg = yr[j:j + L]
+        if np.isnan(seg).all():
+            nan_pieces += 1
+        else:
+            assert np.array_equal(seg, sr[j:j + L].astype(np.float32)), (i, j)
+    assert not np.isnan(yr[:L]).any()  # a row's first piece waits for nothing
+print("spin-ok", nan_pieces)
+"""
+
+
+def test_rows_lookback_wait_limit():
+    """Waits bounded from the host: with RD_TEST_SPIN_LIMIT=0 every wait
+    polls once.  The kernel still ends, and each piece's outputs are either
+    exact or all NaN, never a wrong finite sum.  (The limit is read once per
+    process, so this runs in a child process.)"""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, RD_TEST_SPIN_LIMIT="0")
+    res = subprocess.run([sys.executable, "-c", _SPIN, root], env=env, capture_output=True,
+                         text=True, timeout=240, cwd=root)
+    assert res.returncode == 0 and "spin-ok" in res.stdout, res.stdout + res.stderr[-3000:]
+    H.say(res.stdout.strip())

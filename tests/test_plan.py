@@ -248,10 +248,29 @@ def _scan_invariants(p, outer, R, inner, cu=CU):
     assert p.split * p.rows_per_split >= R > (p.split - 1) * p.rows_per_split
     if inner == 1:
         assert p.rows_per_split % 4096 == 0           # whole tiles per piece
+        look = outer < 4 * cu and R >= 1 << 20 and outer * R >= 1 << 24 and \
+            -(-R // 32768) <= (1 << 20) // outer
+        assert (p.combine == 3) == look, (outer, R, cu, p.as_dict())
+        if look:
+            # one launch, a workgroup of 16 waves per 32768 positions, the
+            # carries by look-back: ticket, chunk totals, group totals
+            assert (p.group, p.block_threads, p.rows_per_split, p.passes) == (1024, 1024, 32768, 1)
+            assert p.split == -(-R // 32768) and p.blocks == outer * p.split
+            assert p.workspace_bytes == 256 + 8 * outer * (p.split + -(-p.split // 64))
+            return
+        # pieces only for fewer rows than a third of the CUs, each of at
+        # least 131072 positions (and of more than one tile)
+        assert (p.split > 1) == (3 * outer < cu and R >= 131072), (outer, R, cu, p.split)
         # a workgroup per uncut row of more than 16384 -- 16 waves from 65536
-        # on, else 8 --, else a wave per piece (4 to a workgroup)
-        want = 64 if p.split > 1 or R <= 16384 else 1024 if R >= 65536 else 512
-        assert p.group == want
+        # on, else 8 --; among fewer than 4 rows a CU, 4 waves per uncut row
+        # of more than a tile; else a wave per piece (4 to a workgroup)
+        if p.split > 1:
+            want = 64
+        elif R > 16384:
+            want = 1024 if R >= 65536 else 512
+        else:
+            want = 256 if R > 4096 and outer < 4 * cu else 64
+        assert p.group == want, (outer, R, cu, p.group)
         if p.group == 64:
             assert p.block_threads == 256
             assert p.blocks == min(-(-outer * p.split // 4), 1 << 20)
@@ -300,8 +319,10 @@ def test_cumsum_row_widths_at_their_edges():
         p = rd.rd_plan_cumsum(CU, 4096, R, 1)
         assert p.split == 1 and p.group == group, (R, p.as_dict())
         assert p.block_threads == max(group, 256)
-    p = rd.rd_plan_cumsum(CU, 16, 1 << 20, 1)   # 16 rows: cut into pieces
-    assert p.split > 1 and p.group == 64
+    p = rd.rd_plan_cumsum(CU, 16, 1 << 19, 1)   # 16 rows of 2^19: cut into pieces
+    assert p.split > 1 and p.group == 64 and p.passes == 3
+    p = rd.rd_plan_cumsum(CU, 16, 1 << 20, 1)   # 16 rows of 2^20: look-back pieces
+    assert p.split == 32 and p.group == 1024 and p.passes == 1
     with rd.tuning(unroll=4):                    # 4-slice chunks: 4 waves
         assert rd.rd_plan_cumsum(CU, 4096, 65536, 1).group == 256
 
@@ -317,8 +338,8 @@ def test_cumsum_rows_streamed():
         with rd.tuning(group=group, unroll=unroll, order=1, split=1):
             assert rd.rd_plan_cumsum(CU, 3, 50_000, 1).blocks == 3  # fewer rows than CUs
         with rd.tuning(group=group, unroll=unroll, order=1):
-            with pytest.raises(rd.RdError):  # few rows are cut into pieces
-                rd.rd_plan_cumsum(CU, 3, 50_000, 1)
+            with pytest.raises(rd.RdError):  # few long rows are cut into pieces
+                rd.rd_plan_cumsum(CU, 3, 150_000, 1)
     with rd.tuning(group=64, order=1):
         with pytest.raises(rd.RdError):
             rd.rd_plan_cumsum(CU, 32768, 32768, 1)
@@ -333,8 +354,9 @@ def test_cumsum_rows_streamed():
 
 def test_cumsum_plans():
     """Rows: a workgroup of 8 waves per row (problem 91: 32768 rows, no pieces,
-    two 16384-position chunks a row); few rows
-    are cut into pieces of whole 4096-element tiles, a wave each.
+    two 16384-position chunks a row); few long rows
+    are cut into pieces of whole 4096-element tiles, a wave each, other few
+    rows take a workgroup each.
     Columns: a wave per 64 lane-columns, slabs of R when there are too few
     waves."""
     p = rd.rd_plan_cumsum(CU, 32768, 32768, 1)
@@ -343,6 +365,24 @@ def test_cumsum_plans():
     assert p.workspace_bytes == 0
     p = rd.rd_plan_cumsum(CU, 1, 1 << 20, 1)
     assert p.split == 256 and p.rows_per_split == 4096 and p.passes == 3
+    p = rd.rd_plan_cumsum(CU, 64, 131072, 1)              # 64 * 3 < 256 CUs
+    assert p.split == 32 and p.group == 64 and p.passes == 3
+    p = rd.rd_plan_cumsum(CU, 1, 1 << 28, 1)              # long rows: look-back
+    assert p.as_dict()["combine"] == "lookback" and p.split == 8192 and p.blocks == 8192
+    assert p.passes == 1 and p.workspace_bytes == 256 + 8 * (8192 + 128)
+    with rd.tuning(combine=1):                            # the three kernels instead
+        p = rd.rd_plan_cumsum(CU, 1, 1 << 28, 1)
+        assert p.split == 4096 and p.passes == 3
+    p = rd.rd_plan_cumsum(CU, 1, 1 << 22, 1)              # 16 MB: too small for it
+    assert p.split == 1024 and p.passes == 3
+    p = rd.rd_plan_cumsum(CU, 86, 131072, 1)              # 86 * 3 >= 256: one pass
+    assert p.split == 1 and p.group == 1024 and p.blocks == 86 and p.workspace_bytes == 0
+    p = rd.rd_plan_cumsum(CU, 64, 65536, 1)               # rows too short to cut
+    assert p.split == 1 and p.group == 1024 and p.passes == 1
+    p = rd.rd_plan_cumsum(CU, 512, 16384, 1)              # few rows of 4 tiles
+    assert p.split == 1 and p.group == 256 and p.block_threads == 256 and p.blocks == 512
+    p = rd.rd_plan_cumsum(CU, 1024, 16384, 1)             # 4 rows a CU: a wave each
+    assert p.split == 1 and p.group == 64 and p.blocks == 256
     p = rd.rd_plan_cumsum(CU, 128, 4096, 4095)
     assert p.as_dict()["path"] == "scan_cols" and p.split == 1
     assert p.col_waves == 8 and p.blocks == 256         # 16 tiles a row: 2 blocks of 8
@@ -355,6 +395,36 @@ def test_cumsum_plans():
             outer = int(rng.integers(1, 8))
         cu = int(rng.integers(1, 300))
         _scan_invariants(rd.rd_plan_cumsum(cu, outer, R, inner), outer, R, inner, cu)
+
+
+def test_lookback_workspace_indices_stay_inside():
+    """Host-side bounds of the look-back kernel's workspace: piece (o, j)
+    publishes chunk total o*P + j, reads those of its group before j, reads
+    the group totals o*NG + h for h < j // 64 and, as the last piece of a
+    group with a successor, publishes o*NG + j // 64; the ticket takes the
+    first 256 bytes.  Every index must fall inside workspace_bytes."""
+    rng = np.random.default_rng(17)
+    cases = [(1, 1 << 28), (3, 64 * 32768), (2, 64 * 32768 + 1), (1, 4097 * 16384 + 3)]
+    cases += [tuple(int(v) for v in rng.integers(1, [600, 1 << 24])) for _ in range(300)]
+    for outer, R in cases:
+        for group in (512, 1024):
+            with rd.tuning(combine=3, group=group):
+                p = rd.rd_plan_cumsum(CU, outer, R, 1)
+            P, L = p.split, p.rows_per_split
+            NG = -(-P // 64)
+            assert L == group // 64 * 2048 and (P - 1) * L < R <= P * L
+            assert p.blocks == outer * P
+            agg_end = 256 + 8 * outer * P            # one past the chunk totals
+            last_gsum = 256 + 8 * (outer * P + (outer - 1) * NG + (NG - 1))
+            assert p.workspace_bytes == last_gsum + 8
+            # the highest group total any piece publishes or reads: the last
+            # row's group (P - 2) // 64, and only when P > 64
+            if P > 64:
+                g_pub = (P - 2) // 64
+                assert 256 + 8 * (outer * P + (outer - 1) * NG + g_pub) < p.workspace_bytes
+            # the highest chunk total read: row outer - 1, piece P - 2
+            if P > 1:
+                assert 256 + 8 * ((outer - 1) * P + P - 2) < agg_end
 
 
 def test_cumsum_forced_split():
