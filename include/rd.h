@@ -41,15 +41,20 @@
  *   library allocates them stream-ordered on `stream` from a pool of its own
  *   and frees them on the same stream, so concurrent calls on different
  *   streams never share memory.  The partials of a split reduce are summed by
- *   a second kernel in fixed order.  With the RD_COMBINE_LAST_BLOCK option the last
- *   workgroup of the first kernel sums them instead; the integer ticket
- *   counter that elects it belongs to the stream (one per stream and device,
- *   zeroed in stream order before each such launch and reset by the kernel
- *   itself), so calls on one stream, which never overlap,
- *   never share it with calls on another (calls on the per-thread default
- *   stream, whose handle stands for a different stream in each thread, take
- *   the second kernel instead).  The pool and the counters are created by
- *   the first call on a device that needs a workspace.  A call that needs a
+ *   a second kernel in fixed order -- or, for a row sum of at most 4 rows cut
+ *   into at most 8192 pieces in all (RD_COMBINE_LAST_BLOCK, the default
+ *   there), by the last workgroup of the one kernel: the others publish their
+ *   piece sums into a buffer of the stream's own (8192 tagged words and their
+ *   values, 96 KB of device memory per stream and device, created by the
+ *   first such call on the stream, kept until the process ends, for up to
+ *   256 streams), each word tagged with that launch's epoch, a number the
+ *   stream gives each launch in turn, so calls on one stream, which never
+ *   overlap, never take another call's words, and calls on another stream
+ *   never touch them.  Same order, same bits as the second kernel.  Calls on
+ *   the per-thread default stream (whose handle stands for a different
+ *   stream in each thread), beyond 256 streams, or with no memory for the
+ *   buffer take the second kernel instead.  The pool is created by the first
+ *   call on a device that needs a workspace.  A call that needs a
  *   workspace is refused with RD_ERR_CAPTURE while its stream is being
  *   captured into a graph (a replay of such a capture faulted in the second
  *   kernel, reading the graph-allocated workspace; the cause is not
@@ -165,8 +170,8 @@ rd_status rd_sum_dim(const float* x, int64_t outer, int64_t R, int64_t inner,
  * that GPU's buffer, so calls that may overlap on one GPU -- on different
  * streams, or from different host threads, without an ordering between
  * them -- race and give wrong results; calls in one stream's order are
- * safe.  The partials are always combined by a second kernel (the
- * RD_COMBINE_LAST_BLOCK tuning option is ignored here).  Set-up: the
+ * safe.  The partials are always combined by a second kernel (a plan's
+ * RD_COMBINE_LAST_BLOCK is not taken here: no stream buffer is used).  Set-up: the
  * library's first call on a device (of any entry point) must not be made
  * while its stream is being captured (RD_ERR_CAPTURE).
  */
@@ -358,10 +363,10 @@ typedef enum rd_combine {
     RD_COMBINE_NONE = 0,       /* one pass, no partial sums */
     RD_COMBINE_PASS = 1,       /* a second kernel sums them in fixed order */
     RD_COMBINE_LAST_BLOCK = 2, /* the last workgroup of the first kernel sums
-                                  them in the same order (one launch; an
-                                  option: slower than RD_COMBINE_PASS on
-                                  MI355X); calls on a capturing stream use
-                                  RD_COMBINE_PASS, with identical results */
+                                  them in the same order, from results the
+                                  others publish as tagged words (one launch;
+                                  the default for row sums of at most 4 rows
+                                  and 8192 pieces; see "Workspace" above) */
     RD_COMBINE_LOOKBACK = 3    /* row scans: one launch, a workgroup per row
                                   piece, each piece's carry summed in a fixed
                                   order from totals that earlier pieces
@@ -400,7 +405,12 @@ typedef struct rd_plan {
     int64_t rows_per_split;  /* COLS*, SCAN_COLS: rows per slab; SCAN_ROWS:
                                 positions per piece */
     int64_t blocks;          /* workgroups of the main pass */
-    int64_t workspace_bytes; /* stream-ordered scratch (0 if passes == 1) */
+    int64_t workspace_bytes; /* stream-ordered scratch (0 if no partial
+                                results are kept; a look-back scan's
+                                ticket and published totals; kept for a
+                                row sum with RD_COMBINE_LAST_BLOCK too,
+                                for the calls that take the second kernel
+                                instead) */
 } rd_plan;
 
 /* Plan of rd_sum_dim for that shape on a device with cu_count CUs (the sum
@@ -427,8 +437,18 @@ rd_status rd_plan_strided(int cu_count, int64_t outer, int64_t R, int64_t inner,
 /* Plan of rd_cumsum_dim for that shape (the tuning override's split,
  * unroll -- SCAN_ROWS 4 or 8, SCAN_COLS 4, 8 or 16 --, group -- SCAN_ROWS 64,
  * 256, 512 or 1024 --, col_waves -- SCAN_COLS 1, 2, 4, 8 or 16 (1 and 2 for
- * inner >= 4) --, row_waves -- SCAN_COLS, see rd_tune -- and nontemporal
- * fields apply). */
+ * inner >= 4) --, row_waves -- SCAN_COLS, see rd_tune --, combine and
+ * nontemporal fields apply).  Rows of at least 2^20 positions, fewer than 4
+ * per CU and 2^24 elements in all take combine = RD_COMBINE_LOOKBACK: one
+ * launch, a workgroup (group 1024, or 512 when tuned) per piece of
+ * rows_per_split = group / 64 * 2048 positions, split pieces per row, whose
+ * carry is the sum, in index order, of the totals that earlier pieces of its
+ * row publish (the pieces are taken in the order of a ticket each workgroup
+ * draws at its start, so a piece only ever waits for pieces of workgroups
+ * that started before it; the same bits on every run).  Its workspace, a
+ * 256-byte ticket and 8 bytes per piece and per group of 64 pieces, is
+ * zeroed in stream order before the launch.  A wait of this kernel ends
+ * after at most 2^18 polls; a piece whose wait runs out writes NaN. */
 rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
                          rd_plan* plan);
 
@@ -458,7 +478,9 @@ typedef struct rd_tune {
     int32_t order;           /* ROWS: rd_order; SCAN_ROWS with a workgroup
                                 per row and no pieces: RD_ORDER_INTERLEAVED */
     int32_t nontemporal;     /* every path: 1 = off, 2 = on */
-    int32_t combine;         /* ROWS: 1 = second pass, 2 = last workgroup */
+    int32_t combine;         /* ROWS: 1 = second pass, 2 = last workgroup;
+                                SCAN_ROWS: 1 = the planner's other plans,
+                                3 = look-back */
     int32_t path;            /* inner >= 4: RD_PATH_COLS or RD_PATH_COLS_SMALL
                                 (the latter for inner <= 256) */
     int64_t split;           /* ROWS: pieces per row; COLS*: slabs of R */

@@ -19,45 +19,56 @@ thread_local int t_last_hip = 0;
 // Per-device state.  The first call on a device reads its CU count (which
 // fixes the plan, hence the summation order); the first call that needs a
 // workspace also creates the library's memory pool for workspaces, which
-// keeps its memory between calls, and the ticket counters of the fused
-// combine.  Calls whose plan needs no workspace, and rd_sum_dim_noalloc,
-// never allocate.
-// Ticket counters for the fused (last-workgroup) combine: one per stream that
-// has made such a call on the device, zeroed when they are created, before
-// every fused launch (in stream order) and by every kernel that uses one.
-// Calls on one stream never overlap, so a stream's counter is 0 when its next
-// kernel starts.
-constexpr int kTicketSlots = 4096;
+// keeps its memory between calls; the first single-launch combine on a
+// stream creates that stream's buffer.  Calls whose plan needs no
+// workspace, and rd_sum_dim_noalloc, never allocate.
+// Buffers of the single-launch combine: one per stream that has made such a
+// call on the device (up to kPubStreams), each with room for kPubWords piece
+// results -- tagged words and their values -- and the stream's last epoch.
+// A launch publishes its words tagged with a new epoch of its stream; calls
+// on one stream never overlap, so every word a launch finds tagged with its
+// own epoch was written by that launch.  Zeroed when created, and again
+// before an epoch is reused (after 2^32 - 1 launches).
+constexpr int kPubStreams = 256;
+using rd::kPubWords;
+struct StreamPub {
+    uint64_t* words = nullptr;
+    float* vals = nullptr;
+    uint32_t epoch = 0;
+};
 struct Device {
     std::once_flag once;
     std::atomic<bool> ready{false};  // set once the CU count is known
     int cu = 0;
     hipError_t err = hipSuccess;
-    std::once_flag mem_once;  // pool and tickets, on the first workspace plan
+    std::once_flag mem_once;  // the workspace pool, on the first workspace plan
     hipMemPool_t pool = nullptr;
     hipError_t mem_err = hipSuccess;
-    uint32_t* tickets = nullptr;  // null: the fused combine is not used
-    std::mutex ticket_mu;
-    std::unordered_map<hipStream_t, int> ticket_of;
+    std::mutex pub_mu;
+    std::unordered_map<hipStream_t, StreamPub> pub_of;
 };
 Device g_devices[rd::kMaxDevices];
 
-// Zeroed ticket counters, or null if they cannot be had (then every split
-// reduce takes the two-kernel combine, with the same results).
-uint32_t* make_tickets() {
-    uint32_t* t = nullptr;
-    if (hipMalloc(reinterpret_cast<void**>(&t), kTicketSlots * sizeof(uint32_t)) != hipSuccess)
-        return nullptr;
+// A zeroed buffer of kPubWords tagged words and their values, or null if
+// it cannot be had (then the call takes the two-kernel combine, with the
+// same results).
+StreamPub make_pub() {
+    StreamPub b;
+    void* mem = nullptr;
+    const size_t bytes = size_t(kPubWords) * (sizeof(uint64_t) + sizeof(float));
+    if (hipMalloc(&mem, bytes) != hipSuccess) return b;
     hipStream_t s = nullptr;
     bool ok = hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess;
-    ok = ok && hipMemsetAsync(t, 0, kTicketSlots * sizeof(uint32_t), s) == hipSuccess;
+    ok = ok && hipMemsetAsync(mem, 0, bytes, s) == hipSuccess;
     ok = ok && hipStreamSynchronize(s) == hipSuccess;
     if (s) (void)hipStreamDestroy(s);
     if (!ok) {
-        (void)hipFree(t);
-        return nullptr;
+        (void)hipFree(mem);
+        return b;
     }
-    return t;
+    b.words = static_cast<uint64_t*>(mem);
+    b.vals = reinterpret_cast<float*>(b.words + kPubWords);
+    return b;
 }
 
 // RD_OK when `stream` is not being captured into a graph, RD_ERR_CAPTURE
@@ -75,20 +86,33 @@ rd_status capture_check(hipStream_t stream) {
     return cap == hipStreamCaptureStatusNone ? RD_OK : RD_ERR_CAPTURE;
 }
 
-// The ticket counter of `stream` (not being captured: such calls are
-// refused before this), or null for the two-kernel combine: every counter
-// taken, or the per-thread default stream, whose one handle stands for a
+// The single-launch combine's buffer of `stream` and a new epoch for one
+// launch on it (the stream is not being captured: such calls are refused
+// before this), or false for the two-kernel combine: every buffer taken, none
+// to be had, or the per-thread default stream, whose one handle stands for a
 // different stream in each host thread -- calls from two threads could run
-// at once and share the counter.
-uint32_t* stream_ticket(Device& d, hipStream_t stream) {
-    if (!d.tickets || stream == hipStreamPerThread) return nullptr;
-    std::lock_guard<std::mutex> lock(d.ticket_mu);
-    auto it = d.ticket_of.find(stream);
-    if (it != d.ticket_of.end()) return d.tickets + it->second;
-    const int slot = static_cast<int>(d.ticket_of.size());
-    if (slot >= kTicketSlots) return nullptr;
-    d.ticket_of.emplace(stream, slot);
-    return d.tickets + slot;
+// at once and share the buffer.
+bool stream_pub(Device& d, hipStream_t stream, rd::Published* pub, hipError_t* err) {
+    *err = hipSuccess;
+    if (stream == hipStreamPerThread) return false;
+    std::lock_guard<std::mutex> lock(d.pub_mu);
+    auto it = d.pub_of.find(stream);
+    if (it == d.pub_of.end()) {
+        if (static_cast<int>(d.pub_of.size()) >= kPubStreams) return false;
+        StreamPub b = make_pub();
+        if (!b.words) return false;
+        it = d.pub_of.emplace(stream, b).first;
+    }
+    StreamPub& b = it->second;
+    if (++b.epoch == 0) {  // every epoch used: clear the words, start again
+        *err = hipMemsetAsync(b.words, 0, size_t(kPubWords) * sizeof(uint64_t), stream);
+        if (*err != hipSuccess) return false;
+        b.epoch = 1;
+    }
+    pub->words = b.words;
+    pub->vals = b.vals;
+    pub->epoch = b.epoch;
+    return true;
 }
 
 std::mutex g_tune_mu;
@@ -148,9 +172,9 @@ rd_status current_device(Device** out, int* index, hipStream_t stream) {
     return RD_OK;
 }
 
-// The device's workspace pool and ticket counters, created by the first call
-// that needs a workspace (never while capturing: such calls are refused
-// first).  The calling thread's current device is d's.
+// The device's workspace pool, created by the first call that needs a
+// workspace (never while capturing: such calls are refused first).  The
+// calling thread's current device is d's.
 rd_status device_memory(Device& d) {
     std::call_once(d.mem_once, [&d] {
         int dev = -1;
@@ -176,7 +200,6 @@ rd_status device_memory(Device& d) {
             d.mem_err = err;
             return;
         }
-        d.tickets = make_tickets();
     });
     if (d.mem_err != hipSuccess) return hip_fail(d.mem_err, RD_ERR_HIP);
     return RD_OK;
@@ -211,25 +234,38 @@ const Injected& injected() {
     return f;
 }
 
-// Runs plan p.  fixed == nullptr: the workspace (if any) is allocated
-// stream-ordered from the device's pool and freed after the last kernel,
-// which is refused while `s` is being captured.  fixed != nullptr: it is the
-// workspace, at least p.workspace_bytes long, and nothing is allocated (the
-// partial results are combined by the second kernel).
+// Runs plan p.  fixed == nullptr: a row reduce whose plan takes the
+// single-launch combine publishes its piece results in the stream's buffer
+// (one kernel); otherwise the workspace (if any) is allocated stream-ordered
+// from the device's pool and freed after the last kernel.  Either is refused
+// while `s` is being captured.  fixed != nullptr: it is the workspace, at
+// least p.workspace_bytes long, and nothing is allocated (the partial
+// results are combined by the second kernel).
 rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const rd::Strides& v,
                   rd::Results out, hipStream_t s, float* fixed) {
     if (p.path == RD_PATH_NONE) return RD_OK;
     if (injected().launch) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
     bool pooled = false;
-    if (p.workspace_bytes > 0 && fixed) {
-        ws = fixed;
-    } else if (p.workspace_bytes > 0) {
+    rd::Published pub;
+    bool published = false;
+    if (p.workspace_bytes > 0 && !fixed) {
         rd_status st = capture_check(s);
         if (st != RD_OK) return st;
-        st = device_memory(dev);
-        if (st != RD_OK) return st;
         if (injected().alloc) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
+        if (p.path == RD_PATH_ROWS && p.combine == RD_COMBINE_LAST_BLOCK &&
+            op != RD_OP_SOFTMAX_DENOM && v.outer * v.inner * p.split <= kPubWords) {
+            hipError_t pe = hipSuccess;
+            published = stream_pub(dev, s, &pub, &pe);
+            if (pe != hipSuccess) return hip_fail(pe, RD_ERR_HIP);
+            pub.spin_limit = injected().spin_limit;
+        }
+    }
+    if (p.workspace_bytes > 0 && fixed) {
+        ws = fixed;
+    } else if (p.workspace_bytes > 0 && !published) {
+        rd_status st = device_memory(dev);
+        if (st != RD_OK) return st;
         hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
                                               size_t(p.workspace_bytes), dev.pool, s);
         if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
@@ -251,19 +287,11 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
         case RD_PATH_ROWS:
             if (p.split == 1) {
                 e = rd::launch_rows(op, p, x, v, out, nullptr, rd::Results{}, s);
+            } else if (published) {
+                e = rd::launch_rows(op, p, x, v, rd::Results{}, &pub, out, s);
             } else {
-                uint32_t* ticket = p.combine == RD_COMBINE_LAST_BLOCK && pooled
-                                       ? stream_ticket(dev, s)
-                                       : nullptr;
-                // the election needs the counter at 0 when the kernel starts:
-                // the kernel leaves it there, and it is zeroed in stream order
-                // before every fused launch as well, so that no earlier launch
-                // (one that did not run to its end) can make a later one elect
-                // the wrong workgroup
-                if (ticket) e = hipMemsetAsync(ticket, 0, sizeof(uint32_t), s);
-                if (e == hipSuccess) e = rd::launch_rows(op, p, x, v, part, ticket, out, s);
-                if (e == hipSuccess && !ticket)
-                    e = rd::launch_rows_combine(op, part, nout, p.split, out, s);
+                e = rd::launch_rows(op, p, x, v, part, nullptr, out, s);
+                if (e == hipSuccess) e = rd::launch_rows_combine(op, part, nout, p.split, out, s);
             }
             break;
         case RD_PATH_COLS:

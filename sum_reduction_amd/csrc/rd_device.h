@@ -1,6 +1,7 @@
 // rd_device.h -- device helpers shared by the reduction and the scan kernels:
 // 16-byte (and 8/12-byte) loads and stores at 4-byte alignment, DPP moves,
-// and the XCD-aware workgroup numbering.
+// floats published between the workgroups of a launch, and the XCD-aware
+// workgroup numbering.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -72,6 +73,27 @@ __device__ __forceinline__ float dpp_or_zero(float v) {
     return __builtin_bit_cast(
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask,
                                            0xF, true));
+}
+
+// A float published to other workgroups of the same launch as one 64-bit
+// word, `tag` in the high half and the float's bits in the low half, stored
+// and loaded by relaxed device-scope atomics (with an L2 per XCD these go to
+// memory, sc1): the value travels with its tag, so a reader that sees the tag
+// has the value, and no release / acquire fence -- an L2 write-back per
+// workgroup on MI355X -- is needed.  await_word polls until the word carries
+// `tag`, at most spin_limit + 1 times; a wait that runs out returns NaN.
+__device__ __forceinline__ void publish_word(uint64_t* w, uint32_t tag, float v) {
+    const uint64_t word = (uint64_t(tag) << 32) | uint64_t(__builtin_bit_cast(uint32_t, v));
+    __hip_atomic_store(w, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float await_word(uint64_t* w, uint32_t tag, uint32_t spin_limit) {
+    for (uint32_t it = 0;; ++it) {
+        const uint64_t word = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (uint32_t(word >> 32) == tag) return __builtin_bit_cast(float, uint32_t(word));
+        if (it >= spin_limit) return __builtin_nanf("");
+        __builtin_amdgcn_s_sleep(1);
+    }
 }
 
 // Workgroups are handed to the XCDs round-robin (hardware id b runs on XCD

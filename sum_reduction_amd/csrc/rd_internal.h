@@ -68,11 +68,29 @@ rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op
 // Kernel launchers (rd_kernels.hip).  Each enqueues on `s` and returns the
 // error hipLaunchKernel reports for the launch; `op` is an rd_op.
 hipError_t launch_fill_start(int op, Results out, int64_t n, hipStream_t s);
-// Rows (v.sr == 1): v.outer * v.inner rows.  ticket == nullptr: dst
-// receives the piece results (or the row results when p.split == 1);
-// otherwise the last workgroup also combines them into out.
+// The single-launch combine of a row reduce cut into pieces (one-float
+// operators): every workgroup publishes its piece results as tagged words
+// (publish_word, tag = epoch) at words[seg]; the grid's last workgroup waits
+// for all outer * P of them (await_word: NaN for one that never comes),
+// copies them to vals and combines each row's pieces into out as the second
+// kernel does, with the same bits.  words holds no word tagged `epoch` when
+// the kernel starts (the host gives each launch on a stream a new epoch and
+// the stream its own buffer).
+// Piece results a stream's buffer holds, and the most rows the planner
+// gives the single-launch combine.
+constexpr int64_t kPubWords = 8192;
+constexpr int64_t kPubMaxRows = 4;
+struct Published {
+    uint64_t* words = nullptr;
+    float* vals = nullptr;
+    uint32_t epoch = 0;
+    uint32_t spin_limit = 0;
+};
+// Rows (v.sr == 1): v.outer * v.inner rows.  pub == nullptr: dst receives
+// the piece results (or the row results when p.split == 1); otherwise they
+// are published and the last workgroup combines them into out.
 hipError_t launch_rows(int op, const rd_plan& p, const float* x, const Strides& v,
-                       Results dst, uint32_t* ticket, Results out, hipStream_t s);
+                       Results dst, const Published* pub, Results out, hipStream_t s);
 hipError_t launch_rows_short(int op, const float* x, const Strides& v, Results out,
                              hipStream_t s);
 hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, Results out,

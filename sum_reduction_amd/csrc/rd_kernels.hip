@@ -522,6 +522,21 @@ __device__ __forceinline__ int64_t row_start(const RowMap& m, int64_t o) {
     return a * m.so + (o - a * m.ninner) * m.si;
 }
 
+constexpr int kPubLoads = 16;
+
+// A piece result: stored to dst, or published (one-float operators).
+template <int OP>
+__device__ __forceinline__ void put_piece(typename St<OP>::Out dst, const Published& pub,
+                                          int64_t seg, typename St<OP>::S1 v) {
+    if constexpr (OP != RD_OP_SOFTMAX_DENOM) {
+        if (pub.words != nullptr) {
+            publish_word(pub.words + seg, pub.epoch, v);
+            return;
+        }
+    }
+    St<OP>::put(dst, seg, v);
+}
+
 // ----------------------------------------------------------------- ROWS
 // Each group of G lanes (one wave, or the whole workgroup) reduces one row
 // piece: segment seg = (row o, piece p), o = seg / P, p = seg % P.  With
@@ -534,13 +549,15 @@ __device__ __forceinline__ int64_t row_start(const RowMap& m, int64_t o) {
 //                C = ceil(nvec / P) rounded up to a multiple of G, and its
 //                lane takes p*C + lane, p*C + lane + G, ... (each group streams
 //                one contiguous stretch of memory)
-// Fused combine (ticket != null, P > 1): after storing its piece results,
-// each workgroup publishes them (device-scope release) and takes a ticket
-// from an integer counter; the workgroup that draws the last ticket acquires,
-// joins every row's pieces with combine_row into out[0 .. outer), and resets
-// the counter to 0 for the next call on the same stream.  The counter must
-// be 0 at launch.  Only the ticket is atomic, and the combine order is the
-// second pass's.
+// Single-launch combine (pub.words != null, P > 1, one-float operators):
+// each piece result is published as a tagged word instead of stored to dst,
+// and the grid's last workgroup (hardware id gridDim.x - 1), once its own
+// pieces are done, waits for every word, copies the values to pub.vals and
+// joins every row's pieces with combine_row into out[0 .. outer) -- the
+// second kernel's code, so the same bits.  No other workgroup waits on
+// anything, so the one that waits can always be outlasted: however the
+// workgroups are scheduled, the others finish and publish.  No fence and no
+// counter: the tag (the launch's epoch) travels with each value.
 // At most 5 waves per SIMD: the U loads of a step are all issued before the
 // first fold waits (about 90 VGPRs at U = 16).  Left free to aim at 8 waves,
 // the compiler squeezed the kernel into 64 VGPRs by waiting after every
@@ -552,8 +569,7 @@ void rows_kernel(const float* __restrict__ x,
                                                       RowMap map, int64_t R, int64_t nseg,
                                                       int64_t P, int32_t blocked,
                                                       typename St<OP>::Out dst,
-                                                      uint32_t nxcd,
-                                                      uint32_t* __restrict__ ticket,
+                                                      uint32_t nxcd, Published pub,
                                                       typename St<OP>::Out out) {
     static_assert(G == kWave || G == kBlock, "group is a wave or a workgroup");
     typedef St<OP> T;
@@ -592,30 +608,40 @@ void rows_kernel(const float* __restrict__ x,
         }
         if constexpr (G == kBlock) {
             total = block_reduce<OP>(total, lds);
-            if (threadIdx.x == 0) T::put(dst, seg, total);
+            if (threadIdx.x == 0) put_piece<OP>(dst, pub, seg, total);
             __syncthreads();
         } else {
             total = wave_reduce<OP>(total);
-            if (gl == 0 && seg < nseg) T::put(dst, seg, total);
+            if (gl == 0 && seg < nseg) put_piece<OP>(dst, pub, seg, total);
         }
     }
-    if (ticket != nullptr) {
-        // One release per workgroup, one acquire in the last one: a full
-        // fence in every wave would write back and invalidate the L2 of
-        // each XCD thousands of times under the still-running stream.
-        __shared__ uint32_t last;
-        __syncthreads();  // the workgroup's piece results are stored
-        if (threadIdx.x == 0)
-            last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELEASE,
-                                          __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
-        __syncthreads();
-        if (last) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if constexpr (OP != RD_OP_SOFTMAX_DENOM) {
+        if (pub.words != nullptr && blockIdx.x == gridDim.x - 1) {
+            __syncthreads();  // lds is free again
+            // kPubLoads words in flight per thread; a word not yet tagged
+            // with this launch's epoch is then polled on its own
+            for (int64_t i0 = threadIdx.x; i0 < nseg; i0 += kPubLoads * kBlock) {
+                uint64_t w[kPubLoads];
+#pragma unroll
+                for (int u = 0; u < kPubLoads; ++u) {
+                    const int64_t i = i0 + u * kBlock;
+                    w[u] = i < nseg ? __hip_atomic_load(pub.words + i, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < kPubLoads; ++u) {
+                    const int64_t i = i0 + u * kBlock;
+                    if (i < nseg)
+                        pub.vals[i] = uint32_t(w[u] >> 32) == pub.epoch
+                                          ? __builtin_bit_cast(float, uint32_t(w[u]))
+                                          : await_word(pub.words + i, pub.epoch, pub.spin_limit);
+                }
+            }
+            __syncthreads();  // every value is in vals
             const int64_t outer = nseg / P;
             for (int64_t o = 0; o < outer; ++o)
-                combine_row<OP>(T::at(dst, o * P), P, T::at(out, o), lds);
-            if (threadIdx.x == 0)
-                __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                combine_row<OP>(pub.vals + o * P, P, T::at(out, o), lds);
         }
     }
 }
@@ -1100,7 +1126,7 @@ struct RowsArgs {
     RowMap map;
     int64_t outer, R;
     Results dst;
-    uint32_t* ticket;
+    Published pub;
     Results out;
 };
 
@@ -1109,7 +1135,7 @@ hipError_t rows_go(const rd_plan& p, const RowsArgs& a, hipStream_t s) {
     if constexpr (rows_built(OP, G, U)) {
         return launch(rows_kernel<OP, G, U, NT>, p.blocks, kBlock, s, a.x, a.map, a.R,
                       a.outer * p.split, p.split, int32_t(p.order == RD_ORDER_BLOCKED),
-                      out_of<OP>(a.dst), uint32_t(p.nxcd), a.ticket, out_of<OP>(a.out));
+                      out_of<OP>(a.dst), uint32_t(p.nxcd), a.pub, out_of<OP>(a.out));
     } else {
         return hipErrorInvalidValue;
     }
@@ -1316,8 +1342,10 @@ RowMap row_map(const Strides& v) {
 }
 
 hipError_t launch_rows(int op, const rd_plan& p, const float* x, const Strides& v,
-                       Results dst, uint32_t* ticket, Results out, hipStream_t s) {
-    const RowsArgs a{x, row_map(v), v.outer * v.inner, v.R, dst, ticket, out};
+                       Results dst, const Published* pub, Results out, hipStream_t s) {
+    if (pub && (op == RD_OP_SOFTMAX_DENOM || p.split < 2 || !pub->words || !pub->vals))
+        return hipErrorInvalidValue;
+    const RowsArgs a{x, row_map(v), v.outer * v.inner, v.R, dst, pub ? *pub : Published{}, out};
     RD_BY_OP(op, rows_op, p, a, s)
 }
 

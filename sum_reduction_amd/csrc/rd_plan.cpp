@@ -132,14 +132,21 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
     p->workspace_bytes = P > 1 ? segs * result_bytes(op) : 0;
     p->combine = RD_COMBINE_NONE;
     if (P > 1) {
-        // The second kernel is the default: the fused last-workgroup
-        // combine needs every workgroup to publish its results with a
-        // device-scope release, which on MI355X (an L2 per XCD) writes back
-        // the L2 and costs about 47 ns per workgroup, serialized -- measured
-        // with 128 KB pieces: 1e8 floats 59.7 us with no ticket, 67.4 with a
-        // relaxed one, 200 with a release; 1e9 566 / 663 / 2037 us -- where
-        // a queued second launch costs a few microseconds.
-        const int32_t c = (t && t->combine) ? t->combine : RD_COMBINE_PASS;
+        // A few rows (one-float operators, at most kPubWords pieces in all):
+        // the last workgroup combines the pieces in the same launch, from
+        // results the others publish as tagged words (no fence, no counter;
+        // launch_rows).  Measured on MI355X, us, second kernel -> one launch:
+        // 1e6 floats 13.6 -> 7.8, 1e7 17.1 -> 11.6, 1e8 65.6 -> 63.2, [5,
+        // 1000003] 14.2 -> 12.3.  More rows lose: the one workgroup combines
+        // them one after another ([64, 262144]: 19.8 -> 69.3); so do more
+        // pieces, whose words it reads a round at a time.  (A first version
+        // published the results with a device-scope release, which writes back
+        // an XCD's L2 -- about 47 ns per workgroup, serialized: 1e8 floats
+        // 200 us.)
+        const bool one = op != RD_OP_SOFTMAX_DENOM && outer <= kPubMaxRows &&
+                         outer * P <= kPubWords;
+        const int32_t c = (t && t->combine) ? t->combine
+                                            : (one ? RD_COMBINE_LAST_BLOCK : RD_COMBINE_PASS);
         if (c != RD_COMBINE_PASS && c != RD_COMBINE_LAST_BLOCK) return RD_ERR_INVALID_ARG;
         p->combine = c;
     }

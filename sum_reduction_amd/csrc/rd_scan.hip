@@ -24,8 +24,10 @@
 //              then row_bcast 15 and 31), shifted one lane for the exclusive e
 //   output     (carry + e) + s_j
 //   carry      carry + (the slice total, lane 63's inclusive value)
-// A row cut into pieces (few rows) runs in three kernels: the piece totals
-// (the same chunks, carry only), their exclusive scan in piece order, and the
+// Long rows among few run in one launch by a fixed-order look-back (a
+// workgroup per piece; scan_rows_lookback_kernel).  Shorter rows among very
+// few are cut into pieces and run in three kernels: the piece totals (the
+// same chunks, carry only), their exclusive scan in piece order, and the
 // scan of each piece from its carry.  The column scans (inner > 1) keep the
 // running sums of 4 adjacent columns in a lane and walk R in processing
 // order: 256 columns a wave for wide rows (scan_cols_kernel), several whole
@@ -457,20 +459,6 @@ scan_rows_block_kernel(const float* x, float* out, int64_t outer, int64_t R, int
 // NaN, so a piece that could not get its carry writes NaN, never a wrong
 // finite sum.  x and out may be the same array (each element is loaded and
 // stored by the same lane).
-__device__ __forceinline__ void look_publish(uint64_t* slot, float v) {
-    const uint64_t w = (uint64_t(1) << 32) | uint64_t(__builtin_bit_cast(uint32_t, v));
-    __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float look_await(uint64_t* slot, uint32_t spin_limit) {
-    for (uint32_t it = 0;; ++it) {
-        const uint64_t w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (w >> 32) return __builtin_bit_cast(float, uint32_t(w));
-        if (it >= spin_limit) return __builtin_nanf("");
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
 template <bool REV, int NW, int K, bool NT>
 __global__ __launch_bounds__(NW * kWave, scan_rows_waves_per_simd<K>()) void
 scan_rows_lookback_kernel(const float* x, float* out, int64_t outer, int64_t R, int64_t so,
@@ -526,17 +514,17 @@ scan_rows_lookback_kernel(const float* x, float* out, int64_t outer, int64_t R, 
         float a = 0.f;  // the chunk total, 0 + t_0 + ... + t_{NW-1}
 #pragma unroll
         for (int w = 0; w < NW; ++w) a = a + slots[w];
-        if (lane == 0) look_publish(agg + item, a);
+        if (lane == 0) publish_word(agg + item, 1u, a);
         const int64_t g = j / kLookGroup;
         const int64_t first = g * kLookGroup;
         // this group's earlier chunk totals, lane i <- piece first + i
-        const float ai = first + lane < j ? look_await(agg + o * P + first + lane, spin_limit) : 0.f;
+        const float ai = first + lane < j ? await_word(agg + o * P + first + lane, 1u, spin_limit) : 0.f;
         const float in_group = lane63(wave_scan_inclusive(ai));
         if (j == first + kLookGroup - 1 && j + 1 < P && lane == 0)
-            look_publish(gsum + o * NG + g, in_group + a);
+            publish_word(gsum + o * NG + g, 1u, in_group + a);
         float before = 0.f;  // the earlier groups' totals
         for (int64_t h0 = 0; h0 < g; h0 += kWave) {
-            const float th = h0 + lane < g ? look_await(gsum + o * NG + h0 + lane, spin_limit) : 0.f;
+            const float th = h0 + lane < g ? await_word(gsum + o * NG + h0 + lane, 1u, spin_limit) : 0.f;
             before = before + lane63(wave_scan_inclusive(th));
         }
         if (lane == 0) s_carry = before + in_group;

@@ -156,7 +156,7 @@ def test_fused_combine_matches_second_pass():
                 two = _run_1d_many(ns, dev, "pass")
             with rd.tuning(combine=2, **common):
                 one = _run_1d_many(ns, dev, "last block")
-                # and again: the stream's counter must have been reset
+                # and again: new epochs, the buffer holding the last call's words
                 again = _run_1d_many(ns, dev, "last block again")
             assert two == one == again, (group, order)
     for n, bits in zip(ns, one):
@@ -167,7 +167,7 @@ def test_fused_combine_matches_second_pass():
 
 def test_fused_combine_several_rows_and_streams():
     """Split row sums (few long rows) combined by the last workgroup, on
-    several streams at once: each stream has its own ticket counter."""
+    several streams at once: each stream has a buffer of its own."""
     t = H.torch()
     outer, R = 5, 1_000_003
     a = workloads.small_ints(outer * R, 62)
@@ -185,6 +185,56 @@ def test_fused_combine_several_rows_and_streams():
     t.cuda.synchronize()
     for o in outs:
         assert np.array_equal(o.cpu().numpy(), want)
+
+
+def test_single_launch_combine_by_default_epochs():
+    """The 1D sums whose pieces the last workgroup combines by default, one
+    call after another on one stream, a large one first: each later call
+    finds the buffer holding words of earlier epochs (more of them than it
+    has pieces) and takes only its own.  Bit for bit the second kernel's
+    results."""
+    a = workloads.random(2_000_003, 63, "normal")
+    dev = H.upload(a)
+    ns = [2_000_003, 70_001, 1_000_000, 4097, 2_000_003, 300_000]
+    for n in ns:
+        p = rd.rd_plan_1d(256, n).as_dict()
+        assert p["combine"] == ("last_block" if p["split"] > 1 else "none"), (n, p)
+    one = _run_1d_many(ns, dev, "default")
+    with rd.tuning(combine=1):
+        two = _run_1d_many(ns, dev, "pass")
+    assert one == two
+
+
+_PUB_SPIN = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import torch
+import sum_reduction_amd as rd
+from tests import gpu_helpers as H
+n = 3_000_000
+assert rd.rd_plan_1d(256, n).as_dict()["combine"] == "last_block"
+x = H.upload(np.ones(n, np.float32))
+got = [rd.rd_sum_1d(x).item() for _ in range(30)]
+assert all(g == float(n) or np.isnan(g) for g in got), got
+print("pub-spin-ok", sum(bool(np.isnan(g)) for g in got))
+"""
+
+
+def test_single_launch_combine_wait_limit():
+    """The last workgroup's waits bounded from the host: with
+    RD_TEST_SPIN_LIMIT=0 each unready word is polled once.  Every call ends,
+    with the exact sum or NaN, never a wrong finite value.  (Read once per
+    process: a child process.)"""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, RD_TEST_SPIN_LIMIT="0")
+    res = subprocess.run([sys.executable, "-c", _PUB_SPIN, root], env=env, capture_output=True,
+                         text=True, timeout=240, cwd=root)
+    assert res.returncode == 0 and "pub-spin-ok" in res.stdout, res.stdout + res.stderr[-3000:]
+    H.say(res.stdout.strip())
 
 
 SMALL_INNERS = [2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128]

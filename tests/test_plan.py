@@ -30,8 +30,14 @@ def check_invariants(p, outer, R, inner, cu=CU):
             assert p.workspace_bytes == (4 * outer * p.split if p.split > 1 else 0)
             groups = outer * p.split
             assert p.blocks == min(-(-groups // (256 // p.group)), MAX_BLOCKS)
-            assert d["combine"] == ("pass" if p.split > 1 else "none")
-        assert p.passes == (2 if p.split > 1 else 1)
+            # pieces of at most 4 rows (8192 in all) are combined by the
+            # last workgroup of the one launch, others by a second kernel
+            one = outer <= 4 and outer * p.split <= 8192
+            assert d["combine"] == (("last_block" if one else "pass") if p.split > 1
+                                    else "none")
+            assert p.passes == (2 if p.split > 1 and not one else 1)
+        else:
+            assert p.passes == 1
     if d["path"] in ("cols", "cols_small"):
         # the slabs tile [0, R) with none empty
         assert p.split * p.rows_per_split >= R
@@ -66,6 +72,10 @@ def test_workload_plans():
     assert plans["normal_1e9"]["order"] == "blocked"
     assert plans["normal_1e9"]["combine"] == "pass"
     assert plans["normal_1e9"]["passes"] == 2
+    # 1e6 and 1e8 floats: 61 and 3052 pieces, combined in the same launch
+    for name, P in (("harmonic_1e6", 61), ("uniform_1e8", 3052)):
+        assert (plans[name]["split"], plans[name]["combine"], plans[name]["passes"]) == \
+            (P, "last_block", 1), plans[name]
     assert all(p["nontemporal"] == 1 for p in plans.values())
     # the [128, 4096, 4095] reduce fills the chip without a split along R:
     # 8 waves side by side cover 512 lane-columns (2048 columns), 2 tiles
