@@ -41,10 +41,11 @@
  *   library allocates them stream-ordered on `stream` from a pool of its own
  *   and frees them on the same stream, so concurrent calls on different
  *   streams never share memory.  The partials of a split reduce are summed by
- *   a second kernel in fixed order -- or, for a row sum of at most 4 rows cut
- *   into at most 8192 pieces in all (RD_COMBINE_LAST_BLOCK, the default
- *   there), by the last workgroup of the one kernel: the others publish their
- *   piece sums into a buffer of the stream's own (8192 tagged words and their
+ *   a second kernel in fixed order -- or, for a row reduce of at most 4 rows
+ *   cut into at most 8192 pieces in all (4096 for the softmax pair;
+ *   RD_COMBINE_LAST_BLOCK, the default there), by the last workgroup of the
+ *   one kernel: the others publish their piece results into a buffer of the
+ *   stream's own (8192 tagged words and their
  *   values, 96 KB of device memory per stream and device, created by the
  *   first such call on the stream, kept until the process ends, for up to
  *   256 streams), each word tagged with that launch's epoch, a number the
@@ -365,8 +366,9 @@ typedef enum rd_combine {
     RD_COMBINE_LAST_BLOCK = 2, /* the last workgroup of the first kernel sums
                                   them in the same order, from results the
                                   others publish as tagged words (one launch;
-                                  the default for row sums of at most 4 rows
-                                  and 8192 pieces; see "Workspace" above) */
+                                  the default for row reduces of at most 4
+                                  rows and 8192 piece words; see "Workspace"
+                                  above) */
     RD_COMBINE_LOOKBACK = 3    /* row scans: one launch, a workgroup per row
                                   piece, each piece's carry summed in a fixed
                                   order from totals that earlier pieces

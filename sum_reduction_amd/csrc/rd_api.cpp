@@ -253,8 +253,8 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
         rd_status st = capture_check(s);
         if (st != RD_OK) return st;
         if (injected().alloc) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
-        if (p.path == RD_PATH_ROWS && p.combine == RD_COMBINE_LAST_BLOCK &&
-            op != RD_OP_SOFTMAX_DENOM && v.outer * v.inner * p.split <= kPubWords) {
+        const int64_t words = (op == RD_OP_SOFTMAX_DENOM ? 2 : 1) * v.outer * v.inner * p.split;
+        if (p.path == RD_PATH_ROWS && p.combine == RD_COMBINE_LAST_BLOCK && words <= kPubWords) {
             hipError_t pe = hipSuccess;
             published = stream_pub(dev, s, &pub, &pe);
             if (pe != hipSuccess) return hip_fail(pe, RD_ERR_HIP);

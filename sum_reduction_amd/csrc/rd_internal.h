@@ -68,12 +68,13 @@ rd_status plan_dim(int cu_count, int64_t outer, int64_t R, int64_t inner, int op
 // Kernel launchers (rd_kernels.hip).  Each enqueues on `s` and returns the
 // error hipLaunchKernel reports for the launch; `op` is an rd_op.
 hipError_t launch_fill_start(int op, Results out, int64_t n, hipStream_t s);
-// The single-launch combine of a row reduce cut into pieces (one-float
-// operators): every workgroup publishes its piece results as tagged words
-// (publish_word, tag = epoch) at words[seg]; the grid's last workgroup waits
-// for all outer * P of them (await_word: NaN for one that never comes),
-// copies them to vals and combines each row's pieces into out as the second
-// kernel does, with the same bits.  words holds no word tagged `epoch` when
+// The single-launch combine of a row reduce cut into pieces: every
+// workgroup publishes its piece results as tagged words (publish_word, tag =
+// epoch) at words[seg] (a softmax pair: its maximum there, its sum at
+// words[nseg + seg]); the grid's last workgroup waits for all of them
+// (await_word: NaN for one that never comes), copies them to vals in the
+// same layout and combines each row's pieces into out as the second kernel
+// does, with the same bits.  words holds no word tagged `epoch` when
 // the kernel starts (the host gives each launch on a stream a new epoch and
 // the stream its own buffer).
 // Piece results a stream's buffer holds, and the most rows the planner

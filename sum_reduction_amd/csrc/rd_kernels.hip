@@ -524,17 +524,34 @@ __device__ __forceinline__ int64_t row_start(const RowMap& m, int64_t o) {
 
 constexpr int kPubLoads = 16;
 
-// A piece result: stored to dst, or published (one-float operators).
+// A piece result: stored to dst, or published -- the softmax pair as two
+// words, its maximum at seg and its sum at nseg + seg.
 template <int OP>
 __device__ __forceinline__ void put_piece(typename St<OP>::Out dst, const Published& pub,
-                                          int64_t seg, typename St<OP>::S1 v) {
-    if constexpr (OP != RD_OP_SOFTMAX_DENOM) {
-        if (pub.words != nullptr) {
+                                          int64_t seg, int64_t nseg, typename St<OP>::S1 v) {
+    if (pub.words != nullptr) {
+        if constexpr (OP == RD_OP_SOFTMAX_DENOM) {
+            publish_word(pub.words + seg, pub.epoch, v.m);
+            publish_word(pub.words + nseg + seg, pub.epoch, v.s);
+        } else {
             publish_word(pub.words + seg, pub.epoch, v);
-            return;
         }
+        return;
     }
     St<OP>::put(dst, seg, v);
+}
+
+// The published values copied to vals, as piece results (words per piece:
+// 1, or 2 for the softmax pair).
+template <int OP>
+constexpr int kPieceWords = OP == RD_OP_SOFTMAX_DENOM ? 2 : 1;
+
+template <int OP>
+__device__ __forceinline__ typename St<OP>::Out vals_out(float* vals, int64_t nseg) {
+    if constexpr (OP == RD_OP_SOFTMAX_DENOM)
+        return SmOut{vals, vals + nseg};
+    else
+        return vals;
 }
 
 // ----------------------------------------------------------------- ROWS
@@ -608,41 +625,40 @@ void rows_kernel(const float* __restrict__ x,
         }
         if constexpr (G == kBlock) {
             total = block_reduce<OP>(total, lds);
-            if (threadIdx.x == 0) put_piece<OP>(dst, pub, seg, total);
+            if (threadIdx.x == 0) put_piece<OP>(dst, pub, seg, nseg, total);
             __syncthreads();
         } else {
             total = wave_reduce<OP>(total);
-            if (gl == 0 && seg < nseg) put_piece<OP>(dst, pub, seg, total);
+            if (gl == 0 && seg < nseg) put_piece<OP>(dst, pub, seg, nseg, total);
         }
     }
-    if constexpr (OP != RD_OP_SOFTMAX_DENOM) {
-        if (pub.words != nullptr && blockIdx.x == gridDim.x - 1) {
-            __syncthreads();  // lds is free again
-            // kPubLoads words in flight per thread; a word not yet tagged
-            // with this launch's epoch is then polled on its own
-            for (int64_t i0 = threadIdx.x; i0 < nseg; i0 += kPubLoads * kBlock) {
-                uint64_t w[kPubLoads];
+    if (pub.words != nullptr && blockIdx.x == gridDim.x - 1) {
+        __syncthreads();  // lds is free again
+        // kPubLoads words in flight per thread; a word not yet tagged with
+        // this launch's epoch is then polled on its own
+        const int64_t nw = kPieceWords<OP> * nseg;
+        for (int64_t i0 = threadIdx.x; i0 < nw; i0 += kPubLoads * kBlock) {
+            uint64_t w[kPubLoads];
 #pragma unroll
-                for (int u = 0; u < kPubLoads; ++u) {
-                    const int64_t i = i0 + u * kBlock;
-                    w[u] = i < nseg ? __hip_atomic_load(pub.words + i, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT)
-                                    : 0;
-                }
-#pragma unroll
-                for (int u = 0; u < kPubLoads; ++u) {
-                    const int64_t i = i0 + u * kBlock;
-                    if (i < nseg)
-                        pub.vals[i] = uint32_t(w[u] >> 32) == pub.epoch
-                                          ? __builtin_bit_cast(float, uint32_t(w[u]))
-                                          : await_word(pub.words + i, pub.epoch, pub.spin_limit);
-                }
+            for (int u = 0; u < kPubLoads; ++u) {
+                const int64_t i = i0 + u * kBlock;
+                w[u] = i < nw ? __hip_atomic_load(pub.words + i, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : 0;
             }
-            __syncthreads();  // every value is in vals
-            const int64_t outer = nseg / P;
-            for (int64_t o = 0; o < outer; ++o)
-                combine_row<OP>(pub.vals + o * P, P, T::at(out, o), lds);
+#pragma unroll
+            for (int u = 0; u < kPubLoads; ++u) {
+                const int64_t i = i0 + u * kBlock;
+                if (i < nw)
+                    pub.vals[i] = uint32_t(w[u] >> 32) == pub.epoch
+                                      ? __builtin_bit_cast(float, uint32_t(w[u]))
+                                      : await_word(pub.words + i, pub.epoch, pub.spin_limit);
+            }
         }
+        __syncthreads();  // every value is in vals
+        const typename T::Out part = vals_out<OP>(pub.vals, nseg);
+        const int64_t outer = nseg / P;
+        for (int64_t o = 0; o < outer; ++o) combine_row<OP>(T::at(part, o * P), P, T::at(out, o), lds);
     }
 }
 
@@ -1094,7 +1110,11 @@ constexpr bool unroll_built(int u) { return u == 2 || u == 4 || u == 8 || u == 1
 
 constexpr bool rows_built(int op, int g, int u) {
     if (g != kWave && g != kBlock) return false;
-    return op == RD_OP_SUM ? unroll_built(u) : (u == 8 || u == 16);
+    if (op == RD_OP_SUM) return unroll_built(u);
+    // the other one-float operators also take the shallow 256-lane shapes
+    // the planner gives small inputs
+    if (op != RD_OP_SOFTMAX_DENOM && g == kBlock && (u == 2 || u == 4)) return true;
+    return u == 8 || u == 16;
 }
 
 constexpr bool col_shape_built(int cw, int rw) {
@@ -1343,8 +1363,7 @@ RowMap row_map(const Strides& v) {
 
 hipError_t launch_rows(int op, const rd_plan& p, const float* x, const Strides& v,
                        Results dst, const Published* pub, Results out, hipStream_t s) {
-    if (pub && (op == RD_OP_SOFTMAX_DENOM || p.split < 2 || !pub->words || !pub->vals))
-        return hipErrorInvalidValue;
+    if (pub && (p.split < 2 || !pub->words || !pub->vals)) return hipErrorInvalidValue;
     const RowsArgs a{x, row_map(v), v.outer * v.inner, v.R, dst, pub ? *pub : Published{}, out};
     RD_BY_OP(op, rows_op, p, a, s)
 }

@@ -119,6 +119,20 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
         const int64_t bytes = outer * R * int64_t(sizeof(float));
         const int64_t per_cu = (bytes > kMidInputLo && bytes <= kMidInputHi) ? 8 : 1;
         P = ceil_div(int64_t(cu) * per_cu * groups_per_block, outer);
+        // A few rows too short to give every CU a piece at the default depth
+        // (their pieces combined in the same launch), but long enough to at
+        // a depth of 2 loads: the shallowest depth that does.  Measured on
+        // MI355X, 1D sums, us: 1e6 floats 8.2 (61 pieces of depth 16) -> 7.1
+        // (256 of depth 2), 4e6 8.6 (244, 16) -> 7.7 (256, 8); 1e7 keeps 306
+        // pieces of 16.
+        if (!(t && t->unroll) && p->group == kBlock && outer <= kPubMaxRows &&
+            op != RD_OP_SOFTMAX_DENOM && nvec / (int64_t(p->group) * 2) >= P) {
+            while (cap < P && p->unroll > 2 && rows_shape_supported(op, p->group, p->unroll / 2)) {
+                p->unroll /= 2;
+                cap = nvec / (int64_t(p->group) * p->unroll);
+                if (cap < 1) cap = 1;
+            }
+        }
         if (P < pieces) P = pieces;
         if (P > cap) P = cap;
     } else if (pieces > 1 && outer * R >= kPieceSplitBytes / int64_t(sizeof(float))) {
@@ -132,7 +146,8 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
     p->workspace_bytes = P > 1 ? segs * result_bytes(op) : 0;
     p->combine = RD_COMBINE_NONE;
     if (P > 1) {
-        // A few rows (one-float operators, at most kPubWords pieces in all):
+        // A few rows (at most kPubWords piece words in all, two per softmax
+        // pair):
         // the last workgroup combines the pieces in the same launch, from
         // results the others publish as tagged words (no fence, no counter;
         // launch_rows).  Measured on MI355X, us, second kernel -> one launch:
@@ -143,8 +158,8 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
         // published the results with a device-scope release, which writes back
         // an XCD's L2 -- about 47 ns per workgroup, serialized: 1e8 floats
         // 200 us.)
-        const bool one = op != RD_OP_SOFTMAX_DENOM && outer <= kPubMaxRows &&
-                         outer * P <= kPubWords;
+        const bool one = outer <= kPubMaxRows &&
+                         (op == RD_OP_SOFTMAX_DENOM ? 2 : 1) * outer * P <= kPubWords;
         const int32_t c = (t && t->combine) ? t->combine
                                             : (one ? RD_COMBINE_LAST_BLOCK : RD_COMBINE_PASS);
         if (c != RD_COMBINE_PASS && c != RD_COMBINE_LAST_BLOCK) return RD_ERR_INVALID_ARG;

@@ -72,10 +72,11 @@ def test_workload_plans():
     assert plans["normal_1e9"]["order"] == "blocked"
     assert plans["normal_1e9"]["combine"] == "pass"
     assert plans["normal_1e9"]["passes"] == 2
-    # 1e6 and 1e8 floats: 61 and 3052 pieces, combined in the same launch
-    for name, P in (("harmonic_1e6", 61), ("uniform_1e8", 3052)):
-        assert (plans[name]["split"], plans[name]["combine"], plans[name]["passes"]) == \
-            (P, "last_block", 1), plans[name]
+    # 1e6 and 1e8 floats: 256 pieces of depth 2 and 3052 of depth 16,
+    # combined in the same launch
+    for name, P, U in (("harmonic_1e6", 256, 2), ("uniform_1e8", 3052, 16)):
+        d = plans[name]
+        assert (d["split"], d["unroll"], d["combine"], d["passes"]) == (P, U, "last_block", 1), d
     assert all(p["nontemporal"] == 1 for p in plans.values())
     # the [128, 4096, 4095] reduce fills the chip without a split along R:
     # 8 waves side by side cover 512 lane-columns (2048 columns), 2 tiles
@@ -96,10 +97,17 @@ def test_workload_plans():
 def test_row_pieces():
     """Long rows are cut into pieces of about 32768 floats: always when there
     are fewer rows than CUs, otherwise from 1 GB of input on; never below one
-    full unrolled step (16 x 16 bytes) per lane."""
+    full unrolled step (16 x 16 bytes) per lane -- except that a few rows
+    which a step of 2 loads per lane lets give every CU a piece take the
+    shallowest depth that does."""
     def P(outer, R):
         return rd.rd_plan_dim(CU, outer, R, 1).split
-    assert P(1, 10**6) == 61                 # one step per lane caps it
+    assert P(1, 10**6) == 256                # depth 2 (16 would allow only 61)
+    assert rd.rd_plan_dim(CU, 1, 10**6, 1).unroll == 2
+    assert (P(1, 4 * 10**6), rd.rd_plan_dim(CU, 1, 4 * 10**6, 1).unroll) == (256, 8)
+    assert (P(1, 300_000), rd.rd_plan_dim(CU, 1, 300_000, 1).unroll) == (18, 16)
+    assert rd.rd_plan_dim(CU, 5, 10**6, 1).unroll == 16      # more than 4 rows
+    assert rd.rd_plan_reduce(CU, 1, 10**6, 1, "softmax_denom").unroll == 16
     assert P(1, 10**7) == 306                # ceil(1e7 / 32768) > one per CU
     assert P(1, 10**8) == 3052
     assert P(100, 10**7) == 306
@@ -225,7 +233,9 @@ def test_tuning_override():
     for op in ("sumsq", "max", "min"):
         assert rd.rd_tune_supported("rows", 256, 0, 16, op)
         assert rd.rd_tune_supported("rows", 64, 0, 8, op)
-        assert not rd.rd_tune_supported("rows", 256, 0, 4, op)
+        assert rd.rd_tune_supported("rows", 256, 0, 2, op)   # small inputs' shapes
+        assert rd.rd_tune_supported("rows", 256, 0, 4, op)
+        assert not rd.rd_tune_supported("rows", 64, 0, 4, op)
         for cw in (1, 2, 4, 8):
             assert rd.rd_tune_supported("cols", cw, 1, 4, op)
         assert not rd.rd_tune_supported("cols", 1, 4, 8, op)
