@@ -359,6 +359,19 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
     if (st != RD_OK) return st;
     if (p.path == RD_PATH_NONE) return RD_OK;
     if (injected().launch) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
+    // A look-back plan of one piece per row waits for nothing (its ticket
+    // only orders the rows): on a capturing stream the workgroup-per-row
+    // kernel with the same chunk runs instead, with the same bits and no
+    // workspace.
+    if (p.path == RD_PATH_SCAN_ROWS && p.combine == RD_COMBINE_LOOKBACK && p.split == 1) {
+        st = capture_check(stream);
+        if (st == RD_ERR_CAPTURE) {
+            p.combine = RD_COMBINE_NONE;
+            p.workspace_bytes = 0;
+        } else if (st != RD_OK) {
+            return st;
+        }
+    }
     float* ws = nullptr;
     if (p.workspace_bytes > 0) {
         st = capture_check(stream);

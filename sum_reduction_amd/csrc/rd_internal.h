@@ -203,6 +203,17 @@ constexpr int64_t kScanRowWavesMin = 4;
 constexpr int64_t kScanRowsCutMinR = 131072;
 constexpr int64_t kScanRowsLookMinR = int64_t(1) << 20;
 constexpr int64_t kScanRowsLookMinN = int64_t(1) << 24;
+// Arrays of at least kScanRowsTicketMinBytes whose rows fill an 8-wave
+// chunk take the look-back kernel too: its workgroups take their pieces by a
+// ticket, so all XCDs work on one narrow stretch of the array at a time,
+// where block ids hand each XCD every eighth piece and the XCDs drift apart
+// (same kernel, [32768, 32768]: 1321.5 us by ticket, 1478.5 us by block id;
+// the block-per-row kernel 1524.8 us).  us, before -> after: [4096, 65536]
+// 377.3 -> 348.5, [8192, 131072] 1570.7 -> 1351.9, [30000, 35791] 1663.2 ->
+// 1513.8 (pieces of 16384), [1000, 262144] 367.2 -> 354.6; below 1 GB its
+// fixed costs (zeroing the workspace, the tickets) lose: [256, 262144] 95.9
+// -> 104.7, [512, 262144] 191.1 -> 191.7.
+constexpr int64_t kScanRowsTicketMinBytes = int64_t(1) << 30;
 constexpr int64_t kScanRowWavesSplit = 16;  // pieces per CU once they are cut
 constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan,
 // 16 for slabs of kScanColsDeepRows rows or more (same box, interleaved:

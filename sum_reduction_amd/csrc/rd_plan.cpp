@@ -517,26 +517,43 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         const int32_t comb = t ? t->combine : 0;
         if (comb != 0 && comb != RD_COMBINE_PASS && comb != RD_COMBINE_LOOKBACK)
             return RD_ERR_INVALID_ARG;
-        // Long rows among few (at least kScanRowsLookMinR positions, fewer
-        // than kScanRowWavesMin rows per CU, kScanRowsLookMinN elements in
-        // all) take the look-back: one launch, x read once.
-        const int64_t look_len = int64_t(16) * kWave * 4 * kScanRowsChunkSlices;
+        // The look-back kernel (one launch, x read once, pieces taken in
+        // ticket order) for long rows among few -- at least kScanRowsLookMinR
+        // positions, fewer than kScanRowWavesMin rows per CU,
+        // kScanRowsLookMinN elements in all -- and for every large array of
+        // rows of at least one 8-wave chunk (kScanRowsTicketMinBytes).
+        // Pieces of 32768 positions (16 waves) for the long rows and for rows
+        // made of whole such pieces, else of 16384 (8 waves): a row's partial
+        // last piece idles fewer lanes in a smaller workgroup (measured on
+        // MI355X, us, 8 / 16 waves: [53687, 20000] 1456 / 1882, [40000,
+        // 24000] 1281 / 1524, [65536, 16384] 1359 / 2148; whole pieces:
+        // [8192, 32768] 365 / 348, [2048, 131072] 369 / 356).
+        const int64_t chunk8 = int64_t(8) * kWave * 4 * kScanRowsChunkSlices;
+        const int64_t chunk16 = 2 * chunk8;
         const bool tuned = t && (t->split || t->order || t->group || t->unroll);
-        const bool look = comb == RD_COMBINE_LOOKBACK ||
-                          (comb == 0 && !tuned && outer < cu * kScanRowWavesMin &&
-                           R >= kScanRowsLookMinR && outer * R >= kScanRowsLookMinN &&
-                           ceil_div(R, look_len) <= kMaxBlocks / outer);
+        const bool few_long = outer < cu * kScanRowWavesMin && R >= kScanRowsLookMinR &&
+                              outer * R >= kScanRowsLookMinN;
+        const bool large =
+            R >= chunk8 && outer * R * int64_t(sizeof(float)) >= kScanRowsTicketMinBytes;
+        const int32_t look_group = few_long || R % chunk16 == 0 ? 16 * kWave : 8 * kWave;
+        const bool look =
+            comb == RD_COMBINE_LOOKBACK ||
+            (comb == 0 && !tuned && (few_long || large) &&
+             ceil_div(R, int64_t(look_group / kWave) * kWave * 4 * kScanRowsChunkSlices) <=
+                 kMaxBlocks / outer);
         if (look) {
-            // one launch, a workgroup of 8 or 16 waves per piece of one block
-            // chunk (8 slices a wave), the carries by look-back
-            if (t && (t->split || t->order || (t->unroll && t->unroll != 8)))
+            // one launch, a workgroup of 4, 8 or 16 waves per piece of one
+            // block chunk (4 or 8 slices a wave), the carries by look-back
+            if (t && (t->split || t->order || (t->unroll && t->unroll != 4 && t->unroll != 8)))
                 return RD_ERR_INVALID_ARG;
-            const int32_t group = (t && t->group) ? t->group : 16 * kWave;
-            if (group != 8 * kWave && group != 16 * kWave) return RD_ERR_INVALID_ARG;
-            const int64_t L = int64_t(group / kWave) * kWave * 4 * kScanRowsChunkSlices;
+            const int32_t group = (t && t->group) ? t->group : look_group;
+            const int32_t slices = (t && t->unroll) ? t->unroll : kScanRowsChunkSlices;
+            if (group != 4 * kWave && group != 8 * kWave && group != 16 * kWave)
+                return RD_ERR_INVALID_ARG;
+            const int64_t L = int64_t(group / kWave) * kWave * 4 * slices;
             const int64_t P = ceil_div(R, L);
             if (P > kMaxBlocks / outer) return RD_ERR_INVALID_ARG;
-            p->unroll = kScanRowsChunkSlices;
+            p->unroll = slices;
             p->group = group;
             p->block_threads = group;
             p->split = P;

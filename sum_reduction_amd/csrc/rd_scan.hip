@@ -1496,15 +1496,24 @@ hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, floa
                    : rows_go<false>(p, x, out, v, carry_in, totals, s);
 }
 
+template <bool REV, int NW, int K>
+hipError_t lookback_k(const rd_plan& p, const float* x, float* out, const Strides& v,
+                      uint32_t* ticket, uint64_t* agg, uint64_t* gsum, int64_t NG,
+                      uint32_t spin_limit, hipStream_t s) {
+    if (p.nontemporal)
+        return launch(scan_rows_lookback_kernel<REV, NW, K, true>, p.blocks, NW * kWave, s, x,
+                      out, v.outer, v.R, v.so, p.split, NG, ticket, agg, gsum, spin_limit);
+    return launch(scan_rows_lookback_kernel<REV, NW, K, false>, p.blocks, NW * kWave, s, x, out,
+                  v.outer, v.R, v.so, p.split, NG, ticket, agg, gsum, spin_limit);
+}
+
 template <bool REV, int NW>
 hipError_t lookback_go(const rd_plan& p, const float* x, float* out, const Strides& v,
                        uint32_t* ticket, uint64_t* agg, uint64_t* gsum, int64_t NG,
                        uint32_t spin_limit, hipStream_t s) {
-    if (p.nontemporal)
-        return launch(scan_rows_lookback_kernel<REV, NW, 8, true>, p.blocks, NW * kWave, s, x,
-                      out, v.outer, v.R, v.so, p.split, NG, ticket, agg, gsum, spin_limit);
-    return launch(scan_rows_lookback_kernel<REV, NW, 8, false>, p.blocks, NW * kWave, s, x, out,
-                  v.outer, v.R, v.so, p.split, NG, ticket, agg, gsum, spin_limit);
+    if (p.unroll == 4)
+        return lookback_k<REV, NW, 4>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+    return lookback_k<REV, NW, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
 }
 
 hipError_t launch_scan_rows_lookback(const rd_plan& p, bool reverse, const float* x, float* out,
@@ -1512,8 +1521,9 @@ hipError_t launch_scan_rows_lookback(const rd_plan& p, bool reverse, const float
                                      hipStream_t s) {
     const int64_t NG = lookback_groups(p.split);
     const int nw = p.group / kWave;
-    if (p.combine != RD_COMBINE_LOOKBACK || p.unroll != 8 || (nw != 8 && nw != 16) ||
-        p.rows_per_split != int64_t(nw) * 256 * 8 || p.blocks != v.outer * p.split ||
+    if (p.combine != RD_COMBINE_LOOKBACK || (p.unroll != 4 && p.unroll != 8) ||
+        (nw != 4 && nw != 8 && nw != 16) ||
+        p.rows_per_split != int64_t(nw) * 256 * p.unroll || p.blocks != v.outer * p.split ||
         p.workspace_bytes != lookback_workspace_bytes(v.outer, p.split) || ws == nullptr)
         return hipErrorInvalidValue;
     hipError_t e = hipMemsetAsync(ws, 0, size_t(p.workspace_bytes), s);
@@ -1522,11 +1532,14 @@ hipError_t launch_scan_rows_lookback(const rd_plan& p, bool reverse, const float
     uint32_t* ticket = reinterpret_cast<uint32_t*>(base);
     uint64_t* agg = reinterpret_cast<uint64_t*>(base + kLookTicketBytes);
     uint64_t* gsum = agg + v.outer * p.split;
-    if (reverse)
-        return nw == 8 ? lookback_go<true, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s)
-                       : lookback_go<true, 16>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
-    return nw == 8 ? lookback_go<false, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s)
-                   : lookback_go<false, 16>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+    switch ((reverse ? 100 : 0) + nw) {
+        case 104: return lookback_go<true, 4>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+        case 108: return lookback_go<true, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+        case 116: return lookback_go<true, 16>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+        case 4: return lookback_go<false, 4>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+        case 8: return lookback_go<false, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+        default: return lookback_go<false, 16>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+    }
 }
 
 hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows, int64_t P,

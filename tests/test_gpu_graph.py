@@ -97,6 +97,35 @@ def test_capture_refuses_workspace_plans():
     assert float(y.sum()) == 3.0 * 16
 
 
+def test_large_row_scan_captures_as_one_kernel():
+    """A row scan whose plan is the look-back kernel with one piece per row
+    (an array of 1 GiB) needs a workspace only for its ticket: on a
+    capturing stream the workgroup-per-row kernel with the same chunk runs
+    instead, and its replays give the eager call's bits."""
+    t = H.torch()
+    o, r = 8192, 32768
+    p = rd.rd_plan_cumsum(256, o, r, 1)
+    assert p.as_dict()["combine"] == "lookback" and p.split == 1
+    x = H.upload(workloads.random(o * r, 2002, "normal"))
+    out = t.empty(o * r, device="cuda")
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(s):
+        rd.rd_cumsum_dim(x, o, r, 1, reverse=True, out=out)   # set-up outside the capture
+    t.cuda.current_stream().wait_stream(s)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        rd.rd_cumsum_dim(x, o, r, 1, reverse=True, out=out)
+    for rep in range(3):
+        x.mul_(1.5).add_(0.25)
+        g.replay()
+        t.cuda.synchronize()
+        want = rd.rd_cumsum_dim(x, o, r, 1, reverse=True)   # eager: the look-back kernel
+        t.cuda.synchronize()
+        assert t.equal(out.view(t.int32), want.view(t.int32)), rep
+
+
 def test_single_kernel_plans_replay():
     """Calls whose plan is one kernel and no workspace (a column reduce, a row
     reduce with a workgroup per row, a cumulative sum of uncut rows) capture

@@ -336,21 +336,24 @@ def test_columns_full_size():
         t.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("group", [512, 1024])
-def test_rows_lookback(group):
+LOOK_SHAPES = [(g, k) for g in (256, 512, 1024) for k in (4, 8)]
+
+
+@pytest.mark.parametrize("group,slices", LOOK_SHAPES, ids=["g%d_k%d" % t for t in LOOK_SHAPES])
+def test_rows_lookback(group, slices):
     """Rows in one launch, a workgroup per piece of one block chunk, each
     piece's carry formed from the totals earlier pieces publish: rows of one
     and of several pieces, around the chunk, more pieces than a group of 64
     (group totals), misaligned bases, both directions; integer data, bit for
     bit."""
-    L = group // 64 * 2048
+    L = group // 64 * 256 * slices
     shapes = [(3, 1, 1), (3, 5, 1), (2, 4096, 1), (2, L - 1, 1), (2, L, 1), (2, L + 1, 1),
               (5, 3 * L + 17, 1), (1, 64 * L, 1), (1, 65 * L + 7, 1), (2, 130 * L + 3, 1)]
-    with rd.tuning(combine=3, group=group):
+    with rd.tuning(combine=3, group=group, unroll=slices):
         for o, r, i in shapes:
             p = rd.rd_plan_cumsum(256, o, r, i)
             assert (p.combine, p.split, p.passes, p.rows_per_split) == (3, -(-r // L), 1, L)
-        _sweep(shapes, [0, 3], 900 + group, "scan lookback g%d" % group)
+        _sweep(shapes, [0, 3], 900 + group + slices, "scan lookback g%d k%d" % (group, slices))
 
 
 def test_rows_lookback_default_plans():
@@ -360,6 +363,17 @@ def test_rows_lookback_default_plans():
         p = rd.rd_plan_cumsum(256, *shape)
         assert p.as_dict()["combine"] == "lookback" and p.group == 1024, (shape, p.as_dict())
     _sweep(shapes, [0, 1], 905, "scan lookback default")
+
+
+def test_rows_lookback_large_arrays():
+    """Arrays of 1 GiB and more take the look-back kernel by default, rows in
+    ticket order: whole 32768-position rows (one piece each), and rows with
+    a partial last piece of 16384 (8 waves); integer data, bit for bit."""
+    shapes = [(8192, 32768, 1), (10_000, 27_000, 1)]
+    for (o, r, i), (group, P) in zip(shapes, ((1024, 1), (512, 2))):
+        p = rd.rd_plan_cumsum(256, o, r, i)
+        assert (p.combine, p.group, p.split) == (3, group, P), p.as_dict()
+    _sweep(shapes, [0], 906, "scan lookback large", reverse_modes=(True,))
 
 
 def test_rows_lookback_many_groups():

@@ -268,14 +268,18 @@ def _scan_invariants(p, outer, R, inner, cu=CU):
     assert p.split * p.rows_per_split >= R > (p.split - 1) * p.rows_per_split
     if inner == 1:
         assert p.rows_per_split % 4096 == 0           # whole tiles per piece
-        look = outer < 4 * cu and R >= 1 << 20 and outer * R >= 1 << 24 and \
-            -(-R // 32768) <= (1 << 20) // outer
+        few_long = outer < 4 * cu and R >= 1 << 20 and outer * R >= 1 << 24
+        large = R >= 16384 and outer * R * 4 >= 1 << 30
+        L = 32768 if few_long or R % 32768 == 0 else 16384
+        look = (few_long or large) and -(-R // L) <= (1 << 20) // outer
         assert (p.combine == 3) == look, (outer, R, cu, p.as_dict())
         if look:
-            # one launch, a workgroup of 16 waves per 32768 positions, the
-            # carries by look-back: ticket, chunk totals, group totals
-            assert (p.group, p.block_threads, p.rows_per_split, p.passes) == (1024, 1024, 32768, 1)
-            assert p.split == -(-R // 32768) and p.blocks == outer * p.split
+            # one launch, a workgroup of 16 waves per 32768 positions (or 8
+            # per 16384), the carries by look-back: ticket, chunk totals,
+            # group totals
+            assert (p.group, p.block_threads, p.rows_per_split, p.passes) == \
+                (L // 32, L // 32, L, 1)
+            assert p.split == -(-R // L) and p.blocks == outer * p.split
             assert p.workspace_bytes == 256 + 8 * outer * (p.split + -(-p.split // 64))
             return
         # pieces only for fewer rows than a third of the CUs, each of at
@@ -333,10 +337,11 @@ def _scan_invariants(p, outer, R, inner, cu=CU):
 def test_cumsum_row_widths_at_their_edges():
     """Uncut rows: a wave per row up to 16384 positions, a workgroup of 8
     waves above, of 16 from 65536 on (two of its 32768-position chunks);
-    rows cut into pieces stay a wave per piece."""
+    rows cut into pieces stay a wave per piece.  (2048 rows: under 1 GB,
+    below the look-back kernel's arrays.)"""
     for R, group in ((4096, 64), (16384, 64), (16385, 512), (32768, 512), (65535, 512),
-                     (65536, 1024), (1 << 20, 1024)):
-        p = rd.rd_plan_cumsum(CU, 4096, R, 1)
+                     (65536, 1024), (100_000, 1024)):
+        p = rd.rd_plan_cumsum(CU, 2048, R, 1)
         assert p.split == 1 and p.group == group, (R, p.as_dict())
         assert p.block_threads == max(group, 256)
     p = rd.rd_plan_cumsum(CU, 16, 1 << 19, 1)   # 16 rows of 2^19: cut into pieces
@@ -379,10 +384,15 @@ def test_cumsum_plans():
     rows take a workgroup each.
     Columns: a wave per 64 lane-columns, slabs of R when there are too few
     waves."""
-    p = rd.rd_plan_cumsum(CU, 32768, 32768, 1)
+    p = rd.rd_plan_cumsum(CU, 32768, 32768, 1)   # 4 GB: rows in ticket order
     assert p.as_dict()["path"] == "scan_rows" and p.split == 1 and p.blocks == 32768
-    assert p.group == 512 and p.block_threads == 512 and p.unroll == 8
-    assert p.workspace_bytes == 0
+    assert p.as_dict()["combine"] == "lookback" and p.rows_per_split == 32768
+    assert p.group == 1024 and p.block_threads == 1024 and p.unroll == 8
+    assert p.workspace_bytes == 256 + 8 * 32768 * 2
+    p = rd.rd_plan_cumsum(CU, 8000, 32768, 1)    # under 1 GiB: a workgroup per row
+    assert p.split == 1 and p.group == 512 and p.workspace_bytes == 0
+    p = rd.rd_plan_cumsum(CU, 30000, 35791, 1)   # a partial last piece: 8 waves
+    assert (p.combine, p.group, p.split, p.rows_per_split) == (3, 512, 3, 16384)
     p = rd.rd_plan_cumsum(CU, 1, 1 << 20, 1)
     assert p.split == 256 and p.rows_per_split == 4096 and p.passes == 3
     p = rd.rd_plan_cumsum(CU, 64, 131072, 1)              # 64 * 3 < 256 CUs
