@@ -205,6 +205,44 @@ def test_single_launch_combine_by_default_epochs():
     assert one == two
 
 
+def test_single_launch_combine_from_threads():
+    """Eight host threads, four streams (two threads on each): every thread
+    runs 1D sums of its own size in the single launch, on its stream, and
+    checks each against the oracle's exact integer sum.  Calls on one stream
+    from two threads take epochs in whatever order they arrive; calls on
+    different streams use different buffers."""
+    import threading
+    t = H.torch()
+    streams = [t.cuda.Stream() for _ in range(4)]
+    sizes = [1_000_000 + 7919 * k for k in range(8)]
+    data = [workloads.small_ints(n, 70 + k) for k, n in enumerate(sizes)]
+    want = [float(a.astype(np.int64).sum()) for a in data]
+    devs = [H.upload(a) for a in data]
+    t.cuda.synchronize()
+    errors = []
+
+    def work(k):
+        try:
+            with t.cuda.stream(streams[k % 4]):
+                for _ in range(40):
+                    got = rd.rd_sum_1d(devs[k])
+                    t.cuda.current_stream().synchronize()
+                    if got.item() != want[k]:
+                        errors.append((k, got.item(), want[k]))
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append((k, repr(e)))
+
+    for n in sizes:
+        assert rd.rd_plan_1d(256, n).as_dict()["combine"] == "last_block"
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads)
+    assert errors == [], errors[:5]
+
+
 _PUB_SPIN = r"""
 import sys
 sys.path.insert(0, sys.argv[1])
