@@ -243,6 +243,27 @@ def test_single_launch_combine_from_threads():
     assert errors == [], errors[:5]
 
 
+def test_single_launch_combine_special_values():
+    """A NaN or an Inf in one piece reaches the single-launch sum; the
+    maximum and minimum keep IEEE 754-2019 semantics through the words."""
+    n = 3_000_000
+    assert rd.rd_plan_1d(256, n).as_dict()["combine"] == "last_block"
+    a = np.ones(n, np.float32)
+    a[2_500_000] = np.inf
+    assert rd.rd_sum_1d(H.upload(a)).item() == np.inf
+    a[100] = -np.inf
+    assert np.isnan(rd.rd_sum_1d(H.upload(a)).item())
+    b = np.zeros(n, np.float32)
+    b[1_234_567] = np.nan
+    assert np.isnan(rd.rd_sum_1d(H.upload(b)).item())
+    assert np.isnan(rd.reduce(H.upload(b), "max").item())
+    c = np.full(n, -1.0, np.float32)
+    c[2_999_999] = -0.0
+    c[17] = 0.0
+    got = rd.reduce(H.upload(c), "max").item()
+    assert got == 0.0 and not np.signbit(got)
+
+
 _PUB_SPIN = r"""
 import sys
 sys.path.insert(0, sys.argv[1])

@@ -376,6 +376,24 @@ def test_rows_lookback_large_arrays():
     _sweep(shapes, [0], 906, "scan lookback large", reverse_modes=(True,))
 
 
+def test_rows_lookback_special_values():
+    """A NaN or Inf crosses pieces by the published totals: it reaches every
+    output after it in processing order, in its own row only."""
+    R = 5 * 16384 + 9
+    a = np.ones((3, R), np.float32)
+    a[1, 20000] = np.nan            # in the second of six 16384-position pieces
+    a[2, R - 100] = np.inf          # in the last piece
+    with rd.tuning(combine=3, group=512):
+        fwd = rd.rd_cumsum_dim(H.upload(a), 3, R, 1, reverse=False).cpu().numpy().reshape(3, R)
+        rev = rd.rd_cumsum_dim(H.upload(a), 3, R, 1, reverse=True).cpu().numpy().reshape(3, R)
+    assert np.array_equal(fwd[0], np.arange(1, R + 1, dtype=np.float32))
+    assert np.isfinite(fwd[1, :20000]).all() and np.isnan(fwd[1, 20000:]).all()
+    assert np.isfinite(fwd[2, :R - 100]).all() and np.isinf(fwd[2, R - 100:]).all()
+    assert np.isnan(rev[1, :20001]).all() and np.isfinite(rev[1, 20001:]).all()
+    assert np.isinf(rev[2, :R - 99]).all() and np.isfinite(rev[2, R - 99:]).all()
+    assert np.array_equal(rev[0], np.arange(R, 0, -1, dtype=np.float32))
+
+
 def test_rows_lookback_many_groups():
     """More than 64 group totals before a piece: they are read 64 at a time."""
     shape = (1, 4097 * 16384 + 3, 1)
