@@ -212,7 +212,9 @@ constexpr int64_t kScanRowsLookMinN = int64_t(1) << 24;
 // 377.3 -> 348.5, [8192, 131072] 1570.7 -> 1351.9, [30000, 35791] 1663.2 ->
 // 1513.8 (pieces of 16384), [1000, 262144] 367.2 -> 354.6; below 1 GB its
 // fixed costs (zeroing the workspace, the tickets) lose: [256, 262144] 95.9
-// -> 104.7, [512, 262144] 191.1 -> 191.7.
+// -> 104.7, [512, 262144] 191.1 -> 191.7 -- except for rows of whole
+// 32768-position pieces, which gain from 512 MB on ([4096, 32768] 188.9 ->
+// 179.9, [1024, 131072] 196.3 -> 187.4; [2048, 32768] 94.9 -> 99.9).
 constexpr int64_t kScanRowsTicketMinBytes = int64_t(1) << 30;
 constexpr int64_t kScanRowWavesSplit = 16;  // pieces per CU once they are cut
 constexpr int kScanColsUnroll = 8;        // rows per load group of the column scan,

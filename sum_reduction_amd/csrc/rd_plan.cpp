@@ -521,7 +521,8 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         // ticket order) for long rows among few -- at least kScanRowsLookMinR
         // positions, fewer than kScanRowWavesMin rows per CU,
         // kScanRowsLookMinN elements in all -- and for every large array of
-        // rows of at least one 8-wave chunk (kScanRowsTicketMinBytes).
+        // rows of at least one 8-wave chunk (kScanRowsTicketMinBytes; half of
+        // that for rows of whole 32768-position pieces).
         // Pieces of 32768 positions (16 waves) for the long rows and for rows
         // made of whole such pieces, else of 16384 (8 waves): a row's partial
         // last piece idles fewer lanes in a smaller workgroup (measured on
@@ -533,8 +534,9 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         const bool tuned = t && (t->split || t->order || t->group || t->unroll);
         const bool few_long = outer < cu * kScanRowWavesMin && R >= kScanRowsLookMinR &&
                               outer * R >= kScanRowsLookMinN;
-        const bool large =
-            R >= chunk8 && outer * R * int64_t(sizeof(float)) >= kScanRowsTicketMinBytes;
+        const bool large = R >= chunk8 && outer * R * int64_t(sizeof(float)) >=
+                                              (R % chunk16 == 0 ? kScanRowsTicketMinBytes / 2
+                                                                : kScanRowsTicketMinBytes);
         const int32_t look_group = few_long || R % chunk16 == 0 ? 16 * kWave : 8 * kWave;
         const bool look =
             comb == RD_COMBINE_LOOKBACK ||

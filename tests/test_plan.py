@@ -269,7 +269,7 @@ def _scan_invariants(p, outer, R, inner, cu=CU):
     if inner == 1:
         assert p.rows_per_split % 4096 == 0           # whole tiles per piece
         few_long = outer < 4 * cu and R >= 1 << 20 and outer * R >= 1 << 24
-        large = R >= 16384 and outer * R * 4 >= 1 << 30
+        large = R >= 16384 and outer * R * 4 >= (1 << 29 if R % 32768 == 0 else 1 << 30)
         L = 32768 if few_long or R % 32768 == 0 else 16384
         look = (few_long or large) and -(-R // L) <= (1 << 20) // outer
         assert (p.combine == 3) == look, (outer, R, cu, p.as_dict())
@@ -341,7 +341,7 @@ def test_cumsum_row_widths_at_their_edges():
     below the look-back kernel's arrays.)"""
     for R, group in ((4096, 64), (16384, 64), (16385, 512), (32768, 512), (65535, 512),
                      (65536, 1024), (100_000, 1024)):
-        p = rd.rd_plan_cumsum(CU, 2048, R, 1)
+        p = rd.rd_plan_cumsum(CU, 1024, R, 1)
         assert p.split == 1 and p.group == group, (R, p.as_dict())
         assert p.block_threads == max(group, 256)
     p = rd.rd_plan_cumsum(CU, 16, 1 << 19, 1)   # 16 rows of 2^19: cut into pieces
@@ -389,8 +389,12 @@ def test_cumsum_plans():
     assert p.as_dict()["combine"] == "lookback" and p.rows_per_split == 32768
     assert p.group == 1024 and p.block_threads == 1024 and p.unroll == 8
     assert p.workspace_bytes == 256 + 8 * 32768 * 2
-    p = rd.rd_plan_cumsum(CU, 8000, 32768, 1)    # under 1 GiB: a workgroup per row
+    p = rd.rd_plan_cumsum(CU, 4000, 32768, 1)    # under 512 MiB: a workgroup per row
     assert p.split == 1 and p.group == 512 and p.workspace_bytes == 0
+    p = rd.rd_plan_cumsum(CU, 4096, 32768, 1)    # 512 MiB of whole pieces: ticket order
+    assert p.as_dict()["combine"] == "lookback" and p.group == 1024
+    p = rd.rd_plan_cumsum(CU, 8192, 16384, 1)    # 512 MiB, 16384: the workgroup per row
+    assert p.as_dict()["combine"] == "none"
     p = rd.rd_plan_cumsum(CU, 30000, 35791, 1)   # a partial last piece: 8 waves
     assert (p.combine, p.group, p.split, p.rows_per_split) == (3, 512, 3, 16384)
     p = rd.rd_plan_cumsum(CU, 1, 1 << 20, 1)
