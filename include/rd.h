@@ -281,12 +281,17 @@ rd_status rd_softmax_denom_strided(const float* x, int64_t outer, int64_t R, int
  *   outer, R, inner  >= 0, with outer*R*inner*4 representable in int64
  *   reverse 0 or not
  *   stream  HIP stream of the current device, 0 for the null stream
- * Returns RD_OK once the work is enqueued (one kernel, or three when there
- * are too few rows or columns to fill the GPU: totals, their carries, the
- * scan); RD_ERR_INVALID_ARG, RD_ERR_NO_DEVICE, RD_ERR_ALLOC (the totals of a
- * split scan), RD_ERR_LAUNCH as for the reductions, out untouched.  fp32
- * adds in a fixed order (bitwise reproducible); each output is within the
- * fp32 rounding of its terms, like the reductions.  Source: POPCORNBENCH
+ * Returns RD_OK once the work is enqueued (one kernel; three when there are
+ * too few rows or columns to fill the GPU: totals, their carries, the scan;
+ * for large arrays of rows and for long rows among few, a zeroing of the
+ * look-back workspace and one kernel -- see rd_plan_cumsum);
+ * RD_ERR_INVALID_ARG, RD_ERR_NO_DEVICE, RD_ERR_ALLOC (the totals of a split
+ * scan, the look-back workspace), RD_ERR_CAPTURE (a plan with a workspace,
+ * on a capturing stream: see "Workspace" above -- a look-back plan of one
+ * piece per row runs the workgroup-per-row kernel there, with the same bits
+ * and no workspace), RD_ERR_LAUNCH as for the reductions, out untouched.
+ * fp32 adds in a fixed order (bitwise reproducible); each output is within
+ * the fp32 rounding of its terms, like the reductions.  Source: POPCORNBENCH
  * Kimi-K2.6 level-1 problem 91 trace (reverse cumulative sum of a
  * [32768, 32768] array along dim 1, y = cumsum(x.flip(1), 1).flip(1), spelled
  * out as y[i][j] = x[i][j] + ... + x[i][N-1]).
