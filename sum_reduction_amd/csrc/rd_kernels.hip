@@ -39,7 +39,10 @@
 //            workgroup of the first.
 //  COLS      wave (cw, rw) folds its k-th row, r0 + rw + k*RW, into float4
 //            accumulator (k mod 2); join(acc[0], acc[1]); then the row phases
-//            in rw order; then (if split) the slabs in slab order.
+//            in rw order; then (if split) the slabs in slab order -- or, with
+//            64 slabs or more and at most 256 outputs, lane l of a wave joins
+//            slabs l, l + 64, ... and the wave butterfly joins the lanes (the
+//            same for COLS_SMALL and STRIDED slabs).
 //  COLS_SMALL  row phase rho folds its k-th row into accumulator (k mod 2);
 //            join(acc[0], acc[1]); then the row phases by a fixed tree (see
 //            cols_small_kernel); then (if split) the slabs in slab order.
@@ -1062,6 +1065,30 @@ __global__ __launch_bounds__(kBlock) void slab_combine_kernel(typename St<OP>::O
     }
 }
 
+// The same for few outputs and many slabs (kSlabWaveMinS or more): a wave
+// per output, lane l joining slabs l, l + 64, l + 128, ... in that order,
+// then the wave's butterfly (wave_reduce) -- a fixed order, with every lane
+// holding at least one slab.  A thread per output would walk all S slabs
+// one after another.
+constexpr int64_t kSlabWaveMinS = kWave;
+constexpr int64_t kSlabWaveMaxN = 256;
+
+template <int OP>
+__global__ __launch_bounds__(kBlock) void slab_combine_wave_kernel(typename St<OP>::Out slab,
+                                                                   int64_t S, int64_t n,
+                                                                   typename St<OP>::Out out) {
+    typedef St<OP> T;
+    const int lane = threadIdx.x % kWave;
+    const int64_t waves = int64_t(gridDim.x) * (kBlock / kWave);
+    for (int64_t e = int64_t(blockIdx.x) * (kBlock / kWave) + wave_in_block(); e < n;
+         e += waves) {
+        typename T::S1 t = T::get(slab, int64_t(lane) * n + e);
+        for (int64_t s = lane + kWave; s < S; s += kWave) t = T::join(t, T::get(slab, s * n + e));
+        t = wave_reduce<OP>(t);
+        if (lane == 0) T::put(out, e, t);
+    }
+}
+
 // R == 0: every output is the operator's start value.
 template <int OP>
 __global__ __launch_bounds__(kBlock) void fill_start_kernel(typename St<OP>::Out out,
@@ -1333,6 +1360,9 @@ hipError_t cols_small_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
 
 template <int OP>
 hipError_t slab_combine_go(Results slab, int64_t S, int64_t n, Results out, hipStream_t s) {
+    if (S >= kSlabWaveMinS && n <= kSlabWaveMaxN)
+        return launch(slab_combine_wave_kernel<OP>, (n + kBlock / kWave - 1) / (kBlock / kWave),
+                      kBlock, s, out_of<OP>(slab), S, n, out_of<OP>(out));
     return launch(slab_combine_kernel<OP>, grid_for(n), kBlock, s, out_of<OP>(slab), S, n,
                   out_of<OP>(out));
 }
