@@ -1153,6 +1153,8 @@ constexpr bool col_shape_built(int cw, int rw) {
 
 constexpr bool cols_built(int op, int cw, int rw, int u) {
     if (op == RD_OP_SUM) return col_shape_built(cw, rw) && unroll_built(u);
+    // the planner's shapes: wide tiles, or one tile with 8 row waves in slabs
+    if (cw == 1 && rw == 8 && u == 4) return true;
     if (op == RD_OP_SOFTMAX_DENOM)
         return rw == 1 && (cw == 1 || cw == 2 || cw == 4 || cw == 8) && (u == 4 || u == 8);
     return rw == 1 && (cw == 1 || cw == 2 || cw == 4 || cw == 8) && u == 4;

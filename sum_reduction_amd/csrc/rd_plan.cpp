@@ -51,6 +51,16 @@ constexpr int kColsUnroll = 4;
 // [262144, 64, 8] 128 -> 115 against a wave per item).
 constexpr int64_t kTinyItemBlocksPerCu = 64;
 constexpr int kColsMaxColWaves = 8;
+// Columns too few for single-wave tiles to give every CU a workgroup are cut
+// into slabs of R; there, blocks of one tile and kColsSlabRowWaves waves
+// taking turns on its rows, with no more blocks than CUs, beat wide tiles
+// (measured on MI355X, us, wide 8-wave tiles in ~CU blocks -> one-wave tiles
+// x 8 row waves in floor(CU / tiles) slabs: [1, 262144, 512] 301 -> 113,
+// [2, 65536, 1024] 138 -> 95, [4, 8192, 2048] 67 -> 51, [1, 4096, 10922] 62
+// -> 37, [1, 32768, 32768] 650 -> 622, [1, 1000000, 200] 136 -> 129; and a
+// grid just past the CU count pays for a second round: [1, 4096, 10922] in
+// 258 blocks 50 us against 37 in 215).
+constexpr int kColsSlabRowWaves = 8;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -242,15 +252,26 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int64_t inn
     const int64_t lane_cols = ceil_div(inner, 4);
     // Wide tiles: every tile edge inside a row is a cache line that two
     // workgroups fetch.  Take the widest tile the row has columns for (up to
-    // 8 waves) that still gives every CU a workgroup; if no width does,
-    // keep the widest and let the split along R fill the chip.
+    // 8 waves) that still gives every CU a workgroup; if no width does, the
+    // split along R fills the chip (kColsSlabRowWaves).
     int32_t widest = kColsMaxColWaves;
     while (widest > 1 && lane_cols <= int64_t(widest / 2) * kWave) widest /= 2;
     int32_t cw = widest;
     while (cw > 1 && ceil_div(lane_cols, int64_t(cw) * kWave) * outer < cu) cw /= 2;
-    if (ceil_div(lane_cols, int64_t(cw) * kWave) * outer < cu) cw = widest;
+    int32_t rw = 1;
+    // even single-wave tiles leave CUs without a workgroup: R is cut into
+    // slabs, each block one tile with row waves (widest tiles if that shape
+    // is not built for op)
+    const bool slabs = ceil_div(lane_cols, int64_t(cw) * kWave) * outer < cu;
+    if (slabs) {
+        if (cols_shape_supported(op, 1, kColsSlabRowWaves, kColsUnroll))
+            rw = kColsSlabRowWaves;
+        else
+            cw = widest;
+    }
+    const bool own_shape = !(t && (t->col_waves || t->row_waves || t->unroll));
     p->col_waves = (t && t->col_waves) ? t->col_waves : cw;
-    p->row_waves = (t && t->row_waves) ? t->row_waves : 1;
+    p->row_waves = (t && t->row_waves) ? t->row_waves : rw;
     p->unroll = (t && t->unroll) ? t->unroll : kColsUnroll;
     if (!cols_shape_supported(op, p->col_waves, p->row_waves, p->unroll))
         return RD_ERR_INVALID_ARG;
@@ -262,6 +283,13 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int64_t inn
     int64_t S = 1;
     if (t && t->split) {
         S = t->split;
+    } else if (slabs && own_shape && rw > 1) {
+        // as many slabs as keep the blocks within one per CU, each with at
+        // least one full step of U rows per row wave
+        S = cu / base > 1 ? cu / base : 1;
+        int64_t cap = R / (int64_t(rw) * p->unroll);
+        if (cap < 1) cap = 1;
+        if (S > cap) S = cap;
     } else {
         // loads in flight over the chip without a split, in lane-waves x U:
         // base * per, compared as base < ceil(want / per) so that the

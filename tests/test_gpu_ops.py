@@ -113,6 +113,28 @@ def test_cols_kernel_shapes(op, cw, split, nt):
         _sweep_dim(op, shapes, [0, 1, 2, 3], 740 + cw + split, "cols")
 
 
+# Columns too few for one-wave tiles to give every CU a workgroup: the
+# default plan is one tile a block with 8 row waves, in slabs of R (ragged
+# last slab, partial tiles, rows of 4095 floats).
+SLAB_SHAPES = [(1, 2000, 1000), (3, 777, 300), (1, 5000, 4095), (2, 20000, 129), (1, 300, 130),
+               (4, 1031, 2048), (1, 257, 4100), (2, 100, 1000)]
+
+
+def _device_cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("op", ("sum",) + OPS3)
+def test_column_slab_plans(op):
+    cu = _device_cus()
+    for o, r, i in SLAB_SHAPES:
+        p = rd.rd_plan_reduce(cu, o, r, i, op)
+        assert (p.col_waves, p.row_waves, p.unroll) == (1, 8, 4), ((o, r, i), p.as_dict())
+        assert p.split > 1 and p.blocks <= cu, ((o, r, i), p.as_dict())
+    _sweep_dim(op, SLAB_SHAPES, [0, 1, 3], 750 + rd.OPS[op], "cols slabs")
+
+
 SMALL = [(op, s, nt) for op in OPS3 for s in (1, 3) for nt in (1, 2)]
 
 

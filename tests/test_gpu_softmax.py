@@ -150,6 +150,23 @@ def test_cols_kernel_shapes(cw, split, nt):
                    "cols uniform", False)
 
 
+def test_column_slab_plans():
+    """Default plans of columns too few for one-wave tiles to reach every CU
+    (one tile a block, 8 row waves joining pairs in LDS, slabs of R)."""
+    import torch
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    shapes = [(1, 2000, 1000), (3, 777, 300), (1, 5000, 4095), (2, 20000, 129), (1, 300, 130),
+              (4, 1031, 2048)]
+    for o, r, i in shapes:
+        p = rd.rd_plan_reduce(cu, o, r, i, "softmax_denom")
+        assert (p.col_waves, p.row_waves, p.unroll) == (1, 8, 4), ((o, r, i), p.as_dict())
+        assert p.split > 1 and p.blocks <= cu, ((o, r, i), p.as_dict())
+    maxn = max(o * r * i for o, r, i in shapes) + 4
+    _sweep_dim(_mask(maxn, 825), shapes, [0, 1, 3], "cols slabs mask", True)
+    _sweep_dim(workloads.random(maxn, 826, "uniform", -30.0, 30.0), shapes, [0, 3],
+               "cols slabs uniform", False)
+
+
 SMALL = [(s, nt) for s in (1, 3) for nt in (1, 2)]
 
 

@@ -178,8 +178,33 @@ def test_column_tile_width():
     assert rd.rd_plan_dim(CU, 64, 4096, 4095).col_waves == 4
     assert rd.rd_plan_dim(CU, 1000, 10, 200).col_waves == 1   # 50 lane-columns
     assert rd.rd_plan_dim(CU, 1000, 10, 1000).col_waves == 4  # 250 lane-columns
-    p = rd.rd_plan_dim(CU, 1, 1 << 16, 4095)                  # never reaches CU tiles
-    assert p.col_waves == 8 and p.split > 1 and p.blocks >= CU
+    p = rd.rd_plan_dim(CU, 256, 4096, 256)                    # 256 one-wave tiles:
+    assert p.col_waves == 1 and p.row_waves == 1                # just reach the CUs
+
+
+@pytest.mark.parametrize("op", ["sum", "sumsq", "max", "min", "softmax_denom"])
+def test_column_slabs_of_one_tile(op):
+    """Columns too few for one-wave tiles to reach every CU: one tile a block,
+    8 waves taking turns on its rows, as many slabs of R as keep the grid
+    within one block per CU (a grid just past the CU count pays for a second
+    round), every row wave with at least one step of 4 rows per slab."""
+    shapes = [(1, 1 << 16, 4095), (1, 4096, 10922), (1, 32768, 32768), (2, 65536, 1024),
+              (1, 262144, 512), (4, 8192, 2048), (1, 1000000, 200), (3, 100000, 300),
+              (1, 40, 4096), (2, 31, 1000), (1, 4096, 129)]
+    for cu in (CU, 80, 304):
+        for outer, R, inner in shapes:
+            p = rd.rd_plan_reduce(cu, outer, R, inner, op)
+            tiles = -(-(-(-inner // 4)) // 64)
+            if tiles * outer >= cu:      # (fewer CUs) one-wave tiles reach them all
+                assert p.row_waves == 1 and p.blocks >= cu, (outer, R, inner, cu)
+                continue
+            assert (p.col_waves, p.row_waves, p.unroll) == (1, 8, 4), (outer, R, inner, cu)
+            want = max(1, min(cu // (tiles * outer), max(1, R // 32)))
+            rps = -(-R // want)
+            assert (p.rows_per_split, p.split) == (rps, -(-R // rps)), (outer, R, inner, cu)
+            assert p.blocks == tiles * outer * p.split <= cu, (outer, R, inner, cu)
+            if op != "softmax_denom":   # (its partial results are pairs)
+                check_invariants(p, outer, R, inner, cu)
 
 
 def test_forced_column_path():
