@@ -1052,6 +1052,10 @@ __global__ __launch_bounds__(kBlock) void strided_kernel(const float* __restrict
 }
 
 // Second pass of a split along R: out[e] = join of slab[0][e], slab[1][e], ...
+// in that order; the slabs are loaded kSlabAhead at a time, so that many are
+// in flight per thread.
+constexpr int kSlabAhead = 8;
+
 template <int OP>
 __global__ __launch_bounds__(kBlock) void slab_combine_kernel(typename St<OP>::Out slab,
                                                               int64_t S, int64_t n,
@@ -1060,7 +1064,15 @@ __global__ __launch_bounds__(kBlock) void slab_combine_kernel(typename St<OP>::O
     const int64_t stride = int64_t(gridDim.x) * kBlock;
     for (int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x; e < n; e += stride) {
         typename T::S1 t = T::get(slab, e);
-        for (int64_t s = 1; s < S; ++s) t = T::join(t, T::get(slab, s * n + e));
+        int64_t s = 1;
+        for (; s + kSlabAhead <= S; s += kSlabAhead) {
+            typename T::S1 v[kSlabAhead];
+#pragma unroll
+            for (int u = 0; u < kSlabAhead; ++u) v[u] = T::get(slab, (s + u) * n + e);
+#pragma unroll
+            for (int u = 0; u < kSlabAhead; ++u) t = T::join(t, v[u]);
+        }
+        for (; s < S; ++s) t = T::join(t, T::get(slab, s * n + e));
         T::put(out, e, t);
     }
 }
@@ -1071,7 +1083,7 @@ __global__ __launch_bounds__(kBlock) void slab_combine_kernel(typename St<OP>::O
 // holding at least one slab.  A thread per output would walk all S slabs
 // one after another.
 constexpr int64_t kSlabWaveMinS = kWave;
-constexpr int64_t kSlabWaveMaxN = 256;
+constexpr int64_t kSlabWaveMaxN = 65536;
 
 template <int OP>
 __global__ __launch_bounds__(kBlock) void slab_combine_wave_kernel(typename St<OP>::Out slab,
