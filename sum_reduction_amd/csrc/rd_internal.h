@@ -227,6 +227,24 @@ constexpr int64_t kScanColsDeepRows = 1024;
 // kScanColsMaxRowWaves of them, aiming at kScanColsRoundWavesPerCu waves per CU.
 constexpr int32_t kScanColsMaxRowWaves = 8;
 constexpr int64_t kScanColsRoundWavesPerCu = 4;
+// Fewer tiles (x outer) than half the CUs: slabs of R, as many as keep the
+// blocks within one per CU; the slab totals by the column reduction (one-wave
+// tiles, kScanSlabTotalsRowWaves row waves, kScanSlabTotalsUnroll rows in
+// flight: the reduction's own plan for such columns), the scan pass a block
+// of kScanSlabRowWaves waves per (tile, slab) taking turns on its rows from
+// the slab's carry -- except for row strides that are a multiple of
+// kScanSlabLockStride floats (8 KB) and at least twice that, which keep
+// single-wave blocks walking the rows for both passes.  Measured on MI355X
+// (same box, us, row rounds vs single waves, both with the reduction's
+// totals): [1, 65536, 4095] 663 vs 714, [1, 131072, 4095] 1279 vs 1433,
+// [1, 65536, 8000] 1021 vs 1065, [3, 100000, 300] 275 vs 316,
+// [2, 100000, 129] 73 vs 104, [4, 8192, 2048] 127 vs 133; but
+// [1, 65536, 4096] 618 vs 531, [1, 65536, 8192] 1157 vs 996,
+// [1, 16384, 16384] 529 vs 498, [1, 65536, 6144] 835 vs 808.
+constexpr int32_t kScanSlabRowWaves = 8;
+constexpr int32_t kScanSlabTotalsRowWaves = 8;
+constexpr int32_t kScanSlabTotalsUnroll = 4;
+constexpr int64_t kScanSlabLockStride = 2048;
 constexpr int kScanSmallUnroll = 8;       // load instructions per step, small inner
 constexpr int64_t kScanSmallWavesPerCu = 16;
 // Inputs up to this size are read by a split scan's totals pass without the

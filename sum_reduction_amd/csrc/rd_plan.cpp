@@ -702,8 +702,7 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
     if (t && t->row_waves) {
         rw = t->row_waves;
         if (rw != 1 && rw != 2 && rw != 4 && rw != 8 && rw != 16) return RD_ERR_INVALID_ARG;
-        if (rw > 1 && (inner < 4 || (t->split && t->split != 1) ||
-                       (t->col_waves && t->col_waves != 1)))
+        if (rw > 1 && (inner < 4 || (t->col_waves && t->col_waves != 1)))
             return RD_ERR_INVALID_ARG;
     } else if (2 * waves >= cu && waves < 2 * cu && inner >= 4 &&
                !(t && (t->split || t->col_waves))) {
@@ -712,6 +711,18 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
     int64_t S = 1;
     if (t && t->split) {
         S = t->split;
+    } else if (2 * waves < cu && rw == 1 && inner >= 4 &&
+               !(t && (t->col_waves || t->row_waves || t->unroll))) {
+        // few tiles: slabs (the blocks within one per CU, at least a round
+        // of kScanSlabRowWaves groups of U rows each) scanned in row rounds,
+        // or by single waves for rows a multiple of 8 KB apart (from 16 KB)
+        const int64_t sr = v->sr;
+        const bool lock = sr >= 2 * kScanSlabLockStride && sr % kScanSlabLockStride == 0;
+        rw = lock ? 1 : kScanSlabRowWaves;
+        S = cu / waves;
+        int64_t cap = R / (int64_t(kScanSlabRowWaves) * p->unroll);
+        if (cap < 1) cap = 1;
+        if (S > cap) S = cap;
     } else if (waves < cu && rw == 1) {
         S = ceil_div(cu, waves);
         int64_t cap = R / 64;

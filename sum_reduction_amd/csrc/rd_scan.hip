@@ -779,35 +779,43 @@ __global__ __launch_bounds__(BW * kWave) void scan_cols_kernel(
 }
 
 // Few tiles, tall columns: a block of RW waves on one tile (64 lane-columns,
-// 256 columns) of one outer index, over the whole of R (one pass, x read
-// once, where slabs would read it twice).  Wave w takes the groups of U rows
-// w, w + RW, w + 2RW, ... in processing order; per round of RW groups each
+// 256 columns) of one outer index and one slab s of R (S == 1: the whole of
+// R, one pass, x read once).  Wave w takes the groups of U rows w, w + RW,
+// w + 2RW, ... of the slab in processing order; per round of RW groups each
 // wave adds its group up (running sums pre_u in processing order, group
 // total t_w), the totals meet in LDS (two slot sets in turn: one barrier a
 // round), wave w's outputs are (carry + t_0 + ... + t_{w-1}) + pre_u, and the
 // carry of the next round is carry + t_0 + ... + t_{RW-1} -- a fixed order, so
-// the results do not depend on timing.  The next round's loads go out before
-// the current round is added up.  inner >= 4; element (o, r, c) at
-// x + o*so + r*sr + c as in scan_cols_kernel, out contiguous.
+// the results do not depend on timing.  The slab's first carry is
+// carry_in[s][o][i] (0 when null).  Items are numbered tile fastest, then
+// slab, then o.  The next round's loads go out before the current round is
+// added up.  inner >= 4; element (o, r, c) at x + o*so + r*sr + c as in
+// scan_cols_kernel, out contiguous.
 template <bool REV, int U, int RW, bool NT>
 __global__ __launch_bounds__(RW * kWave) void scan_cols_rounds_kernel(
     const float* x, float* out, int64_t outer, int64_t R, int64_t inner, int64_t so,
-    int64_t sr, int64_t ntiles, uint32_t nxcd) {
+    int64_t sr, int64_t ntiles, int64_t S, int64_t rps, const float* __restrict__ carry_in,
+    uint32_t nxcd) {
     __shared__ v4f slots[2][RW][kWave];
     const int wave = wave_in_block();
     const int lane = threadIdx.x % kWave;
-    const int64_t nitems = ntiles * outer;
+    const int64_t nitems = ntiles * S * outer;
     const int64_t per_round = int64_t(RW) * U;
-    const int64_t nrounds = (R + per_round - 1) / per_round;
     int parity = 0;
     for (int64_t item = xcd_block(nxcd); item < nitems; item += gridDim.x) {
         const int64_t tile = item % ntiles;
-        const int64_t o = item / ntiles;
+        const int64_t rest = item / ntiles;
+        const int64_t sl = rest % S;
+        const int64_t o = rest / S;
+        const int64_t r_begin = sl * rps;
+        const int64_t r_end = r_begin + rps < R ? r_begin + rps : R;
+        const int64_t m = r_end > r_begin ? r_end - r_begin : 0;  // rows of the slab
+        const int64_t nrounds = (m + per_round - 1) / per_round;
         const int64_t c = 4 * (tile * kWave + lane);
         const bool live = c < inner;
         const int64_t cl = c + 4 > inner ? inner - 4 : c;
         const int keep = live ? int(c - cl) : 4;
-        const int64_t first = REV ? R - 1 : 0;
+        const int64_t first = REV ? r_end - 1 : r_begin;
         const int64_t pstep = REV ? -sr : sr;
         const int64_t qstep = REV ? -inner : inner;
         const float* p = x + o * so + first * sr + cl;
@@ -817,7 +825,7 @@ __global__ __launch_bounds__(RW * kWave) void scan_cols_rounds_kernel(
             const int64_t k0 = g * per_round + int64_t(wave) * U;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                v[u] = live && k0 + u < R ? load4<NT>(p + (k0 + u) * pstep) : v4f{0.f, 0.f, 0.f, 0.f};
+                v[u] = live && k0 + u < m ? load4<NT>(p + (k0 + u) * pstep) : v4f{0.f, 0.f, 0.f, 0.f};
         };
         auto round = [&](int64_t g, v4f (&v)[U], v4f& carry) {
             const int64_t k0 = g * per_round + int64_t(wave) * U;
@@ -841,10 +849,11 @@ __global__ __launch_bounds__(RW * kWave) void scan_cols_rounds_kernel(
             if (live) {
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    if (k0 + u < R) store_cols<4, NT>(q + (k0 + u) * qstep, keep, mine + v[u]);
+                    if (k0 + u < m) store_cols<4, NT>(q + (k0 + u) * qstep, keep, mine + v[u]);
             }
         };
         v4f carry = {0.f, 0.f, 0.f, 0.f};
+        if (live && carry_in != nullptr) carry = load4<false>(carry_in + (sl * outer + o) * inner + cl);
         v4f a[U], b[U];
         load_group(0, a);
         for (int64_t g = 0; g < nrounds; g += 2) {
@@ -1405,15 +1414,35 @@ hipError_t cols_bw(const rd_plan& p, const float* x, float* out, const Strides& 
 
 template <bool REV, int RW, bool NT>
 hipError_t rounds_go(const rd_plan& p, const float* x, float* out, const Strides& v,
-                     int64_t ntiles, hipStream_t s) {
+                     int64_t ntiles, const float* carry_in, hipStream_t s) {
     const uint32_t nx = uint32_t(p.nxcd);
     if (p.unroll == 8)
         return launch(scan_cols_rounds_kernel<REV, 8, RW, NT>, p.blocks, RW * kWave, s, x, out,
-                      v.outer, v.R, v.inner, v.so, v.sr, ntiles, nx);
+                      v.outer, v.R, v.inner, v.so, v.sr, ntiles, p.split, p.rows_per_split,
+                      carry_in, nx);
     if (p.unroll == 4)
         return launch(scan_cols_rounds_kernel<REV, 4, RW, NT>, p.blocks, RW * kWave, s, x, out,
-                      v.outer, v.R, v.inner, v.so, v.sr, ntiles, nx);
+                      v.outer, v.R, v.inner, v.so, v.sr, ntiles, p.split, p.rows_per_split,
+                      carry_in, nx);
     return hipErrorInvalidValue;
+}
+
+// The slab totals of a row-rounds plan cut into slabs: totals[s][o][i] = the
+// sum of slab s of column (o, i), by the column reduction (one-wave tiles,
+// kScanSlabTotalsRowWaves waves taking turns on the rows, the same slabs) --
+// a fixed order of its own; the carries and the scan pass follow.
+hipError_t slab_totals(const rd_plan& p, const float* x, const Strides& v, float* totals,
+                       hipStream_t s) {
+    rd_plan q = p;
+    q.path = RD_PATH_COLS;
+    q.col_waves = 1;
+    q.row_waves = kScanSlabTotalsRowWaves;
+    q.unroll = kScanSlabTotalsUnroll;
+    q.block_threads = kWave * q.row_waves;
+    const int64_t tiles = ((v.inner + 3) / 4 + kWave - 1) / kWave;
+    q.blocks = tiles * p.split * v.outer;
+    if (q.blocks > kMaxBlocks) q.blocks = kMaxBlocks;
+    return launch_cols(RD_OP_SUM, q, x, v, Results{totals, nullptr}, s);
 }
 
 template <bool REV, int V, bool NT>
@@ -1421,14 +1450,16 @@ hipError_t cols_go(const rd_plan& p, const float* x, float* out, const Strides& 
                    const float* carry_in, float* totals, hipStream_t s) {
     const int64_t lane_cols = v.inner >= 4 ? (v.inner + 3) / 4 : 1;
     const int64_t ntiles = (lane_cols + kWave - 1) / kWave;
-    if (p.row_waves > 1) {  // waves of a block taking turns in R: one pass only
+    if (p.row_waves > 1) {  // waves of a block taking turns in R
         if constexpr (V == 4) {
-            if (p.split != 1 || p.col_waves != 1 || carry_in || totals) return hipErrorInvalidValue;
+            if (p.col_waves != 1 || (p.split == 1 && (carry_in || totals)))
+                return hipErrorInvalidValue;
+            if (totals) return slab_totals(p, x, v, totals, s);
             switch (p.row_waves) {
-                case 2: return rounds_go<REV, 2, NT>(p, x, out, v, ntiles, s);
-                case 4: return rounds_go<REV, 4, NT>(p, x, out, v, ntiles, s);
-                case 8: return rounds_go<REV, 8, NT>(p, x, out, v, ntiles, s);
-                case 16: return rounds_go<REV, 16, NT>(p, x, out, v, ntiles, s);
+                case 2: return rounds_go<REV, 2, NT>(p, x, out, v, ntiles, carry_in, s);
+                case 4: return rounds_go<REV, 4, NT>(p, x, out, v, ntiles, carry_in, s);
+                case 8: return rounds_go<REV, 8, NT>(p, x, out, v, ntiles, carry_in, s);
+                case 16: return rounds_go<REV, 16, NT>(p, x, out, v, ntiles, carry_in, s);
                 default: return hipErrorInvalidValue;
             }
         }

@@ -135,6 +135,36 @@ def test_columns_by_row_rounds(rw, unroll):
         _sweep(shapes, [0, 1, 3], 870 + rw + unroll, "scan rounds rw%d u%d" % (rw, unroll))
 
 
+def test_column_slabs_default_plans():
+    """Few tiles (fewer than half the CUs): slabs of R whose totals come from
+    the column reduction, scanned in row rounds of 8 waves -- or by single
+    waves for rows a multiple of 8 KB apart -- from each slab's carry; ragged
+    slabs, partial tiles, both directions, every output bit-exact."""
+    import torch
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    rounds = [(1, 5000, 4095), (2, 3000, 129), (3, 777, 300), (1, 1000, 10922), (4, 513, 2048)]
+    lock = [(1, 4100, 4096), (1, 300, 8192)]
+    for o, r, i in rounds + lock:
+        p = rd.rd_plan_cumsum(cu, o, r, i)
+        assert p.split > 1 and p.passes == 3, ((o, r, i), p.as_dict())
+        assert p.row_waves == (1 if (o, r, i) in lock else 8), ((o, r, i), p.as_dict())
+    _sweep(rounds + lock, [0, 1, 3], 880, "scan col slabs")
+
+
+@pytest.mark.parametrize("rw,unroll,split", [(8, 8, 3), (4, 4, 7), (2, 8, 2), (16, 4, 5)],
+                         ids=["rw8_u8_s3", "rw4_u4_s7", "rw2_u8_s2", "rw16_u4_s5"])
+def test_column_slabs_in_row_rounds(rw, unroll, split):
+    """Forced slabs scanned in row rounds: slabs shorter than a round, around
+    the round and group boundaries, ragged and partial tiles."""
+    per = rw * unroll
+    shapes = [(2, r, i) for r in (split, per - 1, per * split + 1, 3 * per * split - 5)
+              for i in (4, 5, 300)]
+    shapes += [(1, 4 * per * split + 7, 4095), (3, per * split, 1025)]
+    with rd.tuning(row_waves=rw, unroll=unroll, split=split, path=7):
+        _sweep(shapes, [0, 1], 885 + rw + split, "scan slab rounds rw%d u%d s%d"
+               % (rw, unroll, split))
+
+
 def test_columns_by_row_rounds_default_plans():
     """Shapes whose default plan takes row rounds (between half and twice as
     many tiles as CUs), random data: within tolerance of the oracle, and

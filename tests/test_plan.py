@@ -345,6 +345,19 @@ def _scan_invariants(p, outer, R, inner, cu=CU):
             assert waves * rw >= 4 * cu or rw == 8
             assert rw == 1 or waves * (rw // 2) < 4 * cu
             assert p.unroll in (4, 8) and p.blocks == min(waves, 1 << 20)
+        elif 2 * waves < cu and inner >= 4:
+            # fewer tiles than half the CUs: slabs, as many as keep the blocks
+            # within one per CU, each a round of 8 waves x U rows at least;
+            # the scan pass in row rounds of 8 waves a tile (single waves for
+            # rows a multiple of 8 KB apart, from 16 KB), totals by the column
+            # reduction
+            S = max(1, min(cu // waves, max(1, R // 64)))
+            rps = -(-R // S)
+            assert (p.rows_per_split, p.split) == (rps, -(-R // rps)), p.as_dict()
+            lock = inner >= 4096 and inner % 2048 == 0
+            assert bw == 1 and rw == (1 if lock else 8), p.as_dict()
+            assert p.unroll == (16 if lock and rps >= 1024 else 8), p.as_dict()
+            assert p.blocks == waves * p.split <= cu
         else:
             # slabs only when fewer tiles than half the CUs; then the widest
             # block that still gives every CU one
@@ -445,6 +458,15 @@ def test_cumsum_plans():
     p = rd.rd_plan_cumsum(CU, 128, 4096, 4095)
     assert p.as_dict()["path"] == "scan_cols" and p.split == 1
     assert p.col_waves == 8 and p.blocks == 256         # 16 tiles a row: 2 blocks of 8
+    p = rd.rd_plan_cumsum(CU, 1, 65536, 4095)            # 16 tiles: 16 slabs in row rounds
+    assert (p.split, p.row_waves, p.col_waves, p.unroll, p.blocks) == (16, 8, 1, 8, 256)
+    assert p.passes == 3 and p.workspace_bytes == 2 * 16 * 4095 * 4
+    for inner in (4096, 8192, 6144):                      # rows a multiple of 8 KB apart
+        p = rd.rd_plan_cumsum(CU, 1, 65536, inner)
+        assert p.row_waves == 1 and p.col_waves == 1 and p.unroll == 16, (inner, p.as_dict())
+        assert p.blocks == -(-inner // 256) * p.split <= CU
+    p = rd.rd_plan_cumsum(CU, 1, 65536, 2048)             # 8 KB apart: row rounds
+    assert p.row_waves == 8 and p.split == 32
     rng = np.random.default_rng(5)
     for _ in range(3000):
         outer, R, inner = (int(v) for v in rng.integers(1, [3000, 200_000, 5000]))
