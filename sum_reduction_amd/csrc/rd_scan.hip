@@ -658,11 +658,30 @@ __device__ __forceinline__ void store_cols(float* q, int keep, v4f acc) {
     }
 }
 
+// The U rows of a group g (in processing order) added to the running sums
+// acc: row u's outputs are acc + (g[0] + ... + g[u]), stored when scan_out,
+// and the new running sums are acc + (g[0] + ... + g[U-1]).  The running sums
+// take one add per group, not per row, so the rounding they carry down a tall
+// column grows with R/U additions rather than R.
+template <int V, int U, bool NT>
+__device__ __forceinline__ v4f cols_group(float* qc, int64_t qstep, int keep, bool scan_out,
+                                          const v4f (&g)[U], v4f acc) {
+    v4f run = g[0];
+    if (scan_out) store_cols<V, NT>(qc, keep, acc + run);
+#pragma unroll
+    for (int u = 1; u < U; ++u) {
+        run += g[u];
+        if (scan_out) store_cols<V, NT>(qc + u * qstep, keep, acc + run);
+    }
+    return acc + run;
+}
+
 // One group step of a lane-column: issue the loads of the U rows at element
 // offset off_load into `next`, then add the U rows of `cur` (rows at off_cur)
-// to the running sums and store each; then meet the block's other waves.
-// pl: the first row of the group to load (rows pstep floats apart in x);
-// qc: the first output row of the group in `cur` (qstep floats apart in out).
+// to the running sums (cols_group) and store them; then meet the block's
+// other waves.  pl: the first row of the group to load (rows pstep floats
+// apart in x); qc: the first output row of the group in `cur` (qstep floats
+// apart in out).
 template <int V, int U, bool NT>
 __device__ __forceinline__ v4f cols_step(const float* pl, float* qc, int64_t pstep,
                                          int64_t qstep, int keep, bool scan_out,
@@ -670,11 +689,7 @@ __device__ __forceinline__ v4f cols_step(const float* pl, float* qc, int64_t pst
 #pragma unroll
     for (int u = 0; u < U; ++u) next[u] = loadv<V, NT>(pl + u * pstep, 0.f);
     __builtin_amdgcn_sched_barrier(0);  // the loads go out before the adds (as in rows_step)
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        acc += cur[u];
-        if (scan_out) store_cols<V, NT>(qc + u * qstep, keep, acc);
-    }
+    acc = cols_group<V, U, NT>(qc, qstep, keep, scan_out, cur, acc);
     __syncthreads();
     return acc;
 }
@@ -689,8 +704,8 @@ __device__ __forceinline__ v4f cols_step(const float* pl, float* qc, int64_t pst
 // lockstep, the cache lines two neighbouring tiles share at their edge (rows
 // need not be line-aligned) are written by both within one step, not rows
 // apart, so they leave the L2 whole.  Each step issues the next group's loads
-// before adding and storing the current group (two buffers in turn).
-// totals != null: only the slab totals go to totals[s][o][i]; otherwise the
+// before adding and storing the current group (cols_group; two buffers in
+// turn).  totals != null: only the slab totals go to totals[s][o][i]; otherwise the
 // slab is scanned from carry_in[s][o][i] (0 when null) into out.  Element
 // (o, r, c) of x is at x + o*so + r*sr + c (a contiguous array: so = R*inner,
 // sr = inner); out is contiguous.  x and out may be the same array.
@@ -751,17 +766,9 @@ __global__ __launch_bounds__(BW * kWave) void scan_cols_kernel(
             if (g + 1 < ngroups) {
                 acc = cols_step<V, U, NT>(p + (g + 1) * U * pstep, q0, pstep, qstep, keep,
                                           scan_out, a, b, acc);
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    acc += b[u];
-                    if (scan_out) store_cols<V, NT>(q0 + (U + u) * qstep, keep, acc);
-                }
+                acc = cols_group<V, U, NT>(q0 + U * qstep, qstep, keep, scan_out, b, acc);
             } else {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    acc += a[u];
-                    if (scan_out) store_cols<V, NT>(q0 + u * qstep, keep, acc);
-                }
+                acc = cols_group<V, U, NT>(q0, qstep, keep, scan_out, a, acc);
             }
             __syncthreads();
             p += ngroups * U * pstep;

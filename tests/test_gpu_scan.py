@@ -135,6 +135,24 @@ def test_columns_by_row_rounds(rw, unroll):
         _sweep(shapes, [0, 1, 3], 870 + rw + unroll, "scan rounds rw%d u%d" % (rw, unroll))
 
 
+@pytest.mark.parametrize("reverse", [True, False], ids=["reverse", "forward"])
+def test_tall_columns_random_data(reverse):
+    """A 65536-row column scan in one slab (single-wave blocks walking every
+    row), U[0, 1) data: the running sums grow to ~32768, so rounding carried
+    down the column is the error that matters; the running sums take one add
+    per group of rows, which keeps every output within 1e-5 * (sum of |x|
+    over its terms) + 1e-6 (one add per row had reached ~1.4x that here)."""
+    o, r, i = 1, 65536, 1024
+    data = workloads.random(o * r * i, 890 + int(reverse), "uniform", 0.0, 1.0)
+    with rd.tuning(row_waves=1, split=1, path=7):
+        p = rd.rd_plan_cumsum(256, o, r, i)
+        assert (p.split, p.row_waves, p.unroll) == (1, 1, 16), p.as_dict()
+        got = rd.rd_cumsum_dim(H.upload(data), o, r, i, reverse)
+    S, A = oracle.cumsum_dim(data, o, r, i, reverse, threads=4)
+    H.assert_within_tolerance(got.cpu().numpy().reshape(-1), S.reshape(-1), A.reshape(-1),
+                              "tall columns %s" % ("reverse" if reverse else "forward"))
+
+
 def test_column_slabs_default_plans():
     """Few tiles (fewer than half the CUs): slabs of R whose totals come from
     the column reduction, scanned in row rounds of 8 waves -- or by single
