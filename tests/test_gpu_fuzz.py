@@ -172,3 +172,40 @@ def test_random_strided_cumsum(seed):
                                             strides=(4 * so, 4 * sr, 4 * si), writeable=False)
         S, _ = oracle.cumsum_dim(np.ascontiguousarray(v), o, R, i, bool(rev), threads=1)
         H.assert_bitwise_equal_oracle(got, S, what)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_contiguous_cumsum(seed):
+    """rd_cumsum_dim on random contiguous shapes (sizes over orders of
+    magnitude, so every plan -- rows, pieces, look-back, columns in lockstep,
+    row rounds, slabs of few tiles with their totals from the column
+    reduction, small inner -- comes up), both directions, base offsets 0-3,
+    sometimes a forced row-round or slab count; integer data, every prefix
+    exact and bit for bit the oracle's."""
+    rng = np.random.default_rng(9000 + seed)
+    lib = rd.load()
+    for case in range(30):
+        o, R, i = _shape(rng)
+        rev = int(rng.integers(0, 2))
+        off = int(rng.integers(0, 4))
+        tune = {}
+        if i >= 4 and rng.random() < 0.3:
+            tune = dict(path=7, row_waves=int(rng.choice([2, 4, 8])),
+                        unroll=int(rng.choice([4, 8])), split=int(rng.choice([1, 2, 5, 17])))
+        n = o * R * i
+        host = workloads.small_ints(n + off + 1, 9100 + 100 * seed + case)
+        dev = H.upload(host)
+        slots = H.OutSlots([n])
+        what = "seed %d case %d shape %s rev %d off %d tune %s" % (seed, case, (o, R, i), rev,
+                                                                 off, tune)
+        H.say(what)
+        xp = dev.data_ptr() + 4 * off if n else None
+        with rd.tuning(**tune):
+            st = lib.rd_cumsum_dim(xp, o, R, i, rev, slots.ptr(0) if n else None,
+                                   H.stream_handle())
+        assert st == 0, (what, rd.rd_status_string(st))
+        (got,) = slots.fetch()
+        if n == 0:
+            continue
+        S, _ = oracle.cumsum_dim(host[off:off + n], o, R, i, bool(rev), threads=2)
+        H.assert_bitwise_equal_oracle(got, S, what)
