@@ -30,8 +30,13 @@
 // same chunks, carry only), their exclusive scan in piece order, and the
 // scan of each piece from its carry.  The column scans (inner > 1) keep the
 // running sums of 4 adjacent columns in a lane and walk R in processing
-// order: 256 columns a wave for wide rows (scan_cols_kernel), several whole
-// rows a load instruction for inner <= 128 (scan_small_kernel).
+// order, advancing the running sums once per group of rows: 256 columns a
+// wave for wide rows (scan_cols_kernel, or scan_cols_rounds_kernel with the
+// waves of a block taking turns on one tile's rows), several whole rows a
+// load instruction for inner <= 128 (scan_small_kernel).  Too few tiles for
+// the chip are cut into slabs of R: the slab totals (for row rounds, by the
+// column reduction's own kernel), their exclusive scan in slab order, and the
+// scan of each slab from its carry.
 #include <hip/hip_runtime.h>
 
 #include "rd_device.h"
@@ -860,7 +865,8 @@ __global__ __launch_bounds__(RW * kWave) void scan_cols_rounds_kernel(
             }
         };
         v4f carry = {0.f, 0.f, 0.f, 0.f};
-        if (live && carry_in != nullptr) carry = load4<false>(carry_in + (sl * outer + o) * inner + cl);
+        if (live && carry_in != nullptr)
+            carry = load4<false>(carry_in + (sl * outer + o) * inner + cl);
         v4f a[U], b[U];
         load_group(0, a);
         for (int64_t g = 0; g < nrounds; g += 2) {
