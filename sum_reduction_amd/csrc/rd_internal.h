@@ -241,6 +241,13 @@ constexpr int64_t kScanColsRoundWavesPerCu = 4;
 // [2, 100000, 129] 73 vs 104, [4, 8192, 2048] 127 vs 133; but
 // [1, 65536, 4096] 618 vs 531, [1, 65536, 8192] 1157 vs 996,
 // [1, 16384, 16384] 529 vs 498, [1, 65536, 6144] 835 vs 808.
+// A lane-per-column strided scan with at least half as many groups of 64
+// columns as CUs (and fewer than would fill the chip as single lanes): one
+// pass, a block of row waves per group (the fewest of 2, 4, 8 that make about
+// kStridedRoundsWavesPerCu waves per CU), kStridedRoundsUnroll rows a group.
+constexpr int kStridedRoundsUnroll = 8;
+constexpr int32_t kStridedRoundsMaxRowWaves = 8;
+constexpr int64_t kStridedRoundsWavesPerCu = 4;
 constexpr int32_t kScanSlabRowWaves = 8;
 constexpr int32_t kScanSlabTotalsRowWaves = 8;
 constexpr int32_t kScanSlabTotalsUnroll = 4;

@@ -469,11 +469,39 @@ constexpr int64_t kStageCols = 64;
 constexpr int64_t kStageRound = 4 * 32;
 
 rd_status plan_scan_strided(int64_t cu, const Strides& v, const rd_tune* t, rd_plan* p) {
-    if (t && (t->group || t->col_waves || t->row_waves || t->unroll || t->order || t->combine))
+    if (t && (t->group || t->col_waves || t->unroll || t->order || t->combine))
         return RD_ERR_INVALID_ARG;
     const int64_t outer = v.outer, R = v.R, inner = v.inner;
     const int64_t n = outer * inner;
     const bool staged = inner == 1 || v.sr == 1;
+    // Between half a group of 64 columns per CU and enough single lanes for
+    // the chip: one pass, row waves taking turns (scan_strided_rounds_kernel)
+    // where slabs would read x twice.  Measured on MI355X: x[::8, ::3] of
+    // [32768, 32768] (10922 columns, 171 groups), cumsum along dim 0:
+    // 300 us in 25 slabs of a lane per column, 164 us in 8-wave rounds.
+    const int64_t groups = ceil_div(n, kWave);
+    int32_t rw = 1;
+    if (t && t->row_waves) {
+        rw = t->row_waves;
+        if (staged || (rw != 2 && rw != 4 && rw != 8) || (t->split && t->split != 1))
+            return RD_ERR_INVALID_ARG;
+    } else if (!staged && !(t && t->split) && 2 * groups >= cu &&
+               n < cu * kStridedLanesPerCu) {
+        rw = 2;
+        while (rw < kStridedRoundsMaxRowWaves && groups * rw < kStridedRoundsWavesPerCu * cu)
+            rw *= 2;
+    }
+    if (rw > 1) {
+        p->path = RD_PATH_SCAN_STRIDED;
+        p->nontemporal = 0;  // neighbouring lanes share lines: keep them cached
+        p->row_waves = rw;
+        p->unroll = kStridedRoundsUnroll;
+        p->block_threads = rw * kWave;
+        p->blocks = groups < kMaxBlocks ? groups : kMaxBlocks;
+        p->split = 1;
+        p->rows_per_split = R;
+        return RD_OK;
+    }
     const int64_t cols = staged ? kStageCols : kBlock;  // columns per workgroup
     const int64_t nblk = ceil_div(n, cols);
     int64_t S = 1;

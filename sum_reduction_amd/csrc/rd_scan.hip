@@ -1120,6 +1120,85 @@ __global__ __launch_bounds__(kBlock) void scan_strided_kernel(
     }
 }
 
+// A view with no unit stride along its kept inner axis and enough columns for
+// the chip, in one pass: a block of RW waves on 64 columns (a lane each,
+// column e = 64*item + lane of the outer*inner columns), over the whole of R.
+// Wave w takes the groups of U rows w, w + RW, ... in processing order; per
+// round each wave adds its group up (running sums pre_u, group total t_w),
+// the totals meet in LDS, wave w's outputs are (carry + t_0 + ... + t_{w-1})
+// + pre_u and the next round's carry is carry + t_0 + ... + t_{RW-1} -- the
+// order of scan_cols_rounds_kernel, one column a lane.  Lanes past the last
+// column load and store nothing.  Element (o, r, i) at x + o*so + r*sr + i*si,
+// out contiguous.
+template <bool REV, int U, int RW>
+__global__ __launch_bounds__(RW * kWave) void scan_strided_rounds_kernel(
+    const float* x, float* out, int64_t outer, int64_t R, int64_t inner, int64_t so,
+    int64_t sr, int64_t si, int64_t ngroups, uint32_t nxcd) {
+    __shared__ float slots[2][RW][kWave];
+    const int wave = wave_in_block();
+    const int lane = threadIdx.x % kWave;
+    const int64_t n = outer * inner;
+    const int64_t per_round = int64_t(RW) * U;
+    const int64_t nrounds = (R + per_round - 1) / per_round;
+    int parity = 0;
+    for (int64_t item = xcd_block(nxcd); item < ngroups; item += gridDim.x) {
+        const int64_t e0 = item * kWave + lane;
+        const bool live = e0 < n;
+        const int64_t e = live ? e0 : n - 1;
+        const int64_t o = e / inner;
+        const int64_t i = e - o * inner;
+        const int64_t first = REV ? R - 1 : 0;
+        const int64_t pstep = REV ? -sr : sr;
+        const int64_t qstep = REV ? -inner : inner;
+        const float* p = x + o * so + first * sr + i * si;
+        float* q = out + (o * R + first) * inner + i;
+        auto load_group = [&](int64_t g, float (&v)[U]) {
+            const int64_t k0 = g * per_round + int64_t(wave) * U;
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = live && k0 + u < R ? p[(k0 + u) * pstep] : 0.f;
+        };
+        auto round = [&](int64_t g, float (&v)[U], float& carry) {
+            const int64_t k0 = g * per_round + int64_t(wave) * U;
+            float t = 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                t += v[u];
+                v[u] = t;
+            }
+            slots[parity][wave][lane] = t;
+            __syncthreads();
+            float mine = carry, next = carry;
+#pragma unroll
+            for (int w = 0; w < RW; ++w) {
+                const float sw = slots[parity][w][lane];
+                if (w < wave) mine += sw;
+                next += sw;
+            }
+            carry = next;
+            parity ^= 1;
+            if (live) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (k0 + u < R) q[(k0 + u) * qstep] = mine + v[u];
+            }
+        };
+        float carry = 0.f;
+        float a[U], b[U];
+        load_group(0, a);
+        for (int64_t g = 0; g < nrounds; g += 2) {
+            if (g + 1 < nrounds) load_group(g + 1, b);
+            __builtin_amdgcn_sched_barrier(0);  // the next round's loads go out first
+            round(g, a, carry);
+            __builtin_amdgcn_sched_barrier(0);
+            if (g + 1 >= nrounds) break;
+            if (g + 2 < nrounds) load_group(g + 2, a);
+            __builtin_amdgcn_sched_barrier(0);
+            round(g + 1, b, carry);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // Two layouts of scan_strided_kernel's lanes have one unit-stride side that
 // the lanes do not follow; a block then stages that side through LDS.  A
 // block is kStageWaves waves on kStageCols adjacent columns (lane l of every
@@ -1603,6 +1682,18 @@ hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, floa
                          : cols_v<false, false>(p, x, out, v, carry_in, totals, s);
 }
 
+template <int RW>
+hipError_t strided_rounds_go(const rd_plan& p, bool reverse, const float* x, float* out,
+                             const Strides& v, int64_t ngroups, hipStream_t s) {
+    constexpr int U = kStridedRoundsUnroll;
+    const uint32_t nx = uint32_t(p.nxcd);
+    if (reverse)
+        return launch(scan_strided_rounds_kernel<true, U, RW>, p.blocks, RW * kWave, s, x, out,
+                      v.outer, v.R, v.inner, v.so, v.sr, v.si, ngroups, nx);
+    return launch(scan_strided_rounds_kernel<false, U, RW>, p.blocks, RW * kWave, s, x, out,
+                  v.outer, v.R, v.inner, v.so, v.sr, v.si, ngroups, nx);
+}
+
 hipError_t launch_scan_strided(const rd_plan& p, bool reverse, const float* x, float* out,
                                const Strides& v, const float* carry_in, float* totals,
                                hipStream_t s) {
@@ -1621,6 +1712,17 @@ hipError_t launch_scan_strided(const rd_plan& p, bool reverse, const float* x, f
                           totals);
         return launch(scan_tile_in_kernel<false>, blocks, kStageWaves * kWave, s, x, out, v.outer,
                       v.R, v.inner, v.so, v.si, p.split, p.rows_per_split, carry_in, totals);
+    }
+    if (p.row_waves > 1) {  // one pass, RW waves a block taking turns on the rows
+        if (p.split != 1 || carry_in || totals || p.unroll != kStridedRoundsUnroll)
+            return hipErrorInvalidValue;
+        const int64_t ngroups = (v.outer * v.inner + kWave - 1) / kWave;
+        switch (p.row_waves) {
+            case 2: return strided_rounds_go<2>(p, reverse, x, out, v, ngroups, s);
+            case 4: return strided_rounds_go<4>(p, reverse, x, out, v, ngroups, s);
+            case 8: return strided_rounds_go<8>(p, reverse, x, out, v, ngroups, s);
+            default: return hipErrorInvalidValue;
+        }
     }
     // a lane per (slab, column)
     if (reverse)

@@ -173,7 +173,12 @@ void check_scan_plan(const rd::Strides& v, const rd_plan& p) {
             if (!tiles(v.R, p.split, p.rows_per_split)) fail("scan slabs do not tile R", v, -1, p);
             if (p.workspace_bytes != (p.split > 1 ? 8 * p.split * n : 0))
                 fail("scan slab workspace", v, -1, p);
-            if (p.path == RD_PATH_SCAN_STRIDED) {
+            if (p.path == RD_PATH_SCAN_STRIDED && p.row_waves > 1) {
+                // one pass in row rounds: a block of row waves per 64 columns
+                if (p.split != 1 || p.block_threads != 64 * p.row_waves ||
+                    p.blocks != std::min(rd::kMaxBlocks, (n + 63) / 64))
+                    fail("scan strided rounds", v, -1, p);
+            } else if (p.path == RD_PATH_SCAN_STRIDED) {
                 // staged views: blocks of 64 columns; otherwise 256 columns
                 const int64_t cols = (v.inner == 1 || v.sr == 1) ? 64 : rd::kBlock;
                 if (p.blocks != std::min(rd::kMaxBlocks, p.split * ((n + cols - 1) / cols)))

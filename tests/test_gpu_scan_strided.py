@@ -95,6 +95,40 @@ def _run(views, offsets, seed, tag, reverse_modes=(True, False)):
                                       % (tag, name, off, rev))
 
 
+# Views with no unit stride along the lanes' side and between half a group of
+# 64 columns per CU and a chip of single lanes: one pass in row rounds.
+ROUND_VIEWS = [
+    ("every_third_column_rounds", 300 * 33000, 1, 300, 10922, 0, 33000, 3, "scan_strided"),
+    ("every_other_3d_rounds", 4 * 130 * 20000, 4, 130, 9000, 130 * 20000, 20000, 2,
+     "scan_strided"),
+    ("every_fifth_ragged", 97 * 60000, 1, 97, 11001, 0, 60000, 5, "scan_strided"),
+]
+
+
+def test_row_round_views_default_plan():
+    """The default plan of such views is one pass in row rounds (8 waves a
+    group of 64 columns here); R around the round and group boundaries via
+    the shapes, ragged last column group; bit-exact."""
+    for name, n, o, R, i, so, sr, si, _ in ROUND_VIEWS:
+        p = rd.rd_plan_cumsum_strided(256, o, R, i, so, sr, si)
+        assert p.row_waves in (2, 4, 8) and p.split == 1 and p.passes == 1, (name, p.as_dict())
+    _run(ROUND_VIEWS, [0, 3], 960, "strided rounds")
+
+
+@pytest.mark.parametrize("rw", [2, 4, 8])
+def test_row_rounds_forced(rw):
+    """Every lane-per-column view of the table in forced row rounds of rw
+    waves (rounds of 8*rw rows): short and ragged R, one to many groups."""
+    views = [v for v in VIEWS if v[8] == "scan_strided" and v[4] != 1 and v[6] != 1]
+    views += [("rounds_edges_%d" % r, 40 * 1000, 3, r, 70, 13000, 40, 3, "scan_strided")
+              for r in (2, 7, 8, 8 * rw - 1, 8 * rw, 8 * rw + 1, 2 * 8 * rw + 3)]
+    with rd.tuning(path=10, row_waves=rw):
+        for name, n, o, R, i, so, sr, si, _ in views:
+            p = rd.rd_plan_cumsum_strided(256, o, R, i, so, sr, si)
+            assert p.row_waves == rw and p.split == 1, (name, p.as_dict())
+        _run(views, [0, 1], 970 + rw, "strided rounds rw%d" % rw)
+
+
 def test_view_paths():
     for name, n, o, R, i, so, sr, si, path in VIEWS:
         got = rd.rd_plan_cumsum_strided(256, o, R, i, so, sr, si).as_dict()["path"]
