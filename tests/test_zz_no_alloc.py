@@ -67,6 +67,11 @@ def test_noalloc_column_pairs():
     assert rd.rd_plan_dim(256, 3, 50_000, 70).split > 1
     _pair((1, 20_000, 4095), (1, 5_000, 4095), 310, "uniform")
     _pair((3, 50_000, 70), (2, 20_000, 70), 320)
+    # narrow columns: one-wave tiles with row waves in 128 slabs, joined by a
+    # wave per output (258 outputs), then a smaller such pair
+    p = rd.rd_plan_dim(256, 2, 100_000, 129)
+    assert (p.col_waves, p.row_waves, p.split) == (1, 8, 128), p.as_dict()
+    _pair((2, 100_000, 129), (2, 30_000, 129), 330)
 
 
 def test_noalloc_single_kernel_and_empty():
