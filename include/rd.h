@@ -41,14 +41,18 @@
  *   library allocates them stream-ordered on `stream` from a pool of its own
  *   and frees them on the same stream, so concurrent calls on different
  *   streams never share memory.  The partials of a split reduce are summed by
- *   a second kernel in fixed order -- or, for a row reduce of at most 4 rows
- *   cut into at most 8192 pieces in all (4096 for the softmax pair;
- *   RD_COMBINE_LAST_BLOCK, the default there), by the last workgroup of the
- *   one kernel: the others publish their piece results into a buffer of the
- *   stream's own (8192 tagged words and their
- *   values, 96 KB of device memory per stream and device, created by the
- *   first such call on the stream, kept until the process ends, for up to
- *   256 streams), each word tagged with that launch's epoch, a number the
+ *   a second kernel in fixed order -- or, with RD_COMBINE_LAST_BLOCK, in the
+ *   one kernel: for a row reduce of at most 4 rows cut into at most 8192
+ *   pieces in all (4096 for the softmax pair) by its last workgroup, and for
+ *   a column reduce cut into at most 16 slabs of one-wave tiles (256
+ *   columns), no more workgroups than CUs and at most 65536 results outside
+ *   the last slab (not the softmax pair) by the workgroups of the last slab,
+ *   each joining slabs 0, 1, ... of its tile's columns in order (the default
+ *   in both cases).  The others publish their results into a buffer of the
+ *   stream's own (65536 tagged words and 8192 values, 544 KB of device
+ *   memory per stream and device, created by the first such call on the
+ *   stream, kept until the process ends, for up to 256 streams), each word
+ *   tagged with that launch's epoch, a number the
  *   stream gives each launch in turn, so calls on one stream, which never
  *   overlap, never take another call's words, and calls on another stream
  *   never touch them.  Same order, same bits as the second kernel.  Calls on
@@ -368,12 +372,14 @@ typedef enum rd_order {
 typedef enum rd_combine {
     RD_COMBINE_NONE = 0,       /* one pass, no partial sums */
     RD_COMBINE_PASS = 1,       /* a second kernel sums them in fixed order */
-    RD_COMBINE_LAST_BLOCK = 2, /* the last workgroup of the first kernel sums
-                                  them in the same order, from results the
-                                  others publish as tagged words (one launch;
-                                  the default for row reduces of at most 4
-                                  rows and 8192 piece words; see "Workspace"
-                                  above) */
+    RD_COMBINE_LAST_BLOCK = 2, /* the last workgroup of the first kernel (of
+                                  a column reduce: each workgroup of the last
+                                  slab) sums them in the same order, from
+                                  results the others publish as tagged words
+                                  (one launch; the default for row reduces of
+                                  at most 4 rows and 8192 piece words and for
+                                  column reduces of at most 16 slabs of
+                                  one-wave tiles; see "Workspace" above) */
     RD_COMBINE_LOOKBACK = 3    /* row scans: one launch, a workgroup per row
                                   piece, each piece's carry summed in a fixed
                                   order from totals that earlier pieces
@@ -486,6 +492,9 @@ typedef struct rd_tune {
                                 per row and no pieces: RD_ORDER_INTERLEAVED */
     int32_t nontemporal;     /* every path: 1 = off, 2 = on */
     int32_t combine;         /* ROWS: 1 = second pass, 2 = last workgroup;
+                                COLS: 1 = second pass, 2 = the last slab's
+                                workgroups (only where the planner's rule
+                                for it holds); COLS_SMALL: 1;
                                 SCAN_ROWS: 1 = the planner's other plans,
                                 3 = look-back */
     int32_t path;            /* inner >= 4: RD_PATH_COLS or RD_PATH_COLS_SMALL

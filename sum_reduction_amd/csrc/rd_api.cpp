@@ -23,14 +23,16 @@ thread_local int t_last_hip = 0;
 // stream creates that stream's buffer.  Calls whose plan needs no
 // workspace, and rd_sum_dim_noalloc, never allocate.
 // Buffers of the single-launch combine: one per stream that has made such a
-// call on the device (up to kPubStreams), each with room for kPubWords piece
-// results -- tagged words and their values -- and the stream's last epoch.
+// call on the device (up to kPubStreams), each with room for kPubColWords
+// tagged words (row pieces use the first kPubWords, with their values; slab
+// results of a column reduce all of them) and the stream's last epoch.
 // A launch publishes its words tagged with a new epoch of its stream; calls
 // on one stream never overlap, so every word a launch finds tagged with its
 // own epoch was written by that launch.  Zeroed when created, and again
 // before an epoch is reused (after 2^32 - 1 launches).
 constexpr int kPubStreams = 256;
 using rd::kPubWords;
+using rd::kPubColWords;
 struct StreamPub {
     uint64_t* words = nullptr;
     float* vals = nullptr;
@@ -49,13 +51,13 @@ struct Device {
 };
 Device g_devices[rd::kMaxDevices];
 
-// A zeroed buffer of kPubWords tagged words and their values, or null if
+// A zeroed buffer of kPubColWords tagged words and kPubWords values, or null if
 // it cannot be had (then the call takes the two-kernel combine, with the
 // same results).
 StreamPub make_pub() {
     StreamPub b;
     void* mem = nullptr;
-    const size_t bytes = size_t(kPubWords) * (sizeof(uint64_t) + sizeof(float));
+    const size_t bytes = size_t(kPubColWords) * sizeof(uint64_t) + size_t(kPubWords) * sizeof(float);
     if (hipMalloc(&mem, bytes) != hipSuccess) return b;
     hipStream_t s = nullptr;
     bool ok = hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess;
@@ -67,7 +69,7 @@ StreamPub make_pub() {
         return b;
     }
     b.words = static_cast<uint64_t*>(mem);
-    b.vals = reinterpret_cast<float*>(b.words + kPubWords);
+    b.vals = reinterpret_cast<float*>(b.words + kPubColWords);
     return b;
 }
 
@@ -105,7 +107,7 @@ bool stream_pub(Device& d, hipStream_t stream, rd::Published* pub, hipError_t* e
     }
     StreamPub& b = it->second;
     if (++b.epoch == 0) {  // every epoch used: clear the words, start again
-        *err = hipMemsetAsync(b.words, 0, size_t(kPubWords) * sizeof(uint64_t), stream);
+        *err = hipMemsetAsync(b.words, 0, size_t(kPubColWords) * sizeof(uint64_t), stream);
         if (*err != hipSuccess) return false;
         b.epoch = 1;
     }
@@ -254,7 +256,11 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
         if (st != RD_OK) return st;
         if (injected().alloc) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
         const int64_t words = (op == RD_OP_SOFTMAX_DENOM ? 2 : 1) * v.outer * v.inner * p.split;
-        if (p.path == RD_PATH_ROWS && p.combine == RD_COMBINE_LAST_BLOCK && words <= kPubWords) {
+        const bool rows_one = p.path == RD_PATH_ROWS && words <= kPubWords;
+        // the slab results a column reduce publishes: all but the last slab's
+        const bool cols_one = p.path == RD_PATH_COLS && op != RD_OP_SOFTMAX_DENOM &&
+                              v.outer * v.inner * (p.split - 1) <= kPubColWords;
+        if (p.combine == RD_COMBINE_LAST_BLOCK && (rows_one || cols_one)) {
             hipError_t pe = hipSuccess;
             published = stream_pub(dev, s, &pub, &pe);
             if (pe != hipSuccess) return hip_fail(pe, RD_ERR_HIP);
@@ -296,8 +302,12 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
             break;
         case RD_PATH_COLS:
         case RD_PATH_COLS_SMALL: {
+            if (published) {  // the last slab's blocks join the slabs in one launch
+                e = rd::launch_cols(op, p, x, v, rd::Results{}, &pub, out, s);
+                break;
+            }
             const rd::Results dst = p.split == 1 ? out : part;
-            e = p.path == RD_PATH_COLS ? rd::launch_cols(op, p, x, v, dst, s)
+            e = p.path == RD_PATH_COLS ? rd::launch_cols(op, p, x, v, dst, nullptr, rd::Results{}, s)
                                        : rd::launch_cols_small(op, p, x, v, dst, s);
             if (e == hipSuccess && p.split > 1)
                 e = rd::launch_slab_combine(op, part, p.split, nout, out, s);

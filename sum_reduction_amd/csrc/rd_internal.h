@@ -81,6 +81,14 @@ hipError_t launch_fill_start(int op, Results out, int64_t n, hipStream_t s);
 // gives the single-launch combine.
 constexpr int64_t kPubWords = 8192;
 constexpr int64_t kPubMaxRows = 4;
+// The same for a column reduce cut into a few slabs (at most kPubColMaxSlabs,
+// the blocks within one per CU, so all of them run at once): every block
+// but those of the last slab publishes its slab's column results as tagged
+// words at words[(s*outer + o)*inner_out + k], and the last slab's block of
+// each tile joins slabs 0 .. S-1 of its columns in that order (the second
+// kernel's order, so the same bits) into out.  At most kPubColWords words.
+constexpr int64_t kPubColWords = 65536;
+constexpr int64_t kPubColMaxSlabs = 16;
 struct Published {
     uint64_t* words = nullptr;
     float* vals = nullptr;
@@ -96,9 +104,11 @@ hipError_t launch_rows_short(int op, const float* x, const Strides& v, Results o
                              hipStream_t s);
 hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, Results out,
                                hipStream_t s);
-// Columns (v.si == 1, or a dense_columns view).
+// Columns (v.si == 1, or a dense_columns view).  pub == nullptr: dst
+// receives the slab results (or the outputs when p.split == 1); otherwise
+// the slabs are joined in the same launch into out (kPubColWords).
 hipError_t launch_cols(int op, const rd_plan& p, const float* x, const Strides& v,
-                       Results dst, hipStream_t s);
+                       Results dst, const Published* pub, Results out, hipStream_t s);
 hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, const Strides& v,
                              Results dst, hipStream_t s);
 // Any strides: one lane per (slab, output); dst is the output when

@@ -793,13 +793,59 @@ __global__ __launch_bounds__(kBlock) void rows_combine_kernel(typename St<OP>::O
 // span of its rows and only every cstride-th column is kept (each column has
 // accumulator lanes of its own, so the floats in between never reach a kept
 // result).
+// pub.words != nullptr (one-wave tiles with row waves, one float per result,
+// at most kPubColMaxSlabs slabs, a workgroup per item, all resident): the
+// slabs are joined in the same launch.  The workgroups of slabs 0 .. S-2
+// publish their results as tagged words at pub.words[(s*outer + o)*inner_out
+// + k]; in the workgroup of the last slab, wave rw fetches slabs rw, rw + RW,
+// ... of its tile's columns into LDS (a wait that runs out gives NaN), and
+// wave 0 joins slab 0, 1, ..., S-2 and its own result in that order into out
+// -- slab_combine_kernel's order, so the same bits.
+template <int CW, int RW, int OP>
+constexpr bool cols_pub_shape() {
+    return CW == 1 && RW > 1 && OP != RD_OP_SOFTMAX_DENOM;
+}
+
+template <int OP, int CW, int RW>
+constexpr int cols_lds_slots() {
+    if constexpr (cols_pub_shape<CW, RW, OP>())
+        return (RW - 1 > kPubColMaxSlabs - 1 ? RW - 1 : int(kPubColMaxSlabs) - 1) * kWave;
+    return RW > 1 ? (RW - 1) * CW * kWave : 1;
+}
+
+// The four tagged words at base + idx[q] (idx[q] < 0: none, its lane 0),
+// polled together until each carries `tag`, at most spin_limit + 1 times; a
+// word that never comes gives NaN.
+__device__ __forceinline__ v4f await_words4(const uint64_t* base, const int64_t (&idx)[4],
+                                            uint32_t tag, uint32_t spin_limit) {
+    v4f r = {0.f, 0.f, 0.f, 0.f};
+    for (uint32_t it = 0;; ++it) {
+        uint64_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[q] = idx[q] >= 0 ? __hip_atomic_load(base + idx[q], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : uint64_t(tag) << 32;
+        bool all = true;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool ok = uint32_t(w[q] >> 32) == tag;
+            all = all && ok;
+            r[q] = ok ? __builtin_bit_cast(float, uint32_t(w[q]))
+                      : (it >= spin_limit ? __builtin_nanf("") : r[q]);
+        }
+        if (all || it >= spin_limit) return r;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 template <int OP, int CW, int RW, int U, bool NT>
 __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
     const float* __restrict__ x, int64_t outer, int64_t R, int64_t inner, int64_t so,
     int64_t sr, int64_t ntiles, int64_t S, int64_t rps, int64_t cstride, int64_t inner_out,
-    typename St<OP>::Out dst, uint32_t nxcd) {
+    typename St<OP>::Out dst, uint32_t nxcd, Published pub, typename St<OP>::Out out) {
     typedef St<OP> T;
-    __shared__ typename T::S4 lds[RW > 1 ? (RW - 1) * CW * kWave : 1];
+    __shared__ typename T::S4 lds[cols_lds_slots<OP, CW, RW>()];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int cw = wave % CW;
@@ -866,6 +912,42 @@ __global__ __launch_bounds__(kWave* CW* RW) void cols_kernel(
                     a = T::join(a, lds[((q - 1) * CW + cw) * kWave + lane]);
             }
             __syncthreads();
+        }
+        if constexpr (cols_pub_shape<CW, RW, OP>()) {
+            if (pub.words) {
+                // this lane's kept columns: their result index in o's row, or -1
+                int64_t idx[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = cl + q;
+                    const int64_t k = cstride == 1 ? col : col / cstride;
+                    idx[q] = active && col >= c && k * cstride == col ? k : -1;
+                }
+                if (s + 1 < S) {
+                    if (rw == 0) {
+                        uint64_t* w = pub.words + (s * outer + o) * inner_out;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (idx[q] >= 0) publish_word(w + idx[q], pub.epoch, T::lane(a, q));
+                    }
+                    continue;
+                }
+                for (int64_t j = rw; j < S - 1; j += RW)
+                    lds[j * kWave + lane] = await_words4(pub.words + (j * outer + o) * inner_out,
+                                                         idx, pub.epoch, pub.spin_limit);
+                __syncthreads();
+                if (rw == 0) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (idx[q] < 0) continue;
+                        float t = lds[lane][q];
+                        for (int64_t j = 1; j < S - 1; ++j) t = T::join(t, lds[j * kWave + lane][q]);
+                        T::put(out, o * inner_out + idx[q], T::join(t, T::lane(a, q)));
+                    }
+                }
+                __syncthreads();
+                continue;
+            }
         }
         if (rw == 0 && active) {
             const int keep = int(c - cl);  // 0, or 1..3 for the row's last lane
@@ -1231,15 +1313,26 @@ struct ColsArgs {
     int64_t outer, R, inner, so, sr;
     Results dst;
     int64_t cstride, inner_out;
+    Published pub;  // words == nullptr: no single-launch combine
+    Results out;
 };
 
 template <int OP, int CW, int RW, int U, bool NT>
 hipError_t cols_go(const rd_plan& p, const ColsArgs& a, hipStream_t s) {
     if constexpr (cols_built(OP, CW, RW, U)) {
         const int64_t ntiles = ((a.inner + 3) / 4 + CW * kWave - 1) / (CW * kWave);
+        if (a.pub.words) {
+            // every item a workgroup of its own (none waits for itself), the
+            // shape and sizes the single-launch combine is built for
+            if (!cols_pub_shape<CW, RW, OP>() || p.split < 2 || p.split > kPubColMaxSlabs ||
+                p.blocks < ntiles * p.split * a.outer ||
+                (p.split - 1) * a.outer * a.inner_out > kPubColWords)
+                return hipErrorInvalidValue;
+        }
         return launch(cols_kernel<OP, CW, RW, U, NT>, p.blocks, kWave * CW * RW, s, a.x,
                       a.outer, a.R, a.inner, a.so, a.sr, ntiles, p.split, p.rows_per_split,
-                      a.cstride, a.inner_out, out_of<OP>(a.dst), uint32_t(p.nxcd));
+                      a.cstride, a.inner_out, out_of<OP>(a.dst), uint32_t(p.nxcd), a.pub,
+                      out_of<OP>(a.out));
     } else {
         return hipErrorInvalidValue;
     }
@@ -1428,17 +1521,18 @@ hipError_t launch_rows_combine(int op, Results part, int64_t outer, int64_t P, R
 }
 
 hipError_t launch_cols(int op, const rd_plan& p, const float* x, const Strides& v,
-                       Results dst, hipStream_t s) {
+                       Results dst, const Published* pub, Results out, hipStream_t s) {
     if (v.si != 1 && !dense_columns(v)) return hipErrorInvalidValue;
     const int64_t span = (v.inner - 1) * v.si + 1;  // v.inner for an array
-    const ColsArgs a{x, v.outer, v.R, span, v.so, v.sr, dst, v.si, v.inner};
+    const ColsArgs a{x, v.outer, v.R, span, v.so, v.sr, dst, v.si, v.inner,
+                     pub ? *pub : Published{}, out};
     RD_BY_OP(op, cols_op, p, a, s)
 }
 
 hipError_t launch_cols_small(int op, const rd_plan& p, const float* x, const Strides& v,
                              Results dst, hipStream_t s) {
     if (v.si != 1) return hipErrorInvalidValue;
-    const ColsArgs a{x, v.outer, v.R, v.inner, v.so, v.sr, dst, 1, v.inner};
+    const ColsArgs a{x, v.outer, v.R, v.inner, v.so, v.sr, dst, 1, v.inner, Published{}, Results{}};
     RD_BY_OP(op, cols_small_go, p, a, s)
 }
 

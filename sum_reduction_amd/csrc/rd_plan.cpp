@@ -215,6 +215,7 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int64_t inn
             p->unroll = 2 * kColsUnroll;
         if (!small_shape_supported(op, p->unroll)) return RD_ERR_INVALID_ARG;
         if (!nontemporal_choice(t, true, &p->nontemporal)) return RD_ERR_INVALID_ARG;
+        if (t && t->combine && t->combine != RD_COMBINE_PASS) return RD_ERR_INVALID_ARG;
         const int64_t lc = ceil_div(inner, 4);
         const int64_t rpw = kWave / lc;
         const int64_t waves_per_block = kBlock / kWave;
@@ -311,8 +312,23 @@ rd_status plan_cols(int cu, int64_t outer, int64_t R, int64_t inner, int64_t inn
     if (p->split > INT64_MAX / result_bytes(op) / (outer * inner_out)) return RD_ERR_INVALID_ARG;
     p->blocks = base * p->split;
     if (p->blocks > kMaxBlocks) p->blocks = kMaxBlocks;
-    p->passes = p->split > 1 ? 2 : 1;
-    p->combine = p->split > 1 ? RD_COMBINE_PASS : RD_COMBINE_NONE;
+    p->combine = RD_COMBINE_NONE;
+    if (p->split > 1) {
+        // A few slabs of one-wave tiles, a workgroup per item and no more
+        // workgroups than CUs: the last slab's workgroups join the others'
+        // published results in the same launch (cols_kernel), which saves the
+        // second kernel and the gap before it.  Limited to kPubColMaxSlabs,
+        // as many as the last slab's waves fetch in two rounds.
+        const bool one = op != RD_OP_SOFTMAX_DENOM && p->col_waves == 1 && p->row_waves > 1 &&
+                         p->split <= kPubColMaxSlabs && p->blocks == base * p->split &&
+                         p->blocks <= cu && (p->split - 1) * outer * inner_out <= kPubColWords;
+        const int32_t c = (t && t->combine) ? t->combine
+                                            : (one ? RD_COMBINE_LAST_BLOCK : RD_COMBINE_PASS);
+        if (c != RD_COMBINE_PASS && !(c == RD_COMBINE_LAST_BLOCK && one))
+            return RD_ERR_INVALID_ARG;
+        p->combine = c;
+    }
+    p->passes = p->combine == RD_COMBINE_PASS ? 2 : 1;
     p->workspace_bytes = p->split > 1 ? p->split * outer * inner_out * result_bytes(op) : 0;
     return RD_OK;
 }

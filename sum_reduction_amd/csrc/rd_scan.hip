@@ -1534,7 +1534,7 @@ hipError_t slab_totals(const rd_plan& p, const float* x, const Strides& v, float
     const int64_t tiles = ((v.inner + 3) / 4 + kWave - 1) / kWave;
     q.blocks = tiles * p.split * v.outer;
     if (q.blocks > kMaxBlocks) q.blocks = kMaxBlocks;
-    return launch_cols(RD_OP_SUM, q, x, v, Results{totals, nullptr}, s);
+    return launch_cols(RD_OP_SUM, q, x, v, Results{totals, nullptr}, nullptr, Results{}, s);
 }
 
 template <bool REV, int V, bool NT>

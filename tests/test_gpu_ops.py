@@ -135,6 +135,148 @@ def test_column_slab_plans(op):
     _sweep_dim(op, SLAB_SHAPES, [0, 1, 3], 750 + rd.OPS[op], "cols slabs")
 
 
+# few slabs of one-wave tiles: the planner joins them in the one launch
+ONE_LAUNCH_SHAPES = [(1, 5000, 4095), (1, 300, 130), (4, 1031, 2048), (1, 257, 4100),
+                     (2, 100, 1000), (2, 5000, 3000), (1, 200, 4097), (1, 100, 20000)]
+ALL_OPS = ("sum",) + OPS3
+
+
+def _dims_on_stream(dev, cases, op, stream=None):
+    """rd_reduce_dim of every (shape, offset) case, one call after another."""
+    lib = rd.load()
+    slots = H.OutSlots([o * i for (o, r, i), _ in cases])
+    for k, ((o, r, i), off) in enumerate(cases):
+        x = dev[off:off + o * r * i]
+        st = lib.rd_reduce_dim(x.data_ptr(), o, r, i, rd.OPS[op], slots.ptr(k),
+                               stream if stream is not None else H.stream_handle())
+        assert st == 0, (op, (o, r, i), off, rd.rd_status_string(st))
+    return slots.fetch()
+
+
+@pytest.mark.parametrize("op", ALL_OPS)
+def test_column_slabs_one_launch(op):
+    """A few slabs of one-wave tiles (at most 16, the grid within the CUs)
+    are joined by the last slab's workgroups in the same launch, from results
+    the other slabs publish as tagged words: on normal data, bit for bit the
+    second kernel's results (combine = 1, the same join order), and against
+    the oracle (maximum and minimum exactly, the sums within 1e-5 * sum|x| +
+    1e-6).  The calls follow one another on one stream, each finding the
+    words of earlier epochs in the buffer."""
+    cu = _device_cus()
+    for o, r, i in ONE_LAUNCH_SHAPES:
+        p = rd.rd_plan_reduce(cu, o, r, i, op)
+        assert (p.as_dict()["combine"], p.passes) == ("last_block", 1), ((o, r, i), p.as_dict())
+    cases = [(s, off) for s in ONE_LAUNCH_SHAPES for off in (0, 1)]
+    maxn = max(o * r * i for o, r, i in ONE_LAUNCH_SHAPES)
+    data = workloads.random(maxn + 2, 770 + rd.OPS[op], "normal")
+    dev = H.upload(data)
+    H.say("column slabs in one launch, %s: %d calls each way" % (op, len(cases)))
+    one = _dims_on_stream(dev, cases, op)
+    with rd.tuning(combine=1):
+        two = _dims_on_stream(dev, cases, op)
+    for k, ((o, r, i), off) in enumerate(cases):
+        what = "one launch %s shape=%s off=%d" % (op, (o, r, i), off)
+        assert np.array_equal(one[k].view(np.uint32), two[k].view(np.uint32)), what
+        S, A = oracle.reduce_dim(data[off:off + o * r * i], o, r, i, op, threads=1)
+        if op in ("max", "min"):
+            H.assert_bitwise_equal_oracle(one[k], S, what)
+        else:
+            H.assert_within_tolerance(one[k], S, A, what)
+
+
+def test_column_slabs_one_launch_views():
+    """Views read as the dense span of their rows (kept columns 2 and 3
+    floats apart) in a plan of a few slabs: the last slab's workgroups keep
+    every stride-th column of the words they join; bit for bit the second
+    kernel's results, and the oracle's on a contiguous copy of the view."""
+    t = H.torch()
+    cu = _device_cus()
+    base = workloads.random(900 * 6000, 780, "normal")
+    dev = H.upload(base).view(900, 6000)
+    for rs, cs in ((2, 3), (3, 2), (1, 3)):
+        v = dev[::rs, ::cs]
+        R, inner = v.shape
+        st = (0, v.stride(0), v.stride(1))
+        p = rd.rd_plan_strided(cu, 1, R, inner, *st)
+        assert p.as_dict()["combine"] == "last_block", ((rs, cs), p.as_dict())
+        for op in ALL_OPS:
+            one = rd.rd_reduce_strided(dev, 1, R, inner, *st, op=op).cpu().numpy()
+            with rd.tuning(combine=1):
+                two = rd.rd_reduce_strided(dev, 1, R, inner, *st, op=op).cpu().numpy()
+            what = "view [::%d, ::%d] %s" % (rs, cs, op)
+            assert np.array_equal(one.view(np.uint32), two.view(np.uint32)), what
+            host = v.contiguous().cpu().numpy()
+            S, A = oracle.reduce_dim(host, 1, R, inner, op, threads=1)
+            if op in ("max", "min"):
+                H.assert_bitwise_equal_oracle(one.reshape(1, -1), S, what)
+            else:
+                H.assert_within_tolerance(one.reshape(1, -1), S, A, what)
+    t.cuda.synchronize()
+
+
+def test_column_slabs_one_launch_streams():
+    """Column reduces joined in one launch on four streams at once, 8 calls
+    each, exact integer data: each stream's calls use its own buffer."""
+    t = H.torch()
+    shapes = [(2, 5000, 3000), (1, 257, 4100), (4, 1031, 2048), (1, 100, 20000)]
+    maxn = max(o * r * i for o, r, i in shapes)
+    data = workloads.small_ints(maxn, 790)
+    dev = H.upload(data)
+    want = [oracle.sum_dim(data[:o * r * i], o, r, i)[0].astype(np.float32)
+            for o, r, i in shapes]
+    streams = [t.cuda.Stream() for _ in range(4)]
+    outs = []
+    t.cuda.synchronize()
+    for k in range(32):
+        o, r, i = shapes[k % 4]
+        with t.cuda.stream(streams[k // 8]):
+            outs.append((k % 4, rd.reduce(dev[:o * r * i].view(o, r, i), "sum", 1)))
+    t.cuda.synchronize()
+    for j, got in outs:
+        assert np.array_equal(got.cpu().numpy(), want[j]), shapes[j]
+
+
+_COL_PUB_SPIN = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import torch
+import sum_reduction_amd as rd
+import workloads
+from tests import gpu_helpers as H
+o, R, i = 4, 8192, 2048
+assert rd.rd_plan_dim(256, o, R, i).as_dict()["combine"] == "last_block"
+a = workloads.small_ints(o * R * i, 795)
+x = H.upload(a)
+from oracle import sum_dim
+want = sum_dim(a, o, R, i)[0].astype(np.float32)
+nan = 0
+for _ in range(20):
+    got = rd.rd_sum_dim(x, o, R, i).cpu().numpy()
+    bad = ~((got == want) | np.isnan(got))
+    assert not bad.any(), (got[bad][:5], want[bad][:5])
+    nan += int(np.isnan(got).sum())
+print("col-pub-spin-ok", nan)
+"""
+
+
+def test_column_slabs_one_launch_wait_limit():
+    """The last slab's waits bounded from the host: with RD_TEST_SPIN_LIMIT=0
+    each unready word is polled once.  Every call ends, each output the
+    exact sum or NaN, never a wrong finite value.  (Read once per process:
+    a child process.)"""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, RD_TEST_SPIN_LIMIT="0")
+    res = subprocess.run([sys.executable, "-c", _COL_PUB_SPIN, root], env=env,
+                         capture_output=True, text=True, timeout=240, cwd=root)
+    assert res.returncode == 0 and "col-pub-spin-ok" in res.stdout, \
+        res.stdout + res.stderr[-3000:]
+    H.say(res.stdout.strip())
+
+
 SMALL = [(op, s, nt) for op in OPS3 for s in (1, 3) for nt in (1, 2)]
 
 

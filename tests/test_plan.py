@@ -43,7 +43,17 @@ def check_invariants(p, outer, R, inner, cu=CU):
         assert p.split * p.rows_per_split >= R
         assert (p.split - 1) * p.rows_per_split < R
         assert p.workspace_bytes == (4 * p.split * outer * inner if p.split > 1 else 0)
-        assert p.passes == (2 if p.split > 1 else 1)
+        # a few slabs of one-wave tiles, every workgroup resident, are joined
+        # by the last slab's workgroups in the one launch, others by a second
+        # kernel
+        one = False
+        if d["path"] == "cols" and p.split > 1:
+            tiles = -(-(-(-inner // 4)) // (64 * p.col_waves))
+            one = (p.col_waves == 1 and p.row_waves > 1 and p.split <= 16
+                   and p.blocks == tiles * outer * p.split <= cu
+                   and (p.split - 1) * outer * inner <= 65536)
+        assert d["combine"] == (("last_block" if one else "pass") if p.split > 1 else "none"), d
+        assert p.passes == (2 if p.split > 1 and not one else 1)
         if d["path"] == "cols":
             assert inner > 128
             assert p.block_threads == 64 * p.col_waves * p.row_waves <= 1024
@@ -205,6 +215,45 @@ def test_column_slabs_of_one_tile(op):
             assert p.blocks == tiles * outer * p.split <= cu, (outer, R, inner, cu)
             if op != "softmax_denom":   # (its partial results are pairs)
                 check_invariants(p, outer, R, inner, cu)
+            # the slabs joined in the one launch, up to 16 of them and 65536
+            # published words (the softmax pair: a second kernel)
+            one = (op != "softmax_denom" and 1 < p.split <= 16
+                   and (p.split - 1) * outer * inner <= 65536)
+            assert p.as_dict()["combine"] == ("last_block" if one else
+                                              "pass" if p.split > 1 else "none"), (outer, R, inner, cu)
+            assert p.passes == (1 if one or p.split == 1 else 2)
+
+
+def test_column_slab_combine_tuning():
+    """combine = 1 keeps the second kernel for slabs the planner would join in
+    one launch; 2 is taken only where the single launch is built (one-wave
+    tiles with row waves, at most 16 slabs, the grid within the CUs);
+    anything else is refused."""
+    p = rd.rd_plan_dim(CU, 1, 4096, 10922)
+    assert (p.as_dict()["combine"], p.passes, p.split) == ("last_block", 1, 5)
+    with rd.tuning(combine=1):
+        q = rd.rd_plan_dim(CU, 1, 4096, 10922)
+        assert (q.as_dict()["combine"], q.passes) == ("pass", 2)
+        assert (q.split, q.blocks, q.workspace_bytes) == (p.split, p.blocks, p.workspace_bytes)
+    with rd.tuning(combine=2):
+        assert rd.rd_plan_dim(CU, 4, 8192, 2048).as_dict()["combine"] == "last_block"
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 1, 1 << 20, 64)            # cols_small
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 1, 2_000_000, 512)         # 128 slabs of 2 tiles
+    with rd.tuning(combine=2, split=4, col_waves=2, row_waves=1, unroll=4):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 1, 4096, 10922)            # wide tiles
+    with rd.tuning(combine=2, split=40, col_waves=1, row_waves=8, unroll=4):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 1, 4096, 1024)             # more than 16 slabs
+    with rd.tuning(combine=3):
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_dim(CU, 1, 4096, 10922)
+    with rd.tuning(combine=2, split=3):
+        assert rd.rd_plan_reduce(CU, 1, 4096, 10922, "max").as_dict()["combine"] == "last_block"
+        with pytest.raises(rd.RdError):
+            rd.rd_plan_reduce(CU, 1, 4096, 10922, "softmax_denom")
 
 
 def test_forced_column_path():
