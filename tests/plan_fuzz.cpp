@@ -68,7 +68,7 @@ void fail(const char* what, const rd::Strides& v, int op, const rd_plan& p) {
     exit(3);
 }
 
-void check_reduce_plan(const rd::Strides& v, int op, const rd_plan& p) {
+void check_reduce_plan(const rd::Strides& v, int op, const rd_plan& p, int cu) {
     const int64_t max_blocks = rd::kMaxBlocks;
     if (p.path == RD_PATH_NONE) {
         if (v.outer * v.inner != 0) fail("NONE with outputs", v, op, p);
@@ -101,6 +101,17 @@ void check_reduce_plan(const rd::Strides& v, int op, const rd_plan& p) {
                 fail("slabs do not tile R", v, op, p);
             if (p.split > 1 && p.workspace_bytes / bytes != p.split * v.outer * v.inner)
                 fail("slab workspace", v, op, p);
+            if (p.combine == RD_COMBINE_LAST_BLOCK) {
+                // the last slab's workgroups wait for the others: one item
+                // each, all resident, within the words and LDS slots built
+                const int64_t span = (v.inner - 1) * v.si + 1;
+                const int64_t tiles_n = ((span + 3) / 4 + 63) / 64;
+                if (p.path != RD_PATH_COLS || op == RD_OP_SOFTMAX_DENOM || p.col_waves != 1 ||
+                    p.row_waves < 2 || p.split < 2 || p.split > rd::kPubColMaxSlabs ||
+                    p.blocks != tiles_n * v.outer * p.split || p.blocks > cu ||
+                    (p.split - 1) * v.outer * v.inner > rd::kPubColWords)
+                    fail("column slabs joined in one launch", v, op, p);
+            }
             break;
         case RD_PATH_STRIDED:
             if (v.sr == 1 || (v.si == 1 && v.inner > 1)) fail("strided path with a unit stride", v, op, p);
@@ -231,7 +242,7 @@ int main(int argc, char** argv) {
         rd_plan p;
         if (rd::plan_view(cu, &w, op, tuned ? &t : nullptr, &p) == RD_OK) {
             ++accepted;
-            check_reduce_plan(w, op, p);
+            check_reduce_plan(w, op, p, cu);
         }
         rd::Strides u = v;
         rd_plan q;
