@@ -236,6 +236,52 @@ def test_column_slabs_one_launch_streams():
         assert np.array_equal(got.cpu().numpy(), want[j]), shapes[j]
 
 
+def test_one_launch_fallbacks_match():
+    """A stream that gets no buffer of its own -- the per-thread default
+    stream (one handle, a different stream in each thread), or streams past
+    the 256 a device keeps buffers for -- takes the second kernel for the row
+    and column reduces that would otherwise join their partial results in one
+    launch: the same bits as calls on a stream with a buffer."""
+    import ctypes
+    t = H.torch()
+    lib = rd.load()
+    vp = ctypes.c_void_p
+    create, sync, destroy = lib.hipStreamCreate, lib.hipStreamSynchronize, lib.hipStreamDestroy
+    create.argtypes, sync.argtypes, destroy.argtypes = [ctypes.POINTER(vp)], [vp], [vp]
+    create.restype = sync.restype = destroy.restype = ctypes.c_int
+    n, cols = 1_000_003, (2, 100, 1000)
+    assert rd.rd_plan_1d(256, n).as_dict()["combine"] == "last_block"
+    assert rd.rd_plan_dim(256, *cols).as_dict()["combine"] == "last_block"
+    a = workloads.random(n, 797, "normal")
+    x = H.upload(a)
+    o, r, i = cols
+    xc = x[:o * r * i]
+    want1 = rd.rd_sum_1d(x).cpu().numpy().view(np.uint32)
+    want2 = rd.rd_sum_dim(xc, o, r, i).cpu().numpy().view(np.uint32)
+    streams = []
+    try:
+        for _ in range(300):
+            h = vp()
+            assert create(ctypes.byref(h)) == 0
+            streams.append(h.value)
+        per_thread = 2  # hipStreamPerThread
+        handles = [per_thread] + streams
+        outs = t.empty((len(handles), 1 + o * i), device="cuda")
+        t.cuda.synchronize()
+        for k, h in enumerate(handles):
+            assert lib.rd_sum_1d(x.data_ptr(), n, outs[k].data_ptr(), h) == 0
+            assert lib.rd_sum_dim(xc.data_ptr(), o, r, i, outs[k, 1:].data_ptr(), h) == 0
+        for h in handles:
+            assert sync(h) == 0
+        got = outs.cpu().numpy()
+    finally:
+        for h in streams:
+            destroy(h)
+    for k in range(len(handles)):
+        assert got[k, :1].view(np.uint32)[0] == want1[0], k
+        assert np.array_equal(got[k, 1:].view(np.uint32), want2.reshape(-1)), k
+
+
 _COL_PUB_SPIN = r"""
 import sys
 sys.path.insert(0, sys.argv[1])
