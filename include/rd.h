@@ -458,10 +458,15 @@ rd_status rd_plan_strided(int cu_count, int64_t outer, int64_t R, int64_t inner,
  * carry is the sum, in index order, of the totals that earlier pieces of its
  * row publish (the pieces are taken in the order of a ticket each workgroup
  * draws at its start, so a piece only ever waits for pieces of workgroups
- * that started before it; the same bits on every run).  Its workspace, a
- * 256-byte ticket and 8 bytes per piece and per group of 64 pieces, is
- * zeroed in stream order before the launch.  A wait of this kernel ends
- * after at most 2^18 polls; a piece whose wait runs out writes NaN. */
+ * that started before it; the same bits on every run).  Its workspace is a
+ * 256-byte ticket and 8 bytes per piece and per group of 64 pieces (none
+ * with one piece per row): up to 65536 such words it is the stream's own
+ * buffer of the single-launch combine ("Workspace" above), whose ticket the
+ * workgroup that draws the last one sets back to 0 and whose words carry the
+ * launch's epoch, so nothing is zeroed before the launch; otherwise (or on
+ * the per-thread default stream) a workspace zeroed in stream order before
+ * it.  A wait of this kernel ends after at most 2^18 polls; a piece whose
+ * wait runs out writes NaN. */
 rd_status rd_plan_cumsum(int cu_count, int64_t outer, int64_t R, int64_t inner,
                          rd_plan* plan);
 

@@ -25,7 +25,8 @@ thread_local int t_last_hip = 0;
 // Buffers of the single-launch combine: one per stream that has made such a
 // call on the device (up to kPubStreams), each with room for kPubColWords
 // tagged words (row pieces use the first kPubWords, with their values; slab
-// results of a column reduce all of them) and the stream's last epoch.
+// results of a column reduce and the totals of a look-back row scan all of
+// them), the look-back scan's ticket and the stream's last epoch.
 // A launch publishes its words tagged with a new epoch of its stream; calls
 // on one stream never overlap, so every word a launch finds tagged with its
 // own epoch was written by that launch.  Zeroed when created, and again
@@ -36,6 +37,7 @@ using rd::kPubColWords;
 struct StreamPub {
     uint64_t* words = nullptr;
     float* vals = nullptr;
+    uint32_t* ticket = nullptr;
     uint32_t epoch = 0;
 };
 struct Device {
@@ -51,13 +53,14 @@ struct Device {
 };
 Device g_devices[rd::kMaxDevices];
 
-// A zeroed buffer of kPubColWords tagged words and kPubWords values, or null if
-// it cannot be had (then the call takes the two-kernel combine, with the
-// same results).
+// A zeroed buffer of kPubColWords tagged words, kPubWords values and a
+// ticket, or null if it cannot be had (then the call takes the two-kernel
+// combine, or the zeroed workspace, with the same results).
 StreamPub make_pub() {
     StreamPub b;
     void* mem = nullptr;
-    const size_t bytes = size_t(kPubColWords) * sizeof(uint64_t) + size_t(kPubWords) * sizeof(float);
+    const size_t vals_end = size_t(kPubColWords) * sizeof(uint64_t) + size_t(kPubWords) * sizeof(float);
+    const size_t bytes = vals_end + size_t(rd::kLookTicketBytes);
     if (hipMalloc(&mem, bytes) != hipSuccess) return b;
     hipStream_t s = nullptr;
     bool ok = hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess;
@@ -70,6 +73,7 @@ StreamPub make_pub() {
     }
     b.words = static_cast<uint64_t*>(mem);
     b.vals = reinterpret_cast<float*>(b.words + kPubColWords);
+    b.ticket = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + vals_end);
     return b;
 }
 
@@ -113,6 +117,7 @@ bool stream_pub(Device& d, hipStream_t stream, rd::Published* pub, hipError_t* e
     }
     pub->words = b.words;
     pub->vals = b.vals;
+    pub->ticket = b.ticket;
     pub->epoch = b.epoch;
     return true;
 }
@@ -383,12 +388,25 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
         }
     }
     float* ws = nullptr;
+    rd::Published pub;
+    bool published = false;
     if (p.workspace_bytes > 0) {
         st = capture_check(stream);
         if (st != RD_OK) return st;
+        if (injected().alloc) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
+        // a look-back whose totals fit the stream's buffer takes it: its
+        // words are tagged with the launch's epoch and its ticket is 0
+        // between launches, so nothing is zeroed before the launch
+        if (p.path == RD_PATH_SCAN_ROWS && p.combine == RD_COMBINE_LOOKBACK &&
+            rd::lookback_words(v.outer * v.inner, p.split) <= kPubColWords) {
+            hipError_t pe = hipSuccess;
+            published = stream_pub(*dev, stream, &pub, &pe);
+            if (pe != hipSuccess) return hip_fail(pe, RD_ERR_HIP);
+        }
+    }
+    if (p.workspace_bytes > 0 && !published) {
         st = device_memory(*dev);
         if (st != RD_OK) return st;
-        if (injected().alloc) return hip_fail(hipErrorOutOfMemory, RD_ERR_ALLOC);
         hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
                                               size_t(p.workspace_bytes), dev->pool, stream);
         if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
@@ -401,7 +419,8 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
     if (uint64_t(nrow * v.R) * sizeof(float) <= rd::kScanCachedTotalsBytes) pt.nontemporal = 0;
     hipError_t e = hipSuccess;
     if (p.path == RD_PATH_SCAN_ROWS && p.combine == RD_COMBINE_LOOKBACK) {
-        e = rd::launch_scan_rows_lookback(p, rev, x, out, v, ws, injected().spin_limit, stream);
+        e = rd::launch_scan_rows_lookback(p, rev, x, out, v, ws, published ? &pub : nullptr,
+                                          injected().spin_limit, stream);
     } else if (p.path == RD_PATH_SCAN_ROWS) {
         if (p.split == 1) {
             e = rd::launch_scan_rows(p, rev, x, out, v, nullptr, nullptr, stream);

@@ -92,6 +92,7 @@ constexpr int64_t kPubColMaxSlabs = 16;
 struct Published {
     uint64_t* words = nullptr;
     float* vals = nullptr;
+    uint32_t* ticket = nullptr;  // the look-back scan's ticket: 0 between launches
     uint32_t epoch = 0;
     uint32_t spin_limit = 0;
 };
@@ -130,10 +131,15 @@ hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, floa
 hipError_t launch_scan_carries(const float* totals, float* carries, int64_t rows, int64_t P,
                                hipStream_t s);
 // Rows in one pass by a fixed-order look-back (p.combine RD_COMBINE_LOOKBACK):
-// p.split pieces of one block chunk per row, a workgroup each; ws holds
-// p.workspace_bytes, which the call zeroes (in stream order) and the kernel
-// uses for its ticket and the published totals.  A wait of the kernel ends
-// after spin_limit polls (the piece's outputs are then NaN).
+// p.split pieces of one block chunk per row, a workgroup each.  pub ==
+// nullptr: ws holds p.workspace_bytes, which the call zeroes (in stream
+// order) and the kernel uses for its ticket and the published totals (tag 1).
+// Otherwise the stream's buffer serves, with nothing zeroed: its ticket (0
+// between launches: the workgroup that draws the launch's last ticket sets it
+// back to 0) and, with more than one piece per row, lookback_words(outer, P)
+// of its words (at most kPubColWords), tagged with the launch's epoch.  A wait
+// of the kernel ends after spin_limit polls (the piece's outputs are then
+// NaN).
 constexpr int64_t kLookGroup = 64;          // chunk totals per group total
 constexpr int64_t kLookTicketBytes = 256;   // the ticket, padded
 constexpr uint32_t kLookSpinLimit = 1u << 18;
@@ -141,9 +147,14 @@ inline int64_t lookback_groups(int64_t P) { return (P + kLookGroup - 1) / kLookG
 inline int64_t lookback_workspace_bytes(int64_t outer, int64_t P) {
     return kLookTicketBytes + 8 * outer * (P + lookback_groups(P));
 }
+// Tagged words the look-back publishes: chunk totals and group totals, none
+// with one piece per row (no piece has a successor).
+inline int64_t lookback_words(int64_t outer, int64_t P) {
+    return P > 1 ? outer * (P + lookback_groups(P)) : 0;
+}
 hipError_t launch_scan_rows_lookback(const rd_plan& p, bool reverse, const float* x, float* out,
-                                     const Strides& v, void* ws, uint32_t spin_limit,
-                                     hipStream_t s);
+                                     const Strides& v, void* ws, const Published* pub,
+                                     uint32_t spin_limit, hipStream_t s);
 // Columns (inner >= 2, si == 1): item = (64 lane-columns, slab of R, outer index).
 hipError_t launch_scan_cols(const rd_plan& p, bool reverse, const float* x, float* out,
                             const Strides& v, const float* carry_in, float* totals,
@@ -209,10 +220,20 @@ constexpr int64_t kScanRowsWideMinR = 65536;
 // 398.5 -> 381.0, [16, 2^20] 40.4 -> 39.6; shorter rows or smaller arrays
 // lose the zeroing of its workspace (one more dispatch): [1, 2^22] 19.4 ->
 // 21.1, [64, 2^17] 21.8 -> 25.3, [256, 2^18] 95.9 -> 104.7.
+// Since the look-back takes the stream's buffer (nothing zeroed before the
+// launch) it also replaces the three kernels for few rows of at least
+// kScanRowsLookFewMinR positions (fewer rows than a third of the CUs): us,
+// same box, A/B of the two libraries, three kernels (or one workgroup a row)
+// -> look-back: [1, 1000003] 17.8 -> 9.4, [2, 131071] 15.8 -> 7.8, [16,
+// 2^19] 22.0 -> 17.1, [64, 2^17] 21.9 -> 17.4, [80, 2^17] 29.5 -> 24.2, [7,
+// 777777] 22.1 -> 19.3, [64, 2^16] 14.5 -> 12.3, [1, 65537] 12.7 -> 8.1; with
+// more rows one workgroup a row stays ahead ([128, 2^17] 28.9 / 31.7,
+// [256, 2^16] 25.0 / 31.2).
 constexpr int64_t kScanRowWavesMin = 4;
 constexpr int64_t kScanRowsCutMinR = 131072;
 constexpr int64_t kScanRowsLookMinR = int64_t(1) << 20;
 constexpr int64_t kScanRowsLookMinN = int64_t(1) << 24;
+constexpr int64_t kScanRowsLookFewMinR = 65536;
 // Arrays of at least kScanRowsTicketMinBytes whose rows fill an 8-wave
 // chunk take the look-back kernel too: its workgroups take their pieces by a
 // ticket, so all XCDs work on one narrow stretch of the array at a time,

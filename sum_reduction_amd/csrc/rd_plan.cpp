@@ -609,10 +609,13 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         const bool large = R >= chunk8 && outer * R * int64_t(sizeof(float)) >=
                                               (R % chunk16 == 0 ? kScanRowsTicketMinBytes / 2
                                                                 : kScanRowsTicketMinBytes);
+        // fewer rows than a third of the CUs, each of two or more 32768-position
+        // chunks: the look-back in place of the three-kernel scheme
+        const bool few = 3 * outer < cu && R >= kScanRowsLookFewMinR;
         const int32_t look_group = few_long || R % chunk16 == 0 ? 16 * kWave : 8 * kWave;
         const bool look =
             comb == RD_COMBINE_LOOKBACK ||
-            (comb == 0 && !tuned && (few_long || large) &&
+            (comb == 0 && !tuned && (few_long || large || few) &&
              ceil_div(R, int64_t(look_group / kWave) * kWave * 4 * kScanRowsChunkSlices) <=
                  kMaxBlocks / outer);
         if (look) {

@@ -459,16 +459,20 @@ scan_rows_block_kernel(const float* x, float* out, int64_t outer, int64_t R, int
 // run gives the same bits.  A published value is one 64-bit word, 1 in the
 // high half and the float's bits in the low half, stored and loaded by
 // relaxed device-scope atomics: the value travels with its flag, so no fence
-// is needed.  The workspace (ticket, chunk totals, group totals) is zeroed
-// before every launch.  A wait gives up after spin_limit polls and returns
-// NaN, so a piece that could not get its carry writes NaN, never a wrong
-// finite sum.  x and out may be the same array (each element is loaded and
-// stored by the same lane).
+// is needed.  The flag is `tag`: 1 in a workspace zeroed before the launch,
+// or the launch's epoch in a buffer its stream keeps (where earlier launches
+// left words of other epochs).  The ticket starts at 0, and the workgroup
+// that draws the last one sets it back to 0 for the next launch (every
+// workgroup of this one has drawn by then).  With one piece per row nothing
+// is published.  A wait gives up after spin_limit polls and returns NaN, so
+// a piece that could not get its carry writes NaN, never a wrong finite sum.
+// x and out may be the same array (each element is loaded and stored by the
+// same lane).
 template <bool REV, int NW, int K, bool NT>
 __global__ __launch_bounds__(NW * kWave, scan_rows_waves_per_simd<K>()) void
 scan_rows_lookback_kernel(const float* x, float* out, int64_t outer, int64_t R, int64_t so,
                           int64_t P, int64_t NG, uint32_t* __restrict__ ticket, uint64_t* agg,
-                          uint64_t* gsum, uint32_t spin_limit) {
+                          uint64_t* gsum, uint32_t tag, uint32_t spin_limit) {
     constexpr int64_t kSpan = 256 * K;      // a wave's positions
     constexpr int64_t kChunk = NW * kSpan;  // the piece's positions
     __shared__ float slots[NW];
@@ -476,11 +480,16 @@ scan_rows_lookback_kernel(const float* x, float* out, int64_t outer, int64_t R, 
     __shared__ float s_carry;
     const int wave = wave_in_block();
     const int lane = threadIdx.x % kWave;
-    if (threadIdx.x == 0)
-        s_item = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+        const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        if (int64_t(t) == outer * P - 1)
+            __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_item = t;
+    }
     __syncthreads();
     const int64_t item = s_item;
-    if (item >= outer * P) return;  // only if the ticket was not zeroed: never wait on it
+    if (item >= outer * P) return;  // only if the ticket was not 0: never wait on it
     const int64_t o = item / P;
     const int64_t j = item - o * P;
     const float* row = x + o * so;
@@ -519,17 +528,17 @@ scan_rows_lookback_kernel(const float* x, float* out, int64_t outer, int64_t R, 
         float a = 0.f;  // the chunk total, 0 + t_0 + ... + t_{NW-1}
 #pragma unroll
         for (int w = 0; w < NW; ++w) a = a + slots[w];
-        if (lane == 0) publish_word(agg + item, 1u, a);
+        if (lane == 0 && j + 1 < P) publish_word(agg + item, tag, a);
         const int64_t g = j / kLookGroup;
         const int64_t first = g * kLookGroup;
         // this group's earlier chunk totals, lane i <- piece first + i
-        const float ai = first + lane < j ? await_word(agg + o * P + first + lane, 1u, spin_limit) : 0.f;
+        const float ai = first + lane < j ? await_word(agg + o * P + first + lane, tag, spin_limit) : 0.f;
         const float in_group = lane63(wave_scan_inclusive(ai));
         if (j == first + kLookGroup - 1 && j + 1 < P && lane == 0)
-            publish_word(gsum + o * NG + g, 1u, in_group + a);
+            publish_word(gsum + o * NG + g, tag, in_group + a);
         float before = 0.f;  // the earlier groups' totals
         for (int64_t h0 = 0; h0 < g; h0 += kWave) {
-            const float th = h0 + lane < g ? await_word(gsum + o * NG + h0 + lane, 1u, spin_limit) : 0.f;
+            const float th = h0 + lane < g ? await_word(gsum + o * NG + h0 + lane, tag, spin_limit) : 0.f;
             before = before + lane63(wave_scan_inclusive(th));
         }
         if (lane == 0) s_carry = before + in_group;
@@ -1619,49 +1628,71 @@ hipError_t launch_scan_rows(const rd_plan& p, bool reverse, const float* x, floa
                    : rows_go<false>(p, x, out, v, carry_in, totals, s);
 }
 
+struct LookArgs {
+    uint32_t* ticket;
+    uint64_t* agg;
+    uint64_t* gsum;
+    int64_t NG;
+    uint32_t tag, spin_limit;
+};
+
 template <bool REV, int NW, int K>
 hipError_t lookback_k(const rd_plan& p, const float* x, float* out, const Strides& v,
-                      uint32_t* ticket, uint64_t* agg, uint64_t* gsum, int64_t NG,
-                      uint32_t spin_limit, hipStream_t s) {
+                      const LookArgs& a, hipStream_t s) {
     if (p.nontemporal)
         return launch(scan_rows_lookback_kernel<REV, NW, K, true>, p.blocks, NW * kWave, s, x,
-                      out, v.outer, v.R, v.so, p.split, NG, ticket, agg, gsum, spin_limit);
+                      out, v.outer, v.R, v.so, p.split, a.NG, a.ticket, a.agg, a.gsum, a.tag,
+                      a.spin_limit);
     return launch(scan_rows_lookback_kernel<REV, NW, K, false>, p.blocks, NW * kWave, s, x, out,
-                  v.outer, v.R, v.so, p.split, NG, ticket, agg, gsum, spin_limit);
+                  v.outer, v.R, v.so, p.split, a.NG, a.ticket, a.agg, a.gsum, a.tag,
+                  a.spin_limit);
 }
 
 template <bool REV, int NW>
 hipError_t lookback_go(const rd_plan& p, const float* x, float* out, const Strides& v,
-                       uint32_t* ticket, uint64_t* agg, uint64_t* gsum, int64_t NG,
-                       uint32_t spin_limit, hipStream_t s) {
-    if (p.unroll == 4)
-        return lookback_k<REV, NW, 4>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
-    return lookback_k<REV, NW, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+                       const LookArgs& a, hipStream_t s) {
+    if (p.unroll == 4) return lookback_k<REV, NW, 4>(p, x, out, v, a, s);
+    return lookback_k<REV, NW, 8>(p, x, out, v, a, s);
 }
 
 hipError_t launch_scan_rows_lookback(const rd_plan& p, bool reverse, const float* x, float* out,
-                                     const Strides& v, void* ws, uint32_t spin_limit,
-                                     hipStream_t s) {
+                                     const Strides& v, void* ws, const Published* pub,
+                                     uint32_t spin_limit, hipStream_t s) {
     const int64_t NG = lookback_groups(p.split);
     const int nw = p.group / kWave;
     if (p.combine != RD_COMBINE_LOOKBACK || (p.unroll != 4 && p.unroll != 8) ||
         (nw != 4 && nw != 8 && nw != 16) ||
         p.rows_per_split != int64_t(nw) * 256 * p.unroll || p.blocks != v.outer * p.split ||
-        p.workspace_bytes != lookback_workspace_bytes(v.outer, p.split) || ws == nullptr)
+        p.blocks > int64_t(UINT32_MAX) ||
+        p.workspace_bytes != lookback_workspace_bytes(v.outer, p.split))
         return hipErrorInvalidValue;
-    hipError_t e = hipMemsetAsync(ws, 0, size_t(p.workspace_bytes), s);
-    if (e != hipSuccess) return e;
-    char* base = static_cast<char*>(ws);
-    uint32_t* ticket = reinterpret_cast<uint32_t*>(base);
-    uint64_t* agg = reinterpret_cast<uint64_t*>(base + kLookTicketBytes);
-    uint64_t* gsum = agg + v.outer * p.split;
+    LookArgs a{};
+    a.NG = NG;
+    a.spin_limit = spin_limit;
+    if (pub) {
+        if (!pub->ticket || !pub->words || pub->epoch == 0 ||
+            lookback_words(v.outer, p.split) > kPubColWords)
+            return hipErrorInvalidValue;
+        a.ticket = pub->ticket;
+        a.agg = pub->words;
+        a.tag = pub->epoch;
+    } else {
+        if (ws == nullptr) return hipErrorInvalidValue;
+        hipError_t e = hipMemsetAsync(ws, 0, size_t(p.workspace_bytes), s);
+        if (e != hipSuccess) return e;
+        char* base = static_cast<char*>(ws);
+        a.ticket = reinterpret_cast<uint32_t*>(base);
+        a.agg = reinterpret_cast<uint64_t*>(base + kLookTicketBytes);
+        a.tag = 1;
+    }
+    a.gsum = a.agg + v.outer * p.split;
     switch ((reverse ? 100 : 0) + nw) {
-        case 104: return lookback_go<true, 4>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
-        case 108: return lookback_go<true, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
-        case 116: return lookback_go<true, 16>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
-        case 4: return lookback_go<false, 4>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
-        case 8: return lookback_go<false, 8>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
-        default: return lookback_go<false, 16>(p, x, out, v, ticket, agg, gsum, NG, spin_limit, s);
+        case 104: return lookback_go<true, 4>(p, x, out, v, a, s);
+        case 108: return lookback_go<true, 8>(p, x, out, v, a, s);
+        case 116: return lookback_go<true, 16>(p, x, out, v, a, s);
+        case 4: return lookback_go<false, 4>(p, x, out, v, a, s);
+        case 8: return lookback_go<false, 8>(p, x, out, v, a, s);
+        default: return lookback_go<false, 16>(p, x, out, v, a, s);
     }
 }
 

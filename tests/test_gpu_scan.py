@@ -59,10 +59,11 @@ def test_rows_around_tiles():
 def test_few_rows_one_pass_plans():
     """Few rows that are not cut: a workgroup per row in one pass -- 4 waves
     for rows of 2-4 tiles, 8 past 16384 positions, 16 from 65536 -- up to
-    the longest rows the planner leaves uncut."""
-    shapes = [(40, 16384, 1), (5, 16385, 1), (64, 65536, 1), (2, 131071, 1),
+    the longest rows the planner leaves uncut (fewer rows than a third of
+    the CUs take the look-back from 65536 positions on)."""
+    shapes = [(40, 16384, 1), (5, 16385, 1), (86, 65536, 1), (2, 65535, 1),
               (86, 131072, 1), (300, 4097, 1)]
-    for (o, r, i), group in zip(shapes, (256, 512, 1024, 1024, 1024, 256)):
+    for (o, r, i), group in zip(shapes, (256, 512, 1024, 512, 1024, 256)):
         p = rd.rd_plan_cumsum(256, o, r, i)
         assert (p.split, p.group, p.passes) == (1, group, 1), ((o, r, i), p.as_dict())
     _sweep(shapes, [0, 1], 802, "scan few rows")
@@ -267,13 +268,15 @@ def test_rows_streamed_by_persistent_workgroups(group, unroll):
 
 
 def test_default_splits():
-    """Few long rows or few columns: the planner cuts them itself (many slabs:
-    the slab carries go one wave per column)."""
+    """Few long rows or few columns: the planner cuts them itself -- rows
+    into look-back pieces, columns into slabs (many slabs: the slab carries
+    go one wave per column)."""
     shapes = [(1, 1 << 20, 1), (7, 200_000, 1), (1, 100_000, 4), (2, 50_000, 33),
               (1, 1 << 20, 4), (1, 200_000, 300)]
     for shape in shapes:
         p = rd.rd_plan_cumsum(256, *shape).as_dict()
-        assert p["split"] > 1 and p["passes"] == 3, (shape, p)
+        want = ("lookback", 1) if shape[2] == 1 else ("pass", 3)
+        assert p["split"] > 1 and (p["combine"], p["passes"]) == want, (shape, p)
     assert rd.rd_plan_cumsum(256, 1, 1 << 20, 4).split > 64
     _sweep(shapes, [0], 820, "scan default splits")
 
@@ -422,6 +425,56 @@ def test_rows_lookback_large_arrays():
         p = rd.rd_plan_cumsum(256, o, r, i)
         assert (p.combine, p.group, p.split) == (3, group, P), p.as_dict()
     _sweep(shapes, [0], 906, "scan lookback large", reverse_modes=(True,))
+
+
+def test_rows_lookback_stream_buffer_matches_workspace():
+    """A look-back scan on a stream with a buffer of its own takes it (its
+    totals tagged with the launch's epoch, its ticket set back to 0 by the
+    workgroup that draws the last one, nothing zeroed before the launch);
+    the per-thread default stream takes a zeroed workspace.  On normal data
+    the two give the same bits, call after call of different piece counts and
+    both directions on one stream, with single-launch reductions (which
+    publish into the same buffer) in between."""
+    import ctypes
+    t = H.torch()
+    lib = rd.load()
+    shapes = [(16, 1 << 20, 1), (1, (1 << 24) + 5, 1), (5, 300_001, 1), (3, 5 * 16384 + 9, 1)]
+    tunes = [{}, {}, dict(combine=3, group=512), dict(combine=3, group=256, unroll=4)]
+    maxn = max(o * r * i for o, r, i in shapes)
+    a = workloads.random(maxn, 914, "normal")
+    x = H.upload(a)
+    cols = (2, 100, 1000)
+    sizes = [o * r * i for o, r, i in shapes]
+    per_thread = 2  # hipStreamPerThread
+    results = {}
+    for name, h in (("buffer", H.stream_handle()), ("workspace", per_thread)):
+        outs = []
+        for rep in range(2):
+            for (o, r, i), tune, n in zip(shapes, tunes, sizes):
+                with rd.tuning(**tune):
+                    p = rd.rd_plan_cumsum(256, o, r, i)
+                    assert p.combine == 3, ((o, r, i), p.as_dict())
+                    for rev in (True, False):
+                        y = t.empty(n, device="cuda")
+                        t.cuda.synchronize()
+                        assert lib.rd_cumsum_dim(x.data_ptr(), o, r, i, int(rev), y.data_ptr(),
+                                                 h) == 0
+                        outs.append(y)
+                red = t.empty(cols[0] * cols[2], device="cuda")
+                assert lib.rd_sum_dim(x.data_ptr(), *cols, red.data_ptr(), h) == 0
+                outs.append(red)
+        if h == per_thread:
+            assert lib.hipStreamSynchronize(ctypes.c_void_p(per_thread)) == 0
+        t.cuda.synchronize()
+        results[name] = [y.cpu().numpy().view(np.uint32) for y in outs]
+    for k, (u, w) in enumerate(zip(results["buffer"], results["workspace"])):
+        assert np.array_equal(u, w), k
+    k = 0
+    for (o, r, i), n in zip(shapes, sizes):   # the first call of each shape: reverse
+        S, A = oracle.cumsum_dim(a[:n], o, r, i, True)
+        H.assert_within_tolerance(results["buffer"][k].view(np.float32), S, A,
+                                  "look-back on the stream buffer %s" % ((o, r, i),))
+        k += 3
 
 
 def test_rows_lookback_special_values():

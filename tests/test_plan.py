@@ -344,8 +344,9 @@ def _scan_invariants(p, outer, R, inner, cu=CU):
         assert p.rows_per_split % 4096 == 0           # whole tiles per piece
         few_long = outer < 4 * cu and R >= 1 << 20 and outer * R >= 1 << 24
         large = R >= 16384 and outer * R * 4 >= (1 << 29 if R % 32768 == 0 else 1 << 30)
+        few = 3 * outer < cu and R >= 65536
         L = 32768 if few_long or R % 32768 == 0 else 16384
-        look = (few_long or large) and -(-R // L) <= (1 << 20) // outer
+        look = (few_long or large or few) and -(-R // L) <= (1 << 20) // outer
         assert (p.combine == 3) == look, (outer, R, cu, p.as_dict())
         if look:
             # one launch, a workgroup of 16 waves per 32768 positions (or 8
@@ -424,15 +425,15 @@ def _scan_invariants(p, outer, R, inner, cu=CU):
 def test_cumsum_row_widths_at_their_edges():
     """Uncut rows: a wave per row up to 16384 positions, a workgroup of 8
     waves above, of 16 from 65536 on (two of its 32768-position chunks);
-    rows cut into pieces stay a wave per piece.  (2048 rows: under 1 GB,
-    below the look-back kernel's arrays.)"""
+    few long rows take the look-back's 32768-position pieces.  (1024 rows:
+    under 1 GB, below the look-back kernel's arrays.)"""
     for R, group in ((4096, 64), (16384, 64), (16385, 512), (32768, 512), (65535, 512),
                      (65536, 1024), (100_000, 1024)):
         p = rd.rd_plan_cumsum(CU, 1024, R, 1)
         assert p.split == 1 and p.group == group, (R, p.as_dict())
         assert p.block_threads == max(group, 256)
-    p = rd.rd_plan_cumsum(CU, 16, 1 << 19, 1)   # 16 rows of 2^19: cut into pieces
-    assert p.split > 1 and p.group == 64 and p.passes == 3
+    p = rd.rd_plan_cumsum(CU, 16, 1 << 19, 1)   # 16 rows of 2^19: look-back pieces
+    assert p.split == 16 and p.group == 1024 and p.passes == 1
     p = rd.rd_plan_cumsum(CU, 16, 1 << 20, 1)   # 16 rows of 2^20: look-back pieces
     assert p.split == 32 and p.group == 1024 and p.passes == 1
     with rd.tuning(unroll=4):                    # 4-slice chunks: 4 waves
@@ -484,22 +485,33 @@ def test_cumsum_plans():
     assert p.as_dict()["combine"] == "none"
     p = rd.rd_plan_cumsum(CU, 30000, 35791, 1)   # a partial last piece: 8 waves
     assert (p.combine, p.group, p.split, p.rows_per_split) == (3, 512, 3, 16384)
+    # few rows (fewer than a third of the CUs) of 65536 positions or more:
+    # the look-back, 32768-position pieces of 16 waves (8 waves, 16384, for
+    # rows not a multiple of 32768)
     p = rd.rd_plan_cumsum(CU, 1, 1 << 20, 1)
-    assert p.split == 256 and p.rows_per_split == 4096 and p.passes == 3
+    assert p.as_dict()["combine"] == "lookback" and (p.split, p.group, p.passes) == (32, 1024, 1)
     p = rd.rd_plan_cumsum(CU, 64, 131072, 1)              # 64 * 3 < 256 CUs
-    assert p.split == 32 and p.group == 64 and p.passes == 3
+    assert p.as_dict()["combine"] == "lookback" and (p.split, p.blocks) == (4, 256)
+    p = rd.rd_plan_cumsum(CU, 7, 777777, 1)
+    assert (p.combine, p.group, p.split, p.rows_per_split) == (3, 512, 48, 16384)
+    p = rd.rd_plan_cumsum(CU, 64, 65536, 1)
+    assert p.as_dict()["combine"] == "lookback" and p.split == 2
+    with rd.tuning(combine=1):                            # the three kernels instead
+        p = rd.rd_plan_cumsum(CU, 1, 1 << 20, 1)
+        assert p.split == 256 and p.rows_per_split == 4096 and p.passes == 3
+        p = rd.rd_plan_cumsum(CU, 64, 131072, 1)
+        assert p.split == 32 and p.group == 64 and p.passes == 3
+        p = rd.rd_plan_cumsum(CU, 1, 1 << 28, 1)
+        assert p.split == 4096 and p.passes == 3
+        p = rd.rd_plan_cumsum(CU, 64, 65536, 1)           # rows too short to cut
+        assert p.split == 1 and p.group == 1024 and p.passes == 1
     p = rd.rd_plan_cumsum(CU, 1, 1 << 28, 1)              # long rows: look-back
     assert p.as_dict()["combine"] == "lookback" and p.split == 8192 and p.blocks == 8192
     assert p.passes == 1 and p.workspace_bytes == 256 + 8 * (8192 + 128)
-    with rd.tuning(combine=1):                            # the three kernels instead
-        p = rd.rd_plan_cumsum(CU, 1, 1 << 28, 1)
-        assert p.split == 4096 and p.passes == 3
-    p = rd.rd_plan_cumsum(CU, 1, 1 << 22, 1)              # 16 MB: too small for it
-    assert p.split == 1024 and p.passes == 3
     p = rd.rd_plan_cumsum(CU, 86, 131072, 1)              # 86 * 3 >= 256: one pass
     assert p.split == 1 and p.group == 1024 and p.blocks == 86 and p.workspace_bytes == 0
-    p = rd.rd_plan_cumsum(CU, 64, 65536, 1)               # rows too short to cut
-    assert p.split == 1 and p.group == 1024 and p.passes == 1
+    p = rd.rd_plan_cumsum(CU, 1, 32768, 1)                # one chunk: a workgroup
+    assert p.split == 1 and p.passes == 1 and p.workspace_bytes == 0
     p = rd.rd_plan_cumsum(CU, 512, 16384, 1)              # few rows of 4 tiles
     assert p.split == 1 and p.group == 256 and p.block_threads == 256 and p.blocks == 512
     p = rd.rd_plan_cumsum(CU, 1024, 16384, 1)             # 4 rows a CU: a wave each
