@@ -228,12 +228,16 @@ constexpr int64_t kScanRowsWideMinR = 65536;
 // 2^19] 22.0 -> 17.1, [64, 2^17] 21.9 -> 17.4, [80, 2^17] 29.5 -> 24.2, [7,
 // 777777] 22.1 -> 19.3, [64, 2^16] 14.5 -> 12.3, [1, 65537] 12.7 -> 8.1; with
 // more rows one workgroup a row stays ahead ([128, 2^17] 28.9 / 31.7,
-// [256, 2^16] 25.0 / 31.2).
+// [256, 2^16] 25.0 / 31.2).  Up to kScanRowsLookSmallN elements the pieces
+// are of 8 waves (16384 positions), twice the workgroups: us, 16 -> 8 waves,
+// [1, 2^20] 9.4 -> 8.2, [1, 2^16] 7.7 -> 6.9, [2, 2^17] 8.3 -> 7.5; from
+// 8 MB on 16 waves win ([8, 2^20] 17.6 / 21.4, [64, 2^16] 12.4 / 13.4).
 constexpr int64_t kScanRowWavesMin = 4;
 constexpr int64_t kScanRowsCutMinR = 131072;
 constexpr int64_t kScanRowsLookMinR = int64_t(1) << 20;
 constexpr int64_t kScanRowsLookMinN = int64_t(1) << 24;
 constexpr int64_t kScanRowsLookFewMinR = 65536;
+constexpr int64_t kScanRowsLookSmallN = int64_t(1) << 20;
 // Arrays of at least kScanRowsTicketMinBytes whose rows fill an 8-wave
 // chunk take the look-back kernel too: its workgroups take their pieces by a
 // ticket, so all XCDs work on one narrow stretch of the array at a time,

@@ -612,7 +612,12 @@ rd_status plan_cumsum_view(int cu_count, Strides* v, const rd_tune* t, rd_plan* 
         // fewer rows than a third of the CUs, each of two or more 32768-position
         // chunks: the look-back in place of the three-kernel scheme
         const bool few = 3 * outer < cu && R >= kScanRowsLookFewMinR;
-        const int32_t look_group = few_long || R % chunk16 == 0 ? 16 * kWave : 8 * kWave;
+        // (arrays of at most kScanRowsLookSmallN elements: 8-wave pieces, twice
+        // as many workgroups)
+        const int32_t look_group =
+            (few_long || R % chunk16 == 0) && !(few && !large && outer * R <= kScanRowsLookSmallN)
+                ? 16 * kWave
+                : 8 * kWave;
         const bool look =
             comb == RD_COMBINE_LOOKBACK ||
             (comb == 0 && !tuned && (few_long || large || few) &&

@@ -346,6 +346,8 @@ def _scan_invariants(p, outer, R, inner, cu=CU):
         large = R >= 16384 and outer * R * 4 >= (1 << 29 if R % 32768 == 0 else 1 << 30)
         few = 3 * outer < cu and R >= 65536
         L = 32768 if few_long or R % 32768 == 0 else 16384
+        if few and not large and outer * R <= 1 << 20:
+            L = 16384                                   # small arrays: 8-wave pieces
         look = (few_long or large or few) and -(-R // L) <= (1 << 20) // outer
         assert (p.combine == 3) == look, (outer, R, cu, p.as_dict())
         if look:
@@ -488,7 +490,9 @@ def test_cumsum_plans():
     # few rows (fewer than a third of the CUs) of 65536 positions or more:
     # the look-back, 32768-position pieces of 16 waves (8 waves, 16384, for
     # rows not a multiple of 32768)
-    p = rd.rd_plan_cumsum(CU, 1, 1 << 20, 1)
+    p = rd.rd_plan_cumsum(CU, 1, 1 << 20, 1)                # 4 MB: 8-wave pieces
+    assert p.as_dict()["combine"] == "lookback" and (p.split, p.group, p.passes) == (64, 512, 1)
+    p = rd.rd_plan_cumsum(CU, 2, 1 << 20, 1)
     assert p.as_dict()["combine"] == "lookback" and (p.split, p.group, p.passes) == (32, 1024, 1)
     p = rd.rd_plan_cumsum(CU, 64, 131072, 1)              # 64 * 3 < 256 CUs
     assert p.as_dict()["combine"] == "lookback" and (p.split, p.blocks) == (4, 256)
