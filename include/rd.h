@@ -37,10 +37,13 @@
  *   device and the call returns without waiting; out is valid once the
  *   stream is synchronised.  No device-to-host transfer happens inside a call.
  * Workspace.  Where a shape needs per-block partials (a split reduce, or
- *   the piece / slab totals and carries of a split cumulative sum), the
- *   library allocates them stream-ordered on `stream` from a pool of its own
- *   and frees them on the same stream, so concurrent calls on different
- *   streams never share memory.  The partials of a split reduce are summed by
+ *   the piece / slab totals and carries of a split cumulative sum), they go
+ *   to a 1 MiB scratch area of the stream's own buffer (below) when they fit
+ *   -- calls on one stream never overlap, so no call finds another's -- and
+ *   otherwise the library allocates them stream-ordered on `stream` from a
+ *   pool of its own and frees them on the same stream (measured: the pool's
+ *   allocate and free cost about 5 us of GPU time per call), so concurrent
+ *   calls on different streams never share memory.  The partials of a split reduce are summed by
  *   a second kernel in fixed order -- or, with RD_COMBINE_LAST_BLOCK, in the
  *   one kernel: for a row reduce of at most 4 rows cut into at most 8192
  *   pieces in all (4096 for the softmax pair) by its last workgroup, and for
@@ -49,9 +52,10 @@
  *   the last slab (not the softmax pair) by the workgroups of the last slab,
  *   each joining slabs 0, 1, ... of its tile's columns in order (the default
  *   in both cases).  The others publish their results into a buffer of the
- *   stream's own (65536 tagged words and 8192 values, 544 KB of device
- *   memory per stream and device, created by the first such call on the
- *   stream, kept until the process ends, for up to 256 streams), each word
+ *   stream's own (65536 tagged words, 8192 values and the 1 MiB scratch,
+ *   1.6 MB of device memory per stream and device, created by the first call
+ *   on the stream that needs it, kept until the process ends, for up to 256
+ *   streams), each word
  *   tagged with that launch's epoch, a number the
  *   stream gives each launch in turn, so calls on one stream, which never
  *   overlap, never take another call's words, and calls on another stream

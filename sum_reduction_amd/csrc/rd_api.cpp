@@ -26,18 +26,24 @@ thread_local int t_last_hip = 0;
 // call on the device (up to kPubStreams), each with room for kPubColWords
 // tagged words (row pieces use the first kPubWords, with their values; slab
 // results of a column reduce and the totals of a look-back row scan all of
-// them), the look-back scan's ticket and the stream's last epoch.
+// them), the look-back scan's ticket, the stream's last epoch, and
+// kStreamScratchBytes of plain scratch: the workspace of a split plan that
+// takes a second kernel, when it fits (calls on one stream never overlap, so
+// one call's partial results are never another's).  The scratch is kept apart
+// from the tagged words, so its floats can never pass for a published word.
 // A launch publishes its words tagged with a new epoch of its stream; calls
 // on one stream never overlap, so every word a launch finds tagged with its
 // own epoch was written by that launch.  Zeroed when created, and again
 // before an epoch is reused (after 2^32 - 1 launches).
 constexpr int kPubStreams = 256;
+constexpr size_t kStreamScratchBytes = size_t(1) << 20;
 using rd::kPubWords;
 using rd::kPubColWords;
 struct StreamPub {
     uint64_t* words = nullptr;
     float* vals = nullptr;
     uint32_t* ticket = nullptr;
+    float* scratch = nullptr;
     uint32_t epoch = 0;
 };
 struct Device {
@@ -60,7 +66,8 @@ StreamPub make_pub() {
     StreamPub b;
     void* mem = nullptr;
     const size_t vals_end = size_t(kPubColWords) * sizeof(uint64_t) + size_t(kPubWords) * sizeof(float);
-    const size_t bytes = vals_end + size_t(rd::kLookTicketBytes);
+    const size_t ticket_end = vals_end + size_t(rd::kLookTicketBytes);
+    const size_t bytes = ticket_end + kStreamScratchBytes;
     if (hipMalloc(&mem, bytes) != hipSuccess) return b;
     hipStream_t s = nullptr;
     bool ok = hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess;
@@ -74,6 +81,7 @@ StreamPub make_pub() {
     b.words = static_cast<uint64_t*>(mem);
     b.vals = reinterpret_cast<float*>(b.words + kPubColWords);
     b.ticket = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + vals_end);
+    b.scratch = reinterpret_cast<float*>(static_cast<char*>(mem) + ticket_end);
     return b;
 }
 
@@ -98,18 +106,36 @@ rd_status capture_check(hipStream_t stream) {
 // to be had, or the per-thread default stream, whose one handle stands for a
 // different stream in each host thread -- calls from two threads could run
 // at once and share the buffer.
-bool stream_pub(Device& d, hipStream_t stream, rd::Published* pub, hipError_t* err) {
-    *err = hipSuccess;
-    if (stream == hipStreamPerThread) return false;
-    std::lock_guard<std::mutex> lock(d.pub_mu);
+// The buffer of `stream` (created on its first use), or null: see stream_pub.
+// Call with d.pub_mu held; entries are never removed, so the pointer stays
+// valid.
+StreamPub* stream_buffer(Device& d, hipStream_t stream) {
+    if (stream == hipStreamPerThread) return nullptr;
     auto it = d.pub_of.find(stream);
     if (it == d.pub_of.end()) {
-        if (static_cast<int>(d.pub_of.size()) >= kPubStreams) return false;
+        if (static_cast<int>(d.pub_of.size()) >= kPubStreams) return nullptr;
         StreamPub b = make_pub();
-        if (!b.words) return false;
+        if (!b.words) return nullptr;
         it = d.pub_of.emplace(stream, b).first;
     }
-    StreamPub& b = it->second;
+    return &it->second;
+}
+
+// The scratch of `stream`'s buffer for a workspace of `bytes`, or null (too
+// large, or no buffer: the workspace then comes from the pool).
+float* stream_scratch(Device& d, hipStream_t stream, int64_t bytes) {
+    if (bytes <= 0 || size_t(bytes) > kStreamScratchBytes) return nullptr;
+    std::lock_guard<std::mutex> lock(d.pub_mu);
+    StreamPub* b = stream_buffer(d, stream);
+    return b ? b->scratch : nullptr;
+}
+
+bool stream_pub(Device& d, hipStream_t stream, rd::Published* pub, hipError_t* err) {
+    *err = hipSuccess;
+    std::lock_guard<std::mutex> lock(d.pub_mu);
+    StreamPub* bp = stream_buffer(d, stream);
+    if (!bp) return false;
+    StreamPub& b = *bp;
     if (++b.epoch == 0) {  // every epoch used: clear the words, start again
         *err = hipMemsetAsync(b.words, 0, size_t(kPubColWords) * sizeof(uint64_t), stream);
         if (*err != hipSuccess) return false;
@@ -241,11 +267,12 @@ const Injected& injected() {
     return f;
 }
 
-// Runs plan p.  fixed == nullptr: a row reduce whose plan takes the
-// single-launch combine publishes its piece results in the stream's buffer
-// (one kernel); otherwise the workspace (if any) is allocated stream-ordered
-// from the device's pool and freed after the last kernel.  Either is refused
-// while `s` is being captured.  fixed != nullptr: it is the workspace, at
+// Runs plan p.  fixed == nullptr: a reduce whose plan takes the
+// single-launch combine publishes its results in the stream's buffer (one
+// kernel); otherwise the workspace (if any) is the scratch of the stream's
+// buffer when it fits, else allocated stream-ordered from the device's pool
+// and freed after the last kernel.  All of these are refused while `s` is
+// being captured.  fixed != nullptr: it is the workspace, at
 // least p.workspace_bytes long, and nothing is allocated (the partial
 // results are combined by the second kernel).
 rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const rd::Strides& v,
@@ -275,12 +302,15 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
     if (p.workspace_bytes > 0 && fixed) {
         ws = fixed;
     } else if (p.workspace_bytes > 0 && !published) {
-        rd_status st = device_memory(dev);
-        if (st != RD_OK) return st;
-        hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
-                                              size_t(p.workspace_bytes), dev.pool, s);
-        if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
-        pooled = true;
+        ws = stream_scratch(dev, s, p.workspace_bytes);
+        if (!ws) {
+            rd_status st = device_memory(dev);
+            if (st != RD_OK) return st;
+            hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
+                                                  size_t(p.workspace_bytes), dev.pool, s);
+            if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
+            pooled = true;
+        }
     }
     // partial results: one array, or the two halves of the pairs
     rd::Results part{ws, nullptr};
@@ -404,12 +434,17 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
             if (pe != hipSuccess) return hip_fail(pe, RD_ERR_HIP);
         }
     }
+    bool pooled = false;
     if (p.workspace_bytes > 0 && !published) {
-        st = device_memory(*dev);
-        if (st != RD_OK) return st;
-        hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
-                                              size_t(p.workspace_bytes), dev->pool, stream);
-        if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
+        ws = stream_scratch(*dev, stream, p.workspace_bytes);
+        if (!ws) {
+            st = device_memory(*dev);
+            if (st != RD_OK) return st;
+            hipError_t e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws),
+                                                  size_t(p.workspace_bytes), dev->pool, stream);
+            if (e != hipSuccess) return hip_fail(e, RD_ERR_ALLOC);
+            pooled = true;
+        }
     }
     const int64_t nrow = v.outer * v.inner;
     // The totals pass of a split scan reads x without the streaming hint when
@@ -453,7 +488,7 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
             if (e == hipSuccess) e = cols(p, carries, nullptr);
         }
     }
-    if (ws) {
+    if (pooled) {
         hipError_t f = hipFreeAsync(ws, stream);
         if (e == hipSuccess && f != hipSuccess) return hip_fail(f, RD_ERR_HIP);
     }

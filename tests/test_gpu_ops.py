@@ -282,6 +282,61 @@ def test_one_launch_fallbacks_match():
         assert np.array_equal(got[k, 1:].view(np.uint32), want2.reshape(-1)), k
 
 
+def test_split_scratch_streams():
+    """Split plans that take a second kernel keep their partial results in
+    the scratch of the stream's buffer when they fit: reduces of rows and of
+    columns cut into many slabs, and cumulative sums of column slabs, one
+    after another on four streams at once (each stream reusing its scratch
+    in order), exact integer data, every output against the oracle; the same
+    calls on the per-thread default stream (no buffer: the pool) give the
+    same bits."""
+    import ctypes
+    t = H.torch()
+    lib = rd.load()
+    red = [(64, 262144, 1), (2, 100000, 129), (1, 262144, 512), (3, 100000, 300), (300, 1000, 7)]
+    scans = [(1, 5000, 4095), (2, 3000, 129)]
+    for o, r, i in red:
+        p = rd.rd_plan_dim(256, o, r, i)
+        assert p.as_dict()["combine"] == "pass" and 0 < p.workspace_bytes <= 1 << 20, p.as_dict()
+    for o, r, i in scans:
+        p = rd.rd_plan_cumsum(256, o, r, i)
+        assert p.passes == 3 and 0 < p.workspace_bytes <= 1 << 20, p.as_dict()
+    maxn = max(o * r * i for o, r, i in red + scans)
+    data = workloads.small_ints(maxn, 798)
+    x = H.upload(data)
+    calls = [("sum", s_) for s_ in red] + [("cumsum", s_) for s_ in scans]
+    streams = [t.cuda.Stream() for _ in range(4)]
+
+    def run(handle_of):
+        outs = []
+        t.cuda.synchronize()
+        for k in range(3 * len(calls)):
+            kind, (o, r, i) = calls[k % len(calls)]
+            y = t.empty(o * i if kind == "sum" else o * r * i, device="cuda")
+            h = handle_of(k)
+            if kind == "sum":
+                st = lib.rd_sum_dim(x.data_ptr(), o, r, i, y.data_ptr(), h)
+            else:
+                st = lib.rd_cumsum_dim(x.data_ptr(), o, r, i, 0, y.data_ptr(), h)
+            assert st == 0, (kind, (o, r, i), rd.rd_status_string(st))
+            outs.append(y)
+        return outs
+
+    one = run(lambda k: streams[k % 4].cuda_stream)
+    t.cuda.synchronize()
+    pool = run(lambda k: 2)  # hipStreamPerThread
+    assert lib.hipStreamSynchronize(ctypes.c_void_p(2)) == 0
+    t.cuda.synchronize()
+    for k, (a, b) in enumerate(zip(one, pool)):
+        kind, (o, r, i) = calls[k % len(calls)]
+        got = a.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), b.cpu().numpy().view(np.uint32)), (kind, o, r, i)
+        host = data[:o * r * i]
+        S = oracle.sum_dim(host, o, r, i)[0] if kind == "sum" else \
+            oracle.cumsum_dim(host, o, r, i, False)[0]
+        H.assert_bitwise_equal_oracle(got, S, "scratch %s %s" % (kind, (o, r, i)))
+
+
 _COL_PUB_SPIN = r"""
 import sys
 sys.path.insert(0, sys.argv[1])
