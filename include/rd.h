@@ -45,8 +45,9 @@
  *   allocate and free cost about 5 us of GPU time per call), so concurrent
  *   calls on different streams never share memory.  The partials of a split reduce are summed by
  *   a second kernel in fixed order -- or, with RD_COMBINE_LAST_BLOCK, in the
- *   one kernel: for a row reduce of at most 4 rows cut into at most 8192
- *   pieces in all (4096 for the softmax pair) by its last workgroup, and for
+ *   one kernel: for a row reduce of at most 4 rows cut into at most 512
+ *   pieces in all (256 for the softmax pair; up to 8192 / 4096 when the
+ *   tuning override asks for it) by its last workgroup, and for
  *   a column reduce cut into at most 16 slabs of one-wave tiles (256
  *   columns), no more workgroups than CUs and at most 65536 results outside
  *   the last slab (not the softmax pair) by the workgroups of the last slab,
@@ -381,7 +382,7 @@ typedef enum rd_combine {
                                   slab) sums them in the same order, from
                                   results the others publish as tagged words
                                   (one launch; the default for row reduces of
-                                  at most 4 rows and 8192 piece words and for
+                                  at most 4 rows and 512 piece words and for
                                   column reduces of at most 16 slabs of
                                   one-wave tiles; see "Workspace" above) */
     RD_COMBINE_LOOKBACK = 3    /* row scans: one launch, a workgroup per row

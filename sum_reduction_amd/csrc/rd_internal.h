@@ -81,6 +81,7 @@ hipError_t launch_fill_start(int op, Results out, int64_t n, hipStream_t s);
 // gives the single-launch combine.
 constexpr int64_t kPubWords = 8192;
 constexpr int64_t kPubMaxRows = 4;
+constexpr int64_t kPubRowsMaxWords = 512;  // the planner's default limit
 // The same for a column reduce cut into a few slabs (at most kPubColMaxSlabs,
 // the blocks within one per CU, so all of them run at once): every block
 // but those of the last slab publishes its slab's column results as tagged

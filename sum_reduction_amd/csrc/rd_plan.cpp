@@ -167,9 +167,14 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
         // pieces, whose words it reads a round at a time.  (A first version
         // published the results with a device-scope release, which writes back
         // an XCD's L2 -- about 47 ns per workgroup, serialized: 1e8 floats
-        // 200 us.)
+        // 200 us.)  Since the second kernel's partial results live in the
+        // stream's scratch (no pool allocation, ~5 us less), it wins again
+        // from about a thousand piece words: us, one launch / two kernels,
+        // same box, 1e6 floats (256 pieces) 7.4 / 8.5, 1e7 (306) 14.0 /
+        // 14.1, 1e8 (3052) 64.4 / 62.8, [2, 2e7] (1222) 31.0 / 30.0, [4,
+        // 2.5e7] (3052) 69.0 / 64.9: at most kPubRowsMaxWords words.
         const bool one = outer <= kPubMaxRows &&
-                         (op == RD_OP_SOFTMAX_DENOM ? 2 : 1) * outer * P <= kPubWords;
+                         (op == RD_OP_SOFTMAX_DENOM ? 2 : 1) * outer * P <= kPubRowsMaxWords;
         const int32_t c = (t && t->combine) ? t->combine
                                             : (one ? RD_COMBINE_LAST_BLOCK : RD_COMBINE_PASS);
         if (c != RD_COMBINE_PASS && c != RD_COMBINE_LAST_BLOCK) return RD_ERR_INVALID_ARG;

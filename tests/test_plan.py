@@ -30,9 +30,9 @@ def check_invariants(p, outer, R, inner, cu=CU):
             assert p.workspace_bytes == (4 * outer * p.split if p.split > 1 else 0)
             groups = outer * p.split
             assert p.blocks == min(-(-groups // (256 // p.group)), MAX_BLOCKS)
-            # pieces of at most 4 rows (8192 in all) are combined by the
+            # pieces of at most 4 rows (512 in all) are combined by the
             # last workgroup of the one launch, others by a second kernel
-            one = outer <= 4 and outer * p.split <= 8192
+            one = outer <= 4 and outer * p.split <= 512
             assert d["combine"] == (("last_block" if one else "pass") if p.split > 1
                                     else "none")
             assert p.passes == (2 if p.split > 1 and not one else 1)
@@ -82,11 +82,13 @@ def test_workload_plans():
     assert plans["normal_1e9"]["order"] == "blocked"
     assert plans["normal_1e9"]["combine"] == "pass"
     assert plans["normal_1e9"]["passes"] == 2
-    # 1e6 and 1e8 floats: 256 pieces of depth 2 and 3052 of depth 16,
-    # combined in the same launch
-    for name, P, U in (("harmonic_1e6", 256, 2), ("uniform_1e8", 3052, 16)):
+    # 1e6 floats: 256 pieces of depth 2 combined in the same launch; 1e8:
+    # 3052 of depth 16, combined by the second kernel (its partial results
+    # in the stream's scratch)
+    for name, P, U, c, n in (("harmonic_1e6", 256, 2, "last_block", 1),
+                             ("uniform_1e8", 3052, 16, "pass", 2)):
         d = plans[name]
-        assert (d["split"], d["unroll"], d["combine"], d["passes"]) == (P, U, "last_block", 1), d
+        assert (d["split"], d["unroll"], d["combine"], d["passes"]) == (P, U, c, n), d
     assert all(p["nontemporal"] == 1 for p in plans.values())
     # the [128, 4096, 4095] reduce fills the chip without a split along R:
     # 8 waves side by side cover 512 lane-columns (2048 columns), 2 tiles
