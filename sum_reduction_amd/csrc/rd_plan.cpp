@@ -134,9 +134,11 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
         // a depth of 2 loads: the shallowest depth that does.  Measured on
         // MI355X, 1D sums, us: 1e6 floats 8.2 (61 pieces of depth 16) -> 7.1
         // (256 of depth 2), 4e6 8.6 (244, 16) -> 7.7 (256, 8); 1e7 keeps 306
-        // pieces of 16.
+        // pieces of 16.  The softmax denominator's shallowest built depth is
+        // 8: 1e6 floats 13.3 (61 pieces of 16) -> 12.5 (122 of 8), 2e6 15.5
+        // -> 12.6, 4e6 14.4 -> 13.5.
         if (!(t && t->unroll) && p->group == kBlock && outer <= kPubMaxRows &&
-            op != RD_OP_SOFTMAX_DENOM && nvec / (int64_t(p->group) * 2) >= P) {
+            nvec / (int64_t(p->group) * 2) >= P) {
             while (cap < P && p->unroll > 2 && rows_shape_supported(op, p->group, p->unroll / 2)) {
                 p->unroll /= 2;
                 cap = nvec / (int64_t(p->group) * p->unroll);

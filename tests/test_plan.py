@@ -119,7 +119,9 @@ def test_row_pieces():
     assert (P(1, 4 * 10**6), rd.rd_plan_dim(CU, 1, 4 * 10**6, 1).unroll) == (256, 8)
     assert (P(1, 300_000), rd.rd_plan_dim(CU, 1, 300_000, 1).unroll) == (18, 16)
     assert rd.rd_plan_dim(CU, 5, 10**6, 1).unroll == 16      # more than 4 rows
-    assert rd.rd_plan_reduce(CU, 1, 10**6, 1, "softmax_denom").unroll == 16
+    # the softmax denominator: its shallowest built depth, 8 (122 pieces)
+    sm = rd.rd_plan_reduce(CU, 1, 10**6, 1, "softmax_denom")
+    assert (sm.unroll, sm.split) == (8, 122)
     assert P(1, 10**7) == 306                # ceil(1e7 / 32768) > one per CU
     assert P(1, 10**8) == 3052
     assert P(100, 10**7) == 306
