@@ -26,6 +26,9 @@ constexpr int64_t kLoadWavesPerCu = 32;
 // Inputs in (kMidInputLo, kMidInputHi] bytes are cut into 8 pieces per CU.
 constexpr int64_t kMidInputLo = int64_t(256) << 20;
 constexpr int64_t kMidInputHi = int64_t(1) << 30;
+// Few rows of at most kShallowMaxBytes take kShallowUnroll loads per step.
+constexpr int64_t kShallowMaxBytes = int64_t(128) << 20;
+constexpr int32_t kShallowUnroll = 4;
 // Defaults measured on MI355X for the two kernels.
 constexpr int kRowsUnrollBlock = 16;  // 256-lane groups
 // Row pieces of about kPieceFloats floats (128 KB): long rows read by many
@@ -144,6 +147,19 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
                 cap = nvec / (int64_t(p->group) * p->unroll);
                 if (cap < 1) cap = 1;
             }
+        }
+        // Up to kShallowMaxBytes, few rows still at the default depth take 4
+        // loads a step (pieces of the same length, more steps each): us,
+        // same box, A/B, 70001 floats 8.8 -> 7.15 (17 pieces instead of 4),
+        // 3e5 7.8 -> 7.15, 6e6 12.2 -> 11.55, 1e7 13.7 -> 13.0, 2e7 20.1 ->
+        // 18.5; 3.4e7 and 4e7 level.  (Where the rule above has already
+        // gone to 8 it stays: 4e6 8.4 at 8, 8.9 at 4.)
+        if (!(t && t->unroll) && p->group == kBlock && outer <= kPubMaxRows &&
+            p->unroll == kRowsUnrollBlock && bytes <= kShallowMaxBytes &&
+            rows_shape_supported(op, p->group, kShallowUnroll)) {
+            p->unroll = kShallowUnroll;
+            cap = nvec / (int64_t(p->group) * p->unroll);
+            if (cap < 1) cap = 1;
         }
         if (P < pieces) P = pieces;
         if (P > cap) P = cap;
