@@ -39,7 +39,9 @@
  * Workspace.  Where a shape needs per-block partials (a split reduce, or
  *   the piece / slab totals and carries of a split cumulative sum), they go
  *   to a 1 MiB scratch area of the stream's own buffer (below) when they fit
- *   -- calls on one stream never overlap, so no call finds another's -- and
+ *   -- calls on one stream run one after another, and a call holds the
+ *   scratch while it enqueues its kernels, so calls from several host threads
+ *   on one stream do not interleave them -- and
  *   otherwise the library allocates them stream-ordered on `stream` from a
  *   pool of its own and frees them on the same stream (measured: the pool's
  *   allocate and free cost about 5 us of GPU time per call), so concurrent

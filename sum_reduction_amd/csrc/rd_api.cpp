@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <memory>
 #include <mutex>
 #include <unordered_map>
 
@@ -44,6 +45,11 @@ struct StreamPub {
     float* vals = nullptr;
     uint32_t* ticket = nullptr;
     float* scratch = nullptr;
+    // held from a call's first launch that uses the scratch to its last, so
+    // that calls from two host threads on one stream do not interleave their
+    // kernels (the second call's first kernel would overwrite the first's
+    // partial results before its second kernel reads them)
+    std::shared_ptr<std::mutex> scratch_mu;
     uint32_t epoch = 0;
 };
 struct Device {
@@ -82,6 +88,7 @@ StreamPub make_pub() {
     b.vals = reinterpret_cast<float*>(b.words + kPubColWords);
     b.ticket = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + vals_end);
     b.scratch = reinterpret_cast<float*>(static_cast<char*>(mem) + ticket_end);
+    b.scratch_mu = std::make_shared<std::mutex>();
     return b;
 }
 
@@ -121,13 +128,24 @@ StreamPub* stream_buffer(Device& d, hipStream_t stream) {
     return &it->second;
 }
 
-// The scratch of `stream`'s buffer for a workspace of `bytes`, or null (too
-// large, or no buffer: the workspace then comes from the pool).
-float* stream_scratch(Device& d, hipStream_t stream, int64_t bytes) {
+// The scratch of `stream`'s buffer for a workspace of `bytes`, with *hold
+// locking the stream's scratch mutex until the caller has enqueued its last
+// kernel, or null (too large, or no buffer: the workspace then comes from the
+// pool).
+float* stream_scratch(Device& d, hipStream_t stream, int64_t bytes,
+                      std::unique_lock<std::mutex>* hold) {
     if (bytes <= 0 || size_t(bytes) > kStreamScratchBytes) return nullptr;
-    std::lock_guard<std::mutex> lock(d.pub_mu);
-    StreamPub* b = stream_buffer(d, stream);
-    return b ? b->scratch : nullptr;
+    std::shared_ptr<std::mutex> mu;
+    float* scratch = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(d.pub_mu);
+        StreamPub* b = stream_buffer(d, stream);
+        if (!b) return nullptr;
+        mu = b->scratch_mu;
+        scratch = b->scratch;
+    }
+    *hold = std::unique_lock<std::mutex>(*mu);  // the buffer outlives the call
+    return scratch;
 }
 
 bool stream_pub(Device& d, hipStream_t stream, rd::Published* pub, hipError_t* err) {
@@ -281,6 +299,7 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
     if (injected().launch) return hip_fail(hipErrorLaunchFailure, RD_ERR_LAUNCH);
     float* ws = nullptr;
     bool pooled = false;
+    std::unique_lock<std::mutex> scratch_hold;
     rd::Published pub;
     bool published = false;
     if (p.workspace_bytes > 0 && !fixed) {
@@ -302,7 +321,7 @@ rd_status execute(const rd_plan& p, int op, Device& dev, const float* x, const r
     if (p.workspace_bytes > 0 && fixed) {
         ws = fixed;
     } else if (p.workspace_bytes > 0 && !published) {
-        ws = stream_scratch(dev, s, p.workspace_bytes);
+        ws = stream_scratch(dev, s, p.workspace_bytes, &scratch_hold);
         if (!ws) {
             rd_status st = device_memory(dev);
             if (st != RD_OK) return st;
@@ -435,8 +454,9 @@ rd_status cumsum_checked(const float* x, rd::Strides v, bool rev, float* out,
         }
     }
     bool pooled = false;
+    std::unique_lock<std::mutex> scratch_hold;
     if (p.workspace_bytes > 0 && !published) {
-        ws = stream_scratch(*dev, stream, p.workspace_bytes);
+        ws = stream_scratch(*dev, stream, p.workspace_bytes, &scratch_hold);
         if (!ws) {
             st = device_memory(*dev);
             if (st != RD_OK) return st;

@@ -337,6 +337,51 @@ def test_split_scratch_streams():
         H.assert_bitwise_equal_oracle(got, S, "scratch %s %s" % (kind, (o, r, i)))
 
 
+def test_split_scratch_threads_one_stream():
+    """Eight host threads make split calls with a second kernel on one shared
+    stream (the scratch of its buffer): each call holds the stream's scratch
+    from its first launch to its last, so no call's first kernel runs between
+    another's two; every result is the oracle's exact integer sum."""
+    import threading
+    t = H.torch()
+    lib = rd.load()
+    shapes = [(64, 262144, 1), (2, 100000, 129), (300, 1000, 7)]
+    for o, r, i in shapes:
+        assert rd.rd_plan_dim(256, o, r, i).as_dict()["combine"] == "pass"
+    n = max(o * r * i for o, r, i in shapes)
+    data = [workloads.small_ints(n, 800 + k) for k in range(8)]
+    xs = [H.upload(a) for a in data]
+    want = {(k, s_): oracle.sum_dim(data[k][:s_[0] * s_[1] * s_[2]], *s_)[0].astype(np.float32)
+            for k in range(8) for s_ in shapes}
+    stream = t.cuda.Stream()
+    h = stream.cuda_stream
+    outs = {}
+    errors = []
+    t.cuda.synchronize()
+
+    def work(k):
+        try:
+            for rep in range(12):
+                o, r, i = shapes[(k + rep) % len(shapes)]
+                y = t.empty(o * i, device="cuda")
+                st = lib.rd_sum_dim(xs[k].data_ptr(), o, r, i, y.data_ptr(), h)
+                if st != 0:
+                    errors.append((k, rep, st))
+                outs[(k, rep)] = ((o, r, i), y)
+        except Exception as e:  # reported below
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    stream.synchronize()
+    for (k, rep), (shape, y) in outs.items():
+        assert np.array_equal(y.cpu().numpy(), want[(k, shape)].reshape(-1)), (k, rep, shape)
+
+
 _COL_PUB_SPIN = r"""
 import sys
 sys.path.insert(0, sys.argv[1])
