@@ -148,13 +148,15 @@ rd_status plan_rows(int cu, int64_t outer, int64_t R, int op, const rd_tune* t,
                 if (cap < 1) cap = 1;
             }
         }
-        // Up to kShallowMaxBytes, few rows still at the default depth take 4
+        // Up to kShallowMaxBytes, rows still at the default depth take 4
         // loads a step (pieces of the same length, more steps each): us,
         // same box, A/B, 70001 floats 8.8 -> 7.15 (17 pieces instead of 4),
         // 3e5 7.8 -> 7.15, 6e6 12.2 -> 11.55, 1e7 13.7 -> 13.0, 2e7 20.1 ->
-        // 18.5; 3.4e7 and 4e7 level.  (Where the rule above has already
-        // gone to 8 it stays: 4e6 8.4 at 8, 8.9 at 4.)
-        if (!(t && t->unroll) && p->group == kBlock && outer <= kPubMaxRows &&
+        // 18.5; 3.4e7 and 4e7 level; [100, 3e5] 26.4 -> 24.4, [200, 1e5]
+        // 21.5 -> 19.8, [5, 2e5] 9.1 -> 8.4, [8, 2e6] 15.1 -> 14.5, [32, 1e6]
+        // and [10, 3e6] level.  (Where the rule above has already gone to 8
+        // it stays: 4e6 8.4 at 8, 8.9 at 4.)
+        if (!(t && t->unroll) && p->group == kBlock &&
             p->unroll == kRowsUnrollBlock && bytes <= kShallowMaxBytes &&
             rows_shape_supported(op, p->group, kShallowUnroll)) {
             p->unroll = kShallowUnroll;

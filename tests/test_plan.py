@@ -111,8 +111,8 @@ def test_row_pieces():
     are fewer rows than CUs, otherwise from 1 GB of input on; never below one
     full unrolled step (16 x 16 bytes) per lane -- except that a few rows
     which a step of 2 loads per lane lets give every CU a piece take the
-    shallowest depth that does, and few rows of at most 128 MiB left at the
-    default depth take 4 loads a step."""
+    shallowest depth that does, and fewer rows than CUs of at most 128 MiB
+    left at the default depth take 4 loads a step."""
     def P(outer, R):
         return rd.rd_plan_dim(CU, outer, R, 1).split
     assert P(1, 10**6) == 256                # depth 2 (16 would allow only 61)
@@ -121,7 +121,8 @@ def test_row_pieces():
     assert (P(1, 300_000), rd.rd_plan_dim(CU, 1, 300_000, 1).unroll) == (73, 4)
     assert (P(1, 10**7), rd.rd_plan_dim(CU, 1, 10**7, 1).unroll) == (306, 4)
     assert (P(1, 4 * 10**7), rd.rd_plan_dim(CU, 1, 4 * 10**7, 1).unroll) == (1221, 16)
-    assert rd.rd_plan_dim(CU, 5, 10**6, 1).unroll == 16      # more than 4 rows
+    assert rd.rd_plan_dim(CU, 5, 10**6, 1).unroll == 4       # more rows, under 128 MiB
+    assert rd.rd_plan_dim(CU, 16, 4 * 10**6, 1).unroll == 16  # 256 MB: the default depth
     # the softmax denominator: its shallowest built depth, 8 (122 pieces)
     sm = rd.rd_plan_reduce(CU, 1, 10**6, 1, "softmax_denom")
     assert (sm.unroll, sm.split) == (8, 122)
